@@ -1,0 +1,522 @@
+/* hardkv_oracle.c -- TEST INFRASTRUCTURE ONLY.
+ *
+ * Plain CPU definition of one HARD-KV decode step, written from the HARD-KV
+ * explainer pages ("HARD-KV: Head-Adaptive Regularization for Decoding-time KV
+ * Compression", technical summary section 2).  Every step is a scalar loop in
+ * the order the definition states; only qsort (for the ranking) is a library
+ * primitive.  Float work that must match the GPU bit for bit is done in single
+ * precision with one rounding per operation (build with -ffp-contract=off,
+ * never -ffast-math); attention and the condensed sums are done in binary64.
+ *
+ * Points the pages leave open are settled by the readings listed in the
+ * design notes (per-step view over a fixed pool, max over the GQA group of the
+ * current queries, tau-scaled softmax calibration with integer weights, top-p
+ * with ties to the lower position, one condensed slot per merged block, a
+ * ln(n) logit bias for merged slots).
+ */
+#include "hardkv_oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define BK 64
+#define ORC_LOG2E 1.4426950408889634074 /* binary64 nearest log2(e) */
+
+/* ------------------------------------------------------------------------------------
+ * storage elements
+ * ---------------------------------------------------------------------------------- */
+static float elem_get(const void *base, int64_t i, int eb) {
+  if (eb == 4) return ((const float *)base)[i];
+  uint32_t u = (uint32_t)((const uint16_t *)base)[i] << 16; /* bf16 widens exactly */
+  float f;
+  memcpy(&f, &u, 4);
+  return f;
+}
+
+static void row_copy(void *dst, int64_t drow, const void *src, int64_t srow, int D, int eb) {
+  memcpy((char *)dst + drow * D * eb, (const char *)src + srow * D * eb, (size_t)D * eb);
+}
+
+/* pool ring row of position p for unit u (rows counted over the whole buffer) */
+static int64_t pool_row(const orc_cfg *cfg, int64_t u, int64_t p) {
+  int64_t P = cfg->pool_blocks;
+  return (u * P + (p / BK) % P) * BK + p % BK;
+}
+
+/* ------------------------------------------------------------------------------------
+ * Score: max-pooled logits (section 2.B names "max-pooled logits" as an importance
+ * metric; the pooling runs over the GQA group of the current step's queries).
+ * Each query-key logit is a dot product taken as a canonical pairwise tree:
+ * products in index order, then level l+1 element i = level l [2i] + [2i+1].
+ * ---------------------------------------------------------------------------------- */
+float orc_dot_pairwise(const float *a, const float *b, int32_t n) {
+  float lvl[1024];
+  for (int i = 0; i < n; ++i) {
+    float p = a[i] * b[i];
+    lvl[i] = p;
+  }
+  for (int m = n; m > 1; m /= 2) {
+    for (int i = 0; i < m / 2; ++i) {
+      float s = lvl[2 * i] + lvl[2 * i + 1];
+      lvl[i] = s;
+    }
+  }
+  return lvl[0];
+}
+
+float orc_score_row(const float *q, int32_t G, const float *k, int32_t D) {
+  float s = orc_dot_pairwise(q, k, D);
+  for (int g = 1; g < G; ++g) {
+    float d = orc_dot_pairwise(q + (int64_t)g * D, k, D);
+    if (d > s) s = d;
+  }
+  return s + 0.0f; /* a zero score is +0 whatever the signs of the group's zeros */
+}
+
+/* ------------------------------------------------------------------------------------
+ * Logits Calibration (section 2.B): the scores are mapped to one softmax by a
+ * temperature, softmax(s / (sqrt(D) tau)), evaluated in base 2 with
+ * kappa = log2(e) / (sqrt(D) tau).  Probabilities are carried as integer
+ * weights w = max(1, floor(2^24 * 2^((s - m) kappa))), so masses add exactly.
+ * 2^t uses t = n + f with n = floor(t) and f = t - n in [0, 1), and the degree-9
+ * Taylor polynomial of 2^f = sum (f ln 2)^i / i! in Horner form.  With f >= 0
+ * every Horner step multiplies and adds non-negative numbers, so each rounding
+ * is monotone and 2^t, hence w, never decreases as the score grows: the
+ * calibration keeps the order of the scores.
+ * ---------------------------------------------------------------------------------- */
+#define ORC_NCOEFF 10
+static float g_coeff[ORC_NCOEFF];
+
+__attribute__((constructor)) static void init_coeffs(void) {
+  const long double ln2 = 0.693147180559945309417232121458176568L;
+  long double v = 1.0L;
+  for (int i = 0; i < ORC_NCOEFF; ++i) {
+    if (i > 0) v = v * ln2 / (long double)i;
+    g_coeff[i] = (float)v;
+  }
+}
+
+float orc_poly_coeff(int32_t i) { return (i >= 0 && i < ORC_NCOEFF) ? g_coeff[i] : 0.0f; }
+
+float orc_kappa(int32_t D, float tau) {
+  return (float)(ORC_LOG2E / (sqrt((double)D) * (double)tau));
+}
+
+float orc_exp2_poly(float f) {
+  float y = g_coeff[ORC_NCOEFF - 1];
+  for (int i = ORC_NCOEFF - 2; i >= 0; --i) {
+    float p = y * f;
+    y = p + g_coeff[i];
+  }
+  return y;
+}
+
+void orc_exp2_poly_batch(const float *f, float *y, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) y[i] = orc_exp2_poly(f[i]);
+}
+
+static uint32_t weight_from_t(float t) {
+  if (!(t >= -60.0f)) return 1u;
+  float n = floorf(t);
+  float f = t - n; /* in [0, 1); rounded only when n = -1 */
+  float y = orc_exp2_poly(f);
+  float e = ldexpf(y, (int)n);
+  float big = e * 16777216.0f; /* exact: scaling by 2^24 */
+  uint32_t w = (uint32_t)floorf(big);
+  return w < 1u ? 1u : w;
+}
+
+uint32_t orc_weight(float s, float m, float kappa) {
+  float x = s - m;
+  float t = x * kappa;
+  return weight_from_t(t);
+}
+
+void orc_weight_batch(const float *t, uint32_t *w, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) w[i] = weight_from_t(t[i]);
+}
+
+/* ------------------------------------------------------------------------------------
+ * Calibrated Top-p (section 2.A, tier 2; section 2.B): keep the smallest set of
+ * survivors, taken in order of decreasing weight (lower position first on
+ * ties), whose mass reaches T = ceil(p_q W_U / 2^16), p_q = rne(p 2^16).
+ * ---------------------------------------------------------------------------------- */
+uint32_t orc_pq(double p) { return (uint32_t)rint(p * 65536.0); }
+
+typedef struct {
+  uint32_t w;
+  int32_t idx;
+  int64_t pos;
+} wp_t;
+
+static int cmp_wp(const void *pa, const void *pb) {
+  const wp_t *a = (const wp_t *)pa, *b = (const wp_t *)pb;
+  if (a->w != b->w) return a->w > b->w ? -1 : 1;
+  if (a->pos != b->pos) return a->pos < b->pos ? -1 : 1;
+  return 0;
+}
+
+int32_t orc_topp(const uint32_t *w, const int64_t *pos, int32_t n, uint32_t pq, uint8_t *selected,
+                 uint64_t *thresh_out) {
+  if (thresh_out) *thresh_out = 0;
+  if (n <= 0) return 0;
+  uint64_t wu = 0;
+  for (int32_t i = 0; i < n; ++i) wu += w[i];
+  uint64_t T = ((uint64_t)pq * wu + 65535u) / 65536u;
+  if (thresh_out) *thresh_out = T;
+  memset(selected, 0, (size_t)n);
+  wp_t *arr = (wp_t *)malloc(sizeof(wp_t) * (size_t)n);
+  for (int32_t i = 0; i < n; ++i) {
+    arr[i].w = w[i];
+    arr[i].idx = i;
+    arr[i].pos = pos[i];
+  }
+  qsort(arr, (size_t)n, sizeof(wp_t), cmp_wp);
+  uint64_t acc = 0;
+  int32_t k = 0;
+  while (acc < T) {
+    acc += arr[k].w;
+    selected[arr[k].idx] = 1;
+    ++k;
+  }
+  free(arr);
+  return k;
+}
+
+/* ------------------------------------------------------------------------------------
+ * Attention over a list of rows, binary64.  logit_i = (q . key_i) / sqrt(D) + bias_i,
+ * out = sum softmax(logit)_i value_i.  Shared by the tiered attention and the
+ * full-attention reference so that the two agree bit for bit on the same rows.
+ * ---------------------------------------------------------------------------------- */
+typedef void (*row_fn)(const void *ctx, int64_t i, double *key, double *val, double *bias,
+                       int *has_bias);
+
+static void attend_core(const double *qd, int D, int64_t n, row_fn get, const void *ctx,
+                        double *out) {
+  for (int d = 0; d < D; ++d) out[d] = 0.0;
+  if (n == 0) return;
+  double *logit = (double *)malloc(sizeof(double) * (size_t)n);
+  double *key = (double *)malloc(sizeof(double) * (size_t)D);
+  double *val = (double *)malloc(sizeof(double) * (size_t)D);
+  double sq = sqrt((double)D);
+  double mx = -INFINITY;
+  for (int64_t i = 0; i < n; ++i) {
+    double bias = 0.0;
+    int hb = 0;
+    get(ctx, i, key, val, &bias, &hb);
+    double dot = 0.0;
+    for (int d = 0; d < D; ++d) dot += qd[d] * key[d];
+    double l = dot / sq;
+    if (hb) l = l + bias;
+    logit[i] = l;
+    if (l > mx) mx = l;
+  }
+  double sum = 0.0;
+  for (int64_t i = 0; i < n; ++i) {
+    double bias = 0.0;
+    int hb = 0;
+    get(ctx, i, key, val, &bias, &hb);
+    double e = exp(logit[i] - mx);
+    sum += e;
+    for (int d = 0; d < D; ++d) out[d] += e * val[d];
+  }
+  for (int d = 0; d < D; ++d) out[d] /= sum;
+  free(logit);
+  free(key);
+  free(val);
+}
+
+typedef struct {
+  const float *k, *v;
+  int D;
+} flat_ctx;
+
+static void flat_row(const void *ctx, int64_t i, double *key, double *val, double *bias, int *hb) {
+  const flat_ctx *c = (const flat_ctx *)ctx;
+  for (int d = 0; d < c->D; ++d) {
+    key[d] = (double)c->k[i * c->D + d];
+    val[d] = (double)c->v[i * c->D + d];
+  }
+  *bias = 0.0;
+  *hb = 0;
+}
+
+void orc_full_attention(const float *q, const float *k, const float *v, int32_t n, int32_t D,
+                        double *out) {
+  double qd[1024];
+  for (int d = 0; d < D; ++d) qd[d] = (double)q[d];
+  flat_ctx c = {k, v, D};
+  attend_core(qd, D, n, flat_row, &c, out);
+}
+
+/* the tiers of one unit, in attention order: condensed slots with n > 0, view rows
+ * r < k*, dense positions ascending (section 2.A: condensed, sparse, dense tiers) */
+typedef struct {
+  const orc_cfg *cfg;
+  const orc_state *st;
+  int64_t u;
+  int64_t n_cond, n_view, n_dense, dense_lo;
+  int32_t slot[4096];
+} tier_ctx;
+
+static void tier_row(const void *ctx, int64_t i, double *key, double *val, double *bias,
+                     int *hb) {
+  const tier_ctx *tc = (const tier_ctx *)ctx;
+  const orc_cfg *cfg = tc->cfg;
+  const orc_state *st = tc->st;
+  int D = cfg->head_dim, eb = cfg->elem_bytes;
+  if (i < tc->n_cond) {
+    int64_t s = tc->u * cfg->condensed_slots + tc->slot[i];
+    double om = st->cond_omega[s];
+    for (int d = 0; d < D; ++d) {
+      key[d] = st->cond_kn[s * D + d] / om;
+      val[d] = st->cond_vn[s * D + d] / om;
+    }
+    *bias = log((double)st->cond_n[s]);
+    *hb = cfg->merge_bias;
+    return;
+  }
+  i -= tc->n_cond;
+  int64_t row;
+  const void *kb, *vb;
+  if (i < tc->n_view) {
+    row = tc->u * cfg->view_cap + i;
+    kb = st->view_k;
+    vb = st->view_v;
+  } else {
+    int64_t p = tc->dense_lo + (i - tc->n_view);
+    row = tc->u * cfg->dense_window + p % cfg->dense_window;
+    kb = st->dense_k;
+    vb = st->dense_v;
+  }
+  for (int d = 0; d < D; ++d) {
+    key[d] = (double)elem_get(kb, row * D + d, eb);
+    val[d] = (double)elem_get(vb, row * D + d, eb);
+  }
+  *bias = 0.0;
+  *hb = 0;
+}
+
+/* ------------------------------------------------------------------------------------
+ * Prefill: the cascade cache of a context of L tokens with nothing condensed yet.
+ * The last min(L, W) positions sit in the dense ring, [0, L - W) in the pool.
+ * ---------------------------------------------------------------------------------- */
+int32_t orc_prefill(const orc_cfg *cfg, orc_state *st, const void *k_ctx, const void *v_ctx,
+                    const int64_t *ctx_len, int64_t max_len) {
+  int B = cfg->batch, H = cfg->num_kv_heads, D = cfg->head_dim, eb = cfg->elem_bytes;
+  int W = cfg->dense_window, C = cfg->condensed_slots;
+  for (int b = 0; b < B; ++b) {
+    int64_t L = ctx_len[b];
+    if (L < 0 || L > max_len) return -1;
+    if (L - W + 1 > (int64_t)cfg->pool_blocks * BK) return -3;
+  }
+  st->error_word = 0;
+  for (int b = 0; b < B; ++b) {
+    int64_t L = ctx_len[b];
+    st->seq_len[b] = L;
+    for (int h = 0; h < H; ++h) {
+      int64_t u = (int64_t)b * H + h;
+      st->pool_head[u] = 0;
+      st->cond_cursor[u] = 0;
+      for (int s = 0; s < C; ++s) {
+        int64_t si = u * C + s;
+        st->cond_omega[si] = 0.0;
+        st->cond_n[si] = 0;
+        for (int d = 0; d < D; ++d) st->cond_kn[si * D + d] = st->cond_vn[si * D + d] = 0.0;
+      }
+      memset((char *)st->dense_k + u * W * D * eb, 0, (size_t)W * D * eb);
+      memset((char *)st->dense_v + u * W * D * eb, 0, (size_t)W * D * eb);
+      int64_t src0 = u * max_len;
+      int64_t lo = L > W ? L - W : 0;
+      for (int64_t p = lo; p < L; ++p) {
+        row_copy(st->dense_k, u * W + p % W, k_ctx, src0 + p, D, eb);
+        row_copy(st->dense_v, u * W + p % W, v_ctx, src0 + p, D, eb);
+      }
+      for (int64_t p = 0; p < lo; ++p) {
+        row_copy(st->pool_k, pool_row(cfg, u, p), k_ctx, src0 + p, D, eb);
+        row_copy(st->pool_v, pool_row(cfg, u, p), v_ctx, src0 + p, D, eb);
+      }
+    }
+  }
+  return 0;
+}
+
+/* ------------------------------------------------------------------------------------
+ * One unit (sequence b, KV head h) of the step after the append.
+ * ---------------------------------------------------------------------------------- */
+static uint32_t unit_step(const orc_cfg *cfg, orc_state *st, int b, int h, const void *q,
+                          double *out, int do_attend) {
+  const int H = cfg->num_kv_heads, Hq = cfg->num_q_heads, G = Hq / H, D = cfg->head_dim;
+  const int eb = cfg->elem_bytes, W = cfg->dense_window, P = cfg->pool_blocks;
+  const int64_t u = (int64_t)b * H + h;
+  uint32_t err = 0;
+
+  const int64_t t = st->seq_len[b];
+  const int64_t c = st->pool_head[u];
+  const int64_t pend = t > W ? t - W : 0;
+  const int64_t N = pend - c;
+
+  /* plan (section 2.A, tier 3): whole oldest blocks leave the pool once it holds
+   * more than S_cap tokens */
+  int64_t E = 0;
+  if (cfg->cond_mode != ORC_COND_OFF && N > cfg->sparse_cap) E = (N - cfg->sparse_cap + BK - 1) / BK;
+  const int64_t u0 = c + BK * E;
+
+  /* queries of the group, widened */
+  float *qg = (float *)malloc(sizeof(float) * (size_t)G * D);
+  for (int g = 0; g < G; ++g)
+    for (int d = 0; d < D; ++d) qg[g * D + d] = elem_get(q, ((int64_t)b * Hq + h * G + g) * D + d, eb);
+
+  /* score */
+  float *krow = (float *)malloc(sizeof(float) * (size_t)D);
+  float m = -INFINITY;
+  for (int64_t j = c; j < pend; ++j) {
+    int64_t r = pool_row(cfg, u, j);
+    for (int d = 0; d < D; ++d) krow[d] = elem_get(st->pool_k, r * D + d, eb);
+    float s = orc_score_row(qg, G, krow, D);
+    if (!isfinite(s)) err |= ORC_ERR_NONFINITE;
+    st->scores[r] = s;
+    if (s > m) m = s;
+  }
+
+  /* calibrate over the whole pool */
+  const float kappa = orc_kappa(D, cfg->tau[h]);
+  uint64_t w_all = 0, w_u = 0;
+  for (int64_t j = c; j < pend; ++j) {
+    int64_t r = pool_row(cfg, u, j);
+    uint32_t w = orc_weight(st->scores[r], m, kappa);
+    st->weights[r] = w;
+    w_all += w;
+    if (j >= u0) w_u += w;
+  }
+
+  /* top-p over the survivors U = [u0, pend) */
+  const int32_t nU = (int32_t)(pend - u0);
+  uint32_t *wU = (uint32_t *)malloc(sizeof(uint32_t) * (size_t)(nU > 0 ? nU : 1));
+  int64_t *pU = (int64_t *)malloc(sizeof(int64_t) * (size_t)(nU > 0 ? nU : 1));
+  uint8_t *sel = (uint8_t *)malloc((size_t)(nU > 0 ? nU : 1));
+  for (int32_t i = 0; i < nU; ++i) {
+    pU[i] = u0 + i;
+    wU[i] = st->weights[pool_row(cfg, u, u0 + i)];
+  }
+  uint64_t T = 0;
+  const int32_t kstar = orc_topp(wU, pU, nU, orc_pq(cfg->top_p), sel, &T);
+
+  for (int i = 0; i < P; ++i) st->mask[u * P + i] = 0;
+  for (int32_t i = 0; i < nU; ++i)
+    if (sel[i]) {
+      int64_t j = u0 + i;
+      st->mask[u * P + (j / BK) % P] |= (uint64_t)1 << (j % BK);
+    }
+
+  /* Index Regularization, Rewrite Cache with a max-length flat index
+   * (section 2.C): the selected rows, in ascending position, become rows
+   * 0 .. k*-1 of the head's fixed-capacity view */
+  int32_t r = 0;
+  if (kstar > cfg->view_cap) err |= ORC_ERR_VIEW_OVERFLOW;
+  for (int32_t i = 0; i < nU; ++i) {
+    if (!sel[i]) continue;
+    if (r < cfg->view_cap) {
+      int64_t j = u0 + i;
+      row_copy(st->view_k, u * cfg->view_cap + r, st->pool_k, pool_row(cfg, u, j), D, eb);
+      row_copy(st->view_v, u * cfg->view_cap + r, st->pool_v, pool_row(cfg, u, j), D, eb);
+      st->view_pos[u * cfg->view_cap + r] = (int32_t)j;
+    }
+    ++r;
+  }
+
+  /* condense (section 2.A, tier 3): each of the E oldest blocks is dropped
+   * (evict) or merged into the next condensed slot with weights w / W_all */
+  if (cfg->cond_mode == ORC_COND_MERGE) {
+    const int C = cfg->condensed_slots;
+    for (int64_t e = 0; e < E; ++e) {
+      int32_t sigma = st->cond_cursor[u];
+      st->cond_cursor[u] = (sigma + 1) % C;
+      int64_t si = u * C + sigma;
+      for (int64_t j = c + BK * e; j < c + BK * (e + 1); ++j) {
+        int64_t rr = pool_row(cfg, u, j);
+        double om = (double)st->weights[rr] / (double)w_all;
+        st->cond_omega[si] += om;
+        for (int d = 0; d < D; ++d) {
+          st->cond_kn[si * D + d] += om * (double)elem_get(st->pool_k, rr * D + d, eb);
+          st->cond_vn[si * D + d] += om * (double)elem_get(st->pool_v, rr * D + d, eb);
+        }
+      }
+      st->cond_n[si] += BK;
+    }
+  }
+  st->pool_head[u] = c + BK * E;
+  st->budget[u] = kstar;
+  st->n_condense[u] = (int32_t)E;
+  st->w_all[u] = w_all;
+  st->w_u[u] = w_u;
+  st->thresh[u] = T;
+
+  /* attention over condensed, sparse (view) and dense tiers */
+  if (do_attend) {
+    tier_ctx *tc = (tier_ctx *)malloc(sizeof(tier_ctx));
+    tc->cfg = cfg;
+    tc->st = st;
+    tc->u = u;
+    tc->n_cond = 0;
+    for (int s = 0; s < cfg->condensed_slots && s < 4096; ++s)
+      if (st->cond_n[u * cfg->condensed_slots + s] > 0) tc->slot[tc->n_cond++] = s;
+    tc->n_view = kstar < cfg->view_cap ? kstar : cfg->view_cap;
+    tc->dense_lo = t > W ? t - W : 0;
+    tc->n_dense = t - tc->dense_lo;
+    double qd[1024];
+    for (int g = 0; g < G; ++g) {
+      for (int d = 0; d < D; ++d) qd[d] = (double)qg[g * D + d];
+      attend_core(qd, D, tc->n_cond + tc->n_view + tc->n_dense, tier_row, tc,
+                  out + ((int64_t)b * Hq + h * G + g) * D);
+    }
+    free(tc);
+  }
+  free(qg);
+  free(krow);
+  free(wU);
+  free(pU);
+  free(sel);
+  return err;
+}
+
+/* ------------------------------------------------------------------------------------
+ * The step: linear append to the dense tier (section 2.A, stage 1), then per
+ * unit: plan, score, calibrate, top-p (stage 2), regularize (stage 3),
+ * condense (stage 4), and attention.
+ * ---------------------------------------------------------------------------------- */
+int32_t orc_step(const orc_cfg *cfg, orc_state *st, const void *q, const void *k_new,
+                 const void *v_new, double *out, int32_t do_attend, int32_t nthreads) {
+  const int B = cfg->batch, H = cfg->num_kv_heads, D = cfg->head_dim, eb = cfg->elem_bytes;
+  const int W = cfg->dense_window;
+  if (cfg->condensed_slots > 4096 || D > 1024) return -2;
+  uint32_t err = 0;
+  for (int b = 0; b < B; ++b) {
+    const int64_t t = st->seq_len[b];
+    for (int h = 0; h < H; ++h) {
+      const int64_t u = (int64_t)b * H + h;
+      if (t >= W) {
+        const int64_t p = t - W; /* leaves the dense window, joins the pool tail */
+        if (p + 1 - st->pool_head[u] > (int64_t)cfg->pool_blocks * BK) err |= ORC_ERR_POOL_OVERFLOW;
+        row_copy(st->pool_k, pool_row(cfg, u, p), st->dense_k, u * W + p % W, D, eb);
+        row_copy(st->pool_v, pool_row(cfg, u, p), st->dense_v, u * W + p % W, D, eb);
+      }
+      row_copy(st->dense_k, u * W + t % W, k_new, u, D, eb);
+      row_copy(st->dense_v, u * W + t % W, v_new, u, D, eb);
+    }
+    st->seq_len[b] = t + 1;
+  }
+  const int64_t units = (int64_t)B * H;
+#ifdef _OPENMP
+  int nt = nthreads > 0 ? nthreads : omp_get_max_threads();
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nt) reduction(| : err)
+#endif
+  for (int64_t i = 0; i < units; ++i) err |= unit_step(cfg, st, (int)(i / H), (int)(i % H), q, out, do_attend);
+  (void)nthreads;
+  st->error_word |= err;
+  return 0;
+}

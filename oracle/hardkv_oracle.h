@@ -1,0 +1,93 @@
+/* hardkv_oracle.h -- TEST INFRASTRUCTURE ONLY.
+ *
+ * A plain, slow CPU definition of one decode step of HARD-KV ("HARD-KV:
+ * Head-Adaptive Regularization for Decoding-time KV Compression", technical
+ * summary, section 2: Cascade Cache Hierarchy, Logits Calibration Mechanism,
+ * System-Aware Index Regularization).  Only the tests, the smoke check and the
+ * benchmark's CPU baseline may load this library; the product path never does.
+ * It shares no source with the HIP library: its layouts follow the same
+ * written specification, restated here independently.
+ *
+ * All buffers are host memory owned by the caller.
+ *
+ * Layouts (B batch, H KV heads, G = Hq/H, D head_dim, W dense window,
+ * P pool ring blocks of 64 rows, V view capacity, C condensed slots):
+ *   dense_k/v   [B][H][W][D]     storage elements; position p sits in slot p mod W
+ *   pool_k/v    [B][H][P][64][D] position p sits in block (p/64) mod P, row p mod 64
+ *   view_k/v    [B][H][V][D]     row r holds the r-th selected position (ascending)
+ *   view_pos    int32 [B][H][V]
+ *   cond_kn/vn  double [B][H][C][D]   weighted sums (numerators)
+ *   cond_omega  double [B][H][C]      sum of merge weights
+ *   cond_n      int32 [B][H][C]       tokens merged into the slot
+ *   cond_cursor int32 [B][H]          next slot (ring)
+ *   seq_len     int64 [B]             t, tokens so far
+ *   pool_head   int64 [B][H]          c, oldest pool position (multiple of 64)
+ *   scores      float [B][H][P*64]    indexed by pool ring row
+ *   weights     uint32 [B][H][P*64]
+ *   mask        uint64 [B][H][P]      word (p/64) mod P, bit p mod 64
+ *   budget, n_condense int32 [B][H]
+ *   w_all, w_u, thresh uint64 [B][H] (diagnostics: total mass, survivor mass, T)
+ * q is [B][Hq][D], k_new/v_new are [B][H][D], all in the storage type.
+ * out is double [B][Hq][D].
+ */
+#ifndef HARDKV_ORACLE_H
+#define HARDKV_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum { ORC_COND_OFF = 0, ORC_COND_EVICT = 1, ORC_COND_MERGE = 2 };
+enum { ORC_ERR_POOL_OVERFLOW = 1u, ORC_ERR_VIEW_OVERFLOW = 2u, ORC_ERR_NONFINITE = 4u };
+
+typedef struct {
+  int32_t batch, num_q_heads, num_kv_heads, head_dim;
+  int32_t elem_bytes;        /* 2: bf16, 4: fp32 */
+  int32_t dense_window, pool_blocks, sparse_cap, view_cap, condensed_slots, cond_mode;
+  int32_t merge_bias;        /* 1: condensed slot logit gets + ln n (default), 0: none */
+  double top_p;
+  const float *tau;          /* [H] */
+} orc_cfg;
+
+typedef struct {
+  void *dense_k, *dense_v, *pool_k, *pool_v, *view_k, *view_v;
+  int32_t *view_pos;
+  double *cond_kn, *cond_vn, *cond_omega;
+  int32_t *cond_n, *cond_cursor;
+  int64_t *seq_len, *pool_head;
+  float *scores;
+  uint32_t *weights;
+  uint64_t *mask;
+  int32_t *budget, *n_condense;
+  uint64_t *w_all, *w_u, *thresh;
+  uint32_t error_word;
+} orc_state;
+
+/* building blocks, exported for the pin tests */
+float    orc_dot_pairwise(const float *a, const float *b, int32_t n);
+float    orc_score_row(const float *q, int32_t G, const float *k, int32_t D);
+float    orc_kappa(int32_t D, float tau);
+float    orc_poly_coeff(int32_t i);
+float    orc_exp2_poly(float f);
+void     orc_exp2_poly_batch(const float *f, float *y, int64_t n);
+uint32_t orc_weight(float s, float m, float kappa);
+void     orc_weight_batch(const float *t, uint32_t *w, int64_t n);
+uint32_t orc_pq(double p);
+int32_t  orc_topp(const uint32_t *w, const int64_t *pos, int32_t n, uint32_t pq,
+                  uint8_t *selected, uint64_t *thresh_out);
+
+/* the step */
+int32_t orc_prefill(const orc_cfg *cfg, orc_state *st, const void *k_ctx, const void *v_ctx,
+                    const int64_t *ctx_len, int64_t max_len);
+int32_t orc_step(const orc_cfg *cfg, orc_state *st, const void *q, const void *k_new,
+                 const void *v_new, double *out, int32_t do_attend, int32_t nthreads);
+/* full softmax attention over positions [0, t) of a flat cache, binary64 (pin I4) */
+void    orc_full_attention(const float *q, const float *k, const float *v, int32_t n,
+                           int32_t D, double *out);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,22 @@
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) and the built HIP library")
+    config.addinivalue_line("markers", "slow: long CPU test")
+
+
+@pytest.fixture(scope="session", autouse=True)
+def _oracle_built():
+    lib = os.path.join(ROOT, "oracle", "liboracle_hardkv.so")
+    if not os.path.exists(lib):
+        import subprocess
+        subprocess.run([sys.executable, os.path.join(ROOT, "oracle", "build.py"), "-q"], check=True)
+    yield

@@ -1,0 +1,223 @@
+"""Pins of the oracle's whole step (no GPU): closed forms and identities that the
+tiered step must reduce to, and the ring bookkeeping against logical positions."""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import hardkv_oracle as orc
+from synth import make_inputs, tiny_workload
+from synth.configs import COND_EVICT, COND_MERGE, COND_OFF
+
+
+def _f32(x: torch.Tensor) -> np.ndarray:
+    return x.float().cpu().numpy()
+
+
+def _run(wl, inp, steps=1, **kw):
+    o = orc.Oracle(wl, **kw)
+    assert o.prefill(inp.k_ctx, inp.v_ctx, inp.ctx_len) == 0
+    outs = [o.step(inp.q[s], inp.k_new[s], inp.v_new[s]) for s in range(steps)]
+    return o, outs
+
+
+def _positions_kv(inp, b, h, steps):
+    """Keys and values of positions [0, t) of unit (b, h) after `steps` appends."""
+    L = int(inp.ctx_len[b])
+    k = np.concatenate([_f32(inp.k_ctx[b, h, :L]), _f32(inp.k_new[:steps, b, h])], 0)
+    v = np.concatenate([_f32(inp.v_ctx[b, h, :L]), _f32(inp.v_new[:steps, b, h])], 0)
+    return k, v
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_p1_off_equals_full_attention(dtype):
+    """p = 1 with condensation off: the tiers hold every position once, in order, so the
+    tiered attention equals full attention over [0, t) bit for bit, and a library
+    softmax attention in binary64 to 1e-12 (I4)."""
+    steps = 3
+    wl = tiny_workload(dtype=dtype, cond_mode=COND_OFF, top_p=1.0, steps=steps)
+    inp = make_inputs(wl)
+    o, outs = _run(wl, inp, steps)
+    G, D = wl.group, wl.head_dim
+    for b in range(wl.batch):
+        for h in range(wl.num_kv_heads):
+            k, v = _positions_kv(inp, b, h, steps)
+            assert o.budget[b, h] == int(inp.ctx_len[b]) + steps - wl.dense_window
+            for g in range(G):
+                qh = h * G + g
+                q = _f32(inp.q[steps - 1, b, qh])
+                full = orc.full_attention(q, k, v)
+                assert np.array_equal(outs[-1][b, qh], full)
+                ref = torch.nn.functional.scaled_dot_product_attention(
+                    torch.from_numpy(q.astype(np.float64))[None, None, None],
+                    torch.from_numpy(k.astype(np.float64))[None, None],
+                    torch.from_numpy(v.astype(np.float64))[None, None])[0, 0, 0].numpy()
+                np.testing.assert_allclose(full, ref, rtol=1e-12, atol=1e-13)
+
+
+def test_kappa_zero_closed_form():
+    """tau -> inf makes every weight 2^24, so k* = ceil(p_q |U| / 65536) and the
+    selection is the lowest positions of U (I6)."""
+    wl = tiny_workload(top_p=0.9, cond_mode=COND_EVICT)
+    inp = make_inputs(wl)
+    o, _ = _run(wl, inp, tau=np.full(wl.num_kv_heads, np.inf, np.float32))
+    for b in range(wl.batch):
+        for h in range(wl.num_kv_heads):
+            c, E = int(o.pool_head[b, h]), int(o.n_condense[b, h])
+            pend = int(o.seq_len[b]) - wl.dense_window
+            nU = pend - c
+            k = -(-58982 * nU // 65536)
+            assert o.budget[b, h] == k
+            np.testing.assert_array_equal(o.selected_positions(b, h), np.arange(c, c + k))
+            idx = o.pool_row_index(np.arange(c - 64 * E, pend))
+            assert np.all(o.weights[b, h, idx] == 1 << 24)
+
+
+@pytest.mark.parametrize("p", [0.5, 0.9, 0.99])
+def test_step_selection_matches_logical_restatement(p):
+    """Scores, weights, E, U, mask and view of the step equal the pinned building
+    blocks applied to the logical positions (ring indexing, plan, survivors) (I7)."""
+    wl = tiny_workload(top_p=p, cond_mode=COND_MERGE, heavy=(0, 5))
+    inp = make_inputs(wl)
+    o, _ = _run(wl, inp)
+    G, W = wl.group, wl.dense_window
+    for b in range(wl.batch):
+        t = int(inp.ctx_len[b]) + 1
+        pend = t - W
+        N = pend
+        E = max(0, -(-(N - wl.sparse_cap) // 64))
+        assert np.all(o.n_condense[b] == E) and np.all(o.pool_head[b] == 64 * E)
+        for h in range(wl.num_kv_heads):
+            k, v = _positions_kv(inp, b, h, 1)
+            q = _f32(inp.q[0, b, h * G:(h + 1) * G])
+            s = np.array([orc.score_row(q, k[j]) for j in range(pend)], np.float32)
+            rows = o.pool_row_index(np.arange(pend))
+            assert np.array_equal(o.scores[b, h, rows].view(np.uint32), s.view(np.uint32))
+            m = s.max()
+            kap = orc.kappa(wl.head_dim, 1.0)
+            w = np.array([orc.weight(x, m, kap) for x in s], np.uint32)
+            assert np.array_equal(o.weights[b, h, rows], w)
+            assert int(o.w_all[b, h]) == int(w.sum(dtype=np.uint64))
+            u0 = 64 * E
+            kstar, sel, T = orc.topp(w[u0:], np.arange(u0, pend), p)
+            assert o.budget[b, h] == kstar and int(o.thresh[b, h]) == T
+            chosen = np.arange(u0, pend)[sel]
+            np.testing.assert_array_equal(o.selected_positions(b, h), chosen)
+            # mask: one bit per selected position, nothing else
+            mask = np.zeros(wl.P_blk, np.uint64)
+            for j in chosen:
+                mask[(j // 64) % wl.P_blk] |= np.uint64(1) << np.uint64(j % 64)
+            np.testing.assert_array_equal(o.mask[b, h], mask)
+            assert sum(bin(int(x)).count("1") for x in o.mask[b, h]) == kstar
+            # view rows are bit copies of the selected positions, in ascending order
+            vk = o.view_k[b, h, :kstar]
+            src = inp.k_ctx[b, h].contiguous().view(torch.int16).numpy().view(np.uint16)
+            np.testing.assert_array_equal(vk, src[chosen])
+            assert np.all(np.diff(chosen) > 0)
+
+
+def test_merge_identical_block_is_lossless():
+    """A block of 64 identical tokens merged into an empty slot attends exactly like
+    the 64 tokens (ln n bias), with p = 1 so nothing else is dropped (I11)."""
+    W, S = 32, 256
+    wl = tiny_workload(batch=1, num_kv_heads=2, num_q_heads=8, dense_window=W, sparse_cap=S,
+                       ctx_len=S + W, ctx_min=None, cond_mode=COND_MERGE, top_p=1.0, heavy=(0, 0))
+    inp = make_inputs(wl)
+    inp.k_ctx[:, :, :64] = inp.k_ctx[:, :, :1]
+    inp.v_ctx[:, :, :64] = inp.v_ctx[:, :, :1]
+    o, outs = _run(wl, inp)
+    assert np.all(o.n_condense == 1) and np.all(o.pool_head == 64)
+    assert np.all(o.cond_n.sum(-1) == 64) and np.all(o.cond_cursor == 1)
+    for h in range(wl.num_kv_heads):
+        k, v = _positions_kv(inp, 0, h, 1)
+        np.testing.assert_allclose(o.cond_kn[0, h, 0] / o.cond_omega[0, h, 0], k[0], rtol=1e-12)
+        for g in range(wl.group):
+            qh = h * wl.group + g
+            full = orc.full_attention(_f32(inp.q[0, 0, qh]), k, v)
+            np.testing.assert_allclose(outs[0][0, qh], full, rtol=1e-12, atol=1e-14)
+
+
+def test_condense_bookkeeping_modes():
+    """Merged slots count 64 tokens per condensed block; evict leaves the slots
+    untouched; off never condenses (I11)."""
+    base = dict(ctx_len=700, ctx_min=400, sparse_cap=128, dense_window=32, condensed_slots=3)
+    for mode in (COND_MERGE, COND_EVICT, COND_OFF):
+        wl = tiny_workload(cond_mode=mode, **base)
+        inp = make_inputs(wl)
+        o, _ = _run(wl, inp, steps=1)
+        for b in range(wl.batch):
+            N = int(inp.ctx_len[b]) + 1 - wl.dense_window
+            E = max(0, -(-(N - 128) // 64)) if mode != COND_OFF else 0
+            assert np.all(o.n_condense[b] == E)
+            assert np.all(o.pool_head[b] == 64 * E)
+            if mode == COND_MERGE:
+                assert np.all(o.cond_n[b].sum(-1) == 64 * E)
+                assert np.all(o.cond_cursor[b] == E % 3)
+                # ring wrap: slot s received ceil((E - s) / 3) blocks
+                for s in range(3):
+                    assert np.all(o.cond_n[b, :, s] == 64 * len(range(s, E, 3)))
+            else:
+                assert np.all(o.cond_n[b] == 0) and np.all(o.cond_omega[b] == 0)
+            if mode == COND_OFF:
+                assert np.all(o.budget[b] > 0)
+    assert o.error_word == 0
+
+
+def test_one_token_and_equal_keys():
+    """One token: the output is its value.  Equal keys: the mean of the values (I12)."""
+    wl = tiny_workload(batch=1, ctx_len=0, ctx_min=None, heavy=(0, 0))
+    inp = make_inputs(wl)
+    o, outs = _run(wl, inp)
+    for qh in range(wl.num_q_heads):
+        np.testing.assert_array_equal(outs[0][0, qh], _f32(inp.v_new[0, 0, qh // wl.group]).astype(np.float64))
+    wl = tiny_workload(batch=1, ctx_len=20, ctx_min=None, heavy=(0, 0))
+    inp = make_inputs(wl)
+    inp.k_ctx[:] = inp.k_ctx[:, :, :1]
+    inp.k_new[:] = inp.k_ctx[:, :, 0]
+    o, outs = _run(wl, inp)
+    for qh in range(wl.num_q_heads):
+        h = qh // wl.group
+        mean = np.concatenate([_f32(inp.v_ctx[0, h, :20]), _f32(inp.v_new[0, 0, h])[None]]).astype(np.float64).mean(0)
+        np.testing.assert_allclose(outs[0][0, qh], mean, rtol=1e-12, atol=1e-14)
+
+
+def test_error_bits():
+    # pool overflow in mode off
+    wl = tiny_workload(cond_mode=COND_OFF, ctx_len=400, ctx_min=None, pool_blocks=5, view_cap=320)
+    inp = make_inputs(wl)
+    o = orc.Oracle(wl)
+    assert o.prefill(inp.k_ctx, inp.v_ctx, inp.ctx_len) == -3  # does not fit
+    wl = tiny_workload(cond_mode=COND_OFF, ctx_len=320 + 32 - 1, ctx_min=None, pool_blocks=5, view_cap=320, steps=2)
+    inp = make_inputs(wl)
+    o = orc.Oracle(wl)
+    assert o.prefill(inp.k_ctx, inp.v_ctx, inp.ctx_len) == 0
+    o.step(inp.q[0], inp.k_new[0], inp.v_new[0])
+    assert o.error_word == 0
+    o.step(inp.q[1], inp.k_new[1], inp.v_new[1])
+    assert o.error_word & 1
+    # non-finite score
+    wl = tiny_workload()
+    inp = make_inputs(wl)
+    inp.k_ctx[0, 0, 5, 0] = float("inf")
+    o, _ = _run(wl, inp)
+    assert o.error_word & 4
+
+
+def test_streaming_invariants():
+    """Over many steps the pool head stays block aligned, the pool stays within S_cap
+    after condensation, and t advances by one per step."""
+    wl = tiny_workload(steps=70, ctx_len=330, ctx_min=300, cond_mode=COND_MERGE, condensed_slots=2)
+    inp = make_inputs(wl)
+    o = orc.Oracle(wl)
+    o.prefill(inp.k_ctx, inp.v_ctx, inp.ctx_len)
+    total_E = np.zeros((wl.batch, wl.num_kv_heads), np.int64)
+    for s in range(wl.steps):
+        o.step(inp.q[s], inp.k_new[s], inp.v_new[s], attend=(s % 10 == 0))
+        total_E += o.n_condense
+        assert np.all(o.seq_len == inp.ctx_len.numpy() + s + 1)
+        assert np.all(o.pool_head % 64 == 0)
+        N = o.seq_len[:, None] - wl.dense_window - o.pool_head
+        assert np.all(N <= wl.sparse_cap) and np.all(N >= 0)
+        assert np.all(o.budget >= 1)
+    assert np.all(o.cond_n.sum(-1) == 64 * total_E)
+    assert o.error_word == 0

@@ -1,0 +1,310 @@
+// hardkv_api.hip -- the C ABI: argument checks, launch geometry, workspace layout and the
+// stream-ordered kernel sequences of each entry point.  Nothing here allocates, frees,
+// synchronizes, or touches device memory from the host.
+#include <math.h>
+#include <string.h>
+
+#include "hardkv_internal.h"
+
+namespace hardkv {
+namespace {
+
+constexpr int MAX_POOL_BLOCKS = 6144;  // per-block counts of one head live in the select LDS
+constexpr double LOG2E = 1.4426950408889634074;
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+bool aligned16(const void *p) { return p != nullptr && ((uintptr_t)p & 15u) == 0; }
+
+struct Plan {
+  Args a;
+  size_t off_head, off_viewoff, off_part, ws_bytes;
+};
+
+// Checks the configuration and derives every size; fills the size fields of p.a.
+int32_t plan(const hardkv_config *cfg, Plan &p) {
+  if (!cfg) return HARDKV_EINVAL;
+  Args &a = p.a;
+  memset(&a, 0, sizeof(a));
+  if (cfg->batch < 1 || cfg->num_kv_heads < 1 || cfg->num_q_heads < 1) return HARDKV_EINVAL;
+  if (cfg->num_kv_heads > HARDKV_MAX_KV_HEADS) return HARDKV_EUNSUPPORTED;
+  if (cfg->num_q_heads % cfg->num_kv_heads) return HARDKV_EINVAL;
+  const int G = cfg->num_q_heads / cfg->num_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return HARDKV_EUNSUPPORTED;
+  if (cfg->head_dim != HD) return HARDKV_EUNSUPPORTED;
+  if (cfg->dtype != HARDKV_BF16 && cfg->dtype != HARDKV_F32) return HARDKV_EINVAL;
+  if (cfg->dense_window < 1) return HARDKV_EINVAL;
+  if (cfg->sparse_cap < BK || cfg->sparse_cap % BK) return HARDKV_EINVAL;
+  if (cfg->pool_blocks < 1) return HARDKV_EINVAL;
+  if (cfg->pool_blocks > MAX_POOL_BLOCKS) return HARDKV_EUNSUPPORTED;
+  if ((int64_t)cfg->pool_blocks * BK < (int64_t)cfg->sparse_cap + BK) return HARDKV_EINVAL;
+  if (cfg->cond_mode < HARDKV_COND_OFF || cfg->cond_mode > HARDKV_COND_MERGE) return HARDKV_EINVAL;
+  if (cfg->view_cap < cfg->sparse_cap) return HARDKV_EINVAL;
+  if (cfg->cond_mode == HARDKV_COND_OFF && (int64_t)cfg->view_cap < (int64_t)cfg->pool_blocks * BK)
+    return HARDKV_EINVAL;
+  if (cfg->condensed_slots < 1) return HARDKV_EINVAL;
+  if (!(cfg->top_p > 0.0 && cfg->top_p <= 1.0)) return HARDKV_EINVAL;
+  const double pq = rint(cfg->top_p * 65536.0);
+  if (pq < 1.0) return HARDKV_EINVAL;
+  if (!cfg->tau) return HARDKV_EINVAL;
+  for (int h = 0; h < cfg->num_kv_heads; ++h)
+    if (!(cfg->tau[h] > 0.0f)) return HARDKV_EINVAL;
+
+  a.B = cfg->batch;
+  a.Hq = cfg->num_q_heads;
+  a.Hkv = cfg->num_kv_heads;
+  a.G = G;
+  a.W = cfg->dense_window;
+  a.P = cfg->pool_blocks;
+  a.S_cap = cfg->sparse_cap;
+  a.V_cap = cfg->view_cap;
+  a.C = cfg->condensed_slots;
+  a.mode = cfg->cond_mode;
+  a.merge_bias = cfg->merge_bias ? 1 : 0;
+  a.pq = (uint32_t)pq;
+  {
+    // Taylor coefficients (ln 2)^i / i! of 2^f, rounded once to fp32
+    const long double ln2 = 0.693147180559945309417232121458176568L;
+    long double term = 1.0L;
+    for (int i = 0; i < NCOEFF; ++i) {
+      if (i > 0) term = term * ln2 / (long double)i;
+      a.coeff[i] = (float)term;
+    }
+  }
+  for (int h = 0; h < a.Hkv; ++h)
+    a.kappa[h] = (float)(LOG2E / (sqrt((double)HD) * (double)cfg->tau[h]));
+  a.att_scale = (float)(LOG2E / sqrt((double)HD));
+
+  const int64_t BH = (int64_t)a.B * a.Hkv;
+  const int64_t work = (int64_t)a.P * BH;
+  const int cb = (int)std::max<int64_t>(1, std::min<int64_t>(8, work / 1024));
+  a.cb_score = cb;
+  a.nch_score = (a.P + cb - 1) / cb;
+  a.cb_reg = cb;
+  a.nch_reg = (a.P + cb - 1) / cb;
+  a.rv_att = 256;
+  a.nv_att = (a.V_cap + a.rv_att - 1) / a.rv_att;
+  a.rc_att = 64;
+  a.nc_att = (a.C + a.rc_att - 1) / a.rc_att;
+  a.rd_att = 128;
+  a.nd_att = (a.W + a.rd_att - 1) / a.rd_att;
+  a.part_cd_base = std::max(a.nch_reg, a.nv_att);
+  a.npart = a.part_cd_base + a.nc_att + a.nd_att;
+  if (a.mode == HARDKV_COND_MERGE) {
+    const int emax = std::max(1, a.P - a.S_cap / BK);
+    a.ncs = std::min(a.C, emax);
+  } else {
+    a.ncs = 1;
+  }
+
+  p.off_head = 0;
+  p.off_viewoff = align256(p.off_head + (size_t)BH * sizeof(HeadInfo));
+  p.off_part = align256(p.off_viewoff + (size_t)BH * a.P * sizeof(uint32_t));
+  p.ws_bytes = align256(p.off_part + (size_t)BH * a.npart * G * (2 + HD) * sizeof(float));
+  return HARDKV_OK;
+}
+
+// Checks the state's pointers and points the kernel arguments at it.
+int32_t bind(const hardkv_state *st, Plan &p) {
+  if (!st) return HARDKV_EINVAL;
+  const void *ptrs[] = {st->dense_k, st->dense_v, st->pool_k, st->pool_v, st->view_k, st->view_v,
+                        st->view_pos, st->cond_kn, st->cond_vn, st->cond_omega, st->cond_n,
+                        st->cond_cursor, st->seq_len, st->pool_head, st->scores, st->weights,
+                        st->mask, st->budget, st->n_condense, st->w_all, st->w_u, st->thresh,
+                        st->workspace};
+  for (const void *q : ptrs)
+    if (!aligned16(q)) return HARDKV_EINVAL;
+  if (!st->error_word || ((uintptr_t)st->error_word & 3u)) return HARDKV_EINVAL;
+  if (st->workspace_bytes < p.ws_bytes) return HARDKV_ECAPACITY;
+  Args &a = p.a;
+  a.dense_k = st->dense_k;
+  a.dense_v = st->dense_v;
+  a.pool_k = st->pool_k;
+  a.pool_v = st->pool_v;
+  a.view_k = st->view_k;
+  a.view_v = st->view_v;
+  a.view_pos = st->view_pos;
+  a.cond_kn = st->cond_kn;
+  a.cond_vn = st->cond_vn;
+  a.cond_omega = st->cond_omega;
+  a.cond_n = st->cond_n;
+  a.cond_cursor = st->cond_cursor;
+  a.seq_len = st->seq_len;
+  a.pool_head = st->pool_head;
+  a.scores = st->scores;
+  a.weights = st->weights;
+  a.mask = st->mask;
+  a.budget = st->budget;
+  a.n_condense = st->n_condense;
+  a.w_all = st->w_all;
+  a.w_u = st->w_u;
+  a.thresh = st->thresh;
+  a.error_word = st->error_word;
+  char *ws = (char *)st->workspace;
+  a.head = reinterpret_cast<HeadInfo *>(ws + p.off_head);
+  a.viewoff = reinterpret_cast<uint32_t *>(ws + p.off_viewoff);
+  a.part = reinterpret_cast<float *>(ws + p.off_part);
+  return HARDKV_OK;
+}
+
+int32_t setup(const hardkv_config *cfg, const hardkv_state *st, Plan &p) {
+  int32_t rc = plan(cfg, p);
+  if (rc != HARDKV_OK) return rc;
+  return bind(st, p);
+}
+
+int32_t hip_status(hipError_t e) { return e == hipSuccess ? HARDKV_OK : HARDKV_EHIP; }
+
+bool is_bf16(const hardkv_config *cfg) { return cfg->dtype == HARDKV_BF16; }
+
+const char *const kStageNames[] = {"append", "score_select", "rewrite_attend_view", "condense",
+                                   "attend_condensed_dense", "combine"};
+
+// kernel `stage` of the fused step
+hipError_t step_stage(const hardkv_config *cfg, Args &a, int stage, hipStream_t s) {
+  const bool bf = is_bf16(cfg);
+  a.nvp = a.nch_reg;
+  switch (stage) {
+    case 0: return launch_append(a, s, bf);
+    case 1: return launch_score_select(a, s, bf);
+    case 2: return launch_regularize(a, s, bf, true);
+    case 3: return launch_condense(a, s, bf);
+    case 4: return launch_attend(a, s, bf, false);
+    case 5: return launch_combine(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+}  // namespace hardkv
+
+using namespace hardkv;
+
+extern "C" {
+
+int32_t hardkv_workspace_size(const hardkv_config *cfg, size_t *bytes) {
+  if (!bytes) return HARDKV_EINVAL;
+  Plan p;
+  int32_t rc = plan(cfg, p);
+  if (rc != HARDKV_OK) return rc;
+  *bytes = p.ws_bytes;
+  return HARDKV_OK;
+}
+
+int32_t hardkv_prefill(const hardkv_config *cfg, hardkv_state *st, const void *k_ctx,
+                       const void *v_ctx, const int64_t *ctx_len_dev, int64_t max_len, void *stream) {
+  Plan p;
+  int32_t rc = setup(cfg, st, p);
+  if (rc != HARDKV_OK) return rc;
+  if (max_len < 0 || !ctx_len_dev || ((uintptr_t)ctx_len_dev & 7u)) return HARDKV_EINVAL;
+  if (max_len > 0 && (!aligned16(k_ctx) || !aligned16(v_ctx))) return HARDKV_EINVAL;
+  if (max_len - cfg->dense_window + 1 > (int64_t)cfg->pool_blocks * BK) return HARDKV_ECAPACITY;
+  p.a.k_ctx = k_ctx;
+  p.a.v_ctx = v_ctx;
+  p.a.ctx_len = ctx_len_dev;
+  p.a.max_len = max_len;
+  return hip_status(launch_prefill(p.a, (hipStream_t)stream, is_bf16(cfg)));
+}
+
+int32_t hardkv_append(const hardkv_config *cfg, hardkv_state *st, const void *k_new,
+                      const void *v_new, void *stream) {
+  Plan p;
+  int32_t rc = setup(cfg, st, p);
+  if (rc != HARDKV_OK) return rc;
+  if (!aligned16(k_new) || !aligned16(v_new)) return HARDKV_EINVAL;
+  p.a.k_new = k_new;
+  p.a.v_new = v_new;
+  return hip_status(launch_append(p.a, (hipStream_t)stream, is_bf16(cfg)));
+}
+
+int32_t hardkv_select(const hardkv_config *cfg, hardkv_state *st, const void *q, void *stream) {
+  Plan p;
+  int32_t rc = setup(cfg, st, p);
+  if (rc != HARDKV_OK) return rc;
+  if (!aligned16(q)) return HARDKV_EINVAL;
+  p.a.q = q;
+  return hip_status(launch_score_select(p.a, (hipStream_t)stream, is_bf16(cfg)));
+}
+
+int32_t hardkv_regularize(const hardkv_config *cfg, hardkv_state *st, void *stream) {
+  Plan p;
+  int32_t rc = setup(cfg, st, p);
+  if (rc != HARDKV_OK) return rc;
+  return hip_status(launch_regularize(p.a, (hipStream_t)stream, is_bf16(cfg), false));
+}
+
+int32_t hardkv_condense(const hardkv_config *cfg, hardkv_state *st, void *stream) {
+  Plan p;
+  int32_t rc = setup(cfg, st, p);
+  if (rc != HARDKV_OK) return rc;
+  return hip_status(launch_condense(p.a, (hipStream_t)stream, is_bf16(cfg)));
+}
+
+int32_t hardkv_attend(const hardkv_config *cfg, hardkv_state *st, const void *q, float *out,
+                      void *stream) {
+  Plan p;
+  int32_t rc = setup(cfg, st, p);
+  if (rc != HARDKV_OK) return rc;
+  if (!aligned16(q) || !aligned16(out)) return HARDKV_EINVAL;
+  p.a.q = q;
+  p.a.out = out;
+  p.a.nvp = p.a.nv_att;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = launch_attend(p.a, s, is_bf16(cfg), true);
+  if (e == hipSuccess) e = launch_combine(p.a, s);
+  return hip_status(e);
+}
+
+int32_t hardkv_step(const hardkv_config *cfg, hardkv_state *st, const void *q, const void *k_new,
+                    const void *v_new, float *out, void *stream) {
+  Plan p;
+  int32_t rc = setup(cfg, st, p);
+  if (rc != HARDKV_OK) return rc;
+  if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(out)) return HARDKV_EINVAL;
+  p.a.q = q;
+  p.a.k_new = k_new;
+  p.a.v_new = v_new;
+  p.a.out = out;
+  hipStream_t s = (hipStream_t)stream;
+  for (int stage = 0; stage < 6; ++stage) {
+    hipError_t e = step_stage(cfg, p.a, stage, s);
+    if (e != hipSuccess) return HARDKV_EHIP;
+  }
+  return HARDKV_OK;
+}
+
+int32_t hardkv_step_stage(const hardkv_config *cfg, hardkv_state *st, const void *q,
+                          const void *k_new, const void *v_new, float *out, int32_t stage,
+                          void *stream) {
+  Plan p;
+  int32_t rc = setup(cfg, st, p);
+  if (rc != HARDKV_OK) return rc;
+  if (stage < 0 || stage >= 6) return HARDKV_EINVAL;
+  if (stage == 0 && (!aligned16(k_new) || !aligned16(v_new))) return HARDKV_EINVAL;
+  if ((stage == 1 || stage == 2 || stage == 4) && !aligned16(q)) return HARDKV_EINVAL;
+  if (stage == 5 && !aligned16(out)) return HARDKV_EINVAL;
+  p.a.q = q;
+  p.a.k_new = k_new;
+  p.a.v_new = v_new;
+  p.a.out = out;
+  return hip_status(step_stage(cfg, p.a, stage, (hipStream_t)stream));
+}
+
+int32_t hardkv_step_num_stages(void) { return 6; }
+
+const char *hardkv_step_stage_name(int32_t stage) {
+  return (stage >= 0 && stage < 6) ? kStageNames[stage] : "unknown";
+}
+
+const char *hardkv_strerror(int32_t code) {
+  switch (code) {
+    case HARDKV_OK: return "ok";
+    case HARDKV_EINVAL: return "invalid argument";
+    case HARDKV_EUNSUPPORTED: return "unsupported configuration";
+    case HARDKV_ECAPACITY: return "capacity too small";
+    case HARDKV_EHIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

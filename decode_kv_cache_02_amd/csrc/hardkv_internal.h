@@ -1,0 +1,173 @@
+// hardkv_internal.h -- shared definitions of the HIP kernels and the host entry points.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "hardkv.h"
+
+namespace hardkv {
+
+constexpr int BK = 64;        // tokens per block: one wavefront, one mask word
+constexpr int HD = 128;       // head dim
+constexpr int NCOEFF = 10;    // Taylor coefficients of 2^f on [0, 1)
+constexpr int NTHREADS = 256; // threads per workgroup of every kernel
+constexpr int NB1 = 3073;     // level-1 buckets of the mass radix select (key >> 16)
+
+// Per-head scratch in the workspace.  Counters are left at zero by the kernels.
+struct alignas(64) HeadInfo {
+  uint32_t max_enc;    // running max score of the current select (ordered encoding, 0 = none)
+  uint32_t score_cnt;  // workgroups of the score kernel that finished this head
+  uint32_t cond_cnt;   // workgroups of the condense kernel that finished this head
+  uint32_t w_th;       // threshold weight of the top-p cut
+  uint32_t r;          // tokens of weight w_th that are kept (lowest positions first)
+  int32_t kstar;
+  int32_t E;
+  int32_t pad0;
+  uint64_t w_all;
+  uint64_t pad1[3];
+};
+
+// Everything a kernel needs, passed by value.
+struct Args {
+  // inputs and outputs of the call
+  const void *q, *k_new, *v_new;
+  float *out;
+  // state
+  void *dense_k, *dense_v, *pool_k, *pool_v, *view_k, *view_v;
+  int32_t *view_pos;
+  float *cond_kn, *cond_vn, *cond_omega;
+  int32_t *cond_n, *cond_cursor;
+  int64_t *seq_len, *pool_head;
+  float *scores;
+  uint32_t *weights;
+  uint64_t *mask;
+  int32_t *budget, *n_condense;
+  uint64_t *w_all, *w_u, *thresh;
+  uint32_t *error_word;
+  // workspace
+  HeadInfo *head;
+  uint32_t *viewoff;  // [BH][P] first view row of each pool block (by ring block)
+  float *part;        // [BH][npart][G][2 + HD] attention partials (m, l, acc)
+  // prefill
+  const void *k_ctx, *v_ctx;
+  const int64_t *ctx_len;
+  int64_t max_len;
+  // sizes
+  int B, Hq, Hkv, G, W, P, S_cap, V_cap, C, mode, merge_bias;
+  int cb_score, nch_score;  // score: blocks per workgroup, workgroups per head
+  int cb_reg, nch_reg;      // rewrite: blocks per workgroup, workgroups per head
+  int rv_att, nv_att;       // attention over the view (standalone): rows per workgroup, count
+  int rc_att, nc_att;       // attention over condensed slots
+  int rd_att, nd_att;       // attention over the dense window
+  int nvp;                  // view partial slots written by this call
+  int npart, part_cd_base;  // partial slots per head; first condensed/dense slot
+  int ncs;                  // condense workgroups per head
+  uint32_t pq;
+  float coeff[NCOEFF];
+  float kappa[HARDKV_MAX_KV_HEADS];
+  float att_scale;          // log2(e) / sqrt(D): logits in base 2
+};
+
+// launchers (one per kernel); each returns a hipError_t
+hipError_t launch_prefill(const Args &a, hipStream_t s, bool bf16);
+hipError_t launch_append(const Args &a, hipStream_t s, bool bf16);
+hipError_t launch_score_select(const Args &a, hipStream_t s, bool bf16);
+hipError_t launch_regularize(const Args &a, hipStream_t s, bool bf16, bool attend);
+hipError_t launch_condense(const Args &a, hipStream_t s, bool bf16);
+hipError_t launch_attend(const Args &a, hipStream_t s, bool bf16, bool with_view);
+hipError_t launch_combine(const Args &a, hipStream_t s);
+
+// ---------------------------------------------------------------------------------------
+// device helpers
+// ---------------------------------------------------------------------------------------
+#define HK_DEV __device__ __forceinline__
+
+HK_DEV float bf_lo(uint32_t x) { return __uint_as_float(x << 16); }
+HK_DEV float bf_hi(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }
+
+// 8 consecutive elements of a row as floats; T is the storage type tag.
+struct BF16 {};
+struct F32 {};
+
+HK_DEV void load8(const void *p, float (&f)[8], BF16) {
+  uint4 u = *reinterpret_cast<const uint4 *>(p);
+  f[0] = bf_lo(u.x); f[1] = bf_hi(u.x); f[2] = bf_lo(u.y); f[3] = bf_hi(u.y);
+  f[4] = bf_lo(u.z); f[5] = bf_hi(u.z); f[6] = bf_lo(u.w); f[7] = bf_hi(u.w);
+}
+HK_DEV void load8(const void *p, float (&f)[8], F32) {
+  float4 a = reinterpret_cast<const float4 *>(p)[0];
+  float4 b = reinterpret_cast<const float4 *>(p)[1];
+  f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w; f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+}
+
+template <typename T> struct Elem;
+template <> struct Elem<BF16> { static constexpr int bytes = 2; };
+template <> struct Elem<F32> { static constexpr int bytes = 4; };
+
+// raw copy of the 8 elements a lane owns in a row
+template <typename T> struct Raw8;
+template <> struct Raw8<BF16> { uint4 v; };
+template <> struct Raw8<F32> { float4 a, b; };
+
+HK_DEV void raw_load(const void *p, Raw8<BF16> &r) { r.v = *reinterpret_cast<const uint4 *>(p); }
+HK_DEV void raw_load(const void *p, Raw8<F32> &r) {
+  r.a = reinterpret_cast<const float4 *>(p)[0];
+  r.b = reinterpret_cast<const float4 *>(p)[1];
+}
+HK_DEV void raw_store(void *p, const Raw8<BF16> &r) { *reinterpret_cast<uint4 *>(p) = r.v; }
+HK_DEV void raw_store(void *p, const Raw8<F32> &r) {
+  reinterpret_cast<float4 *>(p)[0] = r.a;
+  reinterpret_cast<float4 *>(p)[1] = r.b;
+}
+HK_DEV void raw_to_f(const Raw8<BF16> &r, float (&f)[8]) {
+  f[0] = bf_lo(r.v.x); f[1] = bf_hi(r.v.x); f[2] = bf_lo(r.v.y); f[3] = bf_hi(r.v.y);
+  f[4] = bf_lo(r.v.z); f[5] = bf_hi(r.v.z); f[6] = bf_lo(r.v.w); f[7] = bf_hi(r.v.w);
+}
+HK_DEV void raw_to_f(const Raw8<F32> &r, float (&f)[8]) {
+  f[0] = r.a.x; f[1] = r.a.y; f[2] = r.a.z; f[3] = r.a.w;
+  f[4] = r.b.x; f[5] = r.b.y; f[6] = r.b.z; f[7] = r.b.w;
+}
+
+// DPP lane exchanges inside a row of 16 lanes
+template <int CTRL> HK_DEV float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+constexpr int DPP_XOR1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int DPP_XOR2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int DPP_HALF_MIRROR = 0x141;
+constexpr int DPP_MIRROR = 0x140;
+
+// ordered encoding of finite floats into uint32 (> 0), for atomicMax
+HK_DEV uint32_t f2ord(float x) {
+  uint32_t u = __float_as_uint(x);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+HK_DEV float ord2f(uint32_t e) { return __uint_as_float((e & 0x80000000u) ? (e & 0x7fffffffu) : ~e); }
+
+HK_DEV uint32_t lane_id() { return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)); }
+HK_DEV uint32_t popc_below(uint64_t m) {  // set bits of m below this lane
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+HK_DEV uint64_t ballot(bool p) { return __ballot(p); }
+
+HK_DEV int64_t pool_end(int64_t t, int W) { return t > W ? t - W : 0; }
+HK_DEV int64_t plan_E(int64_t N, int mode, int S_cap) {
+  return (mode != HARDKV_COND_OFF && N > S_cap) ? (N - S_cap + BK - 1) / BK : 0;
+}
+
+// agent-scope atomics and fences (cross-XCD visibility)
+HK_DEV uint32_t atomic_add_acq_rel(uint32_t *p, uint32_t v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+}
+HK_DEV uint32_t atomic_load_acq(uint32_t *p) {
+  return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+}
+HK_DEV void fence_agent() { __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "agent"); }
+HK_DEV void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+}  // namespace hardkv

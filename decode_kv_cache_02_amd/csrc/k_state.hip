@@ -1,0 +1,129 @@
+// k_state.hip -- placing a context into the cascade cache, and stage 1 of the decode
+// step: linear append to the dense tier.
+//
+// HARD-KV explainer, technical summary 2.A: the dense tier buffers the most recent
+// tokens in contiguous memory; tokens that age out of the dense window move to the
+// sparse tier.  The dense tier is a ring of W slots (position p in slot p mod W), the
+// sparse tier a ring of P blocks of 64 rows (position p in block (p / 64) mod P).
+#include "hardkv_internal.h"
+
+namespace hardkv {
+
+namespace {
+
+// grid (ceil(max_len / 64) + 1, B*Hkv): blocks of 64 context positions, then one
+// workgroup per head that resets the head's counters and condensed tier.
+template <typename T>
+__global__ __launch_bounds__(NTHREADS) void hardkv_prefill(Args a) {
+  constexpr int EB = Elem<T>::bytes;
+  constexpr int CPR = HD * EB / 16;  // 16-byte pieces per row
+  const int bh = blockIdx.y, x = blockIdx.x;
+  const int b = bh / a.Hkv, h = bh - b * a.Hkv;
+  const int tid = threadIdx.x;
+  const int64_t L = a.ctx_len[b];
+  const int W = a.W, P = a.P;
+  const size_t ROWB = (size_t)HD * EB;
+
+  if (x == (int)gridDim.x - 1) {
+    if (tid == 0) {
+      a.pool_head[bh] = 0;
+      a.cond_cursor[bh] = 0;
+      if (h == 0) a.seq_len[b] = L;
+      HeadInfo z = {};
+      a.head[bh] = z;
+    }
+    for (int k = tid; k < a.C * HD; k += NTHREADS) {
+      a.cond_kn[(size_t)bh * a.C * HD + k] = 0.0f;
+      a.cond_vn[(size_t)bh * a.C * HD + k] = 0.0f;
+    }
+    for (int k = tid; k < a.C; k += NTHREADS) {
+      a.cond_omega[(size_t)bh * a.C + k] = 0.0f;
+      a.cond_n[(size_t)bh * a.C + k] = 0;
+    }
+    // dense slots that hold no position yet (L < W)
+    for (int64_t k = tid; k < (int64_t)W * CPR; k += NTHREADS) {
+      const int64_t slot = k / CPR, piece = k % CPR;
+      if (slot >= L) {
+        const size_t off = ((size_t)bh * W + slot) * ROWB + piece * 16;
+        *reinterpret_cast<uint4 *>((char *)a.dense_k + off) = uint4{0, 0, 0, 0};
+        *reinterpret_cast<uint4 *>((char *)a.dense_v + off) = uint4{0, 0, 0, 0};
+      }
+    }
+    return;
+  }
+  const int64_t dense_lo = L > W ? L - W : 0;
+  for (int k = tid; k < BK * CPR; k += NTHREADS) {
+    const int64_t p = (int64_t)x * BK + k / CPR;
+    const int piece = k % CPR;
+    if (p >= L) continue;
+    const size_t src = ((size_t)bh * a.max_len + p) * ROWB + piece * 16;
+    size_t dst;
+    void *dk, *dv;
+    if (p >= dense_lo) {
+      dst = ((size_t)bh * W + (size_t)(p % W)) * ROWB + piece * 16;
+      dk = a.dense_k;
+      dv = a.dense_v;
+    } else {
+      dst = (((size_t)bh * P + (size_t)((p / BK) % P)) * BK + (size_t)(p % BK)) * ROWB + piece * 16;
+      dk = a.pool_k;
+      dv = a.pool_v;
+    }
+    *reinterpret_cast<uint4 *>((char *)dk + dst) = *reinterpret_cast<const uint4 *>((const char *)a.k_ctx + src);
+    *reinterpret_cast<uint4 *>((char *)dv + dst) = *reinterpret_cast<const uint4 *>((const char *)a.v_ctx + src);
+  }
+}
+
+// grid B: one workgroup per sequence moves, for each KV head, position t - W from the
+// dense ring to the pool tail, writes the new token into its dense slot (the same slot),
+// and then advances t.
+template <typename T>
+__global__ __launch_bounds__(NTHREADS) void hardkv_append(Args a) {
+  constexpr int EB = Elem<T>::bytes;
+  constexpr int CPR = HD * EB / 16;
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const int W = a.W, P = a.P, H = a.Hkv;
+  const size_t ROWB = (size_t)HD * EB;
+  const int64_t t = a.seq_len[b];
+  const int64_t p = t - W;  // leaves the window when t >= W
+  for (int k = tid; k < H * 2 * CPR; k += NTHREADS) {
+    const int h = k / (2 * CPR), rem = k % (2 * CPR);
+    const int which = rem / CPR, piece = rem % CPR;
+    const size_t bh = (size_t)b * H + h;
+    char *dense = (char *)(which ? a.dense_v : a.dense_k) + (bh * W + (size_t)(t % W)) * ROWB + piece * 16;
+    if (t >= W) {
+      char *pool = (char *)(which ? a.pool_v : a.pool_k) +
+                   ((bh * P + (size_t)((p / BK) % P)) * BK + (size_t)(p % BK)) * ROWB + piece * 16;
+      *reinterpret_cast<uint4 *>(pool) = *reinterpret_cast<const uint4 *>(dense);
+    }
+    const char *src = (const char *)(which ? a.v_new : a.k_new) + bh * ROWB + piece * 16;
+    *reinterpret_cast<uint4 *>(dense) = *reinterpret_cast<const uint4 *>(src);
+  }
+  if (tid < H && t >= W) {
+    const int64_t c = a.pool_head[(size_t)b * H + tid];
+    if (p + 1 - c > (int64_t)P * BK) atomicOr(a.error_word, HARDKV_ERR_POOL_OVERFLOW);
+  }
+  __syncthreads();
+  if (tid == 0) a.seq_len[b] = t + 1;
+}
+
+}  // namespace
+
+hipError_t launch_prefill(const Args &a, hipStream_t s, bool bf16) {
+  dim3 grid((unsigned)((a.max_len + BK - 1) / BK) + 1, a.B * a.Hkv);
+  if (bf16)
+    hipLaunchKernelGGL((hardkv_prefill<BF16>), grid, dim3(NTHREADS), 0, s, a);
+  else
+    hipLaunchKernelGGL((hardkv_prefill<F32>), grid, dim3(NTHREADS), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_append(const Args &a, hipStream_t s, bool bf16) {
+  dim3 grid(a.B);
+  if (bf16)
+    hipLaunchKernelGGL((hardkv_append<BF16>), grid, dim3(NTHREADS), 0, s, a);
+  else
+    hipLaunchKernelGGL((hardkv_append<F32>), grid, dim3(NTHREADS), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace hardkv

@@ -1,0 +1,185 @@
+/* hardkv.h -- C ABI of the HARD-KV decode-time cascade-cache step on one AMD
+ * Instinct MI355X (gfx950).
+ *
+ * HARD-KV ("HARD-KV: Head-Adaptive Regularization for Decoding-time KV
+ * Compression", technical summary section 2) keeps each KV head's cache in
+ * three tiers: a dense window of the most recent tokens, a sparse tier from
+ * which a calibrated top-p selection keeps a head-adaptive set of tokens, and a
+ * constant-size condensed tier into which the oldest blocks are evicted or
+ * merged.  One decode step runs four stages (section 2.A): linear append to the
+ * dense tier; logits calibration and top-p to build sparse masks; index
+ * regularization that rewrites the selected tokens into contiguous blocks; and
+ * eviction or weighted merging of the oldest blocks.  Decode attention then
+ * reads the three tiers.
+ *
+ * Per (sequence b, KV head h) a step computes, with G = Hq / Hkv and query
+ * heads h*G .. h*G+G-1 sharing KV head h:
+ *   1. append: the new (k, v) goes to dense slot t mod W; position t - W, which
+ *      leaves the window, is copied to the tail of the pool; t grows by one.
+ *   2. plan: the pool holds positions [c, t - W); N = t - W - c.  When the mode is
+ *      not OFF and N > S_cap, the E = ceil((N - S_cap) / 64) oldest blocks will be
+ *      condensed; the survivors are U = [c + 64E, t - W).
+ *   3. score: s_j = max over the group's queries of q . k_j, each dot product a
+ *      pairwise tree of fp32 products with one rounding per operation (2.B,
+ *      "max-pooled logits").
+ *   4. calibrate: m = max s over the pool; w_j = max(1, floor(2^24 * 2^t_j)),
+ *      t_j = (s_j - m) * kappa_h, kappa_h = log2(e) / (sqrt(D) tau_h) (2.B,
+ *      temperature calibration into one softmax).
+ *   5. top-p: T = ceil(p_q W_U / 2^16) with p_q = round(p * 2^16) and W_U the mass
+ *      of U; the survivors in order of decreasing w (lower position first on
+ *      ties) are kept until their mass reaches T.  k* tokens are kept (the
+ *      head-adaptive budget of tier 2).
+ *   6. regularize: the kept positions, in ascending order, are copied bit for bit
+ *      into rows 0 .. k*-1 of the head's view (2.C, Rewrite Cache with a
+ *      max-length flat index: every head owns V_cap view rows).
+ *   7. condense: each of the E oldest blocks is dropped (EVICT) or merged into the
+ *      next condensed slot (MERGE, a ring of C slots): Kn += sum w_j/W_all k_j,
+ *      Vn += sum w_j/W_all v_j, Omega += sum w_j/W_all, n += 64.  c += 64 E.
+ *   8. attend: softmax attention of each query over the condensed slots with
+ *      n > 0 (key Kn/Omega, value Vn/Omega, logit bias ln n), the view rows
+ *      r < k*, and the dense window.  Output in fp32.
+ * Steps 2-7 give bit-identical integer results (masks, budgets, indices, view
+ * rows) to a plain CPU definition of the same step.
+ *
+ * Conventions
+ *   - head_dim is 128; the block size is 64 tokens (one mask word).
+ *   - Every device buffer is owned by the caller (for example allocated as
+ *     tensors) on the current HIP device.  The library never allocates, frees,
+ *     synchronizes, or reads device memory from the host.  Calls are
+ *     asynchronous on `stream` (a hipStream_t; NULL is the default stream) and
+ *     may be captured into a HIP graph.
+ *   - Host-detectable errors (bad sizes, null or misaligned pointers, too small a
+ *     workspace) return a negative status before anything is enqueued.
+ *   - Runtime conditions set bits of *error_word on the device (the caller reads
+ *     it after a synchronization of its choosing): HARDKV_ERR_POOL_OVERFLOW (the
+ *     pool ring overflowed; only possible in mode OFF), HARDKV_ERR_VIEW_OVERFLOW,
+ *     HARDKV_ERR_NONFINITE (a non-finite score; outputs are then undefined).
+ *   - The workspace must be zero-filled once before first use; the kernels leave
+ *     its counters at zero after each call.
+ *   - Calls on one state must not overlap (they share the workspace).
+ */
+#ifndef HARDKV_H
+#define HARDKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  HARDKV_OK = 0,
+  HARDKV_EINVAL = -1,      /* bad argument: null/misaligned pointer, inconsistent sizes */
+  HARDKV_EUNSUPPORTED = -2,/* valid but not supported: head_dim != 128, G not in {1,2,4,8} */
+  HARDKV_ECAPACITY = -3,   /* a capacity is too small for the requested contents */
+  HARDKV_EHIP = -4         /* a HIP launch failed */
+} hardkv_status;
+
+typedef enum { HARDKV_BF16 = 0, HARDKV_F32 = 1 } hardkv_dtype;
+typedef enum { HARDKV_COND_OFF = 0, HARDKV_COND_EVICT = 1, HARDKV_COND_MERGE = 2 } hardkv_cond_mode;
+
+#define HARDKV_BLOCK 64
+#define HARDKV_HEAD_DIM 128
+#define HARDKV_MAX_KV_HEADS 64
+#define HARDKV_ERR_POOL_OVERFLOW 1u
+#define HARDKV_ERR_VIEW_OVERFLOW 2u
+#define HARDKV_ERR_NONFINITE 4u
+
+/* Host-side description of one layer; passed by pointer to every call. */
+typedef struct {
+  int32_t batch;           /* B >= 1 */
+  int32_t num_q_heads;     /* Hq */
+  int32_t num_kv_heads;    /* Hkv, 1..64; G = Hq / Hkv in {1, 2, 4, 8} */
+  int32_t head_dim;        /* D, must be 128 */
+  int32_t dtype;           /* storage and compute type of q, K, V: HARDKV_BF16 or HARDKV_F32 */
+  int32_t dense_window;    /* W >= 1 */
+  int32_t pool_blocks;     /* P: pool ring blocks of 64 rows per (b, h); P*64 >= sparse_cap + 64 */
+  int32_t sparse_cap;      /* S_cap: multiple of 64, >= 64 */
+  int32_t view_cap;        /* V_cap >= sparse_cap (>= P*64 in mode OFF) */
+  int32_t condensed_slots; /* C >= 1 */
+  int32_t cond_mode;       /* hardkv_cond_mode */
+  int32_t merge_bias;      /* 1: merged slots get logit bias ln n (default); 0: no bias */
+  double top_p;            /* p in (0, 1]; p_q = round(p * 65536) must be >= 1 */
+  const float *tau;        /* host array [num_kv_heads], calibration temperatures > 0 (+inf allowed) */
+} hardkv_config;
+
+/* Device buffers of one layer.  All fixed capacity; 16-byte aligned.
+ * Element types: "e" is bf16 (2 bytes) or fp32 (4 bytes) per cfg->dtype. */
+typedef struct {
+  void *dense_k, *dense_v;   /* e [B][Hkv][W][128]: position p in slot p mod W                    */
+  void *pool_k, *pool_v;     /* e [B][Hkv][P][64][128]: position p in block (p/64) mod P, row p%64 */
+  void *view_k, *view_v;     /* e [B][Hkv][V_cap][128]: row r = r-th kept position (ascending)    */
+  int32_t *view_pos;         /* [B][Hkv][V_cap]: position of view row r (rows >= k* unspecified)  */
+  float *cond_kn, *cond_vn;  /* fp32 [B][Hkv][C][128]: merged numerators                          */
+  float *cond_omega;         /* fp32 [B][Hkv][C]: merged weight                                   */
+  int32_t *cond_n;           /* [B][Hkv][C]: tokens merged into the slot                          */
+  int32_t *cond_cursor;      /* [B][Hkv]: next slot of the ring                                   */
+  int64_t *seq_len;          /* [B]: t                                                            */
+  int64_t *pool_head;        /* [B][Hkv]: c, a multiple of 64                                     */
+  float *scores;             /* fp32 [B][Hkv][P*64]: s by pool ring row (rows outside the pool unspecified) */
+  uint32_t *weights;         /* [B][Hkv][P*64]: w by pool ring row                                */
+  uint64_t *mask;            /* [B][Hkv][P]: word (p/64) mod P, bit p%64 set iff p is kept        */
+  int32_t *budget;           /* [B][Hkv]: k*                                                      */
+  int32_t *n_condense;       /* [B][Hkv]: E of the last select                                    */
+  uint64_t *w_all;           /* [B][Hkv]: total pool mass                                         */
+  uint64_t *w_u;             /* [B][Hkv]: survivor mass W_U                                       */
+  uint64_t *thresh;          /* [B][Hkv]: T                                                       */
+  uint32_t *error_word;      /* [1]: HARDKV_ERR_* bits, or-ed                                     */
+  void *workspace;           /* hardkv_workspace_size() bytes, zero-filled before first use      */
+  size_t workspace_bytes;
+} hardkv_state;
+
+/* Bytes of workspace a state needs.  Returns HARDKV_EINVAL/EUNSUPPORTED on a bad config. */
+int32_t hardkv_workspace_size(const hardkv_config *cfg, size_t *bytes);
+
+/* Places a context: k_ctx/v_ctx are e [B][Hkv][max_len][128] (device), ctx_len_dev is
+ * int64 [B] (device) with 0 <= L_b <= max_len.  The last min(L_b, W) positions go to the
+ * dense ring, [0, L_b - W) to the pool; t = L_b, c = 0, condensed tier emptied, cursor 0.
+ * HARDKV_ECAPACITY if max_len - W + 1 > P*64 (the first append would not fit). */
+int32_t hardkv_prefill(const hardkv_config *cfg, hardkv_state *st, const void *k_ctx,
+                       const void *v_ctx, const int64_t *ctx_len_dev, int64_t max_len, void *stream);
+
+/* Stage 1 (section 2.A): k_new, v_new are e [B][Hkv][128] (device). */
+int32_t hardkv_append(const hardkv_config *cfg, hardkv_state *st, const void *k_new,
+                      const void *v_new, void *stream);
+
+/* Stage 2 (sections 2.A, 2.B): score, calibrate and top-p for every (b, h); writes scores,
+ * weights, mask, budget, n_condense, w_all, w_u, thresh.  q is e [B][Hq][128] (device). */
+int32_t hardkv_select(const hardkv_config *cfg, hardkv_state *st, const void *q, void *stream);
+
+/* Stage 3 (section 2.C): copies the kept rows into the view and writes view_pos. */
+int32_t hardkv_regularize(const hardkv_config *cfg, hardkv_state *st, void *stream);
+
+/* Stage 4 (section 2.A, tier 3): evicts or merges the E oldest blocks; advances c and
+ * the slot cursor. */
+int32_t hardkv_condense(const hardkv_config *cfg, hardkv_state *st, void *stream);
+
+/* Attention over the condensed, view and dense tiers; out is fp32 [B][Hq][128] (device). */
+int32_t hardkv_attend(const hardkv_config *cfg, hardkv_state *st, const void *q, float *out,
+                      void *stream);
+
+/* The whole step: append, select, regularize, condense, attend, in one stream-ordered,
+ * capturable sequence (the view attention is fused into the rewrite). */
+int32_t hardkv_step(const hardkv_config *cfg, hardkv_state *st, const void *q, const void *k_new,
+                    const void *v_new, float *out, void *stream);
+
+/* Launches only kernel `stage` of hardkv_step (0 append, 1 score+select, 2 rewrite with
+ * view attention, 3 condense, 4 condensed/dense attention, 5 combine), for timing one
+ * kernel on its own.  Stages 1, 2, 4 and 5 only read what earlier stages wrote and may
+ * be repeated; 0 and 3 advance the state. */
+int32_t hardkv_step_stage(const hardkv_config *cfg, hardkv_state *st, const void *q,
+                          const void *k_new, const void *v_new, float *out, int32_t stage,
+                          void *stream);
+
+/* Number of kernels hardkv_step launches, and the name of kernel `stage`. */
+int32_t hardkv_step_num_stages(void);
+const char *hardkv_step_stage_name(int32_t stage);
+
+/* Text for a status code. */
+const char *hardkv_strerror(int32_t code);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* HARDKV_H */

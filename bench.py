@@ -1,0 +1,381 @@
+"""Benchmark of the HARD-KV decode step on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--config c2] [--gpus 1]
+
+One step is hardkv_step on one batch: append, score + calibrate + top-p, rewrite
+(with the view attention fused), condense, tier attention and combine, for every
+(sequence, KV head) of the workload (all layers of it for the 32-layer workload).
+Inputs are seeded synthetic caches generated on the GPU and resident in HBM
+before the timed region.  Prints one JSON line.
+
+Timing:
+  * W warmup steps run eagerly; then K steps are captured into one HIP graph and
+    replayed once between two events (streaming workloads), or each of the K steps
+    starts from the same prefilled state, restored outside the timed region
+    (the mixed-length workload, whose first step condenses hundreds of blocks).
+  * The dominant kernel is timed on its own with events over R launches
+    (hardkv_step_stage on the same stream); its algorithmic bytes per launch over
+    that duration give roofline.achieved.
+  * Algorithmic bytes per step follow the byte model of the design notes and are
+    computed from the per-unit pool sizes, budgets and condensed blocks of the
+    timed steps, replayed eagerly from a snapshot after the timed region.
+  * cpu_baseline: the CPU oracle timed on one step of the same workload (a sample
+    of units when the full step would take too long), on the host's cores.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+import torch  # noqa: E402
+
+from decode_kv_cache_02_amd import hardkv as hk  # noqa: E402
+from synth import get_workload, make_inputs  # noqa: E402
+from synth.configs import COND_MERGE  # noqa: E402
+
+HBM_PEAK_GBPS = 8000.0
+D = 128
+STAGE_NAMES = ["append", "score", "select", "condense", "rewrite_attend", "combine"]
+REPEATABLE = [1, 2, 4, 5]  # stages that only read what earlier stages wrote
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="c2")
+    ap.add_argument("--top-p", type=float, default=None, help="override p (the mixed-length workload sweeps it)")
+    ap.add_argument("--eager", action="store_true", help="no graph (for counter runs)")
+    ap.add_argument("--stage-reps", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-units", type=int, default=0, help="oracle sample size in units (0: automatic)")
+    ap.add_argument("--copy-calib", type=int, default=0,
+                    help="only run a device copy of this many MiB (counter calibration) and exit")
+    return ap.parse_args()
+
+
+# ---- layers ------------------------------------------------------------------------------
+class Layer:
+    def __init__(self, wl, layer, steps, top_p=None):
+        self.wl = wl
+        self.inp = make_inputs(wl, layer=layer, device="cuda", steps=steps)
+        self.cfg = hk.Config.from_workload(wl, top_p=top_p)
+        self.st = hk.State(self.cfg)
+        hk.hardkv_prefill(self.cfg, self.st, self.inp.k_ctx, self.inp.v_ctx, self.inp.ctx_len)
+        self.out = torch.zeros((wl.batch, wl.num_q_heads, D), dtype=torch.float32, device="cuda")
+
+    def drop_context(self):
+        self.inp.k_ctx = self.inp.v_ctx = None
+
+    def step(self, s):
+        hk.hardkv_step(self.cfg, self.st, self.inp.q[s], self.inp.k_new[s], self.inp.v_new[s], self.out)
+
+    def stage(self, s, k):
+        hk.hardkv_step_stage(self.cfg, self.st, self.inp.q[s], self.inp.k_new[s], self.inp.v_new[s],
+                             self.out, k)
+
+    # What a step changes beyond what it rewrites from scratch: counters, the dense ring
+    # (whose slots the append overwrites) and the condensed tier (merged into).  Pool rows
+    # written by the append are rewritten with the same values on a replay.
+    MUTABLE = ("seq_len", "pool_head", "dense_k", "dense_v", "cond_kn", "cond_vn", "cond_omega",
+               "cond_n", "cond_cursor", "error_word")
+
+    def snapshot(self):
+        return {n: getattr(self.st, n).clone() for n in self.MUTABLE}
+
+    def restore(self, snap):
+        for n in self.MUTABLE:
+            getattr(self.st, n).copy_(snap[n])
+
+
+def unit_bytes(wl, N, kstar, E, t, c_occ):
+    """Algorithmic bytes per stage for arrays of per-unit values (one step).
+
+    score: the pool keys; rewrite_attend: the kept rows read and written once, the dense
+    window and the occupied condensed slots read, q in; condense: the values of the
+    condensing blocks and the slot read-modify-write; append: three rows of K and V;
+    combine: the output.  The select stage only moves scores and weights (scratch), which
+    the byte model does not count."""
+    e, G = wl.elem_bytes, wl.group
+    dense_rows = np.minimum(t, wl.dense_window)
+    rmw = 2 * (8 * D + 8) * E if wl.cond_mode == COND_MERGE else 0 * E
+    return {
+        "append": 6 * e * D * np.ones_like(N),
+        "score": e * D * N,
+        "select": 0 * N,
+        "condense": e * D * 64 * E + rmw,
+        "rewrite_attend": 4 * e * D * kstar + 2 * e * D * dense_rows + (8 * D + 8) * c_occ + G * D * e,
+        "combine": G * D * 4 * np.ones_like(N),
+    }
+
+
+def step_accounting(layers, s):
+    """Runs step s of every layer eagerly and returns (bytes per stage, pool tokens scanned)."""
+    tot = {k: 0.0 for k in STAGE_NAMES}
+    scanned = 0
+    for L in layers:
+        wl = L.wl
+        t = L.st.seq_len.cpu().numpy().astype(np.int64)
+        c = L.st.pool_head.cpu().numpy().astype(np.int64)
+        t1 = (t + 1)[:, None]
+        N = np.maximum(0, t1 - wl.dense_window) - c
+        L.step(s)
+        torch.cuda.synchronize()
+        kstar = L.st.budget.cpu().numpy().astype(np.int64)
+        E = L.st.n_condense.cpu().numpy().astype(np.int64)
+        c_occ = (L.st.cond_n.cpu().numpy() > 0).sum(-1)
+        ub = unit_bytes(wl, N, kstar, E, np.broadcast_to(t1, N.shape), c_occ)
+        for k in tot:
+            tot[k] += float(ub[k].sum())
+        scanned += int(N.sum())
+    return tot, scanned
+
+
+def copy_calibration(mib):
+    n = mib * (1 << 20)
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n}))
+
+
+def source_digest(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel, workload):
+    """HBM bytes per launch measured by the counter runs kept under profiles/, if they were
+    taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    ent = rec.get(workload, {}).get(kernel)
+    if not ent:
+        return None
+    if ent.get("source_digest") != source_digest(ent.get("sources", [])):
+        return None
+    return ent.get("hbm_bytes_per_launch")
+
+
+KERNEL_SOURCES = {
+    "score": ["decode_kv_cache_02_amd/csrc/k_select.hip", "decode_kv_cache_02_amd/csrc/hardkv_internal.h"],
+    "rewrite_attend": ["decode_kv_cache_02_amd/csrc/k_rewrite.hip", "decode_kv_cache_02_amd/csrc/attn_common.h",
+                       "decode_kv_cache_02_amd/csrc/hardkv_internal.h"],
+}
+
+
+# ---- CPU baseline -------------------------------------------------------------------------
+def cpu_baseline(wl, layers, units_req):
+    from oracle import hardkv_oracle as orc
+    L = layers[0]
+    inp = L.inp_cpu_source
+    B, H = wl.batch, wl.num_kv_heads
+    total_units = B * H * len(layers)
+    # whole sequences (all KV heads) of the first layer, as many as the sample needs
+    per_seq = H
+    if units_req > 0:
+        nb = max(1, min(B, units_req // per_seq))
+    else:
+        nb = B if wl.batch * wl.ctx_len <= 16 * 16384 else max(1, B // 8)
+    sub = wl.with_(batch=nb)
+    k_ctx = inp["k_ctx"][:nb].cpu()
+    v_ctx = inp["v_ctx"][:nb].cpu()
+    lens = inp["ctx_len"][:nb].cpu()
+    o = orc.Oracle(sub, top_p=L.cfg.c.top_p)
+    assert o.prefill(k_ctx, v_ctx, lens) == 0
+    q = L.inp.q[0][:nb].cpu()
+    kn = L.inp.k_new[0][:nb].cpu()
+    vn = L.inp.v_new[0][:nb].cpu()
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    threads = max(1, min(threads, os.cpu_count() or 1))
+    t0 = time.perf_counter()
+    o.step(q, kn, vn, attend=True, nthreads=threads)
+    dt = time.perf_counter() - t0
+    units = nb * H
+    step_s = dt * total_units / units
+    return {"value": 1.0 / step_s, "unit": "steps/s", "cores": threads, "kind": "oracle",
+            "sample": f"one full step of {units} of the {total_units} (sequence, KV head) units "
+                      f"({nb} sequences x {H} KV heads of layer 0, same inputs), "
+                      f"{dt:.2f} s, scaled to the whole step",
+            "seconds": dt}
+
+
+# ---- main ---------------------------------------------------------------------------------
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}); this build has no multi-GPU path.",
+              file=sys.stderr)
+        sys.exit(2)
+    hk.require_gpu()
+    torch.cuda.set_device(0)
+    if args.copy_calib:
+        copy_calibration(args.copy_calib)
+        return
+    wl = get_workload(args.config)
+    top_p = args.top_p
+    restore_mode = wl.ctx_min is not None  # mixed lengths: every timed step from the prefilled state
+    K, Wm = args.steps, args.warmup
+    nsteps = 1 if restore_mode else Wm + K
+
+    layers = []
+    for layer in range(wl.layers):
+        L = Layer(wl, layer, nsteps, top_p=top_p)
+        if layer == 0 and not args.no_cpu_baseline:
+            L.inp_cpu_source = {"k_ctx": L.inp.k_ctx, "v_ctx": L.inp.v_ctx, "ctx_len": L.inp.ctx_len}
+        else:
+            L.drop_context()
+        layers.append(L)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+
+    if restore_mode:
+        snaps = [L.snapshot() for L in layers]
+        for _ in range(Wm):
+            for L in layers:
+                L.step(0)
+            for L, sn in zip(layers, snaps):
+                L.restore(sn)
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(K):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for L in layers:
+                L.step(0)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+            for L, sn in zip(layers, snaps):
+                L.restore(sn)
+        torch.cuda.synchronize()
+        ms_per_step = float(np.mean(times))
+        acc_steps = [0]
+        snap_after = snaps
+    else:
+        for s in range(Wm):
+            for L in layers:
+                L.step(s)
+        torch.cuda.synchronize()
+        snap_after = [L.snapshot() for L in layers]
+        if args.eager:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for s in range(Wm, Wm + K):
+                for L in layers:
+                    L.step(s)
+            e1.record(stream)
+        else:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for s in range(Wm, Wm + K):
+                    for L in layers:
+                        L.step(s)
+            # capture does not run the kernels; the state is still the post-warmup one
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            g.replay()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        ms_per_step = e0.elapsed_time(e1) / K
+        graph_out = layers[-1].out.clone()
+        acc_steps = list(range(Wm, Wm + K))
+
+    # per-kernel durations on the post-step state (repeatable stages only)
+    stage_us = {}
+    s_last = acc_steps[-1]
+    for k in REPEATABLE:
+        for L in layers:
+            L.stage(s_last, k)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.stage_reps):
+            for L in layers:
+                L.stage(s_last, k)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        stage_us[STAGE_NAMES[k]] = e0.elapsed_time(e1) * 1e3 / (args.stage_reps * len(layers))
+
+    # exact algorithmic bytes of the timed steps, replayed eagerly from the snapshot
+    for L, sn in zip(layers, snap_after):
+        L.restore(sn)
+    torch.cuda.synchronize()
+    bytes_tot = {k: 0.0 for k in STAGE_NAMES}
+    scanned_tot = 0
+    for s in acc_steps:
+        b, n = step_accounting(layers, s)
+        for k in b:
+            bytes_tot[k] += b[k]
+        scanned_tot += n
+    nacc = len(acc_steps)
+    replay_matches = None
+    if not restore_mode:
+        replay_matches = bool(torch.equal(graph_out, layers[-1].out))
+    bytes_step = {k: v / nacc for k, v in bytes_tot.items()}
+    algo_step = sum(bytes_step.values())
+    scanned_step = scanned_tot / nacc
+
+    # the dominant kernel: the longest of the repeatable stages that move algorithmic bytes
+    dom = max((k for k in stage_us if bytes_step[k] > 0), key=stage_us.get)
+    dom_bytes_launch = bytes_step[dom] / len(layers)
+    achieved = dom_bytes_launch / (stage_us[dom] * 1e-6) / 1e9
+    traffic = load_traffic(dom, wl.name)
+
+    steps_per_s = 1e3 / ms_per_step
+    res = {
+        "metric": "hardkv_step decode steps/s + KV tokens scanned/s; % of HBM peak GB/s",
+        "value": steps_per_s,
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": Wm,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if wl.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "layers": wl.layers, "batch": wl.batch,
+                   "ctx_len": wl.ctx_len, "ctx_min": wl.ctx_min, "q_heads": wl.num_q_heads,
+                   "kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim, "dense_window": wl.dense_window,
+                   "sparse_cap": wl.sparse_cap, "condensed_slots": wl.condensed_slots,
+                   "top_p": float(layers[0].cfg.c.top_p), "cond_mode": "merge",
+                   "timing": "restore-per-step" if restore_mode else ("eager" if args.eager else "hip-graph")},
+        "kv_tokens_scanned_per_s": scanned_step * steps_per_s,
+        "algorithmic_bytes_per_step": algo_step,
+        "step_hbm_GBps": algo_step / (ms_per_step * 1e-3) / 1e9,
+        "step_hbm_frac": algo_step / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+        "stage_us": {k: round(v, 2) for k, v in stage_us.items()},
+        "stage_algorithmic_bytes": {k: round(v) for k, v in bytes_step.items()},
+        "roofline": {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
+                     "bytes_per_launch": dom_bytes_launch, "us_per_launch": stage_us[dom]},
+        "graph_replay_matches_eager": replay_matches,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(wl, layers, args.cpu_units)
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

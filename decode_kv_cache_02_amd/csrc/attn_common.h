@@ -123,4 +123,113 @@ HK_DEV void load_q_scaled(const Args &a, int b, int h, int sub, float (&qs)[G][8
   }
 }
 
+// Attention partial of segment `seg` of a head's tiers, written to its partial slot.
+// Segments [0, nv_att) are view rows (rv_att each, up to k*), then nc_att segments of
+// condensed slots (rc_att each, slots with n > 0 only), then nd_att segments of dense
+// positions (rd_att each, positions [max(0, t - W), t)).  A merged slot holding n tokens
+// enters with key Kn/Omega, value Vn/Omega and logit bias ln n (log2 n in base 2).
+template <typename T, int G>
+HK_DEV void attend_segment(const Args &a, int bh, int seg, float (*s_part)[G][2 + HD]) {
+  constexpr int EB = Elem<T>::bytes;
+  constexpr size_t ROWB = (size_t)HD * EB;
+  const int b = bh / a.Hkv, h = bh - b * a.Hkv;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int sub = lane & 15, grp = lane >> 4;
+  const int rloc = wave * 4 + grp;  // row of this lane group inside a batch of 16
+
+  const int64_t t = a.seq_len[b];
+  AttnState<G> st;
+  st.init();
+  float qs[G][8];
+  load_q_scaled<T, G>(a, b, h, sub, qs);
+
+  int slot;
+  if (seg < a.nv_att) {  // view rows
+    slot = seg;
+    const int64_t kst = min((int64_t)a.budget[bh], (int64_t)a.V_cap);
+    const int64_t r0 = (int64_t)seg * a.rv_att, r1 = min(r0 + (int64_t)a.rv_att, kst);
+    const char *vk = (const char *)a.view_k + (size_t)bh * a.V_cap * ROWB + sub * 8 * EB;
+    const char *vv = (const char *)a.view_v + (size_t)bh * a.V_cap * ROWB + sub * 8 * EB;
+    for (int64_t base = r0; base < r1; base += 32) {
+      Raw8<T> kr[2], vr[2];
+      bool act[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int64_t r = base + j * 16 + rloc;
+        act[j] = r < r1;
+        if (act[j]) {
+          raw_load(vk + (size_t)r * ROWB, kr[j]);
+          raw_load(vv + (size_t)r * ROWB, vr[j]);
+        } else {
+          kr[j] = Raw8<T>{};
+          vr[j] = Raw8<T>{};
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        float kf[8], vf[8];
+        raw_to_f(kr[j], kf);
+        raw_to_f(vr[j], vf);
+        attn_row<G>(st, qs, kf, vf, 1.0f, 0.0f, act[j]);
+      }
+    }
+  } else if (seg < a.nv_att + a.nc_att) {  // condensed slots
+    const int xc = seg - a.nv_att;
+    slot = a.part_cd_base + xc;
+    const int s0 = xc * a.rc_att, s1 = min(s0 + a.rc_att, a.C);
+    const size_t cb = (size_t)bh * a.C;
+    for (int base = s0; base < s1; base += 16) {
+      const int sg = base + rloc;
+      const int n = sg < s1 ? a.cond_n[cb + sg] : 0;
+      const bool act = n > 0;
+      float kf[8], vf[8];
+      float inv = 0.0f, bias = 0.0f;
+      if (act) {
+        load8(a.cond_kn + (cb + sg) * HD + sub * 8, kf, F32{});
+        load8(a.cond_vn + (cb + sg) * HD + sub * 8, vf, F32{});
+        inv = 1.0f / a.cond_omega[cb + sg];
+        bias = a.merge_bias ? log2f((float)n) : 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) vf[i] *= inv;
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) kf[i] = vf[i] = 0.0f;
+      }
+      attn_row<G>(st, qs, kf, vf, inv, bias, act);
+    }
+  } else {  // dense positions
+    const int xd = seg - a.nv_att - a.nc_att;
+    slot = a.part_cd_base + a.nc_att + xd;
+    const int64_t lo = t > a.W ? t - a.W : 0;
+    const int64_t p0 = lo + (int64_t)xd * a.rd_att, p1 = min(p0 + (int64_t)a.rd_att, t);
+    const char *dk = (const char *)a.dense_k + (size_t)bh * a.W * ROWB + sub * 8 * EB;
+    const char *dv = (const char *)a.dense_v + (size_t)bh * a.W * ROWB + sub * 8 * EB;
+    for (int64_t base = p0; base < p1; base += 32) {
+      Raw8<T> kr[2], vr[2];
+      bool act[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int64_t p = base + j * 16 + rloc;
+        act[j] = p < p1;
+        if (act[j]) {
+          const size_t row = (size_t)(p % a.W);
+          raw_load(dk + row * ROWB, kr[j]);
+          raw_load(dv + row * ROWB, vr[j]);
+        } else {
+          kr[j] = Raw8<T>{};
+          vr[j] = Raw8<T>{};
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        float kf[8], vf[8];
+        raw_to_f(kr[j], kf);
+        raw_to_f(vr[j], vf);
+        attn_row<G>(st, qs, kf, vf, 1.0f, 0.0f, act[j]);
+      }
+    }
+  }
+  attn_write_partial<G>(st, a.part + ((size_t)bh * a.npart + slot) * G * (2 + HD), s_part);
+}
+
 }  // namespace hardkv

@@ -9,7 +9,6 @@
 namespace hardkv {
 namespace {
 
-constexpr int MAX_POOL_BLOCKS = 6144;  // per-block counts of one head live in the select LDS
 constexpr double LOG2E = 1.4426950408889634074;
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -18,7 +17,7 @@ bool aligned16(const void *p) { return p != nullptr && ((uintptr_t)p & 15u) == 0
 
 struct Plan {
   Args a;
-  size_t off_head, off_viewoff, off_part, ws_bytes;
+  size_t off_head, off_cmax, off_blkinfo, off_part, ws_bytes;
 };
 
 // Checks the configuration and derives every size; fills the size fields of p.a.
@@ -98,8 +97,9 @@ int32_t plan(const hardkv_config *cfg, Plan &p) {
   }
 
   p.off_head = 0;
-  p.off_viewoff = align256(p.off_head + (size_t)BH * sizeof(HeadInfo));
-  p.off_part = align256(p.off_viewoff + (size_t)BH * a.P * sizeof(uint32_t));
+  p.off_cmax = align256(p.off_head + (size_t)BH * sizeof(HeadInfo));
+  p.off_blkinfo = align256(p.off_cmax + (size_t)BH * a.nch_score * sizeof(float));
+  p.off_part = align256(p.off_blkinfo + (size_t)BH * a.P * sizeof(uint2));
   p.ws_bytes = align256(p.off_part + (size_t)BH * a.npart * G * (2 + HD) * sizeof(float));
   return HARDKV_OK;
 }
@@ -142,7 +142,8 @@ int32_t bind(const hardkv_state *st, Plan &p) {
   a.error_word = st->error_word;
   char *ws = (char *)st->workspace;
   a.head = reinterpret_cast<HeadInfo *>(ws + p.off_head);
-  a.viewoff = reinterpret_cast<uint32_t *>(ws + p.off_viewoff);
+  a.cmax = reinterpret_cast<float *>(ws + p.off_cmax);
+  a.blkinfo = reinterpret_cast<uint2 *>(ws + p.off_blkinfo);
   a.part = reinterpret_cast<float *>(ws + p.off_part);
   return HARDKV_OK;
 }
@@ -157,8 +158,9 @@ int32_t hip_status(hipError_t e) { return e == hipSuccess ? HARDKV_OK : HARDKV_E
 
 bool is_bf16(const hardkv_config *cfg) { return cfg->dtype == HARDKV_BF16; }
 
-const char *const kStageNames[] = {"append", "score_select", "rewrite_attend_view", "condense",
-                                   "attend_condensed_dense", "combine"};
+constexpr int NSTAGES = 6;
+const char *const kStageNames[NSTAGES] = {"append", "score", "select", "condense", "rewrite_attend",
+                                          "combine"};
 
 // kernel `stage` of the fused step
 hipError_t step_stage(const hardkv_config *cfg, Args &a, int stage, hipStream_t s) {
@@ -166,10 +168,10 @@ hipError_t step_stage(const hardkv_config *cfg, Args &a, int stage, hipStream_t 
   a.nvp = a.nch_reg;
   switch (stage) {
     case 0: return launch_append(a, s, bf);
-    case 1: return launch_score_select(a, s, bf);
-    case 2: return launch_regularize(a, s, bf, true);
+    case 1: return launch_score(a, s, bf);
+    case 2: return launch_select(a, s);
     case 3: return launch_condense(a, s, bf);
-    case 4: return launch_attend(a, s, bf, false);
+    case 4: return launch_rewrite(a, s, bf, true, true, true);
     case 5: return launch_combine(a, s);
     default: return hipErrorInvalidValue;
   }
@@ -223,14 +225,19 @@ int32_t hardkv_select(const hardkv_config *cfg, hardkv_state *st, const void *q,
   if (rc != HARDKV_OK) return rc;
   if (!aligned16(q)) return HARDKV_EINVAL;
   p.a.q = q;
-  return hip_status(launch_score_select(p.a, (hipStream_t)stream, is_bf16(cfg)));
+  hipStream_t s = (hipStream_t)stream;
+  const bool bf = is_bf16(cfg);
+  hipError_t e = launch_score(p.a, s, bf);
+  if (e == hipSuccess) e = launch_select(p.a, s);
+  if (e == hipSuccess) e = launch_rewrite(p.a, s, bf, true, false, false);  // mask words
+  return hip_status(e);
 }
 
 int32_t hardkv_regularize(const hardkv_config *cfg, hardkv_state *st, void *stream) {
   Plan p;
   int32_t rc = setup(cfg, st, p);
   if (rc != HARDKV_OK) return rc;
-  return hip_status(launch_regularize(p.a, (hipStream_t)stream, is_bf16(cfg), false));
+  return hip_status(launch_rewrite(p.a, (hipStream_t)stream, is_bf16(cfg), false, true, false));
 }
 
 int32_t hardkv_condense(const hardkv_config *cfg, hardkv_state *st, void *stream) {
@@ -250,7 +257,7 @@ int32_t hardkv_attend(const hardkv_config *cfg, hardkv_state *st, const void *q,
   p.a.out = out;
   p.a.nvp = p.a.nv_att;
   hipStream_t s = (hipStream_t)stream;
-  hipError_t e = launch_attend(p.a, s, is_bf16(cfg), true);
+  hipError_t e = launch_attend(p.a, s, is_bf16(cfg));
   if (e == hipSuccess) e = launch_combine(p.a, s);
   return hip_status(e);
 }
@@ -266,7 +273,7 @@ int32_t hardkv_step(const hardkv_config *cfg, hardkv_state *st, const void *q, c
   p.a.v_new = v_new;
   p.a.out = out;
   hipStream_t s = (hipStream_t)stream;
-  for (int stage = 0; stage < 6; ++stage) {
+  for (int stage = 0; stage < NSTAGES; ++stage) {
     hipError_t e = step_stage(cfg, p.a, stage, s);
     if (e != hipSuccess) return HARDKV_EHIP;
   }
@@ -279,9 +286,9 @@ int32_t hardkv_step_stage(const hardkv_config *cfg, hardkv_state *st, const void
   Plan p;
   int32_t rc = setup(cfg, st, p);
   if (rc != HARDKV_OK) return rc;
-  if (stage < 0 || stage >= 6) return HARDKV_EINVAL;
+  if (stage < 0 || stage >= NSTAGES) return HARDKV_EINVAL;
   if (stage == 0 && (!aligned16(k_new) || !aligned16(v_new))) return HARDKV_EINVAL;
-  if ((stage == 1 || stage == 2 || stage == 4) && !aligned16(q)) return HARDKV_EINVAL;
+  if ((stage == 1 || stage == 4) && !aligned16(q)) return HARDKV_EINVAL;
   if (stage == 5 && !aligned16(out)) return HARDKV_EINVAL;
   p.a.q = q;
   p.a.k_new = k_new;
@@ -290,10 +297,10 @@ int32_t hardkv_step_stage(const hardkv_config *cfg, hardkv_state *st, const void
   return hip_status(step_stage(cfg, p.a, stage, (hipStream_t)stream));
 }
 
-int32_t hardkv_step_num_stages(void) { return 6; }
+int32_t hardkv_step_num_stages(void) { return NSTAGES; }
 
 const char *hardkv_step_stage_name(int32_t stage) {
-  return (stage >= 0 && stage < 6) ? kStageNames[stage] : "unknown";
+  return (stage >= 0 && stage < NSTAGES) ? kStageNames[stage] : "unknown";
 }
 
 const char *hardkv_strerror(int32_t code) {

@@ -13,19 +13,23 @@ constexpr int HD = 128;       // head dim
 constexpr int NCOEFF = 10;    // Taylor coefficients of 2^f on [0, 1)
 constexpr int NTHREADS = 256; // threads per workgroup of every kernel
 constexpr int NB1 = 3073;     // level-1 buckets of the mass radix select (key >> 16)
+constexpr int SEL_THREADS = 1024;     // threads of the select workgroup (one per head)
+constexpr int MAX_POOL_BLOCKS = 6144; // pool ring blocks per head the select LDS can index
+constexpr int CAND_CAP = 8192;        // cut-bucket candidates resolved in LDS
 
-// Per-head scratch in the workspace.  Counters are left at zero by the kernels.
+// Per-head plan of the current step, written by the select kernel and read by the
+// kernels after it (rewrite, condense), so that they see the pool as select saw it.
 struct alignas(64) HeadInfo {
-  uint32_t max_enc;    // running max score of the current select (ordered encoding, 0 = none)
-  uint32_t score_cnt;  // workgroups of the score kernel that finished this head
-  uint32_t cond_cnt;   // workgroups of the condense kernel that finished this head
-  uint32_t w_th;       // threshold weight of the top-p cut
-  uint32_t r;          // tokens of weight w_th that are kept (lowest positions first)
+  int64_t t_plan;   // t after the append
+  int64_t c_plan;   // pool head before condensation
+  uint32_t w_th;    // threshold weight of the top-p cut
+  uint32_t r;       // tokens of weight w_th that are kept (lowest positions first)
   int32_t kstar;
-  int32_t E;
+  int32_t E;        // blocks to condense
+  int32_t nu_plan;  // condensed-slot cursor before condensation
   int32_t pad0;
   uint64_t w_all;
-  uint64_t pad1[3];
+  uint64_t pad1[2];
 };
 
 // Everything a kernel needs, passed by value.
@@ -47,7 +51,8 @@ struct Args {
   uint32_t *error_word;
   // workspace
   HeadInfo *head;
-  uint32_t *viewoff;  // [BH][P] first view row of each pool block (by ring block)
+  float *cmax;        // [BH][nch_score] max score of each score workgroup
+  uint2 *blkinfo;     // [BH][P] per ring block: (first view row, ties before the block)
   float *part;        // [BH][npart][G][2 + HD] attention partials (m, l, acc)
   // prefill
   const void *k_ctx, *v_ctx;
@@ -72,10 +77,13 @@ struct Args {
 // launchers (one per kernel); each returns a hipError_t
 hipError_t launch_prefill(const Args &a, hipStream_t s, bool bf16);
 hipError_t launch_append(const Args &a, hipStream_t s, bool bf16);
-hipError_t launch_score_select(const Args &a, hipStream_t s, bool bf16);
-hipError_t launch_regularize(const Args &a, hipStream_t s, bool bf16, bool attend);
+hipError_t launch_score(const Args &a, hipStream_t s, bool bf16);
+hipError_t launch_select(const Args &a, hipStream_t s);
+// rewrite kernel: `mask` writes the mask words, `copy` copies the kept rows into the view,
+// `attend` adds the view attention and the condensed/dense attention segments
+hipError_t launch_rewrite(const Args &a, hipStream_t s, bool bf16, bool mask, bool copy, bool attend);
 hipError_t launch_condense(const Args &a, hipStream_t s, bool bf16);
-hipError_t launch_attend(const Args &a, hipStream_t s, bool bf16, bool with_view);
+hipError_t launch_attend(const Args &a, hipStream_t s, bool bf16);
 hipError_t launch_combine(const Args &a, hipStream_t s);
 
 // ---------------------------------------------------------------------------------------

@@ -1,167 +1,99 @@
 // k_attend.hip -- decode attention over the three tiers, and the split-K combine.
 //
 // HARD-KV explainer, technical summary 2.A: the dense tier keeps the most recent tokens,
-// the sparse tier the kept tokens (here already rewritten into the head's view), and the
-// condensed tier constant-size merged slots.  Each query attends to all three.  A merged
-// slot holding n tokens enters with key Kn/Omega, value Vn/Omega and logit bias ln n, so
-// that n identical tokens merged into one slot weigh exactly as the n tokens did.
+// the sparse tier the kept tokens (here rewritten into the head's view), and the
+// condensed tier constant-size merged slots; each query attends to all three.
 //
-// Grid (segments, B*Hkv), 256 threads.  Segment x selects a range of one tier: view
-// rows (standalone call only; in the fused step the rewrite kernel already attended
-// them), condensed slots, or dense positions.  Each workgroup writes one partial; the
-// combine kernel (one workgroup per head) merges them into the fp32 output.
+// hardkv_attend_tiers, grid (segments, B*Hkv), 256 threads: the standalone attention;
+//   each workgroup attends one range of view rows, condensed slots or dense positions
+//   and writes one partial (the fused step gets the same partials from the rewrite
+//   kernel instead).
+// hardkv_combine, grid (B*Hkv), 256 threads: one wavefront per query of the group; the
+//   lanes first scale every partial's (m, l) against the common max, then sum the
+//   partials' accumulators two head dims per lane, eight partials in flight.
 #include "attn_common.h"
 
 namespace hardkv {
 
 namespace {
 
-
 template <typename T, int G>
-__global__ __launch_bounds__(NTHREADS) void hardkv_attend_tiers(Args a, int seg_offset) {
-  constexpr int EB = Elem<T>::bytes;
-  constexpr size_t ROWB = (size_t)HD * EB;
-  const int bh = blockIdx.y, x = blockIdx.x + seg_offset;
-  const int b = bh / a.Hkv, h = bh - b * a.Hkv;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int sub = lane & 15, grp = lane >> 4;
-  const int rloc = wave * 4 + grp;  // row of this lane group inside a batch of 16
-
+__global__ __launch_bounds__(NTHREADS) void hardkv_attend_tiers(Args a) {
   __shared__ float s_part[4][G][2 + HD];
-
-  const int64_t t = a.seq_len[b];
-  AttnState<G> st;
-  st.init();
-  float qs[G][8];
-  load_q_scaled<T, G>(a, b, h, sub, qs);
-
-  int slot;
-  if (x < a.nv_att) {  // view rows [x*rv, min(x*rv + rv, k*))
-    slot = x;
-    const int64_t kst = min((int64_t)a.budget[bh], (int64_t)a.V_cap);
-    const int64_t r0 = (int64_t)x * a.rv_att, r1 = min(r0 + (int64_t)a.rv_att, kst);
-    const char *vk = (const char *)a.view_k + (size_t)bh * a.V_cap * ROWB + sub * 8 * EB;
-    const char *vv = (const char *)a.view_v + (size_t)bh * a.V_cap * ROWB + sub * 8 * EB;
-    for (int64_t base = r0; base < r1; base += 32) {
-      Raw8<T> kr[2], vr[2];
-      bool act[2];
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int64_t r = base + j * 16 + rloc;
-        act[j] = r < r1;
-        if (act[j]) {
-          raw_load(vk + (size_t)r * ROWB, kr[j]);
-          raw_load(vv + (size_t)r * ROWB, vr[j]);
-        } else {
-          kr[j] = Raw8<T>{};
-          vr[j] = Raw8<T>{};
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        float kf[8], vf[8];
-        raw_to_f(kr[j], kf);
-        raw_to_f(vr[j], vf);
-        attn_row<G>(st, qs, kf, vf, 1.0f, 0.0f, act[j]);
-      }
-    }
-  } else if (x < a.nv_att + a.nc_att) {  // condensed slots
-    const int xc = x - a.nv_att;
-    slot = a.part_cd_base + xc;
-    const int s0 = xc * a.rc_att, s1 = min(s0 + a.rc_att, a.C);
-    const size_t cb = (size_t)bh * a.C;
-    for (int base = s0; base < s1; base += 16) {
-      const int sg = base + rloc;
-      const bool inr = sg < s1;
-      const int n = inr ? a.cond_n[cb + sg] : 0;
-      const bool act = n > 0;
-      float kf[8], vf[8];
-      float inv = 0.0f, bias = 0.0f;
-      if (act) {
-        load8(a.cond_kn + (cb + sg) * HD + sub * 8, kf, F32{});
-        load8(a.cond_vn + (cb + sg) * HD + sub * 8, vf, F32{});
-        inv = 1.0f / a.cond_omega[cb + sg];
-        bias = a.merge_bias ? __log2f((float)n) : 0.0f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) vf[i] *= inv;
-      } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) kf[i] = vf[i] = 0.0f;
-      }
-      attn_row<G>(st, qs, kf, vf, inv, bias, act);
-    }
-  } else {  // dense positions [max(0, t - W), t)
-    const int xd = x - a.nv_att - a.nc_att;
-    slot = a.part_cd_base + a.nc_att + xd;
-    const int64_t lo = t > a.W ? t - a.W : 0;
-    const int64_t p0 = lo + (int64_t)xd * a.rd_att, p1 = min(p0 + (int64_t)a.rd_att, t);
-    const char *dk = (const char *)a.dense_k + (size_t)bh * a.W * ROWB + sub * 8 * EB;
-    const char *dv = (const char *)a.dense_v + (size_t)bh * a.W * ROWB + sub * 8 * EB;
-    for (int64_t base = p0; base < p1; base += 32) {
-      Raw8<T> kr[2], vr[2];
-      bool act[2];
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int64_t p = base + j * 16 + rloc;
-        act[j] = p < p1;
-        if (act[j]) {
-          const size_t row = (size_t)(p % a.W);
-          raw_load(dk + row * ROWB, kr[j]);
-          raw_load(dv + row * ROWB, vr[j]);
-        } else {
-          kr[j] = Raw8<T>{};
-          vr[j] = Raw8<T>{};
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        float kf[8], vf[8];
-        raw_to_f(kr[j], kf);
-        raw_to_f(vr[j], vf);
-        attn_row<G>(st, qs, kf, vf, 1.0f, 0.0f, act[j]);
-      }
-    }
-  }
-  attn_write_partial<G>(st, a.part + ((size_t)bh * a.npart + slot) * G * (2 + HD), s_part);
+  attend_segment<T, G>(a, blockIdx.y, blockIdx.x, s_part);
 }
+
+constexpr int MAX_COMBINE = 2048;  // partials per round of the combine
 
 template <int G>
 __global__ __launch_bounds__(NTHREADS) void hardkv_combine(Args a) {
   const int bh = blockIdx.x;
   const int b = bh / a.Hkv, h = bh - b * a.Hkv;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  __shared__ float s_f[4][MAX_COMBINE];
   const float *base = a.part + (size_t)bh * a.npart * G * (2 + HD);
-  const int ncd = a.nc_att + a.nd_att;
-  for (int idx = threadIdx.x; idx < G * HD; idx += NTHREADS) {
-    const int g = idx / HD, d = idx - g * HD;
+  const int ns = a.nvp + a.nc_att + a.nd_att;
+  auto slot = [&](int i) { return i < a.nvp ? i : a.part_cd_base + (i - a.nvp); };
+  for (int g = wave; g < G; g += 4) {
     float M = -INFINITY;
-    for (int i = 0; i < a.nvp + ncd; ++i) {
-      const int s = i < a.nvp ? i : a.part_cd_base + (i - a.nvp);
-      const float *ps = base + ((size_t)s * G + g) * (2 + HD);
+    for (int i = lane; i < ns; i += 64) {
+      const float *ps = base + ((size_t)slot(i) * G + g) * (2 + HD);
       if (ps[1] > 0.0f) M = fmaxf(M, ps[0]);
     }
-    float L = 0.0f, A = 0.0f;
-    for (int i = 0; i < a.nvp + ncd; ++i) {
-      const int s = i < a.nvp ? i : a.part_cd_base + (i - a.nvp);
-      const float *ps = base + ((size_t)s * G + g) * (2 + HD);
-      if (ps[1] > 0.0f) {
-        const float f = exp2_fast(ps[0] - M);
-        L += ps[1] * f;
-        A += ps[2 + d] * f;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+    float L = 0.0f, A0 = 0.0f, A1 = 0.0f;
+    for (int r0 = 0; r0 < ns; r0 += MAX_COMBINE) {
+      const int r1 = min(ns, r0 + MAX_COMBINE);
+      float Lp = 0.0f;
+      for (int i = r0 + lane; i < r1; i += 64) {
+        const float *ps = base + ((size_t)slot(i) * G + g) * (2 + HD);
+        const float f = ps[1] > 0.0f ? exp2_fast(ps[0] - M) : 0.0f;
+        s_f[wave][i - r0] = f;
+        Lp += ps[1] * f;
       }
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) Lp += __shfl_xor(Lp, off);
+      L += Lp;
+      wave_sync();
+      int i = r0;
+      for (; i + 8 <= r1; i += 8) {
+        float x0[8], x1[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const float *ps = base + ((size_t)slot(i + u) * G + g) * (2 + HD) + 2;
+          x0[u] = ps[lane];
+          x1[u] = ps[lane + 64];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const float f = s_f[wave][i + u - r0];
+          A0 = __builtin_fmaf(x0[u], f, A0);
+          A1 = __builtin_fmaf(x1[u], f, A1);
+        }
+      }
+      for (; i < r1; ++i) {
+        const float *ps = base + ((size_t)slot(i) * G + g) * (2 + HD) + 2;
+        const float f = s_f[wave][i - r0];
+        A0 = __builtin_fmaf(ps[lane], f, A0);
+        A1 = __builtin_fmaf(ps[lane + 64], f, A1);
+      }
+      wave_sync();
     }
-    a.out[((size_t)b * a.Hq + (size_t)h * G + g) * HD + d] = A / L;
+    float *o = a.out + ((size_t)b * a.Hq + (size_t)h * G + g) * HD;
+    o[lane] = A0 / L;
+    o[lane + 64] = A1 / L;
   }
 }
 
 template <typename T>
-hipError_t launch_tiers(const Args &a, hipStream_t s, bool with_view) {
-  const int off = with_view ? 0 : a.nv_att;
-  dim3 grid((with_view ? a.nv_att : 0) + a.nc_att + a.nd_att, a.B * a.Hkv);
+hipError_t launch_tiers(const Args &a, hipStream_t s) {
+  dim3 grid(a.nv_att + a.nc_att + a.nd_att, a.B * a.Hkv);
   switch (a.G) {
-    case 1: hipLaunchKernelGGL((hardkv_attend_tiers<T, 1>), grid, dim3(NTHREADS), 0, s, a, off); break;
-    case 2: hipLaunchKernelGGL((hardkv_attend_tiers<T, 2>), grid, dim3(NTHREADS), 0, s, a, off); break;
-    case 4: hipLaunchKernelGGL((hardkv_attend_tiers<T, 4>), grid, dim3(NTHREADS), 0, s, a, off); break;
-    case 8: hipLaunchKernelGGL((hardkv_attend_tiers<T, 8>), grid, dim3(NTHREADS), 0, s, a, off); break;
+    case 1: hipLaunchKernelGGL((hardkv_attend_tiers<T, 1>), grid, dim3(NTHREADS), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((hardkv_attend_tiers<T, 2>), grid, dim3(NTHREADS), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((hardkv_attend_tiers<T, 4>), grid, dim3(NTHREADS), 0, s, a); break;
+    case 8: hipLaunchKernelGGL((hardkv_attend_tiers<T, 8>), grid, dim3(NTHREADS), 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -169,8 +101,8 @@ hipError_t launch_tiers(const Args &a, hipStream_t s, bool with_view) {
 
 }  // namespace
 
-hipError_t launch_attend(const Args &a, hipStream_t s, bool bf16, bool with_view) {
-  return bf16 ? launch_tiers<BF16>(a, s, with_view) : launch_tiers<F32>(a, s, with_view);
+hipError_t launch_attend(const Args &a, hipStream_t s, bool bf16) {
+  return bf16 ? launch_tiers<BF16>(a, s) : launch_tiers<F32>(a, s);
 }
 
 hipError_t launch_combine(const Args &a, hipStream_t s) {

@@ -10,8 +10,9 @@
 //
 // Grid (slots touched, B*Hkv), 256 threads.  Workgroup i owns ring slot (cursor + i)
 // mod C and folds in, in age order, every condensed block that lands there (blocks i,
-// i + C, ...), so the result does not depend on scheduling.  The last workgroup of a head
-// (agent-scope counter) advances the cursor and the pool head.
+// i + C, ...), so the result does not depend on scheduling.  Every workgroup reads the
+// pool head, the cursor and E from the plan the select kernel saved, so workgroup 0 can
+// advance the state's pool head and cursor without waiting for the others.
 #include "hardkv_internal.h"
 
 namespace hardkv {
@@ -23,20 +24,17 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_condense(Args a) {
   constexpr int EB = Elem<T>::bytes;
   constexpr size_t ROWB = (size_t)HD * EB;
   const int bh = blockIdx.y, i = blockIdx.x;
-  const int b = bh / a.Hkv;
   const int tid = threadIdx.x, rg = tid >> 4, sub = tid & 15;
   const int P = a.P, C = a.C;
 
   __shared__ float s_k[16][HD];
   __shared__ float s_v[16][HD];
   __shared__ unsigned long long s_w[16];
-  __shared__ uint32_t s_last;
 
-  const int64_t t = a.seq_len[b];
-  const int64_t c = a.pool_head[bh];
-  const int64_t pend = pool_end(t, a.W);
-  const int64_t E = plan_E(pend - c, a.mode, a.S_cap);
-  const int32_t nu = a.cond_cursor[bh];
+  const HeadInfo *hd = a.head + bh;
+  const int64_t c = hd->c_plan;
+  const int64_t E = hd->E;
+  const int32_t nu = hd->nu_plan;
 
   if (a.mode == HARDKV_COND_MERGE && i < E) {
     float ak[8], av[8];
@@ -73,7 +71,7 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_condense(Args a) {
     }
     if (sub == 0) s_w[rg] = wsum;
     __syncthreads();
-    const double w_all = (double)a.w_all[bh];
+    const double w_all = (double)hd->w_all;
     const float inv = (float)(1.0 / w_all);
     const size_t sg = (size_t)bh * C + (size_t)((nu + i) % C);
     if (tid < HD) {
@@ -97,16 +95,7 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_condense(Args a) {
     }
   }
 
-  // bookkeeping once every workgroup of the head has read the cursor and the pool head
-  fence_agent();
-  __syncthreads();
-  if (tid == 0) {
-    const uint32_t old = atomic_add_acq_rel(&a.head[bh].cond_cnt, 1u);
-    s_last = (old == gridDim.x - 1) ? 1u : 0u;
-  }
-  __syncthreads();
-  if (s_last && tid == 0) {
-    a.head[bh].cond_cnt = 0u;
+  if (i == 0 && tid == 0) {
     if (a.mode == HARDKV_COND_MERGE) a.cond_cursor[bh] = (int32_t)((nu + E) % C);
     a.pool_head[bh] = c + (int64_t)BK * E;
   }

@@ -4,39 +4,48 @@
 // into contiguous ranges, each head owning a fixed-capacity view (the max-length form
 // of Flatten Index), so that attention reads static, contiguous, fixed-stride blocks.
 //
-// Grid (chunks, B*Hkv), 256 threads.  A wavefront takes one 64-row pool block at a
-// time: the mask word (one bit per row) gives the kept rows; their rank inside the word
-// (mbcnt) plus the block's view offset (from the select stage's scan) gives each row's
-// view row, so the order of positions is preserved.  The kept rows are copied as 16-byte
-// pieces, 16 lanes per row, 16 rows in flight per wavefront.  In the fused step the
-// same kernel also runs the attention of the group's queries over the rows it copies
-// and writes one split-K partial per workgroup, so the view is never read back.
+// Grid (chunks [+ attention segments], B*Hkv), 256 threads.  A wavefront takes one
+// 64-row pool block at a time.  From the block's weights and the head's cut (w_th, r,
+// and the block's ties-before count from the select stage) each lane decides whether its
+// row is kept: w > w_th, or w == w_th and its tie rank (ties before the block plus the
+// mbcnt of equal weights below it) is under r.  The ballot of those bits is the block's
+// mask word.  A kept row's view row is the block's first view row plus the row's rank
+// inside the word, so the order of positions is preserved.  Kept rows are copied as
+// 16-byte pieces, 16 lanes per row, 16 rows in flight per wavefront.
+//
+// In the fused step the kernel also runs the attention of the group's queries over the
+// rows it copies (one split-K partial per workgroup, so the view is never read back),
+// and extra workgroups attend the condensed slots and the dense window.
 #include "attn_common.h"
 
 namespace hardkv {
 
 namespace {
 
-template <typename T, int G, bool ATTN>
+template <typename T, int G, bool MASK, bool COPY, bool ATTN>
 __global__ __launch_bounds__(NTHREADS) void hardkv_rewrite(Args a) {
   constexpr int EB = Elem<T>::bytes;
   constexpr size_t ROWB = (size_t)HD * EB;
   const int bh = blockIdx.y, chunk = blockIdx.x;
+  __shared__ uint8_t s_list[4][64];
+  __shared__ float s_part[ATTN ? 4 : 1][G][2 + HD];
+  if (ATTN && chunk >= a.nch_reg) {  // condensed / dense attention segments
+    attend_segment<T, G>(a, bh, a.nv_att + (chunk - a.nch_reg), s_part);
+    return;
+  }
   const int b = bh / a.Hkv, h = bh - b * a.Hkv;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int sub = lane & 15, grp = lane >> 4;
   const int P = a.P, V = a.V_cap;
 
-  __shared__ uint8_t s_list[4][64];
-  __shared__ float s_part[ATTN ? 4 : 1][G][2 + HD];
-
-  const int64_t t = a.seq_len[b];
-  const int64_t c = a.pool_head[bh];
+  const HeadInfo *hd = a.head + bh;
+  const int64_t t = hd->t_plan, c = hd->c_plan;
+  const uint32_t w_th = hd->w_th, r = hd->r;
+  const int nx = hd->E;
   const int64_t pend = pool_end(t, a.W);
-  const int64_t E = plan_E(pend - c, a.mode, a.S_cap);
-  const int64_t ub_lo = (c + (int64_t)BK * E) / BK, blk_hi = (pend + BK - 1) / BK;
-  const int64_t L0 = ub_lo + (int64_t)chunk * a.cb_reg;
-  const int64_t L1 = min(L0 + (int64_t)a.cb_reg, blk_hi);
+  const int nblk = (int)((pend + BK - 1) / BK - c / BK);
+  const int pb_lo = (int)((c / BK) % P);
+  const int i0 = chunk * a.cb_reg, i1 = min(i0 + a.cb_reg, P);
 
   AttnState<G> st;
   float qs[G][8];
@@ -44,29 +53,37 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_rewrite(Args a) {
     st.init();
     load_q_scaled<T, G>(a, b, h, sub, qs);
   }
-  const char *pk = (const char *)a.pool_k + (size_t)bh * P * BK * ROWB + sub * 8 * EB;
-  const char *pv = (const char *)a.pool_v + (size_t)bh * P * BK * ROWB + sub * 8 * EB;
+  const size_t rowbase = (size_t)bh * P * BK;
+  const char *pk = (const char *)a.pool_k + rowbase * ROWB + sub * 8 * EB;
+  const char *pv = (const char *)a.pool_v + rowbase * ROWB + sub * 8 * EB;
   char *vk = (char *)a.view_k + (size_t)bh * V * ROWB + sub * 8 * EB;
   char *vv = (char *)a.view_v + (size_t)bh * V * ROWB + sub * 8 * EB;
   int32_t *vpos = a.view_pos + (size_t)bh * V;
 
-  const int nl = (int)(L1 - L0);
-  const int pb0 = L0 < L1 ? (int)(L0 % P) : 0;
-  for (int i = wave; i < nl; i += 4) {
-    const int64_t L = L0 + i;
-    const size_t pb = (size_t)(pb0 + i >= P ? pb0 + i - P : pb0 + i);
-    const uint64_t mw = a.mask[(size_t)bh * P + pb];
-    if (mw == 0) continue;  // wave-uniform
-    const uint32_t vo = a.viewoff[(size_t)bh * P + pb];
-    const bool sel = (mw >> lane) & 1ull;
+  for (int i = i0 + wave; i < i1; i += 4) {
+    const int pb = pb_lo + i >= P ? pb_lo + i - P : pb_lo + i;
+    if (i < nx || i >= nblk) {  // condensed this step, or holds no pool position
+      if (MASK && lane == 0) a.mask[(size_t)bh * P + pb] = 0ull;
+      continue;
+    }
+    const int64_t p = c + (int64_t)i * BK + lane;
+    const bool valid = p < pend;
+    const uint32_t w = valid ? a.weights[rowbase + (size_t)pb * BK + lane] : 0u;
+    const uint2 bi = a.blkinfo[(size_t)bh * P + pb];  // (first view row, ties before)
+    const uint64_t eqm = ballot(valid && w == w_th);
+    const bool sel = valid && (w > w_th || (w == w_th && bi.y + popc_below(eqm) < r));
+    const uint64_t mw = ballot(sel);
+    if (MASK && lane == 0) a.mask[(size_t)bh * P + pb] = mw;
+    if (!COPY || mw == 0) continue;  // wave-uniform
+    const uint32_t vo = bi.x;
     const uint32_t idx = popc_below(mw);
     if (sel) {
       s_list[wave][idx] = (uint8_t)lane;
-      if (vo + idx < (uint32_t)V) vpos[vo + idx] = (int32_t)(L * BK + lane);
+      if (vo + idx < (uint32_t)V) vpos[vo + idx] = (int32_t)p;
     }
     wave_sync();
     const int ns = __popcll(mw);
-    const char *pkb = pk + pb * BK * ROWB, *pvb = pv + pb * BK * ROWB;
+    const char *pkb = pk + (size_t)pb * BK * ROWB, *pvb = pv + (size_t)pb * BK * ROWB;
     for (int it = 0; it < ns; it += 16) {
       Raw8<T> kr[4], vr[4];
       bool act[4];
@@ -107,24 +124,31 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_rewrite(Args a) {
   if (ATTN) attn_write_partial<G>(st, a.part + ((size_t)bh * a.npart + chunk) * G * (2 + HD), s_part);
 }
 
-template <typename T, bool ATTN>
+template <typename T, bool MASK, bool COPY, bool ATTN>
 hipError_t launch_g(const Args &a, hipStream_t s) {
-  dim3 grid(a.nch_reg, a.B * a.Hkv);
+  dim3 grid(a.nch_reg + (ATTN ? a.nc_att + a.nd_att : 0), a.B * a.Hkv);
   switch (a.G) {
-    case 1: hipLaunchKernelGGL((hardkv_rewrite<T, 1, ATTN>), grid, dim3(NTHREADS), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((hardkv_rewrite<T, 2, ATTN>), grid, dim3(NTHREADS), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((hardkv_rewrite<T, 4, ATTN>), grid, dim3(NTHREADS), 0, s, a); break;
-    case 8: hipLaunchKernelGGL((hardkv_rewrite<T, 8, ATTN>), grid, dim3(NTHREADS), 0, s, a); break;
+    case 1: hipLaunchKernelGGL((hardkv_rewrite<T, 1, MASK, COPY, ATTN>), grid, dim3(NTHREADS), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((hardkv_rewrite<T, 2, MASK, COPY, ATTN>), grid, dim3(NTHREADS), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((hardkv_rewrite<T, 4, MASK, COPY, ATTN>), grid, dim3(NTHREADS), 0, s, a); break;
+    case 8: hipLaunchKernelGGL((hardkv_rewrite<T, 8, MASK, COPY, ATTN>), grid, dim3(NTHREADS), 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
+template <typename T>
+hipError_t launch_t(const Args &a, hipStream_t s, bool mask, bool copy, bool attend) {
+  if (mask && copy && attend) return launch_g<T, true, true, true>(a, s);
+  if (mask && !copy && !attend) return launch_g<T, true, false, false>(a, s);
+  if (!mask && copy && !attend) return launch_g<T, false, true, false>(a, s);
+  return hipErrorInvalidValue;
+}
+
 }  // namespace
 
-hipError_t launch_regularize(const Args &a, hipStream_t s, bool bf16, bool attend) {
-  if (bf16) return attend ? launch_g<BF16, true>(a, s) : launch_g<BF16, false>(a, s);
-  return attend ? launch_g<F32, true>(a, s) : launch_g<F32, false>(a, s);
+hipError_t launch_rewrite(const Args &a, hipStream_t s, bool bf16, bool mask, bool copy, bool attend) {
+  return bf16 ? launch_t<BF16>(a, s, mask, copy, attend) : launch_t<F32>(a, s, mask, copy, attend);
 }
 
 }  // namespace hardkv

@@ -5,17 +5,25 @@
 // its own budget) and 2.B (max-pooled logits as the importance metric; calibration maps
 // the scores to one softmax by a temperature, keeping their order).
 //
-// One launch, grid (chunks, B*Hkv), 256 threads.  Every workgroup streams a chunk of
-// the head's pool keys with 16-byte loads: 16 lanes hold one 256-byte bf16 row (8
-// elements each), a wavefront covers 4 rows per load.  Each lane forms the pairwise
-// sum of its 8 products in registers (tree levels 1-3); levels 4-7 are DPP exchanges
-// inside the 16-lane row, so every lane ends with the exact tree root.  The score is
-// the max over the G group queries.
+// Two kernels, with the kernel boundary between them as the only synchronization (no
+// cross-workgroup flags: on MI355X each agent-scope release/acquire writes back or
+// invalidates a whole XCD's L2).
 //
-// The last workgroup to finish a head (agent-scope counter) then runs the selection
-// for that head alone: weights from the scores, the exact top-p cut by a three-level
-// radix select weighted by mass on the float bits of w, a scan of per-block counts
-// for the view offsets, and the mask words.  All integer results are exact.
+// hardkv_score, grid (chunks, B*Hkv), 256 threads: streams a chunk of the head's pool
+//   keys with 16-byte loads; 16 lanes hold one 256-byte bf16 row (8 elements each), a
+//   wavefront covers 4 rows per load.  Each lane forms the pairwise sum of its 8
+//   products in registers (tree levels 1-3); levels 4-7 are DPP exchanges inside the
+//   16-lane row, so every lane ends with the exact root.  The score is the max over the
+//   group queries.  Writes the scores and the chunk's maximum.
+//
+// hardkv_select, grid (B*Hkv), 1024 threads: one workgroup per head.  Pass A turns the
+//   scores into integer weights and builds a mass histogram of the survivors on the top
+//   bits of the weight's float encoding; the bucket that holds the cut is found by a
+//   suffix scan.  Pass B counts, per 64-row block, the weights above that bucket and
+//   gathers the bucket's tokens into LDS, where two more histogram levels give the
+//   exact threshold weight w_th and the number r of ties at w_th that are kept (ties go
+//   to the lowest positions).  A scan over blocks gives each block its first view row
+//   and its ties-before count; the rewrite kernel derives the mask bits from them.
 #include "hardkv_internal.h"
 
 namespace hardkv {
@@ -38,274 +46,14 @@ HK_DEV float dot_tree(const float (&q)[8], const float (&k)[8]) {
   return c;
 }
 
-// w = max(1, floor(2^24 * 2^t)), t = (s - m) kappa; 2^t = 2^n * P(f), n = floor(t),
-// f in [0, 1), P the degree-9 Taylor polynomial of 2^f with non-negative terms, so the
-// result never decreases as s grows.
-HK_DEV uint32_t calib_weight(float s, float m, float kap, const float *coeff) {
-  float x = s - m;
-  float t = x * kap;
-  if (!(t >= -60.0f)) return 1u;
-  float n = floorf(t);
-  float f = t - n;
-  float y = coeff[NCOEFF - 1];
-#pragma unroll
-  for (int i = NCOEFF - 2; i >= 0; --i) {
-    float p = y * f;
-    y = p + coeff[i];
-  }
-  float e = ldexpf(y, (int)n);
-  float big = e * 16777216.0f;
-  uint32_t w = (uint32_t)floorf(big);
-  return w < 1u ? 1u : w;
-}
-
-// monotone radix key of a weight: float bits relative to 1.0 (w in [1, 2^24])
-HK_DEV uint32_t wkey(uint32_t w) { return __float_as_uint((float)w) - 0x3F800000u; }
-HK_DEV uint32_t key_to_w(uint32_t k) { return (uint32_t)__uint_as_float(k + 0x3F800000u); }
-
-HK_DEV uint64_t wave_sum_u64(uint64_t v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    uint32_t lo = __shfl_xor((uint32_t)v, off);
-    uint32_t hi = __shfl_xor((uint32_t)(v >> 32), off);
-    v += ((uint64_t)hi << 32) | lo;
-  }
-  return v;
-}
-
 HK_DEV float wave_max(float v) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
   return v;
 }
 
-struct SelShared {
-  unsigned long long hist[NB1];   // mass histogram; later reused as per-block counts
-  unsigned long long scan[NTHREADS];
-  unsigned long long red[8];
-  int res_bucket;
-  unsigned long long res_above;
-  unsigned long long carry;
-};
-
-// block sum of a u64 held by every thread
-HK_DEV uint64_t block_sum_u64(uint64_t v, SelShared &sh) {
-  const int tid = threadIdx.x;
-  v = wave_sum_u64(v);
-  if ((tid & 63) == 0) sh.red[tid >> 6] = v;
-  __syncthreads();
-  uint64_t s = sh.red[0] + sh.red[1] + sh.red[2] + sh.red[3];
-  __syncthreads();
-  return s;
-}
-
-// largest bucket b of hist[0..nb) with sum(hist[b..]) >= target (1 <= target <= total);
-// *above = sum(hist[b+1..]).
-HK_DEV int find_cut(SelShared &sh, int nb, uint64_t target, uint64_t *above) {
-  const int tid = threadIdx.x;
-  const int per = (nb + NTHREADS - 1) / NTHREADS;
-  const int lo = tid * per, hi = min(lo + per, nb);
-  uint64_t mine = 0;
-  for (int i = lo; i < hi; ++i) mine += sh.hist[i];
-  sh.scan[tid] = mine;
-  if (tid == 0) {
-    sh.res_bucket = 0;
-    sh.res_above = 0;
-  }
-  __syncthreads();
-  for (int off = 1; off < NTHREADS; off <<= 1) {  // inclusive suffix sums over threads
-    uint64_t v = (tid + off < NTHREADS) ? sh.scan[tid + off] : 0ull;
-    __syncthreads();
-    sh.scan[tid] += v;
-    __syncthreads();
-  }
-  const uint64_t incl = sh.scan[tid], excl = incl - mine;
-  if (excl < target && incl >= target) {
-    uint64_t acc = excl;
-    for (int i = hi - 1; i >= lo; --i) {
-      if (acc + sh.hist[i] >= target) {
-        sh.res_bucket = i;
-        sh.res_above = acc;
-        break;
-      }
-      acc += sh.hist[i];
-    }
-  }
-  __syncthreads();
-  *above = sh.res_above;
-  int r = sh.res_bucket;
-  __syncthreads();
-  return r;
-}
-
-// the selection of one head, run by its last score workgroup
-HK_DEV void select_head(const Args &a, int bh, int h, int64_t c, int64_t pend, SelShared &sh) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  HeadInfo *hd = a.head + bh;
-  const uint32_t menc = atomic_load_acq(&hd->max_enc);
-  const float m = menc ? ord2f(menc) : 0.0f;
-  __syncthreads();
-  if (tid == 0) {  // every other workgroup of this head is done with the counters
-    hd->max_enc = 0u;
-    hd->score_cnt = 0u;
-  }
-  const int P = a.P;
-  const int64_t N = pend - c;
-  const int64_t E = plan_E(N, a.mode, a.S_cap);
-  const int64_t u0 = c + (int64_t)BK * E;
-  const int64_t blk_lo = c / BK, blk_hi = (pend + BK - 1) / BK, ub_lo = u0 / BK;
-  const int nblk = (int)(blk_hi - blk_lo);   // blocks of the pool, at most P
-  const int nx = (int)(ub_lo - blk_lo);      // condensing blocks, first in age order
-  const int pb_lo = (int)(blk_lo % P);
-  const float kap = a.kappa[h];
-  const size_t rowbase = (size_t)bh * P * BK;
-  auto ring = [&](int i) { int pb = pb_lo + i; return pb >= P ? pb - P : pb; };
-
-  for (int i = tid; i < NB1; i += NTHREADS) sh.hist[i] = 0ull;
-  __syncthreads();
-
-  // pass A: weights of the whole pool, total and survivor mass, level-1 histogram of U
-  uint64_t my_all = 0, my_u = 0;
-  bool bad = false;
-  for (int i = wave; i < nblk; i += 4) {
-    const int64_t p = (blk_lo + i) * BK + lane;
-    if (p < pend) {
-      const size_t row = rowbase + (size_t)ring(i) * BK + lane;
-      const float s = a.scores[row];
-      bad |= !isfinite(s);
-      const uint32_t w = calib_weight(s, m, kap, a.coeff);
-      a.weights[row] = w;
-      my_all += w;
-      if (p >= u0) {
-        my_u += w;
-        atomicAdd(&sh.hist[wkey(w) >> 16], (unsigned long long)w);
-      }
-    }
-  }
-  if (ballot(bad) && lane == 0) atomicOr(a.error_word, HARDKV_ERR_NONFINITE);
-  const uint64_t W_all = block_sum_u64(my_all, sh);
-  const uint64_t W_U = block_sum_u64(my_u, sh);
-  const uint64_t T = ((uint64_t)a.pq * W_U + 65535ull) >> 16;
-
-  uint32_t w_th = 0, r = 0;
-  int64_t kstar = 0;
-  if (W_U > 0) {
-    // levels 2 and 3 of the cut, each over the tokens of the chosen bucket
-    uint64_t above1, above2, above3;
-    const int b1 = find_cut(sh, NB1, T, &above1);
-    for (int i = tid; i < 256; i += NTHREADS) sh.hist[i] = 0ull;
-    __syncthreads();
-    for (int i = wave; i < nblk; i += 4) {
-      const int64_t p = (blk_lo + i) * BK + lane;
-      if (i >= nx && p < pend) {
-        const uint32_t w = a.weights[rowbase + (size_t)ring(i) * BK + lane];
-        const uint32_t k = wkey(w);
-        if ((int)(k >> 16) == b1) atomicAdd(&sh.hist[(k >> 8) & 255u], (unsigned long long)w);
-      }
-    }
-    __syncthreads();
-    const int b2 = find_cut(sh, 256, T - above1, &above2);
-    const uint32_t pre = ((uint32_t)b1 << 8) | (uint32_t)b2;
-    for (int i = tid; i < 256; i += NTHREADS) sh.hist[i] = 0ull;
-    __syncthreads();
-    for (int i = wave; i < nblk; i += 4) {
-      const int64_t p = (blk_lo + i) * BK + lane;
-      if (i >= nx && p < pend) {
-        const uint32_t w = a.weights[rowbase + (size_t)ring(i) * BK + lane];
-        const uint32_t k = wkey(w);
-        if ((k >> 8) == pre) atomicAdd(&sh.hist[k & 255u], (unsigned long long)w);
-      }
-    }
-    __syncthreads();
-    const int b3 = find_cut(sh, 256, T - above1 - above2, &above3);
-    w_th = key_to_w((pre << 8) | (uint32_t)b3);
-    const uint64_t mass_gt = above1 + above2 + above3;
-    r = (uint32_t)((T - mass_gt + w_th - 1) / w_th);
-  }
-
-  // pass D: per-block counts of weights above and at the threshold (LDS, logical order)
-  uint32_t *cnt = reinterpret_cast<uint32_t *>(sh.hist);  // [nU blocks]: gt | eq << 16
-  const int nub = nblk - nx;
-  uint64_t my_gt = 0;
-  if (W_U > 0) {
-    for (int i = wave; i < nblk; i += 4) {
-      if (i < nx) continue;  // wave-uniform
-      const int64_t p = (blk_lo + i) * BK + lane;
-      uint32_t w = 0;
-      if (p < pend) w = a.weights[rowbase + (size_t)ring(i) * BK + lane];
-      const uint64_t gtm = ballot(p < pend && w > w_th);
-      const uint64_t eqm = ballot(p < pend && w == w_th);
-      if (lane == 0) {
-        cnt[i - nx] = (uint32_t)__popcll(gtm) | ((uint32_t)__popcll(eqm) << 16);
-        my_gt += (uint64_t)__popcll(gtm);
-      }
-    }
-  }
-  kstar = (int64_t)block_sum_u64(my_gt, sh) + r;  // (also orders the count writes)
-
-  // pass E: exclusive scan of (gt, eq) over blocks in position order; the view offset of
-  // a block is GT_before + min(EQ_before, r); cnt becomes EQ_before for the mask pass
-  if (tid == 0) sh.carry = 0ull;
-  __syncthreads();
-  for (int base = 0; base < nub; base += NTHREADS) {
-    const int i = base + tid;
-    const uint32_t v = (i < nub) ? cnt[i] : 0u;
-    const uint64_t mine = (uint64_t)(v & 0xffffu) | ((uint64_t)(v >> 16) << 32);
-    sh.scan[tid] = mine;
-    __syncthreads();
-    for (int off = 1; off < NTHREADS; off <<= 1) {
-      uint64_t x = (tid >= off) ? sh.scan[tid - off] : 0ull;
-      __syncthreads();
-      sh.scan[tid] += x;
-      __syncthreads();
-    }
-    const uint64_t before = sh.carry + sh.scan[tid] - mine;
-    const uint64_t total = sh.scan[NTHREADS - 1];
-    __syncthreads();
-    if (i < nub) {
-      const uint32_t gt_b = (uint32_t)before, eq_b = (uint32_t)(before >> 32);
-      a.viewoff[(size_t)bh * P + (size_t)ring(nx + i)] = gt_b + min(eq_b, r);
-      cnt[i] = eq_b;
-    }
-    if (tid == 0) sh.carry += total;
-    __syncthreads();
-  }
-
-  // pass F: mask words of every ring block; zero outside U
-  uint64_t *mask = a.mask + (size_t)bh * P;
-  for (int i = wave; i < P; i += 4) {
-    const size_t pb = (size_t)ring(i);
-    uint64_t word = 0;
-    if (W_U > 0 && i >= nx && i < nblk) {
-      const int64_t p = (blk_lo + i) * BK + lane;
-      uint32_t w = 0;
-      if (p < pend) w = a.weights[rowbase + pb * BK + lane];
-      const bool eq = p < pend && w == w_th;
-      const uint64_t eqm = ballot(eq);
-      const uint32_t rank = cnt[i - nx] + popc_below(eqm);
-      const bool sel = p < pend && (w > w_th || (eq && rank < r));
-      word = ballot(sel);
-    }
-    if (lane == 0) mask[pb] = word;
-  }
-
-  if (tid == 0) {
-    a.budget[bh] = (int32_t)kstar;
-    a.n_condense[bh] = (int32_t)E;
-    a.w_all[bh] = W_all;
-    a.w_u[bh] = W_U;
-    a.thresh[bh] = T;
-    hd->w_th = w_th;
-    hd->r = r;
-    hd->kstar = (int32_t)kstar;
-    hd->E = (int32_t)E;
-    hd->w_all = W_all;
-    if (kstar > a.V_cap) atomicOr(a.error_word, HARDKV_ERR_VIEW_OVERFLOW);
-  }
-}
-
 template <typename T, int G>
-__global__ __launch_bounds__(NTHREADS) void hardkv_score_select(Args a) {
+__global__ __launch_bounds__(NTHREADS) void hardkv_score(Args a) {
   constexpr int EB = Elem<T>::bytes;
   const int bh = blockIdx.y, chunk = blockIdx.x;
   const int b = bh / a.Hkv, h = bh - b * a.Hkv;
@@ -315,8 +63,6 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_score_select(Args a) {
 
   __shared__ float s_stage[4][16];
   __shared__ float s_wmax[4];
-  __shared__ uint32_t s_last;
-  __shared__ SelShared sh;
 
   const int64_t t = a.seq_len[b];
   const int64_t c = a.pool_head[bh];
@@ -332,8 +78,8 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_score_select(Args a) {
     for (int g = 0; g < G; ++g) load8(qb + (size_t)g * HD * EB, qf[g], T{});
     const char *kbase = (const char *)a.pool_k + (size_t)bh * P * BK * HD * EB + sub * 8 * EB;
     float *srow = a.scores + (size_t)bh * P * BK;
-    // row_lo is block aligned; the chunk spans fewer than P blocks, so one subtraction
-    // wraps the ring index
+    // row_lo is block aligned and the chunk spans fewer than P blocks, so one
+    // subtraction wraps the ring index
     const int pb0 = (int)((row_lo / BK) % P);
     const int nrows = (int)(row_hi - row_lo);
     const int ngroups = (nrows + 15) / 16;
@@ -389,29 +135,362 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_score_select(Args a) {
   }
   wmax = wave_max(wmax);
   if (lane == 0) s_wmax[wave] = wmax;
-  fence_agent();  // this thread's score stores are visible to the whole device
   __syncthreads();
+  if (tid == 0)
+    a.cmax[(size_t)bh * a.nch_score + chunk] =
+        fmaxf(fmaxf(s_wmax[0], s_wmax[1]), fmaxf(s_wmax[2], s_wmax[3]));
+}
+
+// ---------------------------------------------------------------------------------------
+// selection
+// ---------------------------------------------------------------------------------------
+
+// w = max(1, floor(2^24 * 2^t)), t = (s - m) kappa; 2^t = 2^n * P(f), n = floor(t),
+// f in [0, 1), P the degree-9 Taylor polynomial of 2^f with non-negative terms, so the
+// result never decreases as s grows.
+HK_DEV uint32_t calib_weight(float s, float m, float kap, const float *coeff) {
+  float x = s - m;
+  float t = x * kap;
+  if (!(t >= -60.0f)) return 1u;
+  float n = floorf(t);
+  float f = t - n;
+  float y = coeff[NCOEFF - 1];
+#pragma unroll
+  for (int i = NCOEFF - 2; i >= 0; --i) {
+    float p = y * f;
+    y = p + coeff[i];
+  }
+  float e = ldexpf(y, (int)n);
+  float big = e * 16777216.0f;
+  uint32_t w = (uint32_t)floorf(big);
+  return w < 1u ? 1u : w;
+}
+
+// monotone radix key of a weight: float bits relative to 1.0 (w in [1, 2^24])
+HK_DEV uint32_t wkey(uint32_t w) { return __float_as_uint((float)w) - 0x3F800000u; }
+HK_DEV uint32_t key_to_w(uint32_t k) { return (uint32_t)__uint_as_float(k + 0x3F800000u); }
+
+HK_DEV uint64_t wave_sum_u64(uint64_t v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    uint32_t lo = __shfl_xor((uint32_t)v, off);
+    uint32_t hi = __shfl_xor((uint32_t)(v >> 32), off);
+    v += ((uint64_t)hi << 32) | lo;
+  }
+  return v;
+}
+
+constexpr int NW = SEL_THREADS / 64;  // wavefronts of the select workgroup
+
+struct SelShared {
+  unsigned long long hist[NB1];        // mass histogram (level 1, then levels 2 and 3)
+  uint32_t blk[MAX_POOL_BLOCKS];       // per survivor block: gt | eq << 16
+  uint32_t cand_w[CAND_CAP];           // weights of the cut bucket's tokens
+  uint32_t cand_i[CAND_CAP];           // their index from the first survivor position
+  unsigned long long scan[SEL_THREADS];
+  unsigned long long red[2][NW];
+  float fred[NW];
+  uint32_t ncand;
+  int res_bucket;
+  unsigned long long res_above;
+  unsigned long long carry;
+};
+
+HK_DEV uint64_t block_sum_u64(uint64_t v, SelShared &sh, int which) {
+  const int tid = threadIdx.x;
+  v = wave_sum_u64(v);
+  if ((tid & 63) == 0) sh.red[which][tid >> 6] = v;
+  __syncthreads();
+  uint64_t s = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) s += sh.red[which][w];
+  return s;
+}
+
+// inclusive suffix sums over threads of a u64 each holds
+HK_DEV uint64_t block_suffix_incl(uint64_t mine, SelShared &sh) {
+  const int tid = threadIdx.x;
+  sh.scan[tid] = mine;
+  __syncthreads();
+  for (int off = 1; off < SEL_THREADS; off <<= 1) {
+    uint64_t v = (tid + off < SEL_THREADS) ? sh.scan[tid + off] : 0ull;
+    __syncthreads();
+    sh.scan[tid] += v;
+    __syncthreads();
+  }
+  uint64_t r = sh.scan[tid];
+  __syncthreads();
+  return r;
+}
+
+// largest bucket b of hist[0..nb) with sum(hist[b..]) >= target (1 <= target <= total);
+// *above = sum(hist[b+1..]).
+HK_DEV int find_cut(SelShared &sh, int nb, uint64_t target, uint64_t *above) {
+  const int tid = threadIdx.x;
+  const int per = (nb + SEL_THREADS - 1) / SEL_THREADS;
+  const int lo = tid * per, hi = min(lo + per, nb);
+  uint64_t mine = 0;
+  for (int i = lo; i < hi; ++i) mine += sh.hist[i];
   if (tid == 0) {
-    const float mx = fmaxf(fmaxf(s_wmax[0], s_wmax[1]), fmaxf(s_wmax[2], s_wmax[3]));
-    if (mx > -INFINITY) atomicMax(&a.head[bh].max_enc, f2ord(mx));
-    fence_agent();
-    const uint32_t old = atomic_add_acq_rel(&a.head[bh].score_cnt, 1u);
-    s_last = (old == gridDim.x - 1) ? 1u : 0u;
+    sh.res_bucket = 0;
+    sh.res_above = 0;
+  }
+  const uint64_t incl = block_suffix_incl(mine, sh), excl = incl - mine;
+  if (excl < target && incl >= target) {
+    uint64_t acc = excl;
+    for (int i = hi - 1; i >= lo; --i) {
+      if (acc + sh.hist[i] >= target) {
+        sh.res_bucket = i;
+        sh.res_above = acc;
+        break;
+      }
+      acc += sh.hist[i];
+    }
   }
   __syncthreads();
-  if (!s_last) return;
-  fence_agent();
-  select_head(a, bh, h, c, pend, sh);
+  *above = sh.res_above;
+  const int r = sh.res_bucket;
+  __syncthreads();
+  return r;
+}
+
+__global__ __launch_bounds__(SEL_THREADS) void hardkv_select(Args a) {
+  const int bh = blockIdx.x;
+  const int b = bh / a.Hkv, h = bh - b * a.Hkv;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int P = a.P;
+  HeadInfo *hd = a.head + bh;
+  extern __shared__ unsigned char smem_raw[];
+  SelShared &sh = *reinterpret_cast<SelShared *>(smem_raw);
+
+  const int64_t t = a.seq_len[b];
+  const int64_t c = a.pool_head[bh];
+  const int64_t pend = pool_end(t, a.W);
+  const int64_t N = pend - c;
+  const int64_t E = plan_E(N, a.mode, a.S_cap);
+  const int64_t u0 = c + (int64_t)BK * E;
+  const int nblk = (int)((pend + BK - 1) / BK - c / BK);  // pool blocks, at most P
+  const int nx = (int)E;                                   // condensing blocks come first
+  const int nub = nblk - nx;                               // survivor blocks
+  const int pb_lo = (int)((c / BK) % P);
+  const float kap = a.kappa[h];
+  const size_t rowbase = (size_t)bh * P * BK;
+  auto ring = [&](int i) {
+    int pb = pb_lo + i;
+    return pb >= P ? pb - P : pb;
+  };
+
+  // m: max of the score workgroups' maxima
+  float mx = -INFINITY;
+  for (int i = tid; i < a.nch_score; i += SEL_THREADS) mx = fmaxf(mx, a.cmax[(size_t)bh * a.nch_score + i]);
+  mx = wave_max(mx);
+  if (lane == 0) sh.fred[wave] = mx;
+  for (int i = tid; i < NB1; i += SEL_THREADS) sh.hist[i] = 0ull;
+  if (tid == 0) sh.ncand = 0;
+  __syncthreads();
+  float m = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) m = fmaxf(m, sh.fred[w]);
+
+  // pass A: weights of the whole pool, total and survivor mass, level-1 histogram of U
+  uint64_t my_all = 0, my_u = 0;
+  bool bad = false;
+  for (int i0 = wave; i0 < nblk; i0 += 4 * NW) {
+    float sv[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = i0 + u * NW;
+      const int64_t p = c + (int64_t)i * BK + lane;
+      sv[u] = (i < nblk && p < pend) ? a.scores[rowbase + (size_t)ring(i) * BK + lane] : 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = i0 + u * NW;
+      const int64_t p = c + (int64_t)i * BK + lane;
+      if (i < nblk && p < pend) {
+        bad |= !isfinite(sv[u]);
+        const uint32_t w = calib_weight(sv[u], m, kap, a.coeff);
+        a.weights[rowbase + (size_t)ring(i) * BK + lane] = w;
+        my_all += w;
+        if (i >= nx) {
+          my_u += w;
+          atomicAdd(&sh.hist[wkey(w) >> 16], (unsigned long long)w);
+        }
+      }
+    }
+  }
+  if (ballot(bad) && lane == 0) atomicOr(a.error_word, HARDKV_ERR_NONFINITE);
+  const uint64_t W_all = block_sum_u64(my_all, sh, 0);
+  const uint64_t W_U = block_sum_u64(my_u, sh, 1);
+  const uint64_t T = ((uint64_t)a.pq * W_U + 65535ull) >> 16;
+
+  uint32_t w_th = 0, r = 0;
+  uint64_t n_gt = 0;
+  if (W_U > 0) {
+    uint64_t above1, above2, above3;
+    const int b1 = find_cut(sh, NB1, T, &above1);
+
+    // pass B: per survivor block, weights above the cut bucket; gather the bucket
+    for (int j0 = wave; j0 < nub; j0 += 4 * NW) {
+      uint32_t wv[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int j = j0 + u * NW;
+        const int64_t p = u0 + (int64_t)j * BK + lane;
+        wv[u] = (j < nub && p < pend) ? a.weights[rowbase + (size_t)ring(nx + j) * BK + lane] : 0u;
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int j = j0 + u * NW;
+        if (j >= nub) break;  // wave-uniform
+        const int64_t p = u0 + (int64_t)j * BK + lane;
+        const bool valid = p < pend;
+        const int kb = (int)(wkey(wv[u]) >> 16);
+        const uint64_t above = ballot(valid && kb > b1);
+        const uint64_t inb = ballot(valid && kb == b1);
+        uint32_t base = 0;
+        if (lane == 0) {
+          sh.blk[j] = (uint32_t)__popcll(above);
+          if (inb) base = atomicAdd(&sh.ncand, (uint32_t)__popcll(inb));
+        }
+        base = __shfl(base, 0);
+        if (valid && kb == b1) {
+          const uint32_t slot = base + popc_below(inb);
+          if (slot < (uint32_t)CAND_CAP) {
+            sh.cand_w[slot] = wv[u];
+            sh.cand_i[slot] = (uint32_t)(j * BK + lane);
+          }
+        }
+      }
+    }
+    __syncthreads();
+    const uint32_t ncand = sh.ncand;
+    if (ncand <= (uint32_t)CAND_CAP) {
+      // levels 2 and 3 over the candidates in LDS
+      for (int i = tid; i < 256; i += SEL_THREADS) sh.hist[i] = 0ull;
+      __syncthreads();
+      for (uint32_t i = tid; i < ncand; i += SEL_THREADS) {
+        const uint32_t w = sh.cand_w[i];
+        atomicAdd(&sh.hist[(wkey(w) >> 8) & 255u], (unsigned long long)w);
+      }
+      __syncthreads();
+      const int b2 = find_cut(sh, 256, T - above1, &above2);
+      const uint32_t pre = ((uint32_t)b1 << 8) | (uint32_t)b2;
+      for (int i = tid; i < 256; i += SEL_THREADS) sh.hist[i] = 0ull;
+      __syncthreads();
+      for (uint32_t i = tid; i < ncand; i += SEL_THREADS) {
+        const uint32_t w = sh.cand_w[i];
+        const uint32_t k = wkey(w);
+        if ((k >> 8) == pre) atomicAdd(&sh.hist[k & 255u], (unsigned long long)w);
+      }
+      __syncthreads();
+      const int b3 = find_cut(sh, 256, T - above1 - above2, &above3);
+      w_th = key_to_w((pre << 8) | (uint32_t)b3);
+      r = (uint32_t)((T - above1 - above2 - above3 + w_th - 1) / w_th);
+      // candidates above w_th and at w_th, per block
+      for (uint32_t i = tid; i < ncand; i += SEL_THREADS) {
+        const uint32_t w = sh.cand_w[i];
+        const uint32_t j = sh.cand_i[i] / BK;
+        if (w > w_th) atomicAdd(&sh.blk[j], 1u);
+        else if (w == w_th) atomicAdd(&sh.blk[j], 1u << 16);
+      }
+    } else {
+      // a bucket too full for LDS (for example many equal weights): levels 2 and 3 and
+      // the per-block counts over the survivors' weights in memory
+      for (int i = tid; i < 256; i += SEL_THREADS) sh.hist[i] = 0ull;
+      __syncthreads();
+      for (int j = wave; j < nub; j += NW) {
+        const int64_t p = u0 + (int64_t)j * BK + lane;
+        if (p < pend) {
+          const uint32_t w = a.weights[rowbase + (size_t)ring(nx + j) * BK + lane];
+          const uint32_t k = wkey(w);
+          if ((int)(k >> 16) == b1) atomicAdd(&sh.hist[(k >> 8) & 255u], (unsigned long long)w);
+        }
+      }
+      __syncthreads();
+      const int b2 = find_cut(sh, 256, T - above1, &above2);
+      const uint32_t pre = ((uint32_t)b1 << 8) | (uint32_t)b2;
+      for (int i = tid; i < 256; i += SEL_THREADS) sh.hist[i] = 0ull;
+      __syncthreads();
+      for (int j = wave; j < nub; j += NW) {
+        const int64_t p = u0 + (int64_t)j * BK + lane;
+        if (p < pend) {
+          const uint32_t w = a.weights[rowbase + (size_t)ring(nx + j) * BK + lane];
+          const uint32_t k = wkey(w);
+          if ((k >> 8) == pre) atomicAdd(&sh.hist[k & 255u], (unsigned long long)w);
+        }
+      }
+      __syncthreads();
+      const int b3 = find_cut(sh, 256, T - above1 - above2, &above3);
+      w_th = key_to_w((pre << 8) | (uint32_t)b3);
+      r = (uint32_t)((T - above1 - above2 - above3 + w_th - 1) / w_th);
+      for (int j = wave; j < nub; j += NW) {
+        const int64_t p = u0 + (int64_t)j * BK + lane;
+        uint32_t w = 0;
+        if (p < pend) w = a.weights[rowbase + (size_t)ring(nx + j) * BK + lane];
+        const uint64_t gtm = ballot(p < pend && w > w_th);
+        const uint64_t eqm = ballot(p < pend && w == w_th);
+        if (lane == 0) sh.blk[j] = (uint32_t)__popcll(gtm) | ((uint32_t)__popcll(eqm) << 16);
+      }
+    }
+    __syncthreads();
+
+    // scan over survivor blocks in position order: first view row GT_before +
+    // min(EQ_before, r), and EQ_before for the tie ranks of the mask bits
+    if (tid == 0) sh.carry = 0ull;
+    __syncthreads();
+    for (int base = 0; base < nub; base += SEL_THREADS) {
+      const int i = base + tid;
+      const uint32_t v = (i < nub) ? sh.blk[i] : 0u;
+      const uint64_t mine = (uint64_t)(v & 0xffffu) | ((uint64_t)(v >> 16) << 32);
+      sh.scan[tid] = mine;
+      __syncthreads();
+      for (int off = 1; off < SEL_THREADS; off <<= 1) {
+        uint64_t x = (tid >= off) ? sh.scan[tid - off] : 0ull;
+        __syncthreads();
+        sh.scan[tid] += x;
+        __syncthreads();
+      }
+      const uint64_t before = sh.carry + sh.scan[tid] - mine;
+      const uint64_t total = sh.scan[SEL_THREADS - 1];
+      __syncthreads();
+      if (i < nub) {
+        const uint32_t gt_b = (uint32_t)before, eq_b = (uint32_t)(before >> 32);
+        a.blkinfo[(size_t)bh * P + ring(nx + i)] = make_uint2(gt_b + min(eq_b, r), eq_b);
+      }
+      if (tid == 0) sh.carry += total;
+      __syncthreads();
+    }
+    n_gt = sh.carry & 0xffffffffull;
+  }
+
+  if (tid == 0) {
+    const int64_t kstar = (int64_t)n_gt + r;
+    a.budget[bh] = (int32_t)kstar;
+    a.n_condense[bh] = (int32_t)E;
+    a.w_all[bh] = W_all;
+    a.w_u[bh] = W_U;
+    a.thresh[bh] = T;
+    hd->t_plan = t;
+    hd->c_plan = c;
+    hd->w_th = w_th;
+    hd->r = r;
+    hd->kstar = (int32_t)kstar;
+    hd->E = (int32_t)E;
+    hd->nu_plan = a.cond_cursor[bh];
+    hd->w_all = W_all;
+    if (kstar > a.V_cap) atomicOr(a.error_word, HARDKV_ERR_VIEW_OVERFLOW);
+  }
 }
 
 template <typename T>
-hipError_t launch_g(const Args &a, hipStream_t s) {
+hipError_t launch_score_g(const Args &a, hipStream_t s) {
   dim3 grid(a.nch_score, a.B * a.Hkv);
   switch (a.G) {
-    case 1: hipLaunchKernelGGL((hardkv_score_select<T, 1>), grid, dim3(NTHREADS), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((hardkv_score_select<T, 2>), grid, dim3(NTHREADS), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((hardkv_score_select<T, 4>), grid, dim3(NTHREADS), 0, s, a); break;
-    case 8: hipLaunchKernelGGL((hardkv_score_select<T, 8>), grid, dim3(NTHREADS), 0, s, a); break;
+    case 1: hipLaunchKernelGGL((hardkv_score<T, 1>), grid, dim3(NTHREADS), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((hardkv_score<T, 2>), grid, dim3(NTHREADS), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((hardkv_score<T, 4>), grid, dim3(NTHREADS), 0, s, a); break;
+    case 8: hipLaunchKernelGGL((hardkv_score<T, 8>), grid, dim3(NTHREADS), 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -419,8 +498,20 @@ hipError_t launch_g(const Args &a, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_score_select(const Args &a, hipStream_t s, bool bf16) {
-  return bf16 ? launch_g<BF16>(a, s) : launch_g<F32>(a, s);
+hipError_t launch_score(const Args &a, hipStream_t s, bool bf16) {
+  return bf16 ? launch_score_g<BF16>(a, s) : launch_score_g<F32>(a, s);
+}
+
+hipError_t launch_select(const Args &a, hipStream_t s) {
+  static bool configured = false;  // the attribute is per function, set once per process
+  if (!configured) {
+    hipError_t e = hipFuncSetAttribute((const void *)hardkv_select,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(SelShared));
+    if (e != hipSuccess) return e;
+    configured = true;
+  }
+  hipLaunchKernelGGL(hardkv_select, dim3(a.B * a.Hkv), dim3(SEL_THREADS), sizeof(SelShared), s, a);
+  return hipGetLastError();
 }
 
 }  // namespace hardkv

@@ -32,7 +32,7 @@ def test_workspace_sizes_and_stage_names():
     for wl in WORKLOADS.values():
         assert hk.hardkv_workspace_size(hk.Config.from_workload(wl)) > 0
     assert hk.hardkv_step_num_stages() == 6
-    assert [hk.hardkv_step_stage_name(i) for i in range(6)][1] == "score_select"
+    assert [hk.hardkv_step_stage_name(i) for i in range(6)] == ["append", "score", "select", "condense", "rewrite_attend", "combine"]
     assert hk.strerror(-3) == "capacity too small"
 
 

@@ -4,9 +4,16 @@ seeded inputs and compare every output to the required bar.
 Integer and layout outputs (scores, weights, masks, budgets, view rows and
 positions, counters) must be bit-identical.  Condensed sums must agree to 1e-4 and
 attention outputs to 2e-3, each measured per row as max |x - ref| / max |ref|.
+
+The oracle runs either on the whole layer, or on a sample of (sequence, KV head)
+units, each as a batch-1, one-KV-head layer with that unit's inputs (units are
+independent), in parallel host threads.
 """
 
 from __future__ import annotations
+
+import concurrent.futures as cf
+import os
 
 import numpy as np
 import torch
@@ -17,14 +24,7 @@ from synth import make_inputs
 
 ATT_TOL = 2e-3
 COND_TOL = 1e-4
-
-
-def u32(t: torch.Tensor) -> np.ndarray:
-    return t.cpu().numpy().view(np.uint32)
-
-
-def u64(t: torch.Tensor) -> np.ndarray:
-    return t.cpu().numpy().view(np.uint64)
+_POOL = cf.ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 1))
 
 
 def raw(t: torch.Tensor) -> np.ndarray:
@@ -36,40 +36,46 @@ def row_rel_err(x: np.ndarray, ref: np.ndarray) -> float:
     """max over rows of max_i |x_i - ref_i| / max_i |ref_i| (last axis is the row)."""
     x = x.astype(np.float64).reshape(-1, x.shape[-1])
     ref = ref.astype(np.float64).reshape(-1, ref.shape[-1])
+    if not x.size:
+        return 0.0
     den = np.maximum(np.abs(ref).max(axis=1), 1e-30)
-    return float((np.abs(x - ref).max(axis=1) / den).max()) if x.size else 0.0
+    return float((np.abs(x - ref).max(axis=1) / den).max())
 
 
 class Pair:
-    """A GPU state and an oracle state of the same layer, fed the same inputs."""
+    """A GPU state and oracle state(s) of the same layer, fed the same inputs."""
 
     def __init__(self, wl, inputs=None, top_p=None, tau=None, cond_mode=None, merge_bias=True,
-                 device="cuda", oracle_units=None):
+                 device="cuda", oracle_units=None, layer=0):
         self.wl = wl if cond_mode is None else wl.with_(cond_mode=cond_mode)
         if top_p is not None:
             self.wl = self.wl.with_(top_p=top_p)
-        self.inp = inputs if inputs is not None else make_inputs(self.wl, device=device)
-        tau_list = [self.wl.tau] * self.wl.num_kv_heads if tau is None else list(tau)
-        self.cfg = hk.Config.from_workload(self.wl, tau=tau_list, merge_bias=merge_bias)
+        self.inp = inputs if inputs is not None else make_inputs(self.wl, layer=layer, device=device)
+        self.tau = [self.wl.tau] * self.wl.num_kv_heads if tau is None else list(tau)
+        self.cfg = hk.Config.from_workload(self.wl, tau=self.tau, merge_bias=merge_bias)
         self.st = hk.State(self.cfg, device=device)
         hk.hardkv_prefill(self.cfg, self.st, self.inp.k_ctx, self.inp.v_ctx, self.inp.ctx_len)
-        # the oracle runs on every unit, or on a sample of (b, h) units as 1x1 layers
         self.units = oracle_units
-        self.cpu = self.inp.to("cpu") if oracle_units is None else None
         self.orcs = {}
         if oracle_units is None:
-            o = orc.Oracle(self.wl, tau=np.asarray(tau_list, np.float32), merge_bias=merge_bias)
-            assert o.prefill(self.cpu.k_ctx, self.cpu.v_ctx, self.cpu.ctx_len) == 0
-            self.orcs[None] = (o, self.cpu)
+            cpu = self.inp.to("cpu")
+            o = orc.Oracle(self.wl, tau=np.asarray(self.tau, np.float32), merge_bias=merge_bias)
+            assert o.prefill(cpu.k_ctx, cpu.v_ctx, cpu.ctx_len) == 0
+            self.orcs[None] = (o, cpu)
         else:
             for (b, h) in oracle_units:
                 ui = self.inp.unit(b, h).to("cpu")
-                o = orc.Oracle(ui.wl, tau=np.asarray(tau_list[h:h + 1], np.float32), merge_bias=merge_bias)
+                ui.wl = self.wl.with_(batch=1, num_kv_heads=1, num_q_heads=self.wl.group)
+                o = orc.Oracle(ui.wl, tau=np.asarray(self.tau[h:h + 1], np.float32), merge_bias=merge_bias)
                 assert o.prefill(ui.k_ctx, ui.v_ctx, ui.ctx_len) == 0
                 self.orcs[(b, h)] = (o, ui)
         self.out = torch.zeros((self.wl.batch, self.wl.num_q_heads, self.wl.head_dim),
                                dtype=torch.float32, device=device)
         self.step_i = 0
+
+    def drop_context(self):
+        """Frees the prefilled context on the device once both sides hold it."""
+        self.inp.k_ctx = self.inp.v_ctx = None
 
     # ---- stepping --------------------------------------------------------------------------
     def gpu_step(self, fused=True):
@@ -86,83 +92,160 @@ class Pair:
 
     def oracle_step(self, attend=True):
         s = self.step_i
-        res = {}
-        for key, (o, ui) in self.orcs.items():
-            res[key] = o.step(ui.q[s], ui.k_new[s], ui.v_new[s], attend=attend)
-        return res
 
-    def step(self, fused=True, attend=True, check=True, check_attend=True):
-        pre = {k: (o.pool_head.copy(), o.seq_len.copy()) for k, (o, _) in self.orcs.items()}
+        def run(item):
+            key, (o, ui) = item
+            return key, o.step(ui.q[s], ui.k_new[s], ui.v_new[s], attend=attend,
+                               nthreads=0 if key is None else 1)
+        return dict(_POOL.map(run, list(self.orcs.items())))
+
+    def step(self, fused=True, attend=True, check=True, check_attend=True, check_views=True):
+        pre = {k: o.pool_head.copy() for k, (o, _) in self.orcs.items()}
         self.gpu_step(fused)
         outs = self.oracle_step(attend)
         torch.cuda.synchronize()
         if check:
-            self.compare(pre, outs if (attend and check_attend) else None)
+            self.compare(pre, outs if (attend and check_attend) else None, check_views)
         self.step_i += 1
 
     # ---- comparison --------------------------------------------------------------------------
-    def compare(self, pre, outs):
-        st = self.st
-        P = self.wl.P_blk
-        g = {n: t.cpu() for n, t in st.tensors().items() if n != "workspace"}
+    def _gpu_unit(self, b, h, names):
+        return {n: getattr(self.st, n)[b, h].cpu() for n in names}
+
+    def compare(self, pre, outs, check_views=True):
+        wl, P = self.wl, self.wl.P_blk
+        small = {n: getattr(self.st, n).cpu() for n in (
+            "seq_len", "budget", "n_condense", "cond_cursor", "pool_head", "w_all", "w_u", "thresh",
+            "error_word")}
+        big_names = ["scores", "weights", "mask", "cond_n", "cond_kn", "cond_vn", "cond_omega"]
+        if check_views:
+            big_names += ["view_pos", "view_k", "view_v"]
+        full = None
+        if None in self.orcs:
+            full = {n: getattr(self.st, n).cpu() for n in big_names}
+        err = 0
         for key, (o, ui) in self.orcs.items():
-            c_before = pre[key][0]
-            if key is None:
-                units = [(b, h) for b in range(self.wl.batch) for h in range(self.wl.num_kv_heads)]
-                sel = lambda arr, b, h: arr[b, h]  # noqa: E731
-                ob = lambda arr, b, h: arr[b, h]   # noqa: E731
-            else:
-                units = [key]
-                sel = lambda arr, b, h: arr[b, h]  # noqa: E731
-                ob = lambda arr, b, h: arr[0, 0]   # noqa: E731
+            err |= o.error_word
+            units = ([(b, h) for b in range(wl.batch) for h in range(wl.num_kv_heads)]
+                     if key is None else [key])
             for (b, h) in units:
+                ob, oh = (b, h) if key is None else (0, 0)
                 tag = f"step {self.step_i} unit (b={b}, h={h})"
-                assert int(g["seq_len"][b]) == int(o.seq_len[0 if key else b]), tag
-                for name in ("budget", "n_condense", "cond_cursor"):
-                    assert int(sel(g[name], b, h)) == int(ob(getattr(o, name), b, h)), f"{tag} {name}"
-                assert int(sel(g["pool_head"], b, h)) == int(ob(o.pool_head, b, h)), f"{tag} pool_head"
+                g = {n: full[n][b, h] for n in big_names} if full is not None else self._gpu_unit(b, h, big_names)
+                assert int(small["seq_len"][b]) == int(o.seq_len[ob]), tag
+                for name in ("budget", "n_condense", "cond_cursor", "pool_head"):
+                    assert int(small[name][b, h]) == int(getattr(o, name)[ob, oh]), f"{tag} {name}"
                 for name in ("w_all", "w_u", "thresh"):
-                    assert int(sel(g[name].numpy().view(np.uint64), b, h)) == int(ob(getattr(o, name), b, h)), f"{tag} {name}"
-                # scores and weights on the rows of the pool before condensation
-                t = int(g["seq_len"][b])
-                pend = max(0, t - self.wl.dense_window)
-                c0 = int(ob(c_before, b, h)) if key is None else int(c_before[0, 0])
+                    gv = int(small[name][b, h].numpy().view(np.uint64))
+                    assert gv == int(getattr(o, name)[ob, oh]), f"{tag} {name}"
+                t = int(small["seq_len"][b])
+                pend = max(0, t - wl.dense_window)
+                c0 = int(pre[key][ob, oh])
                 pos = np.arange(c0, pend)
                 rows = (pos // 64) % P * 64 + pos % 64
-                gs = sel(g["scores"].numpy(), b, h)[rows].view(np.uint32)
-                os_ = ob(o.scores, b, h)[rows].view(np.uint32)
+                gs = g["scores"].numpy()[rows].view(np.uint32)
+                os_ = o.scores[ob, oh][rows].view(np.uint32)
                 if not np.array_equal(gs, os_):
                     bad = np.nonzero(gs != os_)[0][:5]
                     raise AssertionError(f"{tag} scores differ at positions {pos[bad]}: "
                                          f"{gs[bad].view(np.float32)} vs {os_[bad].view(np.float32)}")
-                gw = sel(g["weights"].numpy().view(np.uint32), b, h)[rows]
-                assert np.array_equal(gw, ob(o.weights, b, h)[rows]), f"{tag} weights"
-                gm = sel(g["mask"].numpy().view(np.uint64), b, h)
-                assert np.array_equal(gm, ob(o.mask, b, h)), f"{tag} mask"
-                k = int(sel(g["budget"], b, h))
-                kv = min(k, self.wl.V_cap)
-                assert np.array_equal(sel(g["view_pos"].numpy(), b, h)[:kv], ob(o.view_pos, b, h)[:kv]), f"{tag} view_pos"
-                assert np.array_equal(raw(sel(g["view_k"], b, h)[:kv]), ob(o.view_k, b, h)[:kv]), f"{tag} view_k"
-                assert np.array_equal(raw(sel(g["view_v"], b, h)[:kv]), ob(o.view_v, b, h)[:kv]), f"{tag} view_v"
-                assert np.array_equal(sel(g["cond_n"].numpy(), b, h), ob(o.cond_n, b, h)), f"{tag} cond_n"
-                # condensed sums
-                on = ob(o.cond_n, b, h) > 0
+                assert np.array_equal(g["weights"].numpy().view(np.uint32)[rows], o.weights[ob, oh][rows]), f"{tag} weights"
+                assert np.array_equal(g["mask"].numpy().view(np.uint64), o.mask[ob, oh]), f"{tag} mask"
+                k = int(small["budget"][b, h])
+                kv = min(k, wl.V_cap)
+                if check_views:
+                    assert np.array_equal(g["view_pos"].numpy()[:kv], o.view_pos[ob, oh][:kv]), f"{tag} view_pos"
+                    assert np.array_equal(raw(g["view_k"][:kv]), o.view_k[ob, oh][:kv]), f"{tag} view_k"
+                    assert np.array_equal(raw(g["view_v"][:kv]), o.view_v[ob, oh][:kv]), f"{tag} view_v"
+                assert np.array_equal(g["cond_n"].numpy(), o.cond_n[ob, oh]), f"{tag} cond_n"
+                on = o.cond_n[ob, oh] > 0
                 if on.any():
-                    for gn, on_name in (("cond_kn", "cond_kn"), ("cond_vn", "cond_vn")):
-                        e = row_rel_err(sel(g[gn].numpy(), b, h)[on], ob(getattr(o, on_name), b, h)[on])
-                        assert e <= COND_TOL, f"{tag} {gn} rel err {e}"
-                    e = row_rel_err(sel(g["cond_omega"].numpy(), b, h)[on][None], ob(o.cond_omega, b, h)[on][None])
+                    for n in ("cond_kn", "cond_vn"):
+                        e = row_rel_err(g[n].numpy()[on], getattr(o, n)[ob, oh][on])
+                        assert e <= COND_TOL, f"{tag} {n} rel err {e}"
+                    e = row_rel_err(g["cond_omega"].numpy()[on][None], o.cond_omega[ob, oh][on][None])
                     assert e <= COND_TOL, f"{tag} omega rel err {e}"
                 if outs is not None:
-                    G = self.wl.group
+                    G = wl.group
                     go = self.out[b, h * G:(h + 1) * G].cpu().numpy()
                     oo = outs[key][b, h * G:(h + 1) * G] if key is None else outs[key][0]
                     e = row_rel_err(go, oo)
                     assert e <= ATT_TOL, f"{tag} attention rel err {e}"
-        assert int(g["error_word"][0]) == self.orcs_error(), "error word"
+        if None in self.orcs:
+            assert int(small["error_word"][0]) == err, "error word"
+        else:
+            assert int(small["error_word"][0]) & err == err, "error word"
 
-    def orcs_error(self):
-        e = 0
-        for o, _ in self.orcs.values():
-            e |= o.error_word
-        return e
+
+_POPC8 = None
+
+
+def check_layer_properties(pr: Pair) -> None:
+    """Properties of the selection that hold at any size, checked on the device for every
+    unit of the layer after a step (no oracle needed):
+      * popcount(mask) == k*, and the mask holds survivor positions only;
+      * the kept mass reaches T and dropping the lightest kept token falls below it
+        (the minimal prefix of top-p);
+      * no dropped survivor outweighs a kept one, and among tokens of the threshold weight
+        the kept ones precede the dropped ones (ties to the lower position);
+      * view_pos lists the kept positions in increasing order and every view row is a bit
+        copy of its pool row."""
+    global _POPC8
+    st, wl = pr.st, pr.wl
+    dev = st.mask.device
+    if _POPC8 is None or _POPC8.device != dev:
+        _POPC8 = torch.tensor([bin(i).count("1") for i in range(256)], dtype=torch.int64, device=dev)
+    B, H, P = wl.batch, wl.num_kv_heads, wl.P_blk
+    BH = B * H
+    mask = st.mask.reshape(BH, P)
+    budget = st.budget.reshape(BH).long()
+    pc = _POPC8[mask.view(torch.uint8).long()].sum(1)
+    assert torch.equal(pc, budget), "popcount(mask) != k*"
+    bits = ((mask.view(torch.uint8).reshape(BH, P * 8, 1).long() >> torch.arange(8, device=dev)) & 1)
+    bits = bits.reshape(BH, P * 64).bool()
+    w = st.weights.reshape(BH, P * 64).long() & 0xFFFFFFFF
+    t = st.seq_len.repeat_interleave(H).long()
+    c = st.pool_head.reshape(BH).long()               # after condensation: first survivor
+    pend = torch.clamp(t - wl.dense_window, min=0)
+    ring = torch.arange(P * 64, device=dev)
+    pb_lo = (c // 64) % P
+    blk_off = (ring[None, :] // 64 - pb_lo[:, None]) % P
+    pos = c[:, None] + blk_off * 64 + ring[None, :] % 64
+    in_u = pos < pend[:, None]
+    assert not (bits & ~in_u).any(), "mask bit outside the survivors"
+    T = st.thresh.reshape(BH).long()
+    wsel = torch.where(bits, w, torch.zeros_like(w))
+    mass = wsel.sum(1)
+    has = budget > 0
+    big = torch.full_like(w, 1 << 40)
+    wmin_sel = torch.where(bits, w, big).min(1).values
+    assert torch.all(mass[has] >= T[has]), "kept mass below T"
+    assert torch.all(mass[has] - wmin_sel[has] < T[has]), "kept set not minimal"
+    drop = in_u & ~bits
+    wmax_drop = torch.where(drop, w, torch.full_like(w, -1)).max(1).values
+    assert torch.all(wmax_drop[has] <= wmin_sel[has]), "a dropped survivor outweighs a kept token"
+    at_th = w == wmin_sel[:, None]
+    pos_big = torch.full_like(pos, 1 << 62)
+    last_kept_tie = torch.where(bits & at_th, pos, torch.full_like(pos, -1)).max(1).values
+    first_drop_tie = torch.where(drop & at_th, pos, pos_big).min(1).values
+    assert torch.all(last_kept_tie[has] < first_drop_tie[has]), "ties not taken by lower position"
+    # view: increasing positions, rows bit-equal to the pool rows
+    V = wl.V_cap
+    vpos = st.view_pos.reshape(BH, V).long()
+    r = torch.arange(V, device=dev)
+    live = r[None, :] < budget[:, None]
+    d = vpos[:, 1:] - vpos[:, :-1]
+    assert torch.all((d > 0) | ~live[:, 1:]), "view positions not increasing"
+    sel_pos = torch.where(bits, pos, pos_big).sort(1).values[:, :V]
+    assert torch.equal(torch.where(live, vpos, 0), torch.where(live, sel_pos, 0)), "view_pos != kept positions"
+    vrow = ((vpos // 64) % P) * 64 + vpos % 64
+    for name_v, name_p in (("view_k", "pool_k"), ("view_v", "pool_v")):
+        view = getattr(st, name_v).reshape(BH, V, -1)
+        pool = getattr(st, name_p).reshape(BH, P * 64, -1)
+        for u0 in range(0, BH, 32):
+            u1 = min(BH, u0 + 32)
+            idx = torch.where(live[u0:u1], vrow[u0:u1], 0)
+            src = torch.gather(pool[u0:u1], 1, idx[:, :, None].expand(-1, -1, pool.shape[-1]))
+            ok = (src.view(torch.int16) == view[u0:u1].view(torch.int16)) if src.dtype == torch.bfloat16 \
+                else (src.view(torch.int32) == view[u0:u1].view(torch.int32))
+            assert torch.all(ok.all(-1) | ~live[u0:u1]), f"{name_v} rows differ from the pool"

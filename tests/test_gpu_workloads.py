@@ -1,0 +1,98 @@
+"""Parity on the five benchmark workloads at their full sizes, with the kernels and
+launch geometry bench.py times.  Small layers are compared with the oracle on every
+(sequence, KV head) unit; large ones on a sample of units run by the oracle one by one,
+and on every unit through properties that hold at any size."""
+
+import numpy as np
+import pytest
+import torch
+
+from synth import get_workload
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    from decode_kv_cache_02_amd import hardkv as hk
+    hk.require_gpu()
+    yield
+    torch.cuda.empty_cache()
+
+
+def _sample_units(wl, n, seed, lens=None):
+    rng = np.random.default_rng(seed)
+    units = {(0, 0), (wl.batch - 1, wl.num_kv_heads - 1)}
+    if lens is not None:  # the shortest and the longest sequences
+        units |= {(int(np.argmin(lens)), 1 % wl.num_kv_heads), (int(np.argmax(lens)), 2 % wl.num_kv_heads)}
+    while len(units) < min(n, wl.batch * wl.num_kv_heads):
+        units.add((int(rng.integers(wl.batch)), int(rng.integers(wl.num_kv_heads))))
+    return sorted(units)
+
+
+def test_c1_full_layer():
+    """Batch 1, fp32, 4096-token context with 16 planted heavy keys per head."""
+    from parity import Pair, check_layer_properties
+    wl = get_workload("c1").with_(steps=3)
+    print("workload", wl.name, flush=True)
+    pr = Pair(wl)
+    for _ in range(wl.steps):
+        pr.step()
+        check_layer_properties(pr)
+
+
+def test_c2_full_layer():
+    """Batch 16, 16k context, per-head query temperature in [0.3, 3], p = 0.95."""
+    from parity import Pair, check_layer_properties
+    wl = get_workload("c2").with_(steps=2)
+    print("workload", wl.name, flush=True)
+    pr = Pair(wl)
+    for _ in range(wl.steps):
+        pr.step()
+        check_layer_properties(pr)
+
+
+@pytest.mark.parametrize("p", [0.8, 0.9, 0.99])
+def test_c3_mixed_lengths(p):
+    """Batch 64, lengths 8k..32k, 0..64 heavy keys per head, the first step condenses up
+    to 377 blocks per head into 256 slots (ring wrap)."""
+    from parity import Pair, check_layer_properties
+    wl = get_workload("c3")
+    print("workload", wl.name, "p", p, flush=True)
+    from synth import make_inputs
+    inp = make_inputs(wl, device="cuda")
+    lens = inp.ctx_len.cpu().numpy()
+    pr = Pair(wl, inputs=inp, top_p=p, oracle_units=_sample_units(wl, 24, 3, lens))
+    pr.drop_context()
+    pr.step()
+    check_layer_properties(pr)
+    assert int(pr.st.n_condense.max()) > 256  # the condensed ring wrapped
+
+
+def test_c4_streaming_256_steps():
+    """Batch 4, 128k context, 256 decode steps; blocks condense at steps 1, 65, 129, 193."""
+    from parity import Pair, check_layer_properties
+    wl = get_workload("c4")
+    print("workload", wl.name, flush=True)
+    pr = Pair(wl, oracle_units=[(0, 0), (1, 3), (2, 5), (3, 7)])
+    pr.drop_context()
+    sampled = {0, 1, 63, 64, 65, 128, 200, 255}
+    for s in range(wl.steps):
+        full = s in sampled
+        pr.step(attend=full, check_attend=full, check_views=full)
+        if full:
+            check_layer_properties(pr)
+            print("step", s, "ok", flush=True)
+    assert int(pr.st.seq_len[0]) == 131072 + 256
+
+
+@pytest.mark.parametrize("layer", [0, 17, 31])
+def test_c5_layers(layer):
+    """Layers of the 32-layer batch-32, 16k-context step (each layer is independent)."""
+    from parity import Pair, check_layer_properties
+    wl = get_workload("c5")
+    print("workload", wl.name, "layer", layer, flush=True)
+    pr = Pair(wl, layer=layer, oracle_units=_sample_units(wl, 12, 50 + layer))
+    pr.drop_context()
+    pr.step()
+    check_layer_properties(pr)

@@ -158,8 +158,8 @@ HK_DEV void attend_segment(const Args &a, int bh, int seg, float (*s_part)[G][2 
         const int64_t r = base + j * 16 + rloc;
         act[j] = r < r1;
         if (act[j]) {
-          raw_load(vk + (size_t)r * ROWB, kr[j]);
-          raw_load(vv + (size_t)r * ROWB, vr[j]);
+          raw_load_nt(vk + (size_t)r * ROWB, kr[j]);
+          raw_load_nt(vv + (size_t)r * ROWB, vr[j]);
         } else {
           kr[j] = Raw8<T>{};
           vr[j] = Raw8<T>{};
@@ -213,8 +213,8 @@ HK_DEV void attend_segment(const Args &a, int bh, int seg, float (*s_part)[G][2 
         act[j] = p < p1;
         if (act[j]) {
           const size_t row = (size_t)(p % a.W);
-          raw_load(dk + row * ROWB, kr[j]);
-          raw_load(dv + row * ROWB, vr[j]);
+          raw_load_nt(dk + row * ROWB, kr[j]);
+          raw_load_nt(dv + row * ROWB, vr[j]);
         } else {
           kr[j] = Raw8<T>{};
           vr[j] = Raw8<T>{};

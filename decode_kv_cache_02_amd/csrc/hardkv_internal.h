@@ -118,6 +118,26 @@ template <typename T> struct Raw8;
 template <> struct Raw8<BF16> { uint4 v; };
 template <> struct Raw8<F32> { float4 a, b; };
 
+// Streaming accesses: keys and values are read once per step and view rows written once,
+// so they bypass cache retention (non-temporal), which raises sustained HBM bandwidth.
+typedef unsigned int v4u32 __attribute__((ext_vector_type(4)));
+HK_DEV uint4 nt_load16(const void *p) {
+  return __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const v4u32 *>(p)));
+}
+HK_DEV void nt_store16(void *p, uint4 v) {
+  __builtin_nontemporal_store(__builtin_bit_cast(v4u32, v), reinterpret_cast<v4u32 *>(p));
+}
+HK_DEV void raw_load_nt(const void *p, Raw8<BF16> &r) { r.v = nt_load16(p); }
+HK_DEV void raw_load_nt(const void *p, Raw8<F32> &r) {
+  r.a = __builtin_bit_cast(float4, nt_load16(p));
+  r.b = __builtin_bit_cast(float4, nt_load16((const char *)p + 16));
+}
+HK_DEV void raw_store_nt(void *p, const Raw8<BF16> &r) { nt_store16(p, r.v); }
+HK_DEV void raw_store_nt(void *p, const Raw8<F32> &r) {
+  nt_store16(p, __builtin_bit_cast(uint4, r.a));
+  nt_store16((char *)p + 16, __builtin_bit_cast(uint4, r.b));
+}
+
 HK_DEV void raw_load(const void *p, Raw8<BF16> &r) { r.v = *reinterpret_cast<const uint4 *>(p); }
 HK_DEV void raw_load(const void *p, Raw8<F32> &r) {
   r.a = reinterpret_cast<const float4 *>(p)[0];

@@ -95,8 +95,8 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_rewrite(Args a) {
         act[j] = k < ns && dst[j] < (uint32_t)V;
         const int row = s_list[wave][k < ns ? k : 0];
         if (act[j]) {
-          raw_load(pkb + (size_t)row * ROWB, kr[j]);
-          raw_load(pvb + (size_t)row * ROWB, vr[j]);
+          raw_load_nt(pkb + (size_t)row * ROWB, kr[j]);
+          raw_load_nt(pvb + (size_t)row * ROWB, vr[j]);
         } else {
           kr[j] = Raw8<T>{};
           vr[j] = Raw8<T>{};
@@ -105,8 +105,8 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_rewrite(Args a) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         if (act[j]) {
-          raw_store(vk + (size_t)dst[j] * ROWB, kr[j]);
-          raw_store(vv + (size_t)dst[j] * ROWB, vr[j]);
+          raw_store_nt(vk + (size_t)dst[j] * ROWB, kr[j]);
+          raw_store_nt(vv + (size_t)dst[j] * ROWB, vr[j]);
         }
       }
       if (ATTN) {

@@ -30,7 +30,7 @@ namespace hardkv {
 
 namespace {
 
-constexpr int UNR = 4;  // row groups (16 rows) in flight per wavefront
+constexpr int UNR = 2;  // row groups (16 rows) per batch of loads
 
 // score of one row from this lane's 8 elements: pairwise tree over the 128 products
 HK_DEV float dot_tree(const float (&q)[8], const float (&k)[8]) {
@@ -83,8 +83,10 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_score(Args a) {
     const int pb0 = (int)((row_lo / BK) % P);
     const int nrows = (int)(row_hi - row_lo);
     const int ngroups = (nrows + 15) / 16;
-    for (int g0 = wave; g0 < ngroups; g0 += 4 * UNR) {
-      Raw8<T> raw[UNR][4];
+    // Each wavefront takes row groups wave, wave + 4, ...; a batch is UNR of them
+    // (UNR * 4 loads of 1 KB).  Two batches live in registers: the next batch's loads are
+    // in flight while the current one is scored.
+    auto issue = [&](Raw8<T> (&buf)[UNR][4], int g0) {
 #pragma unroll
       for (int u = 0; u < UNR; ++u) {
         const int gi = g0 + 4 * u;
@@ -94,13 +96,14 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_score(Args a) {
         for (int l = 0; l < 4; ++l) {
           const int rel = gi * 16 + l * 4 + grp;
           if (gi < ngroups && rel < nrows) {
-            const int ring = pb * BK + (rel & (BK - 1));
-            raw_load(kbase + (size_t)ring * (HD * EB), raw[u][l]);
+            raw_load_nt(kbase + (size_t)(pb * BK + (rel & (BK - 1))) * (HD * EB), buf[u][l]);
           } else {
-            raw[u][l] = Raw8<T>{};
+            buf[u][l] = Raw8<T>{};
           }
         }
       }
+    };
+    auto score = [&](const Raw8<T> (&buf)[UNR][4], int g0) {
 #pragma unroll
       for (int u = 0; u < UNR; ++u) {
         const int gi = g0 + 4 * u;
@@ -108,7 +111,7 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_score(Args a) {
 #pragma unroll
         for (int l = 0; l < 4; ++l) {
           float kf[8];
-          raw_to_f(raw[u][l], kf);
+          raw_to_f(buf[u][l], kf);
           float s = dot_tree(qf[0], kf);
 #pragma unroll
           for (int g = 1; g < G; ++g) {
@@ -131,6 +134,19 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_score(Args a) {
         }
         wave_sync();
       }
+    };
+    constexpr int STEP = 4 * UNR;
+    Raw8<T> bufA[UNR][4], bufB[UNR][4];
+    int g0 = wave;
+    if (g0 < ngroups) issue(bufA, g0);
+    while (g0 < ngroups) {
+      if (g0 + STEP < ngroups) issue(bufB, g0 + STEP);
+      score(bufA, g0);
+      g0 += STEP;
+      if (g0 >= ngroups) break;
+      if (g0 + STEP < ngroups) issue(bufA, g0 + STEP);
+      score(bufB, g0);
+      g0 += STEP;
     }
   }
   wmax = wave_max(wmax);

@@ -9,13 +9,15 @@ Inputs are seeded synthetic caches generated on the GPU and resident in HBM
 before the timed region.  Prints one JSON line.
 
 Timing:
-  * W warmup steps run eagerly; then K steps are captured into one HIP graph and
-    replayed once between two events (streaming workloads), or each of the K steps
-    starts from the same prefilled state, restored outside the timed region
-    (the mixed-length workload, whose first step condenses hundreds of blocks).
-  * The dominant kernel is timed on its own with events over R launches
-    (hardkv_step_stage on the same stream); its algorithmic bytes per launch over
-    that duration give roofline.achieved.
+  * Single-step workloads (one decode step from the prefilled context): the step is
+    captured into a HIP graph and replayed K times between two events, each time from
+    the prefilled state restored outside the timed region; every kernel of the step is
+    also timed on its own on exactly that state (hardkv_step_stage, same stream).
+  * The streaming workload: W warmup steps run eagerly, then the K steps are captured
+    into one HIP graph and replayed once between two events; kernels that only read
+    what earlier ones wrote are timed again on the post-step state.
+  * The dominant kernel is the longest one that moves algorithmic bytes; those bytes
+    per launch over its duration give roofline.achieved.
   * Algorithmic bytes per step follow the byte model of the design notes and are
     computed from the per-unit pool sizes, budgets and condensed blocks of the
     timed steps, replayed eagerly from a snapshot after the timed region.
@@ -232,7 +234,8 @@ def main():
         return
     wl = get_workload(args.config)
     top_p = args.top_p
-    restore_mode = wl.ctx_min is not None  # mixed lengths: every timed step from the prefilled state
+    # single-step workloads: every timed step is the step from the prefilled context
+    restore_mode = wl.steps == 1
     K, Wm = args.steps, args.warmup
     nsteps = 1 if restore_mode else Wm + K
 
@@ -247,29 +250,61 @@ def main():
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
 
+    def timed(fn):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1)
+
+    stage_us = {}
     if restore_mode:
+        # the workload is one decode step from the prefilled context: capture that step,
+        # then replay it K times, each from the restored state
         snaps = [L.snapshot() for L in layers]
-        for _ in range(Wm):
-            for L in layers:
-                L.step(0)
+
+        def restore():
             for L, sn in zip(layers, snaps):
                 L.restore(sn)
+
+        for _ in range(max(1, Wm)):
+            for L in layers:
+                L.step(0)
+            restore()
         torch.cuda.synchronize()
+        g = None
+        if not args.eager:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for L in layers:
+                    L.step(0)
+            torch.cuda.synchronize()
         times = []
         for _ in range(K):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            for L in layers:
-                L.step(0)
-            e1.record(stream)
+            restore()
             torch.cuda.synchronize()
-            times.append(e0.elapsed_time(e1))
-            for L, sn in zip(layers, snaps):
-                L.restore(sn)
-        torch.cuda.synchronize()
+            times.append(timed(g.replay if g is not None else (lambda: [L.step(0) for L in layers])))
         ms_per_step = float(np.mean(times))
-        acc_steps = [0]
+        graph_out = layers[-1].out.clone()
+        # every kernel of the step timed on the state it really sees: kernels that only
+        # read what earlier ones wrote run R times back to back; the append and the
+        # condensation (which advance the state) run once per restore
+        for k in range(len(STAGE_NAMES)):
+            reps = args.stage_reps if k in REPEATABLE else 1
+            ts = []
+            for _ in range(args.stage_reps if k not in REPEATABLE else 1):
+                restore()
+                for j in range(k):
+                    for L in layers:
+                        L.stage(0, j)
+                torch.cuda.synchronize()
+                ts.append(timed(lambda: [L.stage(0, k) for _ in range(reps) for L in layers]) / reps)
+            stage_us[STAGE_NAMES[k]] = float(np.median(ts)) * 1e3 / len(layers)
+        restore()
+        torch.cuda.synchronize()
         snap_after = snaps
+        acc_steps = [0]
     else:
         for s in range(Wm):
             for L in layers:
@@ -277,12 +312,7 @@ def main():
         torch.cuda.synchronize()
         snap_after = [L.snapshot() for L in layers]
         if args.eager:
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            for s in range(Wm, Wm + K):
-                for L in layers:
-                    L.step(s)
-            e1.record(stream)
+            ms = timed(lambda: [L.step(s) for s in range(Wm, Wm + K) for L in layers])
         else:
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
@@ -291,30 +321,19 @@ def main():
                         L.step(s)
             # capture does not run the kernels; the state is still the post-warmup one
             torch.cuda.synchronize()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            g.replay()
-            e1.record(stream)
-        torch.cuda.synchronize()
-        ms_per_step = e0.elapsed_time(e1) / K
+            ms = timed(g.replay)
+        ms_per_step = ms / K
         graph_out = layers[-1].out.clone()
         acc_steps = list(range(Wm, Wm + K))
-
-    # per-kernel durations on the post-step state (repeatable stages only)
-    stage_us = {}
-    s_last = acc_steps[-1]
-    for k in REPEATABLE:
-        for L in layers:
-            L.stage(s_last, k)
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(args.stage_reps):
+        # per-kernel durations of the stages that only read what earlier stages wrote,
+        # repeated on the post-step state
+        s_last = acc_steps[-1]
+        for k in REPEATABLE:
             for L in layers:
                 L.stage(s_last, k)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        stage_us[STAGE_NAMES[k]] = e0.elapsed_time(e1) * 1e3 / (args.stage_reps * len(layers))
+            torch.cuda.synchronize()
+            ms = timed(lambda: [L.stage(s_last, k) for _ in range(args.stage_reps) for L in layers])
+            stage_us[STAGE_NAMES[k]] = ms * 1e3 / (args.stage_reps * len(layers))
 
     # exact algorithmic bytes of the timed steps, replayed eagerly from the snapshot
     for L, sn in zip(layers, snap_after):
@@ -328,9 +347,7 @@ def main():
             bytes_tot[k] += b[k]
         scanned_tot += n
     nacc = len(acc_steps)
-    replay_matches = None
-    if not restore_mode:
-        replay_matches = bool(torch.equal(graph_out, layers[-1].out))
+    replay_matches = bool(torch.equal(graph_out, layers[-1].out))
     bytes_step = {k: v / nacc for k, v in bytes_tot.items()}
     algo_step = sum(bytes_step.values())
     scanned_step = scanned_tot / nacc
@@ -360,7 +377,8 @@ def main():
                    "kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim, "dense_window": wl.dense_window,
                    "sparse_cap": wl.sparse_cap, "condensed_slots": wl.condensed_slots,
                    "top_p": float(layers[0].cfg.c.top_p), "cond_mode": "merge",
-                   "timing": "restore-per-step" if restore_mode else ("eager" if args.eager else "hip-graph")},
+                   "timing": ("one-step graph replay from the prefilled state" if restore_mode else
+                              "graph of the K streaming steps") + (" (eager)" if args.eager else "")},
         "kv_tokens_scanned_per_s": scanned_step * steps_per_s,
         "algorithmic_bytes_per_step": algo_step,
         "step_hbm_GBps": algo_step / (ms_per_step * 1e-3) / 1e9,

@@ -4,6 +4,7 @@
 #include <math.h>
 #include <string.h>
 
+
 #include "hardkv_internal.h"
 
 namespace hardkv {
@@ -96,6 +97,9 @@ int32_t plan(const hardkv_config *cfg, Plan &p) {
     a.ncs = 1;
   }
 
+  a.bh0 = 0;
+  a.nbh = (int)BH;
+
   p.off_head = 0;
   p.off_cmax = align256(p.off_head + (size_t)BH * sizeof(HeadInfo));
   p.off_blkinfo = align256(p.off_cmax + (size_t)BH * a.nch_score * sizeof(float));
@@ -175,6 +179,13 @@ hipError_t step_stage(const hardkv_config *cfg, Args &a, int stage, hipStream_t 
     case 5: return launch_combine(a, s);
     default: return hipErrorInvalidValue;
   }
+}
+
+// The fused step: every stage over all units, in stream order.
+hipError_t step_all(const hardkv_config *cfg, Args &a, hipStream_t s) {
+  hipError_t e = hipSuccess;
+  for (int stage = 0; stage < NSTAGES && e == hipSuccess; ++stage) e = step_stage(cfg, a, stage, s);
+  return e;
 }
 
 }  // namespace
@@ -272,12 +283,7 @@ int32_t hardkv_step(const hardkv_config *cfg, hardkv_state *st, const void *q, c
   p.a.k_new = k_new;
   p.a.v_new = v_new;
   p.a.out = out;
-  hipStream_t s = (hipStream_t)stream;
-  for (int stage = 0; stage < NSTAGES; ++stage) {
-    hipError_t e = step_stage(cfg, p.a, stage, s);
-    if (e != hipSuccess) return HARDKV_EHIP;
-  }
-  return HARDKV_OK;
+  return hip_status(step_all(cfg, p.a, (hipStream_t)stream));
 }
 
 int32_t hardkv_step_stage(const hardkv_config *cfg, hardkv_state *st, const void *q,

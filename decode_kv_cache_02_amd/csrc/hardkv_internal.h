@@ -68,6 +68,7 @@ struct Args {
   int nvp;                  // view partial slots written by this call
   int npart, part_cd_base;  // partial slots per head; first condensed/dense slot
   int ncs;                  // condense workgroups per head
+  int bh0, nbh;             // (sequence, KV head) units this launch covers: [bh0, bh0 + nbh)
   uint32_t pq;
   float coeff[NCOEFF];
   float kappa[HARDKV_MAX_KV_HEADS];

@@ -8,9 +8,9 @@
 //   each workgroup attends one range of view rows, condensed slots or dense positions
 //   and writes one partial (the fused step gets the same partials from the rewrite
 //   kernel instead).
-// hardkv_combine, grid (B*Hkv), 256 threads: one wavefront per query of the group; the
-//   lanes first scale every partial's (m, l) against the common max, then sum the
-//   partials' accumulators two head dims per lane, eight partials in flight.
+// hardkv_combine, grid (G, B*Hkv), 256 threads: one workgroup per query; it scales every
+//   partial's (m, l) against the common max, then sums the partials' accumulators in
+//   two streams of 128 head dims, eight partials in flight per thread.
 #include "attn_common.h"
 
 namespace hardkv {
@@ -20,75 +20,75 @@ namespace {
 template <typename T, int G>
 __global__ __launch_bounds__(NTHREADS) void hardkv_attend_tiers(Args a) {
   __shared__ float s_part[4][G][2 + HD];
-  attend_segment<T, G>(a, blockIdx.y, blockIdx.x, s_part);
+  attend_segment<T, G>(a, a.bh0 + blockIdx.y, blockIdx.x, s_part);
 }
 
 constexpr int MAX_COMBINE = 2048;  // partials per round of the combine
 
 template <int G>
 __global__ __launch_bounds__(NTHREADS) void hardkv_combine(Args a) {
-  const int bh = blockIdx.x;
+  const int g = blockIdx.x, bh = a.bh0 + blockIdx.y;
   const int b = bh / a.Hkv, h = bh - b * a.Hkv;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  __shared__ float s_f[4][MAX_COMBINE];
-  const float *base = a.part + (size_t)bh * a.npart * G * (2 + HD);
+  __shared__ float s_f[MAX_COMBINE];
+  __shared__ float s_red[4];
+  __shared__ float s_acc[HD];
+  const float *base = a.part + (size_t)bh * a.npart * G * (2 + HD) + (size_t)g * (2 + HD);
+  const size_t stride = (size_t)G * (2 + HD);  // from one partial slot to the next
   const int ns = a.nvp + a.nc_att + a.nd_att;
   auto slot = [&](int i) { return i < a.nvp ? i : a.part_cd_base + (i - a.nvp); };
-  for (int g = wave; g < G; g += 4) {
-    float M = -INFINITY;
-    for (int i = lane; i < ns; i += 64) {
-      const float *ps = base + ((size_t)slot(i) * G + g) * (2 + HD);
-      if (ps[1] > 0.0f) M = fmaxf(M, ps[0]);
-    }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-    float L = 0.0f, A0 = 0.0f, A1 = 0.0f;
-    for (int r0 = 0; r0 < ns; r0 += MAX_COMBINE) {
-      const int r1 = min(ns, r0 + MAX_COMBINE);
-      float Lp = 0.0f;
-      for (int i = r0 + lane; i < r1; i += 64) {
-        const float *ps = base + ((size_t)slot(i) * G + g) * (2 + HD);
-        const float f = ps[1] > 0.0f ? exp2_fast(ps[0] - M) : 0.0f;
-        s_f[wave][i - r0] = f;
-        Lp += ps[1] * f;
-      }
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) Lp += __shfl_xor(Lp, off);
-      L += Lp;
-      wave_sync();
-      int i = r0;
-      for (; i + 8 <= r1; i += 8) {
-        float x0[8], x1[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const float *ps = base + ((size_t)slot(i + u) * G + g) * (2 + HD) + 2;
-          x0[u] = ps[lane];
-          x1[u] = ps[lane + 64];
-        }
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const float f = s_f[wave][i + u - r0];
-          A0 = __builtin_fmaf(x0[u], f, A0);
-          A1 = __builtin_fmaf(x1[u], f, A1);
-        }
-      }
-      for (; i < r1; ++i) {
-        const float *ps = base + ((size_t)slot(i) * G + g) * (2 + HD) + 2;
-        const float f = s_f[wave][i - r0];
-        A0 = __builtin_fmaf(ps[lane], f, A0);
-        A1 = __builtin_fmaf(ps[lane + 64], f, A1);
-      }
-      wave_sync();
-    }
-    float *o = a.out + ((size_t)b * a.Hq + (size_t)h * G + g) * HD;
-    o[lane] = A0 / L;
-    o[lane + 64] = A1 / L;
+
+  // the common maximum of the partials that saw any row
+  float M = -INFINITY;
+  for (int i = tid; i < ns; i += NTHREADS) {
+    const float *ps = base + (size_t)slot(i) * stride;
+    if (ps[1] > 0.0f) M = fmaxf(M, ps[0]);
   }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+  if (lane == 0) s_red[wave] = M;
+  __syncthreads();
+  M = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+  __syncthreads();
+
+  // per round: scale factors 2^(m - M), the scaled sum of l, and the scaled sum of the
+  // accumulators (two streams of partials, 128 head dims each, 8 partials in flight)
+  const int d = tid & (HD - 1), half = tid >> 7;
+  float L = 0.0f, A = 0.0f;
+  for (int r0 = 0; r0 < ns; r0 += MAX_COMBINE) {
+    const int r1 = min(ns, r0 + MAX_COMBINE);
+    float Lp = 0.0f;
+    for (int i = r0 + tid; i < r1; i += NTHREADS) {
+      const float *ps = base + (size_t)slot(i) * stride;
+      const float f = ps[1] > 0.0f ? exp2_fast(ps[0] - M) : 0.0f;
+      s_f[i - r0] = f;
+      Lp += ps[1] * f;
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) Lp += __shfl_xor(Lp, off);
+    if (lane == 0) s_red[wave] = Lp;
+    __syncthreads();
+    L += s_red[0] + s_red[1] + s_red[2] + s_red[3];
+    int i = r0 + half;
+    for (; i + 14 < r1; i += 16) {
+      float x[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) x[u] = base[(size_t)slot(i + 2 * u) * stride + 2 + d];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) A = __builtin_fmaf(x[u], s_f[i + 2 * u - r0], A);
+    }
+    for (; i < r1; i += 2) A = __builtin_fmaf(base[(size_t)slot(i) * stride + 2 + d], s_f[i - r0], A);
+    __syncthreads();
+  }
+  if (half == 1) s_acc[d] = A;
+  __syncthreads();
+  if (half == 0)
+    a.out[((size_t)b * a.Hq + (size_t)h * G + g) * HD + d] = (A + s_acc[d]) / L;
 }
 
 template <typename T>
 hipError_t launch_tiers(const Args &a, hipStream_t s) {
-  dim3 grid(a.nv_att + a.nc_att + a.nd_att, a.B * a.Hkv);
+  dim3 grid(a.nv_att + a.nc_att + a.nd_att, a.nbh);
   switch (a.G) {
     case 1: hipLaunchKernelGGL((hardkv_attend_tiers<T, 1>), grid, dim3(NTHREADS), 0, s, a); break;
     case 2: hipLaunchKernelGGL((hardkv_attend_tiers<T, 2>), grid, dim3(NTHREADS), 0, s, a); break;
@@ -106,7 +106,7 @@ hipError_t launch_attend(const Args &a, hipStream_t s, bool bf16) {
 }
 
 hipError_t launch_combine(const Args &a, hipStream_t s) {
-  dim3 grid(a.B * a.Hkv);
+  dim3 grid(a.G, a.nbh);
   switch (a.G) {
     case 1: hipLaunchKernelGGL((hardkv_combine<1>), grid, dim3(NTHREADS), 0, s, a); break;
     case 2: hipLaunchKernelGGL((hardkv_combine<2>), grid, dim3(NTHREADS), 0, s, a); break;

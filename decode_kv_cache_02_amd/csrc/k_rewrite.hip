@@ -26,7 +26,7 @@ template <typename T, int G, bool MASK, bool COPY, bool ATTN>
 __global__ __launch_bounds__(NTHREADS) void hardkv_rewrite(Args a) {
   constexpr int EB = Elem<T>::bytes;
   constexpr size_t ROWB = (size_t)HD * EB;
-  const int bh = blockIdx.y, chunk = blockIdx.x;
+  const int bh = a.bh0 + blockIdx.y, chunk = blockIdx.x;
   __shared__ uint8_t s_list[4][64];
   __shared__ float s_part[ATTN ? 4 : 1][G][2 + HD];
   if (ATTN && chunk >= a.nch_reg) {  // condensed / dense attention segments
@@ -126,7 +126,7 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_rewrite(Args a) {
 
 template <typename T, bool MASK, bool COPY, bool ATTN>
 hipError_t launch_g(const Args &a, hipStream_t s) {
-  dim3 grid(a.nch_reg + (ATTN ? a.nc_att + a.nd_att : 0), a.B * a.Hkv);
+  dim3 grid(a.nch_reg + (ATTN ? a.nc_att + a.nd_att : 0), a.nbh);
   switch (a.G) {
     case 1: hipLaunchKernelGGL((hardkv_rewrite<T, 1, MASK, COPY, ATTN>), grid, dim3(NTHREADS), 0, s, a); break;
     case 2: hipLaunchKernelGGL((hardkv_rewrite<T, 2, MASK, COPY, ATTN>), grid, dim3(NTHREADS), 0, s, a); break;

@@ -55,7 +55,7 @@ HK_DEV float wave_max(float v) {
 template <typename T, int G>
 __global__ __launch_bounds__(NTHREADS) void hardkv_score(Args a) {
   constexpr int EB = Elem<T>::bytes;
-  const int bh = blockIdx.y, chunk = blockIdx.x;
+  const int bh = a.bh0 + blockIdx.y, chunk = blockIdx.x;
   const int b = bh / a.Hkv, h = bh - b * a.Hkv;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int sub = lane & 15, grp = lane >> 4;
@@ -197,20 +197,24 @@ HK_DEV uint64_t wave_sum_u64(uint64_t v) {
 }
 
 constexpr int NW = SEL_THREADS / 64;  // wavefronts of the select workgroup
+constexpr int UA = 8;                  // 16-byte loads in flight per lane in the pool passes
 
+// A candidate of the cut bucket b1 packs its survivor block j and the low 16 bits of its
+// key: (j << 16) | (key & 0xffff); its key is (b1 << 16) | (cand & 0xffff).
 struct SelShared {
-  unsigned long long hist[NB1];        // mass histogram (level 1, then levels 2 and 3)
-  uint32_t blk[MAX_POOL_BLOCKS];       // per survivor block: gt | eq << 16
-  uint32_t cand_w[CAND_CAP];           // weights of the cut bucket's tokens
-  uint32_t cand_i[CAND_CAP];           // their index from the first survivor position
-  unsigned long long scan[SEL_THREADS];
+  unsigned long long hist[NB1];  // mass histogram (level 1, then levels 2 and 3)
+  uint32_t cand[CAND_CAP];       // the cut bucket's tokens
   unsigned long long red[2][NW];
   float fred[NW];
   uint32_t ncand;
   int res_bucket;
   unsigned long long res_above;
   unsigned long long carry;
+  unsigned long long total;
+  uint32_t w_th, r;
 };
+// Dynamic LDS: SelShared, then uint32_t blk[P], per survivor block gt | eq << 16.
+constexpr size_t sel_lds_bytes(int P) { return sizeof(SelShared) + sizeof(uint32_t) * (size_t)P; }
 
 HK_DEV uint64_t block_sum_u64(uint64_t v, SelShared &sh, int which) {
   const int tid = threadIdx.x;
@@ -223,20 +227,31 @@ HK_DEV uint64_t block_sum_u64(uint64_t v, SelShared &sh, int which) {
   return s;
 }
 
-// inclusive suffix sums over threads of a u64 each holds
-HK_DEV uint64_t block_suffix_incl(uint64_t mine, SelShared &sh) {
-  const int tid = threadIdx.x;
-  sh.scan[tid] = mine;
-  __syncthreads();
-  for (int off = 1; off < SEL_THREADS; off <<= 1) {
-    uint64_t v = (tid + off < SEL_THREADS) ? sh.scan[tid + off] : 0ull;
-    __syncthreads();
-    sh.scan[tid] += v;
-    __syncthreads();
+HK_DEV uint64_t shfl_u64(uint64_t v, int src) {
+  const uint32_t lo = __shfl((uint32_t)v, src), hi = __shfl((uint32_t)(v >> 32), src);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// inclusive prefix sums over the threads of the workgroup (thread order), or suffix sums
+// (reverse order): a wavefront scan by lane exchanges, then a scan of the wavefront totals
+HK_DEV uint64_t block_scan_u64(uint64_t mine, SelShared &sh, bool suffix) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int pos = suffix ? 63 - lane : lane;  // position in the scan order inside the wave
+  uint64_t v = mine;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int src = suffix ? lane + off : lane - off;
+    const uint64_t x = shfl_u64(v, src < 0 ? 0 : (src > 63 ? 63 : src));
+    if (pos >= off) v += x;
   }
-  uint64_t r = sh.scan[tid];
+  if (pos == 63) sh.red[0][wave] = v;  // wave total
   __syncthreads();
-  return r;
+  uint64_t before = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w)
+    if (suffix ? w > wave : w < wave) before += sh.red[0][w];
+  __syncthreads();
+  return before + v;
 }
 
 // largest bucket b of hist[0..nb) with sum(hist[b..]) >= target (1 <= target <= total);
@@ -251,7 +266,7 @@ HK_DEV int find_cut(SelShared &sh, int nb, uint64_t target, uint64_t *above) {
     sh.res_bucket = 0;
     sh.res_above = 0;
   }
-  const uint64_t incl = block_suffix_incl(mine, sh), excl = incl - mine;
+  const uint64_t incl = block_scan_u64(mine, sh, true), excl = incl - mine;
   if (excl < target && incl >= target) {
     uint64_t acc = excl;
     for (int i = hi - 1; i >= lo; --i) {
@@ -270,14 +285,23 @@ HK_DEV int find_cut(SelShared &sh, int nb, uint64_t target, uint64_t *above) {
   return r;
 }
 
+// the sum of 16-lane groups (lanes 16q .. 16q + 15), in every lane of the group
+HK_DEV uint32_t sum16(uint32_t v) {
+#pragma unroll
+  for (int off = 1; off < 16; off <<= 1) v += __shfl_xor(v, off);
+  return v;
+}
+
 __global__ __launch_bounds__(SEL_THREADS) void hardkv_select(Args a) {
-  const int bh = blockIdx.x;
+  const int bh = a.bh0 + blockIdx.x;
   const int b = bh / a.Hkv, h = bh - b * a.Hkv;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int q4 = lane >> 4, r4 = (lane & 15) * 4;  // a load: block q4 of 4, rows r4 .. r4 + 3
   const int P = a.P;
   HeadInfo *hd = a.head + bh;
   extern __shared__ unsigned char smem_raw[];
   SelShared &sh = *reinterpret_cast<SelShared *>(smem_raw);
+  uint32_t *blk = reinterpret_cast<uint32_t *>(smem_raw + sizeof(SelShared));
 
   const int64_t t = a.seq_len[b];
   const int64_t c = a.pool_head[bh];
@@ -308,29 +332,43 @@ __global__ __launch_bounds__(SEL_THREADS) void hardkv_select(Args a) {
 #pragma unroll
   for (int w = 0; w < NW; ++w) m = fmaxf(m, sh.fred[w]);
 
-  // pass A: weights of the whole pool, total and survivor mass, level-1 histogram of U
+  // pass A: weights of the whole pool, total and survivor mass, level-1 histogram of U.
+  // Wavefront `wave` takes blocks 4 wave + 64 k .. + 3, one 16-byte load per lane each.
   uint64_t my_all = 0, my_u = 0;
   bool bad = false;
-  for (int i0 = wave; i0 < nblk; i0 += 4 * NW) {
-    float sv[4];
+  for (int i0 = wave * 4; i0 < nblk; i0 += 4 * NW * UA) {
+    float4 sv[UA];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int i = i0 + u * NW;
-      const int64_t p = c + (int64_t)i * BK + lane;
-      sv[u] = (i < nblk && p < pend) ? a.scores[rowbase + (size_t)ring(i) * BK + lane] : 0.0f;
+    for (int u = 0; u < UA; ++u) {
+      const int i = i0 + u * 4 * NW + q4;
+      sv[u] = i < nblk ? *reinterpret_cast<const float4 *>(a.scores + rowbase + (size_t)ring(i) * BK + r4)
+                       : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int i = i0 + u * NW;
-      const int64_t p = c + (int64_t)i * BK + lane;
-      if (i < nblk && p < pend) {
-        bad |= !isfinite(sv[u]);
-        const uint32_t w = calib_weight(sv[u], m, kap, a.coeff);
-        a.weights[rowbase + (size_t)ring(i) * BK + lane] = w;
-        my_all += w;
-        if (i >= nx) {
-          my_u += w;
-          atomicAdd(&sh.hist[wkey(w) >> 16], (unsigned long long)w);
+    for (int u = 0; u < UA; ++u) {
+      const int i = i0 + u * 4 * NW + q4;
+      if (i < nblk) {
+        const int64_t p = c + (int64_t)i * BK + r4;
+        const float s4[4] = {sv[u].x, sv[u].y, sv[u].z, sv[u].w};
+        uint32_t w4[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const bool valid = p + k < pend;
+          bad |= valid && !isfinite(s4[k]);
+          w4[k] = valid ? calib_weight(s4[k], m, kap, a.coeff) : 0u;
+          my_all += w4[k];
+          if (valid && i >= nx) {
+            my_u += w4[k];
+            atomicAdd(&sh.hist[wkey(w4[k]) >> 16], (unsigned long long)w4[k]);
+          }
+        }
+        uint32_t *wp = a.weights + rowbase + (size_t)ring(i) * BK + r4;
+        if (p + 3 < pend) {
+          *reinterpret_cast<uint4 *>(wp) = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+        } else {
+#pragma unroll
+          for (int k = 0; k < 4; ++k)
+            if (p + k < pend) wp[k] = w4[k];
         }
       }
     }
@@ -345,70 +383,102 @@ __global__ __launch_bounds__(SEL_THREADS) void hardkv_select(Args a) {
   if (W_U > 0) {
     uint64_t above1, above2, above3;
     const int b1 = find_cut(sh, NB1, T, &above1);
+    const uint64_t R1 = T - above1;  // mass still needed from the cut bucket
 
     // pass B: per survivor block, weights above the cut bucket; gather the bucket
-    for (int j0 = wave; j0 < nub; j0 += 4 * NW) {
-      uint32_t wv[4];
+    for (int j0 = wave * 4; j0 < nub; j0 += 4 * NW * UA) {
+      uint4 wv[UA];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int j = j0 + u * NW;
-        const int64_t p = u0 + (int64_t)j * BK + lane;
-        wv[u] = (j < nub && p < pend) ? a.weights[rowbase + (size_t)ring(nx + j) * BK + lane] : 0u;
+      for (int u = 0; u < UA; ++u) {
+        const int j = j0 + u * 4 * NW + q4;
+        wv[u] = j < nub ? *reinterpret_cast<const uint4 *>(a.weights + rowbase + (size_t)ring(nx + j) * BK + r4)
+                        : make_uint4(0u, 0u, 0u, 0u);
       }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int j = j0 + u * NW;
-        if (j >= nub) break;  // wave-uniform
-        const int64_t p = u0 + (int64_t)j * BK + lane;
-        const bool valid = p < pend;
-        const int kb = (int)(wkey(wv[u]) >> 16);
-        const uint64_t above = ballot(valid && kb > b1);
-        const uint64_t inb = ballot(valid && kb == b1);
-        uint32_t base = 0;
-        if (lane == 0) {
-          sh.blk[j] = (uint32_t)__popcll(above);
-          if (inb) base = atomicAdd(&sh.ncand, (uint32_t)__popcll(inb));
-        }
-        base = __shfl(base, 0);
-        if (valid && kb == b1) {
-          const uint32_t slot = base + popc_below(inb);
-          if (slot < (uint32_t)CAND_CAP) {
-            sh.cand_w[slot] = wv[u];
-            sh.cand_i[slot] = (uint32_t)(j * BK + lane);
+      for (int u = 0; u < UA; ++u) {
+        const int jb = j0 + u * 4 * NW;  // wave-uniform
+        if (jb >= nub) break;
+        const int j = jb + q4;
+        const int64_t p = u0 + (int64_t)j * BK + r4;
+        const uint32_t w4[4] = {wv[u].x, wv[u].y, wv[u].z, wv[u].w};
+        uint32_t n_above = 0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const bool valid = j < nub && p + k < pend;
+          const uint32_t key = wkey(w4[k]);
+          const int kb = (int)(key >> 16);
+          n_above += (valid && kb > b1) ? 1u : 0u;
+          const bool in = valid && kb == b1;
+          const uint64_t inb = ballot(in);
+          if (inb) {  // wave-uniform
+            uint32_t base = 0;
+            if (lane == 0) base = atomicAdd(&sh.ncand, (uint32_t)__popcll(inb));
+            base = __shfl(base, 0);
+            const uint32_t slot = base + popc_below(inb);
+            if (in && slot < (uint32_t)CAND_CAP) sh.cand[slot] = ((uint32_t)j << 16) | (key & 0xffffu);
           }
         }
+        n_above = sum16(n_above);
+        if ((lane & 15) == 0 && j < nub) blk[j] = n_above;
       }
     }
     __syncthreads();
     const uint32_t ncand = sh.ncand;
-    if (ncand <= (uint32_t)CAND_CAP) {
+    const uint32_t kb1 = (uint32_t)b1 << 16;
+    if (ncand <= 64u) {
+      // one wavefront: the largest weight v of the bucket whose candidates of weight >= v
+      // reach R1 is w_th; r ties at w_th make up what those above it leave to R1
+      if (wave == 0) {
+        const bool have = lane < (int)ncand;
+        const uint32_t w = have ? key_to_w(kb1 | (sh.cand[lane] & 0xffffu)) : 0u;
+        uint64_t gt = 0, ge = 0;
+        for (uint32_t k = 0; k < ncand; ++k) {
+          const uint32_t x = key_to_w(kb1 | (sh.cand[k] & 0xffffu));
+          gt += x > w ? x : 0u;
+          ge += x >= w ? x : 0u;
+        }
+        const uint64_t hit = ballot(have && gt < R1 && ge >= R1);
+        const int src = hit ? __ffsll((long long)hit) - 1 : 0;
+        const uint32_t wt = (uint32_t)__shfl((int)w, src);
+        const uint64_t gts = shfl_u64(gt, src);
+        if (lane == 0) {
+          sh.w_th = wt;
+          sh.r = wt ? (uint32_t)((R1 - gts + wt - 1) / wt) : 0u;
+        }
+      }
+      __syncthreads();
+      w_th = sh.w_th;
+      r = sh.r;
+    } else if (ncand <= (uint32_t)CAND_CAP) {
       // levels 2 and 3 over the candidates in LDS
       for (int i = tid; i < 256; i += SEL_THREADS) sh.hist[i] = 0ull;
       __syncthreads();
       for (uint32_t i = tid; i < ncand; i += SEL_THREADS) {
-        const uint32_t w = sh.cand_w[i];
-        atomicAdd(&sh.hist[(wkey(w) >> 8) & 255u], (unsigned long long)w);
+        const uint32_t k = kb1 | (sh.cand[i] & 0xffffu);
+        atomicAdd(&sh.hist[(k >> 8) & 255u], (unsigned long long)key_to_w(k));
       }
       __syncthreads();
-      const int b2 = find_cut(sh, 256, T - above1, &above2);
+      const int b2 = find_cut(sh, 256, R1, &above2);
       const uint32_t pre = ((uint32_t)b1 << 8) | (uint32_t)b2;
       for (int i = tid; i < 256; i += SEL_THREADS) sh.hist[i] = 0ull;
       __syncthreads();
       for (uint32_t i = tid; i < ncand; i += SEL_THREADS) {
-        const uint32_t w = sh.cand_w[i];
-        const uint32_t k = wkey(w);
-        if ((k >> 8) == pre) atomicAdd(&sh.hist[k & 255u], (unsigned long long)w);
+        const uint32_t k = kb1 | (sh.cand[i] & 0xffffu);
+        if ((k >> 8) == pre) atomicAdd(&sh.hist[k & 255u], (unsigned long long)key_to_w(k));
       }
       __syncthreads();
-      const int b3 = find_cut(sh, 256, T - above1 - above2, &above3);
+      const int b3 = find_cut(sh, 256, R1 - above2, &above3);
       w_th = key_to_w((pre << 8) | (uint32_t)b3);
-      r = (uint32_t)((T - above1 - above2 - above3 + w_th - 1) / w_th);
+      r = (uint32_t)((R1 - above2 - above3 + w_th - 1) / w_th);
+    }
+    if (ncand <= (uint32_t)CAND_CAP) {
       // candidates above w_th and at w_th, per block
       for (uint32_t i = tid; i < ncand; i += SEL_THREADS) {
-        const uint32_t w = sh.cand_w[i];
-        const uint32_t j = sh.cand_i[i] / BK;
-        if (w > w_th) atomicAdd(&sh.blk[j], 1u);
-        else if (w == w_th) atomicAdd(&sh.blk[j], 1u << 16);
+        const uint32_t cd = sh.cand[i];
+        const uint32_t w = key_to_w(kb1 | (cd & 0xffffu));
+        const uint32_t j = cd >> 16;
+        if (w > w_th) atomicAdd(&blk[j], 1u);
+        else if (w == w_th) atomicAdd(&blk[j], 1u << 16);
       }
     } else {
       // a bucket too full for LDS (for example many equal weights): levels 2 and 3 and
@@ -424,7 +494,7 @@ __global__ __launch_bounds__(SEL_THREADS) void hardkv_select(Args a) {
         }
       }
       __syncthreads();
-      const int b2 = find_cut(sh, 256, T - above1, &above2);
+      const int b2 = find_cut(sh, 256, R1, &above2);
       const uint32_t pre = ((uint32_t)b1 << 8) | (uint32_t)b2;
       for (int i = tid; i < 256; i += SEL_THREADS) sh.hist[i] = 0ull;
       __syncthreads();
@@ -437,16 +507,16 @@ __global__ __launch_bounds__(SEL_THREADS) void hardkv_select(Args a) {
         }
       }
       __syncthreads();
-      const int b3 = find_cut(sh, 256, T - above1 - above2, &above3);
+      const int b3 = find_cut(sh, 256, R1 - above2, &above3);
       w_th = key_to_w((pre << 8) | (uint32_t)b3);
-      r = (uint32_t)((T - above1 - above2 - above3 + w_th - 1) / w_th);
+      r = (uint32_t)((R1 - above2 - above3 + w_th - 1) / w_th);
       for (int j = wave; j < nub; j += NW) {
         const int64_t p = u0 + (int64_t)j * BK + lane;
         uint32_t w = 0;
         if (p < pend) w = a.weights[rowbase + (size_t)ring(nx + j) * BK + lane];
         const uint64_t gtm = ballot(p < pend && w > w_th);
         const uint64_t eqm = ballot(p < pend && w == w_th);
-        if (lane == 0) sh.blk[j] = (uint32_t)__popcll(gtm) | ((uint32_t)__popcll(eqm) << 16);
+        if (lane == 0) blk[j] = (uint32_t)__popcll(gtm) | ((uint32_t)__popcll(eqm) << 16);
       }
     }
     __syncthreads();
@@ -457,19 +527,13 @@ __global__ __launch_bounds__(SEL_THREADS) void hardkv_select(Args a) {
     __syncthreads();
     for (int base = 0; base < nub; base += SEL_THREADS) {
       const int i = base + tid;
-      const uint32_t v = (i < nub) ? sh.blk[i] : 0u;
+      const uint32_t v = (i < nub) ? blk[i] : 0u;
       const uint64_t mine = (uint64_t)(v & 0xffffu) | ((uint64_t)(v >> 16) << 32);
-      sh.scan[tid] = mine;
+      const uint64_t incl = block_scan_u64(mine, sh, false);
+      if (tid == SEL_THREADS - 1) sh.total = incl;  // round total
+      const uint64_t before = sh.carry + incl - mine;
       __syncthreads();
-      for (int off = 1; off < SEL_THREADS; off <<= 1) {
-        uint64_t x = (tid >= off) ? sh.scan[tid - off] : 0ull;
-        __syncthreads();
-        sh.scan[tid] += x;
-        __syncthreads();
-      }
-      const uint64_t before = sh.carry + sh.scan[tid] - mine;
-      const uint64_t total = sh.scan[SEL_THREADS - 1];
-      __syncthreads();
+      const uint64_t total = sh.total;
       if (i < nub) {
         const uint32_t gt_b = (uint32_t)before, eq_b = (uint32_t)(before >> 32);
         a.blkinfo[(size_t)bh * P + ring(nx + i)] = make_uint2(gt_b + min(eq_b, r), eq_b);
@@ -501,7 +565,7 @@ __global__ __launch_bounds__(SEL_THREADS) void hardkv_select(Args a) {
 
 template <typename T>
 hipError_t launch_score_g(const Args &a, hipStream_t s) {
-  dim3 grid(a.nch_score, a.B * a.Hkv);
+  dim3 grid(a.nch_score, a.nbh);
   switch (a.G) {
     case 1: hipLaunchKernelGGL((hardkv_score<T, 1>), grid, dim3(NTHREADS), 0, s, a); break;
     case 2: hipLaunchKernelGGL((hardkv_score<T, 2>), grid, dim3(NTHREADS), 0, s, a); break;
@@ -521,12 +585,12 @@ hipError_t launch_score(const Args &a, hipStream_t s, bool bf16) {
 hipError_t launch_select(const Args &a, hipStream_t s) {
   static bool configured = false;  // the attribute is per function, set once per process
   if (!configured) {
-    hipError_t e = hipFuncSetAttribute((const void *)hardkv_select,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(SelShared));
+    hipError_t e = hipFuncSetAttribute((const void *)hardkv_select, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)sel_lds_bytes(MAX_POOL_BLOCKS));
     if (e != hipSuccess) return e;
     configured = true;
   }
-  hipLaunchKernelGGL(hardkv_select, dim3(a.B * a.Hkv), dim3(SEL_THREADS), sizeof(SelShared), s, a);
+  hipLaunchKernelGGL(hardkv_select, dim3(a.nbh), dim3(SEL_THREADS), sel_lds_bytes(a.P), s, a);
   return hipGetLastError();
 }
 

@@ -27,6 +27,9 @@ CASES = {
     "one_block": dict(ctx_len=32 + 64, ctx_min=32 + 60, dense_window=32, steps=6),
     "batch3_heads4": dict(batch=3, num_q_heads=16, num_kv_heads=4, cond_mode=COND_MERGE),
     "scap64": dict(sparse_cap=64, ctx_len=300, ctx_min=200, cond_mode=COND_MERGE, condensed_slots=2),
+    # 32 units: more select and combine workgroups than a tiny batch
+    "two_groups": dict(batch=16, cond_mode=COND_MERGE, ctx_len=500, ctx_min=100, steps=3),
+    "two_groups_g8": dict(batch=8, num_q_heads=32, num_kv_heads=4, cond_mode=COND_EVICT, steps=2),
 }
 
 
@@ -127,3 +130,38 @@ def test_determinism_and_fused_equals_composition():
         assert torch.equal(a[n], c[n]), n
     for x, y in zip(ao, co):
         assert row_rel_err(x.cpu().numpy(), y.cpu().numpy()) < 1e-5
+
+
+@pytest.mark.parametrize("batch", [2, 16])
+def test_graph_replay_matches_eager(batch):
+    """hardkv_step captured once in a HIP graph (with static input buffers) and replayed
+    for several steps, with eager copies and synchronizations between the replays, gives
+    bitwise the state and output of the eager calls (I15)."""
+    from decode_kv_cache_02_amd import hardkv as hk
+    from synth import make_inputs
+    wl = tiny_workload(batch=batch, steps=4, cond_mode=COND_MERGE, ctx_len=500, ctx_min=100)
+    inp = make_inputs(wl, device="cuda")
+    cfg = hk.Config.from_workload(wl)
+    ref, gst = hk.State(cfg), hk.State(cfg)
+    for st in (ref, gst):
+        hk.hardkv_prefill(cfg, st, inp.k_ctx, inp.v_ctx, inp.ctx_len)
+    out_ref = torch.zeros((wl.batch, wl.num_q_heads, 128), device="cuda")
+    out_g = torch.zeros_like(out_ref)
+    q_s, k_s, v_s = inp.q[0].clone(), inp.k_new[0].clone(), inp.v_new[0].clone()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        hk.hardkv_step(cfg, gst, q_s, k_s, v_s, out_g)
+    torch.cuda.synchronize()
+    for s in range(wl.steps):
+        hk.hardkv_step(cfg, ref, inp.q[s], inp.k_new[s], inp.v_new[s], out_ref)
+        q_s.copy_(inp.q[s])
+        k_s.copy_(inp.k_new[s])
+        v_s.copy_(inp.v_new[s])
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out_ref, out_g), s
+        for n, t in ref.tensors().items():
+            if n == "workspace":
+                continue
+            assert torch.equal(t, getattr(gst, n)), (s, n)

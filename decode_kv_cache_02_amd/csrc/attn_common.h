@@ -30,6 +30,7 @@ HK_DEV float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // one row (the same row in all 16 lanes of the group); logit = (q . k) * kscale + bias,
 // value v.  Called by every lane of the wavefront; rows with act == false add nothing.
+// (The condensed slots, which carry a scale and a bias per slot, take this form.)
 template <int G>
 HK_DEV void attn_row(AttnState<G> &st, const float (&qs)[G][8], const float (&k)[8],
                      const float (&v)[8], float kscale, float bias, bool act) {
@@ -55,8 +56,60 @@ HK_DEV void attn_row(AttnState<G> &st, const float (&qs)[G][8], const float (&k)
 
 HK_DEV float merge_factor(float m, float mn) { return (m == -INFINITY) ? 0.0f : exp2_fast(m - mn); }
 
+// NR rows per 16-lane group at once (one from each load of a batch): their logits, one
+// rescale of the accumulators to the new running maximum, then the NR value rows.
+template <typename T, int G, int NR>
+HK_DEV void attn_rows(AttnState<G> &st, const float (&qs)[G][8], const Raw8<T> (&kr)[NR],
+                      const Raw8<T> (&vr)[NR], const bool (&act)[NR]) {
+  float lg[G][NR];
+#pragma unroll
+  for (int j = 0; j < NR; ++j) {
+    float kf[8];
+    raw_to_f(kr[j], kf);
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float d = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) d = __builtin_fmaf(qs[g][i], kf[i], d);
+      d += dpp<DPP_XOR1>(d);
+      d += dpp<DPP_XOR2>(d);
+      d += dpp<DPP_HALF_MIRROR>(d);
+      d += dpp<DPP_MIRROR>(d);
+      lg[g][j] = act[j] ? d : -INFINITY;
+    }
+  }
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    float mx = lg[g][0];
+#pragma unroll
+    for (int j = 1; j < NR; ++j) mx = fmaxf(mx, lg[g][j]);
+    const float mn = fmaxf(st.m[g], mx);
+    const float sc = (st.m[g] == mn) ? 1.0f : exp2_fast(st.m[g] - mn);
+    float ps = 0.0f;
+#pragma unroll
+    for (int j = 0; j < NR; ++j) {
+      lg[g][j] = act[j] ? exp2_fast(lg[g][j] - mn) : 0.0f;
+      ps += lg[g][j];
+    }
+    st.l[g] = __builtin_fmaf(st.l[g], sc, ps);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) st.acc[g][i] *= sc;
+    st.m[g] = mn;
+  }
+#pragma unroll
+  for (int j = 0; j < NR; ++j) {
+    float vf[8];
+    raw_to_f(vr[j], vf);
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) st.acc[g][i] = __builtin_fmaf(lg[g][j], vf[i], st.acc[g][i]);
+  }
+}
+
 // merge the four 16-lane groups of each wavefront, then the four wavefronts; write the
-// partial [G][2 + HD] = (m, l, acc) to dst.  Must be reached by all threads.
+// partial [G][2 + HD] = (m, l, acc) to dst (only (m, l) = (-inf, 0) for a query that saw
+// no row: the combine never reads that accumulator).  Must be reached by all threads.
 template <int G>
 HK_DEV void attn_write_partial(AttnState<G> &st, float *dst, float (*s_part)[G][2 + HD]) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, sub = lane & 15;
@@ -102,11 +155,11 @@ HK_DEV void attn_write_partial(AttnState<G> &st, float *dst, float (*s_part)[G][
       A += s_part[w][g][2 + d] * f;
     }
     float *o = dst + (size_t)g * (2 + HD);
-    o[2 + d] = A;
     if (d == 0) {
       o[0] = M;
       o[1] = L;
     }
+    if (L > 0.0f) o[2 + d] = A;  // a partial with l = 0 carries no accumulator
   }
 }
 
@@ -165,13 +218,7 @@ HK_DEV void attend_segment(const Args &a, int bh, int seg, float (*s_part)[G][2 
           vr[j] = Raw8<T>{};
         }
       }
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        float kf[8], vf[8];
-        raw_to_f(kr[j], kf);
-        raw_to_f(vr[j], vf);
-        attn_row<G>(st, qs, kf, vf, 1.0f, 0.0f, act[j]);
-      }
+      attn_rows<T, G, 2>(st, qs, kr, vr, act);
     }
   } else if (seg < a.nv_att + a.nc_att) {  // condensed slots
     const int xc = seg - a.nv_att;
@@ -220,13 +267,7 @@ HK_DEV void attend_segment(const Args &a, int bh, int seg, float (*s_part)[G][2 
           vr[j] = Raw8<T>{};
         }
       }
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        float kf[8], vf[8];
-        raw_to_f(kr[j], kf);
-        raw_to_f(vr[j], vf);
-        attn_row<G>(st, qs, kf, vf, 1.0f, 0.0f, act[j]);
-      }
+      attn_rows<T, G, 2>(st, qs, kr, vr, act);
     }
   }
   attn_write_partial<G>(st, a.part + ((size_t)bh * a.npart + slot) * G * (2 + HD), s_part);

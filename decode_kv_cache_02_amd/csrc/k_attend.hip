@@ -9,8 +9,9 @@
 //   and writes one partial (the fused step gets the same partials from the rewrite
 //   kernel instead).
 // hardkv_combine, grid (G, B*Hkv), 256 threads: one workgroup per query; it scales every
-//   partial's (m, l) against the common max, then sums the partials' accumulators in
-//   two streams of 128 head dims, eight partials in flight per thread.
+//   partial's (m, l) against the common max, lists the partials that carry weight in
+//   partial order, then sums their accumulators in two streams of 128 head dims, eight
+//   partials in flight per thread.
 #include "attn_common.h"
 
 namespace hardkv {
@@ -31,7 +32,9 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_combine(Args a) {
   const int b = bh / a.Hkv, h = bh - b * a.Hkv;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   __shared__ float s_f[MAX_COMBINE];
+  __shared__ int s_slot[MAX_COMBINE];
   __shared__ float s_red[4];
+  __shared__ int s_cnt[4];
   __shared__ float s_acc[HD];
   const float *base = a.part + (size_t)bh * a.npart * G * (2 + HD) + (size_t)g * (2 + HD);
   const size_t stride = (size_t)G * (2 + HD);  // from one partial slot to the next
@@ -51,33 +54,51 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_combine(Args a) {
   M = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
   __syncthreads();
 
-  // per round: scale factors 2^(m - M), the scaled sum of l, and the scaled sum of the
-  // accumulators (two streams of partials, 128 head dims each, 8 partials in flight)
+  // per round: the scale factors 2^(m - M) of the partials that carry weight, listed in
+  // partial order, and the scaled sum of l; then the scaled sum of their accumulators in
+  // two streams of 128 head dims, 8 partials in flight
   const int d = tid & (HD - 1), half = tid >> 7;
   float L = 0.0f, A = 0.0f;
   for (int r0 = 0; r0 < ns; r0 += MAX_COMBINE) {
     const int r1 = min(ns, r0 + MAX_COMBINE);
     float Lp = 0.0f;
-    for (int i = r0 + tid; i < r1; i += NTHREADS) {
-      const float *ps = base + (size_t)slot(i) * stride;
-      const float f = ps[1] > 0.0f ? exp2_fast(ps[0] - M) : 0.0f;
-      s_f[i - r0] = f;
-      Lp += ps[1] * f;
+    int nnz = 0;
+    for (int ib = r0; ib < r1; ib += NTHREADS) {
+      const int i = ib + tid;
+      float f = 0.0f;
+      if (i < r1) {
+        const float *ps = base + (size_t)slot(i) * stride;
+        f = ps[1] > 0.0f ? exp2_fast(ps[0] - M) : 0.0f;
+        Lp += ps[1] * f;
+      }
+      const uint64_t bal = ballot(f > 0.0f);
+      if (lane == 0) s_cnt[wave] = __popcll(bal);
+      __syncthreads();
+      int before = nnz;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) before += w < wave ? s_cnt[w] : 0;
+      if (f > 0.0f) {
+        const int pos = before + (int)popc_below(bal);
+        s_slot[pos] = slot(i);
+        s_f[pos] = f;
+      }
+      nnz += s_cnt[0] + s_cnt[1] + s_cnt[2] + s_cnt[3];
+      __syncthreads();
     }
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) Lp += __shfl_xor(Lp, off);
     if (lane == 0) s_red[wave] = Lp;
     __syncthreads();
     L += s_red[0] + s_red[1] + s_red[2] + s_red[3];
-    int i = r0 + half;
-    for (; i + 14 < r1; i += 16) {
+    int k = half;
+    for (; k + 14 < nnz; k += 16) {
       float x[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) x[u] = base[(size_t)slot(i + 2 * u) * stride + 2 + d];
+      for (int u = 0; u < 8; ++u) x[u] = base[(size_t)s_slot[k + 2 * u] * stride + 2 + d];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) A = __builtin_fmaf(x[u], s_f[i + 2 * u - r0], A);
+      for (int u = 0; u < 8; ++u) A = __builtin_fmaf(x[u], s_f[k + 2 * u], A);
     }
-    for (; i < r1; i += 2) A = __builtin_fmaf(base[(size_t)slot(i) * stride + 2 + d], s_f[i - r0], A);
+    for (; k < nnz; k += 2) A = __builtin_fmaf(base[(size_t)s_slot[k] * stride + 2 + d], s_f[k], A);
     __syncthreads();
   }
   if (half == 1) s_acc[d] = A;

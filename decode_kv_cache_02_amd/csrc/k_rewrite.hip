@@ -4,8 +4,8 @@
 // into contiguous ranges, each head owning a fixed-capacity view (the max-length form
 // of Flatten Index), so that attention reads static, contiguous, fixed-stride blocks.
 //
-// Grid (chunks [+ attention segments], B*Hkv), 256 threads.  A wavefront takes one
-// 64-row pool block at a time.  From the block's weights and the head's cut (w_th, r,
+// Grid (chunks [+ attention segments], B*Hkv), 256 threads.  A chunk is four pool
+// blocks, one per wavefront.  From the block's weights and the head's cut (w_th, r,
 // and the block's ties-before count from the select stage) each lane decides whether its
 // row is kept: w > w_th, or w == w_th and its tie rank (ties before the block plus the
 // mbcnt of equal weights below it) is under r.  The ballot of those bits is the block's
@@ -46,6 +46,29 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_rewrite(Args a) {
   const int nblk = (int)((pend + BK - 1) / BK - c / BK);
   const int pb_lo = (int)((c / BK) % P);
   const int i0 = chunk * a.cb_reg, i1 = min(i0 + a.cb_reg, P);
+  auto ring = [&](int i) { return pb_lo + i >= P ? pb_lo + i - P : pb_lo + i; };
+
+  // A chunk that keeps no row (all its blocks condensed, outside the pool, or with no
+  // kept token: the first view rows of its first survivor block and of the block after
+  // it are equal) only clears its mask words and leaves an empty partial.
+  {
+    const int ia = max(i0, nx), ib = min(i1, nblk);
+    bool empty = ia >= ib;
+    if (!empty) {
+      const uint32_t x0 = a.blkinfo[(size_t)bh * P + ring(ia)].x;
+      const uint32_t x1 = ib < nblk ? a.blkinfo[(size_t)bh * P + ring(ib)].x : (uint32_t)hd->kstar;
+      empty = x1 == x0;
+    }
+    if (empty) {
+      if (MASK && tid < i1 - i0) a.mask[(size_t)bh * P + ring(i0 + tid)] = 0ull;
+      if (ATTN && tid < G) {
+        float *o = a.part + ((size_t)bh * a.npart + chunk) * G * (2 + HD) + (size_t)tid * (2 + HD);
+        o[0] = -INFINITY;
+        o[1] = 0.0f;
+      }
+      return;
+    }
+  }
 
   AttnState<G> st;
   float qs[G][8];
@@ -61,7 +84,7 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_rewrite(Args a) {
   int32_t *vpos = a.view_pos + (size_t)bh * V;
 
   for (int i = i0 + wave; i < i1; i += 4) {
-    const int pb = pb_lo + i >= P ? pb_lo + i - P : pb_lo + i;
+    const int pb = ring(i);
     if (i < nx || i >= nblk) {  // condensed this step, or holds no pool position
       if (MASK && lane == 0) a.mask[(size_t)bh * P + pb] = 0ull;
       continue;
@@ -109,15 +132,7 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_rewrite(Args a) {
           raw_store_nt(vv + (size_t)dst[j] * ROWB, vr[j]);
         }
       }
-      if (ATTN) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          float kf[8], vf[8];
-          raw_to_f(kr[j], kf);
-          raw_to_f(vr[j], vf);
-          attn_row<G>(st, qs, kf, vf, 1.0f, 0.0f, act[j]);
-        }
-      }
+      if (ATTN) attn_rows<T, G, 4>(st, qs, kr, vr, act);
     }
     wave_sync();
   }

@@ -63,6 +63,14 @@ def parse():
     ap.add_argument("--cpu-units", type=int, default=0, help="oracle sample size in units (0: automatic)")
     ap.add_argument("--copy-calib", type=int, default=0,
                     help="only run a device copy of this many MiB (counter calibration) and exit")
+    ap.add_argument("--summarize-kernels", nargs=2, metavar=("KERNEL_STATS_CSV", "OUT_TXT"),
+                    help="write a text summary of a rocprofv3 kernel_stats.csv and exit")
+    ap.add_argument("--summarize-traffic", nargs=4,
+                    metavar=("FETCH_CSV", "WRITE_CSV", "CALIB_FETCH_CSV", "CALIB_WRITE_CSV"),
+                    help="HBM bytes per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE counter runs of "
+                         "--config and of --copy-calib MiB; writes profiles/traffic.json and a text "
+                         "summary, then exits")
+    ap.add_argument("--cmd", action="append", default=[], help="command recorded in a summary")
     return ap.parse_args()
 
 
@@ -104,18 +112,21 @@ def unit_bytes(wl, N, kstar, E, t, c_occ):
     """Algorithmic bytes per stage for arrays of per-unit values (one step).
 
     score: the pool keys; rewrite_attend: the kept rows read and written once, the dense
-    window and the occupied condensed slots read, q in; condense: the values of the
-    condensing blocks and the slot read-modify-write; append: three rows of K and V;
-    combine: the output.  The select stage only moves scores and weights (scratch), which
-    the byte model does not count."""
+    window and the occupied condensed slots read, q in; condense (merge): the keys and
+    values of the condensing blocks read and the slot read-modify-write (eviction moves
+    nothing); append: the leaving dense row read and written to the pool, the new token
+    read and written to the dense window, keys and values; combine: the output.  The
+    select stage only moves scores and weights (scratch), which the byte model does not
+    count."""
     e, G = wl.elem_bytes, wl.group
     dense_rows = np.minimum(t, wl.dense_window)
-    rmw = 2 * (8 * D + 8) * E if wl.cond_mode == COND_MERGE else 0 * E
+    merge = wl.cond_mode == COND_MERGE
+    cond = (2 * e * D * 64 * E + 2 * (8 * D + 8) * np.minimum(E, wl.condensed_slots)) if merge else 0 * E
     return {
-        "append": 6 * e * D * np.ones_like(N),
+        "append": 8 * e * D * np.ones_like(N),
         "score": e * D * N,
         "select": 0 * N,
-        "condense": e * D * 64 * E + rmw,
+        "condense": cond,
         "rewrite_attend": 4 * e * D * kstar + 2 * e * D * dense_rows + (8 * D + 8) * c_occ + G * D * e,
         "combine": G * D * 4 * np.ones_like(N),
     }
@@ -153,6 +164,99 @@ def copy_calibration(mib):
     print(json.dumps({"copy_calibration_bytes": n}))
 
 
+# ---- profile summaries -------------------------------------------------------------------
+KERNEL_STAGE = {"hardkv_rewrite": "rewrite_attend", "hardkv_score": "score", "hardkv_select": "select",
+                "hardkv_condense": "condense", "hardkv_append": "append", "hardkv_combine": "combine",
+                "hardkv_attend_tiers": "attend_tiers", "hardkv_prefill": "prefill"}
+KERNEL_SOURCES = sorted(
+    [os.path.join("decode_kv_cache_02_amd", "csrc", f)
+     for f in os.listdir(os.path.join(ROOT, "decode_kv_cache_02_amd", "csrc"))
+     if f.endswith((".hip", ".h"))] + [os.path.join("include", "hardkv.h")])
+
+
+def kernel_key(name):
+    for k in sorted(KERNEL_STAGE, key=len, reverse=True):
+        if k + "<" in name or k + "(" in name or name.endswith(k) or (k + " ") in name:
+            return k
+    return None
+
+
+def summarize_kernels(src, dst, cmds, title):
+    import csv
+    rows = list(csv.DictReader(open(src)))
+    with open(dst, "w") as f:
+        f.write(f"# {title}\n\nCommands (repository root R, one MI355X):\n\n")
+        for c in cmds:
+            f.write(f"    {c}\n")
+        f.write("\nrocprofv3 kernel statistics (kernel_stats.csv), all dispatches of the run:\n\n")
+        f.write(f"{'kernel':<58} {'calls':>6} {'avg_us':>9} {'min_us':>9} {'max_us':>9} {'pct':>6}\n")
+        for r in rows:
+            name = r["Name"]
+            if kernel_key(name) is None and float(r["Percentage"]) < 1.0:
+                continue
+            name = (name.replace("void hardkv::(anonymous namespace)::", "")
+                    .replace("hardkv::(anonymous namespace)::", "").replace("(hardkv::Args)", "")
+                    .replace("hardkv::", ""))
+            f.write(f"{name[:58]:<58} {r['Calls']:>6} {float(r['AverageNs']) / 1e3:>9.2f} "
+                    f"{float(r['MinNs']) / 1e3:>9.2f} {float(r['MaxNs']) / 1e3:>9.2f} "
+                    f"{float(r['Percentage']):>6.2f}\n")
+    print(open(dst).read())
+
+
+def summarize_traffic(fetch_csv, write_csv, cal_fetch_csv, cal_write_csv, calib_mib, wl, cmds):
+    """Per kernel: the counter's KiB per dispatch, averaged over the run's dispatches and
+    scaled by what it reads for a plain device copy of calib_mib MiB (read and written
+    once)."""
+    import csv
+    import collections
+
+    def per_kernel(path):
+        out = collections.defaultdict(list)
+        for r in csv.DictReader(open(path)):
+            out[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+        return out
+
+    res = {}
+    scale = {}
+    for ctr, path, cal in (("FETCH_SIZE", fetch_csv, cal_fetch_csv), ("WRITE_SIZE", write_csv, cal_write_csv)):
+        calk = per_kernel(cal)
+        copy_kib = max(max(v) for n, v in calk.items() if "copyBuffer" in n or "copy" in n.lower())
+        scale[ctr] = calib_mib * 1024 / copy_kib
+        for n, v in per_kernel(path).items():
+            k = kernel_key(n)
+            if k is None:
+                continue
+            ent = res.setdefault(KERNEL_STAGE[k], {"launches": 0})
+            ent["launches"] = max(ent["launches"], len(v))
+            ent[ctr] = sum(v) / len(v) * scale[ctr] * 1024  # bytes per dispatch
+    digest = source_digest(KERNEL_SOURCES)
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    rec = json.load(open(path)) if os.path.exists(path) else {}
+    rec[wl.name] = {st: {"fetch_bytes_per_launch": e.get("FETCH_SIZE", 0.0),
+                         "write_bytes_per_launch": e.get("WRITE_SIZE", 0.0),
+                         "hbm_bytes_per_launch": e.get("FETCH_SIZE", 0.0) + e.get("WRITE_SIZE", 0.0),
+                         "launches": e["launches"], "sources": KERNEL_SOURCES, "source_digest": digest}
+                    for st, e in res.items()}
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1, sort_keys=True)
+    dst = os.path.join(ROOT, "profiles", f"traffic_{wl.name}.txt")
+    with open(dst, "w") as f:
+        f.write(f"# HBM traffic per launch, workload {wl.name} (counter runs)\n\n")
+        f.write("Commands (repository root R, one MI355X; each counter in its own run):\n\n")
+        for c in cmds:
+            f.write(f"    {c}\n")
+        f.write(f"\nCalibration: a {calib_mib} MiB device copy reads FETCH_SIZE as "
+                f"{calib_mib * 1024 / scale['FETCH_SIZE']:.0f} KiB (scale {scale['FETCH_SIZE']:.3f}) and "
+                f"WRITE_SIZE as {calib_mib * 1024 / scale['WRITE_SIZE']:.0f} KiB "
+                f"(scale {scale['WRITE_SIZE']:.3f}).\n")
+        f.write(f"Kernel sources digest {digest} (bench.py reports this traffic only while it matches).\n\n")
+        f.write(f"{'stage kernel':<16} {'launches':>8} {'fetch MB':>10} {'write MB':>10} {'total MB':>10}\n")
+        for st, e in sorted(rec[wl.name].items(), key=lambda kv: -kv[1]["hbm_bytes_per_launch"]):
+            f.write(f"{st:<16} {e['launches']:>8} {e['fetch_bytes_per_launch'] / 1e6:>10.1f} "
+                    f"{e['write_bytes_per_launch'] / 1e6:>10.1f} {e['hbm_bytes_per_launch'] / 1e6:>10.1f}\n")
+    print(open(dst).read())
+
+
 def source_digest(files):
     h = hashlib.sha256()
     for f in files:
@@ -175,13 +279,6 @@ def load_traffic(kernel, workload):
     if ent.get("source_digest") != source_digest(ent.get("sources", [])):
         return None
     return ent.get("hbm_bytes_per_launch")
-
-
-KERNEL_SOURCES = {
-    "score": ["decode_kv_cache_02_amd/csrc/k_select.hip", "decode_kv_cache_02_amd/csrc/hardkv_internal.h"],
-    "rewrite_attend": ["decode_kv_cache_02_amd/csrc/k_rewrite.hip", "decode_kv_cache_02_amd/csrc/attn_common.h",
-                       "decode_kv_cache_02_amd/csrc/hardkv_internal.h"],
-}
 
 
 # ---- CPU baseline -------------------------------------------------------------------------
@@ -227,6 +324,12 @@ def main():
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); this build has no multi-GPU path.",
               file=sys.stderr)
         sys.exit(2)
+    if args.summarize_kernels:
+        summarize_kernels(*args.summarize_kernels, args.cmd, f"Kernel trace, workload {get_workload(args.config).name}")
+        return
+    if args.summarize_traffic:
+        summarize_traffic(*args.summarize_traffic, args.copy_calib or 1024, get_workload(args.config), args.cmd)
+        return
     hk.require_gpu()
     torch.cuda.set_device(0)
     if args.copy_calib:

@@ -12,7 +12,10 @@ Timing:
   * Single-step workloads (one decode step from the prefilled context): the step is
     captured into a HIP graph and replayed K times between two events, each time from
     the prefilled state restored outside the timed region; every kernel of the step is
-    also timed on its own on exactly that state (hardkv_step_stage, same stream).
+    also timed on its own on exactly that state (hardkv_step_stage, same stream): the
+    ones that only read what earlier kernels wrote R times back to back in one graph, the append and
+    the condensation (which advance the state) as the difference of two graphs, R times
+    (put back what the kernel changes, run it) against R times the put-back alone.
   * The streaming workload: W warmup steps run eagerly, then the K steps are captured
     into one HIP graph and replayed once between two events; kernels that only read
     what earlier ones wrote are timed again on the post-step state.
@@ -22,7 +25,8 @@ Timing:
     computed from the per-unit pool sizes, budgets and condensed blocks of the
     timed steps, replayed eagerly from a snapshot after the timed region.
   * cpu_baseline: the CPU oracle timed on one step of the same workload (a sample
-    of units when the full step would take too long), on the host's cores.
+    of units when the full step would take too long), repeated from the prefilled
+    state for about --cpu-seconds of CPU time, on the host's cores.
 """
 
 from __future__ import annotations
@@ -61,6 +65,7 @@ def parse():
     ap.add_argument("--stage-reps", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-units", type=int, default=0, help="oracle sample size in units (0: automatic)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU time over which the oracle step is timed")
     ap.add_argument("--copy-calib", type=int, default=0,
                     help="only run a device copy of this many MiB (counter calibration) and exit")
     ap.add_argument("--summarize-kernels", nargs=2, metavar=("KERNEL_STATS_CSV", "OUT_TXT"),
@@ -100,12 +105,77 @@ class Layer:
     MUTABLE = ("seq_len", "pool_head", "dense_k", "dense_v", "cond_kn", "cond_vn", "cond_omega",
                "cond_n", "cond_cursor", "error_word")
 
+    # what each state-advancing kernel changes
+    MUTATES = {0: ("seq_len", "dense_k", "dense_v", "error_word"),
+               3: ("pool_head", "cond_kn", "cond_vn", "cond_omega", "cond_n", "cond_cursor")}
+
     def snapshot(self):
         return {n: getattr(self.st, n).clone() for n in self.MUTABLE}
+
+    def time_mutating_stage(self, s, k, reps, trials=5):
+        """Duration of kernel k (append or condense) on the current state: a graph of
+        `reps` times (put back the state it changes, run it) against a graph of the
+        put-backs alone, both replayed between events; the median difference per
+        launch, in us."""
+        names = self.MUTATES[k]
+        snap = {n: getattr(self.st, n).clone() for n in names}
+
+        def put():
+            for n in names:
+                getattr(self.st, n).copy_(snap[n])
+
+        ga, gb = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(ga):
+            for _ in range(reps):
+                put()
+                self.stage(s, k)
+        with torch.cuda.graph(gb):
+            for _ in range(reps):
+                put()
+        torch.cuda.synchronize()
+        diffs = []
+        for _ in range(trials):
+            ta, tb = [], []
+            for g, acc in ((ga, ta), (gb, tb)):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                g.replay()
+                e1.record()
+                torch.cuda.synchronize()
+                acc.append(e0.elapsed_time(e1))
+            diffs.append((ta[0] - tb[0]) * 1e3 / reps)
+        put()
+        torch.cuda.synchronize()
+        return float(np.median(diffs))
 
     def restore(self, snap):
         for n in self.MUTABLE:
             getattr(self.st, n).copy_(snap[n])
+
+
+def time_repeatable_stage(layers, s, k, reps, eager):
+    """Duration per launch of a kernel that only reads what earlier kernels wrote: `reps`
+    launches per layer back to back, captured into one graph (eagerly with --eager) and
+    replayed between events; the median of three replays, in us."""
+    run = lambda: [L.stage(s, k) for _ in range(reps) for L in layers]  # noqa: E731
+    run()
+    torch.cuda.synchronize()
+    g = None
+    if not eager:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            run()
+        torch.cuda.synchronize()
+    ts = []
+    for _ in range(3):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay() if g is not None else run()
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    return float(np.median(ts)) * 1e3 / (reps * len(layers))
 
 
 def unit_bytes(wl, N, kstar, E, t, c_occ):
@@ -282,7 +352,7 @@ def load_traffic(kernel, workload):
 
 
 # ---- CPU baseline -------------------------------------------------------------------------
-def cpu_baseline(wl, layers, units_req):
+def cpu_baseline(wl, layers, units_req, seconds):
     from oracle import hardkv_oracle as orc
     L = layers[0]
     inp = L.inp_cpu_source
@@ -305,16 +375,23 @@ def cpu_baseline(wl, layers, units_req):
     vn = L.inp.v_new[0][:nb].cpu()
     threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     threads = max(1, min(threads, os.cpu_count() or 1))
-    t0 = time.perf_counter()
-    o.step(q, kn, vn, attend=True, nthreads=threads)
-    dt = time.perf_counter() - t0
+    # the sampled step, repeated from the prefilled state until about `seconds` of CPU
+    # time have been measured (the prefill is outside the timed part)
+    total, reps = 0.0, 0
+    while total < seconds and reps < 1000:
+        if reps:
+            assert o.prefill(k_ctx, v_ctx, lens) == 0
+        t0 = time.perf_counter()
+        o.step(q, kn, vn, attend=True, nthreads=threads)
+        total += time.perf_counter() - t0
+        reps += 1
     units = nb * H
-    step_s = dt * total_units / units
+    step_s = total / reps * total_units / units
     return {"value": 1.0 / step_s, "unit": "steps/s", "cores": threads, "kind": "oracle",
-            "sample": f"one full step of {units} of the {total_units} (sequence, KV head) units "
-                      f"({nb} sequences x {H} KV heads of layer 0, same inputs), "
-                      f"{dt:.2f} s, scaled to the whole step",
-            "seconds": dt}
+            "sample": f"{reps} repetitions of one step of {units} of the {total_units} (sequence, KV "
+                      f"head) units ({nb} sequences x {H} KV heads of layer 0, same inputs), "
+                      f"{total:.1f} s in all, scaled to the whole step",
+            "seconds": total}
 
 
 # ---- main ---------------------------------------------------------------------------------
@@ -394,16 +471,15 @@ def main():
         # read what earlier ones wrote run R times back to back; the append and the
         # condensation (which advance the state) run once per restore
         for k in range(len(STAGE_NAMES)):
-            reps = args.stage_reps if k in REPEATABLE else 1
-            ts = []
-            for _ in range(args.stage_reps if k not in REPEATABLE else 1):
-                restore()
-                for j in range(k):
-                    for L in layers:
-                        L.stage(0, j)
-                torch.cuda.synchronize()
-                ts.append(timed(lambda: [L.stage(0, k) for _ in range(reps) for L in layers]) / reps)
-            stage_us[STAGE_NAMES[k]] = float(np.median(ts)) * 1e3 / len(layers)
+            restore()
+            for j in range(k):
+                for L in layers:
+                    L.stage(0, j)
+            torch.cuda.synchronize()
+            if k in REPEATABLE:
+                stage_us[STAGE_NAMES[k]] = time_repeatable_stage(layers, 0, k, args.stage_reps, args.eager)
+            else:
+                stage_us[STAGE_NAMES[k]] = layers[0].time_mutating_stage(0, k, args.stage_reps)
         restore()
         torch.cuda.synchronize()
         snap_after = snaps
@@ -430,13 +506,11 @@ def main():
         acc_steps = list(range(Wm, Wm + K))
         # per-kernel durations of the stages that only read what earlier stages wrote,
         # repeated on the post-step state
+        # (the append and the condensation are not re-run here: an append on the post-step
+        # state would write the next pool row, which may hold a live row of the ring)
         s_last = acc_steps[-1]
         for k in REPEATABLE:
-            for L in layers:
-                L.stage(s_last, k)
-            torch.cuda.synchronize()
-            ms = timed(lambda: [L.stage(s_last, k) for _ in range(args.stage_reps) for L in layers])
-            stage_us[STAGE_NAMES[k]] = ms * 1e3 / (args.stage_reps * len(layers))
+            stage_us[STAGE_NAMES[k]] = time_repeatable_stage(layers, s_last, k, args.stage_reps, args.eager)
 
     # exact algorithmic bytes of the timed steps, replayed eagerly from the snapshot
     for L, sn in zip(layers, snap_after):
@@ -494,7 +568,7 @@ def main():
         "graph_replay_matches_eager": replay_matches,
     }
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(wl, layers, args.cpu_units)
+        res["cpu_baseline"] = cpu_baseline(wl, layers, args.cpu_units, args.cpu_seconds)
     print(json.dumps(res))
 
 

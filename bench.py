@@ -378,7 +378,7 @@ def cpu_baseline(wl, layers, units_req, seconds):
     # the sampled step, repeated from the prefilled state until about `seconds` of CPU
     # time have been measured (the prefill is outside the timed part)
     total, reps = 0.0, 0
-    while total < seconds and reps < 1000:
+    while total < seconds and reps < 20000:
         if reps:
             assert o.prefill(k_ctx, v_ctx, lens) == 0
         t0 = time.perf_counter()

@@ -180,6 +180,15 @@ HK_DEV uint32_t popc_below(uint64_t m) {  // set bits of m below this lane
 }
 HK_DEV uint64_t ballot(bool p) { return __ballot(p); }
 
+// Workgroups of a launch are dispatched round-robin over the 8 XCDs (workgroup i to XCD
+// i mod 8).  xcd_swizzle maps the k-th workgroup that XCD x receives to position k of a
+// contiguous range of the linear work index (XCD x gets range x), so that the chunks one
+// XCD streams are neighbours in memory.  A bijection on [0, total).
+HK_DEV int xcd_swizzle(int lin, int total) {
+  const int q = total >> 3, r = total & 7, x = lin & 7, k = lin >> 3;
+  return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + k;
+}
+
 HK_DEV int64_t pool_end(int64_t t, int W) { return t > W ? t - W : 0; }
 HK_DEV int64_t plan_E(int64_t N, int mode, int S_cap) {
   return (mode != HARDKV_COND_OFF && N > S_cap) ? (N - S_cap + BK - 1) / BK : 0;

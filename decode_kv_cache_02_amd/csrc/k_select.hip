@@ -9,7 +9,7 @@
 // cross-workgroup flags: on MI355X each agent-scope release/acquire writes back or
 // invalidates a whole XCD's L2).
 //
-// hardkv_score, grid (chunks, B*Hkv), 256 threads: streams a chunk of the head's pool
+// hardkv_score, grid (chunks, B*Hkv), 256 threads (XCD-swizzled): streams a chunk of the head's pool
 //   keys with 16-byte loads; 16 lanes hold one 256-byte bf16 row (8 elements each), a
 //   wavefront covers 4 rows per load.  Each lane forms the pairwise sum of its 8
 //   products in registers (tree levels 1-3); levels 4-7 are DPP exchanges inside the
@@ -55,7 +55,8 @@ HK_DEV float wave_max(float v) {
 template <typename T, int G>
 __global__ __launch_bounds__(NTHREADS) void hardkv_score(Args a) {
   constexpr int EB = Elem<T>::bytes;
-  const int bh = a.bh0 + blockIdx.y, chunk = blockIdx.x;
+  const int lin = xcd_swizzle(blockIdx.y * gridDim.x + blockIdx.x, gridDim.x * gridDim.y);
+  const int bh = a.bh0 + lin / gridDim.x, chunk = lin % gridDim.x;
   const int b = bh / a.Hkv, h = bh - b * a.Hkv;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int sub = lane & 15, grp = lane >> 4;

@@ -80,8 +80,11 @@ int32_t plan(const hardkv_config *cfg, Plan &p) {
   const int cb = (int)std::max<int64_t>(1, std::min<int64_t>(8, work / 1024));
   a.cb_score = cb;
   a.nch_score = (a.P + cb - 1) / cb;
-  a.cb_reg = 4;  // one pool block per wavefront of the rewrite workgroup
-  a.nch_reg = (a.P + a.cb_reg - 1) / a.cb_reg;
+  // rewrite chunks of 4 blocks (one per wavefront) over the survivor blocks only: at most
+  // S_cap / 64 of them after condensation, the whole ring in mode OFF
+  const int max_survivor_blocks = a.mode == HARDKV_COND_OFF ? a.P : std::min(a.P, a.S_cap / BK);
+  a.cb_reg = 4;
+  a.nch_reg = (max_survivor_blocks + a.cb_reg - 1) / a.cb_reg;
   a.rv_att = 256;
   a.nv_att = (a.V_cap + a.rv_att - 1) / a.rv_att;
   a.rc_att = 64;

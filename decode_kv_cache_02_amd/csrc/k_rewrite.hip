@@ -4,8 +4,9 @@
 // into contiguous ranges, each head owning a fixed-capacity view (the max-length form
 // of Flatten Index), so that attention reads static, contiguous, fixed-stride blocks.
 //
-// Grid (chunks [+ attention segments], B*Hkv), 256 threads.  A chunk is four pool
-// blocks, one per wavefront.  From the block's weights and the head's cut (w_th, r,
+// Grid (chunks [+ attention segments], B*Hkv), 256 threads.  A chunk is four survivor
+// blocks, one per wavefront (sixteen, four per wavefront, for a head that keeps at most a
+// quarter of its survivors).  From the block's weights and the head's cut (w_th, r,
 // and the block's ties-before count from the select stage) each lane decides whether its
 // row is kept: w > w_th, or w == w_th and its tie rank (ties before the block plus the
 // mbcnt of equal weights below it) is under r.  The ballot of those bits is the block's
@@ -27,7 +28,8 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_rewrite(Args a) {
   constexpr int EB = Elem<T>::bytes;
   constexpr size_t ROWB = (size_t)HD * EB;
   const int bh = a.bh0 + blockIdx.y, chunk = blockIdx.x;
-  __shared__ uint8_t s_list[4][64];
+  __shared__ uint32_t s_src[4][4 * BK];  // per wavefront: kept rows (pool ring row of the head)
+  __shared__ uint32_t s_dst[4][4 * BK];  // and their view rows
   __shared__ float s_part[ATTN ? 4 : 1][G][2 + HD];
   if (ATTN && chunk >= a.nch_reg) {  // condensed / dense attention segments
     attend_segment<T, G>(a, bh, a.nv_att + (chunk - a.nch_reg), s_part);
@@ -45,22 +47,26 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_rewrite(Args a) {
   const int64_t pend = pool_end(t, a.W);
   const int nblk = (int)((pend + BK - 1) / BK - c / BK);
   const int pb_lo = (int)((c / BK) % P);
-  const int i0 = chunk * a.cb_reg, i1 = min(i0 + a.cb_reg, P);
+  // Chunks cover the survivor blocks [nx, nblk) (pool-relative block indices; the select
+  // kernel has cleared every mask word).  Blocks per wavefront: one when the head keeps
+  // more than a quarter of its survivors, else four (a chunk then spans 4 * cb_reg blocks
+  // and the chunks past the survivors are empty), so that sparse selections fill the
+  // 16-row copy batches of fewer workgroups.
+  const int nub = max(0, nblk - nx);
+  const int bpw = ((int64_t)hd->kstar * 4 <= (int64_t)nub * BK) ? 4 : 1;
+  const int i0 = nx + chunk * a.cb_reg * bpw, i1 = min(i0 + a.cb_reg * bpw, nblk);
   auto ring = [&](int i) { return pb_lo + i >= P ? pb_lo + i - P : pb_lo + i; };
 
-  // A chunk that keeps no row (all its blocks condensed, outside the pool, or with no
-  // kept token: the first view rows of its first survivor block and of the block after
-  // it are equal) only clears its mask words and leaves an empty partial.
+  // A chunk that keeps no row (past the survivors, or no kept token: the first view rows
+  // of its first block and of the block after it are equal) leaves an empty partial.
   {
-    const int ia = max(i0, nx), ib = min(i1, nblk);
-    bool empty = ia >= ib;
+    bool empty = i0 >= i1;
     if (!empty) {
-      const uint32_t x0 = a.blkinfo[(size_t)bh * P + ring(ia)].x;
-      const uint32_t x1 = ib < nblk ? a.blkinfo[(size_t)bh * P + ring(ib)].x : (uint32_t)hd->kstar;
+      const uint32_t x0 = a.blkinfo[(size_t)bh * P + ring(i0)].x;
+      const uint32_t x1 = i1 < nblk ? a.blkinfo[(size_t)bh * P + ring(i1)].x : (uint32_t)hd->kstar;
       empty = x1 == x0;
     }
     if (empty) {
-      if (MASK && tid < i1 - i0) a.mask[(size_t)bh * P + ring(i0 + tid)] = 0ull;
       if (ATTN && tid < G) {
         float *o = a.part + ((size_t)bh * a.npart + chunk) * G * (2 + HD) + (size_t)tid * (2 + HD);
         o[0] = -INFINITY;
@@ -83,30 +89,44 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_rewrite(Args a) {
   char *vv = (char *)a.view_v + (size_t)bh * V * ROWB + sub * 8 * EB;
   int32_t *vpos = a.view_pos + (size_t)bh * V;
 
-  for (int i = i0 + wave; i < i1; i += 4) {
+  // the wavefront's blocks: weights and block info of all of them in flight at once
+  const int iw = i0 + wave * bpw;
+  uint32_t wv[4];
+  uint2 bi[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int i = iw + j;
+    const bool live = j < bpw && i < i1;
+    const int64_t p = c + (int64_t)i * BK + lane;
+    wv[j] = (live && p < pend) ? a.weights[rowbase + (size_t)ring(i) * BK + lane] : 0u;
+    bi[j] = live ? a.blkinfo[(size_t)bh * P + ring(i)] : make_uint2(0u, 0u);
+  }
+  // mask words, and the list of kept rows in position order
+  int ns = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int i = iw + j;
+    if (j >= bpw || i >= i1) break;  // wave-uniform
     const int pb = ring(i);
-    if (i < nx || i >= nblk) {  // condensed this step, or holds no pool position
-      if (MASK && lane == 0) a.mask[(size_t)bh * P + pb] = 0ull;
-      continue;
-    }
     const int64_t p = c + (int64_t)i * BK + lane;
     const bool valid = p < pend;
-    const uint32_t w = valid ? a.weights[rowbase + (size_t)pb * BK + lane] : 0u;
-    const uint2 bi = a.blkinfo[(size_t)bh * P + pb];  // (first view row, ties before)
+    const uint32_t w = wv[j];
     const uint64_t eqm = ballot(valid && w == w_th);
-    const bool sel = valid && (w > w_th || (w == w_th && bi.y + popc_below(eqm) < r));
+    const bool sel = valid && (w > w_th || (w == w_th && bi[j].y + popc_below(eqm) < r));
     const uint64_t mw = ballot(sel);
     if (MASK && lane == 0) a.mask[(size_t)bh * P + pb] = mw;
     if (!COPY || mw == 0) continue;  // wave-uniform
-    const uint32_t vo = bi.x;
-    const uint32_t idx = popc_below(mw);
+    const uint32_t vo = bi[j].x, idx = popc_below(mw);
     if (sel) {
-      s_list[wave][idx] = (uint8_t)lane;
+      s_src[wave][ns + idx] = (uint32_t)(pb * BK + lane);
+      s_dst[wave][ns + idx] = vo + idx;
       if (vo + idx < (uint32_t)V) vpos[vo + idx] = (int32_t)p;
     }
+    ns += __popcll(mw);
+  }
+  if (COPY) {
     wave_sync();
-    const int ns = __popcll(mw);
-    const char *pkb = pk + (size_t)pb * BK * ROWB, *pvb = pv + (size_t)pb * BK * ROWB;
+    // kept rows copied 16 at a time (4 per 16-lane group), attended while in registers
     for (int it = 0; it < ns; it += 16) {
       Raw8<T> kr[4], vr[4];
       bool act[4];
@@ -114,12 +134,13 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_rewrite(Args a) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int k = it + j * 4 + grp;
-        dst[j] = vo + (uint32_t)k;
+        const int kk = k < ns ? k : 0;
+        const uint32_t src = s_src[wave][kk];
+        dst[j] = s_dst[wave][kk];
         act[j] = k < ns && dst[j] < (uint32_t)V;
-        const int row = s_list[wave][k < ns ? k : 0];
         if (act[j]) {
-          raw_load_nt(pkb + (size_t)row * ROWB, kr[j]);
-          raw_load_nt(pvb + (size_t)row * ROWB, vr[j]);
+          raw_load_nt(pk + (size_t)src * ROWB, kr[j]);
+          raw_load_nt(pv + (size_t)src * ROWB, vr[j]);
         } else {
           kr[j] = Raw8<T>{};
           vr[j] = Raw8<T>{};
@@ -134,7 +155,6 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_rewrite(Args a) {
       }
       if (ATTN) attn_rows<T, G, 4>(st, qs, kr, vr, act);
     }
-    wave_sync();
   }
   if (ATTN) attn_write_partial<G>(st, a.part + ((size_t)bh * a.npart + chunk) * G * (2 + HD), s_part);
 }

@@ -23,7 +23,8 @@
 //   gathers the bucket's tokens into LDS, where two more histogram levels give the
 //   exact threshold weight w_th and the number r of ties at w_th that are kept (ties go
 //   to the lowest positions).  A scan over blocks gives each block its first view row
-//   and its ties-before count; the rewrite kernel derives the mask bits from them.
+//   and its ties-before count; the rewrite kernel derives the mask bits from them.  The
+//   select kernel clears all the head's mask words; the rewrite writes the survivors'.
 #include "hardkv_internal.h"
 
 namespace hardkv {
@@ -328,6 +329,8 @@ __global__ __launch_bounds__(SEL_THREADS) void hardkv_select(Args a) {
   if (lane == 0) sh.fred[wave] = mx;
   for (int i = tid; i < NB1; i += SEL_THREADS) sh.hist[i] = 0ull;
   if (tid == 0) sh.ncand = 0;
+  // every mask word starts empty; the rewrite kernel writes the survivor blocks' words
+  for (int i = tid; i < P; i += SEL_THREADS) a.mask[(size_t)bh * P + i] = 0ull;
   __syncthreads();
   float m = -INFINITY;
 #pragma unroll

@@ -62,6 +62,11 @@ def parse():
     ap.add_argument("--config", default="c2")
     ap.add_argument("--top-p", type=float, default=None, help="override p (the mixed-length workload sweeps it)")
     ap.add_argument("--eager", action="store_true", help="no graph (for counter runs)")
+    ap.add_argument("--regularize", choices=["rewrite", "sparse", "mti"], default="rewrite",
+                    help="Rewrite Cache for every head (default), Sparse Loading for every head, or "
+                         "the budget-threshold rule (rewrite iff --mti-lower <= k* <= --mti-upper)")
+    ap.add_argument("--mti-lower", type=int, default=0)
+    ap.add_argument("--mti-upper", type=int, default=1 << 30)
     ap.add_argument("--stage-reps", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-units", type=int, default=0, help="oracle sample size in units (0: automatic)")
@@ -80,11 +85,15 @@ def parse():
 
 
 # ---- layers ------------------------------------------------------------------------------
+POLICY = {"rewrite": hk.HARDKV_REG_REWRITE, "sparse": hk.HARDKV_REG_SPARSE, "mti": hk.HARDKV_REG_MTI}
+
+
 class Layer:
-    def __init__(self, wl, layer, steps, top_p=None):
+    def __init__(self, wl, layer, steps, top_p=None, policy=("rewrite", 0, 0)):
         self.wl = wl
         self.inp = make_inputs(wl, layer=layer, device="cuda", steps=steps)
-        self.cfg = hk.Config.from_workload(wl, top_p=top_p)
+        self.cfg = hk.Config.from_workload(wl, top_p=top_p, regularize=POLICY[policy[0]],
+                                           mti_lower=policy[1], mti_upper=policy[2])
         self.st = hk.State(self.cfg)
         hk.hardkv_prefill(self.cfg, self.st, self.inp.k_ctx, self.inp.v_ctx, self.inp.ctx_len)
         self.out = torch.zeros((wl.batch, wl.num_q_heads, D), dtype=torch.float32, device="cuda")
@@ -178,10 +187,11 @@ def time_repeatable_stage(layers, s, k, reps, eager):
     return float(np.median(ts)) * 1e3 / (reps * len(layers))
 
 
-def unit_bytes(wl, N, kstar, E, t, c_occ):
+def unit_bytes(wl, N, kstar, E, t, c_occ, rw):
     """Algorithmic bytes per stage for arrays of per-unit values (one step).
 
-    score: the pool keys; rewrite_attend: the kept rows read and written once, the dense
+    score: the pool keys; rewrite_attend: the kept rows read once, and written once for the
+    heads that are rewritten (rw), the dense
     window and the occupied condensed slots read, q in; condense (merge): the keys and
     values of the condensing blocks read and the slot read-modify-write (eviction moves
     nothing); append: the leaving dense row read and written to the pool, the new token
@@ -197,7 +207,7 @@ def unit_bytes(wl, N, kstar, E, t, c_occ):
         "score": e * D * N,
         "select": 0 * N,
         "condense": cond,
-        "rewrite_attend": 4 * e * D * kstar + 2 * e * D * dense_rows + (8 * D + 8) * c_occ + G * D * e,
+        "rewrite_attend": (2 + 2 * rw) * e * D * kstar + 2 * e * D * dense_rows + (8 * D + 8) * c_occ + G * D * e,
         "combine": G * D * 4 * np.ones_like(N),
     }
 
@@ -217,7 +227,8 @@ def step_accounting(layers, s):
         kstar = L.st.budget.cpu().numpy().astype(np.int64)
         E = L.st.n_condense.cpu().numpy().astype(np.int64)
         c_occ = (L.st.cond_n.cpu().numpy() > 0).sum(-1)
-        ub = unit_bytes(wl, N, kstar, E, np.broadcast_to(t1, N.shape), c_occ)
+        rw = L.st.regularized.cpu().numpy().astype(np.int64)
+        ub = unit_bytes(wl, N, kstar, E, np.broadcast_to(t1, N.shape), c_occ, rw)
         for k in tot:
             tot[k] += float(ub[k].sum())
         scanned += int(N.sum())
@@ -421,7 +432,7 @@ def main():
 
     layers = []
     for layer in range(wl.layers):
-        L = Layer(wl, layer, nsteps, top_p=top_p)
+        L = Layer(wl, layer, nsteps, top_p=top_p, policy=(args.regularize, args.mti_lower, args.mti_upper))
         if layer == 0 and not args.no_cpu_baseline:
             L.inp_cpu_source = {"k_ctx": L.inp.k_ctx, "v_ctx": L.inp.v_ctx, "ctx_len": L.inp.ctx_len}
         else:
@@ -554,6 +565,8 @@ def main():
                    "kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim, "dense_window": wl.dense_window,
                    "sparse_cap": wl.sparse_cap, "condensed_slots": wl.condensed_slots,
                    "top_p": float(layers[0].cfg.c.top_p), "cond_mode": "merge",
+                   "regularize": args.regularize if args.regularize != "mti" else
+                   f"mti [{args.mti_lower}, {args.mti_upper}]",
                    "timing": ("one-step graph replay from the prefilled state" if restore_mode else
                               "graph of the K streaming steps") + (" (eager)" if args.eager else "")},
         "kv_tokens_scanned_per_s": scanned_step * steps_per_s,

@@ -199,7 +199,9 @@ HK_DEV void attend_segment(const Args &a, int bh, int seg, float (*s_part)[G][2 
   int slot;
   if (seg < a.nv_att) {  // view rows
     slot = seg;
-    const int64_t kst = min((int64_t)a.budget[bh], (int64_t)a.V_cap);
+    // a head that was not rewritten this step has no valid view (its kept rows are
+    // attended from the pool by the rewrite kernel instead)
+    const int64_t kst = a.head[bh].rw ? min((int64_t)a.budget[bh], (int64_t)a.V_cap) : 0;
     const int64_t r0 = (int64_t)seg * a.rv_att, r1 = min(r0 + (int64_t)a.rv_att, kst);
     const char *vk = (const char *)a.view_k + (size_t)bh * a.V_cap * ROWB + sub * 8 * EB;
     const char *vv = (const char *)a.view_v + (size_t)bh * a.V_cap * ROWB + sub * 8 * EB;

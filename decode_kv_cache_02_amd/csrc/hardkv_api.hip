@@ -49,6 +49,9 @@ int32_t plan(const hardkv_config *cfg, Plan &p) {
   if (!cfg->tau) return HARDKV_EINVAL;
   for (int h = 0; h < cfg->num_kv_heads; ++h)
     if (!(cfg->tau[h] > 0.0f)) return HARDKV_EINVAL;
+  if (cfg->regularize < HARDKV_REG_REWRITE || cfg->regularize > HARDKV_REG_MTI) return HARDKV_EINVAL;
+  if (cfg->regularize == HARDKV_REG_MTI && (cfg->mti_lower < 0 || cfg->mti_upper < cfg->mti_lower))
+    return HARDKV_EINVAL;
 
   a.B = cfg->batch;
   a.Hq = cfg->num_q_heads;
@@ -61,6 +64,9 @@ int32_t plan(const hardkv_config *cfg, Plan &p) {
   a.C = cfg->condensed_slots;
   a.mode = cfg->cond_mode;
   a.merge_bias = cfg->merge_bias ? 1 : 0;
+  a.reg_policy = cfg->regularize;
+  a.mti_lower = cfg->mti_lower;
+  a.mti_upper = cfg->mti_upper;
   a.pq = (uint32_t)pq;
   {
     // Taylor coefficients (ln 2)^i / i! of 2^f, rounded once to fp32
@@ -92,7 +98,8 @@ int32_t plan(const hardkv_config *cfg, Plan &p) {
   a.rd_att = 128;
   a.nd_att = (a.W + a.rd_att - 1) / a.rd_att;
   a.part_cd_base = std::max(a.nch_reg, a.nv_att);
-  a.npart = a.part_cd_base + a.nc_att + a.nd_att;
+  a.xp_base = a.part_cd_base + a.nc_att + a.nd_att;  // then one slot per rewrite chunk
+  a.npart = a.xp_base + a.nch_reg;
   if (a.mode == HARDKV_COND_MERGE) {
     const int emax = std::max(1, a.P - a.S_cap / BK);
     a.ncs = std::min(a.C, emax);
@@ -146,6 +153,8 @@ int32_t bind(const hardkv_state *st, Plan &p) {
   a.w_all = st->w_all;
   a.w_u = st->w_u;
   a.thresh = st->thresh;
+  if (st->regularized && ((uintptr_t)st->regularized & 3u)) return HARDKV_EINVAL;
+  a.regularized = st->regularized;
   a.error_word = st->error_word;
   char *ws = (char *)st->workspace;
   a.head = reinterpret_cast<HeadInfo *>(ws + p.off_head);
@@ -173,6 +182,8 @@ const char *const kStageNames[NSTAGES] = {"append", "score", "select", "condense
 hipError_t step_stage(const hardkv_config *cfg, Args &a, int stage, hipStream_t s) {
   const bool bf = is_bf16(cfg);
   a.nvp = a.nch_reg;
+  a.nxp = 0;
+  a.gather_mode = GATHER_STEP;
   switch (stage) {
     case 0: return launch_append(a, s, bf);
     case 1: return launch_score(a, s, bf);
@@ -182,6 +193,24 @@ hipError_t step_stage(const hardkv_config *cfg, Args &a, int stage, hipStream_t 
     case 5: return launch_combine(a, s);
     default: return hipErrorInvalidValue;
   }
+}
+
+// The standalone attention: the tier kernel attends the view segments of the rewritten
+// heads (none under SPARSE, or when `sparse` asks for Sparse Loading everywhere) and the
+// condensed and dense segments; the rewrite kernel gathers and attends the kept rows of
+// the other heads (none under REWRITE) from the pool; the combine reduces both.
+hipError_t attend_calls(const hardkv_config *cfg, Args &a, hipStream_t s, bool sparse) {
+  const bool bf = is_bf16(cfg);
+  const bool views = !sparse && a.reg_policy != HARDKV_REG_SPARSE;
+  const bool gather = sparse || a.reg_policy != HARDKV_REG_REWRITE;
+  if (!views) a.nv_att = 0;
+  a.nvp = a.nv_att;
+  a.nxp = gather ? a.nch_reg : 0;
+  a.gather_mode = sparse ? GATHER_ATTEND_ALL : GATHER_ATTEND_NRW;
+  hipError_t e = launch_attend(a, s, bf);
+  if (e == hipSuccess && gather) e = launch_rewrite(a, s, bf, false, true, true);
+  if (e == hipSuccess) e = launch_combine(a, s);
+  return e;
 }
 
 // The fused step: every stage over all units, in stream order.
@@ -251,6 +280,7 @@ int32_t hardkv_regularize(const hardkv_config *cfg, hardkv_state *st, void *stre
   Plan p;
   int32_t rc = setup(cfg, st, p);
   if (rc != HARDKV_OK) return rc;
+  p.a.gather_mode = GATHER_REWRITE;
   return hip_status(launch_rewrite(p.a, (hipStream_t)stream, is_bf16(cfg), false, true, false));
 }
 
@@ -269,11 +299,18 @@ int32_t hardkv_attend(const hardkv_config *cfg, hardkv_state *st, const void *q,
   if (!aligned16(q) || !aligned16(out)) return HARDKV_EINVAL;
   p.a.q = q;
   p.a.out = out;
-  p.a.nvp = p.a.nv_att;
-  hipStream_t s = (hipStream_t)stream;
-  hipError_t e = launch_attend(p.a, s, is_bf16(cfg));
-  if (e == hipSuccess) e = launch_combine(p.a, s);
-  return hip_status(e);
+  return hip_status(attend_calls(cfg, p.a, (hipStream_t)stream, false));
+}
+
+int32_t hardkv_attend_sparse(const hardkv_config *cfg, hardkv_state *st, const void *q, float *out,
+                             void *stream) {
+  Plan p;
+  int32_t rc = setup(cfg, st, p);
+  if (rc != HARDKV_OK) return rc;
+  if (!aligned16(q) || !aligned16(out)) return HARDKV_EINVAL;
+  p.a.q = q;
+  p.a.out = out;
+  return hip_status(attend_calls(cfg, p.a, (hipStream_t)stream, true));
 }
 
 int32_t hardkv_step(const hardkv_config *cfg, hardkv_state *st, const void *q, const void *k_new,

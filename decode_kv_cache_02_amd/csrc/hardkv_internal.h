@@ -27,7 +27,7 @@ struct alignas(64) HeadInfo {
   int32_t kstar;
   int32_t E;        // blocks to condense
   int32_t nu_plan;  // condensed-slot cursor before condensation
-  int32_t pad0;
+  int32_t rw;       // 1: the head's kept rows are rewritten into its view this step
   uint64_t w_all;
   uint64_t pad1[2];
 };
@@ -48,6 +48,7 @@ struct Args {
   uint64_t *mask;
   int32_t *budget, *n_condense;
   uint64_t *w_all, *w_u, *thresh;
+  int32_t *regularized;     // may be null
   uint32_t *error_word;
   // workspace
   HeadInfo *head;
@@ -67,6 +68,9 @@ struct Args {
   int rd_att, nd_att;       // attention over the dense window
   int nvp;                  // view partial slots written by this call
   int npart, part_cd_base;  // partial slots per head; first condensed/dense slot
+  int xp_base, nxp;         // gathered-row partial slots of the standalone attention
+  int reg_policy, mti_lower, mti_upper;  // regularize policy and its budget thresholds
+  int gather_mode;          // rewrite kernel: GATHER_* below
   int ncs;                  // condense workgroups per head
   int bh0, nbh;             // (sequence, KV head) units this launch covers: [bh0, bh0 + nbh)
   uint32_t pq;
@@ -74,6 +78,14 @@ struct Args {
   float kappa[HARDKV_MAX_KV_HEADS];
   float att_scale;          // log2(e) / sqrt(D): logits in base 2
 };
+
+// What the rewrite kernel does with the kept rows it gathers from the pool:
+//   GATHER_STEP       fused step: attend them; store them into the view if the head's rw
+//   GATHER_REWRITE    standalone regularize: store them if rw
+//   GATHER_ATTEND_NRW standalone attention: attend them for heads with rw == 0 only
+//   GATHER_ATTEND_ALL Sparse Loading attention: attend them for every head
+// The attending modes other than GATHER_STEP write their partials at xp_base + chunk.
+enum { GATHER_STEP = 0, GATHER_REWRITE = 1, GATHER_ATTEND_NRW = 2, GATHER_ATTEND_ALL = 3 };
 
 // launchers (one per kernel); each returns a hipError_t
 hipError_t launch_prefill(const Args &a, hipStream_t s, bool bf16);

@@ -38,8 +38,13 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_combine(Args a) {
   __shared__ float s_acc[HD];
   const float *base = a.part + (size_t)bh * a.npart * G * (2 + HD) + (size_t)g * (2 + HD);
   const size_t stride = (size_t)G * (2 + HD);  // from one partial slot to the next
-  const int ns = a.nvp + a.nc_att + a.nd_att;
-  auto slot = [&](int i) { return i < a.nvp ? i : a.part_cd_base + (i - a.nvp); };
+  const int ncd = a.nc_att + a.nd_att;
+  const int ns = a.nvp + ncd + a.nxp;
+  // partials: view or rewrite chunks at [0, nvp), condensed and dense segments at
+  // part_cd_base, gathered-row chunks of the standalone attention at xp_base
+  auto slot = [&](int i) {
+    return i < a.nvp ? i : (i < a.nvp + ncd ? a.part_cd_base + (i - a.nvp) : a.xp_base + (i - a.nvp - ncd));
+  };
 
   // the common maximum of the partials that saw any row
   float M = -INFINITY;

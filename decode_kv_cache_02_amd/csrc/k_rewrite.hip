@@ -31,16 +31,23 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_rewrite(Args a) {
   __shared__ uint32_t s_src[4][4 * BK];  // per wavefront: kept rows (pool ring row of the head)
   __shared__ uint32_t s_dst[4][4 * BK];  // and their view rows
   __shared__ float s_part[ATTN ? 4 : 1][G][2 + HD];
-  if (ATTN && chunk >= a.nch_reg) {  // condensed / dense attention segments
+  if (ATTN && chunk >= a.nch_reg) {  // condensed / dense attention segments (fused step)
     attend_segment<T, G>(a, bh, a.nv_att + (chunk - a.nch_reg), s_part);
     return;
   }
+  // partial slot of this chunk's gathered rows
+  const int pslot = a.gather_mode == GATHER_STEP ? chunk : a.xp_base + chunk;
   const int b = bh / a.Hkv, h = bh - b * a.Hkv;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int sub = lane & 15, grp = lane >> 4;
   const int P = a.P, V = a.V_cap;
 
   const HeadInfo *hd = a.head + bh;
+  // store the gathered rows into the view only when the head is rewritten this step; in
+  // the standalone attention of a mixed policy, rewritten heads are attended from their
+  // views by the tier kernel instead
+  const bool store = COPY && (a.gather_mode == GATHER_STEP || a.gather_mode == GATHER_REWRITE) && hd->rw;
+  const bool skip = a.gather_mode == GATHER_ATTEND_NRW && hd->rw;
   const int64_t t = hd->t_plan, c = hd->c_plan;
   const uint32_t w_th = hd->w_th, r = hd->r;
   const int nx = hd->E;
@@ -60,7 +67,7 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_rewrite(Args a) {
   // A chunk that keeps no row (past the survivors, or no kept token: the first view rows
   // of its first block and of the block after it are equal) leaves an empty partial.
   {
-    bool empty = i0 >= i1;
+    bool empty = i0 >= i1 || skip || (!ATTN && !MASK && !store);
     if (!empty) {
       const uint32_t x0 = a.blkinfo[(size_t)bh * P + ring(i0)].x;
       const uint32_t x1 = i1 < nblk ? a.blkinfo[(size_t)bh * P + ring(i1)].x : (uint32_t)hd->kstar;
@@ -68,7 +75,7 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_rewrite(Args a) {
     }
     if (empty) {
       if (ATTN && tid < G) {
-        float *o = a.part + ((size_t)bh * a.npart + chunk) * G * (2 + HD) + (size_t)tid * (2 + HD);
+        float *o = a.part + ((size_t)bh * a.npart + pslot) * G * (2 + HD) + (size_t)tid * (2 + HD);
         o[0] = -INFINITY;
         o[1] = 0.0f;
       }
@@ -120,7 +127,7 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_rewrite(Args a) {
     if (sel) {
       s_src[wave][ns + idx] = (uint32_t)(pb * BK + lane);
       s_dst[wave][ns + idx] = vo + idx;
-      if (vo + idx < (uint32_t)V) vpos[vo + idx] = (int32_t)p;
+      if (store && vo + idx < (uint32_t)V) vpos[vo + idx] = (int32_t)p;
     }
     ns += __popcll(mw);
   }
@@ -137,7 +144,7 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_rewrite(Args a) {
         const int kk = k < ns ? k : 0;
         const uint32_t src = s_src[wave][kk];
         dst[j] = s_dst[wave][kk];
-        act[j] = k < ns && dst[j] < (uint32_t)V;
+        act[j] = k < ns && (!store || dst[j] < (uint32_t)V);
         if (act[j]) {
           raw_load_nt(pk + (size_t)src * ROWB, kr[j]);
           raw_load_nt(pv + (size_t)src * ROWB, vr[j]);
@@ -146,22 +153,24 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_rewrite(Args a) {
           vr[j] = Raw8<T>{};
         }
       }
+      if (store) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if (act[j]) {
-          raw_store_nt(vk + (size_t)dst[j] * ROWB, kr[j]);
-          raw_store_nt(vv + (size_t)dst[j] * ROWB, vr[j]);
+        for (int j = 0; j < 4; ++j) {
+          if (act[j]) {
+            raw_store_nt(vk + (size_t)dst[j] * ROWB, kr[j]);
+            raw_store_nt(vv + (size_t)dst[j] * ROWB, vr[j]);
+          }
         }
       }
       if (ATTN) attn_rows<T, G, 4>(st, qs, kr, vr, act);
     }
   }
-  if (ATTN) attn_write_partial<G>(st, a.part + ((size_t)bh * a.npart + chunk) * G * (2 + HD), s_part);
+  if (ATTN) attn_write_partial<G>(st, a.part + ((size_t)bh * a.npart + pslot) * G * (2 + HD), s_part);
 }
 
 template <typename T, bool MASK, bool COPY, bool ATTN>
 hipError_t launch_g(const Args &a, hipStream_t s) {
-  dim3 grid(a.nch_reg + (ATTN ? a.nc_att + a.nd_att : 0), a.nbh);
+  dim3 grid(a.nch_reg + (ATTN && a.gather_mode == GATHER_STEP ? a.nc_att + a.nd_att : 0), a.nbh);
   switch (a.G) {
     case 1: hipLaunchKernelGGL((hardkv_rewrite<T, 1, MASK, COPY, ATTN>), grid, dim3(NTHREADS), 0, s, a); break;
     case 2: hipLaunchKernelGGL((hardkv_rewrite<T, 2, MASK, COPY, ATTN>), grid, dim3(NTHREADS), 0, s, a); break;
@@ -177,6 +186,7 @@ hipError_t launch_t(const Args &a, hipStream_t s, bool mask, bool copy, bool att
   if (mask && copy && attend) return launch_g<T, true, true, true>(a, s);
   if (mask && !copy && !attend) return launch_g<T, true, false, false>(a, s);
   if (!mask && copy && !attend) return launch_g<T, false, true, false>(a, s);
+  if (!mask && copy && attend) return launch_g<T, false, true, true>(a, s);
   return hipErrorInvalidValue;
 }
 

@@ -563,7 +563,14 @@ __global__ __launch_bounds__(SEL_THREADS) void hardkv_select(Args a) {
     hd->E = (int32_t)E;
     hd->nu_plan = a.cond_cursor[bh];
     hd->w_all = W_all;
-    if (kstar > a.V_cap) atomicOr(a.error_word, HARDKV_ERR_VIEW_OVERFLOW);
+    // the regularize policy: rewrite every head, none, or those whose budget lies in
+    // [L_lower, L_upper]
+    const int rw = a.reg_policy == HARDKV_REG_REWRITE ? 1
+                   : a.reg_policy == HARDKV_REG_SPARSE ? 0
+                   : (kstar >= a.mti_lower && kstar <= a.mti_upper) ? 1 : 0;
+    hd->rw = rw;
+    if (a.regularized) a.regularized[bh] = rw;
+    if (rw && kstar > a.V_cap) atomicOr(a.error_word, HARDKV_ERR_VIEW_OVERFLOW);
   }
 }
 

@@ -20,11 +20,12 @@ LIB_PATH = os.path.join(HERE, "libhardkv.so")
 HARDKV_OK, HARDKV_EINVAL, HARDKV_EUNSUPPORTED, HARDKV_ECAPACITY, HARDKV_EHIP = 0, -1, -2, -3, -4
 HARDKV_BF16, HARDKV_F32 = 0, 1
 HARDKV_COND_OFF, HARDKV_COND_EVICT, HARDKV_COND_MERGE = 0, 1, 2
+HARDKV_REG_REWRITE, HARDKV_REG_SPARSE, HARDKV_REG_MTI = 0, 1, 2
 HARDKV_ERR_POOL_OVERFLOW, HARDKV_ERR_VIEW_OVERFLOW, HARDKV_ERR_NONFINITE = 1, 2, 4
 BLOCK, HEAD_DIM = 64, 128
 
 EXPORTS = ("hardkv_workspace_size", "hardkv_prefill", "hardkv_append", "hardkv_select",
-           "hardkv_regularize", "hardkv_condense", "hardkv_attend", "hardkv_step",
+           "hardkv_regularize", "hardkv_condense", "hardkv_attend", "hardkv_attend_sparse", "hardkv_step",
            "hardkv_step_stage", "hardkv_step_num_stages", "hardkv_step_stage_name",
            "hardkv_strerror")
 
@@ -42,13 +43,14 @@ class hardkv_config(C.Structure):
         ("pool_blocks", C.c_int32), ("sparse_cap", C.c_int32), ("view_cap", C.c_int32),
         ("condensed_slots", C.c_int32), ("cond_mode", C.c_int32), ("merge_bias", C.c_int32),
         ("top_p", C.c_double), ("tau", C.POINTER(C.c_float)),
+        ("regularize", C.c_int32), ("mti_lower", C.c_int32), ("mti_upper", C.c_int32),
     ]
 
 
 _STATE_FIELDS = ("dense_k", "dense_v", "pool_k", "pool_v", "view_k", "view_v", "view_pos",
                  "cond_kn", "cond_vn", "cond_omega", "cond_n", "cond_cursor", "seq_len",
                  "pool_head", "scores", "weights", "mask", "budget", "n_condense", "w_all",
-                 "w_u", "thresh", "error_word", "workspace")
+                 "w_u", "thresh", "regularized", "error_word", "workspace")
 
 
 class hardkv_state(C.Structure):
@@ -74,6 +76,7 @@ def lib() -> C.CDLL:
         L.hardkv_regularize.argtypes = [cp, sp, vp]
         L.hardkv_condense.argtypes = [cp, sp, vp]
         L.hardkv_attend.argtypes = [cp, sp, vp, vp, vp]
+        L.hardkv_attend_sparse.argtypes = [cp, sp, vp, vp, vp]
         L.hardkv_step.argtypes = [cp, sp, vp, vp, vp, vp, vp]
         L.hardkv_step_stage.argtypes = [cp, sp, vp, vp, vp, vp, i32, vp]
         L.hardkv_step_num_stages.argtypes = []
@@ -118,24 +121,28 @@ class Config:
     def __init__(self, batch: int, num_q_heads: int, num_kv_heads: int, dtype: str,
                  dense_window: int, pool_blocks: int, sparse_cap: int, view_cap: int,
                  condensed_slots: int, cond_mode: int, top_p: float,
-                 tau: Sequence[float], head_dim: int = HEAD_DIM, merge_bias: bool = True):
+                 tau: Sequence[float], head_dim: int = HEAD_DIM, merge_bias: bool = True,
+                 regularize: int = HARDKV_REG_REWRITE, mti_lower: int = 0, mti_upper: int = 0):
         self.tau_arr = (C.c_float * max(1, len(tau)))(*[float(x) for x in tau])
         self.c = hardkv_config(batch, num_q_heads, num_kv_heads, head_dim,
                                HARDKV_BF16 if dtype == "bf16" else HARDKV_F32, dense_window,
                                pool_blocks, sparse_cap, view_cap, condensed_slots, cond_mode,
                                1 if merge_bias else 0, float(top_p),
-                               C.cast(self.tau_arr, C.POINTER(C.c_float)))
+                               C.cast(self.tau_arr, C.POINTER(C.c_float)),
+                               int(regularize), int(mti_lower), int(mti_upper))
         self.dtype = dtype
 
     @classmethod
     def from_workload(cls, wl, top_p: Optional[float] = None, tau=None, cond_mode=None,
-                      merge_bias: bool = True) -> "Config":
+                      merge_bias: bool = True, regularize: int = HARDKV_REG_REWRITE,
+                      mti_lower: int = 0, mti_upper: int = 0) -> "Config":
         return cls(wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.dtype, wl.dense_window, wl.P_blk,
                    wl.sparse_cap, wl.V_cap, wl.condensed_slots,
                    wl.cond_mode if cond_mode is None else cond_mode,
                    wl.top_p if top_p is None else top_p,
                    [wl.tau] * wl.num_kv_heads if tau is None else list(tau),
-                   head_dim=wl.head_dim, merge_bias=merge_bias)
+                   head_dim=wl.head_dim, merge_bias=merge_bias, regularize=regularize,
+                   mti_lower=mti_lower, mti_upper=mti_upper)
 
     def __getattr__(self, name):
         return getattr(self.__dict__["c"], name)
@@ -183,6 +190,7 @@ class State:
         self.w_all = torch.zeros((B, H), dtype=torch.int64, **kw)
         self.w_u = torch.zeros((B, H), dtype=torch.int64, **kw)
         self.thresh = torch.zeros((B, H), dtype=torch.int64, **kw)
+        self.regularized = torch.zeros((B, H), dtype=torch.int32, **kw)
         self.error_word = torch.zeros((4,), dtype=torch.int32, **kw)
         self.workspace_bytes = hardkv_workspace_size(cfg)
         self.workspace = torch.zeros((self.workspace_bytes,), dtype=torch.uint8, **kw)
@@ -219,6 +227,11 @@ def hardkv_condense(cfg: Config, st: State, stream=None) -> None:
 def hardkv_attend(cfg: Config, st: State, q, out, stream=None) -> None:
     _check("hardkv_attend", lib().hardkv_attend(C.byref(cfg.c), C.byref(st.c), _ptr(q), _ptr(out),
                                                 _stream(stream)))
+
+
+def hardkv_attend_sparse(cfg: Config, st: State, q, out, stream=None) -> None:
+    _check("hardkv_attend_sparse", lib().hardkv_attend_sparse(C.byref(cfg.c), C.byref(st.c), _ptr(q),
+                                                              _ptr(out), _stream(stream)))
 
 
 def hardkv_step(cfg: Config, st: State, q, k_new, v_new, out, stream=None) -> None:

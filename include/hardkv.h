@@ -79,6 +79,23 @@ typedef enum {
 typedef enum { HARDKV_BF16 = 0, HARDKV_F32 = 1 } hardkv_dtype;
 typedef enum { HARDKV_COND_OFF = 0, HARDKV_COND_EVICT = 1, HARDKV_COND_MERGE = 2 } hardkv_cond_mode;
 
+/* How the kept tokens reach attention (section 2.C names Rewrite Cache, which moves the
+ * selected blocks into contiguous ranges, and Sparse Loading, which loads them through
+ * hardware-friendly masks, with a memory-time trade-off between the two switched by
+ * budget thresholds L_lower and L_upper; the pages give no formula, so the switch is a
+ * stated rule):
+ *   REWRITE  every head's kept rows are rewritten into its view (the default);
+ *   SPARSE   no head is rewritten: attention gathers the kept rows from the pool ring
+ *            through the mask words;
+ *   MTI      head (b, h) is rewritten iff mti_lower <= k* <= mti_upper: below L_lower so
+ *            few rows are kept that gathering them each step costs less than keeping a
+ *            view; above L_upper the mask covers so much of the pool that masked loads
+ *            are nearly contiguous and a rewrite would copy almost everything.
+ * The attention output, masks and budgets do not depend on the policy (the fused step
+ * attends the kept rows from registers either way); only the views differ: a head that is
+ * not rewritten leaves its view rows and view_pos untouched. */
+typedef enum { HARDKV_REG_REWRITE = 0, HARDKV_REG_SPARSE = 1, HARDKV_REG_MTI = 2 } hardkv_regularize_policy;
+
 #define HARDKV_BLOCK 64
 #define HARDKV_HEAD_DIM 128
 #define HARDKV_MAX_KV_HEADS 64
@@ -102,6 +119,9 @@ typedef struct {
   int32_t merge_bias;      /* 1: merged slots get logit bias ln n (default); 0: no bias */
   double top_p;            /* p in (0, 1]; p_q = round(p * 65536) must be >= 1 */
   const float *tau;        /* host array [num_kv_heads], calibration temperatures > 0 (+inf allowed) */
+  int32_t regularize;      /* hardkv_regularize_policy (0: REWRITE) */
+  int32_t mti_lower;       /* L_lower, tokens, >= 0 (policy MTI) */
+  int32_t mti_upper;       /* L_upper, tokens, >= mti_lower (policy MTI) */
 } hardkv_config;
 
 /* Device buffers of one layer.  All fixed capacity; 16-byte aligned.
@@ -125,6 +145,8 @@ typedef struct {
   uint64_t *w_all;           /* [B][Hkv]: total pool mass                                         */
   uint64_t *w_u;             /* [B][Hkv]: survivor mass W_U                                       */
   uint64_t *thresh;          /* [B][Hkv]: T                                                       */
+  int32_t *regularized;      /* [B][Hkv]: 1 if the head's view is rewritten this step, else 0
+                                (may be NULL: not reported)                                       */
   uint32_t *error_word;      /* [1]: HARDKV_ERR_* bits, or-ed                                     */
   void *workspace;           /* hardkv_workspace_size() bytes, zero-filled before first use      */
   size_t workspace_bytes;
@@ -148,24 +170,33 @@ int32_t hardkv_append(const hardkv_config *cfg, hardkv_state *st, const void *k_
  * weights, mask, budget, n_condense, w_all, w_u, thresh.  q is e [B][Hq][128] (device). */
 int32_t hardkv_select(const hardkv_config *cfg, hardkv_state *st, const void *q, void *stream);
 
-/* Stage 3 (section 2.C): copies the kept rows into the view and writes view_pos. */
+/* Stage 3 (section 2.C): copies the kept rows into the view and writes view_pos, for the
+ * heads that the regularize policy rewrites (all of them under REWRITE). */
 int32_t hardkv_regularize(const hardkv_config *cfg, hardkv_state *st, void *stream);
 
 /* Stage 4 (section 2.A, tier 3): evicts or merges the E oldest blocks; advances c and
  * the slot cursor. */
 int32_t hardkv_condense(const hardkv_config *cfg, hardkv_state *st, void *stream);
 
-/* Attention over the condensed, view and dense tiers; out is fp32 [B][Hq][128] (device). */
+/* Attention over the condensed, view and dense tiers; out is fp32 [B][Hq][128] (device).
+ * Heads that the last select left to Sparse Loading are attended through the pool and
+ * the mask instead of the view. */
 int32_t hardkv_attend(const hardkv_config *cfg, hardkv_state *st, const void *q, float *out,
                       void *stream);
+
+/* Sparse Loading (section 2.C): attention over the condensed tier, the kept rows gathered
+ * from the pool ring through the mask of the last select (whatever the policy; no view is
+ * read), and the dense tier.  Same arguments and output as hardkv_attend. */
+int32_t hardkv_attend_sparse(const hardkv_config *cfg, hardkv_state *st, const void *q, float *out,
+                             void *stream);
 
 /* The whole step: append, select, regularize, condense, attend, in one stream-ordered,
  * capturable sequence (the view attention is fused into the rewrite). */
 int32_t hardkv_step(const hardkv_config *cfg, hardkv_state *st, const void *q, const void *k_new,
                     const void *v_new, float *out, void *stream);
 
-/* Launches only kernel `stage` of hardkv_step (0 append, 1 score+select, 2 rewrite with
- * view attention, 3 condense, 4 condensed/dense attention, 5 combine), for timing one
+/* Launches only kernel `stage` of hardkv_step (0 append, 1 score, 2 select, 3 condense,
+ * 4 rewrite with the view, condensed and dense attention, 5 combine), for timing one
  * kernel on its own.  Stages 1, 2, 4 and 5 only read what earlier stages wrote and may
  * be repeated; 0 and 3 advance the state. */
 int32_t hardkv_step_stage(const hardkv_config *cfg, hardkv_state *st, const void *q,

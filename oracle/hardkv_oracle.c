@@ -260,6 +260,7 @@ typedef struct {
   const orc_state *st;
   int64_t u;
   int64_t n_cond, n_view, n_dense, dense_lo;
+  const int64_t *kept_rows;  /* pool rows of the kept positions, ascending; NULL: the view */
   int32_t slot[4096];
 } tier_ctx;
 
@@ -283,7 +284,11 @@ static void tier_row(const void *ctx, int64_t i, double *key, double *val, doubl
   i -= tc->n_cond;
   int64_t row;
   const void *kb, *vb;
-  if (i < tc->n_view) {
+  if (i < tc->n_view && tc->kept_rows) {  /* Sparse Loading: the kept rows in the pool */
+    row = tc->kept_rows[i];
+    kb = st->pool_k;
+    vb = st->pool_v;
+  } else if (i < tc->n_view) {
     row = tc->u * cfg->view_cap + i;
     kb = st->view_k;
     vb = st->view_v;
@@ -413,20 +418,37 @@ static uint32_t unit_step(const orc_cfg *cfg, orc_state *st, int b, int h, const
       st->mask[u * P + (j / BK) % P] |= (uint64_t)1 << (j % BK);
     }
 
-  /* Index Regularization, Rewrite Cache with a max-length flat index
-   * (section 2.C): the selected rows, in ascending position, become rows
-   * 0 .. k*-1 of the head's fixed-capacity view */
-  int32_t r = 0;
-  if (kstar > cfg->view_cap) err |= ORC_ERR_VIEW_OVERFLOW;
-  for (int32_t i = 0; i < nU; ++i) {
-    if (!sel[i]) continue;
-    if (r < cfg->view_cap) {
-      int64_t j = u0 + i;
-      row_copy(st->view_k, u * cfg->view_cap + r, st->pool_k, pool_row(cfg, u, j), D, eb);
-      row_copy(st->view_v, u * cfg->view_cap + r, st->pool_v, pool_row(cfg, u, j), D, eb);
-      st->view_pos[u * cfg->view_cap + r] = (int32_t)j;
+  /* Index Regularization (section 2.C).  The regularize policy decides whether this
+   * head's kept rows are rewritten (Rewrite Cache) or left in the pool for attention to
+   * load through the mask (Sparse Loading); the pages name budget thresholds L_lower,
+   * L_upper for the switch without a formula: the head is rewritten iff
+   * L_lower <= k* <= L_upper. */
+  const int rw = cfg->regularize == 0 ? 1
+                 : cfg->regularize == 1 ? 0
+                 : (kstar >= cfg->mti_lower && kstar <= cfg->mti_upper) ? 1 : 0;
+  if (st->regularized) st->regularized[u] = rw;
+  /* the pool rows of the kept positions, ascending (Sparse Loading reads these) */
+  int64_t *kept = (int64_t *)malloc(sizeof(int64_t) * (size_t)(kstar > 0 ? kstar : 1));
+  {
+    int32_t r = 0;
+    for (int32_t i = 0; i < nU; ++i)
+      if (sel[i]) kept[r++] = pool_row(cfg, u, u0 + i);
+  }
+  /* Rewrite Cache with a max-length flat index: the selected rows, in ascending
+   * position, become rows 0 .. k*-1 of the head's fixed-capacity view */
+  if (rw) {
+    int32_t r = 0;
+    if (kstar > cfg->view_cap) err |= ORC_ERR_VIEW_OVERFLOW;
+    for (int32_t i = 0; i < nU; ++i) {
+      if (!sel[i]) continue;
+      if (r < cfg->view_cap) {
+        int64_t j = u0 + i;
+        row_copy(st->view_k, u * cfg->view_cap + r, st->pool_k, pool_row(cfg, u, j), D, eb);
+        row_copy(st->view_v, u * cfg->view_cap + r, st->pool_v, pool_row(cfg, u, j), D, eb);
+        st->view_pos[u * cfg->view_cap + r] = (int32_t)j;
+      }
+      ++r;
     }
-    ++r;
   }
 
   /* condense (section 2.A, tier 3): each of the E oldest blocks is dropped
@@ -465,7 +487,8 @@ static uint32_t unit_step(const orc_cfg *cfg, orc_state *st, int b, int h, const
     tc->n_cond = 0;
     for (int s = 0; s < cfg->condensed_slots && s < 4096; ++s)
       if (st->cond_n[u * cfg->condensed_slots + s] > 0) tc->slot[tc->n_cond++] = s;
-    tc->n_view = kstar < cfg->view_cap ? kstar : cfg->view_cap;
+    tc->kept_rows = rw ? NULL : kept;
+    tc->n_view = rw ? (kstar < cfg->view_cap ? kstar : cfg->view_cap) : kstar;
     tc->dense_lo = t > W ? t - W : 0;
     tc->n_dense = t - tc->dense_lo;
     double qd[1024];
@@ -481,6 +504,7 @@ static uint32_t unit_step(const orc_cfg *cfg, orc_state *st, int b, int h, const
   free(wU);
   free(pU);
   free(sel);
+  free(kept);
   return err;
 }
 

@@ -49,6 +49,9 @@ typedef struct {
   int32_t merge_bias;        /* 1: condensed slot logit gets + ln n (default), 0: none */
   double top_p;
   const float *tau;          /* [H] */
+  int32_t regularize;        /* 0 rewrite every head, 1 none (Sparse Loading), 2 the heads with
+                                mti_lower <= k* <= mti_upper */
+  int32_t mti_lower, mti_upper;
 } orc_cfg;
 
 typedef struct {
@@ -62,6 +65,7 @@ typedef struct {
   uint64_t *mask;
   int32_t *budget, *n_condense;
   uint64_t *w_all, *w_u, *thresh;
+  int32_t *regularized;      /* [B*H] 1 if the head's view was rewritten this step (may be NULL) */
   uint32_t error_word;
 } orc_state;
 

@@ -28,6 +28,7 @@ class OrcCfg(C.Structure):
         ("pool_blocks", C.c_int32), ("sparse_cap", C.c_int32), ("view_cap", C.c_int32),
         ("condensed_slots", C.c_int32), ("cond_mode", C.c_int32), ("merge_bias", C.c_int32),
         ("top_p", C.c_double), ("tau", C.POINTER(C.c_float)),
+        ("regularize", C.c_int32), ("mti_lower", C.c_int32), ("mti_upper", C.c_int32),
     ]
 
 
@@ -40,7 +41,7 @@ class OrcState(C.Structure):
         ("seq_len", C.c_void_p), ("pool_head", C.c_void_p), ("scores", C.c_void_p),
         ("weights", C.c_void_p), ("mask", C.c_void_p), ("budget", C.c_void_p),
         ("n_condense", C.c_void_p), ("w_all", C.c_void_p), ("w_u", C.c_void_p),
-        ("thresh", C.c_void_p), ("error_word", C.c_uint32),
+        ("thresh", C.c_void_p), ("regularized", C.c_void_p), ("error_word", C.c_uint32),
     ]
 
 
@@ -172,7 +173,8 @@ class Oracle:
     """
 
     def __init__(self, wl, tau: Optional[np.ndarray] = None, merge_bias: bool = True,
-                 top_p: Optional[float] = None):
+                 top_p: Optional[float] = None, regularize: int = 0, mti_lower: int = 0,
+                 mti_upper: int = 0):
         self.wl = wl
         B, H, Hq, D = wl.batch, wl.num_kv_heads, wl.num_q_heads, wl.head_dim
         W, P, V, Cs = wl.dense_window, wl.P_blk, wl.V_cap, wl.condensed_slots
@@ -181,7 +183,8 @@ class Oracle:
             np.full(H, wl.tau, np.float32) if tau is None else np.asarray(tau, np.float32))
         self.cfg = OrcCfg(B, Hq, H, D, wl.elem_bytes, W, P, wl.sparse_cap, V, Cs, wl.cond_mode,
                           1 if merge_bias else 0, float(wl.top_p if top_p is None else top_p),
-                          self.tau.ctypes.data_as(C.POINTER(C.c_float)))
+                          self.tau.ctypes.data_as(C.POINTER(C.c_float)), int(regularize),
+                          int(mti_lower), int(mti_upper))
         self.dense_k = np.zeros((B, H, W, D), st)
         self.dense_v = np.zeros((B, H, W, D), st)
         self.pool_k = np.zeros((B, H, P, BK, D), st)
@@ -204,10 +207,11 @@ class Oracle:
         self.w_all = np.zeros((B, H), np.uint64)
         self.w_u = np.zeros((B, H), np.uint64)
         self.thresh = np.zeros((B, H), np.uint64)
+        self.regularized = np.zeros((B, H), np.int32)
         self.st = OrcState(*[_p(getattr(self, n)) for n in (
             "dense_k", "dense_v", "pool_k", "pool_v", "view_k", "view_v", "view_pos", "cond_kn",
             "cond_vn", "cond_omega", "cond_n", "cond_cursor", "seq_len", "pool_head", "scores",
-            "weights", "mask", "budget", "n_condense", "w_all", "w_u", "thresh")], 0)
+            "weights", "mask", "budget", "n_condense", "w_all", "w_u", "thresh", "regularized")], 0)
 
     @property
     def error_word(self) -> int:
@@ -234,4 +238,13 @@ class Oracle:
         return (p // BK) % P * BK + p % BK
 
     def selected_positions(self, b: int, h: int) -> np.ndarray:
-        return self.view_pos[b, h, :self.budget[b, h]].astype(np.int64)
+        """The kept positions in ascending order, from the mask words (valid whether or not
+        the head was rewritten this step)."""
+        P = self.wl.P_blk
+        c = int(self.pool_head[b, h]) - BK * int(self.n_condense[b, h])  # pool head before condensing
+        t = int(self.seq_len[b])
+        pend = max(0, t - self.wl.dense_window)
+        p = np.arange(c, pend, dtype=np.int64)
+        words = self.mask[b, h][(p // BK) % P]
+        bits = (words >> (p % BK).astype(np.uint64)) & np.uint64(1)
+        return p[bits.astype(bool)]

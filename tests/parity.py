@@ -46,27 +46,29 @@ class Pair:
     """A GPU state and oracle state(s) of the same layer, fed the same inputs."""
 
     def __init__(self, wl, inputs=None, top_p=None, tau=None, cond_mode=None, merge_bias=True,
-                 device="cuda", oracle_units=None, layer=0):
+                 device="cuda", oracle_units=None, layer=0, regularize=0, mti_lower=0, mti_upper=0):
         self.wl = wl if cond_mode is None else wl.with_(cond_mode=cond_mode)
         if top_p is not None:
             self.wl = self.wl.with_(top_p=top_p)
         self.inp = inputs if inputs is not None else make_inputs(self.wl, layer=layer, device=device)
         self.tau = [self.wl.tau] * self.wl.num_kv_heads if tau is None else list(tau)
-        self.cfg = hk.Config.from_workload(self.wl, tau=self.tau, merge_bias=merge_bias)
+        pol = dict(regularize=regularize, mti_lower=mti_lower, mti_upper=mti_upper)
+        self.cfg = hk.Config.from_workload(self.wl, tau=self.tau, merge_bias=merge_bias, **pol)
         self.st = hk.State(self.cfg, device=device)
         hk.hardkv_prefill(self.cfg, self.st, self.inp.k_ctx, self.inp.v_ctx, self.inp.ctx_len)
         self.units = oracle_units
         self.orcs = {}
         if oracle_units is None:
             cpu = self.inp.to("cpu")
-            o = orc.Oracle(self.wl, tau=np.asarray(self.tau, np.float32), merge_bias=merge_bias)
+            o = orc.Oracle(self.wl, tau=np.asarray(self.tau, np.float32), merge_bias=merge_bias, **pol)
             assert o.prefill(cpu.k_ctx, cpu.v_ctx, cpu.ctx_len) == 0
             self.orcs[None] = (o, cpu)
         else:
             for (b, h) in oracle_units:
                 ui = self.inp.unit(b, h).to("cpu")
                 ui.wl = self.wl.with_(batch=1, num_kv_heads=1, num_q_heads=self.wl.group)
-                o = orc.Oracle(ui.wl, tau=np.asarray(self.tau[h:h + 1], np.float32), merge_bias=merge_bias)
+                o = orc.Oracle(ui.wl, tau=np.asarray(self.tau[h:h + 1], np.float32), merge_bias=merge_bias,
+                               **pol)
                 assert o.prefill(ui.k_ctx, ui.v_ctx, ui.ctx_len) == 0
                 self.orcs[(b, h)] = (o, ui)
         self.out = torch.zeros((self.wl.batch, self.wl.num_q_heads, self.wl.head_dim),
@@ -78,7 +80,7 @@ class Pair:
         self.inp.k_ctx = self.inp.v_ctx = None
 
     # ---- stepping --------------------------------------------------------------------------
-    def gpu_step(self, fused=True):
+    def gpu_step(self, fused=True, sparse_attend=False):
         s = self.step_i
         q, kn, vn = self.inp.q[s], self.inp.k_new[s], self.inp.v_new[s]
         if fused:
@@ -88,7 +90,10 @@ class Pair:
             hk.hardkv_select(self.cfg, self.st, q)
             hk.hardkv_regularize(self.cfg, self.st)
             hk.hardkv_condense(self.cfg, self.st)
-            hk.hardkv_attend(self.cfg, self.st, q, self.out)
+            if sparse_attend:
+                hk.hardkv_attend_sparse(self.cfg, self.st, q, self.out)
+            else:
+                hk.hardkv_attend(self.cfg, self.st, q, self.out)
 
     def oracle_step(self, attend=True):
         s = self.step_i
@@ -99,9 +104,10 @@ class Pair:
                                nthreads=0 if key is None else 1)
         return dict(_POOL.map(run, list(self.orcs.items())))
 
-    def step(self, fused=True, attend=True, check=True, check_attend=True, check_views=True):
+    def step(self, fused=True, attend=True, check=True, check_attend=True, check_views=True,
+             sparse_attend=False):
         pre = {k: o.pool_head.copy() for k, (o, _) in self.orcs.items()}
-        self.gpu_step(fused)
+        self.gpu_step(fused, sparse_attend)
         outs = self.oracle_step(attend)
         torch.cuda.synchronize()
         if check:
@@ -116,7 +122,7 @@ class Pair:
         wl, P = self.wl, self.wl.P_blk
         small = {n: getattr(self.st, n).cpu() for n in (
             "seq_len", "budget", "n_condense", "cond_cursor", "pool_head", "w_all", "w_u", "thresh",
-            "error_word")}
+            "regularized", "error_word")}
         big_names = ["scores", "weights", "mask", "cond_n", "cond_kn", "cond_vn", "cond_omega"]
         if check_views:
             big_names += ["view_pos", "view_k", "view_v"]
@@ -133,7 +139,7 @@ class Pair:
                 tag = f"step {self.step_i} unit (b={b}, h={h})"
                 g = {n: full[n][b, h] for n in big_names} if full is not None else self._gpu_unit(b, h, big_names)
                 assert int(small["seq_len"][b]) == int(o.seq_len[ob]), tag
-                for name in ("budget", "n_condense", "cond_cursor", "pool_head"):
+                for name in ("budget", "n_condense", "cond_cursor", "pool_head", "regularized"):
                     assert int(small[name][b, h]) == int(getattr(o, name)[ob, oh]), f"{tag} {name}"
                 for name in ("w_all", "w_u", "thresh"):
                     gv = int(small[name][b, h].numpy().view(np.uint64))
@@ -153,7 +159,10 @@ class Pair:
                 assert np.array_equal(g["mask"].numpy().view(np.uint64), o.mask[ob, oh]), f"{tag} mask"
                 k = int(small["budget"][b, h])
                 kv = min(k, wl.V_cap)
-                if check_views:
+                if check_views and not int(small["regularized"][b, h]):
+                    # not rewritten this step: both sides keep the view they held before
+                    assert np.array_equal(g["view_pos"].numpy(), o.view_pos[ob, oh]), f"{tag} kept view_pos"
+                elif check_views:
                     assert np.array_equal(g["view_pos"].numpy()[:kv], o.view_pos[ob, oh][:kv]), f"{tag} view_pos"
                     assert np.array_equal(raw(g["view_k"][:kv]), o.view_k[ob, oh][:kv]), f"{tag} view_k"
                     assert np.array_equal(raw(g["view_v"][:kv]), o.view_v[ob, oh][:kv]), f"{tag} view_v"

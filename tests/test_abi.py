@@ -22,7 +22,7 @@ def _declared():
 def test_exports_every_declared_symbol():
     lib = hk.lib()
     names = _declared()
-    assert len(names) == 12, names
+    assert len(names) == 13, names
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(hk.EXPORTS)
@@ -61,6 +61,9 @@ def _cfg(**over):
     (dict(dtype=7), hk.HARDKV_EINVAL),
     (dict(num_kv_heads=65, num_q_heads=65), hk.HARDKV_EUNSUPPORTED),
     (dict(dense_window=0), hk.HARDKV_EINVAL),
+    (dict(regularize=3), hk.HARDKV_EINVAL),
+    (dict(regularize=hk.HARDKV_REG_MTI, mti_lower=-1, mti_upper=5), hk.HARDKV_EINVAL),
+    (dict(regularize=hk.HARDKV_REG_MTI, mti_lower=10, mti_upper=5), hk.HARDKV_EINVAL),
 ])
 def test_config_validation(over, code):
     cfg = _cfg(**over)
@@ -92,7 +95,7 @@ def _fake_state(cfg, ws_bytes=None, misalign=None, null=None):
     for i, (name, _) in enumerate(hk.hardkv_state._fields_[:-1]):
         v = addr + i * (1 << 30)
         if name == misalign:
-            v += 4 if name != "error_word" else 2
+            v += 4 if name not in ("error_word", "regularized") else 2
         if name == null:
             v = None
         setattr(st, name, v)
@@ -101,12 +104,14 @@ def _fake_state(cfg, ws_bytes=None, misalign=None, null=None):
 
 
 @_no_gpu
-@pytest.mark.parametrize("kind", ["null_pool", "misaligned_view", "misaligned_error", "small_ws"])
+@pytest.mark.parametrize("kind", ["null_pool", "misaligned_view", "misaligned_error", "misaligned_regularized",
+                                  "small_ws"])
 def test_state_validation(kind):
     cfg = _cfg()
     st = {"null_pool": lambda: _fake_state(cfg, null="pool_k"),
           "misaligned_view": lambda: _fake_state(cfg, misalign="view_k"),
           "misaligned_error": lambda: _fake_state(cfg, misalign="error_word"),
+          "misaligned_regularized": lambda: _fake_state(cfg, misalign="regularized"),
           "small_ws": lambda: _fake_state(cfg, ws_bytes=16)}[kind]()
     expect = hk.HARDKV_ECAPACITY if kind == "small_ws" else hk.HARDKV_EINVAL
     L = hk.lib()
@@ -126,6 +131,7 @@ def test_call_argument_validation():
     assert L.hardkv_step(C.byref(cfg.c), C.byref(st), bad, ok, ok, ok, None) == hk.HARDKV_EINVAL
     assert L.hardkv_step(C.byref(cfg.c), C.byref(st), ok, None, ok, ok, None) == hk.HARDKV_EINVAL
     assert L.hardkv_attend(C.byref(cfg.c), C.byref(st), ok, bad, None) == hk.HARDKV_EINVAL
+    assert L.hardkv_attend_sparse(C.byref(cfg.c), C.byref(st), bad, ok, None) == hk.HARDKV_EINVAL
     assert L.hardkv_step_stage(C.byref(cfg.c), C.byref(st), ok, ok, ok, ok, 6, None) == hk.HARDKV_EINVAL
     # prefill: the first append of a max_len context would not fit the pool ring
     wl = tiny_workload()

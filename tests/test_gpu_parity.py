@@ -165,3 +165,80 @@ def test_graph_replay_matches_eager(batch):
             if n == "workspace":
                 continue
             assert torch.equal(t, getattr(gst, n)), (s, n)
+
+
+# ---- regularize policy: Rewrite Cache vs Sparse Loading ------------------------------------
+def _mti_bounds(wl):
+    """Thresholds that split the heads of the workload's first step: the oracle's budgets."""
+    from oracle import hardkv_oracle as orc
+    from synth import make_inputs
+    inp = make_inputs(wl)
+    o = orc.Oracle(wl)
+    assert o.prefill(inp.k_ctx, inp.v_ctx, inp.ctx_len) == 0
+    o.step(inp.q[0], inp.k_new[0], inp.v_new[0], attend=False)
+    vals = np.unique(o.budget)
+    assert len(vals) >= 3, vals
+    return int(vals[1]), int(vals[-2])
+
+
+POLICY_CASES = {
+    "sparse_merge_bf16": (dict(cond_mode=COND_MERGE, ctx_len=500, ctx_min=100, steps=3), 1),
+    "sparse_evict_f32": (dict(dtype="f32", steps=2), 1),
+    "sparse_g8": (dict(num_q_heads=16, num_kv_heads=2, cond_mode=COND_MERGE, steps=2), 1),
+    "mti_evict": (dict(batch=4, heavy=(0, 6), steps=2), 2),
+    "mti_merge_batch16": (dict(batch=16, cond_mode=COND_MERGE, ctx_len=500, ctx_min=100, heavy=(0, 6), steps=2), 2),
+}
+
+
+@pytest.mark.parametrize("name", list(POLICY_CASES))
+@pytest.mark.parametrize("fused", [True, False])
+def test_regularize_policy_parity(name, fused):
+    """Under Sparse Loading and the MTI threshold rule the step and the five separate calls
+    match the oracle: masks, budgets and per-head rewrite flags bit for bit, rewritten heads'
+    views bit for bit, other heads' views untouched, attention within 2e-3 (the kept rows
+    of heads that are not rewritten come straight from the pool)."""
+    from parity import Pair
+    kw, pol = POLICY_CASES[name]
+    kw = dict(kw)
+    steps = kw.pop("steps")
+    wl = tiny_workload(steps=steps, **kw)
+    lo, hi = _mti_bounds(wl) if pol == 2 else (0, 0)
+    print(f"case {name} fused={fused}: policy {pol} [{lo}, {hi}] {wl}", flush=True)
+    pr = Pair(wl, regularize=pol, mti_lower=lo, mti_upper=hi)
+    for _ in range(steps):
+        pr.step(fused=fused)
+    if pol == 2:
+        rw = pr.st.regularized.cpu().numpy()
+        assert rw.any() and not rw.all(), rw
+
+
+@pytest.mark.parametrize("name", ["evict_bf16", "merge_wrap", "g8"])
+def test_attend_sparse_parity(name):
+    """hardkv_attend_sparse (kept rows gathered from the pool through the mask) gives the
+    oracle's attention after the separate select, regularize and condense calls."""
+    from parity import Pair
+    wl = tiny_workload(steps=2, **CASES[name])
+    pr = Pair(wl)
+    for _ in range(2):
+        pr.step(fused=False, sparse_attend=True)
+
+
+def test_fused_output_does_not_depend_on_policy():
+    """The fused step attends the kept rows from registers whatever the policy, so the output
+    is bitwise the same under Rewrite Cache, Sparse Loading and a mixed MTI split."""
+    from decode_kv_cache_02_amd import hardkv as hk
+    from synth import make_inputs
+    wl = tiny_workload(batch=4, heavy=(0, 6), cond_mode=COND_MERGE, steps=2)
+    lo, hi = _mti_bounds(wl)
+    inp = make_inputs(wl, device="cuda")
+    outs = []
+    for pol in (0, 1, 2):
+        cfg = hk.Config.from_workload(wl, regularize=pol, mti_lower=lo, mti_upper=hi)
+        st = hk.State(cfg)
+        hk.hardkv_prefill(cfg, st, inp.k_ctx, inp.v_ctx, inp.ctx_len)
+        out = torch.zeros((wl.batch, wl.num_q_heads, 128), device="cuda")
+        for s in range(wl.steps):
+            hk.hardkv_step(cfg, st, inp.q[s], inp.k_new[s], inp.v_new[s], out)
+        torch.cuda.synchronize()
+        outs.append(out.clone())
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])

@@ -221,3 +221,50 @@ def test_streaming_invariants():
         assert np.all(o.budget >= 1)
     assert np.all(o.cond_n.sum(-1) == 64 * total_E)
     assert o.error_word == 0
+
+
+# ---- regularize policy: Rewrite Cache vs Sparse Loading ------------------------------------
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_sparse_loading_attends_the_same_rows(dtype):
+    """Sparse Loading reads the kept rows from the pool instead of the view; the view rows
+    are bit copies of those pool rows in the same order, so the attention output is the
+    same bit for bit over several steps, masks and budgets agree, and no view row or
+    view position is written."""
+    wl = tiny_workload(dtype=dtype, cond_mode=COND_MERGE, steps=3, ctx_len=500, ctx_min=100)
+    inp = make_inputs(wl)
+    o_rw, outs_rw = _run(wl, inp, 3)
+    o_sp, outs_sp = _run(wl, inp, 3, regularize=1)
+    for a, b in zip(outs_rw, outs_sp):
+        assert np.array_equal(a, b)
+    for n in ("mask", "budget", "weights", "cond_kn", "cond_n", "pool_head"):
+        assert np.array_equal(getattr(o_rw, n), getattr(o_sp, n)), n
+    assert not o_sp.regularized.any() and o_rw.regularized.all()
+    assert (o_sp.view_pos == -1).all() and not o_sp.view_k.any()
+    for b in range(wl.batch):
+        for h in range(wl.num_kv_heads):
+            np.testing.assert_array_equal(o_sp.selected_positions(b, h), o_rw.selected_positions(b, h))
+
+
+def test_mti_thresholds_pick_heads_by_budget():
+    """MTI policy: a head is rewritten iff L_lower <= k* <= L_upper; rewritten heads hold
+    the same view as under Rewrite Cache, the others keep whatever the view held before;
+    the attention output does not depend on the choice."""
+    wl = tiny_workload(cond_mode=COND_EVICT, steps=2, heavy=(0, 6), batch=4)
+    inp = make_inputs(wl)
+    o_rw, outs_rw = _run(wl, inp, 1)
+    vals = np.unique(o_rw.budget)
+    assert len(vals) >= 3, vals
+    lo, hi = int(vals[1]), int(vals[-2])
+    o_m, outs_m = _run(wl, inp, 1, regularize=2, mti_lower=lo, mti_upper=hi)
+    assert np.array_equal(outs_rw[0], outs_m[0])
+    rw = (o_m.budget >= lo) & (o_m.budget <= hi)
+    assert rw.any() and (~rw).any()
+    np.testing.assert_array_equal(o_m.regularized.astype(bool), rw)
+    for b in range(wl.batch):
+        for h in range(wl.num_kv_heads):
+            k = int(o_m.budget[b, h])
+            if rw[b, h]:
+                np.testing.assert_array_equal(o_m.view_k[b, h, :k], o_rw.view_k[b, h, :k])
+                np.testing.assert_array_equal(o_m.view_pos[b, h, :k], o_rw.view_pos[b, h, :k])
+            else:
+                assert (o_m.view_pos[b, h] == -1).all()

@@ -67,6 +67,10 @@ def parse():
                          "the budget-threshold rule (rewrite iff --mti-lower <= k* <= --mti-upper)")
     ap.add_argument("--mti-lower", type=int, default=0)
     ap.add_argument("--mti-upper", type=int, default=1 << 30)
+    ap.add_argument("--view-layout", choices=["maxlen", "sum"], default="maxlen",
+                    help="Flatten Index: view_cap rows per head (default) or packed in unit order")
+    ap.add_argument("--view-total", type=int, default=0,
+                    help="packed view rows for --view-layout sum (0: batch * kv_heads * view_cap)")
     ap.add_argument("--stage-reps", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-units", type=int, default=0, help="oracle sample size in units (0: automatic)")
@@ -89,11 +93,14 @@ POLICY = {"rewrite": hk.HARDKV_REG_REWRITE, "sparse": hk.HARDKV_REG_SPARSE, "mti
 
 
 class Layer:
-    def __init__(self, wl, layer, steps, top_p=None, policy=("rewrite", 0, 0)):
+    def __init__(self, wl, layer, steps, top_p=None, policy=("rewrite", 0, 0), view=("maxlen", 0)):
         self.wl = wl
         self.inp = make_inputs(wl, layer=layer, device="cuda", steps=steps)
+        total = view[1] or wl.batch * wl.num_kv_heads * wl.V_cap
         self.cfg = hk.Config.from_workload(wl, top_p=top_p, regularize=POLICY[policy[0]],
-                                           mti_lower=policy[1], mti_upper=policy[2])
+                                           mti_lower=policy[1], mti_upper=policy[2],
+                                           view_layout=hk.HARDKV_VIEW_SUM if view[0] == "sum" else
+                                           hk.HARDKV_VIEW_MAXLEN, view_total=total)
         self.st = hk.State(self.cfg)
         hk.hardkv_prefill(self.cfg, self.st, self.inp.k_ctx, self.inp.v_ctx, self.inp.ctx_len)
         self.out = torch.zeros((wl.batch, wl.num_q_heads, D), dtype=torch.float32, device="cuda")
@@ -432,7 +439,8 @@ def main():
 
     layers = []
     for layer in range(wl.layers):
-        L = Layer(wl, layer, nsteps, top_p=top_p, policy=(args.regularize, args.mti_lower, args.mti_upper))
+        L = Layer(wl, layer, nsteps, top_p=top_p, policy=(args.regularize, args.mti_lower, args.mti_upper),
+                  view=(args.view_layout, args.view_total))
         if layer == 0 and not args.no_cpu_baseline:
             L.inp_cpu_source = {"k_ctx": L.inp.k_ctx, "v_ctx": L.inp.v_ctx, "ctx_len": L.inp.ctx_len}
         else:
@@ -567,6 +575,7 @@ def main():
                    "top_p": float(layers[0].cfg.c.top_p), "cond_mode": "merge",
                    "regularize": args.regularize if args.regularize != "mti" else
                    f"mti [{args.mti_lower}, {args.mti_upper}]",
+                   "view_layout": args.view_layout,
                    "timing": ("one-step graph replay from the prefilled state" if restore_mode else
                               "graph of the K streaming steps") + (" (eager)" if args.eager else "")},
         "kv_tokens_scanned_per_s": scanned_step * steps_per_s,

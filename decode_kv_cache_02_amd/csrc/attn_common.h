@@ -201,10 +201,12 @@ HK_DEV void attend_segment(const Args &a, int bh, int seg, float (*s_part)[G][2 
     slot = seg;
     // a head that was not rewritten this step has no valid view (its kept rows are
     // attended from the pool by the rewrite kernel instead)
-    const int64_t kst = a.head[bh].rw ? min((int64_t)a.budget[bh], (int64_t)a.V_cap) : 0;
+    const int64_t voff = a.head[bh].voff;
+    const int64_t vcap = a.view_sum ? max((int64_t)0, a.view_rows - voff) : (int64_t)a.V_cap;
+    const int64_t kst = a.head[bh].rw ? min((int64_t)a.budget[bh], vcap) : 0;
     const int64_t r0 = (int64_t)seg * a.rv_att, r1 = min(r0 + (int64_t)a.rv_att, kst);
-    const char *vk = (const char *)a.view_k + (size_t)bh * a.V_cap * ROWB + sub * 8 * EB;
-    const char *vv = (const char *)a.view_v + (size_t)bh * a.V_cap * ROWB + sub * 8 * EB;
+    const char *vk = (const char *)a.view_k + (size_t)voff * ROWB + sub * 8 * EB;
+    const char *vv = (const char *)a.view_v + (size_t)voff * ROWB + sub * 8 * EB;
     for (int64_t base = r0; base < r1; base += 32) {
       Raw8<T> kr[2], vr[2];
       bool act[2];

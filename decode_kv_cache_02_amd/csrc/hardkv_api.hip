@@ -52,6 +52,8 @@ int32_t plan(const hardkv_config *cfg, Plan &p) {
   if (cfg->regularize < HARDKV_REG_REWRITE || cfg->regularize > HARDKV_REG_MTI) return HARDKV_EINVAL;
   if (cfg->regularize == HARDKV_REG_MTI && (cfg->mti_lower < 0 || cfg->mti_upper < cfg->mti_lower))
     return HARDKV_EINVAL;
+  if (cfg->view_layout != HARDKV_VIEW_MAXLEN && cfg->view_layout != HARDKV_VIEW_SUM) return HARDKV_EINVAL;
+  if (cfg->view_layout == HARDKV_VIEW_SUM && cfg->view_total < 0) return HARDKV_EINVAL;
 
   a.B = cfg->batch;
   a.Hq = cfg->num_q_heads;
@@ -64,6 +66,9 @@ int32_t plan(const hardkv_config *cfg, Plan &p) {
   a.C = cfg->condensed_slots;
   a.mode = cfg->cond_mode;
   a.merge_bias = cfg->merge_bias ? 1 : 0;
+  a.view_sum = cfg->view_layout == HARDKV_VIEW_SUM ? 1 : 0;
+  a.view_rows = a.view_sum ? (int64_t)cfg->view_total
+                           : (int64_t)cfg->batch * cfg->num_kv_heads * cfg->view_cap;
   a.reg_policy = cfg->regularize;
   a.mti_lower = cfg->mti_lower;
   a.mti_upper = cfg->mti_upper;
@@ -155,6 +160,9 @@ int32_t bind(const hardkv_state *st, Plan &p) {
   a.thresh = st->thresh;
   if (st->regularized && ((uintptr_t)st->regularized & 3u)) return HARDKV_EINVAL;
   a.regularized = st->regularized;
+  if (p.a.view_sum && (!st->view_off || ((uintptr_t)st->view_off & 3u))) return HARDKV_EINVAL;
+  if (st->view_off && ((uintptr_t)st->view_off & 3u)) return HARDKV_EINVAL;
+  a.view_off = st->view_off;
   a.error_word = st->error_word;
   char *ws = (char *)st->workspace;
   a.head = reinterpret_cast<HeadInfo *>(ws + p.off_head);
@@ -187,7 +195,11 @@ hipError_t step_stage(const hardkv_config *cfg, Args &a, int stage, hipStream_t 
   switch (stage) {
     case 0: return launch_append(a, s, bf);
     case 1: return launch_score(a, s, bf);
-    case 2: return launch_select(a, s);
+    case 2: {
+      hipError_t e = launch_select(a, s);
+      if (e == hipSuccess && a.view_sum) e = launch_flatten(a, s);
+      return e;
+    }
     case 3: return launch_condense(a, s, bf);
     case 4: return launch_rewrite(a, s, bf, true, true, true);
     case 5: return launch_combine(a, s);
@@ -272,6 +284,7 @@ int32_t hardkv_select(const hardkv_config *cfg, hardkv_state *st, const void *q,
   const bool bf = is_bf16(cfg);
   hipError_t e = launch_score(p.a, s, bf);
   if (e == hipSuccess) e = launch_select(p.a, s);
+  if (e == hipSuccess && p.a.view_sum) e = launch_flatten(p.a, s);
   if (e == hipSuccess) e = launch_rewrite(p.a, s, bf, true, false, false);  // mask words
   return hip_status(e);
 }

@@ -29,7 +29,8 @@ struct alignas(64) HeadInfo {
   int32_t nu_plan;  // condensed-slot cursor before condensation
   int32_t rw;       // 1: the head's kept rows are rewritten into its view this step
   uint64_t w_all;
-  uint64_t pad1[2];
+  int64_t voff;     // first view row of the head (row index into the view arrays)
+  uint64_t pad1;
 };
 
 // Everything a kernel needs, passed by value.
@@ -49,6 +50,7 @@ struct Args {
   int32_t *budget, *n_condense;
   uint64_t *w_all, *w_u, *thresh;
   int32_t *regularized;     // may be null
+  int32_t *view_off;        // [BH + 1] CSR offsets (SUM layout)
   uint32_t *error_word;
   // workspace
   HeadInfo *head;
@@ -71,6 +73,8 @@ struct Args {
   int xp_base, nxp;         // gathered-row partial slots of the standalone attention
   int reg_policy, mti_lower, mti_upper;  // regularize policy and its budget thresholds
   int gather_mode;          // rewrite kernel: GATHER_* below
+  int view_sum;             // 1: Flatten Index to the sum (packed views)
+  int64_t view_rows;        // rows of the view arrays: B * Hkv * V_cap, or view_total
   int ncs;                  // condense workgroups per head
   int bh0, nbh;             // (sequence, KV head) units this launch covers: [bh0, bh0 + nbh)
   uint32_t pq;
@@ -92,6 +96,8 @@ hipError_t launch_prefill(const Args &a, hipStream_t s, bool bf16);
 hipError_t launch_append(const Args &a, hipStream_t s, bool bf16);
 hipError_t launch_score(const Args &a, hipStream_t s, bool bf16);
 hipError_t launch_select(const Args &a, hipStream_t s);
+// exclusive scan of the rewritten budgets into view_off and each head's voff (SUM layout)
+hipError_t launch_flatten(const Args &a, hipStream_t s);
 // rewrite kernel: `mask` writes the mask words, `copy` copies the kept rows into the view,
 // `attend` adds the view attention and the condensed/dense attention segments
 hipError_t launch_rewrite(const Args &a, hipStream_t s, bool bf16, bool mask, bool copy, bool attend);

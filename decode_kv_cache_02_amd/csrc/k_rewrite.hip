@@ -92,9 +92,13 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_rewrite(Args a) {
   const size_t rowbase = (size_t)bh * P * BK;
   const char *pk = (const char *)a.pool_k + rowbase * ROWB + sub * 8 * EB;
   const char *pv = (const char *)a.pool_v + rowbase * ROWB + sub * 8 * EB;
-  char *vk = (char *)a.view_k + (size_t)bh * V * ROWB + sub * 8 * EB;
-  char *vv = (char *)a.view_v + (size_t)bh * V * ROWB + sub * 8 * EB;
-  int32_t *vpos = a.view_pos + (size_t)bh * V;
+  // the head's view rows start at voff (bh * V_cap, or its packed offset); vcap rows fit
+  const int64_t voff = hd->voff;
+  const uint32_t vcap = a.view_sum ? (uint32_t)max((int64_t)0, min(a.view_rows - voff, (int64_t)UINT32_MAX))
+                                   : (uint32_t)V;
+  char *vk = (char *)a.view_k + (size_t)voff * ROWB + sub * 8 * EB;
+  char *vv = (char *)a.view_v + (size_t)voff * ROWB + sub * 8 * EB;
+  int32_t *vpos = a.view_pos + voff;
 
   // the wavefront's blocks: weights and block info of all of them in flight at once
   const int iw = i0 + wave * bpw;
@@ -127,7 +131,7 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_rewrite(Args a) {
     if (sel) {
       s_src[wave][ns + idx] = (uint32_t)(pb * BK + lane);
       s_dst[wave][ns + idx] = vo + idx;
-      if (store && vo + idx < (uint32_t)V) vpos[vo + idx] = (int32_t)p;
+      if (store && vo + idx < vcap) vpos[vo + idx] = (int32_t)p;
     }
     ns += __popcll(mw);
   }
@@ -144,7 +148,7 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_rewrite(Args a) {
         const int kk = k < ns ? k : 0;
         const uint32_t src = s_src[wave][kk];
         dst[j] = s_dst[wave][kk];
-        act[j] = k < ns && (!store || dst[j] < (uint32_t)V);
+        act[j] = k < ns;  // attended whether or not its view row fits
         if (act[j]) {
           raw_load_nt(pk + (size_t)src * ROWB, kr[j]);
           raw_load_nt(pv + (size_t)src * ROWB, vr[j]);
@@ -156,7 +160,7 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_rewrite(Args a) {
       if (store) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          if (act[j]) {
+          if (act[j] && dst[j] < vcap) {
             raw_store_nt(vk + (size_t)dst[j] * ROWB, kr[j]);
             raw_store_nt(vv + (size_t)dst[j] * ROWB, vr[j]);
           }

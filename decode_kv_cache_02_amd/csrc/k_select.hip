@@ -569,8 +569,53 @@ __global__ __launch_bounds__(SEL_THREADS) void hardkv_select(Args a) {
                    : a.reg_policy == HARDKV_REG_SPARSE ? 0
                    : (kstar >= a.mti_lower && kstar <= a.mti_upper) ? 1 : 0;
     hd->rw = rw;
+    hd->voff = (int64_t)bh * a.V_cap;  // the maximum-length layout; the flatten kernel packs SUM
     if (a.regularized) a.regularized[bh] = rw;
-    if (rw && kstar > a.V_cap) atomicOr(a.error_word, HARDKV_ERR_VIEW_OVERFLOW);
+    if (rw && !a.view_sum && kstar > a.V_cap) atomicOr(a.error_word, HARDKV_ERR_VIEW_OVERFLOW);
+  }
+}
+
+// Flatten Index to the sum: one workgroup scans n_u = k* (rewritten heads) or 0 over
+// the units in order; head u's view starts at row voff_u = sum of n over units before u.
+__global__ __launch_bounds__(SEL_THREADS) void hardkv_flatten(Args a) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int BH = a.B * a.Hkv;
+  __shared__ int64_t s_wave[NW];
+  __shared__ int64_t s_carry;
+  if (tid == 0) s_carry = 0;
+  __syncthreads();
+  for (int base = 0; base < BH; base += SEL_THREADS) {
+    const int u = base + tid;
+    int64_t n = 0;
+    if (u < BH) n = a.head[u].rw ? (int64_t)a.head[u].kstar : 0;
+    int64_t v = n;  // inclusive scan inside the wavefront
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int src = lane - off < 0 ? 0 : lane - off;
+      const uint32_t lo = __shfl((uint32_t)v, src), hi = __shfl((uint32_t)((uint64_t)v >> 32), src);
+      const int64_t x = (int64_t)(((uint64_t)hi << 32) | lo);
+      if (lane >= off) v += x;
+    }
+    if (lane == 63) s_wave[wave] = v;
+    __syncthreads();
+    int64_t before = s_carry, total = s_carry;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      before += w < wave ? s_wave[w] : 0;
+      total += s_wave[w];
+    }
+    if (u < BH) {
+      const int64_t off = before + v - n;
+      a.head[u].voff = off;
+      a.view_off[u] = (int32_t)min(off, (int64_t)INT32_MAX);
+    }
+    __syncthreads();
+    if (tid == 0) s_carry = total;
+    __syncthreads();
+  }
+  if (tid == 0) {
+    a.view_off[BH] = (int32_t)min(s_carry, (int64_t)INT32_MAX);
+    if (s_carry > a.view_rows) atomicOr(a.error_word, HARDKV_ERR_VIEW_OVERFLOW);
   }
 }
 
@@ -591,6 +636,11 @@ hipError_t launch_score_g(const Args &a, hipStream_t s) {
 
 hipError_t launch_score(const Args &a, hipStream_t s, bool bf16) {
   return bf16 ? launch_score_g<BF16>(a, s) : launch_score_g<F32>(a, s);
+}
+
+hipError_t launch_flatten(const Args &a, hipStream_t s) {
+  hipLaunchKernelGGL(hardkv_flatten, dim3(1), dim3(SEL_THREADS), 0, s, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_select(const Args &a, hipStream_t s) {

@@ -30,8 +30,10 @@
  *      ties) are kept until their mass reaches T.  k* tokens are kept (the
  *      head-adaptive budget of tier 2).
  *   6. regularize: the kept positions, in ascending order, are copied bit for bit
- *      into rows 0 .. k*-1 of the head's view (2.C, Rewrite Cache with a
- *      max-length flat index: every head owns V_cap view rows).
+ *      into rows 0 .. k*-1 of the head's view (2.C, Rewrite Cache with a flat index
+ *      to the maximum length, every head owning V_cap view rows, or to the sum, the
+ *      views packed by the budgets), for the heads the regularize policy rewrites; the
+ *      others are attended through the mask (Sparse Loading).
  *   7. condense: each of the E oldest blocks is dropped (EVICT) or merged into the
  *      next condensed slot (MERGE, a ring of C slots): Kn += sum w_j/W_all k_j,
  *      Vn += sum w_j/W_all v_j, Omega += sum w_j/W_all, n += 64.  c += 64 E.
@@ -96,6 +98,18 @@ typedef enum { HARDKV_COND_OFF = 0, HARDKV_COND_EVICT = 1, HARDKV_COND_MERGE = 2
  * not rewritten leaves its view rows and view_pos untouched. */
 typedef enum { HARDKV_REG_REWRITE = 0, HARDKV_REG_SPARSE = 1, HARDKV_REG_MTI = 2 } hardkv_regularize_policy;
 
+/* Flatten Index (section 2.C: indices regularized to the maximum length or to their sum):
+ *   MAXLEN  every head owns view_cap rows: head u's row r is row u * view_cap + r (default);
+ *   SUM     the rewritten heads' kept rows are packed in unit order (CSR): head u's row r is
+ *           row view_off[u] + r, view_off the exclusive prefix sum over units of k* (0 for a
+ *           head that is not rewritten), so view memory follows the sum of the budgets.
+ *           The view arrays then hold view_total rows; rows past view_total are not
+ *           written and set HARDKV_ERR_VIEW_OVERFLOW.  A head's view only lives until the
+ *           next select (the offsets move with every step's budgets). */
+typedef enum { HARDKV_VIEW_MAXLEN = 0, HARDKV_VIEW_SUM = 1 } hardkv_view_layout;
+/* (The fused step's attention reads the kept rows themselves, so it does not depend on
+ * whether their view rows fit; hardkv_attend reads the views and sees only rows that fit.) */
+
 #define HARDKV_BLOCK 64
 #define HARDKV_HEAD_DIM 128
 #define HARDKV_MAX_KV_HEADS 64
@@ -122,6 +136,8 @@ typedef struct {
   int32_t regularize;      /* hardkv_regularize_policy (0: REWRITE) */
   int32_t mti_lower;       /* L_lower, tokens, >= 0 (policy MTI) */
   int32_t mti_upper;       /* L_upper, tokens, >= mti_lower (policy MTI) */
+  int32_t view_layout;     /* hardkv_view_layout (0: MAXLEN) */
+  int32_t view_total;      /* rows of the packed views (layout SUM), >= 0 */
 } hardkv_config;
 
 /* Device buffers of one layer.  All fixed capacity; 16-byte aligned.
@@ -129,8 +145,9 @@ typedef struct {
 typedef struct {
   void *dense_k, *dense_v;   /* e [B][Hkv][W][128]: position p in slot p mod W                    */
   void *pool_k, *pool_v;     /* e [B][Hkv][P][64][128]: position p in block (p/64) mod P, row p%64 */
-  void *view_k, *view_v;     /* e [B][Hkv][V_cap][128]: row r = r-th kept position (ascending)    */
-  int32_t *view_pos;         /* [B][Hkv][V_cap]: position of view row r (rows >= k* unspecified)  */
+  void *view_k, *view_v;     /* e [B][Hkv][V_cap][128] (MAXLEN) or e [view_total][128] (SUM): the
+                                head's row r = its r-th kept position (ascending)                */
+  int32_t *view_pos;         /* [B][Hkv][V_cap] or [view_total]: position of each view row        */
   float *cond_kn, *cond_vn;  /* fp32 [B][Hkv][C][128]: merged numerators                          */
   float *cond_omega;         /* fp32 [B][Hkv][C]: merged weight                                   */
   int32_t *cond_n;           /* [B][Hkv][C]: tokens merged into the slot                          */
@@ -147,6 +164,8 @@ typedef struct {
   uint64_t *thresh;          /* [B][Hkv]: T                                                       */
   int32_t *regularized;      /* [B][Hkv]: 1 if the head's view is rewritten this step, else 0
                                 (may be NULL: not reported)                                       */
+  int32_t *view_off;         /* [B*Hkv + 1]: CSR row offsets of the SUM layout, the last one the
+                                total (written by select; may be NULL in the MAXLEN layout)       */
   uint32_t *error_word;      /* [1]: HARDKV_ERR_* bits, or-ed                                     */
   void *workspace;           /* hardkv_workspace_size() bytes, zero-filled before first use      */
   size_t workspace_bytes;

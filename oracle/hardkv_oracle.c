@@ -427,6 +427,9 @@ static uint32_t unit_step(const orc_cfg *cfg, orc_state *st, int b, int h, const
                  : cfg->regularize == 1 ? 0
                  : (kstar >= cfg->mti_lower && kstar <= cfg->mti_upper) ? 1 : 0;
   if (st->regularized) st->regularized[u] = rw;
+  /* with the packed (sum) layout the views are written after every unit's budget is
+   * known (orc_step); attention reads the kept rows from the pool either way */
+  const int packed = cfg->view_layout == 1;
   /* the pool rows of the kept positions, ascending (Sparse Loading reads these) */
   int64_t *kept = (int64_t *)malloc(sizeof(int64_t) * (size_t)(kstar > 0 ? kstar : 1));
   {
@@ -436,7 +439,7 @@ static uint32_t unit_step(const orc_cfg *cfg, orc_state *st, int b, int h, const
   }
   /* Rewrite Cache with a max-length flat index: the selected rows, in ascending
    * position, become rows 0 .. k*-1 of the head's fixed-capacity view */
-  if (rw) {
+  if (rw && !packed) {
     int32_t r = 0;
     if (kstar > cfg->view_cap) err |= ORC_ERR_VIEW_OVERFLOW;
     for (int32_t i = 0; i < nU; ++i) {
@@ -487,8 +490,8 @@ static uint32_t unit_step(const orc_cfg *cfg, orc_state *st, int b, int h, const
     tc->n_cond = 0;
     for (int s = 0; s < cfg->condensed_slots && s < 4096; ++s)
       if (st->cond_n[u * cfg->condensed_slots + s] > 0) tc->slot[tc->n_cond++] = s;
-    tc->kept_rows = rw ? NULL : kept;
-    tc->n_view = rw ? (kstar < cfg->view_cap ? kstar : cfg->view_cap) : kstar;
+    tc->kept_rows = (rw && !packed) ? NULL : kept;
+    tc->n_view = (rw && !packed) ? (kstar < cfg->view_cap ? kstar : cfg->view_cap) : kstar;
     tc->dense_lo = t > W ? t - W : 0;
     tc->n_dense = t - tc->dense_lo;
     double qd[1024];
@@ -541,6 +544,37 @@ int32_t orc_step(const orc_cfg *cfg, orc_state *st, const void *q, const void *k
 #endif
   for (int64_t i = 0; i < units; ++i) err |= unit_step(cfg, st, (int)(i / H), (int)(i % H), q, out, do_attend);
   (void)nthreads;
+
+  /* Flatten Index to the sum (section 2.C): the rewritten heads' kept rows, each head's in
+   * ascending position, packed in unit order; head u starts at row view_off[u] */
+  if (cfg->view_layout == 1) {
+    const int P = cfg->pool_blocks;
+    int64_t off = 0;
+    for (int64_t u = 0; u < units; ++u) {
+      const int32_t kstar = st->budget[u];
+      const int rw = cfg->regularize == 0 ? 1
+                     : cfg->regularize == 1 ? 0
+                     : (kstar >= cfg->mti_lower && kstar <= cfg->mti_upper) ? 1 : 0;
+      st->view_off[u] = (int32_t)off;
+      if (!rw) continue;
+      const int64_t t = st->seq_len[u / H];
+      const int64_t pend = t > W ? t - W : 0;
+      const int64_t c0 = st->pool_head[u] - (int64_t)BK * st->n_condense[u];
+      int64_t r = 0;
+      for (int64_t j = c0; j < pend; ++j) {
+        if (!((st->mask[u * P + (j / BK) % P] >> (j % BK)) & 1u)) continue;
+        if (off + r < cfg->view_total) {
+          row_copy(st->view_k, off + r, st->pool_k, pool_row(cfg, u, j), D, eb);
+          row_copy(st->view_v, off + r, st->pool_v, pool_row(cfg, u, j), D, eb);
+          st->view_pos[off + r] = (int32_t)j;
+        }
+        ++r;
+      }
+      off += kstar;
+    }
+    st->view_off[units] = (int32_t)off;
+    if (off > cfg->view_total) err |= ORC_ERR_VIEW_OVERFLOW;
+  }
   st->error_word |= err;
   return 0;
 }

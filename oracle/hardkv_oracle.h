@@ -52,6 +52,8 @@ typedef struct {
   int32_t regularize;        /* 0 rewrite every head, 1 none (Sparse Loading), 2 the heads with
                                 mti_lower <= k* <= mti_upper */
   int32_t mti_lower, mti_upper;
+  int32_t view_layout;       /* 0: every head owns view_cap rows; 1: packed in unit order (CSR) */
+  int32_t view_total;        /* rows of the packed views (layout 1) */
 } orc_cfg;
 
 typedef struct {
@@ -66,6 +68,7 @@ typedef struct {
   int32_t *budget, *n_condense;
   uint64_t *w_all, *w_u, *thresh;
   int32_t *regularized;      /* [B*H] 1 if the head's view was rewritten this step (may be NULL) */
+  int32_t *view_off;         /* [B*H + 1] row offsets of the packed views (layout 1) */
   uint32_t error_word;
 } orc_state;
 

@@ -29,6 +29,7 @@ class OrcCfg(C.Structure):
         ("condensed_slots", C.c_int32), ("cond_mode", C.c_int32), ("merge_bias", C.c_int32),
         ("top_p", C.c_double), ("tau", C.POINTER(C.c_float)),
         ("regularize", C.c_int32), ("mti_lower", C.c_int32), ("mti_upper", C.c_int32),
+        ("view_layout", C.c_int32), ("view_total", C.c_int32),
     ]
 
 
@@ -41,7 +42,8 @@ class OrcState(C.Structure):
         ("seq_len", C.c_void_p), ("pool_head", C.c_void_p), ("scores", C.c_void_p),
         ("weights", C.c_void_p), ("mask", C.c_void_p), ("budget", C.c_void_p),
         ("n_condense", C.c_void_p), ("w_all", C.c_void_p), ("w_u", C.c_void_p),
-        ("thresh", C.c_void_p), ("regularized", C.c_void_p), ("error_word", C.c_uint32),
+        ("thresh", C.c_void_p), ("regularized", C.c_void_p), ("view_off", C.c_void_p),
+        ("error_word", C.c_uint32),
     ]
 
 
@@ -174,7 +176,7 @@ class Oracle:
 
     def __init__(self, wl, tau: Optional[np.ndarray] = None, merge_bias: bool = True,
                  top_p: Optional[float] = None, regularize: int = 0, mti_lower: int = 0,
-                 mti_upper: int = 0):
+                 mti_upper: int = 0, view_layout: int = 0, view_total: int = 0):
         self.wl = wl
         B, H, Hq, D = wl.batch, wl.num_kv_heads, wl.num_q_heads, wl.head_dim
         W, P, V, Cs = wl.dense_window, wl.P_blk, wl.V_cap, wl.condensed_slots
@@ -184,14 +186,21 @@ class Oracle:
         self.cfg = OrcCfg(B, Hq, H, D, wl.elem_bytes, W, P, wl.sparse_cap, V, Cs, wl.cond_mode,
                           1 if merge_bias else 0, float(wl.top_p if top_p is None else top_p),
                           self.tau.ctypes.data_as(C.POINTER(C.c_float)), int(regularize),
-                          int(mti_lower), int(mti_upper))
+                          int(mti_lower), int(mti_upper), int(view_layout), int(view_total))
         self.dense_k = np.zeros((B, H, W, D), st)
         self.dense_v = np.zeros((B, H, W, D), st)
         self.pool_k = np.zeros((B, H, P, BK, D), st)
         self.pool_v = np.zeros((B, H, P, BK, D), st)
-        self.view_k = np.zeros((B, H, V, D), st)
-        self.view_v = np.zeros((B, H, V, D), st)
-        self.view_pos = np.full((B, H, V), -1, np.int32)
+        if view_layout == 1:  # packed (CSR) views
+            Vt = max(1, view_total)
+            self.view_k = np.zeros((Vt, D), st)
+            self.view_v = np.zeros((Vt, D), st)
+            self.view_pos = np.full(Vt, -1, np.int32)
+        else:
+            self.view_k = np.zeros((B, H, V, D), st)
+            self.view_v = np.zeros((B, H, V, D), st)
+            self.view_pos = np.full((B, H, V), -1, np.int32)
+        self.view_off = np.zeros(B * H + 1, np.int32)
         self.cond_kn = np.zeros((B, H, Cs, D), np.float64)
         self.cond_vn = np.zeros((B, H, Cs, D), np.float64)
         self.cond_omega = np.zeros((B, H, Cs), np.float64)
@@ -211,7 +220,8 @@ class Oracle:
         self.st = OrcState(*[_p(getattr(self, n)) for n in (
             "dense_k", "dense_v", "pool_k", "pool_v", "view_k", "view_v", "view_pos", "cond_kn",
             "cond_vn", "cond_omega", "cond_n", "cond_cursor", "seq_len", "pool_head", "scores",
-            "weights", "mask", "budget", "n_condense", "w_all", "w_u", "thresh", "regularized")], 0)
+            "weights", "mask", "budget", "n_condense", "w_all", "w_u", "thresh", "regularized",
+            "view_off")], 0)
 
     @property
     def error_word(self) -> int:

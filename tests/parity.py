@@ -46,13 +46,17 @@ class Pair:
     """A GPU state and oracle state(s) of the same layer, fed the same inputs."""
 
     def __init__(self, wl, inputs=None, top_p=None, tau=None, cond_mode=None, merge_bias=True,
-                 device="cuda", oracle_units=None, layer=0, regularize=0, mti_lower=0, mti_upper=0):
+                 device="cuda", oracle_units=None, layer=0, regularize=0, mti_lower=0, mti_upper=0,
+                 view_layout=0, view_total=0):
         self.wl = wl if cond_mode is None else wl.with_(cond_mode=cond_mode)
         if top_p is not None:
             self.wl = self.wl.with_(top_p=top_p)
         self.inp = inputs if inputs is not None else make_inputs(self.wl, layer=layer, device=device)
         self.tau = [self.wl.tau] * self.wl.num_kv_heads if tau is None else list(tau)
-        pol = dict(regularize=regularize, mti_lower=mti_lower, mti_upper=mti_upper)
+        pol = dict(regularize=regularize, mti_lower=mti_lower, mti_upper=mti_upper,
+                   view_layout=view_layout, view_total=view_total)
+        self.packed = view_layout == hk.HARDKV_VIEW_SUM
+        assert not (self.packed and oracle_units is not None), "packed views need the whole layer"
         self.cfg = hk.Config.from_workload(self.wl, tau=self.tau, merge_bias=merge_bias, **pol)
         self.st = hk.State(self.cfg, device=device)
         hk.hardkv_prefill(self.cfg, self.st, self.inp.k_ctx, self.inp.v_ctx, self.inp.ctx_len)
@@ -124,7 +128,7 @@ class Pair:
             "seq_len", "budget", "n_condense", "cond_cursor", "pool_head", "w_all", "w_u", "thresh",
             "regularized", "error_word")}
         big_names = ["scores", "weights", "mask", "cond_n", "cond_kn", "cond_vn", "cond_omega"]
-        if check_views:
+        if check_views and not self.packed:
             big_names += ["view_pos", "view_k", "view_v"]
         full = None
         if None in self.orcs:
@@ -159,7 +163,9 @@ class Pair:
                 assert np.array_equal(g["mask"].numpy().view(np.uint64), o.mask[ob, oh]), f"{tag} mask"
                 k = int(small["budget"][b, h])
                 kv = min(k, wl.V_cap)
-                if check_views and not int(small["regularized"][b, h]):
+                if self.packed:
+                    pass  # the packed views are compared as a whole below
+                elif check_views and not int(small["regularized"][b, h]):
                     # not rewritten this step: both sides keep the view they held before
                     assert np.array_equal(g["view_pos"].numpy(), o.view_pos[ob, oh]), f"{tag} kept view_pos"
                 elif check_views:
@@ -180,6 +186,14 @@ class Pair:
                     oo = outs[key][b, h * G:(h + 1) * G] if key is None else outs[key][0]
                     e = row_rel_err(go, oo)
                     assert e <= ATT_TOL, f"{tag} attention rel err {e}"
+        if self.packed and check_views:
+            o = self.orcs[None][0]
+            voff = self.st.view_off.cpu().numpy()
+            assert np.array_equal(voff, o.view_off), "view_off"
+            n = min(int(voff[-1]), int(self.cfg.c.view_total))
+            assert np.array_equal(self.st.view_pos[:n].cpu().numpy(), o.view_pos[:n]), "packed view_pos"
+            assert np.array_equal(raw(self.st.view_k[:n]), o.view_k[:n]), "packed view_k"
+            assert np.array_equal(raw(self.st.view_v[:n]), o.view_v[:n]), "packed view_v"
         if None in self.orcs:
             assert int(small["error_word"][0]) == err, "error word"
         else:

@@ -242,3 +242,48 @@ def test_fused_output_does_not_depend_on_policy():
         torch.cuda.synchronize()
         outs.append(out.clone())
     assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
+
+
+# ---- Flatten Index to the sum (packed views) ---------------------------------------------
+PACKED_CASES = {
+    "merge_bf16": (dict(cond_mode=COND_MERGE, ctx_len=500, ctx_min=100, steps=3), 0),
+    "evict_f32": (dict(dtype="f32", steps=2), 0),
+    "mti_batch16": (dict(batch=16, cond_mode=COND_MERGE, ctx_len=500, ctx_min=100, heavy=(0, 6), steps=2), 2),
+    "g8_sparse": (dict(num_q_heads=16, num_kv_heads=2, steps=2), 1),
+}
+
+
+@pytest.mark.parametrize("name", list(PACKED_CASES))
+@pytest.mark.parametrize("fused", [True, False])
+def test_packed_views_parity(name, fused):
+    """Views packed in unit order (CSR offsets from the rewritten budgets) match the
+    oracle's row for row, with the offsets, under the fused step and the separate calls."""
+    from parity import Pair
+    kw, pol = PACKED_CASES[name]
+    kw = dict(kw)
+    steps = kw.pop("steps")
+    wl = tiny_workload(steps=steps, **kw)
+    lo, hi = _mti_bounds(wl) if pol == 2 else (0, 0)
+    total = wl.batch * wl.num_kv_heads * wl.V_cap
+    print(f"case {name} fused={fused}: policy {pol}, {total} packed rows, {wl}", flush=True)
+    pr = Pair(wl, regularize=pol, mti_lower=lo, mti_upper=hi, view_layout=1, view_total=total)
+    for _ in range(steps):
+        pr.step(fused=fused)
+
+
+def test_packed_views_overflow_sets_the_bit():
+    """A packed capacity below the sum of the budgets: the overflow bit is set, rows that
+    fit are still the oracle's, nothing is written past the end, and attention (which
+    reads the kept rows, not the view) still matches."""
+    from parity import Pair
+    wl = tiny_workload(cond_mode=COND_EVICT, steps=1)
+    from oracle import hardkv_oracle as orc
+    from synth import make_inputs
+    inp = make_inputs(wl)
+    o = orc.Oracle(wl)
+    o.prefill(inp.k_ctx, inp.v_ctx, inp.ctx_len)
+    o.step(inp.q[0], inp.k_new[0], inp.v_new[0], attend=False)
+    total = int(o.budget.sum()) - 7
+    pr = Pair(wl, view_layout=1, view_total=total)
+    pr.step(fused=True)
+    assert int(pr.st.error_word[0].item()) & 2

@@ -268,3 +268,47 @@ def test_mti_thresholds_pick_heads_by_budget():
                 np.testing.assert_array_equal(o_m.view_pos[b, h, :k], o_rw.view_pos[b, h, :k])
             else:
                 assert (o_m.view_pos[b, h] == -1).all()
+
+
+# ---- Flatten Index to the sum (packed, CSR views) --------------------------------------
+@pytest.mark.parametrize("policy", [0, 2])
+def test_packed_views_are_the_concatenation(policy):
+    """The sum layout packs each rewritten head's view rows (the same rows as the
+    maximum-length layout) in unit order: view_off is the exclusive prefix sum of the
+    rewritten budgets, the packed rows and positions are the per-head ones concatenated,
+    and attention is unchanged."""
+    wl = tiny_workload(cond_mode=COND_MERGE, steps=2, heavy=(0, 6), batch=4, ctx_len=500, ctx_min=100)
+    inp = make_inputs(wl)
+    pol = dict(regularize=policy)
+    if policy == 2:
+        o0, _ = _run(wl, inp, 1)
+        vals = np.unique(o0.budget)
+        pol.update(mti_lower=int(vals[1]), mti_upper=int(vals[-2]))
+    total = wl.batch * wl.num_kv_heads * wl.V_cap
+    o_max, outs_max = _run(wl, inp, 2, **pol)
+    o_sum, outs_sum = _run(wl, inp, 2, view_layout=1, view_total=total, **pol)
+    for a, b in zip(outs_max, outs_sum):
+        assert np.array_equal(a, b)
+    n = (o_sum.budget * o_sum.regularized).ravel().astype(np.int64)
+    np.testing.assert_array_equal(o_sum.view_off, np.concatenate([[0], np.cumsum(n)]))
+    for u in range(wl.batch * wl.num_kv_heads):
+        b, h = divmod(u, wl.num_kv_heads)
+        k, off = int(n[u]), int(o_sum.view_off[u])
+        np.testing.assert_array_equal(o_sum.view_k[off:off + k], o_max.view_k[b, h, :k])
+        np.testing.assert_array_equal(o_sum.view_v[off:off + k], o_max.view_v[b, h, :k])
+        np.testing.assert_array_equal(o_sum.view_pos[off:off + k], o_max.view_pos[b, h, :k])
+    assert o_sum.error_word == 0
+
+
+def test_packed_views_overflow():
+    """Fewer packed rows than the budgets need: the overflow bit, and rows past the end are
+    not written (the ones before are the concatenation's prefix)."""
+    wl = tiny_workload(cond_mode=COND_EVICT, steps=1)
+    inp = make_inputs(wl)
+    o_max, _ = _run(wl, inp, 1)
+    need = int(o_max.budget.sum())
+    o, _ = _run(wl, inp, 1, view_layout=1, view_total=need - 5)
+    assert o.error_word & 2
+    flat = np.concatenate([o_max.view_pos[b, h, :o_max.budget[b, h]]
+                           for b in range(wl.batch) for h in range(wl.num_kv_heads)])
+    np.testing.assert_array_equal(o.view_pos, flat[:need - 5])

@@ -67,6 +67,8 @@ def parse():
                          "the budget-threshold rule (rewrite iff --mti-lower <= k* <= --mti-upper)")
     ap.add_argument("--mti-lower", type=int, default=0)
     ap.add_argument("--mti-upper", type=int, default=1 << 30)
+    ap.add_argument("--calibration", choices=["fixed", "entropy"], default="fixed",
+                    help="calibration temperature: the workload's tau (default) or fitted per head by entropy")
     ap.add_argument("--view-layout", choices=["maxlen", "sum"], default="maxlen",
                     help="Flatten Index: view_cap rows per head (default) or packed in unit order")
     ap.add_argument("--view-total", type=int, default=0,
@@ -93,14 +95,17 @@ POLICY = {"rewrite": hk.HARDKV_REG_REWRITE, "sparse": hk.HARDKV_REG_SPARSE, "mti
 
 
 class Layer:
-    def __init__(self, wl, layer, steps, top_p=None, policy=("rewrite", 0, 0), view=("maxlen", 0)):
+    def __init__(self, wl, layer, steps, top_p=None, policy=("rewrite", 0, 0), view=("maxlen", 0),
+                 calibration="fixed"):
         self.wl = wl
         self.inp = make_inputs(wl, layer=layer, device="cuda", steps=steps)
         total = view[1] or wl.batch * wl.num_kv_heads * wl.V_cap
         self.cfg = hk.Config.from_workload(wl, top_p=top_p, regularize=POLICY[policy[0]],
                                            mti_lower=policy[1], mti_upper=policy[2],
                                            view_layout=hk.HARDKV_VIEW_SUM if view[0] == "sum" else
-                                           hk.HARDKV_VIEW_MAXLEN, view_total=total)
+                                           hk.HARDKV_VIEW_MAXLEN, view_total=total,
+                                           calibration=hk.HARDKV_CAL_ENTROPY if calibration == "entropy"
+                                           else hk.HARDKV_CAL_FIXED)
         self.st = hk.State(self.cfg)
         hk.hardkv_prefill(self.cfg, self.st, self.inp.k_ctx, self.inp.v_ctx, self.inp.ctx_len)
         self.out = torch.zeros((wl.batch, wl.num_q_heads, D), dtype=torch.float32, device="cuda")
@@ -440,7 +445,7 @@ def main():
     layers = []
     for layer in range(wl.layers):
         L = Layer(wl, layer, nsteps, top_p=top_p, policy=(args.regularize, args.mti_lower, args.mti_upper),
-                  view=(args.view_layout, args.view_total))
+                  view=(args.view_layout, args.view_total), calibration=args.calibration)
         if layer == 0 and not args.no_cpu_baseline:
             L.inp_cpu_source = {"k_ctx": L.inp.k_ctx, "v_ctx": L.inp.v_ctx, "ctx_len": L.inp.ctx_len}
         else:
@@ -575,7 +580,7 @@ def main():
                    "top_p": float(layers[0].cfg.c.top_p), "cond_mode": "merge",
                    "regularize": args.regularize if args.regularize != "mti" else
                    f"mti [{args.mti_lower}, {args.mti_upper}]",
-                   "view_layout": args.view_layout,
+                   "view_layout": args.view_layout, "calibration": args.calibration,
                    "timing": ("one-step graph replay from the prefilled state" if restore_mode else
                               "graph of the K streaming steps") + (" (eager)" if args.eager else "")},
         "kv_tokens_scanned_per_s": scanned_step * steps_per_s,

@@ -26,7 +26,6 @@ struct AttnState {
   }
 };
 
-HK_DEV float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // one row (the same row in all 16 lanes of the group); logit = (q . k) * kscale + bias,
 // value v.  Called by every lane of the wavefront; rows with act == false add nothing.

@@ -18,7 +18,7 @@ bool aligned16(const void *p) { return p != nullptr && ((uintptr_t)p & 15u) == 0
 
 struct Plan {
   Args a;
-  size_t off_head, off_cmax, off_blkinfo, off_part, ws_bytes;
+  size_t off_head, off_cmax, off_ent, off_blkinfo, off_part, ws_bytes;
 };
 
 // Checks the configuration and derives every size; fills the size fields of p.a.
@@ -54,6 +54,7 @@ int32_t plan(const hardkv_config *cfg, Plan &p) {
     return HARDKV_EINVAL;
   if (cfg->view_layout != HARDKV_VIEW_MAXLEN && cfg->view_layout != HARDKV_VIEW_SUM) return HARDKV_EINVAL;
   if (cfg->view_layout == HARDKV_VIEW_SUM && cfg->view_total < 0) return HARDKV_EINVAL;
+  if (cfg->calibration != HARDKV_CAL_FIXED && cfg->calibration != HARDKV_CAL_ENTROPY) return HARDKV_EINVAL;
 
   a.B = cfg->batch;
   a.Hq = cfg->num_q_heads;
@@ -67,6 +68,7 @@ int32_t plan(const hardkv_config *cfg, Plan &p) {
   a.mode = cfg->cond_mode;
   a.merge_bias = cfg->merge_bias ? 1 : 0;
   a.view_sum = cfg->view_layout == HARDKV_VIEW_SUM ? 1 : 0;
+  a.calibration = cfg->calibration;
   a.view_rows = a.view_sum ? (int64_t)cfg->view_total
                            : (int64_t)cfg->batch * cfg->num_kv_heads * cfg->view_cap;
   a.reg_policy = cfg->regularize;
@@ -117,7 +119,8 @@ int32_t plan(const hardkv_config *cfg, Plan &p) {
 
   p.off_head = 0;
   p.off_cmax = align256(p.off_head + (size_t)BH * sizeof(HeadInfo));
-  p.off_blkinfo = align256(p.off_cmax + (size_t)BH * a.nch_score * sizeof(float));
+  p.off_ent = align256(p.off_cmax + (size_t)BH * a.nch_score * sizeof(float));
+  p.off_blkinfo = align256(p.off_ent + (a.calibration ? (size_t)BH * a.nch_score * G * 3 * sizeof(float) : 0));
   p.off_part = align256(p.off_blkinfo + (size_t)BH * a.P * sizeof(uint2));
   p.ws_bytes = align256(p.off_part + (size_t)BH * a.npart * G * (2 + HD) * sizeof(float));
   return HARDKV_OK;
@@ -163,10 +166,13 @@ int32_t bind(const hardkv_state *st, Plan &p) {
   if (p.a.view_sum && (!st->view_off || ((uintptr_t)st->view_off & 3u))) return HARDKV_EINVAL;
   if (st->view_off && ((uintptr_t)st->view_off & 3u)) return HARDKV_EINVAL;
   a.view_off = st->view_off;
+  if (st->tau_fit && ((uintptr_t)st->tau_fit & 3u)) return HARDKV_EINVAL;
+  a.tau_fit = st->tau_fit;
   a.error_word = st->error_word;
   char *ws = (char *)st->workspace;
   a.head = reinterpret_cast<HeadInfo *>(ws + p.off_head);
   a.cmax = reinterpret_cast<float *>(ws + p.off_cmax);
+  a.ent = reinterpret_cast<float *>(ws + p.off_ent);
   a.blkinfo = reinterpret_cast<uint2 *>(ws + p.off_blkinfo);
   a.part = reinterpret_cast<float *>(ws + p.off_part);
   return HARDKV_OK;
@@ -196,7 +202,8 @@ hipError_t step_stage(const hardkv_config *cfg, Args &a, int stage, hipStream_t 
     case 0: return launch_append(a, s, bf);
     case 1: return launch_score(a, s, bf);
     case 2: {
-      hipError_t e = launch_select(a, s);
+      hipError_t e = a.calibration ? launch_fit(a, s) : hipSuccess;
+      if (e == hipSuccess) e = launch_select(a, s);
       if (e == hipSuccess && a.view_sum) e = launch_flatten(a, s);
       return e;
     }
@@ -283,6 +290,7 @@ int32_t hardkv_select(const hardkv_config *cfg, hardkv_state *st, const void *q,
   hipStream_t s = (hipStream_t)stream;
   const bool bf = is_bf16(cfg);
   hipError_t e = launch_score(p.a, s, bf);
+  if (e == hipSuccess && p.a.calibration) e = launch_fit(p.a, s);
   if (e == hipSuccess) e = launch_select(p.a, s);
   if (e == hipSuccess && p.a.view_sum) e = launch_flatten(p.a, s);
   if (e == hipSuccess) e = launch_rewrite(p.a, s, bf, true, false, false);  // mask words

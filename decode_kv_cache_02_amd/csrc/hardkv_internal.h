@@ -30,7 +30,8 @@ struct alignas(64) HeadInfo {
   int32_t rw;       // 1: the head's kept rows are rewritten into its view this step
   uint64_t w_all;
   int64_t voff;     // first view row of the head (row index into the view arrays)
-  uint64_t pad1;
+  float kappa;      // calibration slope of the step (fitted temperature)
+  float tau;        // the fitted temperature
 };
 
 // Everything a kernel needs, passed by value.
@@ -51,10 +52,13 @@ struct Args {
   uint64_t *w_all, *w_u, *thresh;
   int32_t *regularized;     // may be null
   int32_t *view_off;        // [BH + 1] CSR offsets (SUM layout)
+  float *tau_fit;           // [BH] fitted temperatures (may be null)
   uint32_t *error_word;
   // workspace
   HeadInfo *head;
   float *cmax;        // [BH][nch_score] max score of each score workgroup
+  float *ent;         // [BH][nch_score][G][3] per query: (max, sum 2^(l-max), sum 2^(l-max)(l-max)),
+                      // l = q . k log2(e) / sqrt(D) (entropy calibration)
   uint2 *blkinfo;     // [BH][P] per ring block: (first view row, ties before the block)
   float *part;        // [BH][npart][G][2 + HD] attention partials (m, l, acc)
   // prefill
@@ -74,6 +78,7 @@ struct Args {
   int reg_policy, mti_lower, mti_upper;  // regularize policy and its budget thresholds
   int gather_mode;          // rewrite kernel: GATHER_* below
   int view_sum;             // 1: Flatten Index to the sum (packed views)
+  int calibration;          // HARDKV_CAL_*
   int64_t view_rows;        // rows of the view arrays: B * Hkv * V_cap, or view_total
   int ncs;                  // condense workgroups per head
   int bh0, nbh;             // (sequence, KV head) units this launch covers: [bh0, bh0 + nbh)
@@ -98,6 +103,8 @@ hipError_t launch_score(const Args &a, hipStream_t s, bool bf16);
 hipError_t launch_select(const Args &a, hipStream_t s);
 // exclusive scan of the rewritten budgets into view_off and each head's voff (SUM layout)
 hipError_t launch_flatten(const Args &a, hipStream_t s);
+// entropy-matched temperature of every head (calibration ENTROPY), before the select
+hipError_t launch_fit(const Args &a, hipStream_t s);
 // rewrite kernel: `mask` writes the mask words, `copy` copies the kept rows into the view,
 // `attend` adds the view attention and the condensed/dense attention segments
 hipError_t launch_rewrite(const Args &a, hipStream_t s, bool bf16, bool mask, bool copy, bool attend);
@@ -109,6 +116,8 @@ hipError_t launch_combine(const Args &a, hipStream_t s);
 // device helpers
 // ---------------------------------------------------------------------------------------
 #define HK_DEV __device__ __forceinline__
+
+HK_DEV float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
 HK_DEV float bf_lo(uint32_t x) { return __uint_as_float(x << 16); }
 HK_DEV float bf_hi(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }

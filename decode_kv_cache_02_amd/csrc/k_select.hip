@@ -53,7 +53,19 @@ HK_DEV float wave_max(float v) {
   return v;
 }
 
-template <typename T, int G>
+// (m, z, a) of a base-2 softmax piece: m its max logit, z = sum 2^(l - m), a = sum
+// 2^(l - m) (l - m); two pieces of the same query merge exactly as below
+HK_DEV void ent_merge(float &m, float &z, float &w, float m2, float z2, float w2) {
+  const float M = fmaxf(m, m2);
+  if (M == -INFINITY) return;
+  const float d1 = m == -INFINITY ? 0.0f : m - M, d2 = m2 == -INFINITY ? 0.0f : m2 - M;
+  const float s1 = m == -INFINITY ? 0.0f : exp2_fast(d1), s2 = m2 == -INFINITY ? 0.0f : exp2_fast(d2);
+  w = s1 * (w + d1 * z) + s2 * (w2 + d2 * z2);
+  z = s1 * z + s2 * z2;
+  m = M;
+}
+
+template <typename T, int G, bool ENT>
 __global__ __launch_bounds__(NTHREADS) void hardkv_score(Args a) {
   constexpr int EB = Elem<T>::bytes;
   const int lin = xcd_swizzle(blockIdx.y * gridDim.x + blockIdx.x, gridDim.x * gridDim.y);
@@ -65,6 +77,10 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_score(Args a) {
 
   __shared__ float s_stage[4][16];
   __shared__ float s_wmax[4];
+  __shared__ float s_ent[ENT ? 4 : 1][G][3];
+  // entropy calibration: lane `sub` < G keeps query sub's softmax piece over its rows
+  float em = -INFINITY, ez = 0.0f, ew = 0.0f;
+  constexpr float c2 = (float)(1.4426950408889634074 / 11.313708498984760390);  // log2(e) / sqrt(128)
 
   const int64_t t = a.seq_len[b];
   const int64_t c = a.pool_head[bh];
@@ -115,11 +131,14 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_score(Args a) {
           float kf[8];
           raw_to_f(buf[u][l], kf);
           float s = dot_tree(qf[0], kf);
+          float dmine = s;  // the dot of query `sub` (lanes sub < G)
 #pragma unroll
           for (int g = 1; g < G; ++g) {
             float d = dot_tree(qf[g], kf);
+            if (ENT && g == sub) dmine = d;
             s = d > s ? d : s;
           }
+          if (ENT && sub < G && gi * 16 + l * 4 + grp < nrows) ent_merge(em, ez, ew, dmine * c2, 1.0f, 0.0f);
           s = s + 0.0f;  // a zero score is +0
           if (sub == 0) s_stage[wave][l * 4 + grp] = s;
         }
@@ -153,10 +172,32 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_score(Args a) {
   }
   wmax = wave_max(wmax);
   if (lane == 0) s_wmax[wave] = wmax;
+  if (ENT) {
+    // the four row groups of the wavefront, then the four wavefronts
+#pragma unroll
+    for (int off = 16; off <= 32; off <<= 1) {
+      const float m2 = __shfl_xor(em, off), z2 = __shfl_xor(ez, off), w2 = __shfl_xor(ew, off);
+      ent_merge(em, ez, ew, m2, z2, w2);
+    }
+    if (lane < G) {
+      s_ent[wave][lane][0] = em;
+      s_ent[wave][lane][1] = ez;
+      s_ent[wave][lane][2] = ew;
+    }
+  }
   __syncthreads();
   if (tid == 0)
     a.cmax[(size_t)bh * a.nch_score + chunk] =
         fmaxf(fmaxf(s_wmax[0], s_wmax[1]), fmaxf(s_wmax[2], s_wmax[3]));
+  if (ENT && tid < G) {
+    float m = s_ent[0][tid][0], z = s_ent[0][tid][1], w = s_ent[0][tid][2];
+#pragma unroll
+    for (int wv = 1; wv < 4; ++wv) ent_merge(m, z, w, s_ent[wv][tid][0], s_ent[wv][tid][1], s_ent[wv][tid][2]);
+    float *e = a.ent + (((size_t)bh * a.nch_score + chunk) * G + tid) * 3;
+    e[0] = m;
+    e[1] = z;
+    e[2] = w;
+  }
 }
 
 // ---------------------------------------------------------------------------------------
@@ -315,7 +356,7 @@ __global__ __launch_bounds__(SEL_THREADS) void hardkv_select(Args a) {
   const int nx = (int)E;                                   // condensing blocks come first
   const int nub = nblk - nx;                               // survivor blocks
   const int pb_lo = (int)((c / BK) % P);
-  const float kap = a.kappa[h];
+  const float kap = a.calibration ? hd->kappa : a.kappa[h];
   const size_t rowbase = (size_t)bh * P * BK;
   auto ring = [&](int i) {
     int pb = pb_lo + i;
@@ -619,23 +660,199 @@ __global__ __launch_bounds__(SEL_THREADS) void hardkv_flatten(Args a) {
   }
 }
 
-template <typename T>
-hipError_t launch_score_g(const Args &a, hipStream_t s) {
+// ---------------------------------------------------------------------------------------
+// calibration temperature fitted by entropy
+// ---------------------------------------------------------------------------------------
+constexpr int FIT_POINTS = 17;  // grid points per round (16 intervals)
+constexpr int FIT_ROUNDS = 5;
+constexpr int FIT_THREADS = 512;  // 2 waves per SIMD: the 3 x 17 per-candidate values stay in registers
+constexpr int FIT_NW = FIT_THREADS / 64;
+
+HK_DEV double shfl_xor_d(double v, int off) {
+  const uint64_t u = __double_as_longlong(v);
+  const uint32_t lo = __shfl_xor((uint32_t)u, off), hi = __shfl_xor((uint32_t)(u >> 32), off);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+// hardkv_fit, grid (B*Hkv), 512 threads: one workgroup per head.  The target is the mean
+// over the group's queries of the entropy (nats) of their raw attention over the pool,
+// from the per-chunk softmax pieces the score kernel left; then five rounds of a 17-point
+// grid on log2 tau in [-12, 12] find the bracket where the entropy of the calibrated
+// softmax(s / (sqrt(D) tau)) over the pool reaches the target (it grows with tau); tau
+// is the midpoint of the last bracket.
+__global__ __launch_bounds__(FIT_THREADS) void hardkv_fit(Args a) {
+  const int bh = a.bh0 + blockIdx.x;
+  const int b = bh / a.Hkv;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int P = a.P, G = a.G;
+  __shared__ double s_acc[FIT_NW][2 * FIT_POINTS];
+  __shared__ float s_ck[FIT_POINTS];
+  __shared__ int s_reach[FIT_POINTS];
+  __shared__ double s_h;
+  __shared__ float s_m;
+  __shared__ double s_lo, s_hi;
+
+  const int64_t t = a.seq_len[b];
+  const int64_t c = a.pool_head[bh];
+  const int64_t pend = pool_end(t, a.W);
+  const int64_t N = pend - c;
+
+  // the target entropy: each thread merges, per query, the pieces of chunks tid,
+  // tid + FIT_THREADS, ...; then the lanes of a wavefront, then the wavefronts
+  __shared__ float s_piece[FIT_NW][8][3];
+  {
+    float pm[8], pz[8], pw[8];
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+      pm[g] = -INFINITY;
+      pz[g] = pw[g] = 0.0f;
+    }
+    for (int ch = tid; ch < a.nch_score; ch += FIT_THREADS) {
+      const float *e = a.ent + ((size_t)bh * a.nch_score + ch) * G * 3;
+#pragma unroll
+      for (int g = 0; g < 8; ++g)
+        if (g < G) ent_merge(pm[g], pz[g], pw[g], e[g * 3], e[g * 3 + 1], e[g * 3 + 2]);
+    }
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+      if (g >= G) break;
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) {
+        const float m2 = __shfl_xor(pm[g], off), z2 = __shfl_xor(pz[g], off), w2 = __shfl_xor(pw[g], off);
+        ent_merge(pm[g], pz[g], pw[g], m2, z2, w2);
+      }
+      if (lane == 0) {
+        s_piece[wave][g][0] = pm[g];
+        s_piece[wave][g][1] = pz[g];
+        s_piece[wave][g][2] = pw[g];
+      }
+    }
+  }
+  __syncthreads();
+  if (tid < G) {
+    float m = s_piece[0][tid][0], z = s_piece[0][tid][1], w = s_piece[0][tid][2];
+    for (int wv = 1; wv < FIT_NW; ++wv) ent_merge(m, z, w, s_piece[wv][tid][0], s_piece[wv][tid][1], s_piece[wv][tid][2]);
+    const double hbits = z > 0.0f ? log2((double)z) - (double)w / (double)z : 0.0;
+    s_acc[0][tid] = hbits * 0.69314718055994530942;  // nats
+  }
+  float mx = -INFINITY;
+  for (int i = tid; i < a.nch_score; i += FIT_THREADS) mx = fmaxf(mx, a.cmax[(size_t)bh * a.nch_score + i]);
+  mx = wave_max(mx);
+  if (lane == 0) s_acc[1][wave] = (double)mx;
+  __syncthreads();
+  if (tid == 0) {
+    double h = 0.0;
+    for (int g = 0; g < G; ++g) h += s_acc[0][g];
+    s_h = h / (double)G;
+    float m = -INFINITY;
+    for (int w = 0; w < FIT_NW; ++w) m = fmaxf(m, (float)s_acc[1][w]);
+    s_m = m;
+    s_lo = -12.0;
+    s_hi = 12.0;
+  }
+  __syncthreads();
+  const double H = s_h;
+  const float m = s_m;
+  const size_t rowbase = (size_t)bh * P * BK;
+  const double rsd = 1.0 / sqrt((double)HD);
+
+  for (int round = 0; round < FIT_ROUNDS && N > 0; ++round) {
+    const double lo = s_lo, hi = s_hi, step = (hi - lo) / 16.0;
+    // per candidate: the base-2 slope log2(e) / (sqrt(D) tau_k); each thread sums its few
+    // rows in fp32, the workgroup in fp64.  x2 = (s - m) * slope is the logit in bits, so
+    // the entropy in nats is ln Z - ln 2 * A / Z with Z = sum 2^x2, A = sum 2^x2 x2.
+    if (tid < FIT_POINTS) s_ck[tid] = (float)(rsd * 1.4426950408889634074 / exp2(lo + tid * step));
+    __syncthreads();
+    float ck[FIT_POINTS], cz[FIT_POINTS], ca[FIT_POINTS];
+#pragma unroll
+    for (int k = 0; k < FIT_POINTS; ++k) {
+      cz[k] = ca[k] = 0.0f;
+      ck[k] = s_ck[k];
+    }
+    for (int64_t i = tid; i < N; i += FIT_THREADS) {
+      const int64_t p = c + i;
+      const float x0 = a.scores[rowbase + (size_t)((p / BK) % P) * BK + (size_t)(p % BK)] - m;
+#pragma unroll
+      for (int k = 0; k < FIT_POINTS; ++k) {
+        const float x2 = x0 * ck[k];
+        const float e = exp2_fast(x2);
+        cz[k] += e;
+        ca[k] = __builtin_fmaf(e, x2, ca[k]);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < FIT_POINTS; ++k) {
+      double z = (double)cz[k], w = (double)ca[k];
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) {
+        z += shfl_xor_d(z, off);
+        w += shfl_xor_d(w, off);
+      }
+      if (lane == 0) {
+        s_acc[wave][k] = z;
+        s_acc[wave][FIT_POINTS + k] = w;
+      }
+    }
+    __syncthreads();
+    if (tid < FIT_POINTS) {  // does the entropy at tau_k reach the target?
+      double Z = 0.0, A = 0.0;
+      for (int w = 0; w < FIT_NW; ++w) {
+        Z += s_acc[w][tid];
+        A += s_acc[w][FIT_POINTS + tid];
+      }
+      s_reach[tid] = log(Z) - 0.69314718055994530942 * A / Z >= H;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      int kk = 0;
+      while (kk < FIT_POINTS && !s_reach[kk]) ++kk;
+      if (kk == 0) {
+        s_hi = lo;
+      } else if (kk >= FIT_POINTS) {
+        s_lo = hi;
+      } else {
+        s_lo = lo + (kk - 1) * step;
+        s_hi = lo + kk * step;
+      }
+    }
+    __syncthreads();
+  }
+  if (tid == 0) {
+    const float tau = N > 0 ? (float)exp2(0.5 * (s_lo + s_hi)) : 1.0f;
+    HeadInfo *hd = a.head + bh;
+    hd->tau = tau;
+    hd->kappa = (float)(1.4426950408889634074 / (sqrt((double)HD) * (double)tau));
+    if (a.tau_fit) a.tau_fit[bh] = tau;
+  }
+}
+
+template <typename T, bool ENT>
+hipError_t launch_score_ge(const Args &a, hipStream_t s) {
   dim3 grid(a.nch_score, a.nbh);
   switch (a.G) {
-    case 1: hipLaunchKernelGGL((hardkv_score<T, 1>), grid, dim3(NTHREADS), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((hardkv_score<T, 2>), grid, dim3(NTHREADS), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((hardkv_score<T, 4>), grid, dim3(NTHREADS), 0, s, a); break;
-    case 8: hipLaunchKernelGGL((hardkv_score<T, 8>), grid, dim3(NTHREADS), 0, s, a); break;
+    case 1: hipLaunchKernelGGL((hardkv_score<T, 1, ENT>), grid, dim3(NTHREADS), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((hardkv_score<T, 2, ENT>), grid, dim3(NTHREADS), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((hardkv_score<T, 4, ENT>), grid, dim3(NTHREADS), 0, s, a); break;
+    case 8: hipLaunchKernelGGL((hardkv_score<T, 8, ENT>), grid, dim3(NTHREADS), 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_score_g(const Args &a, hipStream_t s) {
+  return a.calibration ? launch_score_ge<T, true>(a, s) : launch_score_ge<T, false>(a, s);
 }
 
 }  // namespace
 
 hipError_t launch_score(const Args &a, hipStream_t s, bool bf16) {
   return bf16 ? launch_score_g<BF16>(a, s) : launch_score_g<F32>(a, s);
+}
+
+hipError_t launch_fit(const Args &a, hipStream_t s) {
+  hipLaunchKernelGGL(hardkv_fit, dim3(a.nbh), dim3(FIT_THREADS), 0, s, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_flatten(const Args &a, hipStream_t s) {

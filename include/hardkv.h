@@ -107,6 +107,17 @@ typedef enum { HARDKV_REG_REWRITE = 0, HARDKV_REG_SPARSE = 1, HARDKV_REG_MTI = 2
  *           written and set HARDKV_ERR_VIEW_OVERFLOW.  A head's view only lives until the
  *           next select (the offsets move with every step's budgets). */
 typedef enum { HARDKV_VIEW_MAXLEN = 0, HARDKV_VIEW_SUM = 1 } hardkv_view_layout;
+/* Logits Calibration temperature (section 2.B calibrates the scores by the temperature of
+ * the attention scores without fixing how it is obtained):
+ *   FIXED    tau_h from hardkv_config.tau (default);
+ *   ENTROPY  tau fitted per (b, h) and step: the calibrated softmax of the max-pooled scores,
+ *            softmax(s / (sqrt(D) tau)) over the pool, gets the mean entropy (in nats) of
+ *            the group's raw attention softmax(q_g . k / sqrt(D)) over the pool.  tau is
+ *            the midpoint of the bracket found by five rounds of a 17-point grid on
+ *            log2 tau in [-12, 12] (entropy grows with tau), rounded to fp32; kappa then
+ *            follows from it as for a fixed tau.  Written to hardkv_state.tau_fit. */
+typedef enum { HARDKV_CAL_FIXED = 0, HARDKV_CAL_ENTROPY = 1 } hardkv_calibration;
+
 /* (The fused step's attention reads the kept rows themselves, so it does not depend on
  * whether their view rows fit; hardkv_attend reads the views and sees only rows that fit.) */
 
@@ -138,6 +149,7 @@ typedef struct {
   int32_t mti_upper;       /* L_upper, tokens, >= mti_lower (policy MTI) */
   int32_t view_layout;     /* hardkv_view_layout (0: MAXLEN) */
   int32_t view_total;      /* rows of the packed views (layout SUM), >= 0 */
+  int32_t calibration;     /* hardkv_calibration (0: FIXED) */
 } hardkv_config;
 
 /* Device buffers of one layer.  All fixed capacity; 16-byte aligned.
@@ -166,6 +178,8 @@ typedef struct {
                                 (may be NULL: not reported)                                       */
   int32_t *view_off;         /* [B*Hkv + 1]: CSR row offsets of the SUM layout, the last one the
                                 total (written by select; may be NULL in the MAXLEN layout)       */
+  float *tau_fit;            /* [B][Hkv]: the fitted temperature (calibration ENTROPY; may be NULL
+                                otherwise)                                                        */
   uint32_t *error_word;      /* [1]: HARDKV_ERR_* bits, or-ed                                     */
   void *workspace;           /* hardkv_workspace_size() bytes, zero-filled before first use      */
   size_t workspace_bytes;

@@ -106,6 +106,68 @@ float orc_kappa(int32_t D, float tau) {
   return (float)(ORC_LOG2E / (sqrt((double)D) * (double)tau));
 }
 
+/* ------------------------------------------------------------------------------------
+ * Calibration temperature fitted by entropy (section 2.B says the scores are calibrated
+ * by the temperature of the attention scores; one reading of "the temperature of the
+ * attention": the calibrated softmax of the max-pooled scores gets the mean entropy of
+ * the group's raw attention over the same tokens).  Entropy grows with the temperature,
+ * so a bracket search on log2 tau finds it: five rounds of a 17-point grid on [-12, 12].
+ * ---------------------------------------------------------------------------------- */
+double orc_calibrated_entropy(const float *s, int64_t n, int32_t D, double tau) {
+  if (n <= 0) return 0.0;
+  float m = s[0];
+  for (int64_t j = 1; j < n; ++j)
+    if (s[j] > m) m = s[j];
+  const double c = 1.0 / (sqrt((double)D) * tau);
+  double Z = 0.0, A = 0.0;
+  for (int64_t j = 0; j < n; ++j) {
+    double x = ((double)s[j] - (double)m) * c;
+    double e = exp(x);
+    Z += e;
+    A += e * x;
+  }
+  return log(Z) - A / Z;
+}
+
+static double raw_entropy(const float *d, int64_t n, int32_t D) {
+  const double r = 1.0 / sqrt((double)D);
+  double m = -INFINITY;
+  for (int64_t j = 0; j < n; ++j)
+    if ((double)d[j] * r > m) m = (double)d[j] * r;
+  double Z = 0.0, A = 0.0;
+  for (int64_t j = 0; j < n; ++j) {
+    double x = (double)d[j] * r - m;
+    double e = exp(x);
+    Z += e;
+    A += e * x;
+  }
+  return log(Z) - A / Z;
+}
+
+float orc_fit_tau(const float *d, int32_t G, const float *s, int64_t n, int32_t D, double *h_target) {
+  double H = 0.0;
+  for (int g = 0; g < G; ++g) H += raw_entropy(d + (int64_t)g * n, n, D);
+  H /= (double)G;
+  if (h_target) *h_target = H;
+  if (n <= 0) return 1.0f;
+  double lo = -12.0, hi = 12.0;
+  for (int round = 0; round < 5; ++round) {
+    const double step = (hi - lo) / 16.0;
+    int k = 0;
+    while (k <= 16 && orc_calibrated_entropy(s, n, D, exp2(lo + k * step)) < H) ++k;
+    if (k == 0) {
+      hi = lo;
+    } else if (k > 16) {
+      lo = hi;
+    } else {
+      const double a = lo + (k - 1) * step, b = lo + k * step;
+      lo = a;
+      hi = b;
+    }
+  }
+  return (float)exp2(0.5 * (lo + hi));
+}
+
 float orc_exp2_poly(float f) {
   float y = g_coeff[ORC_NCOEFF - 1];
   for (int i = ORC_NCOEFF - 2; i >= 0; --i) {
@@ -389,7 +451,28 @@ static uint32_t unit_step(const orc_cfg *cfg, orc_state *st, int b, int h, const
   }
 
   /* calibrate over the whole pool */
-  const float kappa = orc_kappa(D, cfg->tau[h]);
+  float tau_u = cfg->tau[h];
+  if (cfg->calibration == 1) {
+    if (cfg->tau_unit) {
+      tau_u = cfg->tau_unit[u];
+    } else {
+      /* every query's dot products over the pool, and the max-pooled scores in order */
+      const int64_t n = pend - c;
+      float *dd = (float *)malloc(sizeof(float) * (size_t)(G * (n > 0 ? n : 1)));
+      float *ss = (float *)malloc(sizeof(float) * (size_t)(n > 0 ? n : 1));
+      for (int64_t j = c; j < pend; ++j) {
+        int64_t r = pool_row(cfg, u, j);
+        for (int d = 0; d < D; ++d) krow[d] = elem_get(st->pool_k, r * D + d, eb);
+        for (int g = 0; g < G; ++g) dd[(int64_t)g * n + (j - c)] = orc_dot_pairwise(qg + (int64_t)g * D, krow, D);
+        ss[j - c] = st->scores[r];
+      }
+      tau_u = orc_fit_tau(dd, G, ss, n, D, NULL);
+      free(dd);
+      free(ss);
+    }
+    if (st->tau_fit) st->tau_fit[u] = tau_u;
+  }
+  const float kappa = orc_kappa(D, tau_u);
   uint64_t w_all = 0, w_u = 0;
   for (int64_t j = c; j < pend; ++j) {
     int64_t r = pool_row(cfg, u, j);

@@ -54,6 +54,8 @@ typedef struct {
   int32_t mti_lower, mti_upper;
   int32_t view_layout;       /* 0: every head owns view_cap rows; 1: packed in unit order (CSR) */
   int32_t view_total;        /* rows of the packed views (layout 1) */
+  int32_t calibration;       /* 0: tau from tau[h]; 1: tau fitted per unit by entropy matching */
+  const float *tau_unit;     /* [B*H] with calibration 1: use these instead of fitting (or NULL) */
 } orc_cfg;
 
 typedef struct {
@@ -69,6 +71,7 @@ typedef struct {
   uint64_t *w_all, *w_u, *thresh;
   int32_t *regularized;      /* [B*H] 1 if the head's view was rewritten this step (may be NULL) */
   int32_t *view_off;         /* [B*H + 1] row offsets of the packed views (layout 1) */
+  float *tau_fit;            /* [B*H] the temperature used (calibration 1; may be NULL) */
   uint32_t error_word;
 } orc_state;
 
@@ -90,6 +93,11 @@ int32_t orc_prefill(const orc_cfg *cfg, orc_state *st, const void *k_ctx, const 
                     const int64_t *ctx_len, int64_t max_len);
 int32_t orc_step(const orc_cfg *cfg, orc_state *st, const void *q, const void *k_new,
                  const void *v_new, double *out, int32_t do_attend, int32_t nthreads);
+/* entropy-matched temperature: d are the G x n raw dot products (query-major), s the n
+ * max-pooled scores; returns the fitted tau (fp32) and the target entropy in *h_target */
+float   orc_fit_tau(const float *d, int32_t G, const float *s, int64_t n, int32_t D, double *h_target);
+/* entropy (nats) of softmax(s / (sqrt(D) tau)) over n scores, binary64 */
+double  orc_calibrated_entropy(const float *s, int64_t n, int32_t D, double tau);
 /* full softmax attention over positions [0, t) of a flat cache, binary64 (pin I4) */
 void    orc_full_attention(const float *q, const float *k, const float *v, int32_t n,
                            int32_t D, double *out);

@@ -30,6 +30,7 @@ class OrcCfg(C.Structure):
         ("top_p", C.c_double), ("tau", C.POINTER(C.c_float)),
         ("regularize", C.c_int32), ("mti_lower", C.c_int32), ("mti_upper", C.c_int32),
         ("view_layout", C.c_int32), ("view_total", C.c_int32),
+        ("calibration", C.c_int32), ("tau_unit", C.POINTER(C.c_float)),
     ]
 
 
@@ -43,7 +44,7 @@ class OrcState(C.Structure):
         ("weights", C.c_void_p), ("mask", C.c_void_p), ("budget", C.c_void_p),
         ("n_condense", C.c_void_p), ("w_all", C.c_void_p), ("w_u", C.c_void_p),
         ("thresh", C.c_void_p), ("regularized", C.c_void_p), ("view_off", C.c_void_p),
-        ("error_word", C.c_uint32),
+        ("tau_fit", C.c_void_p), ("error_word", C.c_uint32),
     ]
 
 
@@ -61,6 +62,10 @@ def lib():
         L.orc_score_row.argtypes = [vp, i32, vp, i32]
         L.orc_kappa.restype = f
         L.orc_kappa.argtypes = [i32, f]
+        L.orc_fit_tau.restype = f
+        L.orc_fit_tau.argtypes = [vp, i32, vp, i64, i32, C.POINTER(d)]
+        L.orc_calibrated_entropy.restype = d
+        L.orc_calibrated_entropy.argtypes = [vp, i64, i32, d]
         L.orc_poly_coeff.restype = f
         L.orc_poly_coeff.argtypes = [i32]
         L.orc_exp2_poly.restype = f
@@ -143,6 +148,21 @@ def weight_of_t(t: np.ndarray) -> np.ndarray:
     return w
 
 
+def fit_tau(d: np.ndarray, s: np.ndarray, D: int = 128):
+    """Entropy-matched temperature: d are the [G, n] raw dot products, s the n max-pooled
+    scores; returns (tau, target entropy in nats)."""
+    d = np.ascontiguousarray(d, np.float32)
+    s = np.ascontiguousarray(s, np.float32)
+    h = C.c_double(0.0)
+    tau = lib().orc_fit_tau(_p(d), int(d.shape[0]), _p(s), int(s.shape[0]), D, C.byref(h))
+    return float(tau), float(h.value)
+
+
+def calibrated_entropy(s: np.ndarray, tau: float, D: int = 128) -> float:
+    s = np.ascontiguousarray(s, np.float32)
+    return float(lib().orc_calibrated_entropy(_p(s), int(s.shape[0]), D, float(tau)))
+
+
 def pq(p: float) -> int:
     return int(lib().orc_pq(p))
 
@@ -176,7 +196,8 @@ class Oracle:
 
     def __init__(self, wl, tau: Optional[np.ndarray] = None, merge_bias: bool = True,
                  top_p: Optional[float] = None, regularize: int = 0, mti_lower: int = 0,
-                 mti_upper: int = 0, view_layout: int = 0, view_total: int = 0):
+                 mti_upper: int = 0, view_layout: int = 0, view_total: int = 0,
+                 calibration: int = 0, tau_unit: Optional[np.ndarray] = None):
         self.wl = wl
         B, H, Hq, D = wl.batch, wl.num_kv_heads, wl.num_q_heads, wl.head_dim
         W, P, V, Cs = wl.dense_window, wl.P_blk, wl.V_cap, wl.condensed_slots
@@ -186,7 +207,12 @@ class Oracle:
         self.cfg = OrcCfg(B, Hq, H, D, wl.elem_bytes, W, P, wl.sparse_cap, V, Cs, wl.cond_mode,
                           1 if merge_bias else 0, float(wl.top_p if top_p is None else top_p),
                           self.tau.ctypes.data_as(C.POINTER(C.c_float)), int(regularize),
-                          int(mti_lower), int(mti_upper), int(view_layout), int(view_total))
+                          int(mti_lower), int(mti_upper), int(view_layout), int(view_total),
+                          int(calibration), None)
+        self.tau_unit = None
+        if tau_unit is not None:
+            self.tau_unit = np.ascontiguousarray(np.asarray(tau_unit, np.float32).ravel())
+            self.cfg.tau_unit = self.tau_unit.ctypes.data_as(C.POINTER(C.c_float))
         self.dense_k = np.zeros((B, H, W, D), st)
         self.dense_v = np.zeros((B, H, W, D), st)
         self.pool_k = np.zeros((B, H, P, BK, D), st)
@@ -201,6 +227,7 @@ class Oracle:
             self.view_v = np.zeros((B, H, V, D), st)
             self.view_pos = np.full((B, H, V), -1, np.int32)
         self.view_off = np.zeros(B * H + 1, np.int32)
+        self.tau_fit = np.zeros((B, H), np.float32)
         self.cond_kn = np.zeros((B, H, Cs, D), np.float64)
         self.cond_vn = np.zeros((B, H, Cs, D), np.float64)
         self.cond_omega = np.zeros((B, H, Cs), np.float64)
@@ -221,7 +248,7 @@ class Oracle:
             "dense_k", "dense_v", "pool_k", "pool_v", "view_k", "view_v", "view_pos", "cond_kn",
             "cond_vn", "cond_omega", "cond_n", "cond_cursor", "seq_len", "pool_head", "scores",
             "weights", "mask", "budget", "n_condense", "w_all", "w_u", "thresh", "regularized",
-            "view_off")], 0)
+            "view_off", "tau_fit")], 0)
 
     @property
     def error_word(self) -> int:

@@ -62,6 +62,9 @@ def _cfg(**over):
     (dict(num_kv_heads=65, num_q_heads=65), hk.HARDKV_EUNSUPPORTED),
     (dict(dense_window=0), hk.HARDKV_EINVAL),
     (dict(regularize=3), hk.HARDKV_EINVAL),
+    (dict(view_layout=2), hk.HARDKV_EINVAL),
+    (dict(view_layout=1, view_total=-1), hk.HARDKV_EINVAL),
+    (dict(calibration=2), hk.HARDKV_EINVAL),
     (dict(regularize=hk.HARDKV_REG_MTI, mti_lower=-1, mti_upper=5), hk.HARDKV_EINVAL),
     (dict(regularize=hk.HARDKV_REG_MTI, mti_lower=10, mti_upper=5), hk.HARDKV_EINVAL),
 ])

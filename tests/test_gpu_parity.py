@@ -287,3 +287,64 @@ def test_packed_views_overflow_sets_the_bit():
     pr = Pair(wl, view_layout=1, view_total=total)
     pr.step(fused=True)
     assert int(pr.st.error_word[0].item()) & 2
+
+
+# ---- calibration temperature fitted by entropy --------------------------------------------
+TAU_TOL = 2e-4
+
+ENTROPY_CASES = {
+    "evict_bf16": dict(),
+    "merge_f32": dict(dtype="f32", cond_mode=COND_MERGE),
+    "g1": dict(num_q_heads=2, num_kv_heads=2),
+    "g8_batch8": dict(batch=8, num_q_heads=16, num_kv_heads=2, cond_mode=COND_MERGE, ctx_len=500, ctx_min=100),
+    "heavy": dict(heavy=(0, 8), cond_mode=COND_MERGE),
+}
+
+
+@pytest.mark.parametrize("name", list(ENTROPY_CASES))
+@pytest.mark.parametrize("fused", [True, False])
+def test_entropy_calibration_parity(name, fused):
+    """The fitted temperature agrees with the oracle's fit to 2e-4 (or, where a few dominant
+    tokens make the calibrated entropy flat in tau, gives the same entropy to 1e-5), and
+    with the GPU's temperatures given to it per unit the oracle reproduces weights, masks,
+    budgets and views bit for bit and the attention within 2e-3."""
+    from decode_kv_cache_02_amd import hardkv as hk
+    from oracle import hardkv_oracle as orc
+    from parity import Pair
+    from synth import make_inputs
+    wl = tiny_workload(steps=1, **ENTROPY_CASES[name])
+    inp = make_inputs(wl, device="cuda")
+    cpu = inp.to("cpu")
+    o_fit = orc.Oracle(wl, calibration=1)
+    assert o_fit.prefill(cpu.k_ctx, cpu.v_ctx, cpu.ctx_len) == 0
+    o_fit.step(cpu.q[0], cpu.k_new[0], cpu.v_new[0], attend=False)
+    # the GPU step
+    pr = Pair(wl, inputs=inp)
+    pr.cfg = hk.Config.from_workload(wl, calibration=hk.HARDKV_CAL_ENTROPY)
+    pr.st = hk.State(pr.cfg)
+    hk.hardkv_prefill(pr.cfg, pr.st, inp.k_ctx, inp.v_ctx, inp.ctx_len)
+    pr.gpu_step(fused)
+    torch.cuda.synchronize()
+    tau_gpu = pr.st.tau_fit.cpu().numpy()
+    rel = np.abs(tau_gpu / o_fit.tau_fit - 1.0)
+    print(f"case {name}: tau gpu {tau_gpu.ravel()} oracle {o_fit.tau_fit.ravel()} max rel {rel.max():.2e}", flush=True)
+    for b in range(wl.batch):
+        for h in range(wl.num_kv_heads):
+            if rel[b, h] <= TAU_TOL:
+                continue
+            # a nearly flat entropy curve (a few dominant tokens) leaves tau loose: then both
+            # temperatures must give the oracle's entropy of this head's scores alike
+            t = int(o_fit.seq_len[b])
+            c0 = int(o_fit.pool_head[b, h]) - 64 * int(o_fit.n_condense[b, h])
+            pos = np.arange(c0, max(0, t - wl.dense_window))
+            sc = o_fit.scores[b, h][(pos // 64) % wl.P_blk * 64 + pos % 64]
+            dh = abs(orc.calibrated_entropy(sc, float(tau_gpu[b, h])) -
+                     orc.calibrated_entropy(sc, float(o_fit.tau_fit[b, h])))
+            assert dh <= 1e-5, (b, h, tau_gpu[b, h], o_fit.tau_fit[b, h], dh)
+    # the oracle with the GPU's temperatures
+    o = orc.Oracle(wl, calibration=1, tau_unit=tau_gpu)
+    assert o.prefill(cpu.k_ctx, cpu.v_ctx, cpu.ctx_len) == 0
+    pr.orcs = {None: (o, cpu)}
+    pre = {None: o.pool_head.copy()}
+    outs = pr.oracle_step()
+    pr.compare(pre, outs)

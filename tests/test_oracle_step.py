@@ -312,3 +312,60 @@ def test_packed_views_overflow():
     flat = np.concatenate([o_max.view_pos[b, h, :o_max.budget[b, h]]
                            for b in range(wl.batch) for h in range(wl.num_kv_heads)])
     np.testing.assert_array_equal(o.view_pos, flat[:need - 5])
+
+
+# ---- calibration temperature fitted by entropy ------------------------------------------
+_GRID_LOG2 = 24.0 / 16 ** 5   # width of the last bracket of the search, in log2 tau
+
+
+def _dots(q, k):
+    """Pairwise-tree dots of every query with every key, as the score computes them."""
+    return np.array([[orc.dot_pairwise(qg, kr) for kr in k] for qg in q], np.float32)
+
+
+@pytest.mark.parametrize("G", [1, 4])
+def test_fit_tau_identical_queries_gives_one(G):
+    """With every query of the group equal (G = 1 is the plain case), the max-pooled score
+    is the raw dot, so the calibrated softmax at tau = 1 is the raw attention and has its
+    entropy: the fitted tau is 1 to within the last bracket of the search."""
+    rng = np.random.default_rng(11)
+    q1 = rng.standard_normal(128).astype(np.float32)
+    k = rng.standard_normal((300, 128)).astype(np.float32)
+    d = _dots(np.repeat(q1[None], G, 0), k)
+    s = d.max(0)
+    tau, h = orc.fit_tau(d, s)
+    assert abs(np.log2(tau)) <= _GRID_LOG2 + 1e-12, tau
+    assert abs(orc.calibrated_entropy(s, 1.0) - h) < 1e-12
+
+
+def test_fit_tau_matches_target_entropy():
+    """For a real group (different queries) the fitted tau reproduces the target entropy up
+    to the slope of the entropy over the last bracket, and sharper calibrated softmaxes
+    (smaller tau) have lower entropy."""
+    rng = np.random.default_rng(12)
+    q = rng.standard_normal((4, 128)).astype(np.float32) * np.array([[0.5], [1.0], [2.0], [3.0]], np.float32)
+    k = rng.standard_normal((500, 128)).astype(np.float32)
+    d = _dots(q, k)
+    s = d.max(0)
+    tau, h = orc.fit_tau(d, s)
+    lo, hi = tau * 2 ** -_GRID_LOG2, tau * 2 ** _GRID_LOG2
+    e_lo, e_hi = orc.calibrated_entropy(s, lo), orc.calibrated_entropy(s, hi)
+    assert e_lo - 1e-9 <= h <= e_hi + 1e-9, (e_lo, h, e_hi)
+    ts = [0.1, 0.3, 1.0, 3.0]
+    es = [orc.calibrated_entropy(s, t) for t in ts]
+    assert all(a < b for a, b in zip(es, es[1:])), es
+
+
+def test_entropy_calibration_step_uses_the_fitted_tau():
+    """The step with the fitted temperature equals the step with that temperature given per
+    unit (the override the GPU parity uses), and reports the temperature it used."""
+    wl = tiny_workload(cond_mode=COND_MERGE, steps=1, ctx_len=500, ctx_min=100)
+    inp = make_inputs(wl)
+    o_fit, outs_fit = _run(wl, inp, 1, calibration=1)
+    taus = o_fit.tau_fit.copy()
+    assert np.all(taus > 0) and np.all(np.isfinite(taus))
+    o_ovr, outs_ovr = _run(wl, inp, 1, calibration=1, tau_unit=taus)
+    for n in ("weights", "mask", "budget", "thresh"):
+        assert np.array_equal(getattr(o_fit, n), getattr(o_ovr, n)), n
+    assert np.array_equal(outs_fit[0], outs_ovr[0])
+    np.testing.assert_array_equal(o_ovr.tau_fit, taus)

@@ -240,7 +240,7 @@ HK_DEV uint64_t wave_sum_u64(uint64_t v) {
 }
 
 constexpr int NW = SEL_THREADS / 64;  // wavefronts of the select workgroup
-constexpr int UA = 8;                  // 16-byte loads in flight per lane in the pool passes
+constexpr int UA = 4;                  // 16-byte loads in flight per lane in the pool passes
 
 // A candidate of the cut bucket b1 packs its survivor block j and the low 16 bits of its
 // key: (j << 16) | (key & 0xffff); its key is (b1 << 16) | (cand & 0xffff).
@@ -356,7 +356,12 @@ __global__ __launch_bounds__(SEL_THREADS) void hardkv_select(Args a) {
   const int nx = (int)E;                                   // condensing blocks come first
   const int nub = nblk - nx;                               // survivor blocks
   const int pb_lo = (int)((c / BK) % P);
-  const float kap = a.calibration ? hd->kappa : a.kappa[h];
+  // both slopes loaded, then a select of values: a select between the argument block and
+  // a global address (which the compiler forms from a plain load under a branch) copies
+  // the whole argument block to scratch
+  const float kfix = a.kappa[h];
+  const float kfit = __builtin_nontemporal_load(&hd->kappa);
+  const float kap = a.calibration ? kfit : kfix;
   const size_t rowbase = (size_t)bh * P * BK;
   auto ring = [&](int i) {
     int pb = pb_lo + i;

@@ -75,7 +75,7 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_score(Args a) {
   const int sub = lane & 15, grp = lane >> 4;
   const int P = a.P;
 
-  __shared__ float s_stage[4][16];
+  __shared__ float s_sc[8 * BK];  // the chunk's scores (at most 8 blocks), stored at the end
   __shared__ float s_wmax[4];
   __shared__ float s_ent[ENT ? 4 : 1][G][3];
   // entropy calibration: lane `sub` < G keeps query sub's softmax piece over its rows
@@ -140,20 +140,11 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_score(Args a) {
           }
           if (ENT && sub < G && gi * 16 + l * 4 + grp < nrows) ent_merge(em, ez, ew, dmine * c2, 1.0f, 0.0f);
           s = s + 0.0f;  // a zero score is +0
-          if (sub == 0) s_stage[wave][l * 4 + grp] = s;
+          // s is needed in every lane here, so that the last tree level stays one DPP add
+          // rather than a move plus an add sunk into the store's branch
+          asm volatile("" : "+v"(s));
+          if (sub == 0) s_sc[gi * 16 + l * 4 + grp] = s;
         }
-        wave_sync();
-        if (lane < 16) {
-          const int rel = gi * 16 + lane;
-          if (rel < nrows) {
-            int pb = pb0 + (gi >> 2);
-            pb = pb >= P ? pb - P : pb;
-            const float s = s_stage[wave][lane];
-            srow[pb * BK + (rel & (BK - 1))] = s;
-            wmax = s > wmax ? s : wmax;
-          }
-        }
-        wave_sync();
       }
     };
     constexpr int STEP = 4 * UNR;
@@ -168,6 +159,15 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_score(Args a) {
       if (g0 + STEP < ngroups) issue(bufA, g0 + STEP);
       score(bufB, g0);
       g0 += STEP;
+    }
+    // the chunk's scores leave in one pass: wavefront w writes blocks w, w + 4, ...
+    __syncthreads();
+    for (int rel = tid; rel < nrows; rel += NTHREADS) {
+      int pb = pb0 + (rel >> 6);
+      pb = pb >= P ? pb - P : pb;
+      const float s = s_sc[rel];
+      srow[pb * BK + (rel & (BK - 1))] = s;
+      wmax = s > wmax ? s : wmax;
     }
   }
   wmax = wave_max(wmax);

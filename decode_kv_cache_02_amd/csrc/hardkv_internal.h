@@ -176,6 +176,39 @@ HK_DEV void raw_store(void *p, const Raw8<F32> &r) {
   reinterpret_cast<float4 *>(p)[0] = r.a;
   reinterpret_cast<float4 *>(p)[1] = r.b;
 }
+// Raw buffer resources (stride 0, byte offsets).  The hardware drops an access whose
+// offset lies outside the resource's range: a load returns zeros, a store writes
+// nothing.  Rows a lane must skip get the offset BUF_SKIP, outside every range made
+// here, instead of a branch around the access: with no branches the compiler can count
+// the accesses in flight and waits only for those whose data it needs next.
+typedef __amdgpu_buffer_rsrc_t BufRes;
+constexpr uint32_t BUF_SKIP = 0x80000000u;
+constexpr uint64_t BUF_MAX_BYTES = 0x7FFFFFF0u;  // every range stays below BUF_SKIP
+constexpr int BUF_NT = 2;                       // cache policy bits: non-temporal
+HK_DEV BufRes make_buf(const void *base, uint64_t bytes) {
+  const uint32_t n = (uint32_t)(bytes < BUF_MAX_BYTES ? bytes : BUF_MAX_BYTES);
+  // word 3 of a gfx9-family raw buffer: 32-bit data format, no swizzle or index stride
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)n, 0x00020000);
+}
+static_assert((uint64_t)MAX_POOL_BLOCKS * 64 * 128 * 4 <= BUF_MAX_BYTES, "a head's pool rows fit one buffer range");
+HK_DEV uint4 buf_load16_nt(BufRes r, uint32_t off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, BUF_NT));
+}
+HK_DEV void buf_store16_nt(BufRes r, uint32_t off, uint4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u32, v), r, off, 0, BUF_NT);
+}
+// a lane's 8 elements of a row at byte offset off (BUF_SKIP: zeros / nothing written)
+HK_DEV void buf_load_nt(BufRes r, uint32_t off, Raw8<BF16> &x) { x.v = buf_load16_nt(r, off); }
+HK_DEV void buf_load_nt(BufRes r, uint32_t off, Raw8<F32> &x) {
+  x.a = __builtin_bit_cast(float4, buf_load16_nt(r, off));
+  x.b = __builtin_bit_cast(float4, buf_load16_nt(r, off + 16));
+}
+HK_DEV void buf_store_nt(BufRes r, uint32_t off, const Raw8<BF16> &x) { buf_store16_nt(r, off, x.v); }
+HK_DEV void buf_store_nt(BufRes r, uint32_t off, const Raw8<F32> &x) {
+  buf_store16_nt(r, off, __builtin_bit_cast(uint4, x.a));
+  buf_store16_nt(r, off + 16, __builtin_bit_cast(uint4, x.b));
+}
+
 HK_DEV void raw_to_f(const Raw8<BF16> &r, float (&f)[8]) {
   f[0] = bf_lo(r.v.x); f[1] = bf_hi(r.v.x); f[2] = bf_lo(r.v.y); f[3] = bf_hi(r.v.y);
   f[4] = bf_lo(r.v.z); f[5] = bf_hi(r.v.z); f[6] = bf_lo(r.v.w); f[7] = bf_hi(r.v.w);

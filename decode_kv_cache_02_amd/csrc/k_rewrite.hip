@@ -90,14 +90,17 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_rewrite(Args a) {
     load_q_scaled<T, G>(a, b, h, sub, qs);
   }
   const size_t rowbase = (size_t)bh * P * BK;
-  const char *pk = (const char *)a.pool_k + rowbase * ROWB + sub * 8 * EB;
-  const char *pv = (const char *)a.pool_v + rowbase * ROWB + sub * 8 * EB;
-  // the head's view rows start at voff (bh * V_cap, or its packed offset); vcap rows fit
+  const uint64_t poolb = (uint64_t)P * BK * ROWB;
+  const BufRes pk = make_buf((const char *)a.pool_k + rowbase * ROWB, poolb);
+  const BufRes pv = make_buf((const char *)a.pool_v + rowbase * ROWB, poolb);
+  // the head's view rows start at voff (bh * V_cap, or its packed offset); vcap rows fit,
+  // and the view buffers end there, so a row past them is not written
   const int64_t voff = hd->voff;
   const uint32_t vcap = a.view_sum ? (uint32_t)max((int64_t)0, min(a.view_rows - voff, (int64_t)UINT32_MAX))
                                    : (uint32_t)V;
-  char *vk = (char *)a.view_k + (size_t)voff * ROWB + sub * 8 * EB;
-  char *vv = (char *)a.view_v + (size_t)voff * ROWB + sub * 8 * EB;
+  const BufRes vk = make_buf((const char *)a.view_k + (size_t)voff * ROWB, (uint64_t)vcap * ROWB);
+  const BufRes vv = make_buf((const char *)a.view_v + (size_t)voff * ROWB, (uint64_t)vcap * ROWB);
+  const uint32_t lane_b = (uint32_t)(sub * 8 * EB);  // the lane's 8 elements of a row
   int32_t *vpos = a.view_pos + voff;
 
   // the wavefront's blocks: weights and block info of all of them in flight at once
@@ -137,33 +140,28 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_rewrite(Args a) {
   }
   if (COPY) {
     wave_sync();
-    // kept rows copied 16 at a time (4 per 16-lane group), attended while in registers
+    // kept rows copied 16 at a time (4 per 16-lane group), attended while in registers;
+    // rows past the list read zeros and write nothing (offset BUF_SKIP), rows past the
+    // view's capacity are still attended but fall outside the view buffers
     for (int it = 0; it < ns; it += 16) {
       Raw8<T> kr[4], vr[4];
       bool act[4];
-      uint32_t dst[4];
+      uint32_t doff[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int k = it + j * 4 + grp;
         const int kk = k < ns ? k : 0;
-        const uint32_t src = s_src[wave][kk];
-        dst[j] = s_dst[wave][kk];
-        act[j] = k < ns;  // attended whether or not its view row fits
-        if (act[j]) {
-          raw_load_nt(pk + (size_t)src * ROWB, kr[j]);
-          raw_load_nt(pv + (size_t)src * ROWB, vr[j]);
-        } else {
-          kr[j] = Raw8<T>{};
-          vr[j] = Raw8<T>{};
-        }
+        act[j] = k < ns;
+        const uint32_t soff = act[j] ? s_src[wave][kk] * (uint32_t)ROWB + lane_b : BUF_SKIP;
+        doff[j] = act[j] ? s_dst[wave][kk] * (uint32_t)ROWB + lane_b : BUF_SKIP;
+        buf_load_nt(pk, soff, kr[j]);
+        buf_load_nt(pv, soff, vr[j]);
       }
       if (store) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          if (act[j] && dst[j] < vcap) {
-            raw_store_nt(vk + (size_t)dst[j] * ROWB, kr[j]);
-            raw_store_nt(vv + (size_t)dst[j] * ROWB, vr[j]);
-          }
+          buf_store_nt(vk, doff[j], kr[j]);
+          buf_store_nt(vv, doff[j], vr[j]);
         }
       }
       if (ATTN) attn_rows<T, G, 4>(st, qs, kr, vr, act);

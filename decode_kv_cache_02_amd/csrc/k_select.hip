@@ -71,7 +71,9 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_score(Args a) {
   const int lin = xcd_swizzle(blockIdx.y * gridDim.x + blockIdx.x, gridDim.x * gridDim.y);
   const int bh = a.bh0 + lin / gridDim.x, chunk = lin % gridDim.x;
   const int b = bh / a.Hkv, h = bh - b * a.Hkv;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // the wavefront index is uniform (readfirstlane tells the compiler so: its batch loop
+  // then runs on scalar branches)
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int sub = lane & 15, grp = lane >> 4;
   const int P = a.P;
 
@@ -94,7 +96,8 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_score(Args a) {
     const char *qb = (const char *)a.q + (((int64_t)b * a.Hq + (int64_t)h * G) * HD + sub * 8) * EB;
 #pragma unroll
     for (int g = 0; g < G; ++g) load8(qb + (size_t)g * HD * EB, qf[g], T{});
-    const char *kbase = (const char *)a.pool_k + (size_t)bh * P * BK * HD * EB + sub * 8 * EB;
+    const BufRes kb = make_buf((const char *)a.pool_k + (size_t)bh * P * BK * HD * EB, (uint64_t)P * BK * HD * EB);
+    const uint32_t lane_b = (uint32_t)(sub * 8 * EB);  // the lane's 8 elements of a row
     float *srow = a.scores + (size_t)bh * P * BK;
     // row_lo is block aligned and the chunk spans fewer than P blocks, so one
     // subtraction wraps the ring index
@@ -113,19 +116,17 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_score(Args a) {
 #pragma unroll
         for (int l = 0; l < 4; ++l) {
           const int rel = gi * 16 + l * 4 + grp;
-          if (gi < ngroups && rel < nrows) {
-            raw_load_nt(kbase + (size_t)(pb * BK + (rel & (BK - 1))) * (HD * EB), buf[u][l]);
-          } else {
-            buf[u][l] = Raw8<T>{};
-          }
+          // rows past the chunk read zeros (offset BUF_SKIP), with no branch
+          const uint32_t row_b = (uint32_t)(pb * BK + (rel & (BK - 1))) * (uint32_t)(HD * EB) + lane_b;
+          const uint32_t off = (gi < ngroups) & (rel < nrows) ? row_b : BUF_SKIP;
+          buf_load_nt(kb, off, buf[u][l]);
         }
       }
     };
     auto score = [&](const Raw8<T> (&buf)[UNR][4], int g0) {
 #pragma unroll
       for (int u = 0; u < UNR; ++u) {
-        const int gi = g0 + 4 * u;
-        if (gi >= ngroups) break;  // wave-uniform
+        const int gi = g0 + 4 * u;  // rows past the chunk are zeros, scored but not kept
 #pragma unroll
         for (int l = 0; l < 4; ++l) {
           float kf[8];
@@ -138,28 +139,33 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_score(Args a) {
             if (ENT && g == sub) dmine = d;
             s = d > s ? d : s;
           }
-          if (ENT && sub < G && gi * 16 + l * 4 + grp < nrows) ent_merge(em, ez, ew, dmine * c2, 1.0f, 0.0f);
+          const int rel = gi * 16 + l * 4 + grp;
+          if (ENT && sub < G && rel < nrows) ent_merge(em, ez, ew, dmine * c2, 1.0f, 0.0f);
           s = s + 0.0f;  // a zero score is +0
           // s is needed in every lane here, so that the last tree level stays one DPP add
           // rather than a move plus an add sunk into the store's branch
           asm volatile("" : "+v"(s));
-          if (sub == 0) s_sc[gi * 16 + l * 4 + grp] = s;
+          if (sub == 0 && rel < nrows) s_sc[rel] = s;
         }
       }
     };
     constexpr int STEP = 4 * UNR;
+    // The wavefront's nb batches, two per trip with no exit inside the trip, and issues
+    // that are unconditional (a batch past the chunk reads nothing): every path into the
+    // loop head then has the same loads in flight, so the wait before scoring a batch
+    // counts only that batch's loads.
     Raw8<T> bufA[UNR][4], bufB[UNR][4];
+    const int nb = wave < ngroups ? (ngroups - 1 - wave) / STEP + 1 : 0;
     int g0 = wave;
-    if (g0 < ngroups) issue(bufA, g0);
-    while (g0 < ngroups) {
-      if (g0 + STEP < ngroups) issue(bufB, g0 + STEP);
+    issue(bufA, g0);
+    for (int i = 0; i + 2 <= nb; i += 2) {
+      issue(bufB, g0 + STEP);
       score(bufA, g0);
-      g0 += STEP;
-      if (g0 >= ngroups) break;
-      if (g0 + STEP < ngroups) issue(bufA, g0 + STEP);
-      score(bufB, g0);
-      g0 += STEP;
+      issue(bufA, g0 + 2 * STEP);
+      score(bufB, g0 + STEP);
+      g0 += 2 * STEP;
     }
+    if (nb & 1) score(bufA, g0);
     // the chunk's scores leave in one pass: wavefront w writes blocks w, w + 4, ...
     __syncthreads();
     for (int rel = tid; rel < nrows; rel += NTHREADS) {

@@ -55,12 +55,13 @@ HK_DEV void attn_row(AttnState<G> &st, const float (&qs)[G][8], const float (&k)
 
 HK_DEV float merge_factor(float m, float mn) { return (m == -INFINITY) ? 0.0f : exp2_fast(m - mn); }
 
-// NR rows per 16-lane group at once (one from each load of a batch): their logits, one
-// rescale of the accumulators to the new running maximum, then the NR value rows.
+// NR rows per 16-lane group at once (one from each load of a batch), in two phases so
+// that a caller can release the key registers before the values are needed:
+// attn_keys forms the NR logits, rescales the accumulators once to the new running
+// maximum and leaves the rows' probabilities in p; attn_values adds the NR value rows.
 template <typename T, int G, int NR>
-HK_DEV void attn_rows(AttnState<G> &st, const float (&qs)[G][8], const Raw8<T> (&kr)[NR],
-                      const Raw8<T> (&vr)[NR], const bool (&act)[NR]) {
-  float lg[G][NR];
+HK_DEV void attn_keys(AttnState<G> &st, const float (&qs)[G][8], const Raw8<T> (&kr)[NR],
+                      const bool (&act)[NR], float (&p)[G][NR]) {
 #pragma unroll
   for (int j = 0; j < NR; ++j) {
     float kf[8];
@@ -74,27 +75,32 @@ HK_DEV void attn_rows(AttnState<G> &st, const float (&qs)[G][8], const Raw8<T> (
       d += dpp<DPP_XOR2>(d);
       d += dpp<DPP_HALF_MIRROR>(d);
       d += dpp<DPP_MIRROR>(d);
-      lg[g][j] = act[j] ? d : -INFINITY;
+      p[g][j] = act[j] ? d : -INFINITY;
     }
   }
 #pragma unroll
   for (int g = 0; g < G; ++g) {
-    float mx = lg[g][0];
+    float mx = p[g][0];
 #pragma unroll
-    for (int j = 1; j < NR; ++j) mx = fmaxf(mx, lg[g][j]);
+    for (int j = 1; j < NR; ++j) mx = fmaxf(mx, p[g][j]);
     const float mn = fmaxf(st.m[g], mx);
     const float sc = (st.m[g] == mn) ? 1.0f : exp2_fast(st.m[g] - mn);
     float ps = 0.0f;
 #pragma unroll
     for (int j = 0; j < NR; ++j) {
-      lg[g][j] = act[j] ? exp2_fast(lg[g][j] - mn) : 0.0f;
-      ps += lg[g][j];
+      p[g][j] = act[j] ? exp2_fast(p[g][j] - mn) : 0.0f;
+      ps += p[g][j];
     }
     st.l[g] = __builtin_fmaf(st.l[g], sc, ps);
 #pragma unroll
     for (int i = 0; i < 8; ++i) st.acc[g][i] *= sc;
     st.m[g] = mn;
   }
+}
+
+// inactive rows must hold finite values (zeros): their probability is 0
+template <typename T, int G, int NR>
+HK_DEV void attn_values(AttnState<G> &st, const float (&p)[G][NR], const Raw8<T> (&vr)[NR]) {
 #pragma unroll
   for (int j = 0; j < NR; ++j) {
     float vf[8];
@@ -102,8 +108,16 @@ HK_DEV void attn_rows(AttnState<G> &st, const float (&qs)[G][8], const Raw8<T> (
 #pragma unroll
     for (int g = 0; g < G; ++g)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) st.acc[g][i] = __builtin_fmaf(lg[g][j], vf[i], st.acc[g][i]);
+      for (int i = 0; i < 8; ++i) st.acc[g][i] = __builtin_fmaf(p[g][j], vf[i], st.acc[g][i]);
   }
+}
+
+template <typename T, int G, int NR>
+HK_DEV void attn_rows(AttnState<G> &st, const float (&qs)[G][8], const Raw8<T> (&kr)[NR],
+                      const Raw8<T> (&vr)[NR], const bool (&act)[NR]) {
+  float p[G][NR];
+  attn_keys<T, G, NR>(st, qs, kr, act, p);
+  attn_values<T, G, NR>(st, p, vr);
 }
 
 // merge the four 16-lane groups of each wavefront, then the four wavefronts; write the

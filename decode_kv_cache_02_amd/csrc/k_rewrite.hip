@@ -12,7 +12,10 @@
 // mbcnt of equal weights below it) is under r.  The ballot of those bits is the block's
 // mask word.  A kept row's view row is the block's first view row plus the row's rank
 // inside the word, so the order of positions is preserved.  Kept rows are copied as
-// 16-byte pieces, 16 lanes per row, 16 rows in flight per wavefront.
+// 16-byte pieces, 16 lanes per row, 16 rows per batch; with buffer accesses whose
+// out-of-range offsets the hardware drops, no branch surrounds a load or store.  A
+// wavefront with more than two batches of 16-bit rows pipelines keys and values half a
+// batch apart, so that its stores drain while the next batch's loads are in flight.
 //
 // In the fused step the kernel also runs the attention of the group's queries over the
 // rows it copies (one split-K partial per workgroup, so the view is never read back),
@@ -22,6 +25,10 @@
 namespace hardkv {
 
 namespace {
+
+// Lists of at most this many kept rows per wavefront are copied batch by batch; longer
+// ones through the pipeline below (which pays a prologue of its own).
+constexpr int PIPE_MIN_ROWS = 32;
 
 template <typename T, int G, bool MASK, bool COPY, bool ATTN>
 __global__ __launch_bounds__(NTHREADS) void hardkv_rewrite(Args a) {
@@ -38,7 +45,7 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_rewrite(Args a) {
   // partial slot of this chunk's gathered rows
   const int pslot = a.gather_mode == GATHER_STEP ? chunk : a.xp_base + chunk;
   const int b = bh / a.Hkv, h = bh - b * a.Hkv;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int sub = lane & 15, grp = lane >> 4;
   const int P = a.P, V = a.V_cap;
 
@@ -140,31 +147,98 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_rewrite(Args a) {
   }
   if (COPY) {
     wave_sync();
-    // kept rows copied 16 at a time (4 per 16-lane group), attended while in registers;
-    // rows past the list read zeros and write nothing (offset BUF_SKIP), rows past the
-    // view's capacity are still attended but fall outside the view buffers
-    for (int it = 0; it < ns; it += 16) {
-      Raw8<T> kr[4], vr[4];
-      bool act[4];
-      uint32_t doff[4];
+    // Kept rows move 16 at a time (4 per 16-lane group) and are attended while in
+    // registers.  Keys and values are pipelined half a batch apart: the next batch's key
+    // loads go out as soon as this batch's keys are stored, before its values are waited
+    // for, so a wait for loads never waits for the stores just issued (the counter of
+    // loads and stores completes in order).  Rows past the list read zeros and write
+    // nothing (offset BUF_SKIP), and so does every store when the view is not written;
+    // rows past the view's capacity are attended but fall outside the view buffers.
+    uint32_t so[4], dof[4];
+    bool ac[4];
+    auto offsets = [&](int it, uint32_t (&o_s)[4], uint32_t (&o_d)[4], bool (&o_a)[4]) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int k = it + j * 4 + grp;
         const int kk = k < ns ? k : 0;
-        act[j] = k < ns;
-        const uint32_t soff = act[j] ? s_src[wave][kk] * (uint32_t)ROWB + lane_b : BUF_SKIP;
-        doff[j] = act[j] ? s_dst[wave][kk] * (uint32_t)ROWB + lane_b : BUF_SKIP;
-        buf_load_nt(pk, soff, kr[j]);
-        buf_load_nt(pv, soff, vr[j]);
+        o_a[j] = k < ns;
+        // read in every lane (kk is in the list), so that no branch surrounds the
+        // memory accesses that follow
+        uint32_t sv = s_src[wave][kk], dv = s_dst[wave][kk];
+        asm volatile("" : "+v"(sv), "+v"(dv));
+        o_s[j] = o_a[j] ? sv * (uint32_t)ROWB + lane_b : BUF_SKIP;
+        o_d[j] = (o_a[j] && store) ? dv * (uint32_t)ROWB + lane_b : BUF_SKIP;
       }
-      if (store) {
+    };
+    Raw8<T> kr[4], vr[4];
+    // The pipeline holds the next batch's keys beside this batch's probabilities: with
+    // fp32 rows or 8 queries per group that costs a wave per SIMD, so only 16-bit rows
+    // with up to 4 queries take it.
+    constexpr bool PIPE = Elem<T>::bytes == 2 && G <= 4;
+    if (!PIPE || ns <= PIPE_MIN_ROWS) {
+      // a short list: batch by batch, each store waiting only for its own load
+      for (int it = 0; it < ns; it += 16) {
+        offsets(it, so, dof, ac);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          buf_store_nt(vk, doff[j], kr[j]);
-          buf_store_nt(vv, doff[j], vr[j]);
+          buf_load_nt(pk, so[j], kr[j]);
+          buf_load_nt(pv, so[j], vr[j]);
         }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          buf_store_nt(vk, dof[j], kr[j]);
+          buf_store_nt(vv, dof[j], vr[j]);
+        }
+        if (ATTN) attn_rows<T, G, 4>(st, qs, kr, vr, ac);
       }
-      if (ATTN) attn_rows<T, G, 4>(st, qs, kr, vr, act);
+    } else if constexpr (PIPE) {
+      // (scheduling barriers keep the phases in this order: the waits depend on the order
+      // in which the loads and stores were issued)
+      offsets(0, so, dof, ac);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) buf_load_nt(pk, so[j], kr[j]);
+      __builtin_amdgcn_sched_barrier(0);
+      {
+        // stores that write nothing, so that the first batch's loads are followed by as
+        // many accesses as every later batch's: the waits in the loop count the same way
+        const Raw8<T> zero{};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) buf_store_nt(vv, BUF_SKIP + 64u * j, zero);  // distinct, not merged
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) buf_load_nt(pv, so[j], vr[j]);
+      __builtin_amdgcn_sched_barrier(0);
+      // every batch but the last loads its successor; the last only stores and attends
+      int it = 0;
+      for (; it + 16 < ns; it += 16) {
+        float p[G][4];
+        if (ATTN) attn_keys<T, G, 4>(st, qs, kr, ac, p);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) buf_store_nt(vk, dof[j], kr[j]);
+        __builtin_amdgcn_sched_barrier(0);
+        {
+          uint32_t so2[4], dof2[4];
+          bool ac2[4];
+          offsets(it + 16, so2, dof2, ac2);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) buf_load_nt(pk, so2[j], kr[j]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (ATTN) attn_values<T, G, 4>(st, p, vr);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) buf_store_nt(vv, dof[j], vr[j]);
+        __builtin_amdgcn_sched_barrier(0);
+        offsets(it + 16, so, dof, ac);  // read again rather than held through the values
+#pragma unroll
+        for (int j = 0; j < 4; ++j) buf_load_nt(pv, so[j], vr[j]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) buf_store_nt(vk, dof[j], kr[j]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) buf_store_nt(vv, dof[j], vr[j]);
+      if (ATTN) attn_rows<T, G, 4>(st, qs, kr, vr, ac);
     }
   }
   if (ATTN) attn_write_partial<G>(st, a.part + ((size_t)bh * a.npart + pslot) * G * (2 + HD), s_part);

@@ -18,7 +18,7 @@ bool aligned16(const void *p) { return p != nullptr && ((uintptr_t)p & 15u) == 0
 
 struct Plan {
   Args a;
-  size_t off_head, off_cmax, off_ent, off_blkinfo, off_part, ws_bytes;
+  size_t off_head, off_cmax, off_ent, off_blkinfo, off_part, off_phist, off_psum, off_selh, off_cand, ws_bytes;
 };
 
 // Checks the configuration and derives every size; fills the size fields of p.a.
@@ -114,6 +114,9 @@ int32_t plan(const hardkv_config *cfg, Plan &p) {
     a.ncs = 1;
   }
 
+  // the select of a long pool is split over slices of SEL_SLICE_BLOCKS blocks
+  a.nsp = (a.P + SEL_SLICE_BLOCKS - 1) / SEL_SLICE_BLOCKS;
+  if (a.nsp < SEL_SPLIT_MIN) a.nsp = 1;
   a.bh0 = 0;
   a.nbh = (int)BH;
 
@@ -122,7 +125,12 @@ int32_t plan(const hardkv_config *cfg, Plan &p) {
   p.off_ent = align256(p.off_cmax + (size_t)BH * a.nch_score * sizeof(float));
   p.off_blkinfo = align256(p.off_ent + (a.calibration ? (size_t)BH * a.nch_score * G * 3 * sizeof(float) : 0));
   p.off_part = align256(p.off_blkinfo + (size_t)BH * a.P * sizeof(uint2));
-  p.ws_bytes = align256(p.off_part + (size_t)BH * a.npart * G * (2 + HD) * sizeof(float));
+  const size_t split = a.nsp > 1 ? 1 : 0;  // the split select's scratch
+  p.off_phist = align256(p.off_part + (size_t)BH * a.npart * G * (2 + HD) * sizeof(float));
+  p.off_psum = align256(p.off_phist + split * (size_t)BH * a.nsp * NB1 * sizeof(unsigned long long));
+  p.off_selh = align256(p.off_psum + split * (size_t)BH * a.nsp * 2 * sizeof(unsigned long long));
+  p.off_cand = align256(p.off_selh + split * (size_t)BH * sizeof(SelHead));
+  p.ws_bytes = align256(p.off_cand + split * (size_t)BH * CAND_CAP * sizeof(uint32_t));
   return HARDKV_OK;
 }
 
@@ -175,6 +183,10 @@ int32_t bind(const hardkv_state *st, Plan &p) {
   a.ent = reinterpret_cast<float *>(ws + p.off_ent);
   a.blkinfo = reinterpret_cast<uint2 *>(ws + p.off_blkinfo);
   a.part = reinterpret_cast<float *>(ws + p.off_part);
+  a.phist = reinterpret_cast<unsigned long long *>(ws + p.off_phist);
+  a.psum = reinterpret_cast<unsigned long long *>(ws + p.off_psum);
+  a.selh = reinterpret_cast<SelHead *>(ws + p.off_selh);
+  a.cand_g = reinterpret_cast<uint32_t *>(ws + p.off_cand);
   return HARDKV_OK;
 }
 

@@ -1,5 +1,6 @@
 // hardkv_internal.h -- shared definitions of the HIP kernels and the host entry points.
 #pragma once
+#include <cstddef>
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -16,6 +17,19 @@ constexpr int NB1 = 3073;     // level-1 buckets of the mass radix select (key >
 constexpr int SEL_THREADS = 1024;     // threads of the select workgroup (one per head)
 constexpr int MAX_POOL_BLOCKS = 6144; // pool ring blocks per head the select LDS can index
 constexpr int CAND_CAP = 8192;        // cut-bucket candidates resolved in LDS
+constexpr int SEL_SLICE_BLOCKS = 256; // pool blocks per workgroup when a head's select is split
+constexpr int SEL_SPLIT_MIN = 4;      // slices per head from which the select is split
+
+// Per-head values that the split select passes between its kernels.
+struct alignas(128) SelHead {
+  unsigned long long w_all, w_u, T, R1;  // masses, the top-p target, mass needed from the cut bucket
+  int32_t b1;                            // level-1 bucket that holds the cut
+  int32_t pad_[7];
+  // candidates of that bucket (a counter, may exceed CAND_CAP); on a 64-byte line of its
+  // own, apart from the fields above, which one workgroup stores while the others add here
+  uint32_t ncand;
+};
+static_assert(offsetof(SelHead, ncand) == 64, "ncand on its own line");
 
 // Per-head plan of the current step, written by the select kernel and read by the
 // kernels after it (rewrite, condense), so that they see the pool as select saw it.
@@ -61,6 +75,11 @@ struct Args {
                       // l = q . k log2(e) / sqrt(D) (entropy calibration)
   uint2 *blkinfo;     // [BH][P] per ring block: (first view row, ties before the block)
   float *part;        // [BH][npart][G][2 + HD] attention partials (m, l, acc)
+  // split select (nsp > 1 slices per head)
+  unsigned long long *phist;  // [BH][nsp][NB1] level-1 mass histogram of each slice
+  unsigned long long *psum;   // [BH][nsp][2] (pool mass, survivor mass) of each slice
+  SelHead *selh;              // [BH]
+  uint32_t *cand_g;           // [BH][CAND_CAP] candidates of the cut bucket
   // prefill
   const void *k_ctx, *v_ctx;
   const int64_t *ctx_len;
@@ -68,6 +87,7 @@ struct Args {
   // sizes
   int B, Hq, Hkv, G, W, P, S_cap, V_cap, C, mode, merge_bias;
   int cb_score, nch_score;  // score: blocks per workgroup, workgroups per head
+  int nsp;                  // select: slices per head (1: one workgroup does the whole select)
   int cb_reg, nch_reg;      // rewrite: blocks per workgroup, workgroups per head
   int rv_att, nv_att;       // attention over the view (standalone): rows per workgroup, count
   int rc_att, nc_att;       // attention over condensed slots

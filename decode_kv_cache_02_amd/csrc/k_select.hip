@@ -118,7 +118,7 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_score(Args a) {
           const int rel = gi * 16 + l * 4 + grp;
           // rows past the chunk read zeros (offset BUF_SKIP), with no branch
           const uint32_t row_b = (uint32_t)(pb * BK + (rel & (BK - 1))) * (uint32_t)(HD * EB) + lane_b;
-          const uint32_t off = (gi < ngroups) & (rel < nrows) ? row_b : BUF_SKIP;
+          const uint32_t off = ((gi < ngroups) & (rel < nrows)) ? row_b : BUF_SKIP;
           buf_load_nt(kb, off, buf[u][l]);
         }
       }
@@ -341,144 +341,174 @@ HK_DEV uint32_t sum16(uint32_t v) {
   return v;
 }
 
-__global__ __launch_bounds__(SEL_THREADS) void hardkv_select(Args a) {
-  const int bh = a.bh0 + blockIdx.x;
-  const int b = bh / a.Hkv, h = bh - b * a.Hkv;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int q4 = lane >> 4, r4 = (lane & 15) * 4;  // a load: block q4 of 4, rows r4 .. r4 + 3
-  const int P = a.P;
-  HeadInfo *hd = a.head + bh;
-  extern __shared__ unsigned char smem_raw[];
-  SelShared &sh = *reinterpret_cast<SelShared *>(smem_raw);
-  uint32_t *blk = reinterpret_cast<uint32_t *>(smem_raw + sizeof(SelShared));
+// The head's pool as the select stage sees it.
+struct SelGeo {
+  int64_t t, c, pend, E, u0;
+  int nblk;   // pool blocks, at most P
+  int nx;     // condensing blocks (they come first)
+  int nub;    // survivor blocks
+  int pb_lo;  // ring block of the pool head
+  float kap;  // calibration slope
+  size_t rowbase;
+  HK_DEV int ring(int i, int P) const {
+    const int pb = pb_lo + i;
+    return pb >= P ? pb - P : pb;
+  }
+};
 
-  const int64_t t = a.seq_len[b];
-  const int64_t c = a.pool_head[bh];
-  const int64_t pend = pool_end(t, a.W);
-  const int64_t N = pend - c;
-  const int64_t E = plan_E(N, a.mode, a.S_cap);
-  const int64_t u0 = c + (int64_t)BK * E;
-  const int nblk = (int)((pend + BK - 1) / BK - c / BK);  // pool blocks, at most P
-  const int nx = (int)E;                                   // condensing blocks come first
-  const int nub = nblk - nx;                               // survivor blocks
-  const int pb_lo = (int)((c / BK) % P);
+HK_DEV SelGeo sel_geo(const Args &a, int bh) {
+  SelGeo g;
+  const int b = bh / a.Hkv, h = bh - b * a.Hkv;
+  g.t = a.seq_len[b];
+  g.c = a.pool_head[bh];
+  g.pend = pool_end(g.t, a.W);
+  const int64_t N = g.pend - g.c;
+  g.E = plan_E(N, a.mode, a.S_cap);
+  g.u0 = g.c + (int64_t)BK * g.E;
+  g.nblk = (int)((g.pend + BK - 1) / BK - g.c / BK);
+  g.nx = (int)g.E;
+  g.nub = g.nblk - g.nx;
+  g.pb_lo = (int)((g.c / BK) % a.P);
   // both slopes loaded, then a select of values: a select between the argument block and
   // a global address (which the compiler forms from a plain load under a branch) copies
   // the whole argument block to scratch
   const float kfix = a.kappa[h];
-  const float kfit = __builtin_nontemporal_load(&hd->kappa);
-  const float kap = a.calibration ? kfit : kfix;
-  const size_t rowbase = (size_t)bh * P * BK;
-  auto ring = [&](int i) {
-    int pb = pb_lo + i;
-    return pb >= P ? pb - P : pb;
-  };
+  const float kfit = __builtin_nontemporal_load(&a.head[bh].kappa);
+  g.kap = a.calibration ? kfit : kfix;
+  g.rowbase = (size_t)bh * a.P * BK;
+  return g;
+}
 
-  // m: max of the score workgroups' maxima
+// m: max of the score workgroups' maxima (every thread gets it)
+HK_DEV float sel_max(const Args &a, int bh, SelShared &sh) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   float mx = -INFINITY;
   for (int i = tid; i < a.nch_score; i += SEL_THREADS) mx = fmaxf(mx, a.cmax[(size_t)bh * a.nch_score + i]);
   mx = wave_max(mx);
   if (lane == 0) sh.fred[wave] = mx;
-  for (int i = tid; i < NB1; i += SEL_THREADS) sh.hist[i] = 0ull;
-  if (tid == 0) sh.ncand = 0;
-  // every mask word starts empty; the rewrite kernel writes the survivor blocks' words
-  for (int i = tid; i < P; i += SEL_THREADS) a.mask[(size_t)bh * P + i] = 0ull;
   __syncthreads();
   float m = -INFINITY;
 #pragma unroll
   for (int w = 0; w < NW; ++w) m = fmaxf(m, sh.fred[w]);
+  return m;
+}
 
-  // pass A: weights of the whole pool, total and survivor mass, level-1 histogram of U.
-  // Wavefront `wave` takes blocks 4 wave + 64 k .. + 3, one 16-byte load per lane each.
-  uint64_t my_all = 0, my_u = 0;
-  bool bad = false;
-  for (int i0 = wave * 4; i0 < nblk; i0 += 4 * NW * UA) {
+// pass A over pool blocks [lo, hi): weights (written), pool and survivor mass, level-1
+// histogram of the survivors' mass in sh.hist.  Wavefront `wave` takes blocks
+// lo + 4 wave + 64 k .. + 3, one 16-byte load per lane each.
+HK_DEV void sel_pass_a(const Args &a, const SelGeo &g, float m, int lo, int hi, SelShared &sh,
+                       uint64_t &my_all, uint64_t &my_u, bool &bad) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int q4 = lane >> 4, r4 = (lane & 15) * 4;  // a load: block q4 of 4, rows r4 .. r4 + 3
+  const int P = a.P;
+  for (int i0 = lo + wave * 4; i0 < hi; i0 += 4 * NW * UA) {
     float4 sv[UA];
 #pragma unroll
     for (int u = 0; u < UA; ++u) {
       const int i = i0 + u * 4 * NW + q4;
-      sv[u] = i < nblk ? *reinterpret_cast<const float4 *>(a.scores + rowbase + (size_t)ring(i) * BK + r4)
-                       : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      sv[u] = i < hi ? *reinterpret_cast<const float4 *>(a.scores + g.rowbase + (size_t)g.ring(i, P) * BK + r4)
+                     : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     }
 #pragma unroll
     for (int u = 0; u < UA; ++u) {
       const int i = i0 + u * 4 * NW + q4;
-      if (i < nblk) {
-        const int64_t p = c + (int64_t)i * BK + r4;
+      if (i < hi) {
+        const int64_t p = g.c + (int64_t)i * BK + r4;
         const float s4[4] = {sv[u].x, sv[u].y, sv[u].z, sv[u].w};
         uint32_t w4[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-          const bool valid = p + k < pend;
+          const bool valid = p + k < g.pend;
           bad |= valid && !isfinite(s4[k]);
-          w4[k] = valid ? calib_weight(s4[k], m, kap, a.coeff) : 0u;
+          w4[k] = valid ? calib_weight(s4[k], m, g.kap, a.coeff) : 0u;
           my_all += w4[k];
-          if (valid && i >= nx) {
+          if (valid && i >= g.nx) {
             my_u += w4[k];
             atomicAdd(&sh.hist[wkey(w4[k]) >> 16], (unsigned long long)w4[k]);
           }
         }
-        uint32_t *wp = a.weights + rowbase + (size_t)ring(i) * BK + r4;
-        if (p + 3 < pend) {
+        uint32_t *wp = a.weights + g.rowbase + (size_t)g.ring(i, P) * BK + r4;
+        if (p + 3 < g.pend) {
           *reinterpret_cast<uint4 *>(wp) = make_uint4(w4[0], w4[1], w4[2], w4[3]);
         } else {
 #pragma unroll
           for (int k = 0; k < 4; ++k)
-            if (p + k < pend) wp[k] = w4[k];
+            if (p + k < g.pend) wp[k] = w4[k];
         }
       }
     }
   }
-  if (ballot(bad) && lane == 0) atomicOr(a.error_word, HARDKV_ERR_NONFINITE);
-  const uint64_t W_all = block_sum_u64(my_all, sh, 0);
-  const uint64_t W_U = block_sum_u64(my_u, sh, 1);
-  const uint64_t T = ((uint64_t)a.pq * W_U + 65535ull) >> 16;
+}
 
+// pass B over survivor blocks [jlo, jhi): per block the weights above the cut bucket b1
+// (into cnt[j], LDS, or the block's blkinfo.x in memory when SPLIT), and the bucket's
+// tokens gathered into cand through the counter *ncand
+template <bool SPLIT>
+HK_DEV void sel_pass_b(const Args &a, int bh, const SelGeo &g, int b1, int jlo, int jhi, uint32_t *cnt,
+                       uint32_t *cand, uint32_t *ncand) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int q4 = lane >> 4, r4 = (lane & 15) * 4;
+  const int P = a.P;
+  for (int j0 = jlo + wave * 4; j0 < jhi; j0 += 4 * NW * UA) {
+    uint4 wv[UA];
+#pragma unroll
+    for (int u = 0; u < UA; ++u) {
+      const int j = j0 + u * 4 * NW + q4;
+      wv[u] = j < jhi ? *reinterpret_cast<const uint4 *>(a.weights + g.rowbase + (size_t)g.ring(g.nx + j, P) * BK + r4)
+                      : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int u = 0; u < UA; ++u) {
+      const int jb = j0 + u * 4 * NW;  // wave-uniform
+      if (jb >= jhi) break;
+      const int j = jb + q4;
+      const int64_t p = g.u0 + (int64_t)j * BK + r4;
+      const uint32_t w4[4] = {wv[u].x, wv[u].y, wv[u].z, wv[u].w};
+      uint32_t n_above = 0;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const bool valid = j < jhi && p + k < g.pend;
+        const uint32_t key = wkey(w4[k]);
+        const int kb = (int)(key >> 16);
+        n_above += (valid && kb > b1) ? 1u : 0u;
+        const bool in = valid && kb == b1;
+        const uint64_t inb = ballot(in);
+        if (inb) {  // wave-uniform
+          uint32_t base = 0;
+          if (lane == 0) base = atomicAdd(ncand, (uint32_t)__popcll(inb));
+          base = __shfl(base, 0);
+          const uint32_t slot = base + popc_below(inb);
+          if (in && slot < (uint32_t)CAND_CAP) cand[slot] = ((uint32_t)j << 16) | (key & 0xffffu);
+        }
+      }
+      n_above = sum16(n_above);
+      if ((lane & 15) == 0 && j < jhi) {
+        if (SPLIT)
+          reinterpret_cast<uint32_t *>(a.blkinfo + (size_t)bh * P + g.ring(g.nx + j, P))[0] = n_above;
+        else
+          cnt[j] = n_above;
+      }
+    }
+  }
+}
+
+// From the cut bucket to the head's plan: the exact threshold w_th and the r ties kept
+// (from the candidates in LDS, or, for a bucket too full for LDS, from the weights in
+// memory), per-block counts, the scan over blocks, and the plan.  blk[j] holds the
+// weights above the bucket of each survivor block, sh.cand / sh.ncand the bucket's tokens.
+HK_DEV void sel_finish(const Args &a, int bh, const SelGeo &g, SelShared &sh, uint32_t *blk, uint64_t W_all,
+                       uint64_t W_U, uint64_t T, uint64_t R1, int b1) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int P = a.P;
+  HeadInfo *hd = a.head + bh;
+  const int64_t t = g.t, c = g.c, pend = g.pend, E = g.E, u0 = g.u0;
+  const int nx = g.nx, nub = g.nub;
+  const size_t rowbase = g.rowbase;
+  auto ring = [&](int i) { return g.ring(i, P); };
   uint32_t w_th = 0, r = 0;
   uint64_t n_gt = 0;
   if (W_U > 0) {
-    uint64_t above1, above2, above3;
-    const int b1 = find_cut(sh, NB1, T, &above1);
-    const uint64_t R1 = T - above1;  // mass still needed from the cut bucket
-
-    // pass B: per survivor block, weights above the cut bucket; gather the bucket
-    for (int j0 = wave * 4; j0 < nub; j0 += 4 * NW * UA) {
-      uint4 wv[UA];
-#pragma unroll
-      for (int u = 0; u < UA; ++u) {
-        const int j = j0 + u * 4 * NW + q4;
-        wv[u] = j < nub ? *reinterpret_cast<const uint4 *>(a.weights + rowbase + (size_t)ring(nx + j) * BK + r4)
-                        : make_uint4(0u, 0u, 0u, 0u);
-      }
-#pragma unroll
-      for (int u = 0; u < UA; ++u) {
-        const int jb = j0 + u * 4 * NW;  // wave-uniform
-        if (jb >= nub) break;
-        const int j = jb + q4;
-        const int64_t p = u0 + (int64_t)j * BK + r4;
-        const uint32_t w4[4] = {wv[u].x, wv[u].y, wv[u].z, wv[u].w};
-        uint32_t n_above = 0;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const bool valid = j < nub && p + k < pend;
-          const uint32_t key = wkey(w4[k]);
-          const int kb = (int)(key >> 16);
-          n_above += (valid && kb > b1) ? 1u : 0u;
-          const bool in = valid && kb == b1;
-          const uint64_t inb = ballot(in);
-          if (inb) {  // wave-uniform
-            uint32_t base = 0;
-            if (lane == 0) base = atomicAdd(&sh.ncand, (uint32_t)__popcll(inb));
-            base = __shfl(base, 0);
-            const uint32_t slot = base + popc_below(inb);
-            if (in && slot < (uint32_t)CAND_CAP) sh.cand[slot] = ((uint32_t)j << 16) | (key & 0xffffu);
-          }
-        }
-        n_above = sum16(n_above);
-        if ((lane & 15) == 0 && j < nub) blk[j] = n_above;
-      }
-    }
-    __syncthreads();
+    uint64_t above2, above3;
     const uint32_t ncand = sh.ncand;
     const uint32_t kb1 = (uint32_t)b1 << 16;
     if (ncand <= 64u) {
@@ -625,6 +655,159 @@ __global__ __launch_bounds__(SEL_THREADS) void hardkv_select(Args a) {
     if (a.regularized) a.regularized[bh] = rw;
     if (rw && !a.view_sum && kstar > a.V_cap) atomicOr(a.error_word, HARDKV_ERR_VIEW_OVERFLOW);
   }
+}
+
+// The whole select stage of one head in one workgroup (pools up to SEL_SPLIT_MIN slices).
+__global__ __launch_bounds__(SEL_THREADS) void hardkv_select(Args a) {
+  const int bh = a.bh0 + blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int P = a.P;
+  extern __shared__ unsigned char smem_raw[];
+  SelShared &sh = *reinterpret_cast<SelShared *>(smem_raw);
+  uint32_t *blk = reinterpret_cast<uint32_t *>(smem_raw + sizeof(SelShared));
+  const SelGeo g = sel_geo(a, bh);
+
+  for (int i = tid; i < NB1; i += SEL_THREADS) sh.hist[i] = 0ull;
+  if (tid == 0) sh.ncand = 0;
+  // every mask word starts empty; the rewrite kernel writes the survivor blocks' words
+  for (int i = tid; i < P; i += SEL_THREADS) a.mask[(size_t)bh * P + i] = 0ull;
+  const float m = sel_max(a, bh, sh);  // (its barrier also orders the clears above)
+
+  uint64_t my_all = 0, my_u = 0;
+  bool bad = false;
+  sel_pass_a(a, g, m, 0, g.nblk, sh, my_all, my_u, bad);
+  if (ballot(bad) && lane == 0) atomicOr(a.error_word, HARDKV_ERR_NONFINITE);
+  const uint64_t W_all = block_sum_u64(my_all, sh, 0);
+  const uint64_t W_U = block_sum_u64(my_u, sh, 1);
+  const uint64_t T = ((uint64_t)a.pq * W_U + 65535ull) >> 16;
+  uint64_t R1 = 0;
+  int b1 = 0;
+  if (W_U > 0) {
+    uint64_t above1;
+    b1 = find_cut(sh, NB1, T, &above1);
+    R1 = T - above1;  // mass still needed from the cut bucket
+    sel_pass_b<false>(a, bh, g, b1, 0, g.nub, blk, sh.cand, &sh.ncand);
+    __syncthreads();
+  }
+  sel_finish(a, bh, g, sh, blk, W_all, W_U, T, R1, b1);
+}
+
+// Split select, for long pools: the head's blocks in slices of SEL_SLICE_BLOCKS, one
+// workgroup each, for the two passes over every token; four kernels in stream order.
+//
+// hardkv_sel_weigh, grid (nsp, B*Hkv): pass A over the slice's pool blocks; the slice's
+//   histogram and masses go to memory (phist, psum); the slice's share of the mask words
+//   is cleared.
+__global__ __launch_bounds__(SEL_THREADS) void hardkv_sel_weigh(Args a) {
+  const int bh = a.bh0 + blockIdx.y, slice = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int P = a.P;
+  extern __shared__ unsigned char smem_raw[];
+  SelShared &sh = *reinterpret_cast<SelShared *>(smem_raw);
+  const SelGeo g = sel_geo(a, bh);
+
+  for (int i = tid; i < NB1; i += SEL_THREADS) sh.hist[i] = 0ull;
+  const int zs = (P + a.nsp - 1) / a.nsp;
+  for (int i = slice * zs + tid; i < min(P, (slice + 1) * zs); i += SEL_THREADS) a.mask[(size_t)bh * P + i] = 0ull;
+  if (slice == 0 && tid == 0) a.selh[bh].ncand = 0u;
+  const float m = sel_max(a, bh, sh);
+
+  uint64_t my_all = 0, my_u = 0;
+  bool bad = false;
+  const int lo = slice * SEL_SLICE_BLOCKS, hi = min(g.nblk, lo + SEL_SLICE_BLOCKS);
+  sel_pass_a(a, g, m, lo, hi, sh, my_all, my_u, bad);
+  if (ballot(bad) && lane == 0) atomicOr(a.error_word, HARDKV_ERR_NONFINITE);
+  const uint64_t s_all = block_sum_u64(my_all, sh, 0);
+  const uint64_t s_u = block_sum_u64(my_u, sh, 1);  // (its barrier also orders the histogram)
+  unsigned long long *ph = a.phist + ((size_t)bh * a.nsp + slice) * NB1;
+  for (int i = tid; i < NB1; i += SEL_THREADS) ph[i] = sh.hist[i];
+  if (tid == 0) {
+    a.psum[((size_t)bh * a.nsp + slice) * 2] = s_all;
+    a.psum[((size_t)bh * a.nsp + slice) * 2 + 1] = s_u;
+  }
+}
+
+// the head's masses from the slices' (every thread gets them)
+HK_DEV void sel_masses(const Args &a, int bh, uint64_t &W_all, uint64_t &W_U) {
+  W_all = 0;
+  W_U = 0;
+  for (int k = 0; k < a.nsp; ++k) {
+    W_all += a.psum[((size_t)bh * a.nsp + k) * 2];
+    W_U += a.psum[((size_t)bh * a.nsp + k) * 2 + 1];
+  }
+}
+
+// hardkv_sel_cut, grid (B*Hkv): the head's masses and histogram from the slices', the
+//   cut bucket and the mass still needed from it, saved for the next two kernels.
+__global__ __launch_bounds__(SEL_THREADS) void hardkv_sel_cut(Args a) {
+  const int bh = a.bh0 + blockIdx.x;
+  const int tid = threadIdx.x;
+  extern __shared__ unsigned char smem_raw[];
+  SelShared &sh = *reinterpret_cast<SelShared *>(smem_raw);
+  uint64_t W_all, W_U;
+  sel_masses(a, bh, W_all, W_U);
+  const uint64_t T = ((uint64_t)a.pq * W_U + 65535ull) >> 16;
+  uint64_t above1 = 0;
+  int b1 = 0;
+  if (W_U > 0) {
+    const unsigned long long *ph = a.phist + (size_t)bh * a.nsp * NB1;
+    for (int i = tid; i < NB1; i += SEL_THREADS) {
+      unsigned long long v = 0;
+      for (int k = 0; k < a.nsp; ++k) v += ph[(size_t)k * NB1 + i];
+      sh.hist[i] = v;
+    }
+    __syncthreads();
+    b1 = find_cut(sh, NB1, T, &above1);
+  }
+  if (tid == 0) {
+    SelHead *sx = a.selh + bh;
+    sx->w_all = W_all;
+    sx->w_u = W_U;
+    sx->T = T;
+    sx->R1 = T - above1;
+    sx->b1 = b1;
+  }
+}
+
+// hardkv_sel_count, grid (nsp, B*Hkv): pass B over the slice's survivor blocks: counts
+//   into blkinfo.x, the cut bucket's tokens into cand_g.
+__global__ __launch_bounds__(SEL_THREADS) void hardkv_sel_count(Args a) {
+  const int bh = a.bh0 + blockIdx.y, slice = blockIdx.x;
+  const SelHead *sx = a.selh + bh;
+  if (sx->w_u == 0) return;  // uniform: nothing to cut
+  const int b1 = sx->b1;
+  const SelGeo g = sel_geo(a, bh);
+  const int lo = max(slice * SEL_SLICE_BLOCKS, g.nx) - g.nx;
+  const int hi = min((slice + 1) * SEL_SLICE_BLOCKS, g.nblk) - g.nx;
+  if (lo < hi) sel_pass_b<true>(a, bh, g, b1, lo, hi, nullptr, a.cand_g + (size_t)bh * CAND_CAP, &a.selh[bh].ncand);
+}
+
+// hardkv_sel_finish, grid (B*Hkv): the per-block counts and the candidates back into LDS,
+//   then the rest of the select stage as in the one-workgroup kernel.
+__global__ __launch_bounds__(SEL_THREADS) void hardkv_sel_finish(Args a) {
+  const int bh = a.bh0 + blockIdx.x;
+  const int tid = threadIdx.x;
+  const int P = a.P;
+  extern __shared__ unsigned char smem_raw[];
+  SelShared &sh = *reinterpret_cast<SelShared *>(smem_raw);
+  uint32_t *blk = reinterpret_cast<uint32_t *>(smem_raw + sizeof(SelShared));
+  const SelGeo g = sel_geo(a, bh);
+  const SelHead *sx = a.selh + bh;
+  const uint64_t W_all = sx->w_all, W_U = sx->w_u, T = sx->T;
+  uint64_t R1 = 0;
+  int b1 = 0;
+  if (W_U > 0) {
+    R1 = sx->R1;
+    b1 = sx->b1;
+    const uint32_t nc = sx->ncand;
+    if (tid == 0) sh.ncand = nc;
+    if (nc <= (uint32_t)CAND_CAP)
+      for (uint32_t i = tid; i < nc; i += SEL_THREADS) sh.cand[i] = a.cand_g[(size_t)bh * CAND_CAP + i];
+    for (int j = tid; j < g.nub; j += SEL_THREADS)
+      blk[j] = reinterpret_cast<const uint32_t *>(a.blkinfo + (size_t)bh * P + g.ring(g.nx + j, P))[0];
+    __syncthreads();
+  }
+  sel_finish(a, bh, g, sh, blk, W_all, W_U, T, R1, b1);
 }
 
 // Flatten Index to the sum: one workgroup scans n_u = k* (rewritten heads) or 0 over
@@ -872,14 +1055,31 @@ hipError_t launch_flatten(const Args &a, hipStream_t s) {
 }
 
 hipError_t launch_select(const Args &a, hipStream_t s) {
-  static bool configured = false;  // the attribute is per function, set once per process
+  static bool configured = false;  // the attributes are per function, set once per process
   if (!configured) {
-    hipError_t e = hipFuncSetAttribute((const void *)hardkv_select, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)sel_lds_bytes(MAX_POOL_BLOCKS));
-    if (e != hipSuccess) return e;
+    const void *fs[] = {(const void *)hardkv_select, (const void *)hardkv_sel_weigh,
+                        (const void *)hardkv_sel_cut, (const void *)hardkv_sel_finish};
+    for (const void *f : fs) {
+      hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                         (int)sel_lds_bytes(MAX_POOL_BLOCKS));
+      if (e != hipSuccess) return e;
+    }
     configured = true;
   }
-  hipLaunchKernelGGL(hardkv_select, dim3(a.nbh), dim3(SEL_THREADS), sel_lds_bytes(a.P), s, a);
+  if (a.nsp <= 1) {
+    hipLaunchKernelGGL(hardkv_select, dim3(a.nbh), dim3(SEL_THREADS), sel_lds_bytes(a.P), s, a);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL(hardkv_sel_weigh, dim3(a.nsp, a.nbh), dim3(SEL_THREADS), sizeof(SelShared), s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(hardkv_sel_cut, dim3(a.nbh), dim3(SEL_THREADS), sizeof(SelShared), s, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(hardkv_sel_count, dim3(a.nsp, a.nbh), dim3(SEL_THREADS), 0, s, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(hardkv_sel_finish, dim3(a.nbh), dim3(SEL_THREADS), sel_lds_bytes(a.P), s, a);
   return hipGetLastError();
 }
 

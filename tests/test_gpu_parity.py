@@ -70,6 +70,41 @@ def test_tau_inf_all_ties():
         pr.step()
 
 
+# Rings of at least four slices of 256 blocks: the select of each head runs as three
+# kernels over the slices (weights and histograms, counts and candidates, finish).
+SPLIT_CASES = {
+    # a 70k-token pool (1094 ring blocks, 5 slices), nothing condensed
+    "split_long": dict(ctx_len=70000, ctx_min=60000, sparse_cap=69632, cond_mode=COND_MERGE),
+    # a short pool in a large ring: most slices hold nothing
+    "split_short_pool": dict(pool_blocks=1100, sparse_cap=4096, ctx_len=3000, ctx_min=2000, cond_mode=COND_MERGE),
+    # the first step condenses ~800 blocks of each head into 64 slots
+    "split_condense": dict(pool_blocks=1024, sparse_cap=8192, ctx_len=60000, ctx_min=40000, cond_mode=COND_MERGE,
+                           condensed_slots=64, dense_window=128),
+    "split_evict_f32": dict(dtype="f32", pool_blocks=1030, sparse_cap=16384, ctx_len=30000, ctx_min=20000),
+}
+
+
+@pytest.mark.parametrize("name", list(SPLIT_CASES))
+def test_split_select_parity(name):
+    from parity import Pair
+    wl = tiny_workload(steps=2, **SPLIT_CASES[name])
+    assert -(-wl.P_blk // 256) >= 4, wl.P_blk
+    print(f"case {name}: {wl}", flush=True)
+    pr = Pair(wl)
+    for fused in (True, False):
+        pr.step(fused=fused)
+
+
+def test_split_select_all_ties():
+    """Every weight equal in a long pool: the cut bucket holds more tokens than LDS takes,
+    and the finishing kernel resolves it from the weights in memory."""
+    from parity import Pair
+    wl = tiny_workload(steps=2, **SPLIT_CASES["split_long"])
+    pr = Pair(wl, tau=[float("inf")] * wl.num_kv_heads)
+    for _ in range(2):
+        pr.step()
+
+
 def test_sharp_tau_and_no_merge_bias():
     from parity import Pair
     wl = tiny_workload(steps=2, cond_mode=COND_MERGE, sparse_cap=128, condensed_slots=2)

@@ -5,9 +5,9 @@
 // its own budget) and 2.B (max-pooled logits as the importance metric; calibration maps
 // the scores to one softmax by a temperature, keeping their order).
 //
-// Two kernels, with the kernel boundary between them as the only synchronization (no
-// cross-workgroup flags: on MI355X each agent-scope release/acquire writes back or
-// invalidates a whole XCD's L2).
+// Kernel boundaries are the only synchronization between workgroups (no cross-workgroup
+// flags: on MI355X each agent-scope release/acquire writes back or invalidates a whole
+// XCD's L2).
 //
 // hardkv_score, grid (chunks, B*Hkv), 256 threads (XCD-swizzled): streams a chunk of the head's pool
 //   keys with 16-byte loads; 16 lanes hold one 256-byte bf16 row (8 elements each), a
@@ -25,6 +25,13 @@
 //   to the lowest positions).  A scan over blocks gives each block its first view row
 //   and its ties-before count; the rewrite kernel derives the mask bits from them.  The
 //   select kernel clears all the head's mask words; the rewrite writes the survivors'.
+//
+// For rings of SEL_SPLIT_MIN or more slices of SEL_SLICE_BLOCKS blocks, one workgroup per
+//   head would spend most of the stage streaming its pool through one CU, so the two
+//   passes run over the slices in parallel: hardkv_sel_weigh (pass A per slice, its
+//   histogram and masses to memory), hardkv_sel_cut (per head: the cut bucket),
+//   hardkv_sel_count (pass B per slice: per-block counts, the bucket's tokens through a
+//   counter) and hardkv_sel_finish (per head: the same ending as the one-workgroup kernel).
 #include "hardkv_internal.h"
 
 namespace hardkv {

@@ -268,6 +268,7 @@ struct SelShared {
   unsigned long long carry;
   unsigned long long total;
   uint32_t w_th, r;
+  uint32_t cand_base;  // split select: the workgroup's first slot in the head's candidate list
 };
 // Dynamic LDS: SelShared, then uint32_t blk[P], per survivor block gt | eq << 16.
 constexpr size_t sel_lds_bytes(int P) { return sizeof(SelShared) + sizeof(uint32_t) * (size_t)P; }
@@ -738,9 +739,20 @@ __global__ __launch_bounds__(SEL_THREADS) void hardkv_sel_weigh(Args a) {
 HK_DEV void sel_masses(const Args &a, int bh, uint64_t &W_all, uint64_t &W_U) {
   W_all = 0;
   W_U = 0;
-  for (int k = 0; k < a.nsp; ++k) {
-    W_all += a.psum[((size_t)bh * a.nsp + k) * 2];
-    W_U += a.psum[((size_t)bh * a.nsp + k) * 2 + 1];
+  const unsigned long long *ps = a.psum + (size_t)bh * a.nsp * 2;
+  for (int k0 = 0; k0 < a.nsp; k0 += 8) {  // eight slices' loads in flight
+    unsigned long long x[8][2];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const bool in = k0 + u < a.nsp;
+      x[u][0] = in ? ps[(k0 + u) * 2] : 0ull;
+      x[u][1] = in ? ps[(k0 + u) * 2 + 1] : 0ull;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      W_all += x[u][0];
+      W_U += x[u][1];
+    }
   }
 }
 
@@ -757,12 +769,30 @@ __global__ __launch_bounds__(SEL_THREADS) void hardkv_sel_cut(Args a) {
   uint64_t above1 = 0;
   int b1 = 0;
   if (W_U > 0) {
+    // the thread's buckets tid, tid + 1024, ... summed over the slices, four slices'
+    // loads per bucket in flight
+    constexpr int PER = (NB1 + SEL_THREADS - 1) / SEL_THREADS;
     const unsigned long long *ph = a.phist + (size_t)bh * a.nsp * NB1;
-    for (int i = tid; i < NB1; i += SEL_THREADS) {
-      unsigned long long v = 0;
-      for (int k = 0; k < a.nsp; ++k) v += ph[(size_t)k * NB1 + i];
-      sh.hist[i] = v;
+    unsigned long long acc[PER];
+#pragma unroll
+    for (int q = 0; q < PER; ++q) acc[q] = 0ull;
+    for (int k0 = 0; k0 < a.nsp; k0 += 4) {
+      unsigned long long x[4][PER];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int q = 0; q < PER; ++q) {
+          const int i = tid + q * SEL_THREADS;
+          x[u][q] = (k0 + u < a.nsp && i < NB1) ? ph[(size_t)(k0 + u) * NB1 + i] : 0ull;
+        }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int q = 0; q < PER; ++q) acc[q] += x[u][q];
     }
+#pragma unroll
+    for (int q = 0; q < PER; ++q)
+      if (tid + q * SEL_THREADS < NB1) sh.hist[tid + q * SEL_THREADS] = acc[q];
     __syncthreads();
     b1 = find_cut(sh, NB1, T, &above1);
   }
@@ -777,16 +807,32 @@ __global__ __launch_bounds__(SEL_THREADS) void hardkv_sel_cut(Args a) {
 }
 
 // hardkv_sel_count, grid (nsp, B*Hkv): pass B over the slice's survivor blocks: counts
-//   into blkinfo.x, the cut bucket's tokens into cand_g.
+//   into blkinfo.x; the cut bucket's tokens gathered in LDS, then appended to cand_g at
+//   an offset reserved with one device-wide atomic per workgroup.
 __global__ __launch_bounds__(SEL_THREADS) void hardkv_sel_count(Args a) {
   const int bh = a.bh0 + blockIdx.y, slice = blockIdx.x;
-  const SelHead *sx = a.selh + bh;
+  const int tid = threadIdx.x;
+  extern __shared__ unsigned char smem_raw[];
+  SelShared &sh = *reinterpret_cast<SelShared *>(smem_raw);
+  SelHead *sx = a.selh + bh;
   if (sx->w_u == 0) return;  // uniform: nothing to cut
   const int b1 = sx->b1;
   const SelGeo g = sel_geo(a, bh);
   const int lo = max(slice * SEL_SLICE_BLOCKS, g.nx) - g.nx;
   const int hi = min((slice + 1) * SEL_SLICE_BLOCKS, g.nblk) - g.nx;
-  if (lo < hi) sel_pass_b<true>(a, bh, g, b1, lo, hi, nullptr, a.cand_g + (size_t)bh * CAND_CAP, &a.selh[bh].ncand);
+  if (lo >= hi) return;  // uniform
+  if (tid == 0) sh.ncand = 0;
+  __syncthreads();
+  sel_pass_b<true>(a, bh, g, b1, lo, hi, nullptr, sh.cand, &sh.ncand);
+  __syncthreads();
+  const uint32_t n = sh.ncand;  // may exceed CAND_CAP: the total then does too
+  if (n == 0) return;           // uniform
+  if (tid == 0) sh.cand_base = atomicAdd(&sx->ncand, n);
+  __syncthreads();
+  const uint32_t base = sh.cand_base;
+  uint32_t *cg = a.cand_g + (size_t)bh * CAND_CAP;
+  for (uint32_t i = tid; i < min(n, (uint32_t)CAND_CAP); i += SEL_THREADS)
+    if (base + i < (uint32_t)CAND_CAP) cg[base + i] = sh.cand[i];
 }
 
 // hardkv_sel_finish, grid (B*Hkv): the per-block counts and the candidates back into LDS,
@@ -1064,8 +1110,8 @@ hipError_t launch_flatten(const Args &a, hipStream_t s) {
 hipError_t launch_select(const Args &a, hipStream_t s) {
   static bool configured = false;  // the attributes are per function, set once per process
   if (!configured) {
-    const void *fs[] = {(const void *)hardkv_select, (const void *)hardkv_sel_weigh,
-                        (const void *)hardkv_sel_cut, (const void *)hardkv_sel_finish};
+    const void *fs[] = {(const void *)hardkv_select, (const void *)hardkv_sel_weigh, (const void *)hardkv_sel_cut,
+                        (const void *)hardkv_sel_count, (const void *)hardkv_sel_finish};
     for (const void *f : fs) {
       hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize,
                                          (int)sel_lds_bytes(MAX_POOL_BLOCKS));
@@ -1083,7 +1129,7 @@ hipError_t launch_select(const Args &a, hipStream_t s) {
   hipLaunchKernelGGL(hardkv_sel_cut, dim3(a.nbh), dim3(SEL_THREADS), sizeof(SelShared), s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(hardkv_sel_count, dim3(a.nsp, a.nbh), dim3(SEL_THREADS), 0, s, a);
+  hipLaunchKernelGGL(hardkv_sel_count, dim3(a.nsp, a.nbh), dim3(SEL_THREADS), sizeof(SelShared), s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(hardkv_sel_finish, dim3(a.nbh), dim3(SEL_THREADS), sel_lds_bytes(a.P), s, a);

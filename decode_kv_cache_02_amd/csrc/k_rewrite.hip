@@ -30,7 +30,9 @@ namespace {
 // ones through the pipeline below (which pays a prologue of its own).
 constexpr int PIPE_MIN_ROWS = 32;
 
-template <typename T, int G, bool MASK, bool COPY, bool ATTN>
+// STORE: whether the launch can write views at all (not under SPARSE, nor for the
+// attention-only gathers): without it the kernel keeps no registers for stores.
+template <typename T, int G, bool MASK, bool COPY, bool ATTN, bool STORE>
 __global__ __launch_bounds__(NTHREADS) void hardkv_rewrite(Args a) {
   constexpr int EB = Elem<T>::bytes;
   constexpr size_t ROWB = (size_t)HD * EB;
@@ -53,7 +55,7 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_rewrite(Args a) {
   // store the gathered rows into the view only when the head is rewritten this step; in
   // the standalone attention of a mixed policy, rewritten heads are attended from their
   // views by the tier kernel instead
-  const bool store = COPY && (a.gather_mode == GATHER_STEP || a.gather_mode == GATHER_REWRITE) && hd->rw;
+  const bool store = STORE && COPY && (a.gather_mode == GATHER_STEP || a.gather_mode == GATHER_REWRITE) && hd->rw;
   const bool skip = a.gather_mode == GATHER_ATTEND_NRW && hd->rw;
   const int64_t t = hd->t_plan, c = hd->c_plan;
   const uint32_t w_th = hd->w_th, r = hd->r;
@@ -174,7 +176,7 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_rewrite(Args a) {
     // The pipeline holds the next batch's keys beside this batch's probabilities: with
     // fp32 rows or 8 queries per group that costs a wave per SIMD, so only 16-bit rows
     // with up to 4 queries take it.
-    constexpr bool PIPE = Elem<T>::bytes == 2 && G <= 4;
+    constexpr bool PIPE = STORE && Elem<T>::bytes == 2 && G <= 4;
     if (!PIPE || ns <= PIPE_MIN_ROWS) {
       // a short list: batch by batch, each store waiting only for its own load
       for (int it = 0; it < ns; it += 16) {
@@ -184,10 +186,12 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_rewrite(Args a) {
           buf_load_nt(pk, so[j], kr[j]);
           buf_load_nt(pv, so[j], vr[j]);
         }
+        if constexpr (STORE) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          buf_store_nt(vk, dof[j], kr[j]);
-          buf_store_nt(vv, dof[j], vr[j]);
+          for (int j = 0; j < 4; ++j) {
+            buf_store_nt(vk, dof[j], kr[j]);
+            buf_store_nt(vv, dof[j], vr[j]);
+          }
         }
         if (ATTN) attn_rows<T, G, 4>(st, qs, kr, vr, ac);
       }
@@ -244,14 +248,14 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_rewrite(Args a) {
   if (ATTN) attn_write_partial<G>(st, a.part + ((size_t)bh * a.npart + pslot) * G * (2 + HD), s_part);
 }
 
-template <typename T, bool MASK, bool COPY, bool ATTN>
+template <typename T, bool MASK, bool COPY, bool ATTN, bool STORE>
 hipError_t launch_g(const Args &a, hipStream_t s) {
   dim3 grid(a.nch_reg + (ATTN && a.gather_mode == GATHER_STEP ? a.nc_att + a.nd_att : 0), a.nbh);
   switch (a.G) {
-    case 1: hipLaunchKernelGGL((hardkv_rewrite<T, 1, MASK, COPY, ATTN>), grid, dim3(NTHREADS), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((hardkv_rewrite<T, 2, MASK, COPY, ATTN>), grid, dim3(NTHREADS), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((hardkv_rewrite<T, 4, MASK, COPY, ATTN>), grid, dim3(NTHREADS), 0, s, a); break;
-    case 8: hipLaunchKernelGGL((hardkv_rewrite<T, 8, MASK, COPY, ATTN>), grid, dim3(NTHREADS), 0, s, a); break;
+    case 1: hipLaunchKernelGGL((hardkv_rewrite<T, 1, MASK, COPY, ATTN, STORE>), grid, dim3(NTHREADS), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((hardkv_rewrite<T, 2, MASK, COPY, ATTN, STORE>), grid, dim3(NTHREADS), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((hardkv_rewrite<T, 4, MASK, COPY, ATTN, STORE>), grid, dim3(NTHREADS), 0, s, a); break;
+    case 8: hipLaunchKernelGGL((hardkv_rewrite<T, 8, MASK, COPY, ATTN, STORE>), grid, dim3(NTHREADS), 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -259,10 +263,14 @@ hipError_t launch_g(const Args &a, hipStream_t s) {
 
 template <typename T>
 hipError_t launch_t(const Args &a, hipStream_t s, bool mask, bool copy, bool attend) {
-  if (mask && copy && attend) return launch_g<T, true, true, true>(a, s);
-  if (mask && !copy && !attend) return launch_g<T, true, false, false>(a, s);
-  if (!mask && copy && !attend) return launch_g<T, false, true, false>(a, s);
-  if (!mask && copy && attend) return launch_g<T, false, true, true>(a, s);
+  // the fused step writes views unless every head only gathers (SPARSE); the attention
+  // gathers never write them
+  if (mask && copy && attend)
+    return a.reg_policy == HARDKV_REG_SPARSE ? launch_g<T, true, true, true, false>(a, s)
+                                             : launch_g<T, true, true, true, true>(a, s);
+  if (mask && !copy && !attend) return launch_g<T, true, false, false, false>(a, s);
+  if (!mask && copy && !attend) return launch_g<T, false, true, false, true>(a, s);
+  if (!mask && copy && attend) return launch_g<T, false, true, true, false>(a, s);
   return hipErrorInvalidValue;
 }
 

@@ -333,6 +333,8 @@ ENTROPY_CASES = {
     "g1": dict(num_q_heads=2, num_kv_heads=2),
     "g8_batch8": dict(batch=8, num_q_heads=16, num_kv_heads=2, cond_mode=COND_MERGE, ctx_len=500, ctx_min=100),
     "heavy": dict(heavy=(0, 8), cond_mode=COND_MERGE),
+    # a ring of five slices: the split select reads the fitted slope
+    "split_long": dict(ctx_len=70000, ctx_min=60000, sparse_cap=69632, cond_mode=COND_MERGE),
 }
 
 

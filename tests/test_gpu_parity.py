@@ -81,6 +81,8 @@ SPLIT_CASES = {
     "split_condense": dict(pool_blocks=1024, sparse_cap=8192, ctx_len=60000, ctx_min=40000, cond_mode=COND_MERGE,
                            condensed_slots=64, dense_window=128),
     "split_evict_f32": dict(dtype="f32", pool_blocks=1030, sparse_cap=16384, ctx_len=30000, ctx_min=20000),
+    # nothing in the pool yet: no survivor mass, nothing to cut
+    "split_empty_pool": dict(pool_blocks=1100, sparse_cap=4096, ctx_len=20, ctx_min=0, dense_window=32),
 }
 
 

@@ -20,7 +20,9 @@ Timing:
     into one HIP graph and replayed once between two events; kernels that only read
     what earlier ones wrote are timed again on the post-step state.
   * The dominant kernel is the longest one that moves algorithmic bytes; those bytes
-    per launch over its duration give roofline.achieved.
+    per launch over its duration give roofline.achieved.  roofline.copy_reference is a
+    plain device copy of the same bytes timed in the same run: the rate a kernel that
+    reads and writes equally can practically reach on the box, beside the 8 TB/s peak.
   * Algorithmic bytes per step follow the byte model of the design notes and are
     computed from the per-unit pool sizes, budgets and condensed blocks of the
     timed steps, replayed eagerly from a snapshot after the timed region.
@@ -197,6 +199,29 @@ def time_repeatable_stage(layers, s, k, reps, eager):
         torch.cuda.synchronize()
         ts.append(e0.elapsed_time(e1))
     return float(np.median(ts)) * 1e3 / (reps * len(layers))
+
+
+def device_copy_reference(nbytes, reps=10):
+    """What a plain device copy moving the same bytes (half read, half written) achieves in
+    this run, in GB/s: the practical ceiling of a kernel that reads and writes equally,
+    beside the data-sheet peak."""
+    half = int(nbytes) // 2 // 16 * 16
+    if half <= 0:
+        return None
+    src = torch.empty(half, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    gbps = 2 * half * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"GBps": gbps, "frac": gbps / HBM_PEAK_GBPS, "what": "torch device copy of the same bytes, this run"}
 
 
 def unit_bytes(wl, N, kstar, E, t, c_occ, rw):
@@ -591,7 +616,8 @@ def main():
         "stage_algorithmic_bytes": {k: round(v) for k, v in bytes_step.items()},
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
-                     "bytes_per_launch": dom_bytes_launch, "us_per_launch": stage_us[dom]},
+                     "bytes_per_launch": dom_bytes_launch, "us_per_launch": stage_us[dom],
+                     "copy_reference": device_copy_reference(dom_bytes_launch)},
         "graph_replay_matches_eager": replay_matches,
     }
     if not args.no_cpu_baseline:

@@ -53,6 +53,20 @@ static int64_t pool_row(const orc_cfg *cfg, int64_t u, int64_t p) {
  * Each query-key logit is a dot product taken as a canonical pairwise tree:
  * products in index order, then level l+1 element i = level l [2i] + [2i+1].
  * ---------------------------------------------------------------------------------- */
+/* Sink prefix (a reading of the pages' "attention sinks" of the dense tier): the first S
+ * positions of a sequence stay in a tier of their own, attended at every step and never
+ * scored, condensed or rewritten.  The dense window then holds the W latest positions
+ * after them, [max(S, t - W), t), and the pool the positions between, [c, max(S, t - W)),
+ * its head c starting at S.  With S = 0 these are the plain windows. */
+static int64_t pool_end_of(const orc_cfg *cfg, int64_t t) {
+  const int64_t e = t - cfg->dense_window;
+  return e > cfg->sink ? e : cfg->sink;
+}
+static int64_t dense_lo_of(const orc_cfg *cfg, int64_t t) {
+  const int64_t lo = pool_end_of(cfg, t);
+  return lo < t ? lo : t;
+}
+
 float orc_dot_pairwise(const float *a, const float *b, int32_t n) {
   float lvl[1024];
   for (int i = 0; i < n; ++i) {
@@ -315,13 +329,14 @@ void orc_full_attention(const float *q, const float *k, const float *v, int32_t 
   attend_core(qd, D, n, flat_row, &c, out);
 }
 
-/* the tiers of one unit, in attention order: condensed slots with n > 0, view rows
- * r < k*, dense positions ascending (section 2.A: condensed, sparse, dense tiers) */
+/* the tiers of one unit, in attention order: sink positions (p < min(S, t)), condensed
+ * slots with n > 0, view rows r < k*, dense positions ascending (section 2.A:
+ * condensed, sparse, dense tiers) */
 typedef struct {
   const orc_cfg *cfg;
   const orc_state *st;
   int64_t u;
-  int64_t n_cond, n_view, n_dense, dense_lo;
+  int64_t n_sink, n_cond, n_view, n_dense, dense_lo;
   const int64_t *kept_rows;  /* pool rows of the kept positions, ascending; NULL: the view */
   int32_t slot[4096];
 } tier_ctx;
@@ -332,6 +347,17 @@ static void tier_row(const void *ctx, int64_t i, double *key, double *val, doubl
   const orc_cfg *cfg = tc->cfg;
   const orc_state *st = tc->st;
   int D = cfg->head_dim, eb = cfg->elem_bytes;
+  if (i < tc->n_sink) {
+    const int64_t row = tc->u * cfg->sink + i;
+    for (int d = 0; d < D; ++d) {
+      key[d] = (double)elem_get(st->sink_k, row * D + d, eb);
+      val[d] = (double)elem_get(st->sink_v, row * D + d, eb);
+    }
+    *bias = 0.0;
+    *hb = 0;
+    return;
+  }
+  i -= tc->n_sink;
   if (i < tc->n_cond) {
     int64_t s = tc->u * cfg->condensed_slots + tc->slot[i];
     double om = st->cond_omega[s];
@@ -379,7 +405,7 @@ int32_t orc_prefill(const orc_cfg *cfg, orc_state *st, const void *k_ctx, const 
   for (int b = 0; b < B; ++b) {
     int64_t L = ctx_len[b];
     if (L < 0 || L > max_len) return -1;
-    if (L - W + 1 > (int64_t)cfg->pool_blocks * BK) return -3;
+    if (L - W + 1 - cfg->sink > (int64_t)cfg->pool_blocks * BK) return -3;
   }
   st->error_word = 0;
   for (int b = 0; b < B; ++b) {
@@ -387,7 +413,7 @@ int32_t orc_prefill(const orc_cfg *cfg, orc_state *st, const void *k_ctx, const 
     st->seq_len[b] = L;
     for (int h = 0; h < H; ++h) {
       int64_t u = (int64_t)b * H + h;
-      st->pool_head[u] = 0;
+      st->pool_head[u] = cfg->sink;
       st->cond_cursor[u] = 0;
       for (int s = 0; s < C; ++s) {
         int64_t si = u * C + s;
@@ -398,12 +424,21 @@ int32_t orc_prefill(const orc_cfg *cfg, orc_state *st, const void *k_ctx, const 
       memset((char *)st->dense_k + u * W * D * eb, 0, (size_t)W * D * eb);
       memset((char *)st->dense_v + u * W * D * eb, 0, (size_t)W * D * eb);
       int64_t src0 = u * max_len;
-      int64_t lo = L > W ? L - W : 0;
+      const int64_t S = cfg->sink;
+      if (S > 0) {
+        memset((char *)st->sink_k + u * S * D * eb, 0, (size_t)S * D * eb);
+        memset((char *)st->sink_v + u * S * D * eb, 0, (size_t)S * D * eb);
+      }
+      for (int64_t p = 0; p < L && p < S; ++p) {
+        row_copy(st->sink_k, u * S + p, k_ctx, src0 + p, D, eb);
+        row_copy(st->sink_v, u * S + p, v_ctx, src0 + p, D, eb);
+      }
+      int64_t lo = dense_lo_of(cfg, L);
       for (int64_t p = lo; p < L; ++p) {
         row_copy(st->dense_k, u * W + p % W, k_ctx, src0 + p, D, eb);
         row_copy(st->dense_v, u * W + p % W, v_ctx, src0 + p, D, eb);
       }
-      for (int64_t p = 0; p < lo; ++p) {
+      for (int64_t p = S; p < lo; ++p) {
         row_copy(st->pool_k, pool_row(cfg, u, p), k_ctx, src0 + p, D, eb);
         row_copy(st->pool_v, pool_row(cfg, u, p), v_ctx, src0 + p, D, eb);
       }
@@ -418,13 +453,13 @@ int32_t orc_prefill(const orc_cfg *cfg, orc_state *st, const void *k_ctx, const 
 static uint32_t unit_step(const orc_cfg *cfg, orc_state *st, int b, int h, const void *q,
                           double *out, int do_attend) {
   const int H = cfg->num_kv_heads, Hq = cfg->num_q_heads, G = Hq / H, D = cfg->head_dim;
-  const int eb = cfg->elem_bytes, W = cfg->dense_window, P = cfg->pool_blocks;
+  const int eb = cfg->elem_bytes, P = cfg->pool_blocks;
   const int64_t u = (int64_t)b * H + h;
   uint32_t err = 0;
 
   const int64_t t = st->seq_len[b];
   const int64_t c = st->pool_head[u];
-  const int64_t pend = t > W ? t - W : 0;
+  const int64_t pend = pool_end_of(cfg, t);
   const int64_t N = pend - c;
 
   /* plan (section 2.A, tier 3): whole oldest blocks leave the pool once it holds
@@ -575,12 +610,13 @@ static uint32_t unit_step(const orc_cfg *cfg, orc_state *st, int b, int h, const
       if (st->cond_n[u * cfg->condensed_slots + s] > 0) tc->slot[tc->n_cond++] = s;
     tc->kept_rows = (rw && !packed) ? NULL : kept;
     tc->n_view = (rw && !packed) ? (kstar < cfg->view_cap ? kstar : cfg->view_cap) : kstar;
-    tc->dense_lo = t > W ? t - W : 0;
+    tc->dense_lo = dense_lo_of(cfg, t);
     tc->n_dense = t - tc->dense_lo;
+    tc->n_sink = t < cfg->sink ? t : cfg->sink;
     double qd[1024];
     for (int g = 0; g < G; ++g) {
       for (int d = 0; d < D; ++d) qd[d] = (double)qg[g * D + d];
-      attend_core(qd, D, tc->n_cond + tc->n_view + tc->n_dense, tier_row, tc,
+      attend_core(qd, D, tc->n_sink + tc->n_cond + tc->n_view + tc->n_dense, tier_row, tc,
                   out + ((int64_t)b * Hq + h * G + g) * D);
     }
     free(tc);
@@ -609,7 +645,13 @@ int32_t orc_step(const orc_cfg *cfg, orc_state *st, const void *q, const void *k
     const int64_t t = st->seq_len[b];
     for (int h = 0; h < H; ++h) {
       const int64_t u = (int64_t)b * H + h;
-      if (t >= W) {
+      const int64_t S = cfg->sink;
+      if (t < S) { /* a sink position */
+        row_copy(st->sink_k, u * S + t, k_new, u, D, eb);
+        row_copy(st->sink_v, u * S + t, v_new, u, D, eb);
+        continue;
+      }
+      if (t - W >= S) {
         const int64_t p = t - W; /* leaves the dense window, joins the pool tail */
         if (p + 1 - st->pool_head[u] > (int64_t)cfg->pool_blocks * BK) err |= ORC_ERR_POOL_OVERFLOW;
         row_copy(st->pool_k, pool_row(cfg, u, p), st->dense_k, u * W + p % W, D, eb);
@@ -641,7 +683,7 @@ int32_t orc_step(const orc_cfg *cfg, orc_state *st, const void *q, const void *k
       st->view_off[u] = (int32_t)off;
       if (!rw) continue;
       const int64_t t = st->seq_len[u / H];
-      const int64_t pend = t > W ? t - W : 0;
+      const int64_t pend = pool_end_of(cfg, t);
       const int64_t c0 = st->pool_head[u] - (int64_t)BK * st->n_condense[u];
       int64_t r = 0;
       for (int64_t j = c0; j < pend; ++j) {

@@ -56,6 +56,7 @@ typedef struct {
   int32_t view_total;        /* rows of the packed views (layout 1) */
   int32_t calibration;       /* 0: tau from tau[h]; 1: tau fitted per unit by entropy matching */
   const float *tau_unit;     /* [B*H] with calibration 1: use these instead of fitting (or NULL) */
+  int32_t sink;              /* S: the first S positions form a sink tier (multiple of 64, or 0) */
 } orc_cfg;
 
 typedef struct {
@@ -73,6 +74,7 @@ typedef struct {
   int32_t *view_off;         /* [B*H + 1] row offsets of the packed views (layout 1) */
   float *tau_fit;            /* [B*H] the temperature used (calibration 1; may be NULL) */
   uint32_t error_word;
+  void *sink_k, *sink_v;     /* [B*H][S][D]: position p < S in row p (S > 0) */
 } orc_state;
 
 /* building blocks, exported for the pin tests */

@@ -30,7 +30,7 @@ class OrcCfg(C.Structure):
         ("top_p", C.c_double), ("tau", C.POINTER(C.c_float)),
         ("regularize", C.c_int32), ("mti_lower", C.c_int32), ("mti_upper", C.c_int32),
         ("view_layout", C.c_int32), ("view_total", C.c_int32),
-        ("calibration", C.c_int32), ("tau_unit", C.POINTER(C.c_float)),
+        ("calibration", C.c_int32), ("tau_unit", C.POINTER(C.c_float)), ("sink", C.c_int32),
     ]
 
 
@@ -44,7 +44,7 @@ class OrcState(C.Structure):
         ("weights", C.c_void_p), ("mask", C.c_void_p), ("budget", C.c_void_p),
         ("n_condense", C.c_void_p), ("w_all", C.c_void_p), ("w_u", C.c_void_p),
         ("thresh", C.c_void_p), ("regularized", C.c_void_p), ("view_off", C.c_void_p),
-        ("tau_fit", C.c_void_p), ("error_word", C.c_uint32),
+        ("tau_fit", C.c_void_p), ("error_word", C.c_uint32), ("sink_k", C.c_void_p), ("sink_v", C.c_void_p),
     ]
 
 
@@ -208,11 +208,14 @@ class Oracle:
                           1 if merge_bias else 0, float(wl.top_p if top_p is None else top_p),
                           self.tau.ctypes.data_as(C.POINTER(C.c_float)), int(regularize),
                           int(mti_lower), int(mti_upper), int(view_layout), int(view_total),
-                          int(calibration), None)
+                          int(calibration), None, int(getattr(wl, "sink", 0)))
         self.tau_unit = None
         if tau_unit is not None:
             self.tau_unit = np.ascontiguousarray(np.asarray(tau_unit, np.float32).ravel())
             self.cfg.tau_unit = self.tau_unit.ctypes.data_as(C.POINTER(C.c_float))
+        S = int(getattr(wl, "sink", 0))
+        self.sink_k = np.zeros((B, H, max(S, 1), D), st)
+        self.sink_v = np.zeros((B, H, max(S, 1), D), st)
         self.dense_k = np.zeros((B, H, W, D), st)
         self.dense_v = np.zeros((B, H, W, D), st)
         self.pool_k = np.zeros((B, H, P, BK, D), st)
@@ -248,7 +251,7 @@ class Oracle:
             "dense_k", "dense_v", "pool_k", "pool_v", "view_k", "view_v", "view_pos", "cond_kn",
             "cond_vn", "cond_omega", "cond_n", "cond_cursor", "seq_len", "pool_head", "scores",
             "weights", "mask", "budget", "n_condense", "w_all", "w_u", "thresh", "regularized",
-            "view_off", "tau_fit")], 0)
+            "view_off", "tau_fit")], 0, _p(self.sink_k), _p(self.sink_v))
 
     @property
     def error_word(self) -> int:
@@ -280,7 +283,7 @@ class Oracle:
         P = self.wl.P_blk
         c = int(self.pool_head[b, h]) - BK * int(self.n_condense[b, h])  # pool head before condensing
         t = int(self.seq_len[b])
-        pend = max(0, t - self.wl.dense_window)
+        pend = max(int(getattr(self.wl, "sink", 0)), t - self.wl.dense_window)
         p = np.arange(c, pend, dtype=np.int64)
         words = self.mask[b, h][(p // BK) % P]
         bits = (words >> (p % BK).astype(np.uint64)) & np.uint64(1)

@@ -43,6 +43,7 @@ class Workload:
     heavy_scale: float = 4.0
     tau_gen: Optional[Tuple[float, float]] = None  # per-(b,h) query temperature, log-uniform
     seed: int = 0
+    sink: int = 0                      # S: sink prefix tokens (a multiple of 64, or 0)
     pool_blocks: Optional[int] = None  # P_blk; derived when None
     view_cap: Optional[int] = None     # V_cap; derived when None
     top_p_sweep: Tuple[float, ...] = field(default_factory=tuple)
@@ -65,10 +66,10 @@ class Workload:
         """
         if self.pool_blocks is not None:
             return self.pool_blocks
-        first = -(-(self.ctx_len - self.dense_window + 1) // BLOCK)
+        first = -(-(self.ctx_len - self.dense_window + 1 - self.sink) // BLOCK)
         steady = self.sparse_cap // BLOCK + 1
         if self.cond_mode == COND_OFF:
-            steady = -(-(self.ctx_len - self.dense_window + self.steps) // BLOCK) + 1
+            steady = -(-(self.ctx_len - self.dense_window + self.steps - self.sink) // BLOCK) + 1
         return max(first, steady, 1)
 
     @property

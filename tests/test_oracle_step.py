@@ -55,6 +55,77 @@ def test_p1_off_equals_full_attention(dtype):
                 np.testing.assert_allclose(full, ref, rtol=1e-12, atol=1e-13)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_sink_p1_off_equals_full_attention(dtype):
+    """A sink prefix of S = 64 with p = 1 and condensation off: sink rows, view rows and
+    the dense window hold every position once, in order, so the output equals full
+    attention over [0, t) bit for bit; the budget counts the pool alone, [S, t - W)."""
+    steps = 3
+    wl = tiny_workload(dtype=dtype, cond_mode=COND_OFF, top_p=1.0, steps=steps, sink=64)
+    inp = make_inputs(wl)
+    o, outs = _run(wl, inp, steps)
+    G = wl.group
+    for b in range(wl.batch):
+        for h in range(wl.num_kv_heads):
+            k, v = _positions_kv(inp, b, h, steps)
+            assert o.budget[b, h] == int(inp.ctx_len[b]) + steps - wl.dense_window - wl.sink
+            for g in range(G):
+                qh = h * G + g
+                full = orc.full_attention(_f32(inp.q[steps - 1, b, qh]), k, v)
+                assert np.array_equal(outs[-1][b, qh], full)
+
+
+def test_sink_tier_placement():
+    """Positions below S sit in the sink rows, from the context and from appends, and in
+    no other tier: the pool starts at S and the dense ring holds [max(S, t - W), t).
+    Contexts shorter than S grow across it."""
+    S, W, steps = 128, 32, 80
+    wl = tiny_workload(sink=S, dense_window=W, ctx_len=100, ctx_min=40, steps=steps, cond_mode=COND_MERGE,
+                       sparse_cap=128, condensed_slots=2)
+    inp = make_inputs(wl)
+    o = orc.Oracle(wl)
+    assert o.prefill(inp.k_ctx, inp.v_ctx, inp.ctx_len) == 0
+    for s in range(steps + 1):
+        for b in range(wl.batch):
+            t = int(o.seq_len[b])
+            L = int(inp.ctx_len[b])
+            for h in range(wl.num_kv_heads):
+                # keys of positions [0, t) in storage form
+                k = np.concatenate([orc._store_np(inp.k_ctx[b, h, :L]), orc._store_np(inp.k_new[:s, b, h])], 0)
+                n = min(S, t)
+                assert np.array_equal(o.sink_k[b, h, :n], k[:n])
+                assert int(o.pool_head[b, h]) >= S
+                lo = min(t, max(S, t - W))
+                for p in range(lo, t):
+                    assert np.array_equal(o.dense_k[b, h, p % W], k[p])
+        if s < steps:
+            o.step(inp.q[s], inp.k_new[s], inp.v_new[s])
+
+
+def test_sink_keeps_a_dominant_first_token():
+    """Position 0 carries a key that dominates every query and a distinct value.  Under
+    eviction with a small sparse cap it leaves the cache without a sink, and the output
+    moves away from its value; with S = 64 it stays, and the output is its value."""
+    wl = tiny_workload(cond_mode=COND_EVICT, sparse_cap=64, ctx_len=400, ctx_min=400, steps=2)
+    inp = make_inputs(wl)
+    q = inp.q.float()
+    q[..., 0] = 8.0
+    inp.q = q.to(inp.q.dtype)
+    k = inp.k_ctx.float()
+    k[:, :, 0] = 0.0
+    k[:, :, 0, 0] = 64.0
+    inp.k_ctx = k.to(inp.k_ctx.dtype)
+    v = inp.v_ctx.float()
+    v[:, :, 0] = 3.0
+    inp.v_ctx = v.to(inp.v_ctx.dtype)
+    res = {}
+    for S in (0, 64):
+        o, outs = _run(wl.with_(sink=S), inp, wl.steps)
+        res[S] = outs[-1]
+    assert np.abs(res[64] - 3.0).max() < 1e-3
+    assert np.abs(res[0] - 3.0).max() > 0.5
+
+
 def test_kappa_zero_closed_form():
     """tau -> inf makes every weight 2^24, so k* = ceil(p_q |U| / 65536) and the
     selection is the lowest positions of U (I6)."""

@@ -34,6 +34,7 @@ Timing:
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -75,6 +76,8 @@ def parse():
                     help="Flatten Index: view_cap rows per head (default) or packed in unit order")
     ap.add_argument("--view-total", type=int, default=0,
                     help="packed view rows for --view-layout sum (0: batch * kv_heads * view_cap)")
+    ap.add_argument("--sink", type=int, default=None,
+                    help="sink prefix tokens S (a multiple of 64; default: the workload's, 0)")
     ap.add_argument("--stage-reps", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-units", type=int, default=0, help="oracle sample size in units (0: automatic)")
@@ -229,14 +232,15 @@ def unit_bytes(wl, N, kstar, E, t, c_occ, rw):
 
     score: the pool keys; rewrite_attend: the kept rows read once, and written once for the
     heads that are rewritten (rw), the dense
-    window and the occupied condensed slots read, q in; condense (merge): the keys and
+    window, the sink rows and the occupied condensed slots read, q in; condense (merge): the keys and
     values of the condensing blocks read and the slot read-modify-write (eviction moves
     nothing); append: the leaving dense row read and written to the pool, the new token
     read and written to the dense window, keys and values; combine: the output.  The
     select stage only moves scores and weights (scratch), which the byte model does not
     count."""
-    e, G = wl.elem_bytes, wl.group
-    dense_rows = np.minimum(t, wl.dense_window)
+    e, G, S = wl.elem_bytes, wl.group, wl.sink
+    dense_rows = np.clip(t - S, 0, wl.dense_window)
+    sink_rows = np.minimum(t, S)
     merge = wl.cond_mode == COND_MERGE
     cond = (2 * e * D * 64 * E + 2 * (8 * D + 8) * np.minimum(E, wl.condensed_slots)) if merge else 0 * E
     return {
@@ -244,7 +248,7 @@ def unit_bytes(wl, N, kstar, E, t, c_occ, rw):
         "score": e * D * N,
         "select": 0 * N,
         "condense": cond,
-        "rewrite_attend": (2 + 2 * rw) * e * D * kstar + 2 * e * D * dense_rows + (8 * D + 8) * c_occ + G * D * e,
+        "rewrite_attend": (2 + 2 * rw) * e * D * kstar + 2 * e * D * (dense_rows + sink_rows) + (8 * D + 8) * c_occ + G * D * e,
         "combine": G * D * 4 * np.ones_like(N),
     }
 
@@ -258,7 +262,7 @@ def step_accounting(layers, s):
         t = L.st.seq_len.cpu().numpy().astype(np.int64)
         c = L.st.pool_head.cpu().numpy().astype(np.int64)
         t1 = (t + 1)[:, None]
-        N = np.maximum(0, t1 - wl.dense_window) - c
+        N = np.maximum(wl.sink, t1 - wl.dense_window) - c
         L.step(s)
         torch.cuda.synchronize()
         kstar = L.st.budget.cpu().numpy().astype(np.int64)
@@ -461,6 +465,8 @@ def main():
         copy_calibration(args.copy_calib)
         return
     wl = get_workload(args.config)
+    if args.sink is not None:
+        wl = dataclasses.replace(wl, sink=args.sink)
     top_p = args.top_p
     # single-step workloads: every timed step is the step from the prefilled context
     restore_mode = wl.steps == 1
@@ -601,7 +607,7 @@ def main():
         "config": {"workload": wl.name, "layers": wl.layers, "batch": wl.batch,
                    "ctx_len": wl.ctx_len, "ctx_min": wl.ctx_min, "q_heads": wl.num_q_heads,
                    "kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim, "dense_window": wl.dense_window,
-                   "sparse_cap": wl.sparse_cap, "condensed_slots": wl.condensed_slots,
+                   "sink": wl.sink, "sparse_cap": wl.sparse_cap, "condensed_slots": wl.condensed_slots,
                    "top_p": float(layers[0].cfg.c.top_p), "cond_mode": "merge",
                    "regularize": args.regularize if args.regularize != "mti" else
                    f"mti [{args.mti_lower}, {args.mti_upper}]",

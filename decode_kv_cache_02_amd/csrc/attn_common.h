@@ -192,7 +192,8 @@ HK_DEV void load_q_scaled(const Args &a, int b, int h, int sub, float (&qs)[G][8
 // Attention partial of segment `seg` of a head's tiers, written to its partial slot.
 // Segments [0, nv_att) are view rows (rv_att each, up to k*), then nc_att segments of
 // condensed slots (rc_att each, slots with n > 0 only), then nd_att segments of dense
-// positions (rd_att each, positions [max(0, t - W), t)).  A merged slot holding n tokens
+// positions (rd_att each, positions [max(S, t - W), t)), then ns_att segments of sink
+// positions (rs_att each, [0, min(S, t))).  A merged slot holding n tokens
 // enters with key Kn/Omega, value Vn/Omega and logit bias ln n (log2 n in base 2).
 template <typename T, int G>
 HK_DEV void attend_segment(const Args &a, int bh, int seg, float (*s_part)[G][2 + HD]) {
@@ -261,10 +262,10 @@ HK_DEV void attend_segment(const Args &a, int bh, int seg, float (*s_part)[G][2 
       }
       attn_row<G>(st, qs, kf, vf, inv, bias, act);
     }
-  } else {  // dense positions
+  } else if (seg < a.nv_att + a.nc_att + a.nd_att) {  // dense positions
     const int xd = seg - a.nv_att - a.nc_att;
     slot = a.part_cd_base + a.nc_att + xd;
-    const int64_t lo = t > a.W ? t - a.W : 0;
+    const int64_t lo = dense_lo_of(t, a.W, a.S);
     const int64_t p0 = lo + (int64_t)xd * a.rd_att, p1 = min(p0 + (int64_t)a.rd_att, t);
     const char *dk = (const char *)a.dense_k + (size_t)bh * a.W * ROWB + sub * 8 * EB;
     const char *dv = (const char *)a.dense_v + (size_t)bh * a.W * ROWB + sub * 8 * EB;
@@ -279,6 +280,29 @@ HK_DEV void attend_segment(const Args &a, int bh, int seg, float (*s_part)[G][2 
           const size_t row = (size_t)(p % a.W);
           raw_load_nt(dk + row * ROWB, kr[j]);
           raw_load_nt(dv + row * ROWB, vr[j]);
+        } else {
+          kr[j] = Raw8<T>{};
+          vr[j] = Raw8<T>{};
+        }
+      }
+      attn_rows<T, G, 2>(st, qs, kr, vr, act);
+    }
+  } else {  // sink positions [0, min(S, t)), row p of the head's sink rows
+    const int xs = seg - a.nv_att - a.nc_att - a.nd_att;
+    slot = a.part_cd_base + a.nc_att + a.nd_att + xs;
+    const int64_t p0 = (int64_t)xs * a.rs_att, p1 = min(min(p0 + (int64_t)a.rs_att, (int64_t)a.S), t);
+    const char *sk = (const char *)a.sink_k + (size_t)bh * a.S * ROWB + sub * 8 * EB;
+    const char *sv = (const char *)a.sink_v + (size_t)bh * a.S * ROWB + sub * 8 * EB;
+    for (int64_t base = p0; base < p1; base += 32) {
+      Raw8<T> kr[2], vr[2];
+      bool act[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int64_t p = base + j * 16 + rloc;
+        act[j] = p < p1;
+        if (act[j]) {
+          raw_load_nt(sk + (size_t)p * ROWB, kr[j]);
+          raw_load_nt(sv + (size_t)p * ROWB, vr[j]);
         } else {
           kr[j] = Raw8<T>{};
           vr[j] = Raw8<T>{};

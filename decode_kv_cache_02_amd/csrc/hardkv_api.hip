@@ -55,6 +55,7 @@ int32_t plan(const hardkv_config *cfg, Plan &p) {
   if (cfg->view_layout != HARDKV_VIEW_MAXLEN && cfg->view_layout != HARDKV_VIEW_SUM) return HARDKV_EINVAL;
   if (cfg->view_layout == HARDKV_VIEW_SUM && cfg->view_total < 0) return HARDKV_EINVAL;
   if (cfg->calibration != HARDKV_CAL_FIXED && cfg->calibration != HARDKV_CAL_ENTROPY) return HARDKV_EINVAL;
+  if (cfg->sink < 0 || cfg->sink % BK || cfg->sink > HARDKV_MAX_SINK) return HARDKV_EINVAL;
 
   a.B = cfg->batch;
   a.Hq = cfg->num_q_heads;
@@ -65,6 +66,7 @@ int32_t plan(const hardkv_config *cfg, Plan &p) {
   a.S_cap = cfg->sparse_cap;
   a.V_cap = cfg->view_cap;
   a.C = cfg->condensed_slots;
+  a.S = cfg->sink;
   a.mode = cfg->cond_mode;
   a.merge_bias = cfg->merge_bias ? 1 : 0;
   a.view_sum = cfg->view_layout == HARDKV_VIEW_SUM ? 1 : 0;
@@ -104,8 +106,10 @@ int32_t plan(const hardkv_config *cfg, Plan &p) {
   a.nc_att = (a.C + a.rc_att - 1) / a.rc_att;
   a.rd_att = 128;
   a.nd_att = (a.W + a.rd_att - 1) / a.rd_att;
+  a.rs_att = 128;
+  a.ns_att = (a.S + a.rs_att - 1) / a.rs_att;
   a.part_cd_base = std::max(a.nch_reg, a.nv_att);
-  a.xp_base = a.part_cd_base + a.nc_att + a.nd_att;  // then one slot per rewrite chunk
+  a.xp_base = a.part_cd_base + a.nc_att + a.nd_att + a.ns_att;  // then one slot per rewrite chunk
   a.npart = a.xp_base + a.nch_reg;
   if (a.mode == HARDKV_COND_MERGE) {
     const int emax = std::max(1, a.P - a.S_cap / BK);
@@ -176,6 +180,9 @@ int32_t bind(const hardkv_state *st, Plan &p) {
   a.view_off = st->view_off;
   if (st->tau_fit && ((uintptr_t)st->tau_fit & 3u)) return HARDKV_EINVAL;
   a.tau_fit = st->tau_fit;
+  if (a.S > 0 && (!aligned16(st->sink_k) || !aligned16(st->sink_v))) return HARDKV_EINVAL;
+  a.sink_k = st->sink_k;
+  a.sink_v = st->sink_v;
   a.error_word = st->error_word;
   char *ws = (char *)st->workspace;
   a.head = reinterpret_cast<HeadInfo *>(ws + p.off_head);
@@ -274,7 +281,7 @@ int32_t hardkv_prefill(const hardkv_config *cfg, hardkv_state *st, const void *k
   if (rc != HARDKV_OK) return rc;
   if (max_len < 0 || !ctx_len_dev || ((uintptr_t)ctx_len_dev & 7u)) return HARDKV_EINVAL;
   if (max_len > 0 && (!aligned16(k_ctx) || !aligned16(v_ctx))) return HARDKV_EINVAL;
-  if (max_len - cfg->dense_window + 1 > (int64_t)cfg->pool_blocks * BK) return HARDKV_ECAPACITY;
+  if (max_len - cfg->dense_window + 1 - cfg->sink > (int64_t)cfg->pool_blocks * BK) return HARDKV_ECAPACITY;
   p.a.k_ctx = k_ctx;
   p.a.v_ctx = v_ctx;
   p.a.ctx_len = ctx_len_dev;

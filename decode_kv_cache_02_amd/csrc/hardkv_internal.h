@@ -55,6 +55,7 @@ struct Args {
   float *out;
   // state
   void *dense_k, *dense_v, *pool_k, *pool_v, *view_k, *view_v;
+  void *sink_k, *sink_v;    // [BH][S][D] (S > 0)
   int32_t *view_pos;
   float *cond_kn, *cond_vn, *cond_omega;
   int32_t *cond_n, *cond_cursor;
@@ -86,12 +87,14 @@ struct Args {
   int64_t max_len;
   // sizes
   int B, Hq, Hkv, G, W, P, S_cap, V_cap, C, mode, merge_bias;
+  int S;                    // sink prefix tokens (0: none)
   int cb_score, nch_score;  // score: blocks per workgroup, workgroups per head
   int nsp;                  // select: slices per head (1: one workgroup does the whole select)
   int cb_reg, nch_reg;      // rewrite: blocks per workgroup, workgroups per head
   int rv_att, nv_att;       // attention over the view (standalone): rows per workgroup, count
   int rc_att, nc_att;       // attention over condensed slots
   int rd_att, nd_att;       // attention over the dense window
+  int rs_att, ns_att;       // attention over the sink rows
   int nvp;                  // view partial slots written by this call
   int npart, part_cd_base;  // partial slots per head; first condensed/dense slot
   int xp_base, nxp;         // gathered-row partial slots of the standalone attention
@@ -269,7 +272,13 @@ HK_DEV int xcd_swizzle(int lin, int total) {
   return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + k;
 }
 
-HK_DEV int64_t pool_end(int64_t t, int W) { return t > W ? t - W : 0; }
+// the pool ends where the dense window starts: max(S, t - W) with a sink prefix of S
+// tokens (the pool then starts at S); the dense window is [dense_lo, t)
+HK_DEV int64_t pool_end(int64_t t, int W, int S) { return t - W > S ? t - W : (int64_t)S; }
+HK_DEV int64_t dense_lo_of(int64_t t, int W, int S) {
+  const int64_t lo = pool_end(t, W, S);
+  return lo < t ? lo : t;
+}
 HK_DEV int64_t plan_E(int64_t N, int mode, int S_cap) {
   return (mode != HARDKV_COND_OFF && N > S_cap) ? (N - S_cap + BK - 1) / BK : 0;
 }

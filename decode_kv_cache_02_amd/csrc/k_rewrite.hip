@@ -60,7 +60,7 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_rewrite(Args a) {
   const int64_t t = hd->t_plan, c = hd->c_plan;
   const uint32_t w_th = hd->w_th, r = hd->r;
   const int nx = hd->E;
-  const int64_t pend = pool_end(t, a.W);
+  const int64_t pend = pool_end(t, a.W, a.S);
   const int nblk = (int)((pend + BK - 1) / BK - c / BK);
   const int pb_lo = (int)((c / BK) % P);
   // Chunks cover the survivor blocks [nx, nblk) (pool-relative block indices; the select
@@ -250,7 +250,7 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_rewrite(Args a) {
 
 template <typename T, bool MASK, bool COPY, bool ATTN, bool STORE>
 hipError_t launch_g(const Args &a, hipStream_t s) {
-  dim3 grid(a.nch_reg + (ATTN && a.gather_mode == GATHER_STEP ? a.nc_att + a.nd_att : 0), a.nbh);
+  dim3 grid(a.nch_reg + (ATTN && a.gather_mode == GATHER_STEP ? a.nc_att + a.nd_att + a.ns_att : 0), a.nbh);
   switch (a.G) {
     case 1: hipLaunchKernelGGL((hardkv_rewrite<T, 1, MASK, COPY, ATTN, STORE>), grid, dim3(NTHREADS), 0, s, a); break;
     case 2: hipLaunchKernelGGL((hardkv_rewrite<T, 2, MASK, COPY, ATTN, STORE>), grid, dim3(NTHREADS), 0, s, a); break;

@@ -93,7 +93,7 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_score(Args a) {
 
   const int64_t t = a.seq_len[b];
   const int64_t c = a.pool_head[bh];
-  const int64_t pend = pool_end(t, a.W);
+  const int64_t pend = pool_end(t, a.W, a.S);
   const int64_t row_lo = c + (int64_t)chunk * a.cb_score * BK;
   const int64_t row_hi = min(row_lo + (int64_t)a.cb_score * BK, pend);
 
@@ -369,7 +369,7 @@ HK_DEV SelGeo sel_geo(const Args &a, int bh) {
   const int b = bh / a.Hkv, h = bh - b * a.Hkv;
   g.t = a.seq_len[b];
   g.c = a.pool_head[bh];
-  g.pend = pool_end(g.t, a.W);
+  g.pend = pool_end(g.t, a.W, a.S);
   const int64_t N = g.pend - g.c;
   g.E = plan_E(N, a.mode, a.S_cap);
   g.u0 = g.c + (int64_t)BK * g.E;
@@ -941,7 +941,7 @@ __global__ __launch_bounds__(FIT_THREADS) void hardkv_fit(Args a) {
 
   const int64_t t = a.seq_len[b];
   const int64_t c = a.pool_head[bh];
-  const int64_t pend = pool_end(t, a.W);
+  const int64_t pend = pool_end(t, a.W, a.S);
   const int64_t N = pend - c;
 
   // the target entropy: each thread merges, per query, the pieces of chunks tid,

@@ -4,7 +4,9 @@
 // HARD-KV explainer, technical summary 2.A: the dense tier buffers the most recent
 // tokens in contiguous memory; tokens that age out of the dense window move to the
 // sparse tier.  The dense tier is a ring of W slots (position p in slot p mod W), the
-// sparse tier a ring of P blocks of 64 rows (position p in block (p / 64) mod P).
+// sparse tier a ring of P blocks of 64 rows (position p in block (p / 64) mod P).  With
+// a sink prefix of S tokens, positions below S go to the sink rows (row p) instead and
+// the dense window holds [max(S, t - W), t).
 #include "hardkv_internal.h"
 
 namespace hardkv {
@@ -24,9 +26,10 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_prefill(Args a) {
   const int W = a.W, P = a.P;
   const size_t ROWB = (size_t)HD * EB;
 
+  const int64_t dense_lo = dense_lo_of(L, W, a.S);
   if (x == (int)gridDim.x - 1) {
     if (tid == 0) {
-      a.pool_head[bh] = 0;
+      a.pool_head[bh] = a.S;
       a.cond_cursor[bh] = 0;
       if (h == 0) a.seq_len[b] = L;
       HeadInfo z = {};
@@ -40,18 +43,25 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_prefill(Args a) {
       a.cond_omega[(size_t)bh * a.C + k] = 0.0f;
       a.cond_n[(size_t)bh * a.C + k] = 0;
     }
-    // dense slots that hold no position yet (L < W)
+    // dense slots that hold no position of [dense_lo, L), and sink rows past L
     for (int64_t k = tid; k < (int64_t)W * CPR; k += NTHREADS) {
       const int64_t slot = k / CPR, piece = k % CPR;
-      if (slot >= L) {
+      if (((slot - dense_lo % W) + W) % W >= L - dense_lo) {
         const size_t off = ((size_t)bh * W + slot) * ROWB + piece * 16;
         *reinterpret_cast<uint4 *>((char *)a.dense_k + off) = uint4{0, 0, 0, 0};
         *reinterpret_cast<uint4 *>((char *)a.dense_v + off) = uint4{0, 0, 0, 0};
       }
     }
+    for (int64_t k = tid; k < (int64_t)a.S * CPR; k += NTHREADS) {
+      const int64_t row = k / CPR, piece = k % CPR;
+      if (row >= L) {
+        const size_t off = ((size_t)bh * a.S + row) * ROWB + piece * 16;
+        *reinterpret_cast<uint4 *>((char *)a.sink_k + off) = uint4{0, 0, 0, 0};
+        *reinterpret_cast<uint4 *>((char *)a.sink_v + off) = uint4{0, 0, 0, 0};
+      }
+    }
     return;
   }
-  const int64_t dense_lo = L > W ? L - W : 0;
   for (int k = tid; k < BK * CPR; k += NTHREADS) {
     const int64_t p = (int64_t)x * BK + k / CPR;
     const int piece = k % CPR;
@@ -59,7 +69,11 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_prefill(Args a) {
     const size_t src = ((size_t)bh * a.max_len + p) * ROWB + piece * 16;
     size_t dst;
     void *dk, *dv;
-    if (p >= dense_lo) {
+    if (p < a.S) {
+      dst = ((size_t)bh * a.S + (size_t)p) * ROWB + piece * 16;
+      dk = a.sink_k;
+      dv = a.sink_v;
+    } else if (p >= dense_lo) {
       dst = ((size_t)bh * W + (size_t)(p % W)) * ROWB + piece * 16;
       dk = a.dense_k;
       dv = a.dense_v;
@@ -74,8 +88,8 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_prefill(Args a) {
 }
 
 // grid B: one workgroup per sequence moves, for each KV head, position t - W from the
-// dense ring to the pool tail, writes the new token into its dense slot (the same slot),
-// and then advances t.
+// dense ring to the pool tail (when it is past the sink prefix), writes the new token
+// into its dense slot (the same slot) or, below S, into its sink row, and then advances t.
 template <typename T>
 __global__ __launch_bounds__(NTHREADS) void hardkv_append(Args a) {
   constexpr int EB = Elem<T>::bytes;
@@ -84,21 +98,28 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_append(Args a) {
   const int W = a.W, P = a.P, H = a.Hkv;
   const size_t ROWB = (size_t)HD * EB;
   const int64_t t = a.seq_len[b];
-  const int64_t p = t - W;  // leaves the window when t >= W
+  const int64_t p = t - W;          // leaves the window when it is past the sinks
+  const bool moves = p >= a.S;      // (and then t >= W)
+  const bool sink = t < a.S;        // the new token is a sink position
   for (int k = tid; k < H * 2 * CPR; k += NTHREADS) {
     const int h = k / (2 * CPR), rem = k % (2 * CPR);
     const int which = rem / CPR, piece = rem % CPR;
     const size_t bh = (size_t)b * H + h;
+    const char *src = (const char *)(which ? a.v_new : a.k_new) + bh * ROWB + piece * 16;
+    if (sink) {
+      char *srow = (char *)(which ? a.sink_v : a.sink_k) + (bh * a.S + (size_t)t) * ROWB + piece * 16;
+      *reinterpret_cast<uint4 *>(srow) = *reinterpret_cast<const uint4 *>(src);
+      continue;
+    }
     char *dense = (char *)(which ? a.dense_v : a.dense_k) + (bh * W + (size_t)(t % W)) * ROWB + piece * 16;
-    if (t >= W) {
+    if (moves) {
       char *pool = (char *)(which ? a.pool_v : a.pool_k) +
                    ((bh * P + (size_t)((p / BK) % P)) * BK + (size_t)(p % BK)) * ROWB + piece * 16;
       *reinterpret_cast<uint4 *>(pool) = *reinterpret_cast<const uint4 *>(dense);
     }
-    const char *src = (const char *)(which ? a.v_new : a.k_new) + bh * ROWB + piece * 16;
     *reinterpret_cast<uint4 *>(dense) = *reinterpret_cast<const uint4 *>(src);
   }
-  if (tid < H && t >= W) {
+  if (tid < H && moves) {
     const int64_t c = a.pool_head[(size_t)b * H + tid];
     if (p + 1 - c > (int64_t)P * BK) atomicOr(a.error_word, HARDKV_ERR_POOL_OVERFLOW);
   }

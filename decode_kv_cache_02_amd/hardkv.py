@@ -47,13 +47,15 @@ class hardkv_config(C.Structure):
         ("top_p", C.c_double), ("tau", C.POINTER(C.c_float)),
         ("regularize", C.c_int32), ("mti_lower", C.c_int32), ("mti_upper", C.c_int32),
         ("view_layout", C.c_int32), ("view_total", C.c_int32), ("calibration", C.c_int32),
+        ("sink", C.c_int32),
     ]
 
 
 _STATE_FIELDS = ("dense_k", "dense_v", "pool_k", "pool_v", "view_k", "view_v", "view_pos",
                  "cond_kn", "cond_vn", "cond_omega", "cond_n", "cond_cursor", "seq_len",
                  "pool_head", "scores", "weights", "mask", "budget", "n_condense", "w_all",
-                 "w_u", "thresh", "regularized", "view_off", "tau_fit", "error_word", "workspace")
+                 "w_u", "thresh", "regularized", "view_off", "tau_fit", "sink_k", "sink_v", "error_word",
+                 "workspace")
 
 
 class hardkv_state(C.Structure):
@@ -127,7 +129,7 @@ class Config:
                  tau: Sequence[float], head_dim: int = HEAD_DIM, merge_bias: bool = True,
                  regularize: int = HARDKV_REG_REWRITE, mti_lower: int = 0, mti_upper: int = 0,
                  view_layout: int = HARDKV_VIEW_MAXLEN, view_total: int = 0,
-                 calibration: int = HARDKV_CAL_FIXED):
+                 calibration: int = HARDKV_CAL_FIXED, sink: int = 0):
         self.tau_arr = (C.c_float * max(1, len(tau)))(*[float(x) for x in tau])
         self.c = hardkv_config(batch, num_q_heads, num_kv_heads, head_dim,
                                HARDKV_BF16 if dtype == "bf16" else HARDKV_F32, dense_window,
@@ -135,14 +137,15 @@ class Config:
                                1 if merge_bias else 0, float(top_p),
                                C.cast(self.tau_arr, C.POINTER(C.c_float)),
                                int(regularize), int(mti_lower), int(mti_upper),
-                               int(view_layout), int(view_total), int(calibration))
+                               int(view_layout), int(view_total), int(calibration), int(sink))
         self.dtype = dtype
 
     @classmethod
     def from_workload(cls, wl, top_p: Optional[float] = None, tau=None, cond_mode=None,
                       merge_bias: bool = True, regularize: int = HARDKV_REG_REWRITE,
                       mti_lower: int = 0, mti_upper: int = 0, view_layout: int = HARDKV_VIEW_MAXLEN,
-                      view_total: int = 0, calibration: int = HARDKV_CAL_FIXED) -> "Config":
+                      view_total: int = 0, calibration: int = HARDKV_CAL_FIXED,
+                      sink: Optional[int] = None) -> "Config":
         return cls(wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.dtype, wl.dense_window, wl.P_blk,
                    wl.sparse_cap, wl.V_cap, wl.condensed_slots,
                    wl.cond_mode if cond_mode is None else cond_mode,
@@ -150,7 +153,8 @@ class Config:
                    [wl.tau] * wl.num_kv_heads if tau is None else list(tau),
                    head_dim=wl.head_dim, merge_bias=merge_bias, regularize=regularize,
                    mti_lower=mti_lower, mti_upper=mti_upper, view_layout=view_layout,
-                   view_total=view_total, calibration=calibration)
+                   view_total=view_total, calibration=calibration,
+                   sink=int(getattr(wl, "sink", 0)) if sink is None else int(sink))
 
     def __getattr__(self, name):
         return getattr(self.__dict__["c"], name)
@@ -191,6 +195,8 @@ class State:
             self.view_pos = torch.full((B, H, V), -1, dtype=torch.int32, **kw)
         self.view_off = torch.zeros((B * H + 1,), dtype=torch.int32, **kw)
         self.tau_fit = torch.zeros((B, H), dtype=torch.float32, **kw)
+        self.sink_k = torch.zeros((B, H, max(1, c.sink), D), dtype=dt, **kw)  # sink position p in row p
+        self.sink_v = torch.zeros((B, H, max(1, c.sink), D), dtype=dt, **kw)
         self.cond_kn = torch.zeros((B, H, Cs, D), dtype=torch.float32, **kw)
         self.cond_vn = torch.zeros((B, H, Cs, D), dtype=torch.float32, **kw)
         self.cond_omega = torch.zeros((B, H, Cs), dtype=torch.float32, **kw)

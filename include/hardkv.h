@@ -39,7 +39,13 @@
  *      Vn += sum w_j/W_all v_j, Omega += sum w_j/W_all, n += 64.  c += 64 E.
  *   8. attend: softmax attention of each query over the condensed slots with
  *      n > 0 (key Kn/Omega, value Vn/Omega, logit bias ln n), the view rows
- *      r < k*, and the dense window.  Output in fp32.
+ *      r < k*, the dense window, and the sink rows.  Output in fp32.
+ * Sink tier (optional, cfg->sink = S > 0; a reading of the dense tier's role of
+ * preserving "attention sinks", 2.A): positions [0, S) are kept apart in the sink
+ * rows, attended at every step and never scored, condensed or rewritten.  Then the
+ * dense window holds [max(S, t - W), t), the pool [c, max(S, t - W)) with c starting
+ * at S, and an append below S writes the sink row instead; with S = 0 every range
+ * above is as written.
  * Steps 2-7 give bit-identical integer results (masks, budgets, indices, view
  * rows) to a plain CPU definition of the same step.
  *
@@ -127,6 +133,7 @@ typedef enum { HARDKV_CAL_FIXED = 0, HARDKV_CAL_ENTROPY = 1 } hardkv_calibration
 #define HARDKV_ERR_POOL_OVERFLOW 1u
 #define HARDKV_ERR_VIEW_OVERFLOW 2u
 #define HARDKV_ERR_NONFINITE 4u
+#define HARDKV_MAX_SINK 8192
 
 /* Host-side description of one layer; passed by pointer to every call. */
 typedef struct {
@@ -150,6 +157,8 @@ typedef struct {
   int32_t view_layout;     /* hardkv_view_layout (0: MAXLEN) */
   int32_t view_total;      /* rows of the packed views (layout SUM), >= 0 */
   int32_t calibration;     /* hardkv_calibration (0: FIXED) */
+  int32_t sink;            /* S: sink prefix tokens, a multiple of 64 in [0, HARDKV_MAX_SINK]
+                              (0: none); see the sink tier above */
 } hardkv_config;
 
 /* Device buffers of one layer.  All fixed capacity; 16-byte aligned.
@@ -180,6 +189,7 @@ typedef struct {
                                 total (written by select; may be NULL in the MAXLEN layout)       */
   float *tau_fit;            /* [B][Hkv]: the fitted temperature (calibration ENTROPY; may be NULL
                                 otherwise)                                                        */
+  void *sink_k, *sink_v;     /* e [B][Hkv][S][128]: sink position p in row p (may be NULL if S = 0) */
   uint32_t *error_word;      /* [1]: HARDKV_ERR_* bits, or-ed                                     */
   void *workspace;           /* hardkv_workspace_size() bytes, zero-filled before first use      */
   size_t workspace_bytes;
@@ -189,9 +199,10 @@ typedef struct {
 int32_t hardkv_workspace_size(const hardkv_config *cfg, size_t *bytes);
 
 /* Places a context: k_ctx/v_ctx are e [B][Hkv][max_len][128] (device), ctx_len_dev is
- * int64 [B] (device) with 0 <= L_b <= max_len.  The last min(L_b, W) positions go to the
- * dense ring, [0, L_b - W) to the pool; t = L_b, c = 0, condensed tier emptied, cursor 0.
- * HARDKV_ECAPACITY if max_len - W + 1 > P*64 (the first append would not fit). */
+ * int64 [B] (device) with 0 <= L_b <= max_len.  Positions below S go to the sink rows,
+ * [max(S, L_b - W), L_b) to the dense ring and the rest to the pool; t = L_b, c = S,
+ * condensed tier emptied, cursor 0.
+ * HARDKV_ECAPACITY if max_len - W + 1 - S > P*64 (the first append would not fit). */
 int32_t hardkv_prefill(const hardkv_config *cfg, hardkv_state *st, const void *k_ctx,
                        const void *v_ctx, const int64_t *ctx_len_dev, int64_t max_len, void *stream);
 

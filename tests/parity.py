@@ -128,6 +128,9 @@ class Pair:
             "seq_len", "budget", "n_condense", "cond_cursor", "pool_head", "w_all", "w_u", "thresh",
             "regularized", "error_word")}
         big_names = ["scores", "weights", "mask", "cond_n", "cond_kn", "cond_vn", "cond_omega"]
+        S = int(getattr(wl, "sink", 0))
+        if S > 0:
+            big_names += ["sink_k", "sink_v"]
         if check_views and not self.packed:
             big_names += ["view_pos", "view_k", "view_v"]
         full = None
@@ -149,7 +152,7 @@ class Pair:
                     gv = int(small[name][b, h].numpy().view(np.uint64))
                     assert gv == int(getattr(o, name)[ob, oh]), f"{tag} {name}"
                 t = int(small["seq_len"][b])
-                pend = max(0, t - wl.dense_window)
+                pend = max(S, t - wl.dense_window)
                 c0 = int(pre[key][ob, oh])
                 pos = np.arange(c0, pend)
                 rows = (pos // 64) % P * 64 + pos % 64
@@ -172,6 +175,10 @@ class Pair:
                     assert np.array_equal(g["view_pos"].numpy()[:kv], o.view_pos[ob, oh][:kv]), f"{tag} view_pos"
                     assert np.array_equal(raw(g["view_k"][:kv]), o.view_k[ob, oh][:kv]), f"{tag} view_k"
                     assert np.array_equal(raw(g["view_v"][:kv]), o.view_v[ob, oh][:kv]), f"{tag} view_v"
+                if S > 0:  # the sink rows that hold a position
+                    ns = min(S, t)
+                    assert np.array_equal(raw(g["sink_k"][:ns]), o.sink_k[ob, oh][:ns]), f"{tag} sink_k"
+                    assert np.array_equal(raw(g["sink_v"][:ns]), o.sink_v[ob, oh][:ns]), f"{tag} sink_v"
                 assert np.array_equal(g["cond_n"].numpy(), o.cond_n[ob, oh]), f"{tag} cond_n"
                 on = o.cond_n[ob, oh] > 0
                 if on.any():
@@ -229,7 +236,7 @@ def check_layer_properties(pr: Pair) -> None:
     w = st.weights.reshape(BH, P * 64).long() & 0xFFFFFFFF
     t = st.seq_len.repeat_interleave(H).long()
     c = st.pool_head.reshape(BH).long()               # after condensation: first survivor
-    pend = torch.clamp(t - wl.dense_window, min=0)
+    pend = torch.clamp(t - wl.dense_window, min=int(getattr(wl, "sink", 0)))
     ring = torch.arange(P * 64, device=dev)
     pb_lo = (c // 64) % P
     blk_off = (ring[None, :] // 64 - pb_lo[:, None]) % P

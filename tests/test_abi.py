@@ -67,6 +67,9 @@ def _cfg(**over):
     (dict(calibration=2), hk.HARDKV_EINVAL),
     (dict(regularize=hk.HARDKV_REG_MTI, mti_lower=-1, mti_upper=5), hk.HARDKV_EINVAL),
     (dict(regularize=hk.HARDKV_REG_MTI, mti_lower=10, mti_upper=5), hk.HARDKV_EINVAL),
+    (dict(sink=32), hk.HARDKV_EINVAL),                # not a multiple of 64
+    (dict(sink=-64), hk.HARDKV_EINVAL),
+    (dict(sink=8192 + 64), hk.HARDKV_EINVAL),          # above HARDKV_MAX_SINK
 ])
 def test_config_validation(over, code):
     cfg = _cfg(**over)
@@ -108,10 +111,11 @@ def _fake_state(cfg, ws_bytes=None, misalign=None, null=None):
 
 @_no_gpu
 @pytest.mark.parametrize("kind", ["null_pool", "misaligned_view", "misaligned_error", "misaligned_regularized",
-                                  "small_ws"])
+                                  "small_ws", "null_sink"])
 def test_state_validation(kind):
-    cfg = _cfg()
+    cfg = _cfg(sink=64) if kind == "null_sink" else _cfg()
     st = {"null_pool": lambda: _fake_state(cfg, null="pool_k"),
+          "null_sink": lambda: _fake_state(cfg, null="sink_v"),
           "misaligned_view": lambda: _fake_state(cfg, misalign="view_k"),
           "misaligned_error": lambda: _fake_state(cfg, misalign="error_word"),
           "misaligned_regularized": lambda: _fake_state(cfg, misalign="regularized"),

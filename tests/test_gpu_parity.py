@@ -387,3 +387,53 @@ def test_entropy_calibration_parity(name, fused):
     pre = {None: o.pool_head.copy()}
     outs = pr.oracle_step()
     pr.compare(pre, outs)
+
+
+# ---- sink prefix: the first S positions kept apart and attended every step ----------------
+SINK_CASES = {
+    "sink_merge": (dict(sink=64, cond_mode=COND_MERGE, ctx_len=500, ctx_min=100, steps=3), 0),
+    # contexts of 190, 134, 198, 112, 160 (= S + W) and 127 tokens: below S, between S and
+    # S + W, and beyond; the last crosses S on its first append
+    "sink_cross": (dict(batch=6, sink=128, ctx_len=200, ctx_min=100, dense_window=32, seed=6, steps=12), 0),
+    "sink_evict_f32": (dict(dtype="f32", sink=192, ctx_len=700, ctx_min=500, sparse_cap=128,
+                            condensed_slots=2, steps=2), 0),
+    "sink_g8_sparse": (dict(num_q_heads=16, num_kv_heads=2, sink=64, cond_mode=COND_MERGE, steps=2), 1),
+    "sink_max": (dict(sink=8192, ctx_len=9000, ctx_min=8100, steps=2), 0),
+    # a ring of five slices: the split select starts its geometry at S
+    "sink_split": (dict(sink=256, pool_blocks=1100, sparse_cap=4096, ctx_len=3000, ctx_min=2000,
+                        cond_mode=COND_MERGE, steps=2), 0),
+}
+
+
+@pytest.mark.parametrize("name", list(SINK_CASES))
+@pytest.mark.parametrize("fused", [True, False])
+def test_sink_parity(name, fused):
+    """With a sink prefix the pool starts at S, appends below S land in the sink rows, and
+    attention covers the sinks beside the other tiers: every state array, the sink rows and
+    the attention output match the oracle."""
+    from parity import Pair
+    kw, pol = SINK_CASES[name]
+    kw = dict(kw)
+    steps = kw.pop("steps")
+    wl = tiny_workload(steps=steps, **kw)
+    print(f"case {name} fused={fused}: policy {pol}, {wl}", flush=True)
+    pr = Pair(wl, regularize=pol)
+    for _ in range(steps):
+        pr.step(fused=fused)
+
+
+@pytest.mark.parametrize("name", ["sink_merge", "sink_cross"])
+def test_sink_attend_sparse_and_packed(name):
+    """The sink tier under the standalone sparse attention and under packed views."""
+    from parity import Pair
+    kw, _ = SINK_CASES[name]
+    kw = dict(kw)
+    steps = kw.pop("steps")
+    wl = tiny_workload(steps=steps, **kw)
+    pr = Pair(wl)
+    for _ in range(steps):
+        pr.step(fused=False, sparse_attend=True)
+    total = wl.batch * wl.num_kv_heads * wl.V_cap
+    pr = Pair(wl, view_layout=1, view_total=total)
+    for _ in range(steps):
+        pr.step(fused=True)

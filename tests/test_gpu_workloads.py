@@ -52,6 +52,17 @@ def test_c2_full_layer():
         check_layer_properties(pr)
 
 
+def test_c2_sink_prefix():
+    """The same layer with the first 1024 positions kept as a sink tier: every unit."""
+    from parity import Pair, check_layer_properties
+    wl = get_workload("c2").with_(steps=2, sink=1024)
+    print("workload", wl.name, "sink", wl.sink, flush=True)
+    pr = Pair(wl)
+    for _ in range(wl.steps):
+        pr.step()
+        check_layer_properties(pr)
+
+
 @pytest.mark.parametrize("p", [0.8, 0.9, 0.99])
 def test_c3_mixed_lengths(p):
     """Batch 64, lengths 8k..32k, 0..64 heavy keys per head, the first step condenses up

@@ -325,10 +325,19 @@ def summarize_kernels(src, dst, cmds, title):
     print(open(dst).read())
 
 
-def summarize_traffic(fetch_csv, write_csv, cal_fetch_csv, cal_write_csv, calib_mib, wl, cmds):
+def run_options(args, wl):
+    """The options that change what the kernels of a run do: counter traffic taken under
+    one set of them is reported only for runs with the same set."""
+    return {"top_p": args.top_p, "regularize": args.regularize,
+            "mti": [args.mti_lower, args.mti_upper] if args.regularize == "mti" else None,
+            "calibration": args.calibration, "view_layout": args.view_layout,
+            "view_total": args.view_total if args.view_layout == "sum" else None, "sink": wl.sink}
+
+
+def summarize_traffic(fetch_csv, write_csv, cal_fetch_csv, cal_write_csv, calib_mib, wl, cmds, options):
     """Per kernel: the counter's KiB per dispatch, averaged over the run's dispatches and
     scaled by what it reads for a plain device copy of calib_mib MiB (read and written
-    once)."""
+    once).  The counter runs are taken with the options given here (run_options)."""
     import csv
     import collections
 
@@ -357,7 +366,8 @@ def summarize_traffic(fetch_csv, write_csv, cal_fetch_csv, cal_write_csv, calib_
     rec[wl.name] = {st: {"fetch_bytes_per_launch": e.get("FETCH_SIZE", 0.0),
                          "write_bytes_per_launch": e.get("WRITE_SIZE", 0.0),
                          "hbm_bytes_per_launch": e.get("FETCH_SIZE", 0.0) + e.get("WRITE_SIZE", 0.0),
-                         "launches": e["launches"], "sources": KERNEL_SOURCES, "source_digest": digest}
+                         "launches": e["launches"], "sources": KERNEL_SOURCES, "source_digest": digest,
+                         "options": options}
                     for st, e in res.items()}
     with open(path, "w") as f:
         json.dump(rec, f, indent=1, sort_keys=True)
@@ -387,9 +397,9 @@ def source_digest(files):
     return h.hexdigest()[:16]
 
 
-def load_traffic(kernel, workload):
+def load_traffic(kernel, workload, options):
     """HBM bytes per launch measured by the counter runs kept under profiles/, if they were
-    taken on the current kernel sources."""
+    taken on the current kernel sources with the same run options."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
@@ -399,6 +409,8 @@ def load_traffic(kernel, workload):
     if not ent:
         return None
     if ent.get("source_digest") != source_digest(ent.get("sources", [])):
+        return None
+    if ent.get("options") != options:
         return None
     return ent.get("hbm_bytes_per_launch")
 
@@ -457,7 +469,10 @@ def main():
         summarize_kernels(*args.summarize_kernels, args.cmd, f"Kernel trace, workload {get_workload(args.config).name}")
         return
     if args.summarize_traffic:
-        summarize_traffic(*args.summarize_traffic, args.copy_calib or 1024, get_workload(args.config), args.cmd)
+        wl = get_workload(args.config)
+        if args.sink is not None:
+            wl = dataclasses.replace(wl, sink=args.sink)
+        summarize_traffic(*args.summarize_traffic, args.copy_calib or 1024, wl, args.cmd, run_options(args, wl))
         return
     hk.require_gpu()
     torch.cuda.set_device(0)
@@ -588,7 +603,7 @@ def main():
     dom = max((k for k in stage_us if bytes_step[k] > 0), key=stage_us.get)
     dom_bytes_launch = bytes_step[dom] / len(layers)
     achieved = dom_bytes_launch / (stage_us[dom] * 1e-6) / 1e9
-    traffic = load_traffic(dom, wl.name)
+    traffic = load_traffic(dom, wl.name, run_options(args, wl))
 
     steps_per_s = 1e3 / ms_per_step
     res = {

@@ -28,6 +28,7 @@ int32_t plan(const hardkv_config *cfg, Plan &p) {
   memset(&a, 0, sizeof(a));
   if (cfg->batch < 1 || cfg->num_kv_heads < 1 || cfg->num_q_heads < 1) return HARDKV_EINVAL;
   if (cfg->num_kv_heads > HARDKV_MAX_KV_HEADS) return HARDKV_EUNSUPPORTED;
+  if ((int64_t)cfg->batch * cfg->num_kv_heads > HARDKV_MAX_UNITS) return HARDKV_EUNSUPPORTED;
   if (cfg->num_q_heads % cfg->num_kv_heads) return HARDKV_EINVAL;
   const int G = cfg->num_q_heads / cfg->num_kv_heads;
   if (G != 1 && G != 2 && G != 4 && G != 8) return HARDKV_EUNSUPPORTED;

@@ -15,7 +15,7 @@ constexpr int NCOEFF = 10;    // Taylor coefficients of 2^f on [0, 1)
 constexpr int NTHREADS = 256; // threads per workgroup of every kernel
 constexpr int NB1 = 3073;     // level-1 buckets of the mass radix select (key >> 16)
 constexpr int SEL_THREADS = 1024;     // threads of the select workgroup (one per head)
-constexpr int MAX_POOL_BLOCKS = 6144; // pool ring blocks per head the select LDS can index
+constexpr int MAX_POOL_BLOCKS = HARDKV_MAX_POOL_BLOCKS; // pool ring blocks per head the select LDS can index
 constexpr int CAND_CAP = 8192;        // cut-bucket candidates resolved in LDS
 constexpr int SEL_SLICE_BLOCKS = 256; // pool blocks per workgroup when a head's select is split
 constexpr int SEL_SPLIT_MIN = 4;      // slices per head from which the select is split

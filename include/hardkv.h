@@ -134,16 +134,19 @@ typedef enum { HARDKV_CAL_FIXED = 0, HARDKV_CAL_ENTROPY = 1 } hardkv_calibration
 #define HARDKV_ERR_VIEW_OVERFLOW 2u
 #define HARDKV_ERR_NONFINITE 4u
 #define HARDKV_MAX_SINK 8192
+#define HARDKV_MAX_UNITS 65535     /* batch * num_kv_heads (one launch row per unit) */
+#define HARDKV_MAX_POOL_BLOCKS 6144 /* pool ring blocks per unit the select can index */
 
 /* Host-side description of one layer; passed by pointer to every call. */
 typedef struct {
-  int32_t batch;           /* B >= 1 */
+  int32_t batch;           /* B >= 1; B * Hkv <= HARDKV_MAX_UNITS (else HARDKV_EUNSUPPORTED) */
   int32_t num_q_heads;     /* Hq */
   int32_t num_kv_heads;    /* Hkv, 1..64; G = Hq / Hkv in {1, 2, 4, 8} */
   int32_t head_dim;        /* D, must be 128 */
   int32_t dtype;           /* storage and compute type of q, K, V: HARDKV_BF16 or HARDKV_F32 */
   int32_t dense_window;    /* W >= 1 */
-  int32_t pool_blocks;     /* P: pool ring blocks of 64 rows per (b, h); P*64 >= sparse_cap + 64 */
+  int32_t pool_blocks;     /* P: pool ring blocks of 64 rows per (b, h); P*64 >= sparse_cap + 64;
+                              P <= HARDKV_MAX_POOL_BLOCKS (else HARDKV_EUNSUPPORTED) */
   int32_t sparse_cap;      /* S_cap: multiple of 64, >= 64 */
   int32_t view_cap;        /* V_cap >= sparse_cap (>= P*64 in mode OFF) */
   int32_t condensed_slots; /* C >= 1 */

@@ -60,6 +60,8 @@ def _cfg(**over):
     (dict(cond_mode=5), hk.HARDKV_EINVAL),
     (dict(dtype=7), hk.HARDKV_EINVAL),
     (dict(num_kv_heads=65, num_q_heads=65), hk.HARDKV_EUNSUPPORTED),
+    (dict(batch=8192, num_kv_heads=8, num_q_heads=32), hk.HARDKV_EUNSUPPORTED),   # 65536 units
+    (dict(pool_blocks=6145, view_cap=6145 * 64), hk.HARDKV_EUNSUPPORTED),
     (dict(dense_window=0), hk.HARDKV_EINVAL),
     (dict(regularize=3), hk.HARDKV_EINVAL),
     (dict(view_layout=2), hk.HARDKV_EINVAL),
@@ -75,6 +77,15 @@ def test_config_validation(over, code):
     cfg = _cfg(**over)
     n = C.c_size_t(0)
     assert hk.lib().hardkv_workspace_size(C.byref(cfg.c), C.byref(n)) == code
+
+
+def test_unit_limit_is_inclusive():
+    """B * Hkv = HARDKV_MAX_UNITS is accepted, one more is not."""
+    cfg = _cfg(batch=65535, num_kv_heads=1, num_q_heads=4)
+    n = C.c_size_t(0)
+    assert hk.lib().hardkv_workspace_size(C.byref(cfg.c), C.byref(n)) == hk.HARDKV_OK
+    cfg = _cfg(batch=65536, num_kv_heads=1, num_q_heads=4)
+    assert hk.lib().hardkv_workspace_size(C.byref(cfg.c), C.byref(n)) == hk.HARDKV_EUNSUPPORTED
 
 
 def test_bad_tau_and_null_config():

@@ -18,7 +18,8 @@ bool aligned16(const void *p) { return p != nullptr && ((uintptr_t)p & 15u) == 0
 
 struct Plan {
   Args a;
-  size_t off_head, off_cmax, off_ent, off_blkinfo, off_part, off_phist, off_psum, off_selh, off_cand, ws_bytes;
+  size_t off_head, off_cmax, off_ent, off_blkinfo, off_part, off_phist, off_psum, off_selh, off_cand, off_kx,
+      ws_bytes;
 };
 
 // Checks the configuration and derives every size; fills the size fields of p.a.
@@ -135,7 +136,8 @@ int32_t plan(const hardkv_config *cfg, Plan &p) {
   p.off_psum = align256(p.off_phist + split * (size_t)BH * a.nsp * NB1 * sizeof(unsigned long long));
   p.off_selh = align256(p.off_psum + split * (size_t)BH * a.nsp * 2 * sizeof(unsigned long long));
   p.off_cand = align256(p.off_selh + split * (size_t)BH * sizeof(SelHead));
-  p.ws_bytes = align256(p.off_cand + split * (size_t)BH * CAND_CAP * sizeof(uint32_t));
+  p.off_kx = align256(p.off_cand + split * (size_t)BH * CAND_CAP * sizeof(uint32_t));
+  p.ws_bytes = align256(p.off_kx + (size_t)BH * sizeof(uint32_t));
   return HARDKV_OK;
 }
 
@@ -195,6 +197,7 @@ int32_t bind(const hardkv_state *st, Plan &p) {
   a.psum = reinterpret_cast<unsigned long long *>(ws + p.off_psum);
   a.selh = reinterpret_cast<SelHead *>(ws + p.off_selh);
   a.cand_g = reinterpret_cast<uint32_t *>(ws + p.off_cand);
+  a.kx = reinterpret_cast<uint32_t *>(ws + p.off_kx);
   return HARDKV_OK;
 }
 

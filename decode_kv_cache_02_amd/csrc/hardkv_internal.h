@@ -81,6 +81,8 @@ struct Args {
   unsigned long long *psum;   // [BH][nsp][2] (pool mass, survivor mass) of each slice
   SelHead *selh;              // [BH]
   uint32_t *cand_g;           // [BH][CAND_CAP] candidates of the cut bucket
+  uint32_t *kx;       // [BH] nonzero once a 16-bit key outside KEY_SAFE has entered the head's
+                      // pool (since its prefill): its scores then take the unfused products
   // prefill
   const void *k_ctx, *v_ctx;
   const int64_t *ctx_len;
@@ -139,6 +141,25 @@ hipError_t launch_combine(const Args &a, hipStream_t s);
 // device helpers
 // ---------------------------------------------------------------------------------------
 #define HK_DEV __device__ __forceinline__
+
+// Magnitudes for which every product of a 16-bit query element and a 16-bit key element
+// is exact in fp32 (KEY_SAFE: biased exponent in [64, 192), |k| in [2^-63, 2^65); the
+// query: |q| in [2^-72, 2^62); zeros always).  A product of two 8-bit significands has at
+// most 16 significant bits, its lowest at 2^(eq + ek - 14) >= 2^-149, and it stays below
+// 2^127.  With exact products, fl(fl(q0 k0) + fl(q1 k1)) equals fma(q0, k0, fl(q1 k1)).
+constexpr uint32_t KEY_EXP_LO = 64, KEY_EXP_HI = 192;
+constexpr float Q_SAFE_LO = 0x1p-72f, Q_SAFE_HI = 0x1p62f;
+
+// whether a 32-bit word holds a nonzero 16-bit key element outside KEY_SAFE
+HK_DEV bool key_word_unsafe(uint32_t w) {
+  const uint32_t e0 = (w >> 7) & 0xFFu, e1 = (w >> 23) & 0xFFu;
+  const bool b0 = (w & 0x7FFFu) != 0u && (e0 < KEY_EXP_LO || e0 >= KEY_EXP_HI);
+  const bool b1 = (w & 0x7FFF0000u) != 0u && (e1 < KEY_EXP_LO || e1 >= KEY_EXP_HI);
+  return b0 || b1;
+}
+HK_DEV bool key_piece_unsafe(const uint4 &x) {
+  return key_word_unsafe(x.x) || key_word_unsafe(x.y) || key_word_unsafe(x.z) || key_word_unsafe(x.w);
+}
 
 HK_DEV float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 

@@ -14,7 +14,10 @@
 //   wavefront covers 4 rows per load.  Each lane forms the pairwise sum of its 8
 //   products in registers (tree levels 1-3); levels 4-7 are DPP exchanges inside the
 //   16-lane row, so every lane ends with the exact root.  The score is the max over the
-//   group queries.  Writes the scores and the chunk's maximum.
+//   group queries.  Writes the scores and the chunk's maximum.  With 16-bit elements
+//   every product is exact unless an element is tiny or huge; while the head's pool
+//   holds no such key and the queries none either, a level-1 node is one fused
+//   multiply-add (the same value, a fifth fewer vector instructions per row).
 //
 // hardkv_select, grid (B*Hkv), 1024 threads: one workgroup per head.  Pass A turns the
 //   scores into integer weights and builds a mass histogram of the survivors on the top
@@ -32,6 +35,8 @@
 //   histogram and masses to memory), hardkv_sel_cut (per head: the cut bucket),
 //   hardkv_sel_count (pass B per slice: per-block counts, the bucket's tokens through a
 //   counter) and hardkv_sel_finish (per head: the same ending as the one-workgroup kernel).
+#include <type_traits>
+
 #include "hardkv_internal.h"
 
 namespace hardkv {
@@ -40,11 +45,36 @@ namespace {
 
 constexpr int UNR = 2;  // row groups (16 rows) per batch of loads
 
-// score of one row from this lane's 8 elements: pairwise tree over the 128 products
+// score of one row from this lane's 8 elements: pairwise tree over the 128 products.
+// bf16 pairs widened by byte permutes: (b1 b0 0 0) and (b3 b2 0 0)
+HK_DEV void raw_to_f_perm(const Raw8<BF16> &r, float (&f)[8]) {
+  const uint32_t w[4] = {r.v.x, r.v.y, r.v.z, r.v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = __uint_as_float(__builtin_amdgcn_perm(0u, w[i], 0x01000c0cu));
+    f[2 * i + 1] = __uint_as_float(__builtin_amdgcn_perm(0u, w[i], 0x03020c0cu));
+  }
+}
+HK_DEV void raw_to_f_perm(const Raw8<F32> &r, float (&f)[8]) { raw_to_f(r, f); }
+
+// FUSED (only when every product is exact: 16-bit operands inside the safe magnitudes):
+// a level-1 node fl(fl(q0 k0) + fl(q1 k1)) is then one fused multiply-add on fl(q1 k1).
+template <bool FUSED>
 HK_DEV float dot_tree(const float (&q)[8], const float (&k)[8]) {
-  float p0 = q[0] * k[0], p1 = q[1] * k[1], p2 = q[2] * k[2], p3 = q[3] * k[3];
-  float p4 = q[4] * k[4], p5 = q[5] * k[5], p6 = q[6] * k[6], p7 = q[7] * k[7];
-  float a0 = p0 + p1, a1 = p2 + p3, a2 = p4 + p5, a3 = p6 + p7;
+  float a0, a1, a2, a3;
+  if (FUSED) {
+    a0 = __builtin_fmaf(q[0], k[0], q[1] * k[1]);
+    a1 = __builtin_fmaf(q[2], k[2], q[3] * k[3]);
+    a2 = __builtin_fmaf(q[4], k[4], q[5] * k[5]);
+    a3 = __builtin_fmaf(q[6], k[6], q[7] * k[7]);
+  } else {
+    float p0 = q[0] * k[0], p1 = q[1] * k[1], p2 = q[2] * k[2], p3 = q[3] * k[3];
+    float p4 = q[4] * k[4], p5 = q[5] * k[5], p6 = q[6] * k[6], p7 = q[7] * k[7];
+    a0 = p0 + p1;
+    a1 = p2 + p3;
+    a2 = p4 + p5;
+    a3 = p6 + p7;
+  }
   float b0 = a0 + a1, b1 = a2 + a3;
   float c = b0 + b1;                 // level 3: node `sub` of 16
   c = c + dpp<DPP_XOR1>(c);          // level 4: nodes (2i, 2i+1) in lanes (2i, 2i+1)
@@ -103,6 +133,24 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_score(Args a) {
     const char *qb = (const char *)a.q + (((int64_t)b * a.Hq + (int64_t)h * G) * HD + sub * 8) * EB;
 #pragma unroll
     for (int g = 0; g < G; ++g) load8(qb + (size_t)g * HD * EB, qf[g], T{});
+    // exact products: 16-bit elements, no key outside the safe magnitudes in the pool,
+    // and every query element zero or inside them (the same in every wavefront); decided
+    // once the first keys are in flight, so that the wait for q does not delay them.
+    // With eight queries the second tree would cost the kernel a wavefront per SIMD.
+    constexpr bool CAN_FUSE = EB == 2 && G <= 4;
+    bool exact_products = false;
+    auto decide = [&]() {
+      bool q_ok = true;
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float x = fabsf(qf[g][i]);
+          q_ok &= x == 0.0f || (x >= Q_SAFE_LO && x < Q_SAFE_HI);
+        }
+      exact_products =
+          CAN_FUSE && __builtin_amdgcn_readfirstlane((int)(a.kx[bh] == 0u && ballot(!q_ok) == 0ull)) != 0;
+    };
     const BufRes kb = make_buf((const char *)a.pool_k + (size_t)bh * P * BK * HD * EB, (uint64_t)P * BK * HD * EB);
     const uint32_t lane_b = (uint32_t)(sub * 8 * EB);  // the lane's 8 elements of a row
     float *srow = a.scores + (size_t)bh * P * BK;
@@ -130,22 +178,37 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_score(Args a) {
         }
       }
     };
-    auto score = [&](const Raw8<T> (&buf)[UNR][4], int g0) {
+    // The group's max dot of a row, and the dot of query `sub` (lanes sub < G).  FUSED
+    // (exact products): no infinities or NaNs can arise either, so the max may be the
+    // hardware max (its choice between +0 and -0 vanishes in s + 0 below).
+    auto group_dots = [&](const float (&kf)[8], float &dmine, auto fused) {
+      constexpr bool FUSED = decltype(fused)::value;
+      float s = dot_tree<FUSED>(qf[0], kf);
+      dmine = s;
+#pragma unroll
+      for (int g = 1; g < G; ++g) {
+        float d = dot_tree<FUSED>(qf[g], kf);
+        if (ENT && g == sub) dmine = d;
+        s = FUSED ? __builtin_fmaxf(s, d) : (d > s ? d : s);
+      }
+      return s;
+    };
+    auto score_with = [&](Raw8<T> (&buf)[UNR][4], int g0, auto fused) {
 #pragma unroll
       for (int u = 0; u < UNR; ++u) {
         const int gi = g0 + 4 * u;  // rows past the chunk are zeros, scored but not kept
 #pragma unroll
         for (int l = 0; l < 4; ++l) {
+          // The plain tree's rows widen through byte permutes, the fused tree's through
+          // shifts: the same values, but not code the compiler would hoist above the
+          // choice of tree (all the batch's widened rows would then be live at once).
           float kf[8];
-          raw_to_f(buf[u][l], kf);
-          float s = dot_tree(qf[0], kf);
-          float dmine = s;  // the dot of query `sub` (lanes sub < G)
-#pragma unroll
-          for (int g = 1; g < G; ++g) {
-            float d = dot_tree(qf[g], kf);
-            if (ENT && g == sub) dmine = d;
-            s = d > s ? d : s;
-          }
+          if (CAN_FUSE && !decltype(fused)::value)
+            raw_to_f_perm(buf[u][l], kf);
+          else
+            raw_to_f(buf[u][l], kf);
+          float dmine;
+          float s = group_dots(kf, dmine, fused);
           const int rel = gi * 16 + l * 4 + grp;
           if (ENT && sub < G && rel < nrows) ent_merge(em, ez, ew, dmine * c2, 1.0f, 0.0f);
           s = s + 0.0f;  // a zero score is +0
@@ -156,15 +219,23 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_score(Args a) {
         }
       }
     };
+    // a uniform choice: a scalar branch per batch
+    auto score = [&](Raw8<T> (&buf)[UNR][4], int g0) {
+      if (exact_products)
+        score_with(buf, g0, std::true_type{});
+      else
+        score_with(buf, g0, std::false_type{});
+    };
     constexpr int STEP = 4 * UNR;
     // The wavefront's nb batches, two per trip with no exit inside the trip, and issues
     // that are unconditional (a batch past the chunk reads nothing): every path into the
     // loop head then has the same loads in flight, so the wait before scoring a batch
     // counts only that batch's loads.
-    Raw8<T> bufA[UNR][4], bufB[UNR][4];
     const int nb = wave < ngroups ? (ngroups - 1 - wave) / STEP + 1 : 0;
+    Raw8<T> bufA[UNR][4], bufB[UNR][4];
     int g0 = wave;
     issue(bufA, g0);
+    decide();
     for (int i = 0; i + 2 <= nb; i += 2) {
       issue(bufB, g0 + STEP);
       score(bufA, g0);

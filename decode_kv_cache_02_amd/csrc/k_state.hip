@@ -13,6 +13,13 @@ namespace hardkv {
 
 namespace {
 
+// grid (ceil(B*Hkv / 256)): clears each head's flag of keys outside the range where the
+// score's products are exact; the placement below and every append set it again.
+__global__ __launch_bounds__(NTHREADS) void hardkv_prefill_clear(Args a) {
+  const int i = blockIdx.x * NTHREADS + threadIdx.x;
+  if (i < a.B * a.Hkv) a.kx[i] = 0u;
+}
+
 // grid (ceil(max_len / 64) + 1, B*Hkv): blocks of 64 context positions, then one
 // workgroup per head that resets the head's counters and condensed tier.
 template <typename T>
@@ -82,8 +89,10 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_prefill(Args a) {
       dk = a.pool_k;
       dv = a.pool_v;
     }
-    *reinterpret_cast<uint4 *>((char *)dk + dst) = *reinterpret_cast<const uint4 *>((const char *)a.k_ctx + src);
+    const uint4 kp = *reinterpret_cast<const uint4 *>((const char *)a.k_ctx + src);
+    *reinterpret_cast<uint4 *>((char *)dk + dst) = kp;
     *reinterpret_cast<uint4 *>((char *)dv + dst) = *reinterpret_cast<const uint4 *>((const char *)a.v_ctx + src);
+    if (EB == 2 && dk == a.pool_k && key_piece_unsafe(kp)) atomicOr(&a.kx[bh], 1u);
   }
 }
 
@@ -115,7 +124,9 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_append(Args a) {
     if (moves) {
       char *pool = (char *)(which ? a.pool_v : a.pool_k) +
                    ((bh * P + (size_t)((p / BK) % P)) * BK + (size_t)(p % BK)) * ROWB + piece * 16;
-      *reinterpret_cast<uint4 *>(pool) = *reinterpret_cast<const uint4 *>(dense);
+      const uint4 x = *reinterpret_cast<const uint4 *>(dense);
+      *reinterpret_cast<uint4 *>(pool) = x;
+      if (EB == 2 && !which && key_piece_unsafe(x)) atomicOr(&a.kx[bh], 1u);
     }
     *reinterpret_cast<uint4 *>(dense) = *reinterpret_cast<const uint4 *>(src);
   }
@@ -130,6 +141,7 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_append(Args a) {
 }  // namespace
 
 hipError_t launch_prefill(const Args &a, hipStream_t s, bool bf16) {
+  hipLaunchKernelGGL(hardkv_prefill_clear, dim3((a.B * a.Hkv + NTHREADS - 1) / NTHREADS), dim3(NTHREADS), 0, s, a);
   dim3 grid((unsigned)((a.max_len + BK - 1) / BK) + 1, a.B * a.Hkv);
   if (bf16)
     hipLaunchKernelGGL((hardkv_prefill<BF16>), grid, dim3(NTHREADS), 0, s, a);

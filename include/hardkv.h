@@ -63,7 +63,11 @@
  *     pool ring overflowed; only possible in mode OFF), HARDKV_ERR_VIEW_OVERFLOW,
  *     HARDKV_ERR_NONFINITE (a non-finite score; outputs are then undefined).
  *   - The workspace must be zero-filled once before first use; the kernels leave
- *     its counters at zero after each call.
+ *     its counters at zero after each call.  It belongs to its state: besides
+ *     per-call scratch it keeps, per (b, h), whether a key whose products with a
+ *     query could round in fp32 (a nonzero 16-bit element of magnitude below 2^-63
+ *     or from 2^65) has entered the pool since the prefill; hardkv_prefill and
+ *     hardkv_append keep it, so a state's pool is filled only through them.
  *   - Calls on one state must not overlap (they share the workspace).
  */
 #ifndef HARDKV_H

@@ -437,3 +437,67 @@ def test_sink_attend_sparse_and_packed(name):
     pr = Pair(wl, view_layout=1, view_total=total)
     for _ in range(steps):
         pr.step(fused=True)
+
+
+# ---- products that round in fp32: the score keeps the plain tree ---------------------------
+# With 16-bit queries and keys the score kernel fuses each level-1 node into one multiply-add
+# when no product can round (every element zero or of a magnitude whose products are exact).
+# Each case plants in row `pos` of unit (0, 0) and in the group's queries two elements whose
+# first product rounds (below the subnormal grid, or past the largest float), chosen so that
+# the fused node would differ from fl(fl(q0 k0) + fl(q1 k1)).
+ROUNDING_CASES = {
+    # a key below 2^-63: q0 k0 = (1 + 2^-4 + 2^-10) 2^-149, q1 k1 = 2^-125 (a tie in the sum)
+    "key_tiny": ([(1 + 2 ** -5) * 2.0 ** -60, 2.0 ** -60], [(1 + 2 ** -5) * 2.0 ** -89, 2.0 ** -65]),
+    # a query element below 2^-72, keys in range
+    "query_tiny": ([(1 + 2 ** -5) * 2.0 ** -86, 2.0 ** -62], [(1 + 2 ** -5) * 2.0 ** -63, 2.0 ** -63]),
+}
+
+
+def _planted(wl, qv, kv, pos):
+    from synth import make_inputs
+    inp = make_inputs(wl)
+    dt = inp.q.dtype
+    q = torch.zeros(wl.head_dim, dtype=torch.float64)
+    k = torch.zeros(wl.head_dim, dtype=torch.float64)
+    q[:len(qv)] = torch.tensor(qv, dtype=torch.float64)
+    k[:len(kv)] = torch.tensor(kv, dtype=torch.float64)
+    assert torch.equal(q.to(dt).double(), q) and torch.equal(k.to(dt).double(), k)
+    inp.q[0, 0, :wl.group] = q.to(dt)
+    inp.k_ctx[0, 0, pos] = k.to(dt)
+    return inp
+
+
+@pytest.mark.parametrize("name", list(ROUNDING_CASES))
+@pytest.mark.parametrize("where", ["prefill", "append"])
+def test_rounding_products_keep_the_plain_tree(name, where):
+    """The planted row's score is the plain tree's (bit-exact with the oracle) whether the
+    key entered the pool at the prefill or through the step's append."""
+    from parity import Pair
+    qv, kv = ROUNDING_CASES[name]
+    p0 = np.float64(qv[0]) * np.float64(kv[0])
+    p1 = np.float32(np.float64(qv[1]) * np.float64(kv[1]))
+    assert np.float32(np.float32(p0) + p1) != np.float32(p0 + np.float64(p1))  # the case bites
+    wl = tiny_workload(steps=1)
+    L0 = int(__import__("synth").make_inputs(wl).ctx_len[0])
+    pos = 3 if where == "prefill" else L0 - wl.dense_window  # the row the first append moves
+    pr = Pair(wl, inputs=_planted(wl, qv, kv, pos).to("cuda"))
+    pr.step()
+
+
+def test_overflowing_product_keeps_the_plain_tree():
+    """A key past 2^65 whose product overflows: the plain tree's score is +inf (and the
+    non-finite bit is set) where a fused node would have stayed finite."""
+    from parity import Pair
+    qv, kv = [1.5 * 2.0 ** 61, -1.5 * 2.0 ** 61], [2.0 ** 67, 2.0 ** 66]
+    wl = tiny_workload(steps=1)
+    pr = Pair(wl, inputs=_planted(wl, qv, kv, 3).to("cuda"))
+    o = pr.orcs[None][0]
+    c0 = int(o.pool_head[0, 0])
+    pr.step(check=False)
+    t = int(o.seq_len[0])
+    pos = np.arange(c0, t - wl.dense_window)
+    rows = (pos // 64) % wl.P_blk * 64 + pos % 64
+    g = pr.st.scores[0, 0].cpu().numpy()[rows].view(np.uint32)
+    assert np.array_equal(g, o.scores[0, 0][rows].view(np.uint32))
+    assert np.isposinf(o.scores[0, 0][3])
+    assert int(pr.st.error_word[0].item()) & 4 and o.error_word & 4

@@ -19,7 +19,7 @@ bool aligned16(const void *p) { return p != nullptr && ((uintptr_t)p & 15u) == 0
 struct Plan {
   Args a;
   size_t off_head, off_cmax, off_ent, off_blkinfo, off_part, off_phist, off_psum, off_selh, off_cand, off_kx,
-      ws_bytes;
+      off_fith, off_fitp, ws_bytes;
 };
 
 // Checks the configuration and derives every size; fills the size fields of p.a.
@@ -123,6 +123,13 @@ int32_t plan(const hardkv_config *cfg, Plan &p) {
   // the select of a long pool is split over slices of SEL_SLICE_BLOCKS blocks
   a.nsp = (a.P + SEL_SLICE_BLOCKS - 1) / SEL_SLICE_BLOCKS;
   if (a.nsp < SEL_SPLIT_MIN) a.nsp = 1;
+  // The entropy fit of long pools is split over slices of FIT_SPLIT_ROWS rows when the
+  // heads alone would leave half the chip's 256 compute units idle (one workgroup per
+  // head spends most of the fit on its own vector ALUs); otherwise its six extra launches
+  // cost more than they save.
+  a.nfs = 1;
+  if (a.calibration && BH * 2 <= 256 && (int64_t)a.P * BK >= FIT_SPLIT_MIN_ROWS)
+    a.nfs = (int)(((int64_t)a.P * BK + FIT_SPLIT_ROWS - 1) / FIT_SPLIT_ROWS);
   a.bh0 = 0;
   a.nbh = (int)BH;
 
@@ -137,7 +144,10 @@ int32_t plan(const hardkv_config *cfg, Plan &p) {
   p.off_selh = align256(p.off_psum + split * (size_t)BH * a.nsp * 2 * sizeof(unsigned long long));
   p.off_cand = align256(p.off_selh + split * (size_t)BH * sizeof(SelHead));
   p.off_kx = align256(p.off_cand + split * (size_t)BH * CAND_CAP * sizeof(uint32_t));
-  p.ws_bytes = align256(p.off_kx + (size_t)BH * sizeof(uint32_t));
+  p.off_fith = align256(p.off_kx + (size_t)BH * sizeof(uint32_t));
+  const size_t fsplit = a.nfs > 1 ? 1 : 0;  // the split fit's scratch
+  p.off_fitp = align256(p.off_fith + fsplit * (size_t)BH * sizeof(FitHead));
+  p.ws_bytes = align256(p.off_fitp + fsplit * (size_t)FIT_ROUNDS * BH * a.nfs * 2 * FIT_POINTS * sizeof(double));
   return HARDKV_OK;
 }
 
@@ -198,6 +208,8 @@ int32_t bind(const hardkv_state *st, Plan &p) {
   a.selh = reinterpret_cast<SelHead *>(ws + p.off_selh);
   a.cand_g = reinterpret_cast<uint32_t *>(ws + p.off_cand);
   a.kx = reinterpret_cast<uint32_t *>(ws + p.off_kx);
+  a.fith = reinterpret_cast<FitHead *>(ws + p.off_fith);
+  a.fitp = reinterpret_cast<double *>(ws + p.off_fitp);
   return HARDKV_OK;
 }
 

@@ -31,6 +31,20 @@ struct alignas(128) SelHead {
 };
 static_assert(offsetof(SelHead, ncand) == 64, "ncand on its own line");
 
+// Entropy fit of the calibration temperature: rounds of a grid on log2 tau.
+constexpr int FIT_POINTS = 17;          // grid points per round (16 intervals)
+constexpr int FIT_ROUNDS = 5;
+constexpr int FIT_SPLIT_ROWS = 4096;    // pool rows per workgroup when a head's fit is split
+constexpr int FIT_SPLIT_MIN_ROWS = 8 * FIT_SPLIT_ROWS;  // pool capacity from which it may be
+
+// Per-head values that the split fit passes between its kernels.
+struct FitHead {
+  double H;                                   // target entropy (nats)
+  float m;                                    // max score
+  int32_t pad_;
+  double lo[FIT_ROUNDS], hi[FIT_ROUNDS];      // bracket of each round (log2 tau)
+};
+
 // Per-head plan of the current step, written by the select kernel and read by the
 // kernels after it (rewrite, condense), so that they see the pool as select saw it.
 struct alignas(64) HeadInfo {
@@ -81,6 +95,8 @@ struct Args {
   unsigned long long *psum;   // [BH][nsp][2] (pool mass, survivor mass) of each slice
   SelHead *selh;              // [BH]
   uint32_t *cand_g;           // [BH][CAND_CAP] candidates of the cut bucket
+  FitHead *fith;      // [BH] split fit: target, max, brackets
+  double *fitp;       // [FIT_ROUNDS][BH][nfs][2 * FIT_POINTS] split fit: each slice's sums
   uint32_t *kx;       // [BH] nonzero once a 16-bit key outside KEY_SAFE has entered the head's
                       // pool (since its prefill): its scores then take the unfused products
   // prefill
@@ -92,6 +108,7 @@ struct Args {
   int S;                    // sink prefix tokens (0: none)
   int cb_score, nch_score;  // score: blocks per workgroup, workgroups per head
   int nsp;                  // select: slices per head (1: one workgroup does the whole select)
+  int nfs;                  // entropy fit: slices per head (1: one workgroup does the whole fit)
   int cb_reg, nch_reg;      // rewrite: blocks per workgroup, workgroups per head
   int rv_att, nv_att;       // attention over the view (standalone): rows per workgroup, count
   int rc_att, nc_att;       // attention over condensed slots

@@ -981,10 +981,10 @@ __global__ __launch_bounds__(SEL_THREADS) void hardkv_flatten(Args a) {
 // ---------------------------------------------------------------------------------------
 // calibration temperature fitted by entropy
 // ---------------------------------------------------------------------------------------
-constexpr int FIT_POINTS = 17;  // grid points per round (16 intervals)
-constexpr int FIT_ROUNDS = 5;
 constexpr int FIT_THREADS = 512;  // 2 waves per SIMD: the 3 x 17 per-candidate values stay in registers
 constexpr int FIT_NW = FIT_THREADS / 64;
+constexpr int FIT_UNR = 8;          // score loads in flight per thread
+constexpr float FIT_FAR = 1.0e30f;  // distance below the max of a padding row (times any slope: finite)
 
 HK_DEV double shfl_xor_d(double v, int off) {
   const uint64_t u = __double_as_longlong(v);
@@ -992,33 +992,20 @@ HK_DEV double shfl_xor_d(double v, int off) {
   return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
 }
 
-// hardkv_fit, grid (B*Hkv), 512 threads: one workgroup per head.  The target is the mean
-// over the group's queries of the entropy (nats) of their raw attention over the pool,
-// from the per-chunk softmax pieces the score kernel left; then five rounds of a 17-point
-// grid on log2 tau in [-12, 12] find the bracket where the entropy of the calibrated
-// softmax(s / (sqrt(D) tau)) over the pool reaches the target (it grows with tau); tau
-// is the midpoint of the last bracket.
-__global__ __launch_bounds__(FIT_THREADS) void hardkv_fit(Args a) {
-  const int bh = a.bh0 + blockIdx.x;
-  const int b = bh / a.Hkv;
+// The target entropy (nats) of head bh: the mean over the group's queries of the entropy
+// of their raw attention over the pool, merged from the per-chunk softmax pieces the
+// score kernel left; and the head's max score.  Every thread gets both.
+HK_DEV void fit_target(const Args &a, int bh, double &H, float &m) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int P = a.P, G = a.G;
-  __shared__ double s_acc[FIT_NW][2 * FIT_POINTS];
-  __shared__ float s_ck[FIT_POINTS];
-  __shared__ int s_reach[FIT_POINTS];
-  __shared__ double s_h;
-  __shared__ float s_m;
-  __shared__ double s_lo, s_hi;
-
-  const int64_t t = a.seq_len[b];
-  const int64_t c = a.pool_head[bh];
-  const int64_t pend = pool_end(t, a.W, a.S);
-  const int64_t N = pend - c;
-
-  // the target entropy: each thread merges, per query, the pieces of chunks tid,
-  // tid + FIT_THREADS, ...; then the lanes of a wavefront, then the wavefronts
+  const int G = a.G;
   __shared__ float s_piece[FIT_NW][8][3];
+  __shared__ double s_hq[8];
+  __shared__ float s_mx[FIT_NW];
+  __shared__ double s_H;
+  __shared__ float s_m;
   {
+    // each thread merges, per query, the pieces of chunks tid, tid + FIT_THREADS, ...;
+    // then the lanes of a wavefront, then the wavefronts
     float pm[8], pz[8], pw[8];
 #pragma unroll
     for (int g = 0; g < 8; ++g) {
@@ -1046,102 +1033,246 @@ __global__ __launch_bounds__(FIT_THREADS) void hardkv_fit(Args a) {
       }
     }
   }
-  __syncthreads();
-  if (tid < G) {
-    float m = s_piece[0][tid][0], z = s_piece[0][tid][1], w = s_piece[0][tid][2];
-    for (int wv = 1; wv < FIT_NW; ++wv) ent_merge(m, z, w, s_piece[wv][tid][0], s_piece[wv][tid][1], s_piece[wv][tid][2]);
-    const double hbits = z > 0.0f ? log2((double)z) - (double)w / (double)z : 0.0;
-    s_acc[0][tid] = hbits * 0.69314718055994530942;  // nats
-  }
   float mx = -INFINITY;
   for (int i = tid; i < a.nch_score; i += FIT_THREADS) mx = fmaxf(mx, a.cmax[(size_t)bh * a.nch_score + i]);
   mx = wave_max(mx);
-  if (lane == 0) s_acc[1][wave] = (double)mx;
+  if (lane == 0) s_mx[wave] = mx;
+  __syncthreads();
+  if (tid < G) {
+    float m1 = s_piece[0][tid][0], z = s_piece[0][tid][1], w = s_piece[0][tid][2];
+    for (int wv = 1; wv < FIT_NW; ++wv)
+      ent_merge(m1, z, w, s_piece[wv][tid][0], s_piece[wv][tid][1], s_piece[wv][tid][2]);
+    const double hbits = z > 0.0f ? log2((double)z) - (double)w / (double)z : 0.0;
+    s_hq[tid] = hbits * 0.69314718055994530942;  // nats
+  }
   __syncthreads();
   if (tid == 0) {
     double h = 0.0;
-    for (int g = 0; g < G; ++g) h += s_acc[0][g];
-    s_h = h / (double)G;
-    float m = -INFINITY;
-    for (int w = 0; w < FIT_NW; ++w) m = fmaxf(m, (float)s_acc[1][w]);
-    s_m = m;
-    s_lo = -12.0;
-    s_hi = 12.0;
+    for (int g = 0; g < G; ++g) h += s_hq[g];
+    s_H = h / (double)G;
+    float mm = -INFINITY;
+    for (int w = 0; w < FIT_NW; ++w) mm = fmaxf(mm, s_mx[w]);
+    s_m = mm;
   }
   __syncthreads();
-  const double H = s_h;
-  const float m = s_m;
-  const size_t rowbase = (size_t)bh * P * BK;
-  const double rsd = 1.0 / sqrt((double)HD);
+  H = s_H;
+  m = s_m;
+}
 
-  for (int round = 0; round < FIT_ROUNDS && N > 0; ++round) {
-    const double lo = s_lo, hi = s_hi, step = (hi - lo) / 16.0;
-    // per candidate: the base-2 slope log2(e) / (sqrt(D) tau_k); each thread sums its few
-    // rows in fp32, the workgroup in fp64.  x2 = (s - m) * slope is the logit in bits, so
-    // the entropy in nats is ln Z - ln 2 * A / Z with Z = sum 2^x2, A = sum 2^x2 x2.
-    if (tid < FIT_POINTS) s_ck[tid] = (float)(rsd * 1.4426950408889634074 / exp2(lo + tid * step));
-    __syncthreads();
-    float ck[FIT_POINTS], cz[FIT_POINTS], ca[FIT_POINTS];
+// The candidates' slopes of a round over [lo, hi]: log2(e) / (sqrt(D) tau_k) with
+// log2 tau_k = lo + k (hi - lo) / 16.
+HK_DEV float fit_slope(double lo, double hi, int k) {
+  return (float)(1.0 / sqrt((double)HD) * 1.4426950408889634074 / exp2(lo + k * ((hi - lo) / 16.0)));
+}
+
+// Per candidate k (threads k < FIT_POINTS get them): Z = sum 2^x2 and A = sum 2^x2 x2 over
+// pool rows [r0, r1) (offsets from the pool head c), x2 = (s - m) slope_k the logit in
+// bits.  Each thread sums rows r0 + tid, r0 + tid + FIT_THREADS, ... in that order in
+// fp32, FIT_UNR loads in flight; a row past r1 scores FIT_FAR below the max, whose terms
+// are exactly 0 (2^x2 is 0 and 0 * x2 is -0).  The workgroup sums in fp64: lanes by
+// exchanges, then wavefronts in order.
+HK_DEV void fit_sums(const Args &a, int bh, int64_t c, int64_t r0, int64_t r1, float m, double lo, double hi,
+                     double &Z, double &A) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int P = a.P;
+  const size_t rowbase = (size_t)bh * P * BK;
+  __shared__ float s_ck[FIT_POINTS];
+  __shared__ double s_acc[FIT_NW][2 * FIT_POINTS];
+  if (tid < FIT_POINTS) s_ck[tid] = fit_slope(lo, hi, tid);
+  __syncthreads();
+  float ck[FIT_POINTS], cz[FIT_POINTS], ca[FIT_POINTS];
 #pragma unroll
-    for (int k = 0; k < FIT_POINTS; ++k) {
-      cz[k] = ca[k] = 0.0f;
-      ck[k] = s_ck[k];
+  for (int k = 0; k < FIT_POINTS; ++k) {
+    cz[k] = ca[k] = 0.0f;
+    ck[k] = s_ck[k];
+  }
+  for (int64_t i0 = r0 + tid; i0 < r1; i0 += (int64_t)FIT_UNR * FIT_THREADS) {
+    float x0[FIT_UNR];
+#pragma unroll
+    for (int u = 0; u < FIT_UNR; ++u) {
+      const int64_t i = i0 + (int64_t)u * FIT_THREADS;
+      const int64_t p = c + (i < r1 ? i : r0);
+      const float sc = a.scores[rowbase + (size_t)((p / BK) % P) * BK + (size_t)(p % BK)];
+      x0[u] = i < r1 ? sc - m : -FIT_FAR;
     }
-    for (int64_t i = tid; i < N; i += FIT_THREADS) {
-      const int64_t p = c + i;
-      const float x0 = a.scores[rowbase + (size_t)((p / BK) % P) * BK + (size_t)(p % BK)] - m;
+#pragma unroll
+    for (int u = 0; u < FIT_UNR; ++u)
 #pragma unroll
       for (int k = 0; k < FIT_POINTS; ++k) {
-        const float x2 = x0 * ck[k];
+        const float x2 = x0[u] * ck[k];
         const float e = exp2_fast(x2);
         cz[k] += e;
         ca[k] = __builtin_fmaf(e, x2, ca[k]);
       }
-    }
-#pragma unroll
-    for (int k = 0; k < FIT_POINTS; ++k) {
-      double z = (double)cz[k], w = (double)ca[k];
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) {
-        z += shfl_xor_d(z, off);
-        w += shfl_xor_d(w, off);
-      }
-      if (lane == 0) {
-        s_acc[wave][k] = z;
-        s_acc[wave][FIT_POINTS + k] = w;
-      }
-    }
-    __syncthreads();
-    if (tid < FIT_POINTS) {  // does the entropy at tau_k reach the target?
-      double Z = 0.0, A = 0.0;
-      for (int w = 0; w < FIT_NW; ++w) {
-        Z += s_acc[w][tid];
-        A += s_acc[w][FIT_POINTS + tid];
-      }
-      s_reach[tid] = log(Z) - 0.69314718055994530942 * A / Z >= H;
-    }
-    __syncthreads();
-    if (tid == 0) {
-      int kk = 0;
-      while (kk < FIT_POINTS && !s_reach[kk]) ++kk;
-      if (kk == 0) {
-        s_hi = lo;
-      } else if (kk >= FIT_POINTS) {
-        s_lo = hi;
-      } else {
-        s_lo = lo + (kk - 1) * step;
-        s_hi = lo + kk * step;
-      }
-    }
-    __syncthreads();
   }
+#pragma unroll
+  for (int k = 0; k < FIT_POINTS; ++k) {
+    double z = (double)cz[k], w = (double)ca[k];
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      z += shfl_xor_d(z, off);
+      w += shfl_xor_d(w, off);
+    }
+    if (lane == 0) {
+      s_acc[wave][k] = z;
+      s_acc[wave][FIT_POINTS + k] = w;
+    }
+  }
+  __syncthreads();
+  Z = A = 0.0;
+  if (tid < FIT_POINTS) {
+    for (int w = 0; w < FIT_NW; ++w) {
+      Z += s_acc[w][tid];
+      A += s_acc[w][FIT_POINTS + tid];
+    }
+  }
+  __syncthreads();  // (s_ck and s_acc are reused by the next call)
+}
+
+// The next bracket from a round's sums (Z, A of candidate k in thread k): the first
+// candidate whose calibrated entropy ln Z - ln 2 A / Z reaches H bounds it from above
+// (the entropy grows with tau).  Every thread gets it.
+HK_DEV void fit_next(double Z, double A, double H, double &lo, double &hi) {
+  const int tid = threadIdx.x;
+  __shared__ int s_reach[FIT_POINTS];
+  __shared__ double s_lo, s_hi;
+  if (tid < FIT_POINTS) s_reach[tid] = log(Z) - 0.69314718055994530942 * A / Z >= H;
+  __syncthreads();
   if (tid == 0) {
-    const float tau = N > 0 ? (float)exp2(0.5 * (s_lo + s_hi)) : 1.0f;
+    const double step = (hi - lo) / 16.0;
+    int kk = 0;
+    while (kk < FIT_POINTS && !s_reach[kk]) ++kk;
+    double nlo = lo, nhi = hi;
+    if (kk == 0) {
+      nhi = lo;
+    } else if (kk >= FIT_POINTS) {
+      nlo = hi;
+    } else {
+      nlo = lo + (kk - 1) * step;
+      nhi = lo + kk * step;
+    }
+    s_lo = nlo;
+    s_hi = nhi;
+  }
+  __syncthreads();
+  lo = s_lo;
+  hi = s_hi;
+  __syncthreads();
+}
+
+// tau = 2^(midpoint of the last bracket) (1 for an empty pool), into the head's plan
+HK_DEV void fit_store(const Args &a, int bh, int64_t N, double lo, double hi) {
+  if (threadIdx.x == 0) {
+    const float tau = N > 0 ? (float)exp2(0.5 * (lo + hi)) : 1.0f;
     HeadInfo *hd = a.head + bh;
     hd->tau = tau;
     hd->kappa = (float)(1.4426950408889634074 / (sqrt((double)HD) * (double)tau));
     if (a.tau_fit) a.tau_fit[bh] = tau;
   }
+}
+
+HK_DEV int64_t fit_pool(const Args &a, int bh, int64_t &c) {
+  const int b = bh / a.Hkv;
+  c = a.pool_head[bh];
+  return pool_end(a.seq_len[b], a.W, a.S) - c;
+}
+
+// hardkv_fit, grid (B*Hkv), 512 threads: one workgroup per head.  The target is the mean over the group's queries of the entropy
+// (nats) of their raw attention over the pool; then five rounds of a 17-point grid on
+// log2 tau in [-12, 12] find the bracket where the entropy of the calibrated
+// softmax(s / (sqrt(D) tau)) over the pool reaches the target (it grows with tau); tau
+// is the midpoint of the last bracket.
+__global__ __launch_bounds__(FIT_THREADS) void hardkv_fit(Args a) {
+  const int bh = a.bh0 + blockIdx.x;
+  int64_t c;
+  const int64_t N = fit_pool(a, bh, c);
+  double H;
+  float m;
+  fit_target(a, bh, H, m);
+  double lo = -12.0, hi = 12.0;
+  for (int round = 0; round < FIT_ROUNDS && N > 0; ++round) {
+    double Z, A;
+    fit_sums(a, bh, c, 0, N, m, lo, hi, Z, A);
+    fit_next(Z, A, H, lo, hi);
+  }
+  fit_store(a, bh, N, lo, hi);
+}
+
+// The same fit for long pools of few heads, the rows of each round spread over slices of
+// FIT_SPLIT_ROWS rows (a.nfs per head), in FIT_ROUNDS + 2 kernels:
+// hardkv_fit_prep, grid (B*Hkv): the target and the max into the head's FitHead.
+__global__ __launch_bounds__(FIT_THREADS) void hardkv_fit_prep(Args a) {
+  const int bh = a.bh0 + blockIdx.x;
+  double H;
+  float m;
+  fit_target(a, bh, H, m);
+  if (threadIdx.x == 0) {
+    a.fith[bh].H = H;
+    a.fith[bh].m = m;
+  }
+}
+
+// hardkv_fit_round, grid (nfs, B*Hkv): round r's bracket from round r - 1's (its slices'
+// sums, summed in slice order, so that every workgroup derives the same bracket; slice 0
+// records it for round r + 1), then the slice's sums for round r's candidates.
+__global__ __launch_bounds__(FIT_THREADS) void hardkv_fit_round(Args a, int r) {
+  const int bh = a.bh0 + blockIdx.y, slice = blockIdx.x;
+  const int tid = threadIdx.x;
+  int64_t c;
+  const int64_t N = fit_pool(a, bh, c);
+  if (N <= 0) return;  // uniform
+  FitHead *fh = a.fith + bh;
+  const double H = fh->H;
+  const float m = fh->m;
+  double lo = -12.0, hi = 12.0;
+  if (r > 0) {
+    lo = fh->lo[r - 1];
+    hi = fh->hi[r - 1];
+    double Z = 0.0, A = 0.0;
+    if (tid < FIT_POINTS)
+      for (int sl = 0; sl < a.nfs; ++sl) {
+        const double *ps = a.fitp + (((size_t)(r - 1) * a.B * a.Hkv + bh) * a.nfs + sl) * 2 * FIT_POINTS;
+        Z += ps[tid];
+        A += ps[FIT_POINTS + tid];
+      }
+    fit_next(Z, A, H, lo, hi);
+  }
+  if (slice == 0 && tid == 0) {
+    fh->lo[r] = lo;
+    fh->hi[r] = hi;
+  }
+  const int64_t r0 = (int64_t)slice * FIT_SPLIT_ROWS, r1 = min(N, r0 + (int64_t)FIT_SPLIT_ROWS);
+  double Z, A;
+  fit_sums(a, bh, c, r0, max(r0, r1), m, lo, hi, Z, A);
+  if (tid < FIT_POINTS) {
+    double *ps = a.fitp + (((size_t)r * a.B * a.Hkv + bh) * a.nfs + slice) * 2 * FIT_POINTS;
+    ps[tid] = Z;
+    ps[FIT_POINTS + tid] = A;
+  }
+}
+
+// hardkv_fit_final, grid (B*Hkv): the last round's bracket and tau.
+__global__ __launch_bounds__(FIT_THREADS) void hardkv_fit_final(Args a) {
+  const int bh = a.bh0 + blockIdx.x;
+  const int tid = threadIdx.x;
+  int64_t c;
+  const int64_t N = fit_pool(a, bh, c);
+  double lo = -12.0, hi = 12.0;
+  if (N > 0) {
+    const FitHead *fh = a.fith + bh;
+    constexpr int r = FIT_ROUNDS - 1;
+    lo = fh->lo[r];
+    hi = fh->hi[r];
+    double Z = 0.0, A = 0.0;
+    if (tid < FIT_POINTS)
+      for (int sl = 0; sl < a.nfs; ++sl) {
+        const double *ps = a.fitp + (((size_t)r * a.B * a.Hkv + bh) * a.nfs + sl) * 2 * FIT_POINTS;
+        Z += ps[tid];
+        A += ps[FIT_POINTS + tid];
+      }
+    fit_next(Z, A, fh->H, lo, hi);
+  }
+  fit_store(a, bh, N, lo, hi);
 }
 
 template <typename T, bool ENT>
@@ -1169,7 +1300,14 @@ hipError_t launch_score(const Args &a, hipStream_t s, bool bf16) {
 }
 
 hipError_t launch_fit(const Args &a, hipStream_t s) {
-  hipLaunchKernelGGL(hardkv_fit, dim3(a.nbh), dim3(FIT_THREADS), 0, s, a);
+  if (a.nfs <= 1) {
+    hipLaunchKernelGGL(hardkv_fit, dim3(a.nbh), dim3(FIT_THREADS), 0, s, a);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL(hardkv_fit_prep, dim3(a.nbh), dim3(FIT_THREADS), 0, s, a);
+  for (int r = 0; r < FIT_ROUNDS; ++r)
+    hipLaunchKernelGGL(hardkv_fit_round, dim3(a.nfs, a.nbh), dim3(FIT_THREADS), 0, s, a, r);
+  hipLaunchKernelGGL(hardkv_fit_final, dim3(a.nbh), dim3(FIT_THREADS), 0, s, a);
   return hipGetLastError();
 }
 

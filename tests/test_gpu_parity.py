@@ -335,8 +335,11 @@ ENTROPY_CASES = {
     "g1": dict(num_q_heads=2, num_kv_heads=2),
     "g8_batch8": dict(batch=8, num_q_heads=16, num_kv_heads=2, cond_mode=COND_MERGE, ctx_len=500, ctx_min=100),
     "heavy": dict(heavy=(0, 8), cond_mode=COND_MERGE),
-    # a ring of five slices: the split select reads the fitted slope
+    # a ring of five slices: the split select reads the fitted slope (and the fit is
+    # split over 18 slices of 4096 rows, the shorter pool's last ones empty)
     "split_long": dict(ctx_len=70000, ctx_min=60000, sparse_cap=69632, cond_mode=COND_MERGE),
+    # the fit over ten slices, the last one ragged
+    "fit_ten_slices": dict(ctx_len=40000, ctx_min=36000, sparse_cap=32768, cond_mode=COND_MERGE),
 }
 
 

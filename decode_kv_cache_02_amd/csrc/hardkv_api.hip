@@ -113,12 +113,11 @@ int32_t plan(const hardkv_config *cfg, Plan &p) {
   a.part_cd_base = std::max(a.nch_reg, a.nv_att);
   a.xp_base = a.part_cd_base + a.nc_att + a.nd_att + a.ns_att;  // then one slot per rewrite chunk
   a.npart = a.xp_base + a.nch_reg;
-  if (a.mode == HARDKV_COND_MERGE) {
-    const int emax = std::max(1, a.P - a.S_cap / BK);
-    a.ncs = std::min(a.C, emax);
-  } else {
-    a.ncs = 1;
-  }
+  // at most emax blocks condense in a step (a pool never exceeds its P*64 rows)
+  const int emax = std::max(1, a.P - a.S_cap / BK);
+  a.ncs = a.mode == HARDKV_COND_MERGE ? std::min(a.C, emax) : 1;
+  a.cond_small = a.mode != HARDKV_COND_OFF && emax <= FUSE_COND_BLOCKS;
+  a.fuse_cond = 0;
 
   // the select of a long pool is split over slices of SEL_SLICE_BLOCKS blocks
   a.nsp = (a.P + SEL_SLICE_BLOCKS - 1) / SEL_SLICE_BLOCKS;
@@ -227,22 +226,27 @@ constexpr int NSTAGES = 6;
 const char *const kStageNames[NSTAGES] = {"append", "score", "select", "condense", "rewrite_attend",
                                           "combine"};
 
-// kernel `stage` of the fused step
-hipError_t step_stage(const hardkv_config *cfg, Args &a, int stage, hipStream_t s) {
+// Kernel `stage` of the fused step.  In the whole step (whole_step) the select launch
+// also condenses when at most FUSE_COND_BLOCKS blocks can condense per step, and stage 3
+// launches nothing; one stage at a time (timing) they stay apart.
+hipError_t step_stage(const hardkv_config *cfg, Args &a, int stage, hipStream_t s, bool whole_step) {
   const bool bf = is_bf16(cfg);
   a.nvp = a.nch_reg;
   a.nxp = 0;
   a.gather_mode = GATHER_STEP;
+  const bool fuse = whole_step && a.cond_small;
   switch (stage) {
     case 0: return launch_append(a, s, bf);
     case 1: return launch_score(a, s, bf);
     case 2: {
       hipError_t e = a.calibration ? launch_fit(a, s) : hipSuccess;
-      if (e == hipSuccess) e = launch_select(a, s);
+      a.fuse_cond = fuse ? 1 : 0;
+      if (e == hipSuccess) e = launch_select(a, s, bf);
+      a.fuse_cond = 0;
       if (e == hipSuccess && a.view_sum) e = launch_flatten(a, s);
       return e;
     }
-    case 3: return launch_condense(a, s, bf);
+    case 3: return fuse ? hipSuccess : launch_condense(a, s, bf);
     case 4: return launch_rewrite(a, s, bf, true, true, true);
     case 5: return launch_combine(a, s);
     default: return hipErrorInvalidValue;
@@ -270,7 +274,7 @@ hipError_t attend_calls(const hardkv_config *cfg, Args &a, hipStream_t s, bool s
 // The fused step: every stage over all units, in stream order.
 hipError_t step_all(const hardkv_config *cfg, Args &a, hipStream_t s) {
   hipError_t e = hipSuccess;
-  for (int stage = 0; stage < NSTAGES && e == hipSuccess; ++stage) e = step_stage(cfg, a, stage, s);
+  for (int stage = 0; stage < NSTAGES && e == hipSuccess; ++stage) e = step_stage(cfg, a, stage, s, true);
   return e;
 }
 
@@ -326,7 +330,7 @@ int32_t hardkv_select(const hardkv_config *cfg, hardkv_state *st, const void *q,
   const bool bf = is_bf16(cfg);
   hipError_t e = launch_score(p.a, s, bf);
   if (e == hipSuccess && p.a.calibration) e = launch_fit(p.a, s);
-  if (e == hipSuccess) e = launch_select(p.a, s);
+  if (e == hipSuccess) e = launch_select(p.a, s, is_bf16(cfg));
   if (e == hipSuccess && p.a.view_sum) e = launch_flatten(p.a, s);
   if (e == hipSuccess) e = launch_rewrite(p.a, s, bf, true, false, false);  // mask words
   return hip_status(e);
@@ -396,7 +400,7 @@ int32_t hardkv_step_stage(const hardkv_config *cfg, hardkv_state *st, const void
   p.a.k_new = k_new;
   p.a.v_new = v_new;
   p.a.out = out;
-  return hip_status(step_stage(cfg, p.a, stage, (hipStream_t)stream));
+  return hip_status(step_stage(cfg, p.a, stage, (hipStream_t)stream, false));
 }
 
 int32_t hardkv_step_num_stages(void) { return NSTAGES; }

@@ -19,6 +19,7 @@ constexpr int MAX_POOL_BLOCKS = HARDKV_MAX_POOL_BLOCKS; // pool ring blocks per 
 constexpr int CAND_CAP = 8192;        // cut-bucket candidates resolved in LDS
 constexpr int SEL_SLICE_BLOCKS = 256; // pool blocks per workgroup when a head's select is split
 constexpr int SEL_SPLIT_MIN = 4;      // slices per head from which the select is split
+constexpr int FUSE_COND_BLOCKS = 4;   // blocks per step up to which the step's select condenses
 
 // Per-head values that the split select passes between its kernels.
 struct alignas(128) SelHead {
@@ -109,6 +110,8 @@ struct Args {
   int cb_score, nch_score;  // score: blocks per workgroup, workgroups per head
   int nsp;                  // select: slices per head (1: one workgroup does the whole select)
   int nfs;                  // entropy fit: slices per head (1: one workgroup does the whole fit)
+  int cond_small;           // at most FUSE_COND_BLOCKS blocks can condense per step
+  int fuse_cond;            // this select launch also condenses (the fused step, cond_small)
   int cb_reg, nch_reg;      // rewrite: blocks per workgroup, workgroups per head
   int rv_att, nv_att;       // attention over the view (standalone): rows per workgroup, count
   int rc_att, nc_att;       // attention over condensed slots
@@ -142,7 +145,7 @@ enum { GATHER_STEP = 0, GATHER_REWRITE = 1, GATHER_ATTEND_NRW = 2, GATHER_ATTEND
 hipError_t launch_prefill(const Args &a, hipStream_t s, bool bf16);
 hipError_t launch_append(const Args &a, hipStream_t s, bool bf16);
 hipError_t launch_score(const Args &a, hipStream_t s, bool bf16);
-hipError_t launch_select(const Args &a, hipStream_t s);
+hipError_t launch_select(const Args &a, hipStream_t s, bool bf16);
 // exclusive scan of the rewritten budgets into view_off and each head's voff (SUM layout)
 hipError_t launch_flatten(const Args &a, hipStream_t s);
 // entropy-matched temperature of every head (calibration ENTROPY), before the select

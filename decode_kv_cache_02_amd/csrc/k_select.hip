@@ -37,7 +37,7 @@
 //   counter) and hardkv_sel_finish (per head: the same ending as the one-workgroup kernel).
 #include <type_traits>
 
-#include "hardkv_internal.h"
+#include "condense_common.h"
 
 namespace hardkv {
 
@@ -736,7 +736,22 @@ HK_DEV void sel_finish(const Args &a, int bh, const SelGeo &g, SelShared &sh, ui
   }
 }
 
-// The whole select stage of one head in one workgroup (pools up to SEL_SPLIT_MIN slices).
+// The condensation of the head's E oldest blocks by the select workgroup itself (FUSE:
+// the fused step, when at most FUSE_COND_BLOCKS blocks can condense per step): one
+// wavefront per ring slot, after the plan is written (its cursor read comes first).
+template <typename T>
+HK_DEV void select_condense(const Args &a, int bh, const SelGeo &g, int32_t nu, uint64_t W_all) {
+  const int tid = threadIdx.x, wave = tid >> 6;
+  __syncthreads();
+  if (a.mode == HARDKV_COND_MERGE)
+    for (int i = wave; i < g.E && i < a.C; i += NW)
+      condense_chain<T, Elem<T>::bytes == 2 ? 4 : 2, true>(a, bh, i, g.c, g.E, nu, W_all);
+  if (tid == 0) condense_advance(a, bh, g.c, g.E, nu);
+}
+
+// The whole select stage of one head in one workgroup (pools up to SEL_SPLIT_MIN slices);
+// FUSE: and the condensation (T: the storage type of the rows it merges).
+template <typename T, bool FUSE>
 __global__ __launch_bounds__(SEL_THREADS) void hardkv_select(Args a) {
   const int bh = a.bh0 + blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -745,6 +760,7 @@ __global__ __launch_bounds__(SEL_THREADS) void hardkv_select(Args a) {
   SelShared &sh = *reinterpret_cast<SelShared *>(smem_raw);
   uint32_t *blk = reinterpret_cast<uint32_t *>(smem_raw + sizeof(SelShared));
   const SelGeo g = sel_geo(a, bh);
+  const int32_t nu = FUSE ? a.cond_cursor[bh] : 0;
 
   for (int i = tid; i < NB1; i += SEL_THREADS) sh.hist[i] = 0ull;
   if (tid == 0) sh.ncand = 0;
@@ -758,17 +774,18 @@ __global__ __launch_bounds__(SEL_THREADS) void hardkv_select(Args a) {
   if (ballot(bad) && lane == 0) atomicOr(a.error_word, HARDKV_ERR_NONFINITE);
   const uint64_t W_all = block_sum_u64(my_all, sh, 0);
   const uint64_t W_U = block_sum_u64(my_u, sh, 1);
-  const uint64_t T = ((uint64_t)a.pq * W_U + 65535ull) >> 16;
+  const uint64_t Tm = ((uint64_t)a.pq * W_U + 65535ull) >> 16;
   uint64_t R1 = 0;
   int b1 = 0;
   if (W_U > 0) {
     uint64_t above1;
-    b1 = find_cut(sh, NB1, T, &above1);
-    R1 = T - above1;  // mass still needed from the cut bucket
+    b1 = find_cut(sh, NB1, Tm, &above1);
+    R1 = Tm - above1;  // mass still needed from the cut bucket
     sel_pass_b<false>(a, bh, g, b1, 0, g.nub, blk, sh.cand, &sh.ncand);
     __syncthreads();
   }
-  sel_finish(a, bh, g, sh, blk, W_all, W_U, T, R1, b1);
+  sel_finish(a, bh, g, sh, blk, W_all, W_U, Tm, R1, b1);
+  if (FUSE) select_condense<T>(a, bh, g, nu, W_all);
 }
 
 // Split select, for long pools: the head's blocks in slices of SEL_SLICE_BLOCKS, one
@@ -907,7 +924,9 @@ __global__ __launch_bounds__(SEL_THREADS) void hardkv_sel_count(Args a) {
 }
 
 // hardkv_sel_finish, grid (B*Hkv): the per-block counts and the candidates back into LDS,
-//   then the rest of the select stage as in the one-workgroup kernel.
+//   then the rest of the select stage as in the one-workgroup kernel (FUSE: with the
+//   condensation).
+template <typename T, bool FUSE>
 __global__ __launch_bounds__(SEL_THREADS) void hardkv_sel_finish(Args a) {
   const int bh = a.bh0 + blockIdx.x;
   const int tid = threadIdx.x;
@@ -916,8 +935,9 @@ __global__ __launch_bounds__(SEL_THREADS) void hardkv_sel_finish(Args a) {
   SelShared &sh = *reinterpret_cast<SelShared *>(smem_raw);
   uint32_t *blk = reinterpret_cast<uint32_t *>(smem_raw + sizeof(SelShared));
   const SelGeo g = sel_geo(a, bh);
+  const int32_t nu = FUSE ? a.cond_cursor[bh] : 0;
   const SelHead *sx = a.selh + bh;
-  const uint64_t W_all = sx->w_all, W_U = sx->w_u, T = sx->T;
+  const uint64_t W_all = sx->w_all, W_U = sx->w_u, Tm = sx->T;
   uint64_t R1 = 0;
   int b1 = 0;
   if (W_U > 0) {
@@ -931,7 +951,8 @@ __global__ __launch_bounds__(SEL_THREADS) void hardkv_sel_finish(Args a) {
       blk[j] = reinterpret_cast<const uint32_t *>(a.blkinfo + (size_t)bh * P + g.ring(g.nx + j, P))[0];
     __syncthreads();
   }
-  sel_finish(a, bh, g, sh, blk, W_all, W_U, T, R1, b1);
+  sel_finish(a, bh, g, sh, blk, W_all, W_U, Tm, R1, b1);
+  if (FUSE) select_condense<T>(a, bh, g, nu, W_all);
 }
 
 // Flatten Index to the sum: one workgroup scans n_u = k* (rewritten heads) or 0 over
@@ -1316,11 +1337,14 @@ hipError_t launch_flatten(const Args &a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_select(const Args &a, hipStream_t s) {
+hipError_t launch_select(const Args &a, hipStream_t s, bool bf16) {
   static bool configured = false;  // the attributes are per function, set once per process
   if (!configured) {
-    const void *fs[] = {(const void *)hardkv_select, (const void *)hardkv_sel_weigh, (const void *)hardkv_sel_cut,
-                        (const void *)hardkv_sel_count, (const void *)hardkv_sel_finish};
+    const void *fs[] = {(const void *)hardkv_select<BF16, false>, (const void *)hardkv_select<BF16, true>,
+                        (const void *)hardkv_select<F32, true>, (const void *)hardkv_sel_weigh,
+                        (const void *)hardkv_sel_cut, (const void *)hardkv_sel_count,
+                        (const void *)hardkv_sel_finish<BF16, false>, (const void *)hardkv_sel_finish<BF16, true>,
+                        (const void *)hardkv_sel_finish<F32, true>};
     for (const void *f : fs) {
       hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize,
                                          (int)sel_lds_bytes(MAX_POOL_BLOCKS));
@@ -1328,8 +1352,13 @@ hipError_t launch_select(const Args &a, hipStream_t s) {
     }
     configured = true;
   }
+  // (the storage type matters only to the condensation; without it one instance serves)
+  auto sel = !a.fuse_cond ? hardkv_select<BF16, false> : bf16 ? hardkv_select<BF16, true> : hardkv_select<F32, true>;
+  auto fin = !a.fuse_cond ? hardkv_sel_finish<BF16, false>
+             : bf16       ? hardkv_sel_finish<BF16, true>
+                          : hardkv_sel_finish<F32, true>;
   if (a.nsp <= 1) {
-    hipLaunchKernelGGL(hardkv_select, dim3(a.nbh), dim3(SEL_THREADS), sel_lds_bytes(a.P), s, a);
+    hipLaunchKernelGGL(sel, dim3(a.nbh), dim3(SEL_THREADS), sel_lds_bytes(a.P), s, a);
     return hipGetLastError();
   }
   hipLaunchKernelGGL(hardkv_sel_weigh, dim3(a.nsp, a.nbh), dim3(SEL_THREADS), sizeof(SelShared), s, a);
@@ -1341,7 +1370,7 @@ hipError_t launch_select(const Args &a, hipStream_t s) {
   hipLaunchKernelGGL(hardkv_sel_count, dim3(a.nsp, a.nbh), dim3(SEL_THREADS), sizeof(SelShared), s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(hardkv_sel_finish, dim3(a.nbh), dim3(SEL_THREADS), sel_lds_bytes(a.P), s, a);
+  hipLaunchKernelGGL(fin, dim3(a.nbh), dim3(SEL_THREADS), sel_lds_bytes(a.P), s, a);
   return hipGetLastError();
 }
 

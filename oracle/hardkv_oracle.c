@@ -53,7 +53,7 @@ static int64_t pool_row(const orc_cfg *cfg, int64_t u, int64_t p) {
  * Each query-key logit is a dot product taken as a canonical pairwise tree:
  * products in index order, then level l+1 element i = level l [2i] + [2i+1].
  * ---------------------------------------------------------------------------------- */
-/* Sink prefix (a reading of the pages' "attention sinks" of the dense tier): the first S
+/* Sink prefix (a reading of the dense tier's role of keeping attention sinks): the first S
  * positions of a sequence stay in a tier of their own, attended at every step and never
  * scored, condensed or rewritten.  The dense window then holds the W latest positions
  * after them, [max(S, t - W), t), and the pool the positions between, [c, max(S, t - W)),
@@ -330,13 +330,14 @@ void orc_full_attention(const float *q, const float *k, const float *v, int32_t 
 }
 
 /* the tiers of one unit, in attention order: sink positions (p < min(S, t)), condensed
- * slots with n > 0, view rows r < k*, dense positions ascending (section 2.A:
+ * slots with n > 0, view rows r < k*, pool positions that arrived after the last
+ * selection (steps without selection only), dense positions ascending (section 2.A:
  * condensed, sparse, dense tiers) */
 typedef struct {
   const orc_cfg *cfg;
   const orc_state *st;
   int64_t u;
-  int64_t n_sink, n_cond, n_view, n_dense, dense_lo;
+  int64_t n_sink, n_cond, n_view, n_tail, tail_lo, n_dense, dense_lo;
   const int64_t *kept_rows;  /* pool rows of the kept positions, ascending; NULL: the view */
   int32_t slot[4096];
 } tier_ctx;
@@ -380,8 +381,12 @@ static void tier_row(const void *ctx, int64_t i, double *key, double *val, doubl
     row = tc->u * cfg->view_cap + i;
     kb = st->view_k;
     vb = st->view_v;
+  } else if (i < tc->n_view + tc->n_tail) {
+    row = pool_row(cfg, tc->u, tc->tail_lo + (i - tc->n_view));
+    kb = st->pool_k;
+    vb = st->pool_v;
   } else {
-    int64_t p = tc->dense_lo + (i - tc->n_view);
+    int64_t p = tc->dense_lo + (i - tc->n_view - tc->n_tail);
     row = tc->u * cfg->dense_window + p % cfg->dense_window;
     kb = st->dense_k;
     vb = st->dense_v;
@@ -414,6 +419,9 @@ int32_t orc_prefill(const orc_cfg *cfg, orc_state *st, const void *k_ctx, const 
     for (int h = 0; h < H; ++h) {
       int64_t u = (int64_t)b * H + h;
       st->pool_head[u] = cfg->sink;
+      st->pend_sel[u] = cfg->sink;  /* no selection yet: the whole pool is unselected */
+      st->budget[u] = 0;
+      if (st->regularized) st->regularized[u] = 0;
       st->cond_cursor[u] = 0;
       for (int s = 0; s < C; ++s) {
         int64_t si = u * C + s;
@@ -593,6 +601,7 @@ static uint32_t unit_step(const orc_cfg *cfg, orc_state *st, int b, int h, const
     }
   }
   st->pool_head[u] = c + BK * E;
+  st->pend_sel[u] = pend;
   st->budget[u] = kstar;
   st->n_condense[u] = (int32_t)E;
   st->w_all[u] = w_all;
@@ -610,6 +619,8 @@ static uint32_t unit_step(const orc_cfg *cfg, orc_state *st, int b, int h, const
       if (st->cond_n[u * cfg->condensed_slots + s] > 0) tc->slot[tc->n_cond++] = s;
     tc->kept_rows = (rw && !packed) ? NULL : kept;
     tc->n_view = (rw && !packed) ? (kstar < cfg->view_cap ? kstar : cfg->view_cap) : kstar;
+    tc->n_tail = 0;
+    tc->tail_lo = pend;
     tc->dense_lo = dense_lo_of(cfg, t);
     tc->n_dense = t - tc->dense_lo;
     tc->n_sink = t < cfg->sink ? t : cfg->sink;
@@ -635,11 +646,11 @@ static uint32_t unit_step(const orc_cfg *cfg, orc_state *st, int b, int h, const
  * unit: plan, score, calibrate, top-p (stage 2), regularize (stage 3),
  * condense (stage 4), and attention.
  * ---------------------------------------------------------------------------------- */
-int32_t orc_step(const orc_cfg *cfg, orc_state *st, const void *q, const void *k_new,
-                 const void *v_new, double *out, int32_t do_attend, int32_t nthreads) {
+/* stage 1, the linear append: the position leaving the dense window moves to the pool
+ * tail (once past the sinks), the new token takes its dense slot (or its sink row) */
+static uint32_t append_all(const orc_cfg *cfg, orc_state *st, const void *k_new, const void *v_new) {
   const int B = cfg->batch, H = cfg->num_kv_heads, D = cfg->head_dim, eb = cfg->elem_bytes;
   const int W = cfg->dense_window;
-  if (cfg->condensed_slots > 4096 || D > 1024) return -2;
   uint32_t err = 0;
   for (int b = 0; b < B; ++b) {
     const int64_t t = st->seq_len[b];
@@ -662,6 +673,14 @@ int32_t orc_step(const orc_cfg *cfg, orc_state *st, const void *q, const void *k
     }
     st->seq_len[b] = t + 1;
   }
+  return err;
+}
+
+int32_t orc_step(const orc_cfg *cfg, orc_state *st, const void *q, const void *k_new,
+                 const void *v_new, double *out, int32_t do_attend, int32_t nthreads) {
+  const int B = cfg->batch, H = cfg->num_kv_heads, D = cfg->head_dim, eb = cfg->elem_bytes;
+  if (cfg->condensed_slots > 4096 || D > 1024) return -2;
+  uint32_t err = append_all(cfg, st, k_new, v_new);
   const int64_t units = (int64_t)B * H;
 #ifdef _OPENMP
   int nt = nthreads > 0 ? nthreads : omp_get_max_threads();
@@ -700,6 +719,73 @@ int32_t orc_step(const orc_cfg *cfg, orc_state *st, const void *q, const void *k
     st->view_off[units] = (int32_t)off;
     if (off > cfg->view_total) err |= ORC_ERR_VIEW_OVERFLOW;
   }
+  st->error_word |= err;
+  return 0;
+}
+
+/* ------------------------------------------------------------------------------------
+ * A step that reuses the last selection (section 2.C: a rewritten cache stays in use for
+ * later steps, its cost spread over them).  Reading: selection reruns when the caller
+ * asks for it (a step with selection is orc_step); in between, each step appends, and
+ * attention covers the sinks, the condensed slots, the rows the last selection kept (the
+ * view of a rewritten head, else the pool rows its mask marks, which stay in place: nothing
+ * is condensed without a selection), every pool position that arrived after that
+ * selection, and the dense window.
+ * ---------------------------------------------------------------------------------- */
+static void unit_reuse(const orc_cfg *cfg, orc_state *st, int b, int h, const void *q, double *out) {
+  const int H = cfg->num_kv_heads, Hq = cfg->num_q_heads, G = Hq / H, D = cfg->head_dim;
+  const int eb = cfg->elem_bytes, P = cfg->pool_blocks;
+  const int64_t u = (int64_t)b * H + h;
+  const int64_t t = st->seq_len[b];
+  const int64_t c = st->pool_head[u];
+  const int64_t psel = st->pend_sel[u];
+  const int64_t pend = pool_end_of(cfg, t);
+  const int32_t kstar = st->budget[u];
+  const int rw = st->regularized ? st->regularized[u]
+                 : cfg->regularize == 0 ? 1
+                 : cfg->regularize == 1 ? 0
+                 : (kstar >= cfg->mti_lower && kstar <= cfg->mti_upper) ? 1 : 0;
+  const int packed = cfg->view_layout == 1;
+  int64_t *kept = (int64_t *)malloc(sizeof(int64_t) * (size_t)(kstar > 0 ? kstar : 1));
+  int64_t nk = 0;
+  for (int64_t j = c; j < psel && nk < kstar; ++j)
+    if ((st->mask[u * P + (j / BK) % P] >> (j % BK)) & 1u) kept[nk++] = pool_row(cfg, u, j);
+  tier_ctx *tc = (tier_ctx *)malloc(sizeof(tier_ctx));
+  tc->cfg = cfg;
+  tc->st = st;
+  tc->u = u;
+  tc->n_cond = 0;
+  for (int s = 0; s < cfg->condensed_slots && s < 4096; ++s)
+    if (st->cond_n[u * cfg->condensed_slots + s] > 0) tc->slot[tc->n_cond++] = s;
+  tc->kept_rows = (rw && !packed) ? NULL : kept;
+  tc->n_view = (rw && !packed) ? (kstar < cfg->view_cap ? kstar : cfg->view_cap) : nk;
+  tc->tail_lo = psel;
+  tc->n_tail = pend > psel ? pend - psel : 0;
+  tc->dense_lo = dense_lo_of(cfg, t);
+  tc->n_dense = t - tc->dense_lo;
+  tc->n_sink = t < cfg->sink ? t : cfg->sink;
+  double qd[1024];
+  for (int g = 0; g < G; ++g) {
+    for (int d = 0; d < D; ++d) qd[d] = (double)elem_get(q, ((int64_t)b * Hq + h * G + g) * D + d, eb);
+    attend_core(qd, D, tc->n_sink + tc->n_cond + tc->n_view + tc->n_tail + tc->n_dense, tier_row, tc,
+                out + ((int64_t)b * Hq + h * G + g) * D);
+  }
+  free(tc);
+  free(kept);
+}
+
+int32_t orc_step_reuse(const orc_cfg *cfg, orc_state *st, const void *q, const void *k_new,
+                       const void *v_new, double *out, int32_t nthreads) {
+  const int B = cfg->batch, H = cfg->num_kv_heads, D = cfg->head_dim;
+  if (cfg->condensed_slots > 4096 || D > 1024) return -2;
+  uint32_t err = append_all(cfg, st, k_new, v_new);
+  const int64_t units = (int64_t)B * H;
+#ifdef _OPENMP
+  int nt = nthreads > 0 ? nthreads : omp_get_max_threads();
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nt)
+#endif
+  for (int64_t i = 0; i < units; ++i) unit_reuse(cfg, st, (int)(i / H), (int)(i % H), q, out);
+  (void)nthreads;
   st->error_word |= err;
   return 0;
 }

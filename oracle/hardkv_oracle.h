@@ -75,6 +75,9 @@ typedef struct {
   float *tau_fit;            /* [B*H] the temperature used (calibration 1; may be NULL) */
   uint32_t error_word;
   void *sink_k, *sink_v;     /* [B*H][S][D]: position p < S in row p (S > 0) */
+  int64_t *pend_sel;         /* [B*H] the pool end at the last selection (the pool head, S, after
+                                a prefill): a step without selection attends the pool positions
+                                from here on in full */
 } orc_state;
 
 /* building blocks, exported for the pin tests */
@@ -95,6 +98,11 @@ int32_t orc_prefill(const orc_cfg *cfg, orc_state *st, const void *k_ctx, const 
                     const int64_t *ctx_len, int64_t max_len);
 int32_t orc_step(const orc_cfg *cfg, orc_state *st, const void *q, const void *k_new,
                  const void *v_new, double *out, int32_t do_attend, int32_t nthreads);
+/* a step that reuses the last selection: the append, then attention over the sinks, the
+ * condensed slots, the rows the last selection kept (its views, or the pool rows its mask
+ * marks), the pool positions that arrived since it, and the dense window */
+int32_t orc_step_reuse(const orc_cfg *cfg, orc_state *st, const void *q, const void *k_new,
+                       const void *v_new, double *out, int32_t nthreads);
 /* entropy-matched temperature: d are the G x n raw dot products (query-major), s the n
  * max-pooled scores; returns the fitted tau (fp32) and the target entropy in *h_target */
 float   orc_fit_tau(const float *d, int32_t G, const float *s, int64_t n, int32_t D, double *h_target);

@@ -45,6 +45,7 @@ class OrcState(C.Structure):
         ("n_condense", C.c_void_p), ("w_all", C.c_void_p), ("w_u", C.c_void_p),
         ("thresh", C.c_void_p), ("regularized", C.c_void_p), ("view_off", C.c_void_p),
         ("tau_fit", C.c_void_p), ("error_word", C.c_uint32), ("sink_k", C.c_void_p), ("sink_v", C.c_void_p),
+        ("pend_sel", C.c_void_p),
     ]
 
 
@@ -84,6 +85,8 @@ def lib():
         L.orc_prefill.argtypes = [C.POINTER(OrcCfg), C.POINTER(OrcState), vp, vp, vp, i64]
         L.orc_step.restype = i32
         L.orc_step.argtypes = [C.POINTER(OrcCfg), C.POINTER(OrcState), vp, vp, vp, vp, i32, i32]
+        L.orc_step_reuse.restype = i32
+        L.orc_step_reuse.argtypes = [C.POINTER(OrcCfg), C.POINTER(OrcState), vp, vp, vp, vp, i32]
         L.orc_full_attention.restype = None
         L.orc_full_attention.argtypes = [vp, vp, vp, i32, i32, vp]
         _lib = L
@@ -247,11 +250,12 @@ class Oracle:
         self.w_u = np.zeros((B, H), np.uint64)
         self.thresh = np.zeros((B, H), np.uint64)
         self.regularized = np.zeros((B, H), np.int32)
+        self.pend_sel = np.zeros((B, H), np.int64)
         self.st = OrcState(*[_p(getattr(self, n)) for n in (
             "dense_k", "dense_v", "pool_k", "pool_v", "view_k", "view_v", "view_pos", "cond_kn",
             "cond_vn", "cond_omega", "cond_n", "cond_cursor", "seq_len", "pool_head", "scores",
             "weights", "mask", "budget", "n_condense", "w_all", "w_u", "thresh", "regularized",
-            "view_off", "tau_fit")], 0, _p(self.sink_k), _p(self.sink_v))
+            "view_off", "tau_fit")], 0, _p(self.sink_k), _p(self.sink_v), _p(self.pend_sel))
 
     @property
     def error_word(self) -> int:
@@ -270,6 +274,18 @@ class Oracle:
                             1 if attend else 0, nthreads)
         if rc != 0:
             raise RuntimeError(f"orc_step failed: {rc}")
+        return out
+
+    def step_reuse(self, q, k_new, v_new, nthreads: int = 0) -> np.ndarray:
+        """A step that keeps the last selection: append, then attention over the sinks,
+        condensed slots, the last selection's kept rows, the pool positions since it, and
+        the dense window."""
+        qn, kn, vn = _store_np(q), _store_np(k_new), _store_np(v_new)
+        out = np.zeros((self.wl.batch, self.wl.num_q_heads, self.wl.head_dim), np.float64)
+        rc = lib().orc_step_reuse(C.byref(self.cfg), C.byref(self.st), _p(qn), _p(kn), _p(vn), _p(out),
+                                  nthreads)
+        if rc != 0:
+            raise RuntimeError(f"orc_step_reuse failed: {rc}")
         return out
 
     # logical views used by the tests ----------------------------------------------------

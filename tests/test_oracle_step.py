@@ -440,3 +440,84 @@ def test_entropy_calibration_step_uses_the_fitted_tau():
         assert np.array_equal(getattr(o_fit, n), getattr(o_ovr, n)), n
     assert np.array_equal(outs_fit[0], outs_ovr[0])
     np.testing.assert_array_equal(o_ovr.tau_fit, taus)
+
+
+# ---- steps that reuse the last selection ---------------------------------------------------
+def _reuse_run(wl, inp, pattern, **kw):
+    """pattern: a string of 's' (a step with selection) and 'r' (a step reusing it)."""
+    o = orc.Oracle(wl, **kw)
+    assert o.prefill(inp.k_ctx, inp.v_ctx, inp.ctx_len) == 0
+    outs = []
+    for s, ch in enumerate(pattern):
+        if ch == "s":
+            outs.append(o.step(inp.q[s], inp.k_new[s], inp.v_new[s]))
+        else:
+            outs.append(o.step_reuse(inp.q[s], inp.k_new[s], inp.v_new[s]))
+    return o, outs
+
+
+@pytest.mark.parametrize("pattern", ["srrr", "rrsr", "r"])
+def test_reuse_p1_off_equals_full_attention(pattern):
+    """p = 1 without condensation: the last selection kept its whole pool and every later
+    pool position is attended in full, so each step, with or without selection (before
+    the first selection too), is full attention over [0, t) bit for bit."""
+    steps = len(pattern)
+    wl = tiny_workload(cond_mode=COND_OFF, top_p=1.0, steps=steps)
+    inp = make_inputs(wl)
+    o, outs = _reuse_run(wl, inp, pattern)
+    G = wl.group
+    for s in range(steps):
+        for b in range(wl.batch):
+            for h in range(wl.num_kv_heads):
+                k, v = _positions_kv(inp, b, h, s + 1)
+                for g in range(G):
+                    qh = h * G + g
+                    full = orc.full_attention(_f32(inp.q[s, b, qh]), k, v)
+                    assert np.array_equal(outs[s][b, qh], full), (s, b, h, g)
+
+
+@pytest.mark.parametrize("policy", [0, 1])
+def test_reuse_attends_the_selection_and_what_came_after(policy):
+    """Eviction at p = 0.9, one selection and then three steps without one: the attended
+    set is the selection's kept positions, every pool position that arrived after it and
+    the dense window, so the output is full attention over exactly those positions, in
+    order (Rewrite Cache: from the view; Sparse Loading: from the pool through the mask)."""
+    pattern = "srrr"
+    wl = tiny_workload(steps=len(pattern), dense_window=16)
+    inp = make_inputs(wl)
+    o = orc.Oracle(wl, regularize=policy)
+    assert o.prefill(inp.k_ctx, inp.v_ctx, inp.ctx_len) == 0
+    outs = [o.step(inp.q[0], inp.k_new[0], inp.v_new[0])]
+    kept = {(b, h): o.selected_positions(b, h) for b in range(wl.batch) for h in range(wl.num_kv_heads)}
+    t_sel = o.seq_len.copy()
+    assert all(len(kept[u]) == o.budget[u] for u in kept) and o.budget.min() > 0
+    for s in range(1, len(pattern)):
+        outs.append(o.step_reuse(inp.q[s], inp.k_new[s], inp.v_new[s]))
+        assert np.array_equal(o.seq_len, t_sel + s)
+    G, W = wl.group, wl.dense_window
+    s = len(pattern) - 1
+    for b in range(wl.batch):
+        t = int(o.seq_len[b])
+        for h in range(wl.num_kv_heads):
+            k, v = _positions_kv(inp, b, h, s + 1)
+            pos = np.concatenate([kept[b, h], np.arange(int(t_sel[b]) - W, t - W), np.arange(t - W, t)])
+            assert np.all(np.diff(pos) > 0)
+            for g in range(G):
+                qh = h * G + g
+                ref = orc.full_attention(_f32(inp.q[s, b, qh]), k[pos], v[pos])
+                assert np.array_equal(outs[s][b, qh], ref), (b, h, g)
+
+
+def test_reuse_then_select_condenses_the_grown_pool():
+    """Steps without selection condense nothing, so the pool grows past S_cap; the next
+    selection condenses it back (its E counts the blocks the reuse steps added), and the
+    pool head and cursor advance as in a run of selections that kept up."""
+    pattern = "s" + "r" * 70 + "s"
+    wl = tiny_workload(steps=len(pattern), ctx_len=330, ctx_min=300, cond_mode=COND_MERGE, condensed_slots=3,
+                       dense_window=16)
+    inp = make_inputs(wl)
+    o, _ = _reuse_run(wl, inp, pattern)
+    N = o.seq_len[:, None] - wl.dense_window - o.pool_head
+    assert np.all(N <= wl.sparse_cap) and np.all(o.pool_head % 64 == 0)
+    assert np.all(o.n_condense >= 1) and o.error_word == 0
+    assert np.all(o.cond_n.sum(-1) == 64 * (o.pool_head // 64))

@@ -193,7 +193,9 @@ HK_DEV void load_q_scaled(const Args &a, int b, int h, int sub, float (&qs)[G][8
 // Segments [0, nv_att) are view rows (rv_att each, up to k*), then nc_att segments of
 // condensed slots (rc_att each, slots with n > 0 only), then nd_att segments of dense
 // positions (rd_att each, positions [max(S, t - W), t)), then ns_att segments of sink
-// positions (rs_att each, [0, min(S, t))).  A merged slot holding n tokens
+// positions (rs_att each, [0, min(S, t))), then (a step without selection) nt_att segments
+// of the pool positions that arrived after the last selection, [pool end at t_plan, pool
+// end at t), each taking every nt_att-th piece of rt_att of them.  A merged slot holding n tokens
 // enters with key Kn/Omega, value Vn/Omega and logit bias ln n (log2 n in base 2).
 template <typename T, int G>
 HK_DEV void attend_segment(const Args &a, int bh, int seg, float (*s_part)[G][2 + HD]) {
@@ -287,7 +289,7 @@ HK_DEV void attend_segment(const Args &a, int bh, int seg, float (*s_part)[G][2 
       }
       attn_rows<T, G, 2>(st, qs, kr, vr, act);
     }
-  } else {  // sink positions [0, min(S, t)), row p of the head's sink rows
+  } else if (seg < a.nv_att + a.nc_att + a.nd_att + a.ns_att) {  // sink positions [0, min(S, t)), row p
     const int xs = seg - a.nv_att - a.nc_att - a.nd_att;
     slot = a.part_cd_base + a.nc_att + a.nd_att + xs;
     const int64_t p0 = (int64_t)xs * a.rs_att, p1 = min(min(p0 + (int64_t)a.rs_att, (int64_t)a.S), t);
@@ -309,6 +311,33 @@ HK_DEV void attend_segment(const Args &a, int bh, int seg, float (*s_part)[G][2 
         }
       }
       attn_rows<T, G, 2>(st, qs, kr, vr, act);
+    }
+  } else {  // pool positions since the last selection
+    const int xt = seg - a.nv_att - a.nc_att - a.nd_att - a.ns_att;
+    slot = a.part_cd_base + a.nc_att + a.nd_att + a.ns_att + xt;
+    const int64_t lo = pool_end(a.head[bh].t_plan, a.W, a.S), hi = pool_end(t, a.W, a.S);
+    const char *pk = (const char *)a.pool_k + (size_t)bh * a.P * BK * ROWB + sub * 8 * EB;
+    const char *pv = (const char *)a.pool_v + (size_t)bh * a.P * BK * ROWB + sub * 8 * EB;
+    for (int64_t q0 = lo + (int64_t)xt * a.rt_att; q0 < hi; q0 += (int64_t)a.nt_att * a.rt_att) {
+      const int64_t q1 = min(q0 + (int64_t)a.rt_att, hi);
+      for (int64_t base = q0; base < q1; base += 32) {
+        Raw8<T> kr[2], vr[2];
+        bool act[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int64_t p = base + j * 16 + rloc;
+          act[j] = p < q1;
+          if (act[j]) {
+            const size_t row = (size_t)((p / BK) % a.P) * BK + (size_t)(p % BK);
+            raw_load_nt(pk + row * ROWB, kr[j]);
+            raw_load_nt(pv + row * ROWB, vr[j]);
+          } else {
+            kr[j] = Raw8<T>{};
+            vr[j] = Raw8<T>{};
+          }
+        }
+        attn_rows<T, G, 2>(st, qs, kr, vr, act);
+      }
     }
   }
   attn_write_partial<G>(st, a.part + ((size_t)bh * a.npart + slot) * G * (2 + HD), s_part);

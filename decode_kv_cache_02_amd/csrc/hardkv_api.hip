@@ -111,7 +111,12 @@ int32_t plan(const hardkv_config *cfg, Plan &p) {
   a.rs_att = 128;
   a.ns_att = (a.S + a.rs_att - 1) / a.rs_att;
   a.part_cd_base = std::max(a.nch_reg, a.nv_att);
-  a.xp_base = a.part_cd_base + a.nc_att + a.nd_att + a.ns_att;  // then one slot per rewrite chunk
+  // a step without selection attends the pool positions since the last one in nt_att
+  // segments that stride over them in pieces of rt_att rows
+  a.rt_att = 128;
+  a.nt_att = 4;
+  a.ntp = 0;
+  a.xp_base = a.part_cd_base + a.nc_att + a.nd_att + a.ns_att + a.nt_att;  // then one slot per rewrite chunk
   a.npart = a.xp_base + a.nch_reg;
   // at most emax blocks condense in a step (a pool never exceeds its P*64 rows)
   const int emax = std::max(1, a.P - a.S_cap / BK);
@@ -233,6 +238,7 @@ hipError_t step_stage(const hardkv_config *cfg, Args &a, int stage, hipStream_t 
   const bool bf = is_bf16(cfg);
   a.nvp = a.nch_reg;
   a.nxp = 0;
+  a.ntp = 0;  // the step's own selection leaves no pool position unselected
   a.gather_mode = GATHER_STEP;
   const bool fuse = whole_step && a.cond_small;
   switch (stage) {
@@ -263,6 +269,7 @@ hipError_t attend_calls(const hardkv_config *cfg, Args &a, hipStream_t s, bool s
   const bool gather = sparse || a.reg_policy != HARDKV_REG_REWRITE;
   if (!views) a.nv_att = 0;
   a.nvp = a.nv_att;
+  a.ntp = a.nt_att;
   a.nxp = gather ? a.nch_reg : 0;
   a.gather_mode = sparse ? GATHER_ATTEND_ALL : GATHER_ATTEND_NRW;
   hipError_t e = launch_attend(a, s, bf);
@@ -384,6 +391,21 @@ int32_t hardkv_step(const hardkv_config *cfg, hardkv_state *st, const void *q, c
   p.a.v_new = v_new;
   p.a.out = out;
   return hip_status(step_all(cfg, p.a, (hipStream_t)stream));
+}
+
+int32_t hardkv_step_reuse(const hardkv_config *cfg, hardkv_state *st, const void *q, const void *k_new,
+                          const void *v_new, float *out, void *stream) {
+  Plan p;
+  int32_t rc = setup(cfg, st, p);
+  if (rc != HARDKV_OK) return rc;
+  if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(out)) return HARDKV_EINVAL;
+  p.a.q = q;
+  p.a.k_new = k_new;
+  p.a.v_new = v_new;
+  p.a.out = out;
+  hipError_t e = launch_append(p.a, (hipStream_t)stream, is_bf16(cfg));
+  if (e == hipSuccess) e = attend_calls(cfg, p.a, (hipStream_t)stream, false);
+  return hip_status(e);
 }
 
 int32_t hardkv_step_stage(const hardkv_config *cfg, hardkv_state *st, const void *q,

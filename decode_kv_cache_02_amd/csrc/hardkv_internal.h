@@ -117,6 +117,8 @@ struct Args {
   int rc_att, nc_att;       // attention over condensed slots
   int rd_att, nd_att;       // attention over the dense window
   int rs_att, ns_att;       // attention over the sink rows
+  int rt_att, nt_att;       // attention over the pool positions since the last selection
+  int ntp;                  // tail segments in this call's partials (0 or nt_att)
   int nvp;                  // view partial slots written by this call
   int npart, part_cd_base;  // partial slots per head; first condensed/dense slot
   int xp_base, nxp;         // gathered-row partial slots of the standalone attention

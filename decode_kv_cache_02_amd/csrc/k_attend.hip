@@ -38,10 +38,11 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_combine(Args a) {
   __shared__ float s_acc[HD];
   const float *base = a.part + (size_t)bh * a.npart * G * (2 + HD) + (size_t)g * (2 + HD);
   const size_t stride = (size_t)G * (2 + HD);  // from one partial slot to the next
-  const int ncd = a.nc_att + a.nd_att + a.ns_att;
+  const int ncd = a.nc_att + a.nd_att + a.ns_att + a.ntp;
   const int ns = a.nvp + ncd + a.nxp;
-  // partials: view or rewrite chunks at [0, nvp), condensed, dense and sink segments at
-  // part_cd_base, gathered-row chunks of the standalone attention at xp_base
+  // partials: view or rewrite chunks at [0, nvp), condensed, dense, sink and (without a
+  // selection this step) pool-tail segments at part_cd_base, gathered-row chunks of the
+  // standalone attention at xp_base
   auto slot = [&](int i) {
     return i < a.nvp ? i : (i < a.nvp + ncd ? a.part_cd_base + (i - a.nvp) : a.xp_base + (i - a.nvp - ncd));
   };
@@ -114,7 +115,7 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_combine(Args a) {
 
 template <typename T>
 hipError_t launch_tiers(const Args &a, hipStream_t s) {
-  dim3 grid(a.nv_att + a.nc_att + a.nd_att + a.ns_att, a.nbh);
+  dim3 grid(a.nv_att + a.nc_att + a.nd_att + a.ns_att + a.ntp, a.nbh);
   switch (a.G) {
     case 1: hipLaunchKernelGGL((hardkv_attend_tiers<T, 1>), grid, dim3(NTHREADS), 0, s, a); break;
     case 2: hipLaunchKernelGGL((hardkv_attend_tiers<T, 2>), grid, dim3(NTHREADS), 0, s, a); break;

@@ -39,7 +39,10 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_prefill(Args a) {
       a.pool_head[bh] = a.S;
       a.cond_cursor[bh] = 0;
       if (h == 0) a.seq_len[b] = L;
+      // no selection yet: an empty plan whose pool ends at the pool head, so that a step
+      // without selection attends the whole pool as positions since the last selection
       HeadInfo z = {};
+      z.c_plan = a.S;
       a.head[bh] = z;
     }
     for (int k = tid; k < a.C * HD; k += NTHREADS) {

@@ -28,7 +28,7 @@ BLOCK, HEAD_DIM = 64, 128
 
 EXPORTS = ("hardkv_workspace_size", "hardkv_prefill", "hardkv_append", "hardkv_select",
            "hardkv_regularize", "hardkv_condense", "hardkv_attend", "hardkv_attend_sparse", "hardkv_step",
-           "hardkv_step_stage", "hardkv_step_num_stages", "hardkv_step_stage_name",
+           "hardkv_step_reuse", "hardkv_step_stage", "hardkv_step_num_stages", "hardkv_step_stage_name",
            "hardkv_strerror")
 
 
@@ -83,6 +83,7 @@ def lib() -> C.CDLL:
         L.hardkv_attend.argtypes = [cp, sp, vp, vp, vp]
         L.hardkv_attend_sparse.argtypes = [cp, sp, vp, vp, vp]
         L.hardkv_step.argtypes = [cp, sp, vp, vp, vp, vp, vp]
+        L.hardkv_step_reuse.argtypes = [cp, sp, vp, vp, vp, vp, vp]
         L.hardkv_step_stage.argtypes = [cp, sp, vp, vp, vp, vp, i32, vp]
         L.hardkv_step_num_stages.argtypes = []
         L.hardkv_step_stage_name.argtypes = [i32]
@@ -259,6 +260,11 @@ def hardkv_attend_sparse(cfg: Config, st: State, q, out, stream=None) -> None:
 def hardkv_step(cfg: Config, st: State, q, k_new, v_new, out, stream=None) -> None:
     _check("hardkv_step", lib().hardkv_step(C.byref(cfg.c), C.byref(st.c), _ptr(q), _ptr(k_new),
                                             _ptr(v_new), _ptr(out), _stream(stream)))
+
+
+def hardkv_step_reuse(cfg: Config, st: State, q, k_new, v_new, out, stream=None) -> None:
+    _check("hardkv_step_reuse", lib().hardkv_step_reuse(C.byref(cfg.c), C.byref(st.c), _ptr(q), _ptr(k_new),
+                                                        _ptr(v_new), _ptr(out), _stream(stream)))
 
 
 def hardkv_step_stage(cfg: Config, st: State, q, k_new, v_new, out, stage: int, stream=None) -> None:

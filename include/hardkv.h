@@ -246,6 +246,20 @@ int32_t hardkv_attend_sparse(const hardkv_config *cfg, hardkv_state *st, const v
 int32_t hardkv_step(const hardkv_config *cfg, hardkv_state *st, const void *q, const void *k_new,
                     const void *v_new, float *out, void *stream);
 
+/* A step that keeps the last selection (section 2.C: a rewritten cache is used for later
+ * steps, spreading its cost over them; when to select again is the caller's choice, for
+ * example every R steps): the append, then attention over the sinks, the condensed slots,
+ * the rows the last selection kept (views of rewritten heads, pool rows through the mask
+ * for the others), every pool position that arrived after that selection (the pool end at
+ * its t up to the pool end now), and the dense window.  Nothing is scored, selected or
+ * condensed, so the pool grows by one position per step: pool_blocks must hold S_cap
+ * plus the positions of the steps between selections (HARDKV_ERR_POOL_OVERFLOW
+ * otherwise), and the next hardkv_step condenses what has accumulated.  Before any
+ * selection since the prefill, the whole pool counts as arrived after the last selection.
+ * Same arguments as hardkv_step; capturable. */
+int32_t hardkv_step_reuse(const hardkv_config *cfg, hardkv_state *st, const void *q, const void *k_new,
+                          const void *v_new, float *out, void *stream);
+
 /* Launches only kernel `stage` of hardkv_step (0 append, 1 score, 2 select, 3 condense,
  * 4 rewrite with the view, condensed and dense attention, 5 combine), for timing one
  * kernel on its own.  Stages 1, 2, 4 and 5 only read what earlier stages wrote and may

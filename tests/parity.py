@@ -118,6 +118,38 @@ class Pair:
             self.compare(pre, outs if (attend and check_attend) else None, check_views)
         self.step_i += 1
 
+    def step_reuse(self):
+        """A step that keeps the last selection on both sides; compares the attention
+        output, the counters and the error word (nothing is scored or selected)."""
+        s = self.step_i
+        hk.hardkv_step_reuse(self.cfg, self.st, self.inp.q[s], self.inp.k_new[s], self.inp.v_new[s], self.out)
+
+        def run(item):
+            key, (o, ui) = item
+            return key, o.step_reuse(ui.q[s], ui.k_new[s], ui.v_new[s], nthreads=0 if key is None else 1)
+        outs = dict(_POOL.map(run, list(self.orcs.items())))
+        torch.cuda.synchronize()
+        wl = self.wl
+        seq = self.st.seq_len.cpu().numpy()
+        head = self.st.pool_head.cpu().numpy()
+        err = 0
+        for key, (o, _) in self.orcs.items():
+            err |= o.error_word
+            units = ([(b, h) for b in range(wl.batch) for h in range(wl.num_kv_heads)] if key is None else [key])
+            for (b, h) in units:
+                ob, oh = (b, h) if key is None else (0, 0)
+                tag = f"reuse step {s} unit (b={b}, h={h})"
+                assert int(seq[b]) == int(o.seq_len[ob]), tag
+                assert int(head[b, h]) == int(o.pool_head[ob, oh]), tag
+                G = wl.group
+                go = self.out[b, h * G:(h + 1) * G].cpu().numpy()
+                oo = outs[key][b, h * G:(h + 1) * G] if key is None else outs[key][0]
+                e = row_rel_err(go, oo)
+                assert e <= ATT_TOL, f"{tag} attention rel err {e}"
+        ew = int(self.st.error_word[0].item())
+        assert (ew == err) if None in self.orcs else (ew & err == err), "error word"
+        self.step_i += 1
+
     # ---- comparison --------------------------------------------------------------------------
     def _gpu_unit(self, b, h, names):
         return {n: getattr(self.st, n)[b, h].cpu() for n in names}

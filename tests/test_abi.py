@@ -22,7 +22,7 @@ def _declared():
 def test_exports_every_declared_symbol():
     lib = hk.lib()
     names = _declared()
-    assert len(names) == 13, names
+    assert len(names) == 14, names
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(hk.EXPORTS)
@@ -135,6 +135,7 @@ def test_state_validation(kind):
     L = hk.lib()
     q = C.c_void_p(1 << 41)
     assert L.hardkv_step(C.byref(cfg.c), C.byref(st), q, q, q, q, None) == expect
+    assert L.hardkv_step_reuse(C.byref(cfg.c), C.byref(st), q, q, q, q, None) == expect
     assert L.hardkv_select(C.byref(cfg.c), C.byref(st), q, None) == expect
     assert L.hardkv_regularize(C.byref(cfg.c), C.byref(st), None) == expect
 
@@ -148,6 +149,7 @@ def test_call_argument_validation():
     bad = C.c_void_p((1 << 41) + 8)
     assert L.hardkv_step(C.byref(cfg.c), C.byref(st), bad, ok, ok, ok, None) == hk.HARDKV_EINVAL
     assert L.hardkv_step(C.byref(cfg.c), C.byref(st), ok, None, ok, ok, None) == hk.HARDKV_EINVAL
+    assert L.hardkv_step_reuse(C.byref(cfg.c), C.byref(st), ok, ok, bad, ok, None) == hk.HARDKV_EINVAL
     assert L.hardkv_attend(C.byref(cfg.c), C.byref(st), ok, bad, None) == hk.HARDKV_EINVAL
     assert L.hardkv_attend_sparse(C.byref(cfg.c), C.byref(st), bad, ok, None) == hk.HARDKV_EINVAL
     assert L.hardkv_step_stage(C.byref(cfg.c), C.byref(st), ok, ok, ok, ok, 6, None) == hk.HARDKV_EINVAL

@@ -504,3 +504,49 @@ def test_overflowing_product_keeps_the_plain_tree():
     assert np.array_equal(g, o.scores[0, 0][rows].view(np.uint32))
     assert np.isposinf(o.scores[0, 0][3])
     assert int(pr.st.error_word[0].item()) & 4 and o.error_word & 4
+
+
+# ---- steps that reuse the last selection ---------------------------------------------------
+# pattern: 's' a step with selection (hardkv_step, or the separate calls for 'c'), 'r' a step
+# that keeps the last selection (hardkv_step_reuse)
+REUSE_CASES = {
+    "evict_bf16": (dict(), 0, "srrsrr"),
+    "merge_f32": (dict(dtype="f32", cond_mode=COND_MERGE), 0, "srrrs"),
+    # before any selection the whole pool is attended as arrived since the last one
+    "before_selection": (dict(cond_mode=COND_MERGE), 0, "rrsr"),
+    "composition": (dict(cond_mode=COND_MERGE), 0, "crrcr"),
+    "sparse_policy": (dict(cond_mode=COND_MERGE, ctx_len=500, ctx_min=100), 1, "srrsr"),
+    "mti": (dict(batch=4, heavy=(0, 6)), 2, "srrr"),
+    "packed": (dict(cond_mode=COND_MERGE), "packed", "srrsr"),
+    "sink": (dict(sink=64, cond_mode=COND_MERGE, ctx_len=500, ctx_min=100), 0, "srrsr"),
+    "g8": (dict(num_q_heads=16, num_kv_heads=2), 0, "srrr"),
+    # 70 steps without selection: the tail outgrows a segment's piece, the pool outgrows
+    # S_cap, and the next selection condenses the backlog (ring wrap of 3 slots)
+    "long_tail": (dict(ctx_len=330, ctx_min=300, cond_mode=COND_MERGE, condensed_slots=3, dense_window=16), 0,
+                  "s" + "r" * 70 + "srr"),
+}
+
+
+@pytest.mark.parametrize("name", list(REUSE_CASES))
+def test_reuse_parity(name):
+    """Steps that keep the last selection attend its kept rows, the pool positions since
+    it, the dense window, condensed slots and sinks: the oracle's output within 2e-3 at
+    every step, and every selection step between them bit-exact as usual."""
+    from parity import Pair
+    kw, pol, pattern = REUSE_CASES[name]
+    wl = tiny_workload(steps=len(pattern), **kw)
+    extra = {}
+    if pol == "packed":
+        extra = dict(view_layout=1, view_total=wl.batch * wl.num_kv_heads * wl.V_cap)
+    elif pol == 2:
+        lo, hi = _mti_bounds(wl)
+        extra = dict(regularize=2, mti_lower=lo, mti_upper=hi)
+    elif pol:
+        extra = dict(regularize=pol)
+    print(f"case {name}: {pattern} {extra} {wl}", flush=True)
+    pr = Pair(wl, **extra)
+    for ch in pattern:
+        if ch == "r":
+            pr.step_reuse()
+        else:
+            pr.step(fused=(ch == "s"))

@@ -78,6 +78,10 @@ def parse():
                     help="packed view rows for --view-layout sum (0: batch * kv_heads * view_cap)")
     ap.add_argument("--sink", type=int, default=None,
                     help="sink prefix tokens S (a multiple of 64; default: the workload's, 0)")
+    ap.add_argument("--select-every", type=int, default=1,
+                    help="also time steps that select once every R steps and reuse the selection in "
+                         "between (hardkv_step_reuse), reported under select_every; the pool ring gets "
+                         "ceil(R / 64) + 1 more blocks for the positions that accumulate between selections")
     ap.add_argument("--stage-reps", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-units", type=int, default=0, help="oracle sample size in units (0: automatic)")
@@ -120,6 +124,9 @@ class Layer:
 
     def step(self, s):
         hk.hardkv_step(self.cfg, self.st, self.inp.q[s], self.inp.k_new[s], self.inp.v_new[s], self.out)
+
+    def reuse(self, s):
+        hk.hardkv_step_reuse(self.cfg, self.st, self.inp.q[s], self.inp.k_new[s], self.inp.v_new[s], self.out)
 
     def stage(self, s, k):
         hk.hardkv_step_stage(self.cfg, self.st, self.inp.q[s], self.inp.k_new[s], self.inp.v_new[s],
@@ -202,6 +209,48 @@ def time_repeatable_stage(layers, s, k, reps, eager):
         torch.cuda.synchronize()
         ts.append(e0.elapsed_time(e1))
     return float(np.median(ts)) * 1e3 / (reps * len(layers))
+
+
+def select_every(layers, R, restore_mode, snaps, Wm, K, timed, eager):
+    """Steps that select once every R steps and keep that selection in between
+    (hardkv_step_reuse): single-step workloads replay [a step with selection, R - 1 steps
+    without] from the prefilled state; the streaming one runs its K timed steps with a
+    selection at every R-th.  Returns the mean time per step and what the R - 1 steps
+    without selection cost each."""
+    def restore():
+        for L, sn in zip(layers, snaps):
+            L.restore(sn)
+
+    steps = list(range(R)) if restore_mode else list(range(Wm, Wm + K))
+    first = steps[0]
+
+    def run():
+        for s in steps:
+            for L in layers:
+                L.step(s) if (s - first) % R == 0 else L.reuse(s)
+
+    restore()
+    run()
+    restore()
+    torch.cuda.synchronize()
+    g = None
+    if not eager:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            run()
+        torch.cuda.synchronize()
+    times = []
+    for _ in range(3 if not restore_mode else max(3, K // R)):
+        restore()
+        torch.cuda.synchronize()
+        times.append(timed(g.replay if g is not None else run))
+    err = int(max(int(L.st.error_word[0].item()) for L in layers))
+    restore()
+    torch.cuda.synchronize()
+    ms_step = float(np.mean(times)) / len(steps)
+    return {"R": R, "ms_per_step": ms_step, "steps_per_s": 1e3 / ms_step, "error_word": err,
+            "timing": ("graph of one step with selection and R - 1 without, from the prefilled state"
+                       if restore_mode else "graph of the K streaming steps, a selection at every R-th")}
 
 
 def device_copy_reference(nbytes, reps=10):
@@ -482,11 +531,14 @@ def main():
     wl = get_workload(args.config)
     if args.sink is not None:
         wl = dataclasses.replace(wl, sink=args.sink)
+    R = max(1, args.select_every)
+    if R > 1:
+        wl = dataclasses.replace(wl, pool_blocks=wl.P_blk + (R + 63) // 64 + 1)
     top_p = args.top_p
     # single-step workloads: every timed step is the step from the prefilled context
     restore_mode = wl.steps == 1
     K, Wm = args.steps, args.warmup
-    nsteps = 1 if restore_mode else Wm + K
+    nsteps = R if restore_mode else Wm + K
 
     layers = []
     for layer in range(wl.layers):
@@ -641,6 +693,10 @@ def main():
                      "copy_reference": device_copy_reference(dom_bytes_launch)},
         "graph_replay_matches_eager": replay_matches,
     }
+    if R > 1:
+        res["select_every"] = select_every(layers, R, restore_mode, snaps if restore_mode else snap_after, Wm, K,
+                                           timed, args.eager)
+        res["config"]["pool_blocks"] = wl.P_blk
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wl, layers, args.cpu_units, args.cpu_seconds)
     print(json.dumps(res))

@@ -221,24 +221,47 @@ HK_DEV void attend_segment(const Args &a, int bh, int seg, float (*s_part)[G][2 
     const int64_t vcap = a.view_sum ? max((int64_t)0, a.view_rows - voff) : (int64_t)a.V_cap;
     const int64_t kst = a.head[bh].rw ? min((int64_t)a.budget[bh], vcap) : 0;
     const int64_t r0 = (int64_t)seg * a.rv_att, r1 = min(r0 + (int64_t)a.rv_att, kst);
-    const char *vk = (const char *)a.view_k + (size_t)voff * ROWB + sub * 8 * EB;
-    const char *vv = (const char *)a.view_v + (size_t)voff * ROWB + sub * 8 * EB;
-    for (int64_t base = r0; base < r1; base += 32) {
-      Raw8<T> kr[2], vr[2];
-      bool act[2];
+    if (r0 < r1) {  // uniform
+      // the head's view rows [0, r1) through buffer resources: a row past r1 gets an
+      // offset outside the range (the load returns zeros, with no branch around it), and
+      // the next batch's loads are in flight while the current one is attended
+      const BufRes vk = make_buf((const char *)a.view_k + (size_t)voff * ROWB, (uint64_t)r1 * ROWB);
+      const BufRes vv = make_buf((const char *)a.view_v + (size_t)voff * ROWB, (uint64_t)r1 * ROWB);
+      const uint32_t lane_b = (uint32_t)(sub * 8 * EB);
+      constexpr int VB = EB == 2 ? 4 : 2;  // rows per 16-lane group in a batch (fp32 rows: registers)
+      auto issue = [&](Raw8<T> (&kr)[VB], Raw8<T> (&vr)[VB], int64_t base) {
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int64_t r = base + j * 16 + rloc;
-        act[j] = r < r1;
-        if (act[j]) {
-          raw_load_nt(vk + (size_t)r * ROWB, kr[j]);
-          raw_load_nt(vv + (size_t)r * ROWB, vr[j]);
-        } else {
-          kr[j] = Raw8<T>{};
-          vr[j] = Raw8<T>{};
+        for (int j = 0; j < VB; ++j) {
+          const int64_t r = base + j * 16 + rloc;
+          const uint32_t off = r < r1 ? (uint32_t)((size_t)r * ROWB) + lane_b : BUF_SKIP;
+          buf_load_nt(vk, off, kr[j]);
+          buf_load_nt(vv, off, vr[j]);
         }
+      };
+      auto consume = [&](const Raw8<T> (&kr)[VB], const Raw8<T> (&vr)[VB], int64_t base) {
+        bool act[VB];
+#pragma unroll
+        for (int j = 0; j < VB; ++j) act[j] = base + j * 16 + rloc < r1;
+        attn_rows<T, G, VB>(st, qs, kr, vr, act);
+      };
+      // (the scheduling barriers keep each batch's loads ahead of the other batch's
+      // arithmetic, where the compiler would otherwise sink them)
+      Raw8<T> kA[VB], vA[VB], kB[VB], vB[VB];
+      const int nb = (int)((r1 - r0 + 16 * VB - 1) / (16 * VB));
+      int64_t base = r0;
+      issue(kA, vA, base);
+      for (int i = 0; i + 2 <= nb; i += 2) {
+        issue(kB, vB, base + 16 * VB);
+        __builtin_amdgcn_sched_barrier(0);
+        consume(kA, vA, base);
+        __builtin_amdgcn_sched_barrier(0);
+        issue(kA, vA, base + 32 * VB);
+        __builtin_amdgcn_sched_barrier(0);
+        consume(kB, vB, base + 16 * VB);
+        __builtin_amdgcn_sched_barrier(0);
+        base += 32 * VB;
       }
-      attn_rows<T, G, 2>(st, qs, kr, vr, act);
+      if (nb & 1) consume(kA, vA, base);
     }
   } else if (seg < a.nv_att + a.nc_att) {  // condensed slots
     const int xc = seg - a.nv_att;

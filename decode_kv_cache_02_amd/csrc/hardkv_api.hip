@@ -102,7 +102,7 @@ int32_t plan(const hardkv_config *cfg, Plan &p) {
   const int max_survivor_blocks = a.mode == HARDKV_COND_OFF ? a.P : std::min(a.P, a.S_cap / BK);
   a.cb_reg = 4;
   a.nch_reg = (max_survivor_blocks + a.cb_reg - 1) / a.cb_reg;
-  a.rv_att = 256;
+  a.rv_att = 512;
   a.nv_att = (a.V_cap + a.rv_att - 1) / a.rv_att;
   a.rc_att = 64;
   a.nc_att = (a.C + a.rc_att - 1) / a.rc_att;

@@ -25,6 +25,10 @@ HK_DEV void condense_chain(const Args &a, int bh, int i, int64_t c, int64_t E, i
   const int lane = threadIdx.x & 63;
   const int sub = lane & 15, grp = lane >> 4;
   const int P = a.P, C = a.C;
+  const size_t sg = (size_t)bh * C + (size_t)((nu + i) % C);
+  // an empty slot (n = 0, as every slot is after a prefill) holds zeros: it is written
+  // without being read back
+  const bool fresh = a.cond_n[sg] == 0;
   float ak[8], av[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) ak[k] = av[k] = 0.0f;
@@ -78,11 +82,17 @@ HK_DEV void condense_chain(const Args &a, int bh, int i, int64_t c, int64_t E, i
   }
   const double wa = (double)w_all;
   const float inv = (float)(1.0 / wa);
-  const size_t sg = (size_t)bh * C + (size_t)((nu + i) % C);
   if (lane < 16) {
     float4 *kn = reinterpret_cast<float4 *>(a.cond_kn + sg * HD + sub * 8);
     float4 *vn = reinterpret_cast<float4 *>(a.cond_vn + sg * HD + sub * 8);
-    float4 k0 = kn[0], k1 = kn[1], v0 = vn[0], v1 = vn[1];
+    const float4 z = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    float4 k0 = z, k1 = z, v0 = z, v1 = z;
+    if (!fresh) {
+      k0 = kn[0];
+      k1 = kn[1];
+      v0 = vn[0];
+      v1 = vn[1];
+    }
     k0.x += ak[0] * inv; k0.y += ak[1] * inv; k0.z += ak[2] * inv; k0.w += ak[3] * inv;
     k1.x += ak[4] * inv; k1.y += ak[5] * inv; k1.z += ak[6] * inv; k1.w += ak[7] * inv;
     v0.x += av[0] * inv; v0.y += av[1] * inv; v0.z += av[2] * inv; v0.w += av[3] * inv;
@@ -90,7 +100,7 @@ HK_DEV void condense_chain(const Args &a, int bh, int i, int64_t c, int64_t E, i
     kn[0] = k0; kn[1] = k1; vn[0] = v0; vn[1] = v1;
   }
   if (lane == 0) {
-    a.cond_omega[sg] += (float)((double)wsum / wa);
+    a.cond_omega[sg] = (fresh ? 0.0f : a.cond_omega[sg]) + (float)((double)wsum / wa);
     a.cond_n[sg] += BK * nblk;
   }
 }

@@ -35,6 +35,7 @@
 //   histogram and masses to memory), hardkv_sel_cut (per head: the cut bucket),
 //   hardkv_sel_count (pass B per slice: per-block counts, the bucket's tokens through a
 //   counter) and hardkv_sel_finish (per head: the same ending as the one-workgroup kernel).
+#include <mutex>
 #include <type_traits>
 
 #include "condense_common.h"
@@ -1338,20 +1339,22 @@ hipError_t launch_flatten(const Args &a, hipStream_t s) {
 }
 
 hipError_t launch_select(const Args &a, hipStream_t s, bool bf16) {
-  static bool configured = false;  // the attributes are per function, set once per process
-  if (!configured) {
+  // the dynamic LDS limit is an attribute of each function: raised once per process
+  static std::once_flag once;
+  static hipError_t configured = hipSuccess;
+  std::call_once(once, [] {
     const void *fs[] = {(const void *)hardkv_select<BF16, false>, (const void *)hardkv_select<BF16, true>,
                         (const void *)hardkv_select<F32, true>, (const void *)hardkv_sel_weigh,
                         (const void *)hardkv_sel_cut, (const void *)hardkv_sel_count,
                         (const void *)hardkv_sel_finish<BF16, false>, (const void *)hardkv_sel_finish<BF16, true>,
                         (const void *)hardkv_sel_finish<F32, true>};
     for (const void *f : fs) {
-      hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                         (int)sel_lds_bytes(MAX_POOL_BLOCKS));
-      if (e != hipSuccess) return e;
+      const hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                               (int)sel_lds_bytes(MAX_POOL_BLOCKS));
+      if (e != hipSuccess && configured == hipSuccess) configured = e;
     }
-    configured = true;
-  }
+  });
+  if (configured != hipSuccess) return configured;
   // (the storage type matters only to the condensation; without it one instance serves)
   auto sel = !a.fuse_cond ? hardkv_select<BF16, false> : bf16 ? hardkv_select<BF16, true> : hardkv_select<F32, true>;
   auto fin = !a.fuse_cond ? hardkv_sel_finish<BF16, false>

@@ -47,7 +47,7 @@ class Pair:
 
     def __init__(self, wl, inputs=None, top_p=None, tau=None, cond_mode=None, merge_bias=True,
                  device="cuda", oracle_units=None, layer=0, regularize=0, mti_lower=0, mti_upper=0,
-                 view_layout=0, view_total=0):
+                 view_layout=0, view_total=0, make_state=None):
         self.wl = wl if cond_mode is None else wl.with_(cond_mode=cond_mode)
         if top_p is not None:
             self.wl = self.wl.with_(top_p=top_p)
@@ -58,7 +58,7 @@ class Pair:
         self.packed = view_layout == hk.HARDKV_VIEW_SUM
         assert not (self.packed and oracle_units is not None), "packed views need the whole layer"
         self.cfg = hk.Config.from_workload(self.wl, tau=self.tau, merge_bias=merge_bias, **pol)
-        self.st = hk.State(self.cfg, device=device)
+        self.st = (make_state or hk.State)(self.cfg, device=device)
         hk.hardkv_prefill(self.cfg, self.st, self.inp.k_ctx, self.inp.v_ctx, self.inp.ctx_len)
         self.units = oracle_units
         self.orcs = {}

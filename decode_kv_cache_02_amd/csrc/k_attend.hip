@@ -26,16 +26,21 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_attend_tiers(Args a) {
 
 constexpr int MAX_COMBINE = 2048;  // partials per round of the combine
 
+constexpr int COMB_THREADS = 512;                // threads of the combine workgroup
+constexpr int COMB_WAVES = COMB_THREADS / 64;
+constexpr int COMB_STREAMS = COMB_THREADS / HD;  // partials summed in this many streams of 128 dims
+constexpr int COMB_UNR = 8;                      // loads in flight per thread
+
 template <int G>
-__global__ __launch_bounds__(NTHREADS) void hardkv_combine(Args a) {
+__global__ __launch_bounds__(COMB_THREADS) void hardkv_combine(Args a) {
   const int g = blockIdx.x, bh = a.bh0 + blockIdx.y;
   const int b = bh / a.Hkv, h = bh - b * a.Hkv;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   __shared__ float s_f[MAX_COMBINE];
   __shared__ int s_slot[MAX_COMBINE];
-  __shared__ float s_red[4];
-  __shared__ int s_cnt[4];
-  __shared__ float s_acc[HD];
+  __shared__ float s_red[COMB_WAVES];
+  __shared__ int s_cnt[COMB_WAVES];
+  __shared__ float s_acc[COMB_STREAMS][HD];
   const float *base = a.part + (size_t)bh * a.npart * G * (2 + HD) + (size_t)g * (2 + HD);
   const size_t stride = (size_t)G * (2 + HD);  // from one partial slot to the next
   const int ncd = a.nc_att + a.nd_att + a.ns_att + a.ntp;
@@ -49,7 +54,7 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_combine(Args a) {
 
   // the common maximum of the partials that saw any row
   float M = -INFINITY;
-  for (int i = tid; i < ns; i += NTHREADS) {
+  for (int i = tid; i < ns; i += COMB_THREADS) {
     const float *ps = base + (size_t)slot(i) * stride;
     if (ps[1] > 0.0f) M = fmaxf(M, ps[0]);
   }
@@ -57,19 +62,21 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_combine(Args a) {
   for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
   if (lane == 0) s_red[wave] = M;
   __syncthreads();
-  M = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+  M = s_red[0];
+#pragma unroll
+  for (int w = 1; w < COMB_WAVES; ++w) M = fmaxf(M, s_red[w]);
   __syncthreads();
 
   // per round: the scale factors 2^(m - M) of the partials that carry weight, listed in
   // partial order, and the scaled sum of l; then the scaled sum of their accumulators in
-  // two streams of 128 head dims, 8 partials in flight
-  const int d = tid & (HD - 1), half = tid >> 7;
+  // COMB_STREAMS streams of 128 head dims, COMB_UNR partials in flight per stream
+  const int d = tid & (HD - 1), strm = tid >> 7;
   float L = 0.0f, A = 0.0f;
   for (int r0 = 0; r0 < ns; r0 += MAX_COMBINE) {
     const int r1 = min(ns, r0 + MAX_COMBINE);
     float Lp = 0.0f;
     int nnz = 0;
-    for (int ib = r0; ib < r1; ib += NTHREADS) {
+    for (int ib = r0; ib < r1; ib += COMB_THREADS) {
       const int i = ib + tid;
       float f = 0.0f;
       if (i < r1) {
@@ -80,37 +87,45 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_combine(Args a) {
       const uint64_t bal = ballot(f > 0.0f);
       if (lane == 0) s_cnt[wave] = __popcll(bal);
       __syncthreads();
-      int before = nnz;
+      int before = nnz, all = 0;
 #pragma unroll
-      for (int w = 0; w < 4; ++w) before += w < wave ? s_cnt[w] : 0;
+      for (int w = 0; w < COMB_WAVES; ++w) {
+        before += w < wave ? s_cnt[w] : 0;
+        all += s_cnt[w];
+      }
       if (f > 0.0f) {
         const int pos = before + (int)popc_below(bal);
         s_slot[pos] = slot(i);
         s_f[pos] = f;
       }
-      nnz += s_cnt[0] + s_cnt[1] + s_cnt[2] + s_cnt[3];
+      nnz += all;
       __syncthreads();
     }
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) Lp += __shfl_xor(Lp, off);
     if (lane == 0) s_red[wave] = Lp;
     __syncthreads();
-    L += s_red[0] + s_red[1] + s_red[2] + s_red[3];
-    int k = half;
-    for (; k + 14 < nnz; k += 16) {
-      float x[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) x[u] = base[(size_t)s_slot[k + 2 * u] * stride + 2 + d];
+    for (int w = 0; w < COMB_WAVES; ++w) L += s_red[w];
+    int k = strm;
+    for (; k + (COMB_UNR - 1) * COMB_STREAMS < nnz; k += COMB_UNR * COMB_STREAMS) {
+      float x[COMB_UNR];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) A = __builtin_fmaf(x[u], s_f[k + 2 * u], A);
+      for (int u = 0; u < COMB_UNR; ++u) x[u] = base[(size_t)s_slot[k + COMB_STREAMS * u] * stride + 2 + d];
+#pragma unroll
+      for (int u = 0; u < COMB_UNR; ++u) A = __builtin_fmaf(x[u], s_f[k + COMB_STREAMS * u], A);
     }
-    for (; k < nnz; k += 2) A = __builtin_fmaf(base[(size_t)s_slot[k] * stride + 2 + d], s_f[k], A);
+    for (; k < nnz; k += COMB_STREAMS) A = __builtin_fmaf(base[(size_t)s_slot[k] * stride + 2 + d], s_f[k], A);
     __syncthreads();
   }
-  if (half == 1) s_acc[d] = A;
+  s_acc[strm][d] = A;
   __syncthreads();
-  if (half == 0)
-    a.out[((size_t)b * a.Hq + (size_t)h * G + g) * HD + d] = (A + s_acc[d]) / L;
+  if (strm == 0) {
+    float sum = s_acc[0][d];
+#pragma unroll
+    for (int q = 1; q < COMB_STREAMS; ++q) sum += s_acc[q][d];
+    a.out[((size_t)b * a.Hq + (size_t)h * G + g) * HD + d] = sum / L;
+  }
 }
 
 template <typename T>
@@ -135,10 +150,10 @@ hipError_t launch_attend(const Args &a, hipStream_t s, bool bf16) {
 hipError_t launch_combine(const Args &a, hipStream_t s) {
   dim3 grid(a.G, a.nbh);
   switch (a.G) {
-    case 1: hipLaunchKernelGGL((hardkv_combine<1>), grid, dim3(NTHREADS), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((hardkv_combine<2>), grid, dim3(NTHREADS), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((hardkv_combine<4>), grid, dim3(NTHREADS), 0, s, a); break;
-    case 8: hipLaunchKernelGGL((hardkv_combine<8>), grid, dim3(NTHREADS), 0, s, a); break;
+    case 1: hipLaunchKernelGGL((hardkv_combine<1>), grid, dim3(COMB_THREADS), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((hardkv_combine<2>), grid, dim3(COMB_THREADS), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((hardkv_combine<4>), grid, dim3(COMB_THREADS), 0, s, a); break;
+    case 8: hipLaunchKernelGGL((hardkv_combine<8>), grid, dim3(COMB_THREADS), 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

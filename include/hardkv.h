@@ -242,7 +242,8 @@ int32_t hardkv_attend_sparse(const hardkv_config *cfg, hardkv_state *st, const v
                              void *stream);
 
 /* The whole step: append, select, regularize, condense, attend, in one stream-ordered,
- * capturable sequence (the view attention is fused into the rewrite). */
+ * capturable sequence (the view attention is fused into the rewrite, and when at most four
+ * blocks can condense per step, P - S_cap/64 <= 4, the condensation into the select). */
 int32_t hardkv_step(const hardkv_config *cfg, hardkv_state *st, const void *q, const void *k_new,
                     const void *v_new, float *out, void *stream);
 
@@ -262,8 +263,8 @@ int32_t hardkv_step_reuse(const hardkv_config *cfg, hardkv_state *st, const void
 
 /* Launches only kernel `stage` of hardkv_step (0 append, 1 score, 2 select, 3 condense,
  * 4 rewrite with the view, condensed and dense attention, 5 combine), for timing one
- * kernel on its own.  Stages 1, 2, 4 and 5 only read what earlier stages wrote and may
- * be repeated; 0 and 3 advance the state. */
+ * kernel on its own; the condensation is always its own stage here.  Stages 1, 2, 4 and 5
+ * only read what earlier stages wrote and may be repeated; 0 and 3 advance the state. */
 int32_t hardkv_step_stage(const hardkv_config *cfg, hardkv_state *st, const void *q,
                           const void *k_new, const void *v_new, float *out, int32_t stage,
                           void *stream);

@@ -340,6 +340,8 @@ ENTROPY_CASES = {
     "split_long": dict(ctx_len=70000, ctx_min=60000, sparse_cap=69632, cond_mode=COND_MERGE),
     # the fit over ten slices, the last one ragged
     "fit_ten_slices": dict(ctx_len=40000, ctx_min=36000, sparse_cap=32768, cond_mode=COND_MERGE),
+    # with a sink prefix the pool (and the fit's rows) start at S
+    "sink": dict(sink=128, cond_mode=COND_MERGE, ctx_len=500, ctx_min=200),
 }
 
 

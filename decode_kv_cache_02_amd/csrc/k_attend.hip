@@ -26,13 +26,15 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_attend_tiers(Args a) {
 
 constexpr int MAX_COMBINE = 2048;  // partials per round of the combine
 
-constexpr int COMB_THREADS = 512;                // threads of the combine workgroup
-constexpr int COMB_WAVES = COMB_THREADS / 64;
-constexpr int COMB_STREAMS = COMB_THREADS / HD;  // partials summed in this many streams of 128 dims
-constexpr int COMB_UNR = 8;                      // loads in flight per thread
+constexpr int COMB_UNR = 8;  // loads in flight per thread
+// heads with at least this many partials are combined by 512 threads (four streams of 128
+// head dims), fewer by 256 (two streams), which start and finish sooner
+constexpr int COMB_WIDE_MIN = 256;
 
-template <int G>
+template <int G, int COMB_THREADS>
 __global__ __launch_bounds__(COMB_THREADS) void hardkv_combine(Args a) {
+  constexpr int COMB_WAVES = COMB_THREADS / 64;
+  constexpr int COMB_STREAMS = COMB_THREADS / HD;  // partials summed in this many streams of 128 dims
   const int g = blockIdx.x, bh = a.bh0 + blockIdx.y;
   const int b = bh / a.Hkv, h = bh - b * a.Hkv;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -147,16 +149,22 @@ hipError_t launch_attend(const Args &a, hipStream_t s, bool bf16) {
   return bf16 ? launch_tiers<BF16>(a, s) : launch_tiers<F32>(a, s);
 }
 
-hipError_t launch_combine(const Args &a, hipStream_t s) {
+template <int CT>
+hipError_t launch_combine_t(const Args &a, hipStream_t s) {
   dim3 grid(a.G, a.nbh);
   switch (a.G) {
-    case 1: hipLaunchKernelGGL((hardkv_combine<1>), grid, dim3(COMB_THREADS), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((hardkv_combine<2>), grid, dim3(COMB_THREADS), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((hardkv_combine<4>), grid, dim3(COMB_THREADS), 0, s, a); break;
-    case 8: hipLaunchKernelGGL((hardkv_combine<8>), grid, dim3(COMB_THREADS), 0, s, a); break;
+    case 1: hipLaunchKernelGGL((hardkv_combine<1, CT>), grid, dim3(CT), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((hardkv_combine<2, CT>), grid, dim3(CT), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((hardkv_combine<4, CT>), grid, dim3(CT), 0, s, a); break;
+    case 8: hipLaunchKernelGGL((hardkv_combine<8, CT>), grid, dim3(CT), 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+hipError_t launch_combine(const Args &a, hipStream_t s) {
+  const int ns = a.nvp + a.nc_att + a.nd_att + a.ns_att + a.ntp + a.nxp;  // partials per head
+  return ns >= COMB_WIDE_MIN ? launch_combine_t<512>(a, s) : launch_combine_t<256>(a, s);
 }
 
 }  // namespace hardkv

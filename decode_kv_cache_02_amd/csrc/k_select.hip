@@ -1199,8 +1199,9 @@ HK_DEV int64_t fit_pool(const Args &a, int bh, int64_t &c) {
   return pool_end(a.seq_len[b], a.W, a.S) - c;
 }
 
-// hardkv_fit, grid (B*Hkv), 512 threads: one workgroup per head.  The target is the mean over the group's queries of the entropy
-// (nats) of their raw attention over the pool; then five rounds of a 17-point grid on
+// hardkv_fit, grid (B*Hkv), 512 threads: one workgroup per head.  The target is the mean
+// over the group's queries of the entropy (nats) of their raw attention over the pool;
+// then five rounds of a 17-point grid on
 // log2 tau in [-12, 12] find the bracket where the entropy of the calibrated
 // softmax(s / (sqrt(D) tau)) over the pool reaches the target (it grows with tau); tau
 // is the midpoint of the last bracket.

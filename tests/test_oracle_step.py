@@ -521,3 +521,59 @@ def test_reuse_then_select_condenses_the_grown_pool():
     assert np.all(N <= wl.sparse_cap) and np.all(o.pool_head % 64 == 0)
     assert np.all(o.n_condense >= 1) and o.error_word == 0
     assert np.all(o.cond_n.sum(-1) == 64 * (o.pool_head // 64))
+
+
+def test_reuse_with_sinks_p1_off_equals_full_attention():
+    """A sink prefix of S = 64 under steps that reuse a selection: at p = 1 without
+    condensation every step is still full attention over [0, t) bit for bit."""
+    pattern = "srrsr"
+    wl = tiny_workload(cond_mode=COND_OFF, top_p=1.0, steps=len(pattern), sink=64)
+    inp = make_inputs(wl)
+    o, outs = _reuse_run(wl, inp, pattern)
+    G = wl.group
+    for s in range(len(pattern)):
+        for b in range(wl.batch):
+            for h in range(wl.num_kv_heads):
+                k, v = _positions_kv(inp, b, h, s + 1)
+                for g in range(G):
+                    full = orc.full_attention(_f32(inp.q[s, b, h * G + g]), k, v)
+                    assert np.array_equal(outs[s][b, h * G + g], full), (s, b, h, g)
+
+
+def test_reuse_with_merged_slots_matches_a_flat_softmax():
+    """With merged slots, a step that reuses the selection attends: each occupied slot as
+    one entry with key Kn/Omega, value Vn/Omega and logit bias ln n, then the kept rows,
+    the positions since the selection and the dense window.  A plain binary64 softmax
+    over exactly those entries, built here from the state and the inputs, agrees to
+    1e-12."""
+    pattern = "srrr"
+    wl = tiny_workload(steps=len(pattern), cond_mode=COND_MERGE, ctx_len=500, ctx_min=400, condensed_slots=3,
+                       dense_window=16)
+    inp = make_inputs(wl)
+    o = orc.Oracle(wl)
+    assert o.prefill(inp.k_ctx, inp.v_ctx, inp.ctx_len) == 0
+    o.step(inp.q[0], inp.k_new[0], inp.v_new[0])
+    assert o.cond_n.sum() > 0
+    kept = {(b, h): o.selected_positions(b, h) for b in range(wl.batch) for h in range(wl.num_kv_heads)}
+    t_sel = o.seq_len.copy()
+    outs = None
+    for s in range(1, len(pattern)):
+        outs = o.step_reuse(inp.q[s], inp.k_new[s], inp.v_new[s])
+    s = len(pattern) - 1
+    G, W, D = wl.group, wl.dense_window, wl.head_dim
+    for b in range(wl.batch):
+        t = int(o.seq_len[b])
+        for h in range(wl.num_kv_heads):
+            k, v = _positions_kv(inp, b, h, s + 1)
+            pos = np.concatenate([kept[b, h], np.arange(int(t_sel[b]) - W, t - W), np.arange(t - W, t)])
+            occ = np.nonzero(o.cond_n[b, h] > 0)[0]
+            om = o.cond_omega[b, h][occ][:, None]
+            keys = np.concatenate([o.cond_kn[b, h][occ] / om, k[pos].astype(np.float64)])
+            vals = np.concatenate([o.cond_vn[b, h][occ] / om, v[pos].astype(np.float64)])
+            bias = np.concatenate([np.log(o.cond_n[b, h][occ].astype(np.float64)), np.zeros(len(pos))])
+            for g in range(G):
+                q = _f32(inp.q[s, b, h * G + g]).astype(np.float64)
+                lg = keys @ q / np.sqrt(D) + bias
+                e = np.exp(lg - lg.max())
+                ref = (e[:, None] * vals).sum(0) / e.sum()
+                np.testing.assert_allclose(outs[b, h * G + g], ref, rtol=1e-12, atol=1e-14)

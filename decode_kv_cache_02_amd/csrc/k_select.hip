@@ -1235,6 +1235,24 @@ __global__ __launch_bounds__(FIT_THREADS) void hardkv_fit_prep(Args a) {
   }
 }
 
+// Round r's sums over the head's slices, added in slice order (candidate k's in thread k
+// < FIT_POINTS).  Every thread first copies some of the slices' sums into LDS, so that
+// the loads are in flight together rather than one slice after another.
+HK_DEV void fit_slice_sums(const Args &a, int bh, int r, double &Z, double &A) {
+  constexpr int PER = 2 * FIT_POINTS;
+  __shared__ double s_sl[FIT_MAX_SLICES * PER];
+  const int tid = threadIdx.x;
+  const double *ps = a.fitp + ((size_t)r * a.B * a.Hkv + bh) * a.nfs * PER;
+  for (int i = tid; i < a.nfs * PER; i += FIT_THREADS) s_sl[i] = ps[i];
+  __syncthreads();
+  Z = A = 0.0;
+  if (tid < FIT_POINTS)
+    for (int sl = 0; sl < a.nfs; ++sl) {
+      Z += s_sl[sl * PER + tid];
+      A += s_sl[sl * PER + FIT_POINTS + tid];
+    }
+}
+
 // hardkv_fit_round, grid (nfs, B*Hkv): round r's bracket from round r - 1's (its slices'
 // sums, summed in slice order, so that every workgroup derives the same bracket; slice 0
 // records it for round r + 1), then the slice's sums for round r's candidates.
@@ -1251,13 +1269,8 @@ __global__ __launch_bounds__(FIT_THREADS) void hardkv_fit_round(Args a, int r) {
   if (r > 0) {
     lo = fh->lo[r - 1];
     hi = fh->hi[r - 1];
-    double Z = 0.0, A = 0.0;
-    if (tid < FIT_POINTS)
-      for (int sl = 0; sl < a.nfs; ++sl) {
-        const double *ps = a.fitp + (((size_t)(r - 1) * a.B * a.Hkv + bh) * a.nfs + sl) * 2 * FIT_POINTS;
-        Z += ps[tid];
-        A += ps[FIT_POINTS + tid];
-      }
+    double Z, A;
+    fit_slice_sums(a, bh, r - 1, Z, A);
     fit_next(Z, A, H, lo, hi);
   }
   if (slice == 0 && tid == 0) {
@@ -1286,13 +1299,8 @@ __global__ __launch_bounds__(FIT_THREADS) void hardkv_fit_final(Args a) {
     constexpr int r = FIT_ROUNDS - 1;
     lo = fh->lo[r];
     hi = fh->hi[r];
-    double Z = 0.0, A = 0.0;
-    if (tid < FIT_POINTS)
-      for (int sl = 0; sl < a.nfs; ++sl) {
-        const double *ps = a.fitp + (((size_t)r * a.B * a.Hkv + bh) * a.nfs + sl) * 2 * FIT_POINTS;
-        Z += ps[tid];
-        A += ps[FIT_POINTS + tid];
-      }
+    double Z, A;
+    fit_slice_sums(a, bh, r, Z, A);
     fit_next(Z, A, fh->H, lo, hi);
   }
   fit_store(a, bh, N, lo, hi);

@@ -36,7 +36,7 @@ static_assert(offsetof(SelHead, ncand) == 64, "ncand on its own line");
 constexpr int FIT_POINTS = 17;          // grid points per round (16 intervals)
 constexpr int FIT_ROUNDS = 5;
 constexpr int FIT_SPLIT_ROWS = 4096;    // pool rows per workgroup when a head's fit is split
-constexpr int FIT_SPLIT_MIN_ROWS = 8 * FIT_SPLIT_ROWS;  // pool capacity from which it may be split
+constexpr int FIT_SPLIT_MIN_ROWS = 2 * FIT_SPLIT_ROWS;  // pool capacity from which it may be split
 constexpr int FIT_MAX_SLICES = (MAX_POOL_BLOCKS * 64 + FIT_SPLIT_ROWS - 1) / FIT_SPLIT_ROWS;  // per head
 
 // Per-head values that the split fit passes between its kernels.

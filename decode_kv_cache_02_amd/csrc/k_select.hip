@@ -1014,6 +1014,40 @@ HK_DEV double shfl_xor_d(double v, int off) {
   return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
 }
 
+// Sums over the wavefront's 64 lanes of each of the NV values v[0..NV), in six exchange
+// steps that each halve the values a lane holds: at the step of offset o, a lane with bit
+// o clear keeps the lower half of its values and one with it set the upper half (the
+// upper half one shorter, padded with zero, when the count is odd); each adds what its
+// partner lane ^ o held of the half it keeps.  Partners have made the same choices at the
+// earlier steps, so they hold the same values.  37 exchanges for NV = 34, against 6 NV
+// for a butterfly per value.  Returns the index whose sum v[0] now holds, or -1 for a
+// lane left with padding.
+template <int NV>
+HK_DEV int wave_sum_halving(double (&v)[NV]) {
+  static_assert(NV >= 1 && NV <= 64, "one value per lane at the end");
+  const int lane = threadIdx.x & 63;
+  int lo = 0, cnt = NV;
+  int n = NV;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const int h = (n + 1) / 2;
+    const bool up = (lane & off) != 0;
+#pragma unroll
+    for (int i = 0; i < h; ++i) {
+      const double x = v[i], y = i + h < n ? v[i + h] : 0.0;
+      v[i] = (up ? y : x) + shfl_xor_d(up ? x : y, off);
+    }
+    if (up) {
+      lo += h;
+      cnt = max(0, cnt - h);
+    } else {
+      cnt = min(cnt, h);
+    }
+    n = h;
+  }
+  return cnt > 0 ? lo : -1;
+}
+
 // The target entropy (nats) of head bh: the mean over the group's queries of the entropy
 // of their raw attention over the pool, merged from the per-chunk softmax pieces the
 // score kernel left; and the head's max score.  Every thread gets both.
@@ -1092,7 +1126,7 @@ HK_DEV float fit_slope(double lo, double hi, int k) {
 // bits.  Each thread sums rows r0 + tid, r0 + tid + FIT_THREADS, ... in that order in
 // fp32, FIT_UNR loads in flight; a row past r1 scores FIT_FAR below the max, whose terms
 // are exactly 0 (2^x2 is 0 and 0 * x2 is -0).  The workgroup sums in fp64: lanes by
-// exchanges, then wavefronts in order.
+// halving exchanges, then wavefronts in order.
 HK_DEV void fit_sums(const Args &a, int bh, int64_t c, int64_t r0, int64_t r1, float m, double lo, double hi,
                      double &Z, double &A) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -1127,19 +1161,14 @@ HK_DEV void fit_sums(const Args &a, int bh, int64_t c, int64_t r0, int64_t r1, f
         ca[k] = __builtin_fmaf(e, x2, ca[k]);
       }
   }
+  double v[2 * FIT_POINTS];
 #pragma unroll
   for (int k = 0; k < FIT_POINTS; ++k) {
-    double z = (double)cz[k], w = (double)ca[k];
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      z += shfl_xor_d(z, off);
-      w += shfl_xor_d(w, off);
-    }
-    if (lane == 0) {
-      s_acc[wave][k] = z;
-      s_acc[wave][FIT_POINTS + k] = w;
-    }
+    v[k] = (double)cz[k];
+    v[FIT_POINTS + k] = (double)ca[k];
   }
+  const int idx = wave_sum_halving(v);
+  if (idx >= 0) s_acc[wave][idx] = v[0];
   __syncthreads();
   Z = A = 0.0;
   if (tid < FIT_POINTS) {

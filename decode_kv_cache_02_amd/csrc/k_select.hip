@@ -103,6 +103,24 @@ HK_DEV void ent_merge(float &m, float &z, float &w, float m2, float z2, float w2
   m = M;
 }
 
+// A piece (m, z, a) after one more logit x, with one exponential: of the old max and x,
+// the lower one is scaled by 2^(lower - higher).  The same values as merging the
+// single-logit piece (x, 1, 0) above, rounded in a different order; x = -inf adds
+// nothing, as there.
+HK_DEV void ent_add(float &m, float &z, float &w, float x) {
+  const bool keep = x == -INFINITY;   // (every select below, not a branch)
+  const bool first = m == -INFINITY;  // empty piece so far
+  const bool up = x > m;              // x becomes the max
+  const float d = first ? 0.0f : (up ? m - x : x - m);
+  const float e = first ? 0.0f : exp2_fast(d);
+  // up: old sums scaled by e, new term (1, 0); else: old sums kept, new term (e, e d)
+  const float zn = (up ? e * z : z) + (up ? 1.0f : e);
+  const float wn = up ? e * __builtin_fmaf(d, z, w) : __builtin_fmaf(e, d, w);
+  z = keep ? z : zn;
+  w = keep ? w : wn;
+  m = up ? x : m;
+}
+
 template <typename T, int G, bool ENT>
 __global__ __launch_bounds__(NTHREADS) void hardkv_score(Args a) {
   constexpr int EB = Elem<T>::bytes;
@@ -211,7 +229,7 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_score(Args a) {
           float dmine;
           float s = group_dots(kf, dmine, fused);
           const int rel = gi * 16 + l * 4 + grp;
-          if (ENT && sub < G && rel < nrows) ent_merge(em, ez, ew, dmine * c2, 1.0f, 0.0f);
+          if (ENT && sub < G && rel < nrows) ent_add(em, ez, ew, dmine * c2);
           s = s + 0.0f;  // a zero score is +0
           // s is needed in every lane here, so that the last tree level stays one DPP add
           // rather than a move plus an add sunk into the store's branch

@@ -229,9 +229,12 @@ int32_t hardkv_regularize(const hardkv_config *cfg, hardkv_state *st, void *stre
  * the slot cursor. */
 int32_t hardkv_condense(const hardkv_config *cfg, hardkv_state *st, void *stream);
 
-/* Attention over the condensed, view and dense tiers; out is fp32 [B][Hq][128] (device).
- * Heads that the last select left to Sparse Loading are attended through the pool and
- * the mask instead of the view. */
+/* Decode attention over the three tiers (technical summary 2.A: the dense tier of recent
+ * tokens, the sparse tier's kept tokens and the constant-size condensed tier together
+ * stand for the whole context): each query's softmax over the condensed slots with n > 0,
+ * the view rows r < k*, the dense window and the sink rows; out is fp32 [B][Hq][128]
+ * (device).  Heads that the last select left to Sparse Loading are attended through the
+ * pool and the mask instead of the view. */
 int32_t hardkv_attend(const hardkv_config *cfg, hardkv_state *st, const void *q, float *out,
                       void *stream);
 
@@ -241,9 +244,13 @@ int32_t hardkv_attend(const hardkv_config *cfg, hardkv_state *st, const void *q,
 int32_t hardkv_attend_sparse(const hardkv_config *cfg, hardkv_state *st, const void *q, float *out,
                              void *stream);
 
-/* The whole step: append, select, regularize, condense, attend, in one stream-ordered,
- * capturable sequence (the view attention is fused into the rewrite, and when at most four
- * blocks can condense per step, P - S_cap/64 <= 4, the condensation into the select). */
+/* The whole step (technical summary 2.A: the four stages of a step -- linear append to
+ * the dense tier, calibrated top-p masks, index regularization, eviction or weighted
+ * merging of the oldest blocks -- followed by attention over the tiers; 2.C: static
+ * shapes and persistent pointers so that the step can be captured into a graph): append,
+ * select, regularize, condense, attend, in one stream-ordered, capturable sequence (the
+ * view attention is fused into the rewrite, and when at most four blocks can condense per
+ * step, P - S_cap/64 <= 4, the condensation into the select). */
 int32_t hardkv_step(const hardkv_config *cfg, hardkv_state *st, const void *q, const void *k_new,
                     const void *v_new, float *out, void *stream);
 

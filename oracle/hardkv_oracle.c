@@ -69,6 +69,7 @@ static int64_t dense_lo_of(const orc_cfg *cfg, int64_t t) {
 
 float orc_dot_pairwise(const float *a, const float *b, int32_t n) {
   float lvl[1024];
+  if (n < 1 || n > 1024) return NAN; /* head dims up to 1024 */
   for (int i = 0; i < n; ++i) {
     float p = a[i] * b[i];
     lvl[i] = p;

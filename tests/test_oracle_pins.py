@@ -59,6 +59,13 @@ def test_pairwise_tree_golden():
         if "exact_rounded" in case:
             exact = _nearest_f32(sum(Fraction(float(a)) * Fraction(float(b)) for a, b in zip(q, k)))
             assert exact == np.float32(case["exact_rounded"]) and exact != got
+        if "strided" in case:
+            # the other tree shape: level l+1 element i = level l element i + element i + n/2
+            lvl = (q * k).astype(np.float32)
+            while lvl.size > 1:
+                h = lvl.size // 2
+                lvl = (lvl[:h] + lvl[h:]).astype(np.float32)
+            assert lvl[0] == np.float32(case["strided"]) and lvl[0] != got
 
 
 def test_signed_zero_score_is_plus_zero():

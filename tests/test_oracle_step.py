@@ -208,6 +208,78 @@ def test_merge_identical_block_is_lossless():
             np.testing.assert_allclose(outs[0][0, qh], full, rtol=1e-12, atol=1e-14)
 
 
+def test_merge_weights_tau_inf_closed_form():
+    """tau -> inf makes every calibrated probability equal: each pool token's weight is
+    the maximum 2^24, so the merge weight of a token is 1/N over the N pool tokens of the
+    step (including the condensing blocks), a merged block's Omega is 64/N and its Kn, Vn
+    the plain sums of its keys and values over N (I6 with I11's numerators).  A weight
+    normalised per block (Omega = 1) or over the survivors only (64/(N - 64E)) fails."""
+    W, S, E = 32, 128, 2
+    L0 = W + S + 64 * E - 1  # the first step's pool holds S + 64E tokens: E blocks condense
+    wl = tiny_workload(batch=2, num_kv_heads=2, num_q_heads=8, dense_window=W, sparse_cap=S,
+                       ctx_len=L0, ctx_min=None, cond_mode=COND_MERGE, condensed_slots=4,
+                       top_p=0.9, heavy=(0, 0), dtype="f32")
+    inp = make_inputs(wl)
+    o, _ = _run(wl, inp, tau=np.full(wl.num_kv_heads, np.inf, np.float32))
+    N = L0 + 1 - W
+    assert np.all(o.n_condense == E)
+    assert np.all(o.w_all == np.uint64(N) << np.uint64(24))
+    for b in range(wl.batch):
+        for h in range(wl.num_kv_heads):
+            k, v = _positions_kv(inp, b, h, 1)
+            for e in range(E):
+                blk = slice(64 * e, 64 * (e + 1))
+                np.testing.assert_allclose(o.cond_omega[b, h, e], 64.0 / N, rtol=1e-13)
+                np.testing.assert_allclose(o.cond_kn[b, h, e], k[blk].astype(np.float64).sum(0) / N,
+                                           rtol=1e-11, atol=1e-14)
+                np.testing.assert_allclose(o.cond_vn[b, h, e], v[blk].astype(np.float64).sum(0) / N,
+                                           rtol=1e-11, atol=1e-14)
+            assert np.all(o.cond_omega[b, h, E:] == 0) and np.all(o.cond_n[b, h, E:] == 0)
+
+
+def test_merge_weights_two_token_classes():
+    """Merge weights fixed by construction, across two condensations with different pool
+    masses into one slot.  Each query is the unit vector e_0, so a token's score is exactly
+    its key's first element, chosen 0 (class A) or -3 (class B); with tau such that
+    kappa = fp32(log2(e) / (sqrt(128) tau)) is exactly 1, t = s - max s is 0 or -3 and the
+    weights are exactly 2^24 and 2^21 (the integer-exponent weights of the calibration
+    golden file).  With C = 1 both condensed blocks land in slot 0, so
+    Omega = sum over block 0 of w / W_1 + sum over block 1 of w / W_2, with W_1, W_2 the
+    pool masses of the two steps summed here by hand; Kn and Vn are the same weighted sums
+    of the raw keys and values (the weighted merging of tier 3, technical summary 2.A)."""
+    W, S = 32, 128
+    L0 = W + S + 63  # step 1 condenses block [0, 64), step 2 block [64, 128)
+    wl = tiny_workload(batch=1, num_kv_heads=1, num_q_heads=4, dense_window=W, sparse_cap=S,
+                       ctx_len=L0, ctx_min=None, cond_mode=COND_MERGE, condensed_slots=1,
+                       top_p=0.9, heavy=(0, 0), dtype="f32", steps=2)
+    inp = make_inputs(wl)
+    rng = np.random.default_rng(11)
+    cls_a = rng.random(L0 + 2) < 0.3  # class of every position [0, L0 + 2)
+    cls_a[[5, 100, 150]] = True       # a class-A token in each step's pool: max s = 0
+    first = np.where(cls_a, 0.0, -3.0).astype(np.float32)
+    inp.k_ctx[0, 0, :L0, 0] = torch.from_numpy(first[:L0])
+    inp.k_new[:, 0, 0, 0] = torch.from_numpy(first[L0:L0 + 2])
+    inp.q.zero_()
+    inp.q[..., 0] = 1.0
+    tau = np.float32(1.4426950408889634 / np.sqrt(128.0))
+    assert np.float32(1.4426950408889634 / (np.sqrt(128.0) * np.float64(tau))) == np.float32(1.0)
+    assert orc.kappa(128, float(tau)) == np.float32(1.0)
+    o, _ = _run(wl, inp, steps=2, tau=np.array([tau], np.float32))
+    w = np.where(cls_a, 1 << 24, 1 << 21).astype(np.int64)
+    W1 = int(w[0:L0 + 1 - W].sum())        # pool of step 1: [0, 192)
+    W2 = int(w[64:L0 + 2 - W].sum())       # pool of step 2: [64, 193)
+    assert W1 != W2
+    assert int(o.w_all[0, 0]) == W2 and int(o.pool_head[0, 0]) == 128
+    k, v = _positions_kv(inp, 0, 0, 2)
+    om = np.concatenate([w[0:64] / W1, w[64:128] / W2])
+    assert o.cond_n[0, 0, 0] == 128 and o.cond_cursor[0, 0] == 0
+    np.testing.assert_allclose(o.cond_omega[0, 0, 0], om.sum(), rtol=1e-13)
+    kv = k[:128].astype(np.float64)
+    vv = v[:128].astype(np.float64)
+    np.testing.assert_allclose(o.cond_kn[0, 0, 0], (om[:, None] * kv).sum(0), rtol=1e-11, atol=1e-14)
+    np.testing.assert_allclose(o.cond_vn[0, 0, 0], (om[:, None] * vv).sum(0), rtol=1e-11, atol=1e-14)
+
+
 def test_condense_bookkeeping_modes():
     """Merged slots count 64 tokens per condensed block; evict leaves the slots
     untouched; off never condenses (I11)."""

@@ -4,11 +4,36 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
 
 #include "hardkv_internal.h"
 
+// Scratch of hardkv_step_noalloc, one copy per GPU (zero-filled at load; nothing in it has to
+// start at zero).  Host code never passes this name to a kernel: it stands for the array
+// only on the device; the host uses the address looked up per device below.
+static __device__ __align__(256) unsigned char scratch[HARDKV_STATIC_SCRATCH_BYTES];
+
 namespace hardkv {
 namespace {
+
+constexpr int MAX_DEVICES = 64;
+
+// The device address of `scratch` on the current device, looked up once per device with
+// that device current.
+int32_t scratch_address(void **out) {
+  static std::mutex mu;
+  static void *addr[MAX_DEVICES] = {};
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return HARDKV_EHIP;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return HARDKV_EHIP;
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return HARDKV_OK;
+}
 
 constexpr double LOG2E = 1.4426950408889634074;
 
@@ -408,6 +433,36 @@ int32_t hardkv_step_reuse(const hardkv_config *cfg, hardkv_state *st, const void
   return hip_status(e);
 }
 
+int32_t hardkv_step_noalloc(const hardkv_config *cfg, hardkv_state *st, const void *q, const void *k_new,
+                            const void *v_new, float *out, void *stream) {
+  Plan p;
+  int32_t rc = plan(cfg, p);
+  if (rc != HARDKV_OK) return rc;
+  if (!st) return HARDKV_EINVAL;
+  if (p.ws_bytes > (size_t)HARDKV_STATIC_SCRATCH_BYTES) return HARDKV_ESCRATCH;
+  if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(out)) return HARDKV_EINVAL;
+  // the state's own buffers, with the library's scratch in place of its workspace; the
+  // pointer checks of bind() run on a stand-in address first, so that a bad state is
+  // rejected before the array's address is looked up
+  hardkv_state sc = *st;
+  sc.workspace = reinterpret_cast<void *>((uintptr_t)256);
+  sc.workspace_bytes = HARDKV_STATIC_SCRATCH_BYTES;
+  rc = bind(&sc, p);
+  if (rc != HARDKV_OK) return rc;
+  void *ws = nullptr;
+  rc = scratch_address(&ws);
+  if (rc != HARDKV_OK) return rc;
+  sc.workspace = ws;
+  rc = bind(&sc, p);
+  if (rc != HARDKV_OK) return rc;
+  p.a.kx_unknown = 1;
+  p.a.q = q;
+  p.a.k_new = k_new;
+  p.a.v_new = v_new;
+  p.a.out = out;
+  return hip_status(step_all(cfg, p.a, (hipStream_t)stream));
+}
+
 int32_t hardkv_step_stage(const hardkv_config *cfg, hardkv_state *st, const void *q,
                           const void *k_new, const void *v_new, float *out, int32_t stage,
                           void *stream) {
@@ -438,6 +493,7 @@ const char *hardkv_strerror(int32_t code) {
     case HARDKV_EUNSUPPORTED: return "unsupported configuration";
     case HARDKV_ECAPACITY: return "capacity too small";
     case HARDKV_EHIP: return "HIP launch failed";
+    case HARDKV_ESCRATCH: return "scratch needed exceeds the library's static scratch";
     default: return "unknown status";
   }
 }

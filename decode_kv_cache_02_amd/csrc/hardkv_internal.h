@@ -101,6 +101,8 @@ struct Args {
   double *fitp;       // [FIT_ROUNDS][BH][nfs][2 * FIT_POINTS] split fit: each slice's sums
   uint32_t *kx;       // [BH] nonzero once a 16-bit key outside KEY_SAFE has entered the head's
                       // pool (since its prefill): its scores then take the unfused products
+  int kx_unknown;     // 1: kx is not kept for this state (the no-alloc step): every head's
+                      // scores take the unfused products
   // prefill
   const void *k_ctx, *v_ctx;
   const int64_t *ctx_len;

@@ -168,7 +168,8 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_score(Args a) {
           q_ok &= x == 0.0f || (x >= Q_SAFE_LO && x < Q_SAFE_HI);
         }
       exact_products =
-          CAN_FUSE && __builtin_amdgcn_readfirstlane((int)(a.kx[bh] == 0u && ballot(!q_ok) == 0ull)) != 0;
+          CAN_FUSE && a.kx_unknown == 0 &&
+          __builtin_amdgcn_readfirstlane((int)(a.kx[bh] == 0u && ballot(!q_ok) == 0ull)) != 0;
     };
     const BufRes kb = make_buf((const char *)a.pool_k + (size_t)bh * P * BK * HD * EB, (uint64_t)P * BK * HD * EB);
     const uint32_t lane_b = (uint32_t)(sub * 8 * EB);  // the lane's 8 elements of a row

@@ -17,7 +17,8 @@ import torch
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libhardkv.so")
 
-HARDKV_OK, HARDKV_EINVAL, HARDKV_EUNSUPPORTED, HARDKV_ECAPACITY, HARDKV_EHIP = 0, -1, -2, -3, -4
+HARDKV_OK, HARDKV_EINVAL, HARDKV_EUNSUPPORTED, HARDKV_ECAPACITY, HARDKV_EHIP, HARDKV_ESCRATCH = 0, -1, -2, -3, -4, -5
+HARDKV_STATIC_SCRATCH_BYTES = 128 << 20
 HARDKV_BF16, HARDKV_F32 = 0, 1
 HARDKV_COND_OFF, HARDKV_COND_EVICT, HARDKV_COND_MERGE = 0, 1, 2
 HARDKV_REG_REWRITE, HARDKV_REG_SPARSE, HARDKV_REG_MTI = 0, 1, 2
@@ -28,7 +29,7 @@ BLOCK, HEAD_DIM = 64, 128
 
 EXPORTS = ("hardkv_workspace_size", "hardkv_prefill", "hardkv_append", "hardkv_select",
            "hardkv_regularize", "hardkv_condense", "hardkv_attend", "hardkv_attend_sparse", "hardkv_step",
-           "hardkv_step_reuse", "hardkv_step_stage", "hardkv_step_num_stages", "hardkv_step_stage_name",
+           "hardkv_step_reuse", "hardkv_step_noalloc", "hardkv_step_stage", "hardkv_step_num_stages", "hardkv_step_stage_name",
            "hardkv_strerror")
 
 
@@ -84,6 +85,7 @@ def lib() -> C.CDLL:
         L.hardkv_attend_sparse.argtypes = [cp, sp, vp, vp, vp]
         L.hardkv_step.argtypes = [cp, sp, vp, vp, vp, vp, vp]
         L.hardkv_step_reuse.argtypes = [cp, sp, vp, vp, vp, vp, vp]
+        L.hardkv_step_noalloc.argtypes = [cp, sp, vp, vp, vp, vp, vp]
         L.hardkv_step_stage.argtypes = [cp, sp, vp, vp, vp, vp, i32, vp]
         L.hardkv_step_num_stages.argtypes = []
         L.hardkv_step_stage_name.argtypes = [i32]
@@ -265,6 +267,12 @@ def hardkv_step(cfg: Config, st: State, q, k_new, v_new, out, stream=None) -> No
 def hardkv_step_reuse(cfg: Config, st: State, q, k_new, v_new, out, stream=None) -> None:
     _check("hardkv_step_reuse", lib().hardkv_step_reuse(C.byref(cfg.c), C.byref(st.c), _ptr(q), _ptr(k_new),
                                                         _ptr(v_new), _ptr(out), _stream(stream)))
+
+
+def hardkv_step_noalloc(cfg: Config, st: State, q, k_new, v_new, out, stream=None) -> None:
+    """hardkv_step with the library's static scratch in place of the state's workspace."""
+    _check("hardkv_step_noalloc", lib().hardkv_step_noalloc(C.byref(cfg.c), C.byref(st.c), _ptr(q), _ptr(k_new),
+                                                            _ptr(v_new), _ptr(out), _stream(stream)))
 
 
 def hardkv_step_stage(cfg: Config, st: State, q, k_new, v_new, out, stage: int, stream=None) -> None:

@@ -85,7 +85,9 @@ typedef enum {
   HARDKV_EINVAL = -1,      /* bad argument: null/misaligned pointer, inconsistent sizes */
   HARDKV_EUNSUPPORTED = -2,/* valid but not supported: head_dim != 128, G not in {1,2,4,8} */
   HARDKV_ECAPACITY = -3,   /* a capacity is too small for the requested contents */
-  HARDKV_EHIP = -4         /* a HIP launch failed */
+  HARDKV_EHIP = -4,        /* a HIP launch failed */
+  HARDKV_ESCRATCH = -5     /* hardkv_step_noalloc: the step needs more scratch than the
+                              library's static array holds (HARDKV_STATIC_SCRATCH_BYTES) */
 } hardkv_status;
 
 typedef enum { HARDKV_BF16 = 0, HARDKV_F32 = 1 } hardkv_dtype;
@@ -140,6 +142,7 @@ typedef enum { HARDKV_CAL_FIXED = 0, HARDKV_CAL_ENTROPY = 1 } hardkv_calibration
 #define HARDKV_MAX_SINK 8192
 #define HARDKV_MAX_UNITS 65535     /* batch * num_kv_heads (one launch row per unit) */
 #define HARDKV_MAX_POOL_BLOCKS 6144 /* pool ring blocks per unit the select can index */
+#define HARDKV_STATIC_SCRATCH_BYTES (128u << 20) /* the no-alloc step's scratch per GPU */
 
 /* Host-side description of one layer; passed by pointer to every call. */
 typedef struct {
@@ -267,6 +270,29 @@ int32_t hardkv_step(const hardkv_config *cfg, hardkv_state *st, const void *q, c
  * Same arguments as hardkv_step; capturable. */
 int32_t hardkv_step_reuse(const hardkv_config *cfg, hardkv_state *st, const void *q, const void *k_new,
                           const void *v_new, float *out, void *stream);
+
+/* hardkv_step for callers that cannot allocate device memory (code under graph capture,
+ * tight serving loops, harnesses that forbid allocation): the same kernels and results,
+ * with the step's scratch (plan, per-block offsets, attention partials, select and fit
+ * scratch) in a static device array of the library, HARDKV_STATIC_SCRATCH_BYTES on every
+ * GPU it runs on, held from the first call on that GPU until the process ends, instead of
+ * st->workspace (which may be NULL; workspace_bytes is ignored).  Allocates nothing.
+ *   - HARDKV_ESCRATCH (before anything is enqueued) when hardkv_workspace_size(cfg) exceeds
+ *     HARDKV_STATIC_SCRATCH_BYTES; the other checks and statuses are hardkv_step's.
+ *   - Every call on one GPU shares that GPU's array, which keeps the last call's contents:
+ *     calls that overlap on one GPU (other streams, other threads) race, and their results
+ *     are undefined.  Nothing in the array has to start at zero.
+ *   - The first call on a GPU looks up the array's address on it (HARDKV_EHIP if that
+ *     fails); make it outside graph capture.
+ *   - The array keeps nothing of a state between calls, so the record of keys whose
+ *     products with a query could round in fp32 (see the workspace above) is not kept:
+ *     every head's scores take the plain pairwise tree, which gives the same bits.  A state
+ *     stepped by this call lacks that record in its own workspace afterwards: keep stepping
+ *     it with this call (or prefill it again) rather than with the calls that read the
+ *     workspace (hardkv_step, hardkv_step_reuse, hardkv_regularize, hardkv_condense,
+ *     hardkv_attend, hardkv_attend_sparse). */
+int32_t hardkv_step_noalloc(const hardkv_config *cfg, hardkv_state *st, const void *q, const void *k_new,
+                            const void *v_new, float *out, void *stream);
 
 /* Launches only kernel `stage` of hardkv_step (0 append, 1 score, 2 select, 3 condense,
  * 4 rewrite with the view, condensed and dense attention, 5 combine), for timing one

@@ -22,7 +22,7 @@ def _declared():
 def test_exports_every_declared_symbol():
     lib = hk.lib()
     names = _declared()
-    assert len(names) == 14, names
+    assert len(names) == 15, names
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(hk.EXPORTS)
@@ -138,6 +138,27 @@ def test_state_validation(kind):
     assert L.hardkv_step_reuse(C.byref(cfg.c), C.byref(st), q, q, q, q, None) == expect
     assert L.hardkv_select(C.byref(cfg.c), C.byref(st), q, None) == expect
     assert L.hardkv_regularize(C.byref(cfg.c), C.byref(st), None) == expect
+
+
+@_no_gpu
+def test_noalloc_validation():
+    """The no-alloc step checks what hardkv_step checks, ignores the state's workspace, and
+    refuses a layer whose scratch exceeds the library's static array."""
+    cfg = _cfg()
+    L = hk.lib()
+    ok = C.c_void_p(1 << 41)
+    bad = C.c_void_p((1 << 41) + 8)
+    st = _fake_state(cfg, null="workspace", ws_bytes=0)  # no workspace: not needed
+    st.pool_k = None
+    assert L.hardkv_step_noalloc(C.byref(cfg.c), C.byref(st), ok, ok, ok, ok, None) == hk.HARDKV_EINVAL
+    st = _fake_state(cfg, null="workspace", ws_bytes=0)
+    assert L.hardkv_step_noalloc(C.byref(cfg.c), C.byref(st), bad, ok, ok, ok, None) == hk.HARDKV_EINVAL
+    assert L.hardkv_step_noalloc(C.byref(cfg.c), None, ok, ok, ok, ok, None) == hk.HARDKV_EINVAL
+    big = hk.Config.from_workload(WORKLOADS["c3"].with_(batch=128))
+    assert hk.hardkv_workspace_size(big) > hk.HARDKV_STATIC_SCRATCH_BYTES
+    assert L.hardkv_step_noalloc(C.byref(big.c), C.byref(_fake_state(big)), ok, ok, ok, ok, None) \
+        == hk.HARDKV_ESCRATCH
+    assert hk.strerror(hk.HARDKV_ESCRATCH) == "scratch needed exceeds the library's static scratch"
 
 
 @_no_gpu

@@ -1,6 +1,11 @@
 """Benchmark of the HARD-KV decode step on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--config c2] [--gpus 1]
+    python bench.py [--steps K] [--warmup W] [--config c5] [--extra-configs ...] [--gpus 1]
+
+The headline (value, roofline, cpu_baseline) is the 32-layer workload, the largest that
+fits one GPU; the other workloads (the batch-1, batch-16 and mixed-length layers, the
+last at each p of its sweep, and the streaming one) are measured the same way in child
+processes and reported under "configs".
 
 One step is hardkv_step on one batch: append, score + calibrate + top-p, rewrite
 (with the view attention fused), condense, tier attention and combine, for every
@@ -55,6 +60,9 @@ HBM_PEAK_GBPS = 8000.0
 D = 128
 STAGE_NAMES = ["append", "score", "select", "condense", "rewrite_attend", "combine"]
 REPEATABLE = [1, 2, 4, 5]  # stages that only read what earlier stages wrote
+# the workloads measured beside the headline: the three target workloads (the mixed-length
+# one at each p of its sweep) and the streaming one
+EXTRA_DEFAULT = "c1,c2,c3:0.8,c3:0.9,c3:0.99,c4"
 
 
 def parse():
@@ -62,7 +70,12 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="c2")
+    ap.add_argument("--config", default="c5",
+                    help="the headline workload (default: the 32-layer step, the largest that fits one GPU)")
+    ap.add_argument("--extra-configs", default=EXTRA_DEFAULT,
+                    help="workloads also measured (each in a child process, before the headline) and "
+                         "reported under 'configs': comma-separated keys, key:p for a top-p override; "
+                         "'none' for none")
     ap.add_argument("--top-p", type=float, default=None, help="override p (the mixed-length workload sweeps it)")
     ap.add_argument("--eager", action="store_true", help="no graph (for counter runs)")
     ap.add_argument("--regularize", choices=["rewrite", "sparse", "mti"], default="rewrite",
@@ -96,6 +109,7 @@ def parse():
                          "--config and of --copy-calib MiB; writes profiles/traffic.json and a text "
                          "summary, then exits")
     ap.add_argument("--cmd", action="append", default=[], help="command recorded in a summary")
+    ap.add_argument("--child", action="store_true", help=argparse.SUPPRESS)
     return ap.parse_args()
 
 
@@ -508,6 +522,38 @@ def cpu_baseline(wl, layers, units_req, seconds):
 
 
 # ---- main ---------------------------------------------------------------------------------
+def run_extras(args):
+    """Each extra workload in a child process of its own (so that its device memory is
+    freed before the next one): the same timing, no CPU baseline; a summary per workload."""
+    import subprocess
+    out = []
+    if not args.extra_configs or args.extra_configs == "none":
+        return out
+    for spec in args.extra_configs.split(","):
+        key, _, p = spec.partition(":")
+        cmd = [sys.executable, os.path.abspath(__file__), "--child", "--config", key, "--steps", str(args.steps),
+               "--warmup", str(args.warmup), "--no-cpu-baseline", "--extra-configs", "none"]
+        if p:
+            cmd += ["--top-p", p]
+        t0 = time.perf_counter()
+        r = subprocess.run(cmd, capture_output=True, text=True, timeout=300)
+        wall = time.perf_counter() - t0
+        if r.returncode != 0:
+            raise RuntimeError(f"bench child {spec} failed ({r.returncode}):\n{r.stderr[-2000:]}")
+        d = json.loads(r.stdout.strip().splitlines()[-1])
+        rf = d["roofline"]
+        out.append({"workload": d["config"]["workload"], "top_p": d["config"]["top_p"],
+                    "ms_per_step": d["ms_per_step"], "steps_per_s": d["value"],
+                    "kv_tokens_scanned_per_s": d["kv_tokens_scanned_per_s"],
+                    "algorithmic_bytes_per_step": d["algorithmic_bytes_per_step"],
+                    "step_hbm_GBps": d["step_hbm_GBps"], "step_hbm_frac": d["step_hbm_frac"],
+                    "dominant_kernel": rf["kernel"], "dominant_GBps": rf["achieved"], "dominant_frac": rf["frac"],
+                    "stage_us": d["stage_us"], "timing": d["config"]["timing"], "wall_s": round(wall, 1)})
+        print(f"bench: {spec} {d['ms_per_step']:.4f} ms/step, step {d['step_hbm_frac']:.3f} of HBM peak "
+              f"({wall:.0f} s)", file=sys.stderr, flush=True)
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -523,6 +569,7 @@ def main():
             wl = dataclasses.replace(wl, sink=args.sink)
         summarize_traffic(*args.summarize_traffic, args.copy_calib or 1024, wl, args.cmd, run_options(args, wl))
         return
+    extras = [] if (args.child or args.copy_calib) else run_extras(args)
     hk.require_gpu()
     torch.cuda.set_device(0)
     if args.copy_calib:
@@ -699,6 +746,8 @@ def main():
         res["config"]["pool_blocks"] = wl.P_blk
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wl, layers, args.cpu_units, args.cpu_seconds)
+    if extras:
+        res["configs"] = extras
     print(json.dumps(res))
 
 

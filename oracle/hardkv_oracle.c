@@ -41,6 +41,91 @@ static void row_copy(void *dst, int64_t drow, const void *src, int64_t srow, int
   memcpy((char *)dst + drow * D * eb, (const char *)src + srow * D * eb, (size_t)D * eb);
 }
 
+/* ------------------------------------------------------------------------------------
+ * System-aware index regularization (section 2.C): the trade-off between Rewrite Cache and
+ * Sparse Loading is weighed by a memory-time integral, switched by budget thresholds
+ * L_lower and L_upper.  Reading: the memory time a head's kept rows cost over a horizon of
+ * the selection step and the H later steps that reuse it, in femtoseconds,
+ *   Sparse Loading: every one of the H + 1 steps gathers the k* kept rows through the
+ *     mask, g(b) each (b = floor(8 k* / n), the kept eighth of the n survivors), and walks
+ *     the mask over the n survivors, c_scan each;
+ *   Rewrite Cache: the selection step gathers them and writes the view, c_write each;
+ *     each later step reads them from the view, c_view each, while the view holds them,
+ *     c_hold per row and step; plus a fixed F per rewritten head.
+ * The head is rewritten iff the rewrite's integral is the smaller one.  The selection
+ * step's gather appears on both sides and cancels; what remains is compared exactly in
+ * 64-bit integers (k*, n < 2^20, H < 2^16, costs < 2^24).
+ * ---------------------------------------------------------------------------------- */
+int32_t orc_mti_rewrite(const orc_cfg *cfg, int64_t kstar, int64_t n) {
+  if (kstar <= 0 || n <= 0) return 0;
+  int64_t b = (8 * kstar) / n;
+  if (b > 8) b = 8;
+  const int64_t H = cfg->mti_horizon;
+  const int64_t g = cfg->mti_c_gather[b];
+  /* sparse: (H + 1) (k g + n c_scan);  rewrite: k g + n c_scan + k c_write
+   * + H k (c_view + c_hold) + F */
+  const int64_t rewrite_extra = kstar * (int64_t)cfg->mti_c_write +
+                                H * kstar * ((int64_t)cfg->mti_c_view + (int64_t)cfg->mti_c_hold) + cfg->mti_fixed;
+  const int64_t sparse_extra = H * (kstar * g + n * (int64_t)cfg->mti_c_scan);
+  return rewrite_extra < sparse_extra ? 1 : 0;
+}
+
+void orc_mti_thresholds(const orc_cfg *cfg, int64_t n, int64_t *lo, int64_t *hi) {
+  *lo = 0;
+  *hi = -1;
+  for (int64_t k = 1; k <= n; ++k)
+    if (orc_mti_rewrite(cfg, k, n)) {
+      if (*lo == 0) *lo = k;
+      *hi = k;
+    }
+}
+
+/* Steps per selection (a reading of when to select again, by the same integral): a head
+ * that selects every R steps pays, per period, the score over its n_pool pool rows
+ * (c_score each), the cheaper of the two policies above for H = R - 1, and, at the j-th
+ * step after the selection, the j pool rows that arrived since it, attended from the pool
+ * (c_view each, contiguous rows).  R minimises that cost over R (the smallest R on ties),
+ * compared exactly as cost(R1) R2 against cost(R2) R1. */
+static unsigned __int128 mti_period_cost(const orc_cfg *cfg, int64_t n_pool, int64_t n, int64_t k, int64_t R) {
+  orc_cfg c2 = *cfg;
+  c2.mti_horizon = (int32_t)(R - 1);
+  int64_t b = n > 0 ? (8 * k) / n : 0;
+  if (b > 8) b = 8;
+  const unsigned __int128 H = (unsigned __int128)(R - 1);
+  const unsigned __int128 kk = (unsigned __int128)k, nn = (unsigned __int128)n;
+  const unsigned __int128 sparse = (H + 1) * (kk * cfg->mti_c_gather[b] + nn * cfg->mti_c_scan);
+  const unsigned __int128 rewrite = kk * cfg->mti_c_gather[b] + nn * cfg->mti_c_scan + kk * cfg->mti_c_write +
+                                    H * kk * ((unsigned __int128)cfg->mti_c_view + cfg->mti_c_hold) +
+                                    (unsigned __int128)cfg->mti_fixed;
+  const unsigned __int128 policy = orc_mti_rewrite(&c2, k, n) ? rewrite : sparse;
+  const unsigned __int128 tail = (unsigned __int128)cfg->mti_c_view * (H * (H + 1) / 2);
+  return (unsigned __int128)n_pool * cfg->mti_c_score + policy + tail;
+}
+
+int32_t orc_mti_period(const orc_cfg *cfg, int64_t n_pool, int64_t n, int64_t kstar, int32_t max_period) {
+  if (max_period < 1) return 0;
+  int64_t best = 1;
+  unsigned __int128 best_cost = mti_period_cost(cfg, n_pool, n, kstar, 1);
+  for (int64_t R = 2; R <= max_period; ++R) {
+    const unsigned __int128 cst = mti_period_cost(cfg, n_pool, n, kstar, R);
+    if (cst * (unsigned __int128)best < best_cost * (unsigned __int128)R) {
+      best = R;
+      best_cost = cst;
+    }
+  }
+  return (int32_t)best;
+}
+
+/* whether head u keeps a rewritten view this selection (the regularize policy) */
+static int head_rewritten(const orc_cfg *cfg, int64_t kstar, int64_t n_survivors) {
+  switch (cfg->regularize) {
+    case 0: return 1;
+    case 1: return 0;
+    case 2: return (kstar >= cfg->mti_lower && kstar <= cfg->mti_upper) ? 1 : 0;
+    default: return orc_mti_rewrite(cfg, kstar, n_survivors);
+  }
+}
+
 /* pool ring row of position p for unit u (rows counted over the whole buffer) */
 static int64_t pool_row(const orc_cfg *cfg, int64_t u, int64_t p) {
   int64_t P = cfg->pool_blocks;
@@ -547,12 +632,10 @@ static uint32_t unit_step(const orc_cfg *cfg, orc_state *st, int b, int h, const
 
   /* Index Regularization (section 2.C).  The regularize policy decides whether this
    * head's kept rows are rewritten (Rewrite Cache) or left in the pool for attention to
-   * load through the mask (Sparse Loading); the pages name budget thresholds L_lower,
-   * L_upper for the switch without a formula: the head is rewritten iff
-   * L_lower <= k* <= L_upper. */
-  const int rw = cfg->regularize == 0 ? 1
-                 : cfg->regularize == 1 ? 0
-                 : (kstar >= cfg->mti_lower && kstar <= cfg->mti_upper) ? 1 : 0;
+   * load through the mask (Sparse Loading): every head, none, the heads whose budget lies
+   * in caller thresholds [L_lower, L_upper], or the memory-time controller above over the
+   * nU survivors. */
+  const int rw = head_rewritten(cfg, kstar, nU);
   if (st->regularized) st->regularized[u] = rw;
   /* with the packed (sum) layout the views are written after every unit's budget is
    * known (orc_step); attention reads the kept rows from the pool either way */
@@ -697,13 +780,11 @@ int32_t orc_step(const orc_cfg *cfg, orc_state *st, const void *q, const void *k
     int64_t off = 0;
     for (int64_t u = 0; u < units; ++u) {
       const int32_t kstar = st->budget[u];
-      const int rw = cfg->regularize == 0 ? 1
-                     : cfg->regularize == 1 ? 0
-                     : (kstar >= cfg->mti_lower && kstar <= cfg->mti_upper) ? 1 : 0;
-      st->view_off[u] = (int32_t)off;
-      if (!rw) continue;
       const int64_t t = st->seq_len[u / H];
       const int64_t pend = pool_end_of(cfg, t);
+      const int rw = head_rewritten(cfg, kstar, pend - st->pool_head[u]);  /* survivors */
+      st->view_off[u] = (int32_t)off;
+      if (!rw) continue;
       const int64_t c0 = st->pool_head[u] - (int64_t)BK * st->n_condense[u];
       int64_t r = 0;
       for (int64_t j = c0; j < pend; ++j) {
@@ -742,10 +823,8 @@ static void unit_reuse(const orc_cfg *cfg, orc_state *st, int b, int h, const vo
   const int64_t psel = st->pend_sel[u];
   const int64_t pend = pool_end_of(cfg, t);
   const int32_t kstar = st->budget[u];
-  const int rw = st->regularized ? st->regularized[u]
-                 : cfg->regularize == 0 ? 1
-                 : cfg->regularize == 1 ? 0
-                 : (kstar >= cfg->mti_lower && kstar <= cfg->mti_upper) ? 1 : 0;
+  /* survivors of the last selection: [pool head, its pool end) (nothing condenses since) */
+  const int rw = st->regularized ? st->regularized[u] : head_rewritten(cfg, kstar, psel - c);
   const int packed = cfg->view_layout == 1;
   int64_t *kept = (int64_t *)malloc(sizeof(int64_t) * (size_t)(kstar > 0 ? kstar : 1));
   int64_t nk = 0;

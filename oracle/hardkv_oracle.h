@@ -50,13 +50,25 @@ typedef struct {
   double top_p;
   const float *tau;          /* [H] */
   int32_t regularize;        /* 0 rewrite every head, 1 none (Sparse Loading), 2 the heads with
-                                mti_lower <= k* <= mti_upper */
+                                mti_lower <= k* <= mti_upper, 3 the memory-time controller
+                                (orc_mti_rewrite) */
   int32_t mti_lower, mti_upper;
   int32_t view_layout;       /* 0: every head owns view_cap rows; 1: packed in unit order (CSR) */
   int32_t view_total;        /* rows of the packed views (layout 1) */
   int32_t calibration;       /* 0: tau from tau[h]; 1: tau fitted per unit by entropy matching */
   const float *tau_unit;     /* [B*H] with calibration 1: use these instead of fitting (or NULL) */
   int32_t sink;              /* S: the first S positions form a sink tier (multiple of 64, or 0) */
+  /* memory-time controller (regularize 3): H, the steps expected to reuse a selection, and
+   * costs in femtoseconds per kept row (K and V) unless stated */
+  int32_t mti_horizon;
+  uint32_t mti_c_view;       /* a later step reading the row from a contiguous view */
+  uint32_t mti_c_write;      /* writing the row into the view at the selection step */
+  uint32_t mti_c_scan;       /* per survivor row, per step that gathers through the mask */
+  uint32_t mti_c_hold;       /* holding the row in a view for one step (memory occupancy) */
+  uint32_t mti_c_score;      /* per pool row scored at a selection (reselection period only) */
+  uint32_t mti_c_gather[9];  /* a later step gathering the row from the pool, by the kept
+                                eighth of the survivors: floor(8 k* / N_U) */
+  int64_t mti_fixed;         /* per rewritten head and selection */
 } orc_cfg;
 
 typedef struct {
@@ -108,6 +120,13 @@ int32_t orc_step_reuse(const orc_cfg *cfg, orc_state *st, const void *q, const v
 float   orc_fit_tau(const float *d, int32_t G, const float *s, int64_t n, int32_t D, double *h_target);
 /* entropy (nats) of softmax(s / (sqrt(D) tau)) over n scores, binary64 */
 double  orc_calibrated_entropy(const float *s, int64_t n, int32_t D, double tau);
+/* memory-time controller: whether a head with k* kept rows out of n survivors is rewritten
+ * (regularize 3); the smallest and largest budgets in [1, n] that are rewritten (lo = 0,
+ * hi = -1 when none); and the steps per selection in [1, max_period] that minimise the memory
+ * time per step of a head with n_pool pool rows, n survivors and k* kept rows */
+int32_t orc_mti_rewrite(const orc_cfg *cfg, int64_t kstar, int64_t n);
+void    orc_mti_thresholds(const orc_cfg *cfg, int64_t n, int64_t *lo, int64_t *hi);
+int32_t orc_mti_period(const orc_cfg *cfg, int64_t n_pool, int64_t n, int64_t kstar, int32_t max_period);
 /* full softmax attention over positions [0, t) of a flat cache, binary64 (pin I4) */
 void    orc_full_attention(const float *q, const float *k, const float *v, int32_t n,
                            int32_t D, double *out);

@@ -31,7 +31,26 @@ class OrcCfg(C.Structure):
         ("regularize", C.c_int32), ("mti_lower", C.c_int32), ("mti_upper", C.c_int32),
         ("view_layout", C.c_int32), ("view_total", C.c_int32),
         ("calibration", C.c_int32), ("tau_unit", C.POINTER(C.c_float)), ("sink", C.c_int32),
+        ("mti_horizon", C.c_int32), ("mti_c_view", C.c_uint32), ("mti_c_write", C.c_uint32),
+        ("mti_c_scan", C.c_uint32), ("mti_c_hold", C.c_uint32), ("mti_c_score", C.c_uint32),
+        ("mti_c_gather", C.c_uint32 * 9), ("mti_fixed", C.c_int64),
     ]
+
+MTI_FIELDS = ("mti_horizon", "mti_c_view", "mti_c_write", "mti_c_scan", "mti_c_hold", "mti_c_score",
+              "mti_c_gather", "mti_fixed")
+
+
+def set_mti(cfg, mti: Optional[dict]) -> None:
+    """Copies the memory-time controller's inputs (a dict with MTI_FIELDS keys, mti_c_gather a
+    sequence of 9) into an OrcCfg."""
+    if not mti:
+        return
+    for k, v in mti.items():
+        if k == "mti_c_gather":
+            arr = (C.c_uint32 * 9)(*[int(x) for x in v])
+            setattr(cfg, k, arr)
+        else:
+            setattr(cfg, k, int(v))
 
 
 class OrcState(C.Structure):
@@ -87,6 +106,12 @@ def lib():
         L.orc_step.argtypes = [C.POINTER(OrcCfg), C.POINTER(OrcState), vp, vp, vp, vp, i32, i32]
         L.orc_step_reuse.restype = i32
         L.orc_step_reuse.argtypes = [C.POINTER(OrcCfg), C.POINTER(OrcState), vp, vp, vp, vp, i32]
+        L.orc_mti_rewrite.restype = i32
+        L.orc_mti_rewrite.argtypes = [C.POINTER(OrcCfg), i64, i64]
+        L.orc_mti_thresholds.restype = None
+        L.orc_mti_thresholds.argtypes = [C.POINTER(OrcCfg), i64, C.POINTER(i64), C.POINTER(i64)]
+        L.orc_mti_period.restype = i32
+        L.orc_mti_period.argtypes = [C.POINTER(OrcCfg), i64, i64, i64, i32]
         L.orc_full_attention.restype = None
         L.orc_full_attention.argtypes = [vp, vp, vp, i32, i32, vp]
         _lib = L
@@ -180,6 +205,30 @@ def topp(w: np.ndarray, pos: np.ndarray, p: float):
     return int(k), sel[:w.size].astype(bool), int(T[0])
 
 
+def _mti_cfg(mti: dict) -> OrcCfg:
+    cfg = OrcCfg()
+    cfg.regularize = 3
+    set_mti(cfg, mti)
+    return cfg
+
+
+def mti_rewrite(mti: dict, kstar: int, n: int) -> bool:
+    """The memory-time controller's decision for a head with kstar kept of n survivors."""
+    return bool(lib().orc_mti_rewrite(C.byref(_mti_cfg(mti)), int(kstar), int(n)))
+
+
+def mti_thresholds(mti: dict, n: int):
+    """(L_lower, L_upper): the smallest and largest rewritten budgets in [1, n] ((0, -1): none)."""
+    lo, hi = C.c_int64(0), C.c_int64(0)
+    lib().orc_mti_thresholds(C.byref(_mti_cfg(mti)), int(n), C.byref(lo), C.byref(hi))
+    return int(lo.value), int(hi.value)
+
+
+def mti_period(mti: dict, n_pool: int, n: int, kstar: int, max_period: int) -> int:
+    """Steps per selection in [1, max_period] with the least memory time per step."""
+    return int(lib().orc_mti_period(C.byref(_mti_cfg(mti)), int(n_pool), int(n), int(kstar), int(max_period)))
+
+
 def full_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray) -> np.ndarray:
     q = np.ascontiguousarray(q, np.float32)
     k = np.ascontiguousarray(k, np.float32)
@@ -200,7 +249,8 @@ class Oracle:
     def __init__(self, wl, tau: Optional[np.ndarray] = None, merge_bias: bool = True,
                  top_p: Optional[float] = None, regularize: int = 0, mti_lower: int = 0,
                  mti_upper: int = 0, view_layout: int = 0, view_total: int = 0,
-                 calibration: int = 0, tau_unit: Optional[np.ndarray] = None):
+                 calibration: int = 0, tau_unit: Optional[np.ndarray] = None,
+                 mti: Optional[dict] = None):
         self.wl = wl
         B, H, Hq, D = wl.batch, wl.num_kv_heads, wl.num_q_heads, wl.head_dim
         W, P, V, Cs = wl.dense_window, wl.P_blk, wl.V_cap, wl.condensed_slots
@@ -212,6 +262,7 @@ class Oracle:
                           self.tau.ctypes.data_as(C.POINTER(C.c_float)), int(regularize),
                           int(mti_lower), int(mti_upper), int(view_layout), int(view_total),
                           int(calibration), None, int(getattr(wl, "sink", 0)))
+        set_mti(self.cfg, mti)
         self.tau_unit = None
         if tau_unit is not None:
             self.tau_unit = np.ascontiguousarray(np.asarray(tau_unit, np.float32).ravel())

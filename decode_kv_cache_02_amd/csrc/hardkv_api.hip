@@ -41,6 +41,23 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 bool aligned16(const void *p) { return p != nullptr && ((uintptr_t)p & 15u) == 0; }
 
+// the memory-time controller's inputs stay inside the ranges its exact integer comparison
+// covers
+bool mti_config_ok(const hardkv_config *cfg) {
+  if (cfg->mti_horizon < 0 || cfg->mti_horizon > HARDKV_MTI_MAX_HORIZON) return false;
+  const uint32_t c[] = {cfg->mti_c_view, cfg->mti_c_write, cfg->mti_c_scan, cfg->mti_c_hold, cfg->mti_c_score};
+  for (uint32_t x : c)
+    if (x >= HARDKV_MTI_MAX_COST) return false;
+  for (int i = 0; i < 9; ++i)
+    if (cfg->mti_c_gather[i] >= HARDKV_MTI_MAX_COST) return false;
+  return cfg->mti_fixed >= 0 && cfg->mti_fixed <= HARDKV_MTI_MAX_FIXED;
+}
+
+bool mti_rewrites_cfg(const hardkv_config *cfg, int64_t H, int64_t kstar, int64_t n) {
+  return mti_rewrites(kstar, n, H, cfg->mti_c_view, cfg->mti_c_write, cfg->mti_c_scan, cfg->mti_c_hold,
+                      cfg->mti_c_gather, cfg->mti_fixed);
+}
+
 struct Plan {
   Args a;
   size_t off_head, off_cmax, off_ent, off_blkinfo, off_part, off_phist, off_psum, off_selh, off_cand, off_kx,
@@ -76,7 +93,8 @@ int32_t plan(const hardkv_config *cfg, Plan &p) {
   if (!cfg->tau) return HARDKV_EINVAL;
   for (int h = 0; h < cfg->num_kv_heads; ++h)
     if (!(cfg->tau[h] > 0.0f)) return HARDKV_EINVAL;
-  if (cfg->regularize < HARDKV_REG_REWRITE || cfg->regularize > HARDKV_REG_MTI) return HARDKV_EINVAL;
+  if (cfg->regularize < HARDKV_REG_REWRITE || cfg->regularize > HARDKV_REG_MTI_AUTO) return HARDKV_EINVAL;
+  if (cfg->regularize == HARDKV_REG_MTI_AUTO && !mti_config_ok(cfg)) return HARDKV_EINVAL;
   if (cfg->regularize == HARDKV_REG_MTI && (cfg->mti_lower < 0 || cfg->mti_upper < cfg->mti_lower))
     return HARDKV_EINVAL;
   if (cfg->view_layout != HARDKV_VIEW_MAXLEN && cfg->view_layout != HARDKV_VIEW_SUM) return HARDKV_EINVAL;
@@ -103,6 +121,13 @@ int32_t plan(const hardkv_config *cfg, Plan &p) {
   a.reg_policy = cfg->regularize;
   a.mti_lower = cfg->mti_lower;
   a.mti_upper = cfg->mti_upper;
+  a.mti_horizon = cfg->mti_horizon;
+  a.mti_c_view = cfg->mti_c_view;
+  a.mti_c_write = cfg->mti_c_write;
+  a.mti_c_scan = cfg->mti_c_scan;
+  a.mti_c_hold = cfg->mti_c_hold;
+  for (int i = 0; i < 9; ++i) a.mti_c_gather[i] = cfg->mti_c_gather[i];
+  a.mti_fixed = cfg->mti_fixed;
   a.pq = (uint32_t)pq;
   {
     // Taylor coefficients (ln 2)^i / i! of 2^f, rounded once to fp32
@@ -484,6 +509,54 @@ int32_t hardkv_step_num_stages(void) { return NSTAGES; }
 
 const char *hardkv_step_stage_name(int32_t stage) {
   return (stage >= 0 && stage < NSTAGES) ? kStageNames[stage] : "unknown";
+}
+
+int32_t hardkv_mti_thresholds(const hardkv_config *cfg, int64_t n_survivors, int32_t *l_lower,
+                              int32_t *l_upper) {
+  if (!cfg || !l_lower || !l_upper || !mti_config_ok(cfg)) return HARDKV_EINVAL;
+  if (n_survivors < 0 || n_survivors >= (1 << 20)) return HARDKV_EINVAL;
+  // the policy's choice at every budget, smallest and largest rewritten
+  int32_t lo = 0, hi = -1;
+  for (int64_t k = 1; k <= n_survivors; ++k)
+    if (mti_rewrites_cfg(cfg, cfg->mti_horizon, k, n_survivors)) {
+      if (lo == 0) lo = (int32_t)k;
+      hi = (int32_t)k;
+    }
+  *l_lower = lo;
+  *l_upper = hi;
+  return HARDKV_OK;
+}
+
+int32_t hardkv_mti_period(const hardkv_config *cfg, int64_t n_pool, int64_t n_survivors, int64_t kstar,
+                          int32_t max_period, int32_t *period) {
+  if (!cfg || !period || !mti_config_ok(cfg)) return HARDKV_EINVAL;
+  if (n_pool < 0 || n_pool >= (1 << 20) || n_survivors < 0 || n_survivors > n_pool || kstar < 0 ||
+      kstar > n_survivors || max_period < 1 || max_period > HARDKV_MTI_MAX_HORIZON + 1)
+    return HARDKV_EINVAL;
+  // memory time of one period of R steps: the score, the cheaper policy at H = R - 1, and the
+  // rows that arrived since the selection (1 + 2 + ... + (R - 1) of them), in 128 bits
+  typedef unsigned __int128 u128;
+  const int64_t b = n_survivors > 0 ? std::min<int64_t>(8, (8 * kstar) / n_survivors) : 0;
+  const u128 per_gather = (u128)kstar * cfg->mti_c_gather[b] + (u128)n_survivors * cfg->mti_c_scan;
+  auto cost = [&](int64_t R) -> u128 {
+    const u128 H = (u128)(R - 1);
+    const u128 sparse = (H + 1) * per_gather;
+    const u128 rewrite = per_gather + (u128)kstar * cfg->mti_c_write +
+                         H * (u128)kstar * ((u128)cfg->mti_c_view + cfg->mti_c_hold) + (u128)cfg->mti_fixed;
+    const u128 pol = mti_rewrites_cfg(cfg, R - 1, kstar, n_survivors) ? rewrite : sparse;
+    return (u128)n_pool * cfg->mti_c_score + pol + (u128)cfg->mti_c_view * (H * (H + 1) / 2);
+  };
+  int64_t best = 1;
+  u128 best_cost = cost(1);
+  for (int64_t R = 2; R <= max_period; ++R) {
+    const u128 c = cost(R);
+    if (c * (u128)best < best_cost * (u128)R) {  // c / R < best_cost / best
+      best = R;
+      best_cost = c;
+    }
+  }
+  *period = (int32_t)best;
+  return HARDKV_OK;
 }
 
 const char *hardkv_strerror(int32_t code) {

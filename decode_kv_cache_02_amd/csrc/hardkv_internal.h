@@ -126,6 +126,11 @@ struct Args {
   int npart, part_cd_base;  // partial slots per head; first condensed/dense slot
   int xp_base, nxp;         // gathered-row partial slots of the standalone attention
   int reg_policy, mti_lower, mti_upper;  // regularize policy and its budget thresholds
+  // the memory-time controller (policy MTI_AUTO): H, per-row costs (fs), fixed cost
+  int mti_horizon;
+  uint32_t mti_c_view, mti_c_write, mti_c_scan, mti_c_hold;
+  uint32_t mti_c_gather[9];
+  int64_t mti_fixed;
   int gather_mode;          // rewrite kernel: GATHER_* below
   int view_sum;             // 1: Flatten Index to the sum (packed views)
   int calibration;          // HARDKV_CAL_*
@@ -161,6 +166,20 @@ hipError_t launch_rewrite(const Args &a, hipStream_t s, bool bf16, bool mask, bo
 hipError_t launch_condense(const Args &a, hipStream_t s, bool bf16);
 hipError_t launch_attend(const Args &a, hipStream_t s, bool bf16);
 hipError_t launch_combine(const Args &a, hipStream_t s);
+
+// The memory-time controller's choice for a head with kstar kept rows out of n survivors:
+// rewrite iff k* c_write + H k* (c_view + c_hold) + F < H (k* g[b] + n c_scan), b the kept
+// eighth (the terms both policies share cancel); exact in 64-bit integers for k*, n < 2^20,
+// H < 2^16, costs < 2^24, F < 2^41.
+__host__ __device__ inline bool mti_rewrites(int64_t kstar, int64_t n, int64_t H, uint32_t c_view,
+                                             uint32_t c_write, uint32_t c_scan, uint32_t c_hold,
+                                             const uint32_t *c_gather, int64_t fixed) {
+  if (kstar <= 0 || n <= 0) return false;
+  const int64_t b = (8 * kstar) / n < 8 ? (8 * kstar) / n : 8;
+  const int64_t lhs = kstar * (int64_t)c_write + H * kstar * ((int64_t)c_view + (int64_t)c_hold) + fixed;
+  const int64_t rhs = H * (kstar * (int64_t)c_gather[b] + n * (int64_t)c_scan);
+  return lhs < rhs;
+}
 
 // ---------------------------------------------------------------------------------------
 // device helpers

@@ -748,7 +748,9 @@ HK_DEV void sel_finish(const Args &a, int bh, const SelGeo &g, SelShared &sh, ui
     // [L_lower, L_upper]
     const int rw = a.reg_policy == HARDKV_REG_REWRITE ? 1
                    : a.reg_policy == HARDKV_REG_SPARSE ? 0
-                   : (kstar >= a.mti_lower && kstar <= a.mti_upper) ? 1 : 0;
+                   : a.reg_policy == HARDKV_REG_MTI ? ((kstar >= a.mti_lower && kstar <= a.mti_upper) ? 1 : 0)
+                   : (mti_rewrites(kstar, pend - u0, a.mti_horizon, a.mti_c_view, a.mti_c_write, a.mti_c_scan,
+                                   a.mti_c_hold, a.mti_c_gather, a.mti_fixed) ? 1 : 0);
     hd->rw = rw;
     hd->voff = (int64_t)bh * a.V_cap;  // the maximum-length layout; the flatten kernel packs SUM
     if (a.regularized) a.regularized[bh] = rw;

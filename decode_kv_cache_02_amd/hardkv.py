@@ -21,7 +21,11 @@ HARDKV_OK, HARDKV_EINVAL, HARDKV_EUNSUPPORTED, HARDKV_ECAPACITY, HARDKV_EHIP, HA
 HARDKV_STATIC_SCRATCH_BYTES = 128 << 20
 HARDKV_BF16, HARDKV_F32 = 0, 1
 HARDKV_COND_OFF, HARDKV_COND_EVICT, HARDKV_COND_MERGE = 0, 1, 2
-HARDKV_REG_REWRITE, HARDKV_REG_SPARSE, HARDKV_REG_MTI = 0, 1, 2
+HARDKV_REG_REWRITE, HARDKV_REG_SPARSE, HARDKV_REG_MTI, HARDKV_REG_MTI_AUTO = 0, 1, 2, 3
+# the memory-time controller's default costs (fs per row of K and V; the header's
+# HARDKV_MTI_C_* values, measured with this library's kernels on a bf16 layer)
+MTI_DEFAULT = dict(mti_horizon=0, mti_c_view=97000, mti_c_write=68000, mti_c_scan=0, mti_c_hold=0,
+                   mti_c_score=44000, mti_c_gather=[124000] * 9, mti_fixed=0)
 HARDKV_VIEW_MAXLEN, HARDKV_VIEW_SUM = 0, 1
 HARDKV_CAL_FIXED, HARDKV_CAL_ENTROPY = 0, 1
 HARDKV_ERR_POOL_OVERFLOW, HARDKV_ERR_VIEW_OVERFLOW, HARDKV_ERR_NONFINITE = 1, 2, 4
@@ -30,7 +34,7 @@ BLOCK, HEAD_DIM = 64, 128
 EXPORTS = ("hardkv_workspace_size", "hardkv_prefill", "hardkv_append", "hardkv_select",
            "hardkv_regularize", "hardkv_condense", "hardkv_attend", "hardkv_attend_sparse", "hardkv_step",
            "hardkv_step_reuse", "hardkv_step_noalloc", "hardkv_step_stage", "hardkv_step_num_stages", "hardkv_step_stage_name",
-           "hardkv_strerror")
+           "hardkv_mti_thresholds", "hardkv_mti_period", "hardkv_strerror")
 
 
 class HardKVError(RuntimeError):
@@ -49,6 +53,9 @@ class hardkv_config(C.Structure):
         ("regularize", C.c_int32), ("mti_lower", C.c_int32), ("mti_upper", C.c_int32),
         ("view_layout", C.c_int32), ("view_total", C.c_int32), ("calibration", C.c_int32),
         ("sink", C.c_int32),
+        ("mti_horizon", C.c_int32), ("mti_c_view", C.c_uint32), ("mti_c_write", C.c_uint32),
+        ("mti_c_scan", C.c_uint32), ("mti_c_hold", C.c_uint32), ("mti_c_score", C.c_uint32),
+        ("mti_c_gather", C.c_uint32 * 9), ("mti_fixed", C.c_int64),
     ]
 
 
@@ -88,6 +95,8 @@ def lib() -> C.CDLL:
         L.hardkv_step_noalloc.argtypes = [cp, sp, vp, vp, vp, vp, vp]
         L.hardkv_step_stage.argtypes = [cp, sp, vp, vp, vp, vp, i32, vp]
         L.hardkv_step_num_stages.argtypes = []
+        L.hardkv_mti_thresholds.argtypes = [cp, i64, C.POINTER(i32), C.POINTER(i32)]
+        L.hardkv_mti_period.argtypes = [cp, i64, i64, i64, i32, C.POINTER(i32)]
         L.hardkv_step_stage_name.argtypes = [i32]
         L.hardkv_step_stage_name.restype = C.c_char_p
         L.hardkv_strerror.argtypes = [i32]
@@ -132,7 +141,7 @@ class Config:
                  tau: Sequence[float], head_dim: int = HEAD_DIM, merge_bias: bool = True,
                  regularize: int = HARDKV_REG_REWRITE, mti_lower: int = 0, mti_upper: int = 0,
                  view_layout: int = HARDKV_VIEW_MAXLEN, view_total: int = 0,
-                 calibration: int = HARDKV_CAL_FIXED, sink: int = 0):
+                 calibration: int = HARDKV_CAL_FIXED, sink: int = 0, mti: Optional[dict] = None):
         self.tau_arr = (C.c_float * max(1, len(tau)))(*[float(x) for x in tau])
         self.c = hardkv_config(batch, num_q_heads, num_kv_heads, head_dim,
                                HARDKV_BF16 if dtype == "bf16" else HARDKV_F32, dense_window,
@@ -141,6 +150,10 @@ class Config:
                                C.cast(self.tau_arr, C.POINTER(C.c_float)),
                                int(regularize), int(mti_lower), int(mti_upper),
                                int(view_layout), int(view_total), int(calibration), int(sink))
+        m = dict(MTI_DEFAULT)
+        m.update(mti or {})
+        for k, v in m.items():
+            setattr(self.c, k, (C.c_uint32 * 9)(*[int(x) for x in v]) if k == "mti_c_gather" else int(v))
         self.dtype = dtype
 
     @classmethod
@@ -148,7 +161,7 @@ class Config:
                       merge_bias: bool = True, regularize: int = HARDKV_REG_REWRITE,
                       mti_lower: int = 0, mti_upper: int = 0, view_layout: int = HARDKV_VIEW_MAXLEN,
                       view_total: int = 0, calibration: int = HARDKV_CAL_FIXED,
-                      sink: Optional[int] = None) -> "Config":
+                      sink: Optional[int] = None, mti: Optional[dict] = None) -> "Config":
         return cls(wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.dtype, wl.dense_window, wl.P_blk,
                    wl.sparse_cap, wl.V_cap, wl.condensed_slots,
                    wl.cond_mode if cond_mode is None else cond_mode,
@@ -157,7 +170,7 @@ class Config:
                    head_dim=wl.head_dim, merge_bias=merge_bias, regularize=regularize,
                    mti_lower=mti_lower, mti_upper=mti_upper, view_layout=view_layout,
                    view_total=view_total, calibration=calibration,
-                   sink=int(getattr(wl, "sink", 0)) if sink is None else int(sink))
+                   sink=int(getattr(wl, "sink", 0)) if sink is None else int(sink), mti=mti)
 
     def __getattr__(self, name):
         return getattr(self.__dict__["c"], name)
@@ -278,6 +291,22 @@ def hardkv_step_noalloc(cfg: Config, st: State, q, k_new, v_new, out, stream=Non
 def hardkv_step_stage(cfg: Config, st: State, q, k_new, v_new, out, stage: int, stream=None) -> None:
     _check("hardkv_step_stage", lib().hardkv_step_stage(C.byref(cfg.c), C.byref(st.c), _ptr(q), _ptr(k_new),
                                                         _ptr(v_new), _ptr(out), int(stage), _stream(stream)))
+
+
+def hardkv_mti_thresholds(cfg: Config, n_survivors: int):
+    """(L_lower, L_upper) of the memory-time controller for a head of n_survivors survivors."""
+    lo, hi = C.c_int32(0), C.c_int32(0)
+    _check("hardkv_mti_thresholds", lib().hardkv_mti_thresholds(C.byref(cfg.c), int(n_survivors), C.byref(lo),
+                                                                C.byref(hi)))
+    return int(lo.value), int(hi.value)
+
+
+def hardkv_mti_period(cfg: Config, n_pool: int, n_survivors: int, kstar: int, max_period: int) -> int:
+    """Steps per selection with the least memory time per step (the controller's reselect period)."""
+    r = C.c_int32(0)
+    _check("hardkv_mti_period", lib().hardkv_mti_period(C.byref(cfg.c), int(n_pool), int(n_survivors), int(kstar),
+                                                        int(max_period), C.byref(r)))
+    return int(r.value)
 
 
 def hardkv_step_num_stages() -> int:

@@ -104,11 +104,40 @@ typedef enum { HARDKV_COND_OFF = 0, HARDKV_COND_EVICT = 1, HARDKV_COND_MERGE = 2
  *   MTI      head (b, h) is rewritten iff mti_lower <= k* <= mti_upper: below L_lower so
  *            few rows are kept that gathering them each step costs less than keeping a
  *            view; above L_upper the mask covers so much of the pool that masked loads
- *            are nearly contiguous and a rewrite would copy almost everything.
+ *            are nearly contiguous and a rewrite would copy almost everything;
+ *   MTI_AUTO the memory-time controller below decides per head from its k*, its survivor
+ *            count and the reuse horizon.
  * The attention output, masks and budgets do not depend on the policy (the fused step
  * attends the kept rows from registers either way); only the views differ: a head that is
  * not rewritten leaves its view rows and view_pos untouched. */
-typedef enum { HARDKV_REG_REWRITE = 0, HARDKV_REG_SPARSE = 1, HARDKV_REG_MTI = 2 } hardkv_regularize_policy;
+typedef enum { HARDKV_REG_REWRITE = 0, HARDKV_REG_SPARSE = 1, HARDKV_REG_MTI = 2, HARDKV_REG_MTI_AUTO = 3 }
+    hardkv_regularize_policy;
+
+/* The memory-time controller (policy MTI_AUTO; a reading of section 2.C's memory-time integral
+ * that weighs the one-off rewrite against the per-step gains).  For a head with k* kept rows
+ * out of N_U survivors and a horizon of H later steps that reuse the selection
+ * (cfg->mti_horizon, what the caller expects until it selects again), the memory time the
+ * kept rows cost over the selection step and those H steps, in femtoseconds:
+ *   Sparse Loading  (H + 1) (k* g[b] + N_U c_scan)
+ *   Rewrite Cache   k* g[b] + N_U c_scan + k* c_write + H k* (c_view + c_hold) + F
+ * with b = min(8, floor(8 k* / N_U)) the kept eighth of the survivors, g[b] a later step's
+ * gather of one kept row through the mask, c_scan its walk over one survivor row's mask bit,
+ * c_write the view write of one row at the selection, c_view a later step's read of one
+ * view row, c_hold one view row held for one step, F a fixed cost per rewritten head.  The
+ * head is rewritten iff the second is smaller, compared exactly in 64-bit integers (k* = 0 is
+ * never rewritten; with H = 0 nothing is).  For a given N_U the rewritten budgets run from
+ * L_lower to L_upper (hardkv_mti_thresholds) when g does not grow with b.  Costs are per row
+ * of K and V in the layer's dtype; the defaults below were measured with this library's own
+ * kernels on the 16k-context, batch-16 bf16 layer (per kept row: the view attention 97 ps, the
+ * fused step's view stores 68 ps, the gathered attention 124 ps; the score 44 ps per pool
+ * row), so on this part a rewrite pays from H = 3 reused steps on. */
+#define HARDKV_MTI_C_VIEW 97000u
+#define HARDKV_MTI_C_WRITE 68000u
+#define HARDKV_MTI_C_GATHER 124000u
+#define HARDKV_MTI_C_SCORE 44000u
+#define HARDKV_MTI_MAX_HORIZON 65535
+#define HARDKV_MTI_MAX_COST (1u << 24)     /* every cost below this, in fs */
+#define HARDKV_MTI_MAX_FIXED (1ll << 40)
 
 /* Flatten Index (section 2.C: indices regularized to the maximum length or to their sum):
  *   MAXLEN  every head owns view_cap rows: head u's row r is row u * view_cap + r (default);
@@ -169,6 +198,12 @@ typedef struct {
   int32_t calibration;     /* hardkv_calibration (0: FIXED) */
   int32_t sink;            /* S: sink prefix tokens, a multiple of 64 in [0, HARDKV_MAX_SINK]
                               (0: none); see the sink tier above */
+  /* the memory-time controller (policy MTI_AUTO; see above; femtoseconds per row of K and V) */
+  int32_t mti_horizon;     /* H in [0, HARDKV_MTI_MAX_HORIZON] */
+  uint32_t mti_c_view, mti_c_write, mti_c_scan, mti_c_hold;
+  uint32_t mti_c_score;    /* per pool row scored at a selection (hardkv_mti_period only) */
+  uint32_t mti_c_gather[9];/* by the kept eighth b of the survivors */
+  int64_t mti_fixed;       /* F per rewritten head, in [0, HARDKV_MTI_MAX_FIXED] */
 } hardkv_config;
 
 /* Device buffers of one layer.  All fixed capacity; 16-byte aligned.
@@ -305,6 +340,22 @@ int32_t hardkv_step_stage(const hardkv_config *cfg, hardkv_state *st, const void
 /* Number of kernels hardkv_step launches, and the name of kernel `stage`. */
 int32_t hardkv_step_num_stages(void);
 const char *hardkv_step_stage_name(int32_t stage);
+
+/* The memory-time controller's thresholds (host only): *l_lower and *l_upper are the smallest
+ * and the largest budget k* in [1, n_survivors] that policy MTI_AUTO rewrites for a head of
+ * n_survivors survivors (0 and -1 when it rewrites none).  HARDKV_EINVAL on a bad config or
+ * n_survivors outside [0, 2^20). */
+int32_t hardkv_mti_thresholds(const hardkv_config *cfg, int64_t n_survivors, int32_t *l_lower,
+                              int32_t *l_upper);
+
+/* When to select again (host only; a reading by the same memory-time integral): the number of
+ * steps R in [1, max_period] per selection that minimises the memory time per step of a head
+ * with n_pool pool rows, n_survivors survivors and budget kstar, selecting every R steps: the
+ * score of the pool (c_score per row), the cheaper of the two policies above for H = R - 1,
+ * and, j steps after the selection, the j pool rows that arrived since (c_view each); the
+ * smallest such R.  Nothing here bounds how stale a selection may grow: max_period does. */
+int32_t hardkv_mti_period(const hardkv_config *cfg, int64_t n_pool, int64_t n_survivors, int64_t kstar,
+                          int32_t max_period, int32_t *period);
 
 /* Text for a status code. */
 const char *hardkv_strerror(int32_t code);

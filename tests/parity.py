@@ -47,7 +47,7 @@ class Pair:
 
     def __init__(self, wl, inputs=None, top_p=None, tau=None, cond_mode=None, merge_bias=True,
                  device="cuda", oracle_units=None, layer=0, regularize=0, mti_lower=0, mti_upper=0,
-                 view_layout=0, view_total=0, make_state=None):
+                 view_layout=0, view_total=0, make_state=None, mti=None):
         self.wl = wl if cond_mode is None else wl.with_(cond_mode=cond_mode)
         if top_p is not None:
             self.wl = self.wl.with_(top_p=top_p)
@@ -57,14 +57,17 @@ class Pair:
                    view_layout=view_layout, view_total=view_total)
         self.packed = view_layout == hk.HARDKV_VIEW_SUM
         assert not (self.packed and oracle_units is not None), "packed views need the whole layer"
-        self.cfg = hk.Config.from_workload(self.wl, tau=self.tau, merge_bias=merge_bias, **pol)
+        # the memory-time controller's inputs (policy MTI_AUTO), the same on both sides
+        self.mti = dict(hk.MTI_DEFAULT, **(mti or {}))
+        self.cfg = hk.Config.from_workload(self.wl, tau=self.tau, merge_bias=merge_bias, mti=self.mti, **pol)
         self.st = (make_state or hk.State)(self.cfg, device=device)
         hk.hardkv_prefill(self.cfg, self.st, self.inp.k_ctx, self.inp.v_ctx, self.inp.ctx_len)
         self.units = oracle_units
         self.orcs = {}
         if oracle_units is None:
             cpu = self.inp.to("cpu")
-            o = orc.Oracle(self.wl, tau=np.asarray(self.tau, np.float32), merge_bias=merge_bias, **pol)
+            o = orc.Oracle(self.wl, tau=np.asarray(self.tau, np.float32), merge_bias=merge_bias, mti=self.mti,
+                           **pol)
             assert o.prefill(cpu.k_ctx, cpu.v_ctx, cpu.ctx_len) == 0
             self.orcs[None] = (o, cpu)
         else:
@@ -72,7 +75,7 @@ class Pair:
                 ui = self.inp.unit(b, h).to("cpu")
                 ui.wl = self.wl.with_(batch=1, num_kv_heads=1, num_q_heads=self.wl.group)
                 o = orc.Oracle(ui.wl, tau=np.asarray(self.tau[h:h + 1], np.float32), merge_bias=merge_bias,
-                               **pol)
+                               mti=self.mti, **pol)
                 assert o.prefill(ui.k_ctx, ui.v_ctx, ui.ctx_len) == 0
                 self.orcs[(b, h)] = (o, ui)
         self.out = torch.zeros((self.wl.batch, self.wl.num_q_heads, self.wl.head_dim),
@@ -250,8 +253,8 @@ def check_layer_properties(pr: Pair) -> None:
         (the minimal prefix of top-p);
       * no dropped survivor outweighs a kept one, and among tokens of the threshold weight
         the kept ones precede the dropped ones (ties to the lower position);
-      * view_pos lists the kept positions in increasing order and every view row is a bit
-        copy of its pool row."""
+      * for every rewritten head, view_pos lists the kept positions in increasing order and
+        every view row is a bit copy of its pool row."""
     global _POPC8
     st, wl = pr.st, pr.wl
     dev = st.mask.device
@@ -291,11 +294,13 @@ def check_layer_properties(pr: Pair) -> None:
     last_kept_tie = torch.where(bits & at_th, pos, torch.full_like(pos, -1)).max(1).values
     first_drop_tie = torch.where(drop & at_th, pos, pos_big).min(1).values
     assert torch.all(last_kept_tie[has] < first_drop_tie[has]), "ties not taken by lower position"
-    # view: increasing positions, rows bit-equal to the pool rows
+    # view of every rewritten head: increasing positions, rows bit-equal to the pool rows
+    # (a head left to Sparse Loading keeps whatever its view held)
     V = wl.V_cap
     vpos = st.view_pos.reshape(BH, V).long()
     r = torch.arange(V, device=dev)
-    live = r[None, :] < budget[:, None]
+    rewritten = st.regularized.reshape(BH).bool()
+    live = (r[None, :] < budget[:, None]) & rewritten[:, None]
     d = vpos[:, 1:] - vpos[:, :-1]
     assert torch.all((d > 0) | ~live[:, 1:]), "view positions not increasing"
     sel_pos = torch.where(bits, pos, pos_big).sort(1).values[:, :V]

@@ -22,7 +22,7 @@ def _declared():
 def test_exports_every_declared_symbol():
     lib = hk.lib()
     names = _declared()
-    assert len(names) == 15, names
+    assert len(names) == 17, names
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(hk.EXPORTS)
@@ -63,7 +63,12 @@ def _cfg(**over):
     (dict(batch=8192, num_kv_heads=8, num_q_heads=32), hk.HARDKV_EUNSUPPORTED),   # 65536 units
     (dict(pool_blocks=6145, view_cap=6145 * 64), hk.HARDKV_EUNSUPPORTED),
     (dict(dense_window=0), hk.HARDKV_EINVAL),
-    (dict(regularize=3), hk.HARDKV_EINVAL),
+    (dict(regularize=4), hk.HARDKV_EINVAL),
+    (dict(regularize=hk.HARDKV_REG_MTI_AUTO, mti_horizon=-1), hk.HARDKV_EINVAL),
+    (dict(regularize=hk.HARDKV_REG_MTI_AUTO, mti_horizon=65536), hk.HARDKV_EINVAL),
+    (dict(regularize=hk.HARDKV_REG_MTI_AUTO, mti_c_write=1 << 24), hk.HARDKV_EINVAL),
+    (dict(regularize=hk.HARDKV_REG_MTI_AUTO, mti_fixed=-1), hk.HARDKV_EINVAL),
+    (dict(regularize=hk.HARDKV_REG_MTI_AUTO, mti_fixed=(1 << 40) + 1), hk.HARDKV_EINVAL),
     (dict(view_layout=2), hk.HARDKV_EINVAL),
     (dict(view_layout=1, view_total=-1), hk.HARDKV_EINVAL),
     (dict(calibration=2), hk.HARDKV_EINVAL),
@@ -179,3 +184,51 @@ def test_call_argument_validation():
     big = wl.P_blk * 64 + wl.dense_window
     assert L.hardkv_prefill(C.byref(cfg.c), C.byref(st), ok, ok, ok, big, None) == hk.HARDKV_ECAPACITY
     assert L.hardkv_prefill(C.byref(cfg.c), C.byref(st), ok, ok, C.c_void_p((1 << 41) + 4), 10, None) == hk.HARDKV_EINVAL
+
+
+def test_mti_helpers_match_the_oracle():
+    """The library's thresholds and reselection period equal the oracle's for random costs,
+    horizons and heads (integer results, compared exactly)."""
+    import numpy as np
+    from oracle import hardkv_oracle as orc
+    rng = np.random.default_rng(17)
+    for trial in range(60):
+        m = dict(mti_horizon=int(rng.integers(0, 12)), mti_c_view=int(rng.integers(1, 200)),
+                 mti_c_write=int(rng.integers(0, 400)), mti_c_scan=int(rng.integers(0, 3)),
+                 mti_c_hold=int(rng.integers(0, 20)), mti_c_score=int(rng.integers(0, 100)),
+                 mti_c_gather=sorted([int(x) for x in rng.integers(50, 400, 9)], reverse=True),
+                 mti_fixed=int(rng.integers(0, 5000)))
+        cfg = hk.Config.from_workload(tiny_workload(), regularize=hk.HARDKV_REG_MTI_AUTO, mti=m)
+        n = int(rng.integers(0, 3000))
+        assert hk.hardkv_mti_thresholds(cfg, n) == orc.mti_thresholds(m, n), (m, n)
+        n_pool = n + int(rng.integers(0, 500))
+        k = int(rng.integers(0, n + 1))
+        maxp = int(rng.integers(1, 200))
+        assert hk.hardkv_mti_period(cfg, n_pool, n, k, maxp) == orc.mti_period(m, n_pool, n, k, maxp), (m, n, k)
+
+
+def test_mti_defaults_match_the_header():
+    with open(os.path.join(ROOT, "include", "hardkv.h")) as f:
+        text = f.read()
+    val = lambda name: int(re.search(r"#define " + name + r" (\d+)u", text).group(1))  # noqa: E731
+    d = hk.MTI_DEFAULT
+    assert d["mti_c_view"] == val("HARDKV_MTI_C_VIEW")
+    assert d["mti_c_write"] == val("HARDKV_MTI_C_WRITE")
+    assert d["mti_c_score"] == val("HARDKV_MTI_C_SCORE")
+    assert d["mti_c_gather"] == [val("HARDKV_MTI_C_GATHER")] * 9
+
+
+def test_mti_helper_validation():
+    cfg = hk.Config.from_workload(tiny_workload(), regularize=hk.HARDKV_REG_MTI_AUTO)
+    L = hk.lib()
+    lo, hi = C.c_int32(0), C.c_int32(0)
+    assert L.hardkv_mti_thresholds(C.byref(cfg.c), -1, C.byref(lo), C.byref(hi)) == hk.HARDKV_EINVAL
+    assert L.hardkv_mti_thresholds(C.byref(cfg.c), 1 << 20, C.byref(lo), C.byref(hi)) == hk.HARDKV_EINVAL
+    r = C.c_int32(0)
+    assert L.hardkv_mti_period(C.byref(cfg.c), 100, 200, 10, 8, C.byref(r)) == hk.HARDKV_EINVAL  # n > n_pool
+    assert L.hardkv_mti_period(C.byref(cfg.c), 100, 50, 60, 8, C.byref(r)) == hk.HARDKV_EINVAL   # k > n
+    assert L.hardkv_mti_period(C.byref(cfg.c), 100, 50, 10, 0, C.byref(r)) == hk.HARDKV_EINVAL
+    # the default costs: a rewrite pays from three reused steps on
+    for H, want in ((2, (0, -1)), (3, (1, 15809))):
+        c = hk.Config.from_workload(tiny_workload(), regularize=hk.HARDKV_REG_MTI_AUTO, mti=dict(mti_horizon=H))
+        assert hk.hardkv_mti_thresholds(c, 15809) == want

@@ -218,12 +218,35 @@ def _mti_bounds(wl):
     return int(vals[1]), int(vals[-2])
 
 
+def _mti_auto_costs(wl, horizon=3):
+    """Controller costs that split the heads of the workload's last step: per kept row a
+    view read 100, a write 250 and a gather 200 fs, so a rewrite saves 50 fs per row over
+    H = 3 reused steps, against a fixed cost per head of 50 fs times the median budget:
+    heads keeping more than the median are rewritten."""
+    from oracle import hardkv_oracle as orc
+    from synth import make_inputs
+    inp = make_inputs(wl)
+    o = orc.Oracle(wl)
+    assert o.prefill(inp.k_ctx, inp.v_ctx, inp.ctx_len) == 0
+    for s in range(wl.steps):
+        o.step(inp.q[s], inp.k_new[s], inp.v_new[s], attend=False)
+    med = int(np.median(o.budget))
+    assert o.budget.max() > med, o.budget
+    return dict(mti_horizon=horizon, mti_c_view=100, mti_c_write=250, mti_c_gather=[200] * 9, mti_c_scan=0,
+                mti_c_hold=0, mti_fixed=50 * med)
+
+
 POLICY_CASES = {
     "sparse_merge_bf16": (dict(cond_mode=COND_MERGE, ctx_len=500, ctx_min=100, steps=3), 1),
     "sparse_evict_f32": (dict(dtype="f32", steps=2), 1),
     "sparse_g8": (dict(num_q_heads=16, num_kv_heads=2, cond_mode=COND_MERGE, steps=2), 1),
     "mti_evict": (dict(batch=4, heavy=(0, 6), steps=2), 2),
     "mti_merge_batch16": (dict(batch=16, cond_mode=COND_MERGE, ctx_len=500, ctx_min=100, heavy=(0, 6), steps=2), 2),
+    # the memory-time controller (policy 3)
+    "mti_auto_evict": (dict(batch=4, heavy=(0, 6), steps=2), 3),
+    "mti_auto_merge_batch16": (dict(batch=16, cond_mode=COND_MERGE, ctx_len=500, ctx_min=100, heavy=(0, 6),
+                                    steps=3), 3),
+    "mti_auto_f32": (dict(dtype="f32", batch=6, heavy=(0, 6), steps=2), 3),
 }
 
 
@@ -240,11 +263,12 @@ def test_regularize_policy_parity(name, fused):
     steps = kw.pop("steps")
     wl = tiny_workload(steps=steps, **kw)
     lo, hi = _mti_bounds(wl) if pol == 2 else (0, 0)
-    print(f"case {name} fused={fused}: policy {pol} [{lo}, {hi}] {wl}", flush=True)
-    pr = Pair(wl, regularize=pol, mti_lower=lo, mti_upper=hi)
+    mti = _mti_auto_costs(wl) if pol == 3 else None
+    print(f"case {name} fused={fused}: policy {pol} [{lo}, {hi}] {mti} {wl}", flush=True)
+    pr = Pair(wl, regularize=pol, mti_lower=lo, mti_upper=hi, mti=mti)
     for _ in range(steps):
         pr.step(fused=fused)
-    if pol == 2:
+    if pol in (2, 3):
         rw = pr.st.regularized.cpu().numpy()
         assert rw.any() and not rw.all(), rw
 
@@ -519,6 +543,7 @@ REUSE_CASES = {
     "composition": (dict(cond_mode=COND_MERGE), 0, "crrcr"),
     "sparse_policy": (dict(cond_mode=COND_MERGE, ctx_len=500, ctx_min=100), 1, "srrsr"),
     "mti": (dict(batch=4, heavy=(0, 6)), 2, "srrr"),
+    "mti_auto": (dict(batch=4, heavy=(0, 6), cond_mode=COND_MERGE), 3, "srrrsrr"),
     "packed": (dict(cond_mode=COND_MERGE), "packed", "srrsr"),
     "sink": (dict(sink=64, cond_mode=COND_MERGE, ctx_len=500, ctx_min=100), 0, "srrsr"),
     "g8": (dict(num_q_heads=16, num_kv_heads=2), 0, "srrr"),
@@ -543,6 +568,8 @@ def test_reuse_parity(name):
     elif pol == 2:
         lo, hi = _mti_bounds(wl)
         extra = dict(regularize=2, mti_lower=lo, mti_upper=hi)
+    elif pol == 3:
+        extra = dict(regularize=3, mti=_mti_auto_costs(wl))
     elif pol:
         extra = dict(regularize=pol)
     print(f"case {name}: {pattern} {extra} {wl}", flush=True)

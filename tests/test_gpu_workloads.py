@@ -63,6 +63,24 @@ def test_c2_sink_prefix():
         check_layer_properties(pr)
 
 
+def test_c2_memory_time_controller():
+    """The same layer under the memory-time controller: the default per-row costs, a horizon
+    of 7 reused steps (a rewrite saves 7 (124000 - 97000) - 68000 = 121000 fs per kept row)
+    and a fixed cost per head of 121000 fs times 10000, so heads keeping more than 10000
+    rows are rewritten and the others gathered; every unit's rewrite flag, mask, budget and
+    views against the oracle, then two steps that reuse the selection."""
+    from parity import Pair, check_layer_properties
+    wl = get_workload("c2").with_(steps=3)
+    print("workload", wl.name, "memory-time controller", flush=True)
+    pr = Pair(wl, regularize=3, mti=dict(mti_horizon=7, mti_fixed=121000 * 10000))
+    pr.step()
+    check_layer_properties(pr)
+    rw = pr.st.regularized.cpu().numpy()
+    assert rw.any() and not rw.all(), rw
+    pr.step_reuse()
+    pr.step_reuse()
+
+
 @pytest.mark.parametrize("p", [0.8, 0.9, 0.99])
 def test_c3_mixed_lengths(p):
     """Batch 64, lengths 8k..32k, 0..64 heavy keys per head, the first step condenses up

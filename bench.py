@@ -63,6 +63,7 @@ REPEATABLE = [1, 2, 4, 5]  # stages that only read what earlier stages wrote
 # the workloads measured beside the headline: the three target workloads (the mixed-length
 # one at each p of its sweep) and the streaming one
 EXTRA_DEFAULT = "c1,c2,c3:0.8,c3:0.9,c3:0.99,c4"
+POLICY_DEFAULT = "c2,c4,c5"
 
 
 def parse():
@@ -78,9 +79,18 @@ def parse():
                          "'none' for none")
     ap.add_argument("--top-p", type=float, default=None, help="override p (the mixed-length workload sweeps it)")
     ap.add_argument("--eager", action="store_true", help="no graph (for counter runs)")
-    ap.add_argument("--regularize", choices=["rewrite", "sparse", "mti"], default="rewrite",
-                    help="Rewrite Cache for every head (default), Sparse Loading for every head, or "
-                         "the budget-threshold rule (rewrite iff --mti-lower <= k* <= --mti-upper)")
+    ap.add_argument("--regularize", choices=["rewrite", "sparse", "mti", "mti-auto"], default="rewrite",
+                    help="Rewrite Cache for every head (default), Sparse Loading for every head, the "
+                         "budget-threshold rule (rewrite iff --mti-lower <= k* <= --mti-upper), or the "
+                         "memory-time controller (default costs, horizon --mti-horizon)")
+    ap.add_argument("--mti-horizon", type=int, default=-1,
+                    help="reused steps the controller plans for (default: --select-every minus one)")
+    ap.add_argument("--quick", action="store_true",
+                    help="step time only (and --select-every): no per-kernel timing, bytes or roofline")
+    ap.add_argument("--policy-configs", default=POLICY_DEFAULT,
+                    help="workloads on which the headline run also compares Rewrite Cache, Sparse "
+                         "Loading and the memory-time controller at one selection every 1 and 8 steps "
+                         "(child processes, reported under 'policies'); 'none' for none")
     ap.add_argument("--mti-lower", type=int, default=0)
     ap.add_argument("--mti-upper", type=int, default=1 << 30)
     ap.add_argument("--calibration", choices=["fixed", "entropy"], default="fixed",
@@ -114,17 +124,19 @@ def parse():
 
 
 # ---- layers ------------------------------------------------------------------------------
-POLICY = {"rewrite": hk.HARDKV_REG_REWRITE, "sparse": hk.HARDKV_REG_SPARSE, "mti": hk.HARDKV_REG_MTI}
+POLICY = {"rewrite": hk.HARDKV_REG_REWRITE, "sparse": hk.HARDKV_REG_SPARSE, "mti": hk.HARDKV_REG_MTI,
+          "mti-auto": hk.HARDKV_REG_MTI_AUTO}
 
 
 class Layer:
-    def __init__(self, wl, layer, steps, top_p=None, policy=("rewrite", 0, 0), view=("maxlen", 0),
+    def __init__(self, wl, layer, steps, top_p=None, policy=("rewrite", 0, 0, 0), view=("maxlen", 0),
                  calibration="fixed"):
         self.wl = wl
         self.inp = make_inputs(wl, layer=layer, device="cuda", steps=steps)
         total = view[1] or wl.batch * wl.num_kv_heads * wl.V_cap
         self.cfg = hk.Config.from_workload(wl, top_p=top_p, regularize=POLICY[policy[0]],
                                            mti_lower=policy[1], mti_upper=policy[2],
+                                           mti=dict(mti_horizon=policy[3]),
                                            view_layout=hk.HARDKV_VIEW_SUM if view[0] == "sum" else
                                            hk.HARDKV_VIEW_MAXLEN, view_total=total,
                                            calibration=hk.HARDKV_CAL_ENTROPY if calibration == "entropy"
@@ -554,6 +566,36 @@ def run_extras(args):
     return out
 
 
+def run_policies(args):
+    """Rewrite Cache, Sparse Loading and the memory-time controller (default costs, horizon =
+    the steps that reuse a selection) on each workload, with a selection every step and every
+    8 steps, each in a child process; step times only."""
+    import subprocess
+    out = []
+    if not args.policy_configs or args.policy_configs == "none":
+        return out
+    for key in args.policy_configs.split(","):
+        for R in (1, 8):
+            row = {"workload": get_workload(key).name, "select_every": R}
+            for pol in ("rewrite", "sparse", "mti-auto"):
+                cmd = [sys.executable, os.path.abspath(__file__), "--child", "--quick", "--config", key, "--steps",
+                       str(args.steps), "--warmup", str(args.warmup), "--no-cpu-baseline", "--extra-configs", "none",
+                       "--policy-configs", "none", "--regularize", pol, "--select-every", str(R)]
+                r = subprocess.run(cmd, capture_output=True, text=True, timeout=300)
+                if r.returncode != 0:
+                    raise RuntimeError(f"bench policy child {key} {pol} R={R} failed ({r.returncode}):\n{r.stderr[-2000:]}")
+                d = json.loads(r.stdout.strip().splitlines()[-1])
+                ms = d["select_every"]["ms_per_step"] if R > 1 else d["ms_per_step"]
+                row[pol] = {"ms_per_step": ms, "steps_per_s": 1e3 / ms, "rewritten_heads": d["rewritten_heads"]}
+            best_fixed = max(row["rewrite"]["steps_per_s"], row["sparse"]["steps_per_s"])
+            row["controller_vs_best_fixed"] = row["mti-auto"]["steps_per_s"] / best_fixed
+            print(f"bench: policies {key} R={R}: " + ", ".join(f"{p} {row[p]['ms_per_step']:.4f} ms"
+                                                              for p in ("rewrite", "sparse", "mti-auto")),
+                  file=sys.stderr, flush=True)
+            out.append(row)
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -570,6 +612,7 @@ def main():
         summarize_traffic(*args.summarize_traffic, args.copy_calib or 1024, wl, args.cmd, run_options(args, wl))
         return
     extras = [] if (args.child or args.copy_calib) else run_extras(args)
+    policies = [] if (args.child or args.copy_calib) else run_policies(args)
     hk.require_gpu()
     torch.cuda.set_device(0)
     if args.copy_calib:
@@ -589,7 +632,9 @@ def main():
 
     layers = []
     for layer in range(wl.layers):
-        L = Layer(wl, layer, nsteps, top_p=top_p, policy=(args.regularize, args.mti_lower, args.mti_upper),
+        horizon = args.mti_horizon if args.mti_horizon >= 0 else R - 1
+        L = Layer(wl, layer, nsteps, top_p=top_p,
+                  policy=(args.regularize, args.mti_lower, args.mti_upper, horizon),
                   view=(args.view_layout, args.view_total), calibration=args.calibration)
         if layer == 0 and not args.no_cpu_baseline:
             L.inp_cpu_source = {"k_ctx": L.inp.k_ctx, "v_ctx": L.inp.v_ctx, "ctx_len": L.inp.ctx_len}
@@ -639,7 +684,7 @@ def main():
         # every kernel of the step timed on the state it really sees: kernels that only
         # read what earlier ones wrote run R times back to back; the append and the
         # condensation (which advance the state) run once per restore
-        for k in range(len(STAGE_NAMES)):
+        for k in range(0 if args.quick else len(STAGE_NAMES)):
             restore()
             for j in range(k):
                 for L in layers:
@@ -678,8 +723,19 @@ def main():
         # (the append and the condensation are not re-run here: an append on the post-step
         # state would write the next pool row, which may hold a live row of the ring)
         s_last = acc_steps[-1]
-        for k in REPEATABLE:
+        for k in ([] if args.quick else REPEATABLE):
             stage_us[STAGE_NAMES[k]] = time_repeatable_stage(layers, s_last, k, args.stage_reps, args.eager)
+
+    if args.quick:
+        res = {"workload": wl.name, "regularize": args.regularize, "ms_per_step": ms_per_step,
+               "steps_per_s": 1e3 / ms_per_step,
+               "rewritten_heads": float(np.mean([L.st.regularized.float().mean().item() for L in layers]))}
+        if R > 1:
+            res["select_every"] = select_every(layers, R, restore_mode, snaps if restore_mode else snap_after, Wm, K,
+                                               timed, args.eager)
+            res["select_every"]["mti_horizon"] = horizon
+        print(json.dumps(res))
+        return
 
     # exact algorithmic bytes of the timed steps, replayed eagerly from the snapshot
     for L, sn in zip(layers, snap_after):
@@ -725,6 +781,7 @@ def main():
                    "top_p": float(layers[0].cfg.c.top_p), "cond_mode": "merge",
                    "regularize": args.regularize if args.regularize != "mti" else
                    f"mti [{args.mti_lower}, {args.mti_upper}]",
+                   "mti_horizon": horizon if args.regularize == "mti-auto" else None,
                    "view_layout": args.view_layout, "calibration": args.calibration,
                    "timing": ("one-step graph replay from the prefilled state" if restore_mode else
                               "graph of the K streaming steps") + (" (eager)" if args.eager else "")},
@@ -748,6 +805,8 @@ def main():
         res["cpu_baseline"] = cpu_baseline(wl, layers, args.cpu_units, args.cpu_seconds)
     if extras:
         res["configs"] = extras
+    if policies:
+        res["policies"] = policies
     print(json.dumps(res))
 
 

@@ -58,6 +58,21 @@ bool mti_rewrites_cfg(const hardkv_config *cfg, int64_t H, int64_t kstar, int64_
                       cfg->mti_c_gather, cfg->mti_fixed);
 }
 
+// The launches a policy needs: the memory-time controller decides per head on the device,
+// but without a scan cost or a fixed cost its choice for a head that keeps a row depends
+// only on the kept eighth b (k* cancels); when it is the same for all nine, the step is
+// shaped like REWRITE (no gather of views' rows) or SPARSE (no store path).  The device
+// still applies the controller (a head keeping nothing is never rewritten).
+int launch_policy(const hardkv_config *cfg) {
+  if (cfg->regularize != HARDKV_REG_MTI_AUTO || cfg->mti_c_scan != 0 || cfg->mti_fixed != 0)
+    return cfg->regularize;
+  const int64_t H = cfg->mti_horizon;
+  const int64_t lhs = (int64_t)cfg->mti_c_write + H * ((int64_t)cfg->mti_c_view + (int64_t)cfg->mti_c_hold);
+  int n_rw = 0;
+  for (int b = 0; b < 9; ++b) n_rw += lhs < H * (int64_t)cfg->mti_c_gather[b] ? 1 : 0;
+  return n_rw == 9 ? HARDKV_REG_REWRITE : n_rw == 0 ? HARDKV_REG_SPARSE : HARDKV_REG_MTI_AUTO;
+}
+
 struct Plan {
   Args a;
   size_t off_head, off_cmax, off_ent, off_blkinfo, off_part, off_phist, off_psum, off_selh, off_cand, off_kx,
@@ -119,6 +134,7 @@ int32_t plan(const hardkv_config *cfg, Plan &p) {
   a.view_rows = a.view_sum ? (int64_t)cfg->view_total
                            : (int64_t)cfg->batch * cfg->num_kv_heads * cfg->view_cap;
   a.reg_policy = cfg->regularize;
+  a.reg_launch = launch_policy(cfg);
   a.mti_lower = cfg->mti_lower;
   a.mti_upper = cfg->mti_upper;
   a.mti_horizon = cfg->mti_horizon;
@@ -315,8 +331,8 @@ hipError_t step_stage(const hardkv_config *cfg, Args &a, int stage, hipStream_t 
 // the other heads (none under REWRITE) from the pool; the combine reduces both.
 hipError_t attend_calls(const hardkv_config *cfg, Args &a, hipStream_t s, bool sparse) {
   const bool bf = is_bf16(cfg);
-  const bool views = !sparse && a.reg_policy != HARDKV_REG_SPARSE;
-  const bool gather = sparse || a.reg_policy != HARDKV_REG_REWRITE;
+  const bool views = !sparse && a.reg_launch != HARDKV_REG_SPARSE;
+  const bool gather = sparse || a.reg_launch != HARDKV_REG_REWRITE;
   if (!views) a.nv_att = 0;
   a.nvp = a.nv_att;
   a.ntp = a.nt_att;

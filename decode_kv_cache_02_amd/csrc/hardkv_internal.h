@@ -126,6 +126,9 @@ struct Args {
   int npart, part_cd_base;  // partial slots per head; first condensed/dense slot
   int xp_base, nxp;         // gathered-row partial slots of the standalone attention
   int reg_policy, mti_lower, mti_upper;  // regularize policy and its budget thresholds
+  int reg_launch;           // the policy the launches are shaped for: reg_policy, or for the
+                            // memory-time controller REWRITE / SPARSE when its choice is the same
+                            // for every head that keeps a row
   // the memory-time controller (policy MTI_AUTO): H, per-row costs (fs), fixed cost
   int mti_horizon;
   uint32_t mti_c_view, mti_c_write, mti_c_scan, mti_c_hold;

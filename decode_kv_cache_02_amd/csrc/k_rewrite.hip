@@ -266,7 +266,7 @@ hipError_t launch_t(const Args &a, hipStream_t s, bool mask, bool copy, bool att
   // the fused step writes views unless every head only gathers (SPARSE); the attention
   // gathers never write them
   if (mask && copy && attend)
-    return a.reg_policy == HARDKV_REG_SPARSE ? launch_g<T, true, true, true, false>(a, s)
+    return a.reg_launch == HARDKV_REG_SPARSE ? launch_g<T, true, true, true, false>(a, s)
                                              : launch_g<T, true, true, true, true>(a, s);
   if (mask && !copy && !attend) return launch_g<T, true, false, false, false>(a, s);
   if (!mask && copy && !attend) return launch_g<T, false, true, false, true>(a, s);

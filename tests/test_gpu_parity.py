@@ -247,6 +247,10 @@ POLICY_CASES = {
     "mti_auto_merge_batch16": (dict(batch=16, cond_mode=COND_MERGE, ctx_len=500, ctx_min=100, heavy=(0, 6),
                                     steps=3), 3),
     "mti_auto_f32": (dict(dtype="f32", batch=6, heavy=(0, 6), steps=2), 3),
+    # the default costs with no reuse (no head is rewritten: launched as Sparse Loading) and
+    # with 7 reused steps (every head that keeps a row is: launched as Rewrite Cache)
+    "mti_auto_h0": (dict(cond_mode=COND_MERGE, steps=2), "3h0"),
+    "mti_auto_h7": (dict(cond_mode=COND_MERGE, steps=2), "3h7"),
 }
 
 
@@ -264,13 +268,18 @@ def test_regularize_policy_parity(name, fused):
     wl = tiny_workload(steps=steps, **kw)
     lo, hi = _mti_bounds(wl) if pol == 2 else (0, 0)
     mti = _mti_auto_costs(wl) if pol == 3 else None
+    if isinstance(pol, str):  # the controller with the default costs and a horizon
+        mti, pol = dict(mti_horizon=int(pol[2:])), 3
     print(f"case {name} fused={fused}: policy {pol} [{lo}, {hi}] {mti} {wl}", flush=True)
     pr = Pair(wl, regularize=pol, mti_lower=lo, mti_upper=hi, mti=mti)
     for _ in range(steps):
         pr.step(fused=fused)
-    if pol in (2, 3):
-        rw = pr.st.regularized.cpu().numpy()
+    rw = pr.st.regularized.cpu().numpy()
+    kept = pr.st.budget.cpu().numpy() > 0
+    if pol == 2 or (pol == 3 and mti.get("mti_fixed")):
         assert rw.any() and not rw.all(), rw
+    elif pol == 3:  # the default costs: a view pays from three reused steps on
+        assert np.array_equal(rw.astype(bool), kept & (mti["mti_horizon"] >= 3)), rw
 
 
 @pytest.mark.parametrize("name", ["evict_bf16", "merge_wrap", "g8"])

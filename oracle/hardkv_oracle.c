@@ -544,8 +544,11 @@ int32_t orc_prefill(const orc_cfg *cfg, orc_state *st, const void *k_ctx, const 
 /* ------------------------------------------------------------------------------------
  * One unit (sequence b, KV head h) of the step after the append.
  * ---------------------------------------------------------------------------------- */
+/* ahead: a selection made ahead of its use (seq_len is the snapshot of the step it is made
+ * for): plan, score, calibrate, top-p and regularize only; the planned condensation waits for
+ * orc_condense_plan and there is no attention. */
 static uint32_t unit_step(const orc_cfg *cfg, orc_state *st, int b, int h, const void *q,
-                          double *out, int do_attend) {
+                          double *out, int do_attend, int ahead) {
   const int H = cfg->num_kv_heads, Hq = cfg->num_q_heads, G = Hq / H, D = cfg->head_dim;
   const int eb = cfg->elem_bytes, P = cfg->pool_blocks;
   const int64_t u = (int64_t)b * H + h;
@@ -666,7 +669,7 @@ static uint32_t unit_step(const orc_cfg *cfg, orc_state *st, int b, int h, const
 
   /* condense (section 2.A, tier 3): each of the E oldest blocks is dropped
    * (evict) or merged into the next condensed slot with weights w / W_all */
-  if (cfg->cond_mode == ORC_COND_MERGE) {
+  if (cfg->cond_mode == ORC_COND_MERGE && !ahead) {
     const int C = cfg->condensed_slots;
     for (int64_t e = 0; e < E; ++e) {
       int32_t sigma = st->cond_cursor[u];
@@ -684,7 +687,7 @@ static uint32_t unit_step(const orc_cfg *cfg, orc_state *st, int b, int h, const
       st->cond_n[si] += BK;
     }
   }
-  st->pool_head[u] = c + BK * E;
+  if (!ahead) st->pool_head[u] = c + BK * E;
   st->pend_sel[u] = pend;
   st->budget[u] = kstar;
   st->n_condense[u] = (int32_t)E;
@@ -693,7 +696,7 @@ static uint32_t unit_step(const orc_cfg *cfg, orc_state *st, int b, int h, const
   st->thresh[u] = T;
 
   /* attention over condensed, sparse (view) and dense tiers */
-  if (do_attend) {
+  if (do_attend && !ahead) {
     tier_ctx *tc = (tier_ctx *)malloc(sizeof(tier_ctx));
     tc->cfg = cfg;
     tc->st = st;
@@ -770,7 +773,7 @@ int32_t orc_step(const orc_cfg *cfg, orc_state *st, const void *q, const void *k
   int nt = nthreads > 0 ? nthreads : omp_get_max_threads();
 #pragma omp parallel for schedule(dynamic, 1) num_threads(nt) reduction(| : err)
 #endif
-  for (int64_t i = 0; i < units; ++i) err |= unit_step(cfg, st, (int)(i / H), (int)(i % H), q, out, do_attend);
+  for (int64_t i = 0; i < units; ++i) err |= unit_step(cfg, st, (int)(i / H), (int)(i % H), q, out, do_attend, 0);
   (void)nthreads;
 
   /* Flatten Index to the sum (section 2.C): the rewritten heads' kept rows, each head's in
@@ -867,5 +870,52 @@ int32_t orc_step_reuse(const orc_cfg *cfg, orc_state *st, const void *q, const v
   for (int64_t i = 0; i < units; ++i) unit_reuse(cfg, st, (int)(i / H), (int)(i % H), q, out);
   (void)nthreads;
   st->error_word |= err;
+  return 0;
+}
+
+/* ------------------------------------------------------------------------------------
+ * The asynchronous pipeline of the four stages (section 2.A names it; reading: with a
+ * selection reused over later steps, the next one can be made on the side while decode
+ * steps continue on the current one, and switched in at a later step).  A selection made
+ * ahead runs plan, score, calibrate, top-p and regularize over the pool as it stood after
+ * the append of step t_snap (seq_len holds that snapshot here; the pool head is the live
+ * one, which only a condensation moves), into a state of its own that shares the pool,
+ * the dense and sink rows and the condensed tier; its condensation is applied at the
+ * switch, with its own weights and mass, by orc_condense_plan.
+ * ---------------------------------------------------------------------------------- */
+int32_t orc_select_ahead(const orc_cfg *cfg, orc_state *st, const void *q) {
+  const int B = cfg->batch, H = cfg->num_kv_heads;
+  uint32_t err = 0;
+  if (cfg->view_layout == 1) return -2; /* packed views are written by orc_step only */
+  for (int64_t i = 0; i < (int64_t)B * H; ++i) err |= unit_step(cfg, st, (int)(i / H), (int)(i % H), q, NULL, 0, 1);
+  st->error_word |= err;
+  return 0;
+}
+
+int32_t orc_condense_plan(const orc_cfg *cfg, orc_state *st) {
+  const int B = cfg->batch, H = cfg->num_kv_heads, D = cfg->head_dim, eb = cfg->elem_bytes;
+  const int C = cfg->condensed_slots;
+  for (int64_t u = 0; u < (int64_t)B * H; ++u) {
+    const int64_t c = st->pool_head[u], E = st->n_condense[u];
+    const uint64_t w_all = st->w_all[u];
+    if (cfg->cond_mode == ORC_COND_MERGE) {
+      for (int64_t e = 0; e < E; ++e) {
+        int32_t sigma = st->cond_cursor[u];
+        st->cond_cursor[u] = (sigma + 1) % C;
+        int64_t si = u * C + sigma;
+        for (int64_t j = c + BK * e; j < c + BK * (e + 1); ++j) {
+          int64_t rr = pool_row(cfg, u, j);
+          double om = (double)st->weights[rr] / (double)w_all;
+          st->cond_omega[si] += om;
+          for (int d = 0; d < D; ++d) {
+            st->cond_kn[si * D + d] += om * (double)elem_get(st->pool_k, rr * D + d, eb);
+            st->cond_vn[si * D + d] += om * (double)elem_get(st->pool_v, rr * D + d, eb);
+          }
+        }
+        st->cond_n[si] += BK;
+      }
+    }
+    st->pool_head[u] = c + BK * E;
+  }
   return 0;
 }

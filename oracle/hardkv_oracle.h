@@ -115,6 +115,14 @@ int32_t orc_step(const orc_cfg *cfg, orc_state *st, const void *q, const void *k
  * marks), the pool positions that arrived since it, and the dense window */
 int32_t orc_step_reuse(const orc_cfg *cfg, orc_state *st, const void *q, const void *k_new,
                        const void *v_new, double *out, int32_t nthreads);
+/* a selection made ahead of its use (the asynchronous pipeline): st's seq_len holds the
+ * snapshot of the step it is made for, its pool, dense, sink and condensed buffers and pool
+ * head are the live ones; plan, score, calibrate, top-p and regularize, no condensation and
+ * no attention (max-length views only) */
+int32_t orc_select_ahead(const orc_cfg *cfg, orc_state *st, const void *q);
+/* the switch to a selection made ahead: its planned condensation (E blocks from the pool
+ * head, its weights and mass), and the pool head moved past them */
+int32_t orc_condense_plan(const orc_cfg *cfg, orc_state *st);
 /* entropy-matched temperature: d are the G x n raw dot products (query-major), s the n
  * max-pooled scores; returns the fitted tau (fp32) and the target entropy in *h_target */
 float   orc_fit_tau(const float *d, int32_t G, const float *s, int64_t n, int32_t D, double *h_target);

@@ -112,6 +112,10 @@ def lib():
         L.orc_mti_thresholds.argtypes = [C.POINTER(OrcCfg), i64, C.POINTER(i64), C.POINTER(i64)]
         L.orc_mti_period.restype = i32
         L.orc_mti_period.argtypes = [C.POINTER(OrcCfg), i64, i64, i64, i32]
+        L.orc_select_ahead.restype = i32
+        L.orc_select_ahead.argtypes = [C.POINTER(OrcCfg), C.POINTER(OrcState), vp]
+        L.orc_condense_plan.restype = i32
+        L.orc_condense_plan.argtypes = [C.POINTER(OrcCfg), C.POINTER(OrcState)]
         L.orc_full_attention.restype = None
         L.orc_full_attention.argtypes = [vp, vp, vp, i32, i32, vp]
         _lib = L
@@ -338,6 +342,38 @@ class Oracle:
         if rc != 0:
             raise RuntimeError(f"orc_step_reuse failed: {rc}")
         return out
+
+    # the asynchronous pipeline -----------------------------------------------------------
+    SHARED = ("dense_k", "dense_v", "pool_k", "pool_v", "cond_kn", "cond_vn", "cond_omega", "cond_n",
+              "cond_cursor", "pool_head", "sink_k", "sink_v")
+
+    def twin(self) -> "Oracle":
+        """A state for a selection made ahead: it shares this one's pool, dense and sink rows,
+        condensed tier and pool head, and has its own step counter and selection buffers."""
+        o = Oracle.__new__(Oracle)
+        o.__dict__.update({k: v for k, v in self.__dict__.items()})
+        for n in ("view_k", "view_v", "view_pos", "view_off", "tau_fit", "scores", "weights", "mask", "budget",
+                  "n_condense", "w_all", "w_u", "thresh", "regularized", "pend_sel", "seq_len"):
+            setattr(o, n, getattr(self, n).copy())
+        o.st = OrcState(*[_p(getattr(o, n)) for n in (
+            "dense_k", "dense_v", "pool_k", "pool_v", "view_k", "view_v", "view_pos", "cond_kn",
+            "cond_vn", "cond_omega", "cond_n", "cond_cursor", "seq_len", "pool_head", "scores",
+            "weights", "mask", "budget", "n_condense", "w_all", "w_u", "thresh", "regularized",
+            "view_off", "tau_fit")], 0, _p(o.sink_k), _p(o.sink_v), _p(o.pend_sel))
+        for n in self.SHARED:
+            assert getattr(o, n) is getattr(self, n)
+        return o
+
+    def select_ahead(self, q, t_snapshot) -> None:
+        """The selection made ahead for the step whose append left seq_len = t_snapshot."""
+        self.seq_len[:] = np.asarray(t_snapshot, np.int64)
+        rc = lib().orc_select_ahead(C.byref(self.cfg), C.byref(self.st), _p(_store_np(q)))
+        if rc != 0:
+            raise RuntimeError(f"orc_select_ahead failed: {rc}")
+
+    def condense_plan(self) -> None:
+        """The switch: the planned condensation of the selection made ahead."""
+        lib().orc_condense_plan(C.byref(self.cfg), C.byref(self.st))
 
     # logical views used by the tests ----------------------------------------------------
     def pool_row_index(self, p: np.ndarray) -> np.ndarray:

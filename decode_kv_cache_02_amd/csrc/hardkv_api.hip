@@ -76,7 +76,7 @@ int launch_policy(const hardkv_config *cfg) {
 struct Plan {
   Args a;
   size_t off_head, off_cmax, off_ent, off_blkinfo, off_part, off_phist, off_psum, off_selh, off_cand, off_kx,
-      off_fith, off_fitp, ws_bytes;
+      off_fith, off_fitp, off_tsnap, ws_bytes;
 };
 
 // Checks the configuration and derives every size; fills the size fields of p.a.
@@ -217,7 +217,8 @@ int32_t plan(const hardkv_config *cfg, Plan &p) {
   p.off_fith = align256(p.off_kx + (size_t)BH * sizeof(uint32_t));
   const size_t fsplit = a.nfs > 1 ? 1 : 0;  // the split fit's scratch
   p.off_fitp = align256(p.off_fith + fsplit * (size_t)BH * sizeof(FitHead));
-  p.ws_bytes = align256(p.off_fitp + fsplit * (size_t)FIT_ROUNDS * BH * a.nfs * 2 * FIT_POINTS * sizeof(double));
+  p.off_tsnap = align256(p.off_fitp + fsplit * (size_t)FIT_ROUNDS * BH * a.nfs * 2 * FIT_POINTS * sizeof(double));
+  p.ws_bytes = align256(p.off_tsnap + (size_t)a.B * sizeof(int64_t));
   return HARDKV_OK;
 }
 
@@ -280,6 +281,7 @@ int32_t bind(const hardkv_state *st, Plan &p) {
   a.kx = reinterpret_cast<uint32_t *>(ws + p.off_kx);
   a.fith = reinterpret_cast<FitHead *>(ws + p.off_fith);
   a.fitp = reinterpret_cast<double *>(ws + p.off_fitp);
+  a.tsnap = reinterpret_cast<int64_t *>(ws + p.off_tsnap);
   return HARDKV_OK;
 }
 
@@ -502,6 +504,59 @@ int32_t hardkv_step_noalloc(const hardkv_config *cfg, hardkv_state *st, const vo
   p.a.v_new = v_new;
   p.a.out = out;
   return hip_status(step_all(cfg, p.a, (hipStream_t)stream));
+}
+
+// The pipeline's two states: the buffers that hold the cache itself are shared, those a
+// selection writes are not.
+int32_t check_pipeline_pair(const hardkv_state *nx, const hardkv_state *cur) {
+  if (!nx || !cur) return HARDKV_EINVAL;
+  const void *shared[][2] = {{nx->dense_k, cur->dense_k}, {nx->dense_v, cur->dense_v}, {nx->pool_k, cur->pool_k},
+                             {nx->pool_v, cur->pool_v}, {nx->cond_kn, cur->cond_kn}, {nx->cond_vn, cur->cond_vn},
+                             {nx->cond_omega, cur->cond_omega}, {nx->cond_n, cur->cond_n},
+                             {nx->cond_cursor, cur->cond_cursor}, {nx->seq_len, cur->seq_len},
+                             {nx->pool_head, cur->pool_head}, {nx->sink_k, cur->sink_k}, {nx->sink_v, cur->sink_v}};
+  for (auto &pr : shared)
+    if (pr[0] != pr[1]) return HARDKV_EINVAL;
+  const void *own[][2] = {{nx->view_k, cur->view_k}, {nx->view_v, cur->view_v}, {nx->view_pos, cur->view_pos},
+                          {nx->scores, cur->scores}, {nx->weights, cur->weights}, {nx->mask, cur->mask},
+                          {nx->budget, cur->budget}, {nx->n_condense, cur->n_condense}, {nx->w_all, cur->w_all},
+                          {nx->w_u, cur->w_u}, {nx->thresh, cur->thresh}, {nx->workspace, cur->workspace}};
+  for (auto &pr : own)
+    if (pr[0] == pr[1]) return HARDKV_EINVAL;
+  if (nx->regularized && nx->regularized == cur->regularized) return HARDKV_EINVAL;
+  if (nx->tau_fit && nx->tau_fit == cur->tau_fit) return HARDKV_EINVAL;
+  return HARDKV_OK;
+}
+
+int32_t hardkv_select_fork(const hardkv_config *cfg, hardkv_state *st_next, const hardkv_state *st_cur,
+                           void *stream) {
+  Plan p, pc;
+  int32_t rc = setup(cfg, st_next, p);
+  if (rc != HARDKV_OK) return rc;
+  rc = setup(cfg, st_cur, pc);
+  if (rc != HARDKV_OK) return rc;
+  rc = check_pipeline_pair(st_next, st_cur);
+  if (rc != HARDKV_OK) return rc;
+  p.a.kx_src = pc.a.kx;
+  return hip_status(launch_fork(p.a, (hipStream_t)stream));
+}
+
+int32_t hardkv_select_ahead(const hardkv_config *cfg, hardkv_state *st_next, const void *q, void *stream) {
+  Plan p;
+  int32_t rc = setup(cfg, st_next, p);
+  if (rc != HARDKV_OK) return rc;
+  if (p.a.view_sum) return HARDKV_EUNSUPPORTED;
+  if (!aligned16(q)) return HARDKV_EINVAL;
+  p.a.q = q;
+  p.a.seq_len = p.a.tsnap;  // the pool as it stood at the forked step
+  p.a.gather_mode = GATHER_REWRITE;
+  hipStream_t s = (hipStream_t)stream;
+  const bool bf = is_bf16(cfg);
+  hipError_t e = launch_score(p.a, s, bf);
+  if (e == hipSuccess && p.a.calibration) e = launch_fit(p.a, s);
+  if (e == hipSuccess) e = launch_select(p.a, s, bf);
+  if (e == hipSuccess) e = launch_rewrite(p.a, s, bf, true, true, false);  // mask words and views
+  return hip_status(e);
 }
 
 int32_t hardkv_step_stage(const hardkv_config *cfg, hardkv_state *st, const void *q,

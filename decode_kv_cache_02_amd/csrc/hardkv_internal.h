@@ -103,6 +103,8 @@ struct Args {
                       // pool (since its prefill): its scores then take the unfused products
   int kx_unknown;     // 1: kx is not kept for this state (the no-alloc step): every head's
                       // scores take the unfused products
+  int64_t *tsnap;     // [B] t of the step a selection made ahead is for (the pipeline)
+  const uint32_t *kx_src;  // the current state's kx, copied by the pipeline's fork
   // prefill
   const void *k_ctx, *v_ctx;
   const int64_t *ctx_len;
@@ -157,6 +159,9 @@ enum { GATHER_STEP = 0, GATHER_REWRITE = 1, GATHER_ATTEND_NRW = 2, GATHER_ATTEND
 // launchers (one per kernel); each returns a hipError_t
 hipError_t launch_prefill(const Args &a, hipStream_t s, bool bf16);
 hipError_t launch_append(const Args &a, hipStream_t s, bool bf16);
+// the pipeline's fork: t of every sequence and the current state's key-magnitude flags into
+// the state of the selection made ahead
+hipError_t launch_fork(const Args &a, hipStream_t s);
 hipError_t launch_score(const Args &a, hipStream_t s, bool bf16);
 hipError_t launch_select(const Args &a, hipStream_t s, bool bf16);
 // exclusive scan of the rewritten budgets into view_off and each head's voff (SUM layout)

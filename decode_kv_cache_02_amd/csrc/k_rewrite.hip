@@ -147,7 +147,8 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_rewrite(Args a) {
     }
     ns += __popcll(mw);
   }
-  if (COPY) {
+  // a launch that only rewrites (no attention) copies nothing for a head it does not rewrite
+  if (COPY && (ATTN || store)) {
     wave_sync();
     // Kept rows move 16 at a time (4 per 16-lane group) and are attended while in
     // registers.  Keys and values are pipelined half a batch apart: the next batch's key
@@ -269,6 +270,7 @@ hipError_t launch_t(const Args &a, hipStream_t s, bool mask, bool copy, bool att
     return a.reg_launch == HARDKV_REG_SPARSE ? launch_g<T, true, true, true, false>(a, s)
                                              : launch_g<T, true, true, true, true>(a, s);
   if (mask && !copy && !attend) return launch_g<T, true, false, false, false>(a, s);
+  if (mask && copy && !attend) return launch_g<T, true, true, false, true>(a, s);
   if (!mask && copy && !attend) return launch_g<T, false, true, false, true>(a, s);
   if (!mask && copy && attend) return launch_g<T, false, true, true, false>(a, s);
   return hipErrorInvalidValue;

@@ -141,7 +141,20 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_append(Args a) {
   if (tid == 0) a.seq_len[b] = t + 1;
 }
 
+// grid (ceil(B*Hkv / 256)): the snapshot of t for a selection made ahead, and the key
+// flags of the state it forks from (kept through that state's appends so far).
+__global__ __launch_bounds__(NTHREADS) void hardkv_fork(Args a) {
+  const int i = blockIdx.x * NTHREADS + threadIdx.x;
+  if (i < a.B) a.tsnap[i] = a.seq_len[i];
+  if (i < a.B * a.Hkv) a.kx[i] = a.kx_src[i];
+}
+
 }  // namespace
+
+hipError_t launch_fork(const Args &a, hipStream_t s) {
+  hipLaunchKernelGGL(hardkv_fork, dim3((a.B * a.Hkv + NTHREADS - 1) / NTHREADS), dim3(NTHREADS), 0, s, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_prefill(const Args &a, hipStream_t s, bool bf16) {
   hipLaunchKernelGGL(hardkv_prefill_clear, dim3((a.B * a.Hkv + NTHREADS - 1) / NTHREADS), dim3(NTHREADS), 0, s, a);

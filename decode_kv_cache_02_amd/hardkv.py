@@ -34,7 +34,8 @@ BLOCK, HEAD_DIM = 64, 128
 EXPORTS = ("hardkv_workspace_size", "hardkv_prefill", "hardkv_append", "hardkv_select",
            "hardkv_regularize", "hardkv_condense", "hardkv_attend", "hardkv_attend_sparse", "hardkv_step",
            "hardkv_step_reuse", "hardkv_step_noalloc", "hardkv_step_stage", "hardkv_step_num_stages", "hardkv_step_stage_name",
-           "hardkv_mti_thresholds", "hardkv_mti_period", "hardkv_strerror")
+           "hardkv_mti_thresholds", "hardkv_mti_period", "hardkv_select_fork", "hardkv_select_ahead",
+           "hardkv_strerror")
 
 
 class HardKVError(RuntimeError):
@@ -96,6 +97,8 @@ def lib() -> C.CDLL:
         L.hardkv_step_stage.argtypes = [cp, sp, vp, vp, vp, vp, i32, vp]
         L.hardkv_step_num_stages.argtypes = []
         L.hardkv_mti_thresholds.argtypes = [cp, i64, C.POINTER(i32), C.POINTER(i32)]
+        L.hardkv_select_fork.argtypes = [cp, sp, sp, vp]
+        L.hardkv_select_ahead.argtypes = [cp, sp, vp, vp]
         L.hardkv_mti_period.argtypes = [cp, i64, i64, i64, i32, C.POINTER(i32)]
         L.hardkv_step_stage_name.argtypes = [i32]
         L.hardkv_step_stage_name.restype = C.c_char_p
@@ -234,6 +237,23 @@ class State:
         self.workspace = torch.zeros((self.workspace_bytes,), dtype=torch.uint8, **kw)
         self.c = hardkv_state(*[_ptr(getattr(self, n)) for n in _STATE_FIELDS], self.workspace_bytes)
 
+    # buffers that hold the cache itself, shared by the two states of the pipeline
+    SHARED = ("dense_k", "dense_v", "pool_k", "pool_v", "sink_k", "sink_v", "cond_kn", "cond_vn", "cond_omega",
+              "cond_n", "cond_cursor", "seq_len", "pool_head", "error_word")
+
+    def twin(self) -> "State":
+        """A state for a selection made ahead (hardkv_select_fork / hardkv_select_ahead): the
+        same cache buffers, its own selection buffers and workspace."""
+        o = State.__new__(State)
+        o.cfg = self.cfg
+        for n in _STATE_FIELDS:
+            t = getattr(self, n)
+            setattr(o, n, t if n in self.SHARED else torch.zeros_like(t))
+        o.view_pos.fill_(-1)
+        o.workspace_bytes = self.workspace_bytes
+        o.c = hardkv_state(*[_ptr(getattr(o, n)) for n in _STATE_FIELDS], o.workspace_bytes)
+        return o
+
     def tensors(self):
         return {n: getattr(self, n) for n in _STATE_FIELDS}
 
@@ -307,6 +327,16 @@ def hardkv_mti_period(cfg: Config, n_pool: int, n_survivors: int, kstar: int, ma
     _check("hardkv_mti_period", lib().hardkv_mti_period(C.byref(cfg.c), int(n_pool), int(n_survivors), int(kstar),
                                                         int(max_period), C.byref(r)))
     return int(r.value)
+
+
+def hardkv_select_fork(cfg: Config, st_next: State, st_cur: State, stream=None) -> None:
+    _check("hardkv_select_fork", lib().hardkv_select_fork(C.byref(cfg.c), C.byref(st_next.c), C.byref(st_cur.c),
+                                                          _stream(stream)))
+
+
+def hardkv_select_ahead(cfg: Config, st_next: State, q, stream=None) -> None:
+    _check("hardkv_select_ahead", lib().hardkv_select_ahead(C.byref(cfg.c), C.byref(st_next.c), _ptr(q),
+                                                            _stream(stream)))
 
 
 def hardkv_step_num_stages() -> int:

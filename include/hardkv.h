@@ -329,6 +329,35 @@ int32_t hardkv_step_reuse(const hardkv_config *cfg, hardkv_state *st, const void
 int32_t hardkv_step_noalloc(const hardkv_config *cfg, hardkv_state *st, const void *q, const void *k_new,
                             const void *v_new, float *out, void *stream);
 
+/* The asynchronous pipeline (section 2.A: the four stages run as an asynchronous pipeline;
+ * a reading with selections reused over later steps): the next selection is made on a second
+ * stream while decode steps continue on the current one (hardkv_step_reuse), and switched in
+ * at a later step.  It takes a second state, st_next, that shares the cache itself with the
+ * current one (dense_k/v, pool_k/v, sink_k/v, cond_kn/vn/omega/n, cond_cursor, seq_len,
+ * pool_head: the same pointers) and has its own selection buffers (scores, weights, mask,
+ * budget, n_condense, w_all, w_u, thresh, view_k/v, view_pos, regularized, tau_fit) and its
+ * own workspace; otherwise HARDKV_EINVAL.
+ *   1. hardkv_select_fork(cfg, st_next, st_cur, s_main): on the main stream, right after the
+ *      append of the step the selection is made for: records t of every sequence and the
+ *      current state's key-magnitude record in st_next's workspace.
+ *   2. hardkv_select_ahead(cfg, st_next, q, s_side): on a second stream, after an event the
+ *      caller records on s_main behind the fork: score, calibrate, top-p and Rewrite Cache
+ *      (the views of the heads the policy rewrites) over the pool as it stood at the forked
+ *      step, with that step's queries q; the planned condensation is not applied.  The
+ *      max-length view layout only (HARDKV_EUNSUPPORTED for SUM).
+ *   3. Meanwhile s_main may take hardkv_step_reuse steps on st_cur (no selection, no
+ *      condensation): they append and attend the current selection.  The pool ring must
+ *      hold S_cap plus the positions of the steps until the switch.
+ *   4. The switch, on s_main after the caller waits for the side stream: hardkv_condense(cfg,
+ *      st_next) applies the planned condensation (the blocks and merge weights of the forked
+ *      step), and from then on st_next is the current state (hardkv_step_reuse attends its
+ *      kept rows and every position since the forked step).
+ * Switched in at once (fork, ahead and condense before the next append), the selection is
+ * the step's own: the same masks, budgets, views and condensed tier as hardkv_step. */
+int32_t hardkv_select_fork(const hardkv_config *cfg, hardkv_state *st_next, const hardkv_state *st_cur,
+                           void *stream);
+int32_t hardkv_select_ahead(const hardkv_config *cfg, hardkv_state *st_next, const void *q, void *stream);
+
 /* Launches only kernel `stage` of hardkv_step (0 append, 1 score, 2 select, 3 condense,
  * 4 rewrite with the view, condensed and dense attention, 5 combine), for timing one
  * kernel on its own; the condensation is always its own stage here.  Stages 1, 2, 4 and 5

@@ -22,7 +22,7 @@ def _declared():
 def test_exports_every_declared_symbol():
     lib = hk.lib()
     names = _declared()
-    assert len(names) == 17, names
+    assert len(names) == 19, names
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(hk.EXPORTS)
@@ -232,3 +232,25 @@ def test_mti_helper_validation():
     for H, want in ((2, (0, -1)), (3, (1, 15809))):
         c = hk.Config.from_workload(tiny_workload(), regularize=hk.HARDKV_REG_MTI_AUTO, mti=dict(mti_horizon=H))
         assert hk.hardkv_mti_thresholds(c, 15809) == want
+
+
+@_no_gpu
+def test_pipeline_pair_validation():
+    """The pipeline's fork refuses states that do not share the cache or that share a
+    selection buffer."""
+    cfg = _cfg()
+    L = hk.lib()
+    cur = _fake_state(cfg)
+    nxt = _fake_state(cfg)
+    # every buffer of nxt differs from cur's: the cache is not shared
+    assert L.hardkv_select_fork(C.byref(cfg.c), C.byref(nxt), C.byref(cur), None) == hk.HARDKV_EINVAL
+    for n in hk.State.SHARED:
+        setattr(nxt, n, getattr(cur, n))
+    nxt.mask = cur.mask  # a selection buffer shared
+    assert L.hardkv_select_fork(C.byref(cfg.c), C.byref(nxt), C.byref(cur), None) == hk.HARDKV_EINVAL
+    ok = C.c_void_p(1 << 41)
+    bad = C.c_void_p((1 << 41) + 8)
+    assert L.hardkv_select_ahead(C.byref(cfg.c), C.byref(nxt), bad, None) == hk.HARDKV_EINVAL
+    packed = _cfg(view_layout=1, view_total=100)
+    st = _fake_state(packed)
+    assert L.hardkv_select_ahead(C.byref(packed.c), C.byref(st), ok, None) == hk.HARDKV_EUNSUPPORTED

@@ -85,6 +85,12 @@ def parse():
                          "memory-time controller (default costs, horizon --mti-horizon)")
     ap.add_argument("--mti-horizon", type=int, default=-1,
                     help="reused steps the controller plans for (default: --select-every minus one)")
+    ap.add_argument("--pipeline", type=int, default=0,
+                    help="with --select-every R: also time the asynchronous pipeline, each selection made "
+                         "ahead on a second stream and switched in this many steps later (0: off)")
+    ap.add_argument("--pipeline-mode", choices=["side", "spread"], default="side",
+                    help="the selection made ahead: all of it on a second stream (side), or in --pipeline "
+                         "parts of the units, one after each step before the switch, on the main stream (spread)")
     ap.add_argument("--quick", action="store_true",
                     help="step time only (and --select-every): no per-kernel timing, bytes or roofline")
     ap.add_argument("--policy-configs", default=POLICY_DEFAULT,
@@ -250,10 +256,11 @@ def select_every(layers, R, restore_mode, snaps, Wm, K, timed, eager):
     steps = list(range(R)) if restore_mode else list(range(Wm, Wm + K))
     first = steps[0]
 
-    def run():
+    def run(mark=lambda: None):
         for s in steps:
             for L in layers:
                 L.step(s) if (s - first) % R == 0 else L.reuse(s)
+            mark()
 
     restore()
     run()
@@ -272,11 +279,119 @@ def select_every(layers, R, restore_mode, snaps, Wm, K, timed, eager):
         times.append(timed(g.replay if g is not None else run))
     err = int(max(int(L.st.error_word[0].item()) for L in layers))
     restore()
+    lat = step_latencies(run, len(steps))
+    restore()
     torch.cuda.synchronize()
     ms_step = float(np.mean(times)) / len(steps)
     return {"R": R, "ms_per_step": ms_step, "steps_per_s": 1e3 / ms_step, "error_word": err,
+            "eager_step_latency": lat,
             "timing": ("graph of one step with selection and R - 1 without, from the prefilled state"
                        if restore_mode else "graph of the K streaming steps, a selection at every R-th")}
+
+
+def step_latencies(run_steps, nsteps):
+    """Per-step latency of a schedule run eagerly: an event on the main stream after each step
+    (run_steps(mark) calls mark() after each); the time between consecutive marks, in ms (the
+    host stays ahead of the device, so the gaps are the device's time per step)."""
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(nsteps + 1)]
+    i = [0]
+
+    def mark():
+        evs[i[0]].record()
+        i[0] += 1
+    mark()
+    run_steps(mark)
+    torch.cuda.synchronize()
+    lat = [evs[k].elapsed_time(evs[k + 1]) for k in range(i[0] - 1)]
+    return {"p50_ms": float(np.median(lat)), "max_ms": float(np.max(lat)), "min_ms": float(np.min(lat))}
+
+
+def pipeline_every(layers, R, lag, restore_mode, snaps, Wm, timed, eager, mode="side"):
+    """Steps with one selection every R steps made ahead: at the first step of each period the
+    main stream takes a step on the current selection and forks; a second stream makes the
+    selection for that step (hardkv_select_ahead); `lag` steps later the main stream waits for
+    it, condenses by its plan and goes on with it.  Two periods (the two states swap roles)
+    are captured in one graph with the cross-stream waits; each replay starts from a step
+    with selection made the usual way (outside the timing).  Returns the mean time per step."""
+    assert 1 <= lag < R
+    side = torch.cuda.Stream()
+    twins = [L.st.twin() for L in layers]
+    first = 0 if restore_mode else Wm
+    steps = list(range(first + 1, first + 1 + 2 * R))
+
+    def restore():
+        for L, sn in zip(layers, snaps):
+            L.restore(sn)
+
+    def setup():
+        restore()
+        for L in layers:
+            L.step(first)  # the selection the first period starts from
+
+    def run(mark=lambda: None):
+        main = torch.cuda.current_stream()  # (the capture stream while a graph is captured)
+        cur = [L.st for L in layers]
+        nxt = list(twins)
+        done = None
+        for i, s in enumerate(steps):
+            k = i % R
+            if k == lag and done is not None:  # the switch
+                if done != "spread":
+                    main.wait_event(done)
+                for j, L in enumerate(layers):
+                    hk.hardkv_condense(L.cfg, nxt[j], main)
+                cur, nxt = nxt, cur
+                done = None
+            for j, L in enumerate(layers):
+                hk.hardkv_step_reuse(L.cfg, cur[j], L.inp.q[s], L.inp.k_new[s], L.inp.v_new[s], L.out, main)
+            if k == 0:  # the fork and the selection made ahead
+                for j, L in enumerate(layers):
+                    hk.hardkv_select_fork(L.cfg, nxt[j], cur[j], main)
+                q_fork = s
+                if mode == "side":
+                    ev = torch.cuda.Event()
+                    ev.record(main)
+                    side.wait_event(ev)
+                    for j, L in enumerate(layers):
+                        hk.hardkv_select_ahead(L.cfg, nxt[j], L.inp.q[s], side)
+                    done = torch.cuda.Event()
+                    done.record(side)
+            if mode == "spread" and k < lag:  # part k of the units, behind this step
+                for j, L in enumerate(layers):
+                    n = L.cfg.c.batch * L.cfg.c.num_kv_heads
+                    u0, u1 = k * n // lag, (k + 1) * n // lag
+                    hk.hardkv_select_ahead(L.cfg, nxt[j], L.inp.q[q_fork], main, u0, u1 - u0)
+                done = "spread"
+            mark()
+        if done is not None and done != "spread":
+            main.wait_event(done)
+
+    setup()
+    run()
+    torch.cuda.synchronize()
+    g = None
+    if not eager:
+        setup()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            run()
+        torch.cuda.synchronize()
+    times = []
+    for _ in range(3):
+        setup()
+        torch.cuda.synchronize()
+        times.append(timed(g.replay if g is not None else run))
+    err = int(max(int(L.st.error_word[0].item()) for L in layers))
+    setup()
+    lat = step_latencies(run, len(steps))
+    restore()
+    torch.cuda.synchronize()
+    ms_step = float(np.mean(times)) / len(steps)
+    return {"R": R, "lag": lag, "mode": mode, "ms_per_step": ms_step, "steps_per_s": 1e3 / ms_step,
+            "error_word": err, "eager_step_latency": lat,
+            "timing": "graph of two periods of R steps, each selection made ahead on a second stream and "
+                      "switched in lag steps later"}
 
 
 def device_copy_reference(nbytes, reps=10):
@@ -589,6 +704,26 @@ def run_policies(args):
                 row[pol] = {"ms_per_step": ms, "steps_per_s": 1e3 / ms, "rewritten_heads": d["rewritten_heads"]}
             best_fixed = max(row["rewrite"]["steps_per_s"], row["sparse"]["steps_per_s"])
             row["controller_vs_best_fixed"] = row["mti-auto"]["steps_per_s"] / best_fixed
+            # Rewrite Cache with each selection made ahead: all of it on a second stream and
+            # switched in 2 steps later, or in R - 1 parts behind the steps before the switch
+            for mode, lag in (("side", 2), ("spread", R - 1)) if R > 1 else ():
+                cmd = [sys.executable, os.path.abspath(__file__), "--child", "--quick", "--config", key, "--steps",
+                       str(args.steps), "--warmup", str(args.warmup), "--no-cpu-baseline", "--extra-configs", "none",
+                       "--policy-configs", "none", "--select-every", str(R), "--pipeline", str(lag),
+                       "--pipeline-mode", mode]
+                r = subprocess.run(cmd, capture_output=True, text=True, timeout=300)
+                if r.returncode != 0:
+                    raise RuntimeError(f"bench pipeline child {key} R={R} failed ({r.returncode}):\n{r.stderr[-2000:]}")
+                d = json.loads(r.stdout.strip().splitlines()[-1])
+                pl = d["pipeline"]
+                row[f"rewrite_pipelined_{mode}"] = {
+                    "ms_per_step": pl["ms_per_step"], "steps_per_s": pl["steps_per_s"], "lag": pl["lag"],
+                    "eager_step_latency": pl["eager_step_latency"],
+                    "same_run_without": {"ms_per_step": d["select_every"]["ms_per_step"],
+                                         "eager_step_latency": d["select_every"]["eager_step_latency"]}}
+                print(f"bench: pipeline {key} R={R} {mode} lag {lag}: {pl['ms_per_step']:.4f} ms/step, max step "
+                      f"{pl['eager_step_latency']['max_ms']:.3f} ms (without: {d['select_every']['ms_per_step']:.4f}, "
+                      f"max {d['select_every']['eager_step_latency']['max_ms']:.3f})", file=sys.stderr, flush=True)
             print(f"bench: policies {key} R={R}: " + ", ".join(f"{p} {row[p]['ms_per_step']:.4f} ms"
                                                               for p in ("rewrite", "sparse", "mti-auto")),
                   file=sys.stderr, flush=True)
@@ -629,6 +764,8 @@ def main():
     restore_mode = wl.steps == 1
     K, Wm = args.steps, args.warmup
     nsteps = R if restore_mode else Wm + K
+    if args.pipeline:
+        nsteps = max(nsteps, (0 if restore_mode else Wm) + 1 + 2 * R)
 
     layers = []
     for layer in range(wl.layers):
@@ -734,6 +871,10 @@ def main():
             res["select_every"] = select_every(layers, R, restore_mode, snaps if restore_mode else snap_after, Wm, K,
                                                timed, args.eager)
             res["select_every"]["mti_horizon"] = horizon
+            if args.pipeline:
+                res["pipeline"] = pipeline_every(layers, R, args.pipeline, restore_mode,
+                                                 snaps if restore_mode else snap_after, Wm, timed, args.eager,
+                                                 args.pipeline_mode)
         print(json.dumps(res))
         return
 
@@ -801,6 +942,10 @@ def main():
         res["select_every"] = select_every(layers, R, restore_mode, snaps if restore_mode else snap_after, Wm, K,
                                            timed, args.eager)
         res["config"]["pool_blocks"] = wl.P_blk
+        if args.pipeline:
+            res["pipeline"] = pipeline_every(layers, R, args.pipeline, restore_mode,
+                                             snaps if restore_mode else snap_after, Wm, timed, args.eager,
+                                             args.pipeline_mode)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wl, layers, args.cpu_units, args.cpu_seconds)
     if extras:

@@ -541,12 +541,18 @@ int32_t hardkv_select_fork(const hardkv_config *cfg, hardkv_state *st_next, cons
   return hip_status(launch_fork(p.a, (hipStream_t)stream));
 }
 
-int32_t hardkv_select_ahead(const hardkv_config *cfg, hardkv_state *st_next, const void *q, void *stream) {
+int32_t hardkv_select_ahead(const hardkv_config *cfg, hardkv_state *st_next, const void *q, int32_t unit_begin,
+                            int32_t unit_count, void *stream) {
   Plan p;
   int32_t rc = setup(cfg, st_next, p);
   if (rc != HARDKV_OK) return rc;
   if (p.a.view_sum) return HARDKV_EUNSUPPORTED;
   if (!aligned16(q)) return HARDKV_EINVAL;
+  if (unit_begin < 0 || unit_count < 0 || (int64_t)unit_begin + unit_count > (int64_t)p.a.B * p.a.Hkv)
+    return HARDKV_EINVAL;
+  if (unit_count == 0) return HARDKV_OK;
+  p.a.bh0 = unit_begin;  // every kernel below covers units [bh0, bh0 + nbh)
+  p.a.nbh = unit_count;
   p.a.q = q;
   p.a.seq_len = p.a.tsnap;  // the pool as it stood at the forked step
   p.a.gather_mode = GATHER_REWRITE;

@@ -98,7 +98,7 @@ def lib() -> C.CDLL:
         L.hardkv_step_num_stages.argtypes = []
         L.hardkv_mti_thresholds.argtypes = [cp, i64, C.POINTER(i32), C.POINTER(i32)]
         L.hardkv_select_fork.argtypes = [cp, sp, sp, vp]
-        L.hardkv_select_ahead.argtypes = [cp, sp, vp, vp]
+        L.hardkv_select_ahead.argtypes = [cp, sp, vp, i32, i32, vp]
         L.hardkv_mti_period.argtypes = [cp, i64, i64, i64, i32, C.POINTER(i32)]
         L.hardkv_step_stage_name.argtypes = [i32]
         L.hardkv_step_stage_name.restype = C.c_char_p
@@ -334,9 +334,11 @@ def hardkv_select_fork(cfg: Config, st_next: State, st_cur: State, stream=None) 
                                                           _stream(stream)))
 
 
-def hardkv_select_ahead(cfg: Config, st_next: State, q, stream=None) -> None:
+def hardkv_select_ahead(cfg: Config, st_next: State, q, stream=None, unit_begin: int = 0,
+                        unit_count: Optional[int] = None) -> None:
+    n = cfg.c.batch * cfg.c.num_kv_heads if unit_count is None else int(unit_count)
     _check("hardkv_select_ahead", lib().hardkv_select_ahead(C.byref(cfg.c), C.byref(st_next.c), _ptr(q),
-                                                            _stream(stream)))
+                                                            int(unit_begin), n, _stream(stream)))
 
 
 def hardkv_step_num_stages() -> int:

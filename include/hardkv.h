@@ -340,11 +340,15 @@ int32_t hardkv_step_noalloc(const hardkv_config *cfg, hardkv_state *st, const vo
  *   1. hardkv_select_fork(cfg, st_next, st_cur, s_main): on the main stream, right after the
  *      append of the step the selection is made for: records t of every sequence and the
  *      current state's key-magnitude record in st_next's workspace.
- *   2. hardkv_select_ahead(cfg, st_next, q, s_side): on a second stream, after an event the
- *      caller records on s_main behind the fork: score, calibrate, top-p and Rewrite Cache
- *      (the views of the heads the policy rewrites) over the pool as it stood at the forked
- *      step, with that step's queries q; the planned condensation is not applied.  The
- *      max-length view layout only (HARDKV_EUNSUPPORTED for SUM).
+ *   2. hardkv_select_ahead(cfg, st_next, q, unit_begin, unit_count, stream): score, calibrate,
+ *      top-p and Rewrite Cache (the views of the heads the policy rewrites) of units
+ *      [unit_begin, unit_begin + unit_count) (unit b * Hkv + h) over the pool as it stood at
+ *      the forked step, with that step's queries q (kept alive by the caller until the last
+ *      part has run); the planned condensation is not applied.  Either all units at once on
+ *      a second stream, after an event the caller records on s_main behind the fork, or in
+ *      parts spread over the steps before the switch on any stream ordered after the fork.
+ *      HARDKV_EINVAL for a range outside [0, B * Hkv]; the max-length view layout only
+ *      (HARDKV_EUNSUPPORTED for SUM).
  *   3. Meanwhile s_main may take hardkv_step_reuse steps on st_cur (no selection, no
  *      condensation): they append and attend the current selection.  The pool ring must
  *      hold S_cap plus the positions of the steps until the switch.
@@ -356,7 +360,8 @@ int32_t hardkv_step_noalloc(const hardkv_config *cfg, hardkv_state *st, const vo
  * the step's own: the same masks, budgets, views and condensed tier as hardkv_step. */
 int32_t hardkv_select_fork(const hardkv_config *cfg, hardkv_state *st_next, const hardkv_state *st_cur,
                            void *stream);
-int32_t hardkv_select_ahead(const hardkv_config *cfg, hardkv_state *st_next, const void *q, void *stream);
+int32_t hardkv_select_ahead(const hardkv_config *cfg, hardkv_state *st_next, const void *q, int32_t unit_begin,
+                            int32_t unit_count, void *stream);
 
 /* Launches only kernel `stage` of hardkv_step (0 append, 1 score, 2 select, 3 condense,
  * 4 rewrite with the view, condensed and dense attention, 5 combine), for timing one

@@ -250,7 +250,11 @@ def test_pipeline_pair_validation():
     assert L.hardkv_select_fork(C.byref(cfg.c), C.byref(nxt), C.byref(cur), None) == hk.HARDKV_EINVAL
     ok = C.c_void_p(1 << 41)
     bad = C.c_void_p((1 << 41) + 8)
-    assert L.hardkv_select_ahead(C.byref(cfg.c), C.byref(nxt), bad, None) == hk.HARDKV_EINVAL
+    units = cfg.c.batch * cfg.c.num_kv_heads
+    assert L.hardkv_select_ahead(C.byref(cfg.c), C.byref(nxt), bad, 0, units, None) == hk.HARDKV_EINVAL
+    assert L.hardkv_select_ahead(C.byref(cfg.c), C.byref(nxt), ok, 1, units, None) == hk.HARDKV_EINVAL
+    assert L.hardkv_select_ahead(C.byref(cfg.c), C.byref(nxt), ok, -1, 1, None) == hk.HARDKV_EINVAL
+    assert L.hardkv_select_ahead(C.byref(cfg.c), C.byref(nxt), ok, units, 0, None) == hk.HARDKV_OK  # nothing
     packed = _cfg(view_layout=1, view_total=100)
     st = _fake_state(packed)
-    assert L.hardkv_select_ahead(C.byref(packed.c), C.byref(st), ok, None) == hk.HARDKV_EUNSUPPORTED
+    assert L.hardkv_select_ahead(C.byref(packed.c), C.byref(st), ok, 0, 1, None) == hk.HARDKV_EUNSUPPORTED

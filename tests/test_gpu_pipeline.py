@@ -40,6 +40,10 @@ def _check_selection(g, o, wl, tag):
             assert np.array_equal(vv[b, h, :k], o.view_v[b, h, :k]), f"{tag} view_v {b} {h}"
 
 
+def _part(p):
+    return p[0], p[1] - p[0]
+
+
 def _check_cache(g, o, tag):
     from parity import COND_TOL, row_rel_err
     for n in ("pool_head", "cond_cursor", "cond_n", "seq_len"):
@@ -61,6 +65,9 @@ PIPE_CASES = {
     "g8_lag2": (dict(num_q_heads=16, num_kv_heads=2, cond_mode=COND_MERGE), 2),
     "sparse_policy_lag2": (dict(cond_mode=COND_MERGE, ctx_len=500, ctx_min=300, regularize=1), 2),
     "batch16_lag1": (dict(batch=16, cond_mode=COND_MERGE, ctx_len=600, ctx_min=100), 1),
+    # the selection made ahead in parts, one after each step before the switch, on the main stream
+    "batch16_spread3": (dict(batch=16, cond_mode=COND_MERGE, ctx_len=600, ctx_min=100), -3),
+    "mixed_spread2": (dict(batch=5, num_q_heads=12, num_kv_heads=3, cond_mode=COND_EVICT), -2),
 }
 
 
@@ -69,6 +76,8 @@ def test_pipeline_parity(name):
     from decode_kv_cache_02_amd import hardkv as hk
     from parity import Pair
     kw, lag = PIPE_CASES[name]
+    spread = lag < 0  # the selection in parts on the main stream, one after each step before the switch
+    lag = abs(lag)
     kw = dict(kw)
     reg = kw.pop("regularize", 0)
     steps = 2 + 2 * (lag + 2)
@@ -85,21 +94,31 @@ def test_pipeline_parity(name):
         st_next = pr.st.twin()
         pr.step_reuse()
         hk.hardkv_select_fork(pr.cfg, st_next, pr.st, main)
-        forked = torch.cuda.Event()
-        forked.record(main)
-        with torch.cuda.stream(side):
-            side.wait_event(forked)
-            hk.hardkv_select_ahead(pr.cfg, st_next, pr.inp.q[s], side)
-            done = torch.cuda.Event()
-            done.record(side)
+        q_fork = pr.inp.q[s]
+        units = wl.batch * wl.num_kv_heads
+        parts = [(i * units // lag, (i + 1) * units // lag) for i in range(lag)]
+        if spread:
+            done = None
+            hk.hardkv_select_ahead(pr.cfg, st_next, q_fork, main, *_part(parts[0]))
+        else:
+            forked = torch.cuda.Event()
+            forked.record(main)
+            with torch.cuda.stream(side):
+                side.wait_event(forked)
+                hk.hardkv_select_ahead(pr.cfg, st_next, q_fork, side)
+                done = torch.cuda.Event()
+                done.record(side)
         o_next = o_cur.twin()
         o_next.select_ahead(cpu.q[s], o_cur.seq_len)
         s += 1
-        for _ in range(lag - 1):  # steps on the current selection while the side stream works
+        for i in range(lag - 1):  # steps on the current selection while the selection is made
             pr.step_reuse()
+            if spread:
+                hk.hardkv_select_ahead(pr.cfg, st_next, q_fork, main, *_part(parts[i + 1]))
             s += 1
         # the switch
-        main.wait_event(done)
+        if done is not None:
+            main.wait_event(done)
         torch.cuda.synchronize()
         _check_selection(st_next, o_next, wl, f"{name} round {rnd} ahead")
         hk.hardkv_condense(pr.cfg, st_next, main)

@@ -339,8 +339,8 @@ HK_DEV void attend_segment(const Args &a, int bh, int seg, float (*s_part)[G][2 
     const int xt = seg - a.nv_att - a.nc_att - a.nd_att - a.ns_att;
     slot = a.part_cd_base + a.nc_att + a.nd_att + a.ns_att + xt;
     const int64_t lo = pool_end(a.head[bh].t_plan, a.W, a.S), hi = pool_end(t, a.W, a.S);
-    const char *pk = (const char *)a.pool_k + (size_t)bh * a.P * BK * ROWB + sub * 8 * EB;
-    const char *pv = (const char *)a.pool_v + (size_t)bh * a.P * BK * ROWB + sub * 8 * EB;
+    const char *pk = (const char *)a.pool_k + sub * 8 * EB;
+    const char *pv = (const char *)a.pool_v + sub * 8 * EB;
     for (int64_t q0 = lo + (int64_t)xt * a.rt_att; q0 < hi; q0 += (int64_t)a.nt_att * a.rt_att) {
       const int64_t q1 = min(q0 + (int64_t)a.rt_att, hi);
       for (int64_t base = q0; base < q1; base += 32) {
@@ -351,7 +351,7 @@ HK_DEV void attend_segment(const Args &a, int bh, int seg, float (*s_part)[G][2 
           const int64_t p = base + j * 16 + rloc;
           act[j] = p < q1;
           if (act[j]) {
-            const size_t row = (size_t)((p / BK) % a.P) * BK + (size_t)(p % BK);
+            const size_t row = pool_row0(a, bh, (int)((p / BK) % a.P)) + (size_t)(p % BK);
             raw_load_nt(pk + row * ROWB, kr[j]);
             raw_load_nt(pv + row * ROWB, vr[j]);
           } else {

@@ -37,8 +37,9 @@ HK_DEV void condense_chain(const Args &a, int bh, int i, int64_t c, int64_t E, i
   for (int64_t e = i; e < E; e += C) {
     ++nblk;
     const size_t pb = (size_t)((c / BK + e) % P);
-    const char *kb = (const char *)a.pool_k + ((size_t)bh * P + pb) * BK * ROWB + sub * 8 * EB;
-    const char *vb = (const char *)a.pool_v + ((size_t)bh * P + pb) * BK * ROWB + sub * 8 * EB;
+    const size_t row0 = pool_row0(a, bh, (int)pb);
+    const char *kb = (const char *)a.pool_k + row0 * ROWB + sub * 8 * EB;
+    const char *vb = (const char *)a.pool_v + row0 * ROWB + sub * 8 * EB;
     const uint32_t wl = a.weights[((size_t)bh * P + pb) * BK + lane];  // weight of row `lane`
     wsum += wl;
     constexpr int UNB = LEAN ? 1 : 16 / NB;
@@ -106,9 +107,26 @@ HK_DEV void condense_chain(const Args &a, int bh, int i, int64_t c, int64_t E, i
 }
 
 // After the slots: the cursor (MERGE) and the pool head move past the E condensed blocks.
+// In the shared pool the condensed blocks go back to the free list (their table entries
+// stay: nothing reads a ring block outside the pool, and the append that reuses the ring
+// block sets it again).
 HK_DEV void condense_advance(const Args &a, int bh, int64_t c, int64_t E, int32_t nu) {
   if (a.mode == HARDKV_COND_MERGE) a.cond_cursor[bh] = (int32_t)((nu + E) % a.C);
   a.pool_head[bh] = c + (int64_t)BK * E;
+  if (a.pool_shared && E > 0) {
+    // (a block the pool never got, after an overflow, has no entry to return)
+    const int32_t *tb = a.btab + (size_t)bh * a.P;
+    int32_t n = 0;
+    for (int64_t e = 0; e < E; ++e) n += tb[(c / BK + e) % a.P] >= 0 ? 1 : 0;
+    const int32_t at = atomicAdd(a.free_top, n);
+    int32_t k = 0;
+    for (int64_t e = 0; e < E; ++e) {
+      const int32_t ph = tb[(c / BK + e) % a.P];
+      if (ph < 0) continue;
+      if (at + k < a.NB) a.free_list[at + k] = ph;
+      ++k;
+    }
+  }
 }
 
 }  // namespace hardkv

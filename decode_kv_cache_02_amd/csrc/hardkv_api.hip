@@ -116,6 +116,9 @@ int32_t plan(const hardkv_config *cfg, Plan &p) {
   if (cfg->view_layout == HARDKV_VIEW_SUM && cfg->view_total < 0) return HARDKV_EINVAL;
   if (cfg->calibration != HARDKV_CAL_FIXED && cfg->calibration != HARDKV_CAL_ENTROPY) return HARDKV_EINVAL;
   if (cfg->sink < 0 || cfg->sink % BK || cfg->sink > HARDKV_MAX_SINK) return HARDKV_EINVAL;
+  if (cfg->pool_layout != HARDKV_POOL_RING && cfg->pool_layout != HARDKV_POOL_SHARED) return HARDKV_EINVAL;
+  if (cfg->pool_layout == HARDKV_POOL_SHARED && (cfg->pool_total_blocks < 1 || cfg->pool_total_blocks >= (1 << 26)))
+    return HARDKV_EINVAL;
 
   a.B = cfg->batch;
   a.Hq = cfg->num_q_heads;
@@ -133,6 +136,8 @@ int32_t plan(const hardkv_config *cfg, Plan &p) {
   a.calibration = cfg->calibration;
   a.view_rows = a.view_sum ? (int64_t)cfg->view_total
                            : (int64_t)cfg->batch * cfg->num_kv_heads * cfg->view_cap;
+  a.pool_shared = cfg->pool_layout == HARDKV_POOL_SHARED ? 1 : 0;
+  a.NB = a.pool_shared ? cfg->pool_total_blocks : 0;
   a.reg_policy = cfg->regularize;
   a.reg_launch = launch_policy(cfg);
   a.mti_lower = cfg->mti_lower;
@@ -235,6 +240,14 @@ int32_t bind(const hardkv_state *st, Plan &p) {
   if (!st->error_word || ((uintptr_t)st->error_word & 3u)) return HARDKV_EINVAL;
   if (st->workspace_bytes < p.ws_bytes) return HARDKV_ECAPACITY;
   Args &a = p.a;
+  if (a.pool_shared) {
+    if (!aligned16(st->block_table) || !aligned16(st->free_list) || !st->free_top ||
+        ((uintptr_t)st->free_top & 3u))
+      return HARDKV_EINVAL;
+    a.btab = st->block_table;
+    a.free_list = st->free_list;
+    a.free_top = st->free_top;
+  }
   a.dense_k = st->dense_k;
   a.dense_v = st->dense_v;
   a.pool_k = st->pool_k;
@@ -514,7 +527,9 @@ int32_t check_pipeline_pair(const hardkv_state *nx, const hardkv_state *cur) {
                              {nx->pool_v, cur->pool_v}, {nx->cond_kn, cur->cond_kn}, {nx->cond_vn, cur->cond_vn},
                              {nx->cond_omega, cur->cond_omega}, {nx->cond_n, cur->cond_n},
                              {nx->cond_cursor, cur->cond_cursor}, {nx->seq_len, cur->seq_len},
-                             {nx->pool_head, cur->pool_head}, {nx->sink_k, cur->sink_k}, {nx->sink_v, cur->sink_v}};
+                             {nx->pool_head, cur->pool_head}, {nx->sink_k, cur->sink_k}, {nx->sink_v, cur->sink_v},
+                             {nx->block_table, cur->block_table}, {nx->free_list, cur->free_list},
+                             {nx->free_top, cur->free_top}};
   for (auto &pr : shared)
     if (pr[0] != pr[1]) return HARDKV_EINVAL;
   const void *own[][2] = {{nx->view_k, cur->view_k}, {nx->view_v, cur->view_v}, {nx->view_pos, cur->view_pos},
@@ -601,6 +616,24 @@ int32_t hardkv_mti_thresholds(const hardkv_config *cfg, int64_t n_survivors, int
     }
   *l_lower = lo;
   *l_upper = hi;
+  return HARDKV_OK;
+}
+
+int32_t hardkv_shared_pool_blocks(const hardkv_config *cfg, const int64_t *ctx_len, int64_t steps,
+                                  int64_t *blocks) {
+  Plan p;
+  if (!cfg || !ctx_len || !blocks || steps < 0) return HARDKV_EINVAL;
+  const int32_t rc = plan(cfg, p);
+  if (rc != HARDKV_OK) return rc;
+  int64_t total = 0;
+  for (int b = 0; b < cfg->batch; ++b) {
+    if (ctx_len[b] < 0 || ctx_len[b] > ((int64_t)1 << 40)) return HARDKV_EINVAL;
+    const int64_t t = ctx_len[b] + steps;
+    const int64_t pend = t - cfg->dense_window > cfg->sink ? t - cfg->dense_window : (int64_t)cfg->sink;
+    const int64_t need = pend > cfg->sink ? (pend + BK - 1) / BK - cfg->sink / BK : 0;
+    total += std::min<int64_t>(need, cfg->pool_blocks) * cfg->num_kv_heads;
+  }
+  *blocks = total;
   return HARDKV_OK;
 }
 

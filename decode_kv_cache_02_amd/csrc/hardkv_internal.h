@@ -103,6 +103,11 @@ struct Args {
                       // pool (since its prefill): its scores then take the unfused products
   int kx_unknown;     // 1: kx is not kept for this state (the no-alloc step): every head's
                       // scores take the unfused products
+  // the shared head-wise block pool (pool_shared): pool_k / pool_v hold NB physical blocks of
+  // 64 rows; btab maps ring block pb of unit bh to its physical block (-1: none); the free
+  // blocks are free_list[0 .. *free_top)
+  int pool_shared, NB;
+  int32_t *btab, *free_list, *free_top;
   int64_t *tsnap;     // [B] t of the step a selection made ahead is for (the pipeline)
   const uint32_t *kx_src;  // the current state's kx, copied by the pipeline's fork
   // prefill
@@ -352,6 +357,16 @@ HK_DEV int64_t dense_lo_of(int64_t t, int W, int S) {
   const int64_t lo = pool_end(t, W, S);
   return lo < t ? lo : t;
 }
+// Row 0 of ring block pb of unit bh in the pool arrays: the unit's own ring, or the physical
+// block the block table gives it in the shared pool.
+HK_DEV size_t pool_row0(const Args &a, int bh, int pb) {
+  if (a.pool_shared) {
+    const int32_t phys = a.btab[(size_t)bh * a.P + pb];
+    return (size_t)(phys < 0 ? 0 : phys) * BK;
+  }
+  return ((size_t)bh * a.P + pb) * BK;
+}
+
 HK_DEV int64_t plan_E(int64_t N, int mode, int S_cap) {
   return (mode != HARDKV_COND_OFF && N > S_cap) ? (N - S_cap + BK - 1) / BK : 0;
 }

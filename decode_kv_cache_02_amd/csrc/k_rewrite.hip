@@ -20,6 +20,8 @@
 // In the fused step the kernel also runs the attention of the group's queries over the
 // rows it copies (one split-K partial per workgroup, so the view is never read back),
 // and extra workgroups attend the condensed slots and the dense window.
+#include <type_traits>
+
 #include "attn_common.h"
 
 namespace hardkv {
@@ -32,7 +34,9 @@ constexpr int PIPE_MIN_ROWS = 32;
 
 // STORE: whether the launch can write views at all (not under SPARSE, nor for the
 // attention-only gathers): without it the kernel keeps no registers for stores.
-template <typename T, int G, bool MASK, bool COPY, bool ATTN, bool STORE>
+// SHARED: the shared block pool (kept rows anywhere in it, loaded through flat addresses of
+// their physical rows), else the unit's own ring (one buffer resource).
+template <typename T, int G, bool MASK, bool COPY, bool ATTN, bool STORE, bool SHARED>
 __global__ __launch_bounds__(NTHREADS) void hardkv_rewrite(Args a) {
   constexpr int EB = Elem<T>::bytes;
   constexpr size_t ROWB = (size_t)HD * EB;
@@ -100,8 +104,8 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_rewrite(Args a) {
   }
   const size_t rowbase = (size_t)bh * P * BK;
   const uint64_t poolb = (uint64_t)P * BK * ROWB;
-  const BufRes pk = make_buf((const char *)a.pool_k + rowbase * ROWB, poolb);
-  const BufRes pv = make_buf((const char *)a.pool_v + rowbase * ROWB, poolb);
+  const BufRes pk = make_buf((const char *)a.pool_k + (SHARED ? 0 : rowbase * ROWB), poolb);
+  const BufRes pv = make_buf((const char *)a.pool_v + (SHARED ? 0 : rowbase * ROWB), poolb);
   // the head's view rows start at voff (bh * V_cap, or its packed offset); vcap rows fit,
   // and the view buffers end there, so a row past them is not written
   const int64_t voff = hd->voff;
@@ -116,6 +120,7 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_rewrite(Args a) {
   const int iw = i0 + wave * bpw;
   uint32_t wv[4];
   uint2 bi[4];
+  int32_t ph[4];  // physical blocks (shared pool)
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int i = iw + j;
@@ -123,6 +128,7 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_rewrite(Args a) {
     const int64_t p = c + (int64_t)i * BK + lane;
     wv[j] = (live && p < pend) ? a.weights[rowbase + (size_t)ring(i) * BK + lane] : 0u;
     bi[j] = live ? a.blkinfo[(size_t)bh * P + ring(i)] : make_uint2(0u, 0u);
+    ph[j] = (SHARED && live) ? a.btab[(size_t)bh * P + ring(i)] : 0;
   }
   // mask words, and the list of kept rows in position order
   int ns = 0;
@@ -141,7 +147,7 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_rewrite(Args a) {
     if (!COPY || mw == 0) continue;  // wave-uniform
     const uint32_t vo = bi[j].x, idx = popc_below(mw);
     if (sel) {
-      s_src[wave][ns + idx] = (uint32_t)(pb * BK + lane);
+      s_src[wave][ns + idx] = SHARED ? (uint32_t)(max(ph[j], 0) * BK + lane) : (uint32_t)(pb * BK + lane);
       s_dst[wave][ns + idx] = vo + idx;
       if (store && vo + idx < vcap) vpos[vo + idx] = (int32_t)p;
     }
@@ -157,9 +163,14 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_rewrite(Args a) {
     // loads and stores completes in order).  Rows past the list read zeros and write
     // nothing (offset BUF_SKIP), and so does every store when the view is not written;
     // rows past the view's capacity are attended but fall outside the view buffers.
-    uint32_t so[4], dof[4];
+    // source offsets: 32-bit into the unit's ring (BUF_SKIP for rows past the list), or, in
+    // the shared pool, 64-bit byte offsets of physical rows (rows past the list read a listed
+    // row, which nothing uses)
+    using SOff = typename std::conditional<SHARED, size_t, uint32_t>::type;
+    SOff so[4];
+    uint32_t dof[4];
     bool ac[4];
-    auto offsets = [&](int it, uint32_t (&o_s)[4], uint32_t (&o_d)[4], bool (&o_a)[4]) {
+    auto offsets = [&](int it, SOff (&o_s)[4], uint32_t (&o_d)[4], bool (&o_a)[4]) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int k = it + j * 4 + grp;
@@ -169,9 +180,24 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_rewrite(Args a) {
         // memory accesses that follow
         uint32_t sv = s_src[wave][kk], dv = s_dst[wave][kk];
         asm volatile("" : "+v"(sv), "+v"(dv));
-        o_s[j] = o_a[j] ? sv * (uint32_t)ROWB + lane_b : BUF_SKIP;
+        if constexpr (SHARED)
+          o_s[j] = (size_t)sv * ROWB + lane_b;
+        else
+          o_s[j] = o_a[j] ? sv * (uint32_t)ROWB + lane_b : BUF_SKIP;
         o_d[j] = (o_a[j] && store) ? dv * (uint32_t)ROWB + lane_b : BUF_SKIP;
       }
+    };
+    auto ldk = [&](SOff o, Raw8<T> &r) {
+      if constexpr (SHARED)
+        raw_load_nt((const char *)a.pool_k + o, r);
+      else
+        buf_load_nt(pk, o, r);
+    };
+    auto ldv = [&](SOff o, Raw8<T> &r) {
+      if constexpr (SHARED)
+        raw_load_nt((const char *)a.pool_v + o, r);
+      else
+        buf_load_nt(pv, o, r);
     };
     Raw8<T> kr[4], vr[4];
     // The pipeline holds the next batch's keys beside this batch's probabilities: with
@@ -184,8 +210,8 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_rewrite(Args a) {
         offsets(it, so, dof, ac);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          buf_load_nt(pk, so[j], kr[j]);
-          buf_load_nt(pv, so[j], vr[j]);
+          ldk(so[j], kr[j]);
+          ldv(so[j], vr[j]);
         }
         if constexpr (STORE) {
 #pragma unroll
@@ -201,7 +227,7 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_rewrite(Args a) {
       // in which the loads and stores were issued)
       offsets(0, so, dof, ac);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) buf_load_nt(pk, so[j], kr[j]);
+      for (int j = 0; j < 4; ++j) ldk(so[j], kr[j]);
       __builtin_amdgcn_sched_barrier(0);
       {
         // stores that write nothing, so that the first batch's loads are followed by as
@@ -212,7 +238,7 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_rewrite(Args a) {
       }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) buf_load_nt(pv, so[j], vr[j]);
+      for (int j = 0; j < 4; ++j) ldv(so[j], vr[j]);
       __builtin_amdgcn_sched_barrier(0);
       // every batch but the last loads its successor; the last only stores and attends
       int it = 0;
@@ -223,11 +249,12 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_rewrite(Args a) {
         for (int j = 0; j < 4; ++j) buf_store_nt(vk, dof[j], kr[j]);
         __builtin_amdgcn_sched_barrier(0);
         {
-          uint32_t so2[4], dof2[4];
+          SOff so2[4];
+          uint32_t dof2[4];
           bool ac2[4];
           offsets(it + 16, so2, dof2, ac2);
 #pragma unroll
-          for (int j = 0; j < 4; ++j) buf_load_nt(pk, so2[j], kr[j]);
+          for (int j = 0; j < 4; ++j) ldk(so2[j], kr[j]);
         }
         __builtin_amdgcn_sched_barrier(0);
         if (ATTN) attn_values<T, G, 4>(st, p, vr);
@@ -236,7 +263,7 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_rewrite(Args a) {
         __builtin_amdgcn_sched_barrier(0);
         offsets(it + 16, so, dof, ac);  // read again rather than held through the values
 #pragma unroll
-        for (int j = 0; j < 4; ++j) buf_load_nt(pv, so[j], vr[j]);
+        for (int j = 0; j < 4; ++j) ldv(so[j], vr[j]);
         __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll
@@ -249,17 +276,23 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_rewrite(Args a) {
   if (ATTN) attn_write_partial<G>(st, a.part + ((size_t)bh * a.npart + pslot) * G * (2 + HD), s_part);
 }
 
-template <typename T, bool MASK, bool COPY, bool ATTN, bool STORE>
-hipError_t launch_g(const Args &a, hipStream_t s) {
+template <typename T, bool MASK, bool COPY, bool ATTN, bool STORE, bool SHARED>
+hipError_t launch_gs(const Args &a, hipStream_t s) {
   dim3 grid(a.nch_reg + (ATTN && a.gather_mode == GATHER_STEP ? a.nc_att + a.nd_att + a.ns_att : 0), a.nbh);
   switch (a.G) {
-    case 1: hipLaunchKernelGGL((hardkv_rewrite<T, 1, MASK, COPY, ATTN, STORE>), grid, dim3(NTHREADS), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((hardkv_rewrite<T, 2, MASK, COPY, ATTN, STORE>), grid, dim3(NTHREADS), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((hardkv_rewrite<T, 4, MASK, COPY, ATTN, STORE>), grid, dim3(NTHREADS), 0, s, a); break;
-    case 8: hipLaunchKernelGGL((hardkv_rewrite<T, 8, MASK, COPY, ATTN, STORE>), grid, dim3(NTHREADS), 0, s, a); break;
+    case 1: hipLaunchKernelGGL((hardkv_rewrite<T, 1, MASK, COPY, ATTN, STORE, SHARED>), grid, dim3(NTHREADS), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((hardkv_rewrite<T, 2, MASK, COPY, ATTN, STORE, SHARED>), grid, dim3(NTHREADS), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((hardkv_rewrite<T, 4, MASK, COPY, ATTN, STORE, SHARED>), grid, dim3(NTHREADS), 0, s, a); break;
+    case 8: hipLaunchKernelGGL((hardkv_rewrite<T, 8, MASK, COPY, ATTN, STORE, SHARED>), grid, dim3(NTHREADS), 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+template <typename T, bool MASK, bool COPY, bool ATTN, bool STORE>
+hipError_t launch_g(const Args &a, hipStream_t s) {
+  return a.pool_shared ? launch_gs<T, MASK, COPY, ATTN, STORE, true>(a, s)
+                       : launch_gs<T, MASK, COPY, ATTN, STORE, false>(a, s);
 }
 
 template <typename T>

@@ -121,7 +121,9 @@ HK_DEV void ent_add(float &m, float &z, float &w, float x) {
   m = up ? x : m;
 }
 
-template <typename T, int G, bool ENT>
+// SHARED: the pool is the shared block pool (rows of a chunk's blocks anywhere in it, loaded
+// through flat addresses from the block table), else the unit's own ring (one buffer resource).
+template <typename T, int G, bool ENT, bool SHARED>
 __global__ __launch_bounds__(NTHREADS) void hardkv_score(Args a) {
   constexpr int EB = Elem<T>::bytes;
   const int lin = xcd_swizzle(blockIdx.y * gridDim.x + blockIdx.x, gridDim.x * gridDim.y);
@@ -134,6 +136,7 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_score(Args a) {
   const int P = a.P;
 
   __shared__ float s_sc[8 * BK];  // the chunk's scores (at most 8 blocks), stored at the end
+  __shared__ int32_t s_phys[8];   // the chunk's physical blocks (shared pool)
   __shared__ float s_wmax[4];
   __shared__ float s_ent[ENT ? 4 : 1][G][3];
   // entropy calibration: lane `sub` < G keeps query sub's softmax piece over its rows
@@ -171,7 +174,8 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_score(Args a) {
           CAN_FUSE && a.kx_unknown == 0 &&
           __builtin_amdgcn_readfirstlane((int)(a.kx[bh] == 0u && ballot(!q_ok) == 0ull)) != 0;
     };
-    const BufRes kb = make_buf((const char *)a.pool_k + (size_t)bh * P * BK * HD * EB, (uint64_t)P * BK * HD * EB);
+    const BufRes kb = make_buf((const char *)a.pool_k + (SHARED ? 0 : (size_t)bh * P * BK * HD * EB),
+                               (uint64_t)P * BK * HD * EB);
     const uint32_t lane_b = (uint32_t)(sub * 8 * EB);  // the lane's 8 elements of a row
     float *srow = a.scores + (size_t)bh * P * BK;
     // row_lo is block aligned and the chunk spans fewer than P blocks, so one
@@ -179,6 +183,16 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_score(Args a) {
     const int pb0 = (int)((row_lo / BK) % P);
     const int nrows = (int)(row_hi - row_lo);
     const int ngroups = (nrows + 15) / 16;
+    const int nblk_c = (nrows + BK - 1) / BK;  // blocks of the chunk
+    if constexpr (SHARED) {
+      if (tid < nblk_c) {
+        int pb = pb0 + tid;
+        pb = pb >= P ? pb - P : pb;
+        const int32_t ph = a.btab[(size_t)bh * P + pb];
+        s_phys[tid] = ph < 0 ? 0 : ph;
+      }
+      __syncthreads();
+    }
     // Each wavefront takes row groups wave, wave + 4, ...; a batch is UNR of them
     // (UNR * 4 loads of 1 KB).  Two batches live in registers: the next batch's loads are
     // in flight while the current one is scored.
@@ -191,10 +205,18 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_score(Args a) {
 #pragma unroll
         for (int l = 0; l < 4; ++l) {
           const int rel = gi * 16 + l * 4 + grp;
-          // rows past the chunk read zeros (offset BUF_SKIP), with no branch
-          const uint32_t row_b = (uint32_t)(pb * BK + (rel & (BK - 1))) * (uint32_t)(HD * EB) + lane_b;
-          const uint32_t off = ((gi < ngroups) & (rel < nrows)) ? row_b : BUF_SKIP;
-          buf_load_nt(kb, off, buf[u][l]);
+          if constexpr (SHARED) {
+            // a row of one of the chunk's blocks (rows past the chunk read a row of its last
+            // block and are not kept)
+            const int bi = min(gi >> 2, nblk_c - 1);
+            const size_t row = (size_t)s_phys[bi] * BK + (size_t)(rel & (BK - 1));
+            raw_load_nt((const char *)a.pool_k + row * (HD * EB) + lane_b, buf[u][l]);
+          } else {
+            // rows past the chunk read zeros (offset BUF_SKIP), with no branch
+            const uint32_t row_b = (uint32_t)(pb * BK + (rel & (BK - 1))) * (uint32_t)(HD * EB) + lane_b;
+            const uint32_t off = ((gi < ngroups) & (rel < nrows)) ? row_b : BUF_SKIP;
+            buf_load_nt(kb, off, buf[u][l]);
+          }
         }
       }
     };
@@ -1356,14 +1378,14 @@ __global__ __launch_bounds__(FIT_THREADS) void hardkv_fit_final(Args a) {
   fit_store(a, bh, N, lo, hi);
 }
 
-template <typename T, bool ENT>
+template <typename T, bool ENT, bool SHARED>
 hipError_t launch_score_ge(const Args &a, hipStream_t s) {
   dim3 grid(a.nch_score, a.nbh);
   switch (a.G) {
-    case 1: hipLaunchKernelGGL((hardkv_score<T, 1, ENT>), grid, dim3(NTHREADS), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((hardkv_score<T, 2, ENT>), grid, dim3(NTHREADS), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((hardkv_score<T, 4, ENT>), grid, dim3(NTHREADS), 0, s, a); break;
-    case 8: hipLaunchKernelGGL((hardkv_score<T, 8, ENT>), grid, dim3(NTHREADS), 0, s, a); break;
+    case 1: hipLaunchKernelGGL((hardkv_score<T, 1, ENT, SHARED>), grid, dim3(NTHREADS), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((hardkv_score<T, 2, ENT, SHARED>), grid, dim3(NTHREADS), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((hardkv_score<T, 4, ENT, SHARED>), grid, dim3(NTHREADS), 0, s, a); break;
+    case 8: hipLaunchKernelGGL((hardkv_score<T, 8, ENT, SHARED>), grid, dim3(NTHREADS), 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -1371,7 +1393,9 @@ hipError_t launch_score_ge(const Args &a, hipStream_t s) {
 
 template <typename T>
 hipError_t launch_score_g(const Args &a, hipStream_t s) {
-  return a.calibration ? launch_score_ge<T, true>(a, s) : launch_score_ge<T, false>(a, s);
+  if (a.pool_shared)
+    return a.calibration ? launch_score_ge<T, true, true>(a, s) : launch_score_ge<T, false, true>(a, s);
+  return a.calibration ? launch_score_ge<T, true, false>(a, s) : launch_score_ge<T, false, false>(a, s);
 }
 
 }  // namespace

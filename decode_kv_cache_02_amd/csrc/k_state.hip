@@ -20,6 +20,59 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_prefill_clear(Args a) {
   if (i < a.B * a.Hkv) a.kx[i] = 0u;
 }
 
+// grid 1 (the shared pool only): every unit gets, in unit order, the physical blocks its pool
+// [S, max(S, L_b - W)) holds, ring block S / 64 + i -> physical block base_u + i; the table's
+// other entries are -1 and the blocks left over form the free list.  A unit whose blocks do
+// not fit gets none past the end (its rows are not placed) and the overflow bit is set.
+__global__ __launch_bounds__(NTHREADS) void hardkv_prefill_alloc(Args a) {
+  __shared__ int64_t s_need[NTHREADS];
+  __shared__ int64_t s_carry;
+  const int tid = threadIdx.x, BH = a.B * a.Hkv, P = a.P;
+  if (tid == 0) s_carry = 0;
+  __syncthreads();
+  for (int u0 = 0; u0 < BH; u0 += NTHREADS) {
+    const int u = u0 + tid;
+    int64_t need = 0;
+    if (u < BH) {
+      const int64_t L = a.ctx_len[u / a.Hkv];
+      const int64_t pend = pool_end(L, a.W, a.S);
+      need = pend > a.S ? (pend + BK - 1) / BK - a.S / BK : 0;
+    }
+    s_need[tid] = need;
+    __syncthreads();
+    // exclusive scan of the chunk (a plain serial pass by one thread: setup, not the step)
+    if (tid == 0) {
+      int64_t run = s_carry;
+      for (int k = 0; k < NTHREADS; ++k) {
+        const int64_t n = s_need[k];
+        s_need[k] = run;
+        run += n;
+      }
+      s_carry = run;
+    }
+    __syncthreads();
+    for (int k = 0; k < NTHREADS && u0 + k < BH; ++k) {
+      const int uk = u0 + k;
+      const int64_t base = s_need[k];
+      const int64_t L = a.ctx_len[uk / a.Hkv];
+      const int64_t pend = pool_end(L, a.W, a.S);
+      const int64_t n = pend > a.S ? (pend + BK - 1) / BK - a.S / BK : 0;
+      for (int i = tid; i < P; i += NTHREADS) a.btab[(size_t)uk * P + i] = -1;
+      __syncthreads();
+      for (int64_t i = tid; i < n; i += NTHREADS) {
+        const int64_t phys = base + i;
+        a.btab[(size_t)uk * P + (size_t)((a.S / BK + i) % P)] = phys < a.NB ? (int32_t)phys : -1;
+      }
+      __syncthreads();
+    }
+  }
+  const int64_t used = s_carry;
+  if (used > a.NB && tid == 0) atomicOr(a.error_word, HARDKV_ERR_POOL_OVERFLOW);
+  const int64_t nfree = used < a.NB ? a.NB - used : 0;
+  for (int64_t k = tid; k < nfree; k += NTHREADS) a.free_list[k] = (int32_t)(used + k);
+  if (tid == 0) *a.free_top = (int32_t)nfree;
+}
+
 // grid (ceil(max_len / 64) + 1, B*Hkv): blocks of 64 context positions, then one
 // workgroup per head that resets the head's counters and condensed tier.
 template <typename T>
@@ -88,7 +141,9 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_prefill(Args a) {
       dk = a.dense_k;
       dv = a.dense_v;
     } else {
-      dst = (((size_t)bh * P + (size_t)((p / BK) % P)) * BK + (size_t)(p % BK)) * ROWB + piece * 16;
+      const int pb = (int)((p / BK) % P);
+      if (a.pool_shared && a.btab[(size_t)bh * P + pb] < 0) continue;  // no block (pool overflow)
+      dst = (pool_row0(a, bh, pb) + (size_t)(p % BK)) * ROWB + piece * 16;
       dk = a.pool_k;
       dv = a.pool_v;
     }
@@ -113,6 +168,24 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_append(Args a) {
   const int64_t p = t - W;          // leaves the window when it is past the sinks
   const bool moves = p >= a.S;      // (and then t >= W)
   const bool sink = t < a.S;        // the new token is a sink position
+  const int pb = (int)((p / BK) % P);
+  if (a.pool_shared && moves && p % BK == 0) {
+    // the position starts a new block: each head takes one from the free list (unless its
+    // ring is full: the block then stays mapped and is overwritten, as in the ring layout)
+    if (tid < H && p + 1 - a.pool_head[(size_t)b * H + tid] <= (int64_t)P * BK) {
+      const size_t bh = (size_t)b * H + tid;
+      const int32_t idx = atomicSub(a.free_top, 1) - 1;
+      int32_t phys = -1;
+      if (idx >= 0 && idx < a.NB) {
+        phys = a.free_list[idx];
+      } else {
+        atomicAdd(a.free_top, 1);
+        atomicOr(a.error_word, HARDKV_ERR_POOL_OVERFLOW);
+      }
+      a.btab[bh * P + pb] = phys;
+    }
+    __syncthreads();
+  }
   for (int k = tid; k < H * 2 * CPR; k += NTHREADS) {
     const int h = k / (2 * CPR), rem = k % (2 * CPR);
     const int which = rem / CPR, piece = rem % CPR;
@@ -124,9 +197,9 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_append(Args a) {
       continue;
     }
     char *dense = (char *)(which ? a.dense_v : a.dense_k) + (bh * W + (size_t)(t % W)) * ROWB + piece * 16;
-    if (moves) {
-      char *pool = (char *)(which ? a.pool_v : a.pool_k) +
-                   ((bh * P + (size_t)((p / BK) % P)) * BK + (size_t)(p % BK)) * ROWB + piece * 16;
+    if (moves && !(a.pool_shared && a.btab[bh * P + pb] < 0)) {
+      char *pool = (char *)(which ? a.pool_v : a.pool_k) + (pool_row0(a, (int)bh, pb) + (size_t)(p % BK)) * ROWB +
+                   piece * 16;
       const uint4 x = *reinterpret_cast<const uint4 *>(dense);
       *reinterpret_cast<uint4 *>(pool) = x;
       if (EB == 2 && !which && key_piece_unsafe(x)) atomicOr(&a.kx[bh], 1u);
@@ -158,6 +231,7 @@ hipError_t launch_fork(const Args &a, hipStream_t s) {
 
 hipError_t launch_prefill(const Args &a, hipStream_t s, bool bf16) {
   hipLaunchKernelGGL(hardkv_prefill_clear, dim3((a.B * a.Hkv + NTHREADS - 1) / NTHREADS), dim3(NTHREADS), 0, s, a);
+  if (a.pool_shared) hipLaunchKernelGGL(hardkv_prefill_alloc, dim3(1), dim3(NTHREADS), 0, s, a);
   dim3 grid((unsigned)((a.max_len + BK - 1) / BK) + 1, a.B * a.Hkv);
   if (bf16)
     hipLaunchKernelGGL((hardkv_prefill<BF16>), grid, dim3(NTHREADS), 0, s, a);

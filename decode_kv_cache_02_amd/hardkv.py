@@ -27,6 +27,7 @@ HARDKV_REG_REWRITE, HARDKV_REG_SPARSE, HARDKV_REG_MTI, HARDKV_REG_MTI_AUTO = 0, 
 MTI_DEFAULT = dict(mti_horizon=0, mti_c_view=97000, mti_c_write=68000, mti_c_scan=0, mti_c_hold=0,
                    mti_c_score=44000, mti_c_gather=[124000] * 9, mti_fixed=0)
 HARDKV_VIEW_MAXLEN, HARDKV_VIEW_SUM = 0, 1
+HARDKV_POOL_RING, HARDKV_POOL_SHARED = 0, 1
 HARDKV_CAL_FIXED, HARDKV_CAL_ENTROPY = 0, 1
 HARDKV_ERR_POOL_OVERFLOW, HARDKV_ERR_VIEW_OVERFLOW, HARDKV_ERR_NONFINITE = 1, 2, 4
 BLOCK, HEAD_DIM = 64, 128
@@ -35,6 +36,7 @@ EXPORTS = ("hardkv_workspace_size", "hardkv_prefill", "hardkv_append", "hardkv_s
            "hardkv_regularize", "hardkv_condense", "hardkv_attend", "hardkv_attend_sparse", "hardkv_step",
            "hardkv_step_reuse", "hardkv_step_noalloc", "hardkv_step_stage", "hardkv_step_num_stages", "hardkv_step_stage_name",
            "hardkv_mti_thresholds", "hardkv_mti_period", "hardkv_select_fork", "hardkv_select_ahead",
+           "hardkv_shared_pool_blocks",
            "hardkv_strerror")
 
 
@@ -57,6 +59,7 @@ class hardkv_config(C.Structure):
         ("mti_horizon", C.c_int32), ("mti_c_view", C.c_uint32), ("mti_c_write", C.c_uint32),
         ("mti_c_scan", C.c_uint32), ("mti_c_hold", C.c_uint32), ("mti_c_score", C.c_uint32),
         ("mti_c_gather", C.c_uint32 * 9), ("mti_fixed", C.c_int64),
+        ("pool_layout", C.c_int32), ("pool_total_blocks", C.c_int32),
     ]
 
 
@@ -67,8 +70,14 @@ _STATE_FIELDS = ("dense_k", "dense_v", "pool_k", "pool_v", "view_k", "view_v", "
                  "workspace")
 
 
+# the shared block pool's table and free list (after workspace_bytes in the struct)
+_STATE_POOL_FIELDS = ("block_table", "free_list", "free_top")
+_STATE_PTRS = _STATE_FIELDS + _STATE_POOL_FIELDS
+
+
 class hardkv_state(C.Structure):
-    _fields_ = [(n, C.c_void_p) for n in _STATE_FIELDS] + [("workspace_bytes", C.c_size_t)]
+    _fields_ = ([(n, C.c_void_p) for n in _STATE_FIELDS] + [("workspace_bytes", C.c_size_t)] +
+                [(n, C.c_void_p) for n in _STATE_POOL_FIELDS])
 
 
 _lib = None
@@ -100,6 +109,7 @@ def lib() -> C.CDLL:
         L.hardkv_select_fork.argtypes = [cp, sp, sp, vp]
         L.hardkv_select_ahead.argtypes = [cp, sp, vp, i32, i32, vp]
         L.hardkv_mti_period.argtypes = [cp, i64, i64, i64, i32, C.POINTER(i32)]
+        L.hardkv_shared_pool_blocks.argtypes = [cp, C.POINTER(i64), i64, C.POINTER(i64)]
         L.hardkv_step_stage_name.argtypes = [i32]
         L.hardkv_step_stage_name.restype = C.c_char_p
         L.hardkv_strerror.argtypes = [i32]
@@ -144,7 +154,8 @@ class Config:
                  tau: Sequence[float], head_dim: int = HEAD_DIM, merge_bias: bool = True,
                  regularize: int = HARDKV_REG_REWRITE, mti_lower: int = 0, mti_upper: int = 0,
                  view_layout: int = HARDKV_VIEW_MAXLEN, view_total: int = 0,
-                 calibration: int = HARDKV_CAL_FIXED, sink: int = 0, mti: Optional[dict] = None):
+                 calibration: int = HARDKV_CAL_FIXED, sink: int = 0, mti: Optional[dict] = None,
+                 pool_layout: int = HARDKV_POOL_RING, pool_total_blocks: int = 0):
         self.tau_arr = (C.c_float * max(1, len(tau)))(*[float(x) for x in tau])
         self.c = hardkv_config(batch, num_q_heads, num_kv_heads, head_dim,
                                HARDKV_BF16 if dtype == "bf16" else HARDKV_F32, dense_window,
@@ -157,6 +168,8 @@ class Config:
         m.update(mti or {})
         for k, v in m.items():
             setattr(self.c, k, (C.c_uint32 * 9)(*[int(x) for x in v]) if k == "mti_c_gather" else int(v))
+        self.c.pool_layout = int(pool_layout)
+        self.c.pool_total_blocks = int(pool_total_blocks)
         self.dtype = dtype
 
     @classmethod
@@ -164,7 +177,8 @@ class Config:
                       merge_bias: bool = True, regularize: int = HARDKV_REG_REWRITE,
                       mti_lower: int = 0, mti_upper: int = 0, view_layout: int = HARDKV_VIEW_MAXLEN,
                       view_total: int = 0, calibration: int = HARDKV_CAL_FIXED,
-                      sink: Optional[int] = None, mti: Optional[dict] = None) -> "Config":
+                      sink: Optional[int] = None, mti: Optional[dict] = None,
+                      pool_layout: int = HARDKV_POOL_RING, pool_total_blocks: int = 0) -> "Config":
         return cls(wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.dtype, wl.dense_window, wl.P_blk,
                    wl.sparse_cap, wl.V_cap, wl.condensed_slots,
                    wl.cond_mode if cond_mode is None else cond_mode,
@@ -173,7 +187,8 @@ class Config:
                    head_dim=wl.head_dim, merge_bias=merge_bias, regularize=regularize,
                    mti_lower=mti_lower, mti_upper=mti_upper, view_layout=view_layout,
                    view_total=view_total, calibration=calibration,
-                   sink=int(getattr(wl, "sink", 0)) if sink is None else int(sink), mti=mti)
+                   sink=int(getattr(wl, "sink", 0)) if sink is None else int(sink), mti=mti,
+                   pool_layout=pool_layout, pool_total_blocks=pool_total_blocks)
 
     def __getattr__(self, name):
         return getattr(self.__dict__["c"], name)
@@ -201,8 +216,17 @@ class State:
         self.cfg = cfg
         self.dense_k = torch.zeros((B, H, W, D), dtype=dt, **kw)
         self.dense_v = torch.zeros((B, H, W, D), dtype=dt, **kw)
-        self.pool_k = torch.zeros((B, H, P, BLOCK, D), dtype=dt, **kw)
-        self.pool_v = torch.zeros((B, H, P, BLOCK, D), dtype=dt, **kw)
+        if c.pool_layout == HARDKV_POOL_SHARED:  # physical blocks, a table per unit, a free list
+            NB = c.pool_total_blocks
+            self.pool_k = torch.zeros((NB, BLOCK, D), dtype=dt, **kw)
+            self.pool_v = torch.zeros((NB, BLOCK, D), dtype=dt, **kw)
+            self.block_table = torch.full((B, H, P), -1, dtype=torch.int32, **kw)
+            self.free_list = torch.zeros((NB,), dtype=torch.int32, **kw)
+            self.free_top = torch.zeros((4,), dtype=torch.int32, **kw)
+        else:
+            self.pool_k = torch.zeros((B, H, P, BLOCK, D), dtype=dt, **kw)
+            self.pool_v = torch.zeros((B, H, P, BLOCK, D), dtype=dt, **kw)
+            self.block_table = self.free_list = self.free_top = None
         if c.view_layout == HARDKV_VIEW_SUM:   # packed (CSR) views of view_total rows
             Vt = max(1, c.view_total)
             self.view_k = torch.zeros((Vt, D), dtype=dt, **kw)
@@ -235,27 +259,31 @@ class State:
         self.error_word = torch.zeros((4,), dtype=torch.int32, **kw)
         self.workspace_bytes = hardkv_workspace_size(cfg)
         self.workspace = torch.zeros((self.workspace_bytes,), dtype=torch.uint8, **kw)
-        self.c = hardkv_state(*[_ptr(getattr(self, n)) for n in _STATE_FIELDS], self.workspace_bytes)
+        self._bind()
+
+    def _bind(self):
+        self.c = hardkv_state(*[_ptr(getattr(self, n)) for n in _STATE_FIELDS], self.workspace_bytes,
+                              *[_ptr(getattr(self, n)) for n in _STATE_POOL_FIELDS])
 
     # buffers that hold the cache itself, shared by the two states of the pipeline
     SHARED = ("dense_k", "dense_v", "pool_k", "pool_v", "sink_k", "sink_v", "cond_kn", "cond_vn", "cond_omega",
-              "cond_n", "cond_cursor", "seq_len", "pool_head", "error_word")
+              "cond_n", "cond_cursor", "seq_len", "pool_head", "error_word") + _STATE_POOL_FIELDS
 
     def twin(self) -> "State":
         """A state for a selection made ahead (hardkv_select_fork / hardkv_select_ahead): the
         same cache buffers, its own selection buffers and workspace."""
         o = State.__new__(State)
         o.cfg = self.cfg
-        for n in _STATE_FIELDS:
+        for n in _STATE_PTRS:
             t = getattr(self, n)
-            setattr(o, n, t if n in self.SHARED else torch.zeros_like(t))
+            setattr(o, n, t if (n in self.SHARED or t is None) else torch.zeros_like(t))
         o.view_pos.fill_(-1)
         o.workspace_bytes = self.workspace_bytes
-        o.c = hardkv_state(*[_ptr(getattr(o, n)) for n in _STATE_FIELDS], o.workspace_bytes)
+        o._bind()
         return o
 
     def tensors(self):
-        return {n: getattr(self, n) for n in _STATE_FIELDS}
+        return {n: getattr(self, n) for n in _STATE_PTRS if getattr(self, n) is not None}
 
 
 # ---- entry points ----------------------------------------------------------------------------
@@ -327,6 +355,16 @@ def hardkv_mti_period(cfg: Config, n_pool: int, n_survivors: int, kstar: int, ma
     _check("hardkv_mti_period", lib().hardkv_mti_period(C.byref(cfg.c), int(n_pool), int(n_survivors), int(kstar),
                                                         int(max_period), C.byref(r)))
     return int(r.value)
+
+
+def hardkv_shared_pool_blocks(cfg: Config, ctx_len, steps: int = 0) -> int:
+    """Physical blocks a SHARED pool needs for a prefill of ctx_len (host lengths) and `steps`
+    appends without a condensation."""
+    lens = [int(x) for x in (ctx_len.tolist() if hasattr(ctx_len, "tolist") else ctx_len)]
+    arr = (C.c_int64 * max(1, len(lens)))(*lens)
+    n = C.c_int64(0)
+    _check("hardkv_shared_pool_blocks", lib().hardkv_shared_pool_blocks(C.byref(cfg.c), arr, int(steps), C.byref(n)))
+    return int(n.value)
 
 
 def hardkv_select_fork(cfg: Config, st_next: State, st_cur: State, stream=None) -> None:

@@ -59,8 +59,9 @@
  *   - Host-detectable errors (bad sizes, null or misaligned pointers, too small a
  *     workspace) return a negative status before anything is enqueued.
  *   - Runtime conditions set bits of *error_word on the device (the caller reads
- *     it after a synchronization of its choosing): HARDKV_ERR_POOL_OVERFLOW (the
- *     pool ring overflowed; only possible in mode OFF), HARDKV_ERR_VIEW_OVERFLOW,
+ *     it after a synchronization of its choosing): HARDKV_ERR_POOL_OVERFLOW (a
+ *     unit's pool ring overflowed, or the SHARED pool had no free block),
+ *     HARDKV_ERR_VIEW_OVERFLOW,
  *     HARDKV_ERR_NONFINITE (a non-finite score; outputs are then undefined).
  *   - The workspace must be zero-filled once before first use; the kernels leave
  *     its counters at zero after each call.  It belongs to its state: besides
@@ -148,6 +149,19 @@ typedef enum { HARDKV_REG_REWRITE = 0, HARDKV_REG_SPARSE = 1, HARDKV_REG_MTI = 2
  *           written and set HARDKV_ERR_VIEW_OVERFLOW.  A head's view only lives until the
  *           next select (the offsets move with every step's budgets). */
 typedef enum { HARDKV_VIEW_MAXLEN = 0, HARDKV_VIEW_SUM = 1 } hardkv_view_layout;
+/* The pool's memory (section 2.C: a head-wise block manager allocates head-adaptively while
+ * keeping static shapes and persistent pointers for graph capture):
+ *   RING    every (b, h) owns a ring of pool_blocks blocks in pool_k/v (default);
+ *   SHARED  one pool of pool_total_blocks physical blocks of 64 rows for all (b, h): ring
+ *           block pb of unit u is physical block block_table[u][pb] (-1: none).  The prefill
+ *           gives each unit the blocks its pool holds, in unit order, and leaves the others
+ *           on the free list; an append takes a block from the free list when a position
+ *           starts a new one; a condensation returns the blocks it condenses.  Memory then
+ *           follows what the pools hold instead of B * Hkv worst-case rings; pool_blocks stays
+ *           the per-unit ring (the table's length).  An append or prefill that finds the free
+ *           list empty sets HARDKV_ERR_POOL_OVERFLOW and writes nothing. */
+typedef enum { HARDKV_POOL_RING = 0, HARDKV_POOL_SHARED = 1 } hardkv_pool_layout;
+
 /* Logits Calibration temperature (section 2.B calibrates the scores by the temperature of
  * the attention scores without fixing how it is obtained):
  *   FIXED    tau_h from hardkv_config.tau (default);
@@ -204,13 +218,17 @@ typedef struct {
   uint32_t mti_c_score;    /* per pool row scored at a selection (hardkv_mti_period only) */
   uint32_t mti_c_gather[9];/* by the kept eighth b of the survivors */
   int64_t mti_fixed;       /* F per rewritten head, in [0, HARDKV_MTI_MAX_FIXED] */
+  int32_t pool_layout;     /* hardkv_pool_layout (0: RING) */
+  int32_t pool_total_blocks; /* NB, physical blocks of the SHARED pool, in [1, 2^26) */
 } hardkv_config;
 
 /* Device buffers of one layer.  All fixed capacity; 16-byte aligned.
  * Element types: "e" is bf16 (2 bytes) or fp32 (4 bytes) per cfg->dtype. */
 typedef struct {
   void *dense_k, *dense_v;   /* e [B][Hkv][W][128]: position p in slot p mod W                    */
-  void *pool_k, *pool_v;     /* e [B][Hkv][P][64][128]: position p in block (p/64) mod P, row p%64 */
+  void *pool_k, *pool_v;     /* e [B][Hkv][P][64][128] (RING): position p in block (p/64) mod P, row
+                                p%64; e [NB][64][128] (SHARED): in physical block
+                                block_table[b][h][(p/64) mod P], row p%64                         */
   void *view_k, *view_v;     /* e [B][Hkv][V_cap][128] (MAXLEN) or e [view_total][128] (SUM): the
                                 head's row r = its r-th kept position (ascending)                */
   int32_t *view_pos;         /* [B][Hkv][V_cap] or [view_total]: position of each view row        */
@@ -238,6 +256,9 @@ typedef struct {
   uint32_t *error_word;      /* [1]: HARDKV_ERR_* bits, or-ed                                     */
   void *workspace;           /* hardkv_workspace_size() bytes, zero-filled before first use      */
   size_t workspace_bytes;
+  int32_t *block_table;      /* SHARED pool: [B][Hkv][P] physical block of each ring block (-1: none) */
+  int32_t *free_list;        /* SHARED pool: [pool_total_blocks] free physical blocks               */
+  int32_t *free_top;         /* SHARED pool: [1] free blocks in free_list (written by the prefill)  */
 } hardkv_state;
 
 /* Bytes of workspace a state needs.  Returns HARDKV_EINVAL/EUNSUPPORTED on a bad config. */
@@ -374,6 +395,15 @@ int32_t hardkv_step_stage(const hardkv_config *cfg, hardkv_state *st, const void
 /* Number of kernels hardkv_step launches, and the name of kernel `stage`. */
 int32_t hardkv_step_num_stages(void);
 const char *hardkv_step_stage_name(int32_t stage);
+
+/* Size of a SHARED pool (host only): *blocks is the number of physical blocks the units'
+ * pools hold after a prefill of the lengths ctx_len[0 .. batch) (a host array) followed by
+ * `steps` appends with no condensation: per unit, the blocks that cover its pool
+ * [S, max(S, L + steps - W)), at most pool_blocks, summed over num_kv_heads heads per sequence.
+ * A pool of that many blocks never overflows over those steps; a condensation only returns
+ * blocks.  HARDKV_EINVAL on a bad config, a null pointer, a negative length or step count. */
+int32_t hardkv_shared_pool_blocks(const hardkv_config *cfg, const int64_t *ctx_len, int64_t steps,
+                                  int64_t *blocks);
 
 /* The memory-time controller's thresholds (host only): *l_lower and *l_upper are the smallest
  * and the largest budget k* in [1, n_survivors] that policy MTI_AUTO rewrites for a head of

@@ -47,7 +47,7 @@ class Pair:
 
     def __init__(self, wl, inputs=None, top_p=None, tau=None, cond_mode=None, merge_bias=True,
                  device="cuda", oracle_units=None, layer=0, regularize=0, mti_lower=0, mti_upper=0,
-                 view_layout=0, view_total=0, make_state=None, mti=None):
+                 view_layout=0, view_total=0, make_state=None, mti=None, pool_layout=0, pool_total_blocks=0):
         self.wl = wl if cond_mode is None else wl.with_(cond_mode=cond_mode)
         if top_p is not None:
             self.wl = self.wl.with_(top_p=top_p)
@@ -59,7 +59,14 @@ class Pair:
         assert not (self.packed and oracle_units is not None), "packed views need the whole layer"
         # the memory-time controller's inputs (policy MTI_AUTO), the same on both sides
         self.mti = dict(hk.MTI_DEFAULT, **(mti or {}))
-        self.cfg = hk.Config.from_workload(self.wl, tau=self.tau, merge_bias=merge_bias, mti=self.mti, **pol)
+        # the shared block pool is a device layout only: the oracle keeps a ring per unit; with
+        # no size given it gets exactly the blocks the prefill and the workload's steps can hold
+        self.shared = pool_layout == hk.HARDKV_POOL_SHARED
+        if self.shared and not pool_total_blocks:
+            ring = hk.Config.from_workload(self.wl, tau=self.tau, **pol)
+            pool_total_blocks = max(1, hk.hardkv_shared_pool_blocks(ring, self.inp.ctx_len.cpu(), self.wl.steps))
+        self.cfg = hk.Config.from_workload(self.wl, tau=self.tau, merge_bias=merge_bias, mti=self.mti,
+                                           pool_layout=pool_layout, pool_total_blocks=pool_total_blocks, **pol)
         self.st = (make_state or hk.State)(self.cfg, device=device)
         hk.hardkv_prefill(self.cfg, self.st, self.inp.k_ctx, self.inp.v_ctx, self.inp.ctx_len)
         self.units = oracle_units
@@ -151,6 +158,8 @@ class Pair:
                 assert e <= ATT_TOL, f"{tag} attention rel err {e}"
         ew = int(self.st.error_word[0].item())
         assert (ew == err) if None in self.orcs else (ew & err == err), "error word"
+        if self.shared:
+            check_shared_pool(self)
         self.step_i += 1
 
     # ---- comparison --------------------------------------------------------------------------
@@ -228,6 +237,8 @@ class Pair:
                     oo = outs[key][b, h * G:(h + 1) * G] if key is None else outs[key][0]
                     e = row_rel_err(go, oo)
                     assert e <= ATT_TOL, f"{tag} attention rel err {e}"
+        if self.shared:
+            check_shared_pool(self)
         if self.packed and check_views:
             o = self.orcs[None][0]
             voff = self.st.view_off.cpu().numpy()
@@ -243,6 +254,64 @@ class Pair:
 
 
 _POPC8 = None
+
+
+def logical_pool_rows(st, wl, pos: torch.Tensor, units: torch.Tensor) -> torch.Tensor:
+    """Row index into pool_k/v viewed as [rows][128] of position pos[i] of unit units[i]
+    (flat b * Hkv + h): its ring row, or in the shared pool the row of the physical block the
+    block table maps its ring block to."""
+    P = wl.P_blk
+    pb = (pos // 64) % P
+    if st.block_table is None:
+        return (units * P + pb) * 64 + pos % 64
+    phys = st.block_table.reshape(-1, P)[units, pb].long()
+    assert torch.all(phys >= 0), "a pool position without a physical block"
+    return phys * 64 + pos % 64
+
+
+def check_shared_pool(pr) -> None:
+    """The shared block pool after a step: the blocks the units' pools hold (ring blocks
+    c/64 .. ceil(pend/64) - 1 of each unit) and the free list are a permutation of the
+    physical blocks (none lost, none held twice), and every pool position's row holds the
+    oracle's pool row bit for bit (the whole layer's oracle only)."""
+    st, wl = pr.st, pr.wl
+    P, NB = wl.P_blk, int(pr.cfg.c.pool_total_blocks)
+    S = int(getattr(wl, "sink", 0))
+    tab = st.block_table.cpu().numpy().reshape(-1, P)
+    top = int(st.free_top[0].item())
+    free = st.free_list[:max(top, 0)].cpu().numpy()
+    seq = st.seq_len.cpu().numpy()
+    head = st.pool_head.cpu().numpy().reshape(-1)
+    H = wl.num_kv_heads
+    held = []
+    spans = []
+    for u in range(wl.batch * H):
+        pend = max(S, int(seq[u // H]) - wl.dense_window)
+        c = int(head[u])
+        nblk = max(0, -(-pend // 64) - c // 64)
+        spans.append((c, pend))
+        held.extend(int(tab[u, (c // 64 + i) % P]) for i in range(nblk))
+    assert 0 <= top <= NB, f"free_top {top} outside [0, {NB}]"
+    allb = np.sort(np.concatenate([np.asarray(held, np.int64), free.astype(np.int64)]))
+    assert np.array_equal(allb, np.arange(NB)), "held and free blocks are not a permutation of the pool"
+    if None not in pr.orcs:
+        return
+    o = pr.orcs[None][0]
+    pos_l, unit_l = [], []
+    for u, (c, pend) in enumerate(spans):
+        pos_l.append(np.arange(c, pend))
+        unit_l.append(np.full(pend - c, u))
+    pos = np.concatenate(pos_l).astype(np.int64)
+    units = np.concatenate(unit_l).astype(np.int64)
+    if pos.size == 0:
+        return
+    rows = logical_pool_rows(st, wl, torch.from_numpy(pos).to(st.pool_k.device),
+                             torch.from_numpy(units).to(st.pool_k.device))
+    for name in ("pool_k", "pool_v"):
+        g = raw(getattr(st, name).reshape(-1, wl.head_dim)[rows])
+        ring = getattr(o, name).reshape(-1, P * 64, wl.head_dim)
+        want = ring[units, (pos // 64) % P * 64 + pos % 64]
+        assert np.array_equal(g, want), f"{name} rows of the shared pool differ from the oracle's pool"
 
 
 def check_layer_properties(pr: Pair) -> None:
@@ -305,14 +374,16 @@ def check_layer_properties(pr: Pair) -> None:
     assert torch.all((d > 0) | ~live[:, 1:]), "view positions not increasing"
     sel_pos = torch.where(bits, pos, pos_big).sort(1).values[:, :V]
     assert torch.equal(torch.where(live, vpos, 0), torch.where(live, sel_pos, 0)), "view_pos != kept positions"
-    vrow = ((vpos // 64) % P) * 64 + vpos % 64
     for name_v, name_p in (("view_k", "pool_k"), ("view_v", "pool_v")):
         view = getattr(st, name_v).reshape(BH, V, -1)
-        pool = getattr(st, name_p).reshape(BH, P * 64, -1)
+        pool = getattr(st, name_p).reshape(-1, wl.head_dim)
         for u0 in range(0, BH, 32):
             u1 = min(BH, u0 + 32)
-            idx = torch.where(live[u0:u1], vrow[u0:u1], 0)
-            src = torch.gather(pool[u0:u1], 1, idx[:, :, None].expand(-1, -1, pool.shape[-1]))
-            ok = (src.view(torch.int16) == view[u0:u1].view(torch.int16)) if src.dtype == torch.bfloat16 \
-                else (src.view(torch.int32) == view[u0:u1].view(torch.int32))
-            assert torch.all(ok.all(-1) | ~live[u0:u1]), f"{name_v} rows differ from the pool"
+            uu, rr = live[u0:u1].nonzero(as_tuple=True)
+            if uu.numel() == 0:
+                continue
+            src = pool[logical_pool_rows(st, wl, vpos[u0:u1][uu, rr], uu + u0)]
+            dst = view[u0:u1][uu, rr]
+            ok = (src.view(torch.int16) == dst.view(torch.int16)) if src.dtype == torch.bfloat16 \
+                else (src.view(torch.int32) == dst.view(torch.int32))
+            assert torch.all(ok), f"{name_v} rows differ from the pool"

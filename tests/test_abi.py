@@ -22,7 +22,7 @@ def _declared():
 def test_exports_every_declared_symbol():
     lib = hk.lib()
     names = _declared()
-    assert len(names) == 19, names
+    assert len(names) == 20, names
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(hk.EXPORTS)
@@ -69,6 +69,9 @@ def _cfg(**over):
     (dict(regularize=hk.HARDKV_REG_MTI_AUTO, mti_c_write=1 << 24), hk.HARDKV_EINVAL),
     (dict(regularize=hk.HARDKV_REG_MTI_AUTO, mti_fixed=-1), hk.HARDKV_EINVAL),
     (dict(regularize=hk.HARDKV_REG_MTI_AUTO, mti_fixed=(1 << 40) + 1), hk.HARDKV_EINVAL),
+    (dict(pool_layout=2), hk.HARDKV_EINVAL),
+    (dict(pool_layout=hk.HARDKV_POOL_SHARED, pool_total_blocks=0), hk.HARDKV_EINVAL),
+    (dict(pool_layout=hk.HARDKV_POOL_SHARED, pool_total_blocks=1 << 26), hk.HARDKV_EINVAL),
     (dict(view_layout=2), hk.HARDKV_EINVAL),
     (dict(view_layout=1, view_total=-1), hk.HARDKV_EINVAL),
     (dict(calibration=2), hk.HARDKV_EINVAL),
@@ -114,10 +117,10 @@ def _fake_state(cfg, ws_bytes=None, misalign=None, null=None):
     """A state of fake, aligned device addresses: validation runs before any launch."""
     st = hk.hardkv_state()
     addr = 1 << 40
-    for i, (name, _) in enumerate(hk.hardkv_state._fields_[:-1]):
+    for i, (name, _) in enumerate(f for f in hk.hardkv_state._fields_ if f[0] != "workspace_bytes"):
         v = addr + i * (1 << 30)
         if name == misalign:
-            v += 4 if name not in ("error_word", "regularized") else 2
+            v += 4 if name not in ("error_word", "regularized", "free_top") else 2
         if name == null:
             v = None
         setattr(st, name, v)
@@ -258,3 +261,40 @@ def test_pipeline_pair_validation():
     packed = _cfg(view_layout=1, view_total=100)
     st = _fake_state(packed)
     assert L.hardkv_select_ahead(C.byref(packed.c), C.byref(st), ok, 0, 1, None) == hk.HARDKV_EUNSUPPORTED
+
+
+@_no_gpu
+@pytest.mark.parametrize("kind", ["null_table", "misaligned_free_list", "null_top", "misaligned_top"])
+def test_shared_pool_state_validation(kind):
+    """The shared pool's table, free list and free count are checked like every other buffer."""
+    L = hk.lib()
+    ok = C.c_void_p(1 << 41)
+    cfg = _cfg(pool_layout=hk.HARDKV_POOL_SHARED, pool_total_blocks=100)
+    st = {"null_table": lambda: _fake_state(cfg, null="block_table"),
+          "misaligned_free_list": lambda: _fake_state(cfg, misalign="free_list"),
+          "null_top": lambda: _fake_state(cfg, null="free_top"),
+          "misaligned_top": lambda: _fake_state(cfg, misalign="free_top")}[kind]()
+    assert L.hardkv_step(C.byref(cfg.c), C.byref(st), ok, ok, ok, ok, None) == hk.HARDKV_EINVAL
+    assert L.hardkv_prefill(C.byref(cfg.c), C.byref(st), ok, ok, ok, 10, None) == hk.HARDKV_EINVAL
+    assert L.hardkv_append(C.byref(cfg.c), C.byref(st), ok, ok, None) == hk.HARDKV_EINVAL
+
+
+def test_shared_pool_blocks_by_hand():
+    """The pool size helper: blocks that cover [S, max(S, L + steps - W)) per unit, at most P,
+    times the KV heads; checked against the sum written out for mixed lengths."""
+    wl = tiny_workload(batch=5, num_kv_heads=3, num_q_heads=12, ctx_len=900, ctx_min=100)
+    cfg = hk.Config.from_workload(wl)
+    W, P = wl.dense_window, wl.P_blk
+    for lens, steps in (([100, 300, 900, 64 + W, 65 + W], 0), ([100, 300, 900, 64 + W, 65 + W], 7),
+                        ([0, 0, 0, 0, 0], 3), ([W - 1] * 5, 1)):
+        want = 0
+        for L_ in lens:
+            pend = max(0, L_ + steps - W)
+            want += min(-(-pend // 64), P) * 3
+        assert hk.hardkv_shared_pool_blocks(cfg, lens, steps) == want, (lens, steps)
+    sunk = hk.Config.from_workload(wl, sink=64)
+    # with 64 sink positions the pool starts at 64: L = W + 64 holds none, W + 65 one block
+    assert hk.hardkv_shared_pool_blocks(sunk, [W + 64, W + 65, W + 64 + 64, W + 65 + 64, 0], 0) == (0 + 1 + 1 + 2) * 3
+    for bad in (([1, 2, 3, 4, -1], 0), ([1, 2, 3, 4, 5], -1)):
+        with pytest.raises(hk.HardKVError):
+            hk.hardkv_shared_pool_blocks(cfg, *bad)

@@ -28,14 +28,16 @@ class GuardedState(hk.State):
     def __init__(self, cfg, device="cuda"):
         super().__init__(cfg, device=device)
         self.guarded = {}
-        for n in hk._STATE_FIELDS:
+        for n in hk._STATE_PTRS:
             t = getattr(self, n)
+            if t is None:
+                continue
             nb = t.numel() * t.element_size()
             big = torch.full((GUARD + nb + GUARD,), PATTERN, dtype=torch.uint8, device=t.device)
             big[GUARD:GUARD + nb].copy_(t.contiguous().view(-1).view(torch.uint8))
             setattr(self, n, big[GUARD:GUARD + nb].view(t.dtype).view(t.shape))
             self.guarded[n] = (big, nb)
-        self.c = hk.hardkv_state(*[hk._ptr(getattr(self, n)) for n in hk._STATE_FIELDS], self.workspace_bytes)
+        self._bind()
 
     def check(self, tag):
         torch.cuda.synchronize()
@@ -55,7 +57,7 @@ CASES = {
 
 
 @pytest.mark.parametrize("name", list(CASES))
-@pytest.mark.parametrize("layout", ["maxlen", "packed_short"])
+@pytest.mark.parametrize("layout", ["maxlen", "packed_short", "shared", "shared_short"])
 def test_guards_untouched(name, layout):
     kw = dict(CASES[name])
     steps = kw.pop("steps")
@@ -64,6 +66,11 @@ def test_guards_untouched(name, layout):
     extra = {}
     if layout == "packed_short":  # fewer packed rows than the budgets need: overflow bit, no write past
         extra = dict(view_layout=hk.HARDKV_VIEW_SUM, view_total=wl.batch * wl.num_kv_heads * 40)
+    elif layout.startswith("shared"):  # the shared block pool, sized for the steps or a block short of the prefill
+        ring = hk.Config.from_workload(wl)
+        need = (hk.hardkv_shared_pool_blocks(ring, inp.ctx_len.cpu(), steps + 2) if layout == "shared"
+                else hk.hardkv_shared_pool_blocks(ring, inp.ctx_len.cpu(), 0) - 1)
+        extra = dict(pool_layout=hk.HARDKV_POOL_SHARED, pool_total_blocks=need)
     for cal in (hk.HARDKV_CAL_FIXED, hk.HARDKV_CAL_ENTROPY):
         cfg = hk.Config.from_workload(wl, calibration=cal, **extra)
         st = GuardedState(cfg)
@@ -86,3 +93,5 @@ def test_guards_untouched(name, layout):
         st.check(f"{name} {layout} cal {cal} steps")
         if layout == "packed_short":
             assert int(st.error_word[0].item()) & hk.HARDKV_ERR_VIEW_OVERFLOW
+        if layout == "shared_short":
+            assert int(st.error_word[0].item()) & hk.HARDKV_ERR_POOL_OVERFLOW

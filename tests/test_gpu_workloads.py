@@ -98,6 +98,40 @@ def test_c3_mixed_lengths(p):
     assert int(pr.st.n_condense.max()) > 256  # the condensed ring wrapped
 
 
+def test_c3_shared_pool():
+    """c3 in the shared block pool sized by the prefilled lengths: about 60% of the rings'
+    blocks; the same outputs and selection bits as the ring layout, sampled units against
+    the oracle, the layer's properties (views read through the block table) and the
+    conservation of blocks after the step."""
+    from decode_kv_cache_02_amd import hardkv as hk
+    from parity import Pair, check_layer_properties
+    from synth import make_inputs
+    wl = get_workload("c3")
+    print("workload", wl.name, "shared pool", flush=True)
+    inp = make_inputs(wl, device="cuda")
+    lens = inp.ctx_len.cpu().numpy()
+    ring_cfg = hk.Config.from_workload(wl)
+    ring = hk.State(ring_cfg)
+    hk.hardkv_prefill(ring_cfg, ring, inp.k_ctx, inp.v_ctx, inp.ctx_len)
+    out_ring = torch.zeros((wl.batch, wl.num_q_heads, wl.head_dim), dtype=torch.float32, device="cuda")
+    hk.hardkv_step(ring_cfg, ring, inp.q[0], inp.k_new[0], inp.v_new[0], out_ring)
+    torch.cuda.synchronize()
+    keep = {n: getattr(ring, n).clone() for n in ("mask", "budget", "n_condense", "cond_kn", "cond_omega")}
+    del ring
+    torch.cuda.empty_cache()
+    pr = Pair(wl, inputs=inp, oracle_units=_sample_units(wl, 16, 7, lens), pool_layout=hk.HARDKV_POOL_SHARED)
+    nb = int(pr.cfg.c.pool_total_blocks)
+    ratio = nb / (wl.batch * wl.num_kv_heads * wl.P_blk)
+    print(f"shared pool {nb} blocks, {ratio:.3f} of the rings", flush=True)
+    assert ratio < 0.7
+    pr.drop_context()
+    pr.step()
+    check_layer_properties(pr)
+    assert torch.equal(pr.out, out_ring)
+    for n, t in keep.items():
+        assert torch.equal(getattr(pr.st, n), t), n
+
+
 def test_c4_streaming_256_steps():
     """Batch 4, 128k context, 256 decode steps; blocks condense at steps 1, 65, 129, 193."""
     from parity import Pair, check_layer_properties

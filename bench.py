@@ -25,9 +25,12 @@ Timing:
     into one HIP graph and replayed once between two events; kernels that only read
     what earlier ones wrote are timed again on the post-step state.
   * The dominant kernel is the longest one that moves algorithmic bytes; those bytes
-    per launch over its duration give roofline.achieved.  roofline.copy_reference is a
-    plain device copy of the same bytes timed in the same run: the rate a kernel that
-    reads and writes equally can practically reach on the box, beside the 8 TB/s peak.
+    per launch over its duration give roofline.achieved.  roofline.copy_reference times
+    the rewrite's copy alone in the same run (layer 0's kept rows gathered from the pool
+    and written contiguously): one 16-byte piece per thread, wavefronts that loop over 64
+    rows with the next batch in flight (the pattern a kernel that also consumes the rows
+    must take), and a plain device copy of the same bytes; the rates a kernel that reads
+    and writes equally can practically reach on the box, beside the 8 TB/s peak.
   * Algorithmic bytes per step follow the byte model of the design notes and are
     computed from the per-unit pool sizes, budgets and condensed blocks of the
     timed steps, replayed eagerly from a snapshot after the timed region.
@@ -61,8 +64,8 @@ D = 128
 STAGE_NAMES = ["append", "score", "select", "condense", "rewrite_attend", "combine"]
 REPEATABLE = [1, 2, 4, 5]  # stages that only read what earlier stages wrote
 # the workloads measured beside the headline: the three target workloads (the mixed-length
-# one at each p of its sweep) and the streaming one
-EXTRA_DEFAULT = "c1,c2,c3:0.8,c3:0.9,c3:0.99,c4"
+# one at each p of its sweep, and at p = 0.9 in the shared block pool) and the streaming one
+EXTRA_DEFAULT = "c1,c2,c3:0.8,c3:0.9,c3:0.99,c3:0.9:shared,c4"
 POLICY_DEFAULT = "c2,c4,c5"
 
 
@@ -107,6 +110,9 @@ def parse():
                     help="packed view rows for --view-layout sum (0: batch * kv_heads * view_cap)")
     ap.add_argument("--sink", type=int, default=None,
                     help="sink prefix tokens S (a multiple of 64; default: the workload's, 0)")
+    ap.add_argument("--pool-layout", choices=["ring", "shared"], default="ring",
+                    help="the pool: a ring per (sequence, KV head), or the shared block pool sized for the "
+                         "prefilled lengths")
     ap.add_argument("--select-every", type=int, default=1,
                     help="also time steps that select once every R steps and reuse the selection in "
                          "between (hardkv_step_reuse), reported under select_every; the pool ring gets "
@@ -130,24 +136,33 @@ def parse():
 
 
 # ---- layers ------------------------------------------------------------------------------
+# the shared pool's allocation state, changed by appends (a block taken) and condensations
+# (blocks returned)
+POOL_STATE = ("block_table", "free_list", "free_top")
 POLICY = {"rewrite": hk.HARDKV_REG_REWRITE, "sparse": hk.HARDKV_REG_SPARSE, "mti": hk.HARDKV_REG_MTI,
           "mti-auto": hk.HARDKV_REG_MTI_AUTO}
 
 
 class Layer:
     def __init__(self, wl, layer, steps, top_p=None, policy=("rewrite", 0, 0, 0), view=("maxlen", 0),
-                 calibration="fixed"):
+                 calibration="fixed", pool_layout="ring"):
         self.wl = wl
         self.inp = make_inputs(wl, layer=layer, device="cuda", steps=steps)
         total = view[1] or wl.batch * wl.num_kv_heads * wl.V_cap
-        self.cfg = hk.Config.from_workload(wl, top_p=top_p, regularize=POLICY[policy[0]],
-                                           mti_lower=policy[1], mti_upper=policy[2],
-                                           mti=dict(mti_horizon=policy[3]),
-                                           view_layout=hk.HARDKV_VIEW_SUM if view[0] == "sum" else
-                                           hk.HARDKV_VIEW_MAXLEN, view_total=total,
-                                           calibration=hk.HARDKV_CAL_ENTROPY if calibration == "entropy"
-                                           else hk.HARDKV_CAL_FIXED)
+        kw = dict(top_p=top_p, regularize=POLICY[policy[0]], mti_lower=policy[1], mti_upper=policy[2],
+                  mti=dict(mti_horizon=policy[3]),
+                  view_layout=hk.HARDKV_VIEW_SUM if view[0] == "sum" else hk.HARDKV_VIEW_MAXLEN, view_total=total,
+                  calibration=hk.HARDKV_CAL_ENTROPY if calibration == "entropy" else hk.HARDKV_CAL_FIXED)
+        self.cfg = hk.Config.from_workload(wl, **kw)
+        self.shared = pool_layout == "shared"
+        if self.shared:
+            # the shared block pool, sized for the prefilled lengths and the steps taken
+            nb = max(1, hk.hardkv_shared_pool_blocks(self.cfg, self.inp.ctx_len.cpu(), steps))
+            self.cfg = hk.Config.from_workload(wl, pool_layout=hk.HARDKV_POOL_SHARED, pool_total_blocks=nb, **kw)
+            self.MUTABLE = Layer.MUTABLE + POOL_STATE
+            self.MUTATES = {0: Layer.MUTATES[0] + POOL_STATE, 3: Layer.MUTATES[3] + POOL_STATE}
         self.st = hk.State(self.cfg)
+        self.pool_bytes = 2 * self.st.pool_k.numel() * self.st.pool_k.element_size()
         hk.hardkv_prefill(self.cfg, self.st, self.inp.k_ctx, self.inp.v_ctx, self.inp.ctx_len)
         self.out = torch.zeros((wl.batch, wl.num_q_heads, D), dtype=torch.float32, device="cuda")
 
@@ -417,6 +432,64 @@ def device_copy_reference(nbytes, reps=10):
     return {"GBps": gbps, "frac": gbps / HBM_PEAK_GBPS, "what": "torch device copy of the same bytes, this run"}
 
 
+def gather_copy_reference(L, reps=10):
+    """The rewrite's copy alone, in the two access patterns of the copy probes (one 16-byte
+    piece per thread, or wavefronts looping over 64 rows with the next batch in flight), and
+    torch's device copy of the same bytes: the kept rows of layer 0's last selection (K and
+    V) gathered from the pool and written contiguously, timed in this run, in GB/s of bytes
+    read plus written."""
+    import ctypes as C
+    wl, st = L.wl, L.st
+    if wl.dtype != "bf16":
+        return None
+    lib = C.CDLL(os.path.join(ROOT, "decode_kv_cache_02_amd", "libhardkv_probe.so"))
+    lib.hardkv_probe_gather_copy.argtypes = [C.c_void_p] * 5 + [C.c_int64, C.c_int32, C.c_void_p]
+    lib.hardkv_probe_gather_copy.restype = C.c_int32
+    BH, P = wl.batch * wl.num_kv_heads, wl.P_blk
+    bits = (st.mask.reshape(BH, P, 1) >> torch.arange(64, device="cuda")) & 1
+    u, ring_row = bits.reshape(BH, P * 64).nonzero(as_tuple=True)
+    if L.shared:
+        rows = st.block_table.reshape(BH, P)[u, ring_row // 64].long() * 64 + ring_row % 64
+    else:
+        rows = u * (P * 64) + ring_row
+    n = int(rows.numel())
+    pool_rows = st.pool_k.numel() // D
+    if n == 0 or int(rows.min()) < 0 or int(rows.max()) >= pool_rows:
+        return None
+    rows = rows.to(torch.int32).contiguous()
+    dk = torch.empty((n, D), dtype=torch.bfloat16, device="cuda")
+    dv = torch.empty_like(dk)
+    stream = torch.cuda.current_stream()
+    nbytes = 2 * 2 * n * D * 2  # K and V, read and written
+
+    def launch(mode):
+        rc = lib.hardkv_probe_gather_copy(st.pool_k.data_ptr(), st.pool_v.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                                          rows.data_ptr(), n, mode, stream.cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"copy probe failed: {rc}")
+
+    res = {"rows": n, "bytes": nbytes}
+    for name, mode in (("one_shot_GBps", 0), ("looping_GBps", 1)):
+        launch(mode)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            launch(mode)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        res[name] = nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    ok = torch.equal(dk[:: max(1, n // 1000)], st.pool_k.reshape(-1, D)[rows[:: max(1, n // 1000)].long()])
+    del dk, dv, rows
+    torch.cuda.empty_cache()
+    plain = device_copy_reference(nbytes)
+    res["torch_copy_GBps"] = plain["GBps"] if plain else None
+    res["copy_checked"] = bool(ok)
+    res["what"] = ("the kept rows of layer 0 (K and V) gathered from the pool into contiguous rows: one piece "
+                   "per thread, wavefronts looping over 64 rows, and a plain device copy of the same bytes")
+    return res
+
+
 def unit_bytes(wl, N, kstar, E, t, c_occ, rw):
     """Algorithmic bytes per stage for arrays of per-unit values (one step).
 
@@ -657,11 +730,14 @@ def run_extras(args):
     if not args.extra_configs or args.extra_configs == "none":
         return out
     for spec in args.extra_configs.split(","):
-        key, _, p = spec.partition(":")
+        key, _, rest = spec.partition(":")
+        p, _, layout = rest.partition(":")
         cmd = [sys.executable, os.path.abspath(__file__), "--child", "--config", key, "--steps", str(args.steps),
                "--warmup", str(args.warmup), "--no-cpu-baseline", "--extra-configs", "none"]
         if p:
             cmd += ["--top-p", p]
+        if layout:
+            cmd += ["--pool-layout", layout]
         t0 = time.perf_counter()
         r = subprocess.run(cmd, capture_output=True, text=True, timeout=300)
         wall = time.perf_counter() - t0
@@ -670,15 +746,35 @@ def run_extras(args):
         d = json.loads(r.stdout.strip().splitlines()[-1])
         rf = d["roofline"]
         out.append({"workload": d["config"]["workload"], "top_p": d["config"]["top_p"],
+                    "pool_layout": d["config"]["pool_layout"], "pool_bytes": d["pool_bytes"],
                     "ms_per_step": d["ms_per_step"], "steps_per_s": d["value"],
                     "kv_tokens_scanned_per_s": d["kv_tokens_scanned_per_s"],
                     "algorithmic_bytes_per_step": d["algorithmic_bytes_per_step"],
                     "step_hbm_GBps": d["step_hbm_GBps"], "step_hbm_frac": d["step_hbm_frac"],
                     "dominant_kernel": rf["kernel"], "dominant_GBps": rf["achieved"], "dominant_frac": rf["frac"],
+                    "copy_reference": rf.get("copy_reference"),
                     "stage_us": d["stage_us"], "timing": d["config"]["timing"], "wall_s": round(wall, 1)})
         print(f"bench: {spec} {d['ms_per_step']:.4f} ms/step, step {d['step_hbm_frac']:.3f} of HBM peak "
               f"({wall:.0f} s)", file=sys.stderr, flush=True)
     return out
+
+
+def shared_pool_summary(extras):
+    """The shared block pool beside the rings on the same workload and p (the first such pair
+    among the extra workloads): pool memory, and the score, rewrite and step times."""
+    for sh in extras:
+        if sh["pool_layout"] != "shared":
+            continue
+        for rg in extras:
+            if rg["pool_layout"] == "ring" and rg["workload"] == sh["workload"] and rg["top_p"] == sh["top_p"]:
+                def pair(x, y):
+                    return {"ring": x, "shared": y, "shared_over_ring": y / x if x else None}
+                return {"workload": sh["workload"], "top_p": sh["top_p"],
+                        "pool_bytes": pair(rg["pool_bytes"], sh["pool_bytes"]),
+                        "score_us": pair(rg["stage_us"]["score"], sh["stage_us"]["score"]),
+                        "rewrite_attend_us": pair(rg["stage_us"]["rewrite_attend"], sh["stage_us"]["rewrite_attend"]),
+                        "ms_per_step": pair(rg["ms_per_step"], sh["ms_per_step"])}
+    return None
 
 
 def run_policies(args):
@@ -772,7 +868,8 @@ def main():
         horizon = args.mti_horizon if args.mti_horizon >= 0 else R - 1
         L = Layer(wl, layer, nsteps, top_p=top_p,
                   policy=(args.regularize, args.mti_lower, args.mti_upper, horizon),
-                  view=(args.view_layout, args.view_total), calibration=args.calibration)
+                  view=(args.view_layout, args.view_total), calibration=args.calibration,
+                  pool_layout=args.pool_layout)
         if layer == 0 and not args.no_cpu_baseline:
             L.inp_cpu_source = {"k_ctx": L.inp.k_ctx, "v_ctx": L.inp.v_ctx, "ctx_len": L.inp.ctx_len}
         else:
@@ -924,6 +1021,7 @@ def main():
                    f"mti [{args.mti_lower}, {args.mti_upper}]",
                    "mti_horizon": horizon if args.regularize == "mti-auto" else None,
                    "view_layout": args.view_layout, "calibration": args.calibration,
+                   "pool_layout": args.pool_layout,
                    "timing": ("one-step graph replay from the prefilled state" if restore_mode else
                               "graph of the K streaming steps") + (" (eager)" if args.eager else "")},
         "kv_tokens_scanned_per_s": scanned_step * steps_per_s,
@@ -935,8 +1033,11 @@ def main():
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
                      "bytes_per_launch": dom_bytes_launch, "us_per_launch": stage_us[dom],
-                     "copy_reference": device_copy_reference(dom_bytes_launch)},
+                     "copy_reference": gather_copy_reference(layers[0])},
         "graph_replay_matches_eager": replay_matches,
+        # device bytes of the pools' K and V (all layers): the rings' worst case, or the
+        # shared pool sized for the prefilled lengths
+        "pool_bytes": sum(L.pool_bytes for L in layers),
     }
     if R > 1:
         res["select_every"] = select_every(layers, R, restore_mode, snaps if restore_mode else snap_after, Wm, K,
@@ -950,6 +1051,7 @@ def main():
         res["cpu_baseline"] = cpu_baseline(wl, layers, args.cpu_units, args.cpu_seconds)
     if extras:
         res["configs"] = extras
+        res["shared_pool"] = shared_pool_summary(extras)
     if policies:
         res["policies"] = policies
     print(json.dumps(res))

@@ -109,22 +109,35 @@ HK_DEV void condense_chain(const Args &a, int bh, int i, int64_t c, int64_t E, i
 // After the slots: the cursor (MERGE) and the pool head move past the E condensed blocks.
 // In the shared pool the condensed blocks go back to the free list (their table entries
 // stay: nothing reads a ring block outside the pool, and the append that reuses the ring
-// block sets it again).
+// block sets it again).  Called by all 64 lanes of one wavefront: lane 0 moves the counters,
+// the lanes return the blocks 64 at a time.
 HK_DEV void condense_advance(const Args &a, int bh, int64_t c, int64_t E, int32_t nu) {
-  if (a.mode == HARDKV_COND_MERGE) a.cond_cursor[bh] = (int32_t)((nu + E) % a.C);
-  a.pool_head[bh] = c + (int64_t)BK * E;
+  const int lane = threadIdx.x & 63;
+  if (lane == 0) {
+    if (a.mode == HARDKV_COND_MERGE) a.cond_cursor[bh] = (int32_t)((nu + E) % a.C);
+    a.pool_head[bh] = c + (int64_t)BK * E;
+  }
   if (a.pool_shared && E > 0) {
     // (a block the pool never got, after an overflow, has no entry to return)
     const int32_t *tb = a.btab + (size_t)bh * a.P;
+    const int64_t blk0 = c / BK;
     int32_t n = 0;
-    for (int64_t e = 0; e < E; ++e) n += tb[(c / BK + e) % a.P] >= 0 ? 1 : 0;
-    const int32_t at = atomicAdd(a.free_top, n);
+    for (int64_t e0 = 0; e0 < E; e0 += 64) {
+      const int64_t e = e0 + lane;
+      const int32_t ph = e < E ? tb[(blk0 + e) % a.P] : -1;
+      n += __popcll(ballot(ph >= 0));
+    }
+    int32_t at = 0;
+    if (lane == 0) at = atomicAdd(a.free_top, n);
+    at = __shfl(at, 0);
     int32_t k = 0;
-    for (int64_t e = 0; e < E; ++e) {
-      const int32_t ph = tb[(c / BK + e) % a.P];
-      if (ph < 0) continue;
-      if (at + k < a.NB) a.free_list[at + k] = ph;
-      ++k;
+    for (int64_t e0 = 0; e0 < E; e0 += 64) {
+      const int64_t e = e0 + lane;
+      const int32_t ph = e < E ? tb[(blk0 + e) % a.P] : -1;
+      const uint64_t m = ballot(ph >= 0);
+      const int32_t slot = at + k + (int32_t)popc_below(m);
+      if (ph >= 0 && slot < a.NB) a.free_list[slot] = ph;
+      k += __popcll(m);
     }
   }
 }

@@ -20,8 +20,6 @@
 // In the fused step the kernel also runs the attention of the group's queries over the
 // rows it copies (one split-K partial per workgroup, so the view is never read back),
 // and extra workgroups attend the condensed slots and the dense window.
-#include <type_traits>
-
 #include "attn_common.h"
 
 namespace hardkv {
@@ -163,10 +161,10 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_rewrite(Args a) {
     // loads and stores completes in order).  Rows past the list read zeros and write
     // nothing (offset BUF_SKIP), and so does every store when the view is not written;
     // rows past the view's capacity are attended but fall outside the view buffers.
-    // source offsets: 32-bit into the unit's ring (BUF_SKIP for rows past the list), or, in
-    // the shared pool, 64-bit byte offsets of physical rows (rows past the list read a listed
-    // row, which nothing uses)
-    using SOff = typename std::conditional<SHARED, size_t, uint32_t>::type;
+    // source offsets: bytes into the unit's ring (BUF_SKIP for rows past the list), or, in
+    // the shared pool, physical rows, whose 64-bit address is formed at the load (rows past
+    // the list read a listed row, which nothing uses)
+    using SOff = uint32_t;
     SOff so[4];
     uint32_t dof[4];
     bool ac[4];
@@ -181,23 +179,29 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_rewrite(Args a) {
         uint32_t sv = s_src[wave][kk], dv = s_dst[wave][kk];
         asm volatile("" : "+v"(sv), "+v"(dv));
         if constexpr (SHARED)
-          o_s[j] = (size_t)sv * ROWB + lane_b;
+          o_s[j] = sv;
         else
           o_s[j] = o_a[j] ? sv * (uint32_t)ROWB + lane_b : BUF_SKIP;
         o_d[j] = (o_a[j] && store) ? dv * (uint32_t)ROWB + lane_b : BUF_SKIP;
       }
     };
     auto ldk = [&](SOff o, Raw8<T> &r) {
-      if constexpr (SHARED)
-        raw_load_nt((const char *)a.pool_k + o, r);
-      else
+      if constexpr (SHARED) {
+        size_t off = (size_t)o * ROWB + lane_b;
+        asm volatile("" : "+v"(off));  // formed here, not held from earlier
+        raw_load_nt((const char *)a.pool_k + off, r);
+      } else {
         buf_load_nt(pk, o, r);
+      }
     };
     auto ldv = [&](SOff o, Raw8<T> &r) {
-      if constexpr (SHARED)
-        raw_load_nt((const char *)a.pool_v + o, r);
-      else
+      if constexpr (SHARED) {
+        size_t off = (size_t)o * ROWB + lane_b;
+        asm volatile("" : "+v"(off));
+        raw_load_nt((const char *)a.pool_v + off, r);
+      } else {
         buf_load_nt(pv, o, r);
+      }
     };
     Raw8<T> kr[4], vr[4];
     // The pipeline holds the next batch's keys beside this batch's probabilities: with

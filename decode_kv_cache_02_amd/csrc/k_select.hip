@@ -136,7 +136,6 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_score(Args a) {
   const int P = a.P;
 
   __shared__ float s_sc[8 * BK];  // the chunk's scores (at most 8 blocks), stored at the end
-  __shared__ int32_t s_phys[8];   // the chunk's physical blocks (shared pool)
   __shared__ float s_wmax[4];
   __shared__ float s_ent[ENT ? 4 : 1][G][3];
   // entropy calibration: lane `sub` < G keeps query sub's softmax piece over its rows
@@ -183,15 +182,17 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_score(Args a) {
     const int pb0 = (int)((row_lo / BK) % P);
     const int nrows = (int)(row_hi - row_lo);
     const int ngroups = (nrows + 15) / 16;
-    const int nblk_c = (nrows + BK - 1) / BK;  // blocks of the chunk
+    const int nblk_c = (nrows + BK - 1) / BK;  // blocks of the chunk (at most 8)
+    // shared pool: lane i < nblk_c holds the physical block of the chunk's block i, read out
+    // by the wavefront for each batch (the batch's block is the same in every lane)
+    int32_t phys_lane = 0;
     if constexpr (SHARED) {
-      if (tid < nblk_c) {
-        int pb = pb0 + tid;
+      if (lane < nblk_c) {
+        int pb = pb0 + lane;
         pb = pb >= P ? pb - P : pb;
         const int32_t ph = a.btab[(size_t)bh * P + pb];
-        s_phys[tid] = ph < 0 ? 0 : ph;
+        phys_lane = ph < 0 ? 0 : ph;
       }
-      __syncthreads();
     }
     // Each wavefront takes row groups wave, wave + 4, ...; a batch is UNR of them
     // (UNR * 4 loads of 1 KB).  Two batches live in registers: the next batch's loads are
@@ -209,7 +210,8 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_score(Args a) {
             // a row of one of the chunk's blocks (rows past the chunk read a row of its last
             // block and are not kept)
             const int bi = min(gi >> 2, nblk_c - 1);
-            const size_t row = (size_t)s_phys[bi] * BK + (size_t)(rel & (BK - 1));
+            const uint32_t phys = (uint32_t)__builtin_amdgcn_readlane(phys_lane, bi);
+            const size_t row = (size_t)phys * BK + (size_t)(rel & (BK - 1));
             raw_load_nt((const char *)a.pool_k + row * (HD * EB) + lane_b, buf[u][l]);
           } else {
             // rows past the chunk read zeros (offset BUF_SKIP), with no branch
@@ -790,7 +792,7 @@ HK_DEV void select_condense(const Args &a, int bh, const SelGeo &g, int32_t nu, 
   if (a.mode == HARDKV_COND_MERGE)
     for (int i = wave; i < g.E && i < a.C; i += NW)
       condense_chain<T, Elem<T>::bytes == 2 ? 4 : 2, true>(a, bh, i, g.c, g.E, nu, W_all);
-  if (tid == 0) condense_advance(a, bh, g.c, g.E, nu);
+  if (wave == 0) condense_advance(a, bh, g.c, g.E, nu);
 }
 
 // The whole select stage of one head in one workgroup (pools up to SEL_SPLIT_MIN slices);

@@ -61,7 +61,7 @@ HK_DEV void raw_to_f_perm(const Raw8<F32> &r, float (&f)[8]) { raw_to_f(r, f); }
 // FUSED (only when every product is exact: 16-bit operands inside the safe magnitudes):
 // a level-1 node fl(fl(q0 k0) + fl(q1 k1)) is then one fused multiply-add on fl(q1 k1).
 template <bool FUSED>
-HK_DEV float dot_tree(const float (&q)[8], const float (&k)[8]) {
+HK_DEV float dot_lane(const float (&q)[8], const float (&k)[8]) {
   float a0, a1, a2, a3;
   if (FUSED) {
     a0 = __builtin_fmaf(q[0], k[0], q[1] * k[1]);
@@ -77,12 +77,24 @@ HK_DEV float dot_tree(const float (&q)[8], const float (&k)[8]) {
     a3 = p6 + p7;
   }
   float b0 = a0 + a1, b1 = a2 + a3;
-  float c = b0 + b1;                 // level 3: node `sub` of 16
-  c = c + dpp<DPP_XOR1>(c);          // level 4: nodes (2i, 2i+1) in lanes (2i, 2i+1)
-  c = c + dpp<DPP_XOR2>(c);          // level 5: lanes 4i..4i+3
-  c = c + dpp<DPP_HALF_MIRROR>(c);   // level 6: lanes 8i..8i+7
-  c = c + dpp<DPP_MIRROR>(c);        // level 7: all 16 lanes
-  return c;
+  return b0 + b1;                    // level 3: node `sub` of 16
+}
+
+// The G trees of one row: levels 1-3 in each lane, then levels 4-7 across the 16 lanes of
+// the row, one level for every query before the next (the DPP reads then never wait for
+// the instruction just before them).
+template <bool FUSED, int G>
+HK_DEV void dot_trees(const float (&q)[G][8], const float (&k)[8], float (&c)[G]) {
+#pragma unroll
+  for (int g = 0; g < G; ++g) c[g] = dot_lane<FUSED>(q[g], k);
+#pragma unroll
+  for (int g = 0; g < G; ++g) c[g] = c[g] + dpp<DPP_XOR1>(c[g]);         // level 4: nodes (2i, 2i+1)
+#pragma unroll
+  for (int g = 0; g < G; ++g) c[g] = c[g] + dpp<DPP_XOR2>(c[g]);         // level 5: lanes 4i..4i+3
+#pragma unroll
+  for (int g = 0; g < G; ++g) c[g] = c[g] + dpp<DPP_HALF_MIRROR>(c[g]);  // level 6: lanes 8i..8i+7
+#pragma unroll
+  for (int g = 0; g < G; ++g) c[g] = c[g] + dpp<DPP_MIRROR>(c[g]);       // level 7: all 16 lanes
 }
 
 HK_DEV float wave_max(float v) {
@@ -227,11 +239,13 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_score(Args a) {
     // hardware max (its choice between +0 and -0 vanishes in s + 0 below).
     auto group_dots = [&](const float (&kf)[8], float &dmine, auto fused) {
       constexpr bool FUSED = decltype(fused)::value;
-      float s = dot_tree<FUSED>(qf[0], kf);
+      float c[G];
+      dot_trees<FUSED, G>(qf, kf, c);
+      float s = c[0];
       dmine = s;
 #pragma unroll
       for (int g = 1; g < G; ++g) {
-        float d = dot_tree<FUSED>(qf[g], kf);
+        const float d = c[g];
         if (ENT && g == sub) dmine = d;
         s = FUSED ? __builtin_fmaxf(s, d) : (d > s ? d : s);
       }

@@ -123,6 +123,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU time over which the oracle step is timed")
     ap.add_argument("--copy-calib", type=int, default=0,
                     help="only run a device copy of this many MiB (counter calibration) and exit")
+    ap.add_argument("--summarize-counters", nargs="+", metavar="OUT_TXT COUNTER_CSV",
+                    help="summary of rocprofv3 --pmc runs: OUT_TXT then the counter_collection.csv files")
     ap.add_argument("--summarize-kernels", nargs=2, metavar=("KERNEL_STATS_CSV", "OUT_TXT"),
                     help="write a text summary of a rocprofv3 kernel_stats.csv and exit")
     ap.add_argument("--summarize-traffic", nargs=4,
@@ -552,7 +554,8 @@ def copy_calibration(mib):
 # ---- profile summaries -------------------------------------------------------------------
 KERNEL_STAGE = {"hardkv_rewrite": "rewrite_attend", "hardkv_score": "score", "hardkv_select": "select",
                 "hardkv_condense": "condense", "hardkv_append": "append", "hardkv_combine": "combine",
-                "hardkv_attend_tiers": "attend_tiers", "hardkv_prefill": "prefill"}
+                "hardkv_attend_tiers": "attend_tiers", "hardkv_prefill": "prefill",
+                "probe_one_shot": "copy_one_shot", "probe_loop": "copy_loop"}
 KERNEL_SOURCES = sorted(
     [os.path.join("decode_kv_cache_02_amd", "csrc", f)
      for f in os.listdir(os.path.join(ROOT, "decode_kv_cache_02_amd", "csrc"))
@@ -588,13 +591,68 @@ def summarize_kernels(src, dst, cmds, title):
     print(open(dst).read())
 
 
+def _short(name):
+    return (name.replace("void hardkv::(anonymous namespace)::", "").replace("hardkv::(anonymous namespace)::", "")
+            .replace("(hardkv::Args)", "").replace("hardkv::", "").replace("(anonymous namespace)::", ""))
+
+
+def summarize_counters(dst, srcs, cmds, title):
+    """Per kernel instance: dispatches, mean duration and the mean of every counter per
+    dispatch over the counter runs (rocprofv3 --pmc CSVs), with derived ratios whose
+    formulas are printed beside them."""
+    import csv
+    import collections
+    acc = collections.defaultdict(lambda: collections.defaultdict(list))
+    dur = collections.defaultdict(dict)
+    for src in srcs:
+        for r in csv.DictReader(open(src)):
+            name = _short(r["Kernel_Name"])
+            if kernel_key(r["Kernel_Name"]) is None:
+                continue
+            key = (src, r["Dispatch_Id"])
+            acc[name][r["Counter_Name"]].append(float(r["Counter_Value"]))
+            dur[name][key] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+    xcd, simds = 8, 1024
+    with open(dst, "w") as f:
+        f.write(f"# {title}\n\nCommands (repository root R, one MI355X; each counter set in its own run):\n\n")
+        for c in cmds:
+            f.write(f"    {c}\n")
+        f.write("\nMeans per dispatch (durations are those of the counter runs, which serialise dispatches).\n"
+                "Derived: clock GHz = GRBM_GUI_ACTIVE / 8 XCDs / duration; VALU busy = SQ_ACTIVE_INST_VALU x 4 /\n"
+                "(1024 SIMDs x GRBM_GUI_ACTIVE / 8); VALU instr per wave = SQ_INSTS_VALU / SQ_WAVES; TA busy =\n"
+                "TA_BUSY_avr / (GRBM_GUI_ACTIVE / 8).\n\n")
+        for name in sorted(acc, key=lambda n: -np.mean(list(dur[n].values()))):
+            c = {k: float(np.mean(v)) for k, v in acc[name].items()}
+            d = float(np.mean(list(dur[name].values())))
+            f.write(f"## {name}\n\ndispatches {len(dur[name])}, mean duration {d:.2f} us\n\n")
+            for k in sorted(c):
+                f.write(f"    {k:<26} {c[k]:>18.1f}\n")
+            gui = c.get("GRBM_GUI_ACTIVE")
+            der = []
+            if gui:
+                der.append(("clock GHz", gui / xcd / (d * 1e3)))
+                if "SQ_ACTIVE_INST_VALU" in c:
+                    der.append(("VALU busy", c["SQ_ACTIVE_INST_VALU"] * 4 / (simds * gui / xcd)))
+                if "TA_BUSY_avr" in c:
+                    der.append(("TA busy", c["TA_BUSY_avr"] / (gui / xcd)))
+            if c.get("SQ_WAVES") and "SQ_INSTS_VALU" in c:
+                der.append(("VALU instr per wave", c["SQ_INSTS_VALU"] / c["SQ_WAVES"]))
+            if der:
+                f.write("\n")
+                for k, v in der:
+                    f.write(f"    {k:<26} {v:>18.3f}\n")
+            f.write("\n")
+    print(open(dst).read())
+
+
 def run_options(args, wl):
     """The options that change what the kernels of a run do: counter traffic taken under
     one set of them is reported only for runs with the same set."""
     return {"top_p": args.top_p, "regularize": args.regularize,
             "mti": [args.mti_lower, args.mti_upper] if args.regularize == "mti" else None,
             "calibration": args.calibration, "view_layout": args.view_layout,
-            "view_total": args.view_total if args.view_layout == "sum" else None, "sink": wl.sink}
+            "view_total": args.view_total if args.view_layout == "sum" else None, "sink": wl.sink,
+            "pool_layout": args.pool_layout, "select_every": max(1, args.select_every)}
 
 
 def summarize_traffic(fetch_csv, write_csv, cal_fetch_csv, cal_write_csv, calib_mib, wl, cmds, options):
@@ -833,6 +891,10 @@ def main():
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); this build has no multi-GPU path.",
               file=sys.stderr)
         sys.exit(2)
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters[0], args.summarize_counters[1:], args.cmd,
+                           f"Counters, workload {get_workload(args.config).name}")
+        return
     if args.summarize_kernels:
         summarize_kernels(*args.summarize_kernels, args.cmd, f"Kernel trace, workload {get_workload(args.config).name}")
         return

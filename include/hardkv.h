@@ -355,7 +355,8 @@ int32_t hardkv_step_noalloc(const hardkv_config *cfg, hardkv_state *st, const vo
  * stream while decode steps continue on the current one (hardkv_step_reuse), and switched in
  * at a later step.  It takes a second state, st_next, that shares the cache itself with the
  * current one (dense_k/v, pool_k/v, sink_k/v, cond_kn/vn/omega/n, cond_cursor, seq_len,
- * pool_head: the same pointers) and has its own selection buffers (scores, weights, mask,
+ * pool_head, and the SHARED pool's block_table, free_list and free_top: the same pointers)
+ * and has its own selection buffers (scores, weights, mask,
  * budget, n_condense, w_all, w_u, thresh, view_k/v, view_pos, regularized, tau_fit) and its
  * own workspace; otherwise HARDKV_EINVAL.
  *   1. hardkv_select_fork(cfg, st_next, st_cur, s_main): on the main stream, right after the

@@ -236,6 +236,35 @@ class Layer:
             getattr(self.st, n).copy_(snap[n])
 
 
+def in_step_stage_times(layers, restore, timed, reps):
+    """Each kernel's cost inside the step, in us per layer: the step as its six kernels
+    (hardkv_step_stage 0..5 for every layer, one graph) against the same graph without
+    kernel k, both replayed from the restored state, interleaved, `reps` times; the
+    difference of the medians.  Beside the back-to-back durations of stage_us, this keeps
+    each kernel between the kernels it really follows and precedes (a kernel that keeps
+    the vector ALUs busy runs at a lower clock when repeated back to back)."""
+    graphs = {}
+    for skip in [None] + list(range(len(STAGE_NAMES))):
+        restore()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for L in layers:
+                for j in range(len(STAGE_NAMES)):
+                    if j != skip:
+                        L.stage(0, j)
+        graphs[skip] = g
+    times = {k: [] for k in graphs}
+    for _ in range(max(5, reps)):
+        for k, g in graphs.items():
+            restore()
+            torch.cuda.synchronize()
+            times[k].append(timed(g.replay))
+    full = float(np.median(times[None]))
+    return {STAGE_NAMES[k]: round((full - float(np.median(times[k]))) * 1e3 / len(layers), 2)
+            for k in range(len(STAGE_NAMES))}
+
+
 def time_repeatable_stage(layers, s, k, reps, eager):
     """Duration per launch of a kernel that only reads what earlier kernels wrote: `reps`
     launches per layer back to back, captured into one graph (eagerly with --eager) and
@@ -811,7 +840,8 @@ def run_extras(args):
                     "step_hbm_GBps": d["step_hbm_GBps"], "step_hbm_frac": d["step_hbm_frac"],
                     "dominant_kernel": rf["kernel"], "dominant_GBps": rf["achieved"], "dominant_frac": rf["frac"],
                     "copy_reference": rf.get("copy_reference"),
-                    "stage_us": d["stage_us"], "timing": d["config"]["timing"], "wall_s": round(wall, 1)})
+                    "stage_us": d["stage_us"], "stage_us_in_step": d.get("stage_us_in_step"),
+                    "timing": d["config"]["timing"], "wall_s": round(wall, 1)})
         print(f"bench: {spec} {d['ms_per_step']:.4f} ms/step, step {d['step_hbm_frac']:.3f} of HBM peak "
               f"({wall:.0f} s)", file=sys.stderr, flush=True)
     return out
@@ -949,6 +979,7 @@ def main():
         return e0.elapsed_time(e1)
 
     stage_us = {}
+    stage_in_step = None
     if restore_mode:
         # the workload is one decode step from the prefilled context: capture that step,
         # then replay it K times, each from the restored state
@@ -990,6 +1021,8 @@ def main():
                 stage_us[STAGE_NAMES[k]] = time_repeatable_stage(layers, 0, k, args.stage_reps, args.eager)
             else:
                 stage_us[STAGE_NAMES[k]] = layers[0].time_mutating_stage(0, k, args.stage_reps)
+        if not args.quick and not args.eager:
+            stage_in_step = in_step_stage_times(layers, restore, timed, K)
         restore()
         torch.cuda.synchronize()
         snap_after = snaps
@@ -1091,6 +1124,7 @@ def main():
         "step_hbm_GBps": algo_step / (ms_per_step * 1e-3) / 1e9,
         "step_hbm_frac": algo_step / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
         "stage_us": {k: round(v, 2) for k, v in stage_us.items()},
+        "stage_us_in_step": stage_in_step,
         "stage_algorithmic_bytes": {k: round(v) for k, v in bytes_step.items()},
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,

@@ -584,7 +584,11 @@ def copy_calibration(mib):
 KERNEL_STAGE = {"hardkv_rewrite": "rewrite_attend", "hardkv_score": "score", "hardkv_select": "select",
                 "hardkv_condense": "condense", "hardkv_append": "append", "hardkv_combine": "combine",
                 "hardkv_attend_tiers": "attend_tiers", "hardkv_prefill": "prefill",
-                "probe_one_shot": "copy_one_shot", "probe_loop": "copy_loop"}
+                "probe_one_shot": "copy_one_shot", "probe_loop": "copy_loop",
+                "hardkv_fit": "select", "hardkv_fit_prep": "select", "hardkv_fit_round": "select",
+                "hardkv_fit_final": "select", "hardkv_sel_weigh": "select", "hardkv_sel_cut": "select",
+                "hardkv_sel_count": "select", "hardkv_sel_finish": "select", "hardkv_flatten": "select",
+                "hardkv_fork": "select", "hardkv_prefill_alloc": "prefill", "hardkv_prefill_clear": "prefill"}
 KERNEL_SOURCES = sorted(
     [os.path.join("decode_kv_cache_02_amd", "csrc", f)
      for f in os.listdir(os.path.join(ROOT, "decode_kv_cache_02_amd", "csrc"))
@@ -649,7 +653,8 @@ def summarize_counters(dst, srcs, cmds, title):
         f.write("\nMeans per dispatch (durations are those of the counter runs, which serialise dispatches).\n"
                 "Derived: clock GHz = GRBM_GUI_ACTIVE / 8 XCDs / duration; VALU busy = SQ_ACTIVE_INST_VALU x 4 /\n"
                 "(1024 SIMDs x GRBM_GUI_ACTIVE / 8); VALU instr per wave = SQ_INSTS_VALU / SQ_WAVES; TA busy =\n"
-                "TA_BUSY_avr / (GRBM_GUI_ACTIVE / 8).\n\n")
+                "TA_BUSY_avr / (GRBM_GUI_ACTIVE / 8).  GRBM_GUI_ACTIVE also counts the dispatch around the\n"
+                "kernel, so the clock reads high for kernels shorter than a few tens of us.\n\n")
         for name in sorted(acc, key=lambda n: -np.mean(list(dur[n].values()))):
             c = {k: float(np.mean(v)) for k, v in acc[name].items()}
             d = float(np.mean(list(dur[name].values())))

@@ -320,6 +320,8 @@ PACKED_CASES = {
     "evict_f32": (dict(dtype="f32", steps=2), 0),
     "mti_batch16": (dict(batch=16, cond_mode=COND_MERGE, ctx_len=500, ctx_min=100, heavy=(0, 6), steps=2), 2),
     "g8_sparse": (dict(num_q_heads=16, num_kv_heads=2, steps=2), 1),
+    # the memory-time controller packs only the heads it rewrites
+    "mti_auto_batch16": (dict(batch=16, cond_mode=COND_MERGE, ctx_len=500, ctx_min=100, heavy=(0, 6), steps=2), 3),
 }
 
 
@@ -336,7 +338,8 @@ def test_packed_views_parity(name, fused):
     lo, hi = _mti_bounds(wl) if pol == 2 else (0, 0)
     total = wl.batch * wl.num_kv_heads * wl.V_cap
     print(f"case {name} fused={fused}: policy {pol}, {total} packed rows, {wl}", flush=True)
-    pr = Pair(wl, regularize=pol, mti_lower=lo, mti_upper=hi, view_layout=1, view_total=total)
+    mti = _mti_auto_costs(wl) if pol == 3 else None
+    pr = Pair(wl, regularize=pol, mti_lower=lo, mti_upper=hi, view_layout=1, view_total=total, mti=mti)
     for _ in range(steps):
         pr.step(fused=fused)
 

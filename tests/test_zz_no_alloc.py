@@ -72,6 +72,36 @@ def test_noalloc_16k_layer_then_a_tiny_one():
     _run_pair(LAYERS[1][1])
 
 
+def test_noalloc_over_a_shared_pool():
+    """The no-alloc step over the shared block pool: the same outputs and selection state as
+    hardkv_step (the pools' physical blocks may be taken in another order, so the pool
+    arrays are compared through the outputs)."""
+    from decode_kv_cache_02_amd import hardkv as hk
+    wl = tiny_workload(batch=6, num_q_heads=16, num_kv_heads=4, cond_mode=COND_MERGE, ctx_len=900, ctx_min=300,
+                       sparse_cap=256, condensed_slots=3, steps=3)
+    print(f"shared pool: {wl}", flush=True)
+    dev = "cuda:0"
+    inp = make_inputs(wl, device=dev)
+    nb = hk.hardkv_shared_pool_blocks(hk.Config.from_workload(wl), inp.ctx_len.cpu(), wl.steps)
+    cfg = hk.Config.from_workload(wl, pool_layout=hk.HARDKV_POOL_SHARED, pool_total_blocks=nb)
+    ref, na = hk.State(cfg, device=dev), hk.State(cfg, device=dev)
+    for st in (ref, na):
+        hk.hardkv_prefill(cfg, st, inp.k_ctx, inp.v_ctx, inp.ctx_len)
+    o_ref = torch.zeros((wl.batch, wl.num_q_heads, wl.head_dim), dtype=torch.float32, device=dev)
+    o_na = torch.full_like(o_ref, float("nan"))
+    for s in range(wl.steps):
+        hk.hardkv_step(cfg, ref, inp.q[s], inp.k_new[s], inp.v_new[s], o_ref)
+        hk.hardkv_step_noalloc(cfg, na, inp.q[s], inp.k_new[s], inp.v_new[s], o_na)
+        torch.cuda.synchronize()
+        assert _same(o_ref, o_na), f"output differs at step {s}"
+        for n in STATE:
+            if n in ("pool_k", "pool_v"):
+                continue
+            assert _same(getattr(ref, n), getattr(na, n)), f"{n} differs at step {s}"
+        assert int(ref.free_top[0].item()) == int(na.free_top[0].item())
+    assert int(ref.error_word[0].item()) == 0
+
+
 def test_noalloc_rejects_a_step_beyond_its_scratch():
     from decode_kv_cache_02_amd import hardkv as hk
     import ctypes as C

@@ -402,11 +402,17 @@ def pipeline_every(layers, R, lag, restore_mode, snaps, Wm, timed, eager, mode="
                         hk.hardkv_select_ahead(L.cfg, nxt[j], L.inp.q[s], side)
                     done = torch.cuda.Event()
                     done.record(side)
-            if mode == "spread" and k < lag:  # part k of the units, behind this step
-                for j, L in enumerate(layers):
-                    n = L.cfg.c.batch * L.cfg.c.num_kv_heads
-                    u0, u1 = k * n // lag, (k + 1) * n // lag
-                    hk.hardkv_select_ahead(L.cfg, nxt[j], L.inp.q[q_fork], main, u0, u1 - u0)
+            if mode == "spread" and k < lag:  # part k of the selection, behind this step
+                nl = len(layers)
+                if nl >= lag:  # whole layers per part (every launch as wide as the step's)
+                    for j in range(k * nl // lag, (k + 1) * nl // lag):
+                        L = layers[j]
+                        hk.hardkv_select_ahead(L.cfg, nxt[j], L.inp.q[q_fork], main)
+                else:  # a range of every layer's units per part
+                    for j, L in enumerate(layers):
+                        n = L.cfg.c.batch * L.cfg.c.num_kv_heads
+                        u0, u1 = k * n // lag, (k + 1) * n // lag
+                        hk.hardkv_select_ahead(L.cfg, nxt[j], L.inp.q[q_fork], main, u0, u1 - u0)
                 done = "spread"
             mark()
         if done is not None and done != "spread":
@@ -436,8 +442,9 @@ def pipeline_every(layers, R, lag, restore_mode, snaps, Wm, timed, eager, mode="
     ms_step = float(np.mean(times)) / len(steps)
     return {"R": R, "lag": lag, "mode": mode, "ms_per_step": ms_step, "steps_per_s": 1e3 / ms_step,
             "error_word": err, "eager_step_latency": lat,
-            "timing": "graph of two periods of R steps, each selection made ahead on a second stream and "
-                      "switched in lag steps later"}
+            "timing": "graph of two periods of R steps, each selection made ahead " +
+                      ("on a second stream" if mode == "side" else
+                       f"in {lag} parts behind the steps before the switch") + ", switched in lag steps later"}
 
 
 def device_copy_reference(nbytes, reps=10):

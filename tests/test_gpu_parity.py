@@ -169,16 +169,23 @@ def test_determinism_and_fused_equals_composition():
         assert row_rel_err(x.cpu().numpy(), y.cpu().numpy()) < 1e-5
 
 
+@pytest.mark.parametrize("layout", ["ring", "shared"])
 @pytest.mark.parametrize("batch", [2, 16])
-def test_graph_replay_matches_eager(batch):
+def test_graph_replay_matches_eager(batch, layout):
     """hardkv_step captured once in a HIP graph (with static input buffers) and replayed
     for several steps, with eager copies and synchronizations between the replays, gives
-    bitwise the state and output of the eager calls (I15)."""
+    bitwise the state and output of the eager calls (I15).  In the shared pool the blocks
+    may be taken from the free list in another order, so its pool, table and list are
+    compared through everything computed from them (and the free count)."""
     from decode_kv_cache_02_amd import hardkv as hk
     from synth import make_inputs
     wl = tiny_workload(batch=batch, steps=4, cond_mode=COND_MERGE, ctx_len=500, ctx_min=100)
     inp = make_inputs(wl, device="cuda")
     cfg = hk.Config.from_workload(wl)
+    if layout == "shared":
+        nb = hk.hardkv_shared_pool_blocks(cfg, inp.ctx_len.cpu(), wl.steps)
+        cfg = hk.Config.from_workload(wl, pool_layout=hk.HARDKV_POOL_SHARED, pool_total_blocks=nb)
+    physical = ("pool_k", "pool_v", "block_table", "free_list") if layout == "shared" else ()
     ref, gst = hk.State(cfg), hk.State(cfg)
     for st in (ref, gst):
         hk.hardkv_prefill(cfg, st, inp.k_ctx, inp.v_ctx, inp.ctx_len)
@@ -199,7 +206,7 @@ def test_graph_replay_matches_eager(batch):
         torch.cuda.synchronize()
         assert torch.equal(out_ref, out_g), s
         for n, t in ref.tensors().items():
-            if n == "workspace":
+            if n == "workspace" or n in physical:
                 continue
             assert torch.equal(t, getattr(gst, n)), (s, n)
 

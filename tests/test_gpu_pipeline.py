@@ -180,3 +180,74 @@ def test_switch_at_once_equals_the_step():
         hk.hardkv_step_reuse(cfg, nxt, inp.q[s], inp.k_new[s], inp.v_new[s], out_c)
         torch.cuda.synchronize()
         assert torch.equal(out_r, out_c), s
+
+
+def _two_periods(hk, cfg, cur, nxt, inp, steps, outs, main, side, R, lag):
+    """Two periods of R steps that reuse the current selection; at the first step of each the
+    next selection is forked and made ahead on the side stream, switched in `lag` steps
+    later (the states swap roles at each switch)."""
+    done = None
+    for i, s in enumerate(steps):
+        k = i % R
+        if k == lag and done is not None:
+            main.wait_event(done)
+            hk.hardkv_condense(cfg, nxt, main)
+            cur, nxt = nxt, cur
+            done = None
+        hk.hardkv_step_reuse(cfg, cur, inp.q[s], inp.k_new[s], inp.v_new[s], outs[i], main)
+        if k == 0:
+            hk.hardkv_select_fork(cfg, nxt, cur, main)
+            ev = torch.cuda.Event()
+            ev.record(main)
+            side.wait_event(ev)
+            hk.hardkv_select_ahead(cfg, nxt, inp.q[s], side)
+            done = torch.cuda.Event()
+            done.record(side)
+    if done is not None:
+        main.wait_event(done)
+    return cur, nxt
+
+
+@pytest.mark.parametrize("layout", ["ring", "shared"])
+def test_pipeline_captured_in_a_graph(layout):
+    """Two pipelined periods (fork, selection ahead on a second stream, switch) captured in
+    one HIP graph with the cross-stream waits and replayed give the eager run's outputs at
+    every step and its state bit for bit."""
+    from decode_kv_cache_02_amd import hardkv as hk
+    from synth import make_inputs
+    R, lag = 3, 2
+    wl = tiny_workload(batch=4, cond_mode=COND_MERGE, ctx_len=600, ctx_min=100, steps=1 + 2 * R)
+    inp = make_inputs(wl, device="cuda")
+    cfg = hk.Config.from_workload(wl)
+    if layout == "shared":
+        nb = hk.hardkv_shared_pool_blocks(cfg, inp.ctx_len.cpu(), wl.steps)
+        cfg = hk.Config.from_workload(wl, pool_layout=hk.HARDKV_POOL_SHARED, pool_total_blocks=nb)
+    physical = ("pool_k", "pool_v", "block_table", "free_list") if layout == "shared" else ()
+    shape = (wl.batch, wl.num_q_heads, wl.head_dim)
+    runs = []
+    for _ in range(2):
+        st = hk.State(cfg)
+        hk.hardkv_prefill(cfg, st, inp.k_ctx, inp.v_ctx, inp.ctx_len)
+        first = torch.zeros(shape, dtype=torch.float32, device="cuda")
+        hk.hardkv_step(cfg, st, inp.q[0], inp.k_new[0], inp.v_new[0], first)  # the selection to start from
+        runs.append((st, st.twin(), [torch.zeros(shape, dtype=torch.float32, device="cuda") for _ in range(2 * R)]))
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    steps = list(range(1, 1 + 2 * R))
+    (ea, eb, eouts), (ga, gb, gouts) = runs
+    _two_periods(hk, cfg, ea, eb, inp, steps, eouts, torch.cuda.current_stream(), side, R, lag)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        _two_periods(hk, cfg, ga, gb, inp, steps, gouts, torch.cuda.current_stream(), side, R, lag)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    for i in range(2 * R):
+        assert torch.equal(eouts[i], gouts[i]), f"step {i}"
+    for e, gg in ((ea, ga), (eb, gb)):
+        for n, t in e.tensors().items():
+            if n == "workspace" or n in physical:
+                continue
+            assert torch.equal(t, getattr(gg, n)), n
+    assert int(ea.error_word[0].item()) == 0

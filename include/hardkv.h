@@ -159,7 +159,10 @@ typedef enum { HARDKV_VIEW_MAXLEN = 0, HARDKV_VIEW_SUM = 1 } hardkv_view_layout;
  *           starts a new one; a condensation returns the blocks it condenses.  Memory then
  *           follows what the pools hold instead of B * Hkv worst-case rings; pool_blocks stays
  *           the per-unit ring (the table's length).  An append or prefill that finds the free
- *           list empty sets HARDKV_ERR_POOL_OVERFLOW and writes nothing. */
+ *           list empty sets HARDKV_ERR_POOL_OVERFLOW and writes nothing.  The prefill writes
+ *           the table and the free list (they need no initialisation); which free block an
+ *           append takes depends on the order of the appends' atomics, every result does
+ *           not.  hardkv_shared_pool_blocks sizes a pool that cannot overflow. */
 typedef enum { HARDKV_POOL_RING = 0, HARDKV_POOL_SHARED = 1 } hardkv_pool_layout;
 
 /* Logits Calibration temperature (section 2.B calibrates the scores by the temperature of

@@ -622,7 +622,7 @@ int32_t hardkv_mti_thresholds(const hardkv_config *cfg, int64_t n_survivors, int
 int32_t hardkv_shared_pool_blocks(const hardkv_config *cfg, const int64_t *ctx_len, int64_t steps,
                                   int64_t *blocks) {
   Plan p;
-  if (!cfg || !ctx_len || !blocks || steps < 0) return HARDKV_EINVAL;
+  if (!cfg || !ctx_len || !blocks || steps < 0 || steps > ((int64_t)1 << 40)) return HARDKV_EINVAL;
   const int32_t rc = plan(cfg, p);
   if (rc != HARDKV_OK) return rc;
   int64_t total = 0;

@@ -405,7 +405,8 @@ const char *hardkv_step_stage_name(int32_t stage);
  * `steps` appends with no condensation: per unit, the blocks that cover its pool
  * [S, max(S, L + steps - W)), at most pool_blocks, summed over num_kv_heads heads per sequence.
  * A pool of that many blocks never overflows over those steps; a condensation only returns
- * blocks.  HARDKV_EINVAL on a bad config, a null pointer, a negative length or step count. */
+ * blocks.  HARDKV_EINVAL on a bad config, a null pointer, or a length or step count outside
+ * [0, 2^40]. */
 int32_t hardkv_shared_pool_blocks(const hardkv_config *cfg, const int64_t *ctx_len, int64_t steps,
                                   int64_t *blocks);
 

@@ -295,6 +295,7 @@ def test_shared_pool_blocks_by_hand():
     sunk = hk.Config.from_workload(wl, sink=64)
     # with 64 sink positions the pool starts at 64: L = W + 64 holds none, W + 65 one block
     assert hk.hardkv_shared_pool_blocks(sunk, [W + 64, W + 65, W + 64 + 64, W + 65 + 64, 0], 0) == (0 + 1 + 1 + 2) * 3
-    for bad in (([1, 2, 3, 4, -1], 0), ([1, 2, 3, 4, 5], -1)):
+    for bad in (([1, 2, 3, 4, -1], 0), ([1, 2, 3, 4, 5], -1), ([1, 2, 3, 4, 5], (1 << 40) + 1),
+                ([1, 2, 3, 4, (1 << 40) + 1], 0)):
         with pytest.raises(hk.HardKVError):
             hk.hardkv_shared_pool_blocks(cfg, *bad)

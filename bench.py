@@ -30,7 +30,7 @@ Timing:
     and written contiguously): one 16-byte piece per thread, wavefronts that loop over 64
     rows with the next batch in flight (the pattern a kernel that also consumes the rows
     must take), and a plain device copy of the same bytes; the rates a kernel that reads
-    and writes equally can practically reach on the box, beside the 8 TB/s peak.
+    and writes equally can practically reach on this part, beside the 8 TB/s peak.
   * Algorithmic bytes per step follow the byte model of the design notes and are
     computed from the per-unit pool sizes, budgets and condensed blocks of the
     timed steps, replayed eagerly from a snapshot after the timed region.
@@ -930,7 +930,7 @@ def run_policies(args):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for {args.gpus}); this build has no multi-GPU path.",
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}); the library has no multi-GPU path.",
               file=sys.stderr)
         sys.exit(2)
     if args.summarize_counters:

@@ -570,7 +570,15 @@ static uint32_t unit_step(const orc_cfg *cfg, orc_state *st, int b, int h, const
   for (int g = 0; g < G; ++g)
     for (int d = 0; d < D; ++d) qg[g * D + d] = elem_get(q, ((int64_t)b * Hq + h * G + g) * D + d, eb);
 
-  /* score */
+  /* the rows still in play: all of them, or with destructive selection the rows the last
+   * selection kept and the positions that arrived since it (read before this selection
+   * replaces the mask) */
+  const int64_t psel = st->pend_sel[u];
+  uint8_t *live = (uint8_t *)malloc((size_t)(N > 0 ? N : 1));
+  for (int64_t j = c; j < pend; ++j)
+    live[j - c] = cfg->selection == 0 || j >= psel || ((st->mask[u * P + (j / BK) % P] >> (j % BK)) & 1u);
+
+  /* score; the calibration's maximum is over the rows in play */
   float *krow = (float *)malloc(sizeof(float) * (size_t)D);
   float m = -INFINITY;
   for (int64_t j = c; j < pend; ++j) {
@@ -579,7 +587,7 @@ static uint32_t unit_step(const orc_cfg *cfg, orc_state *st, int b, int h, const
     float s = orc_score_row(qg, G, krow, D);
     if (!isfinite(s)) err |= ORC_ERR_NONFINITE;
     st->scores[r] = s;
-    if (s > m) m = s;
+    if (live[j - c] && s > m) m = s;
   }
 
   /* calibrate over the whole pool */
@@ -608,7 +616,8 @@ static uint32_t unit_step(const orc_cfg *cfg, orc_state *st, int b, int h, const
   uint64_t w_all = 0, w_u = 0;
   for (int64_t j = c; j < pend; ++j) {
     int64_t r = pool_row(cfg, u, j);
-    uint32_t w = orc_weight(st->scores[r], m, kappa);
+    /* a dropped row weighs nothing: it is in no mass, never kept and never merged */
+    uint32_t w = live[j - c] ? orc_weight(st->scores[r], m, kappa) : 0u;
     st->weights[r] = w;
     w_all += w;
     if (j >= u0) w_u += w;
@@ -675,8 +684,11 @@ static uint32_t unit_step(const orc_cfg *cfg, orc_state *st, int b, int h, const
       int32_t sigma = st->cond_cursor[u];
       st->cond_cursor[u] = (sigma + 1) % C;
       int64_t si = u * C + sigma;
+      int32_t nlive = 0;  /* the block's rows still in play (all 64 unless dropped) */
       for (int64_t j = c + BK * e; j < c + BK * (e + 1); ++j) {
         int64_t rr = pool_row(cfg, u, j);
+        if (st->weights[rr] == 0) continue;
+        ++nlive;
         double om = (double)st->weights[rr] / (double)w_all;
         st->cond_omega[si] += om;
         for (int d = 0; d < D; ++d) {
@@ -684,7 +696,7 @@ static uint32_t unit_step(const orc_cfg *cfg, orc_state *st, int b, int h, const
           st->cond_vn[si * D + d] += om * (double)elem_get(st->pool_v, rr * D + d, eb);
         }
       }
-      st->cond_n[si] += BK;
+      st->cond_n[si] += nlive;
     }
   }
   if (!ahead) st->pool_head[u] = c + BK * E;
@@ -720,6 +732,7 @@ static uint32_t unit_step(const orc_cfg *cfg, orc_state *st, int b, int h, const
     free(tc);
   }
   free(qg);
+  free(live);
   free(krow);
   free(wU);
   free(pU);
@@ -887,6 +900,7 @@ int32_t orc_select_ahead(const orc_cfg *cfg, orc_state *st, const void *q) {
   const int B = cfg->batch, H = cfg->num_kv_heads;
   uint32_t err = 0;
   if (cfg->view_layout == 1) return -2; /* packed views are written by orc_step only */
+  if (cfg->selection != 0) return -2;   /* a selection ahead of its use keeps views only */
   for (int64_t i = 0; i < (int64_t)B * H; ++i) err |= unit_step(cfg, st, (int)(i / H), (int)(i % H), q, NULL, 0, 1);
   st->error_word |= err;
   return 0;

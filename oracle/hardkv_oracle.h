@@ -69,6 +69,10 @@ typedef struct {
   uint32_t mti_c_gather[9];  /* a later step gathering the row from the pool, by the kept
                                 eighth of the survivors: floor(8 k* / N_U) */
   int64_t mti_fixed;         /* per rewritten head and selection */
+  int32_t selection;         /* 0: each selection picks a view of the whole pool; 1: destructive:
+                                a selection drops for good the survivors it does not keep, so the
+                                next one chooses among the rows it kept and the positions that
+                                arrived since (the whole pool before the first) */
 } orc_cfg;
 
 typedef struct {

@@ -34,7 +34,12 @@ class OrcCfg(C.Structure):
         ("mti_horizon", C.c_int32), ("mti_c_view", C.c_uint32), ("mti_c_write", C.c_uint32),
         ("mti_c_scan", C.c_uint32), ("mti_c_hold", C.c_uint32), ("mti_c_score", C.c_uint32),
         ("mti_c_gather", C.c_uint32 * 9), ("mti_fixed", C.c_int64),
+        ("selection", C.c_int32),
     ]
+
+# selection modes: a view of the whole pool at every selection, or destructive (a selection
+# drops for good the survivors it does not keep)
+SEL_VIEW, SEL_DESTRUCTIVE = 0, 1
 
 MTI_FIELDS = ("mti_horizon", "mti_c_view", "mti_c_write", "mti_c_scan", "mti_c_hold", "mti_c_score",
               "mti_c_gather", "mti_fixed")
@@ -254,7 +259,7 @@ class Oracle:
                  top_p: Optional[float] = None, regularize: int = 0, mti_lower: int = 0,
                  mti_upper: int = 0, view_layout: int = 0, view_total: int = 0,
                  calibration: int = 0, tau_unit: Optional[np.ndarray] = None,
-                 mti: Optional[dict] = None):
+                 mti: Optional[dict] = None, selection: int = SEL_VIEW):
         self.wl = wl
         B, H, Hq, D = wl.batch, wl.num_kv_heads, wl.num_q_heads, wl.head_dim
         W, P, V, Cs = wl.dense_window, wl.P_blk, wl.V_cap, wl.condensed_slots
@@ -267,6 +272,11 @@ class Oracle:
                           int(mti_lower), int(mti_upper), int(view_layout), int(view_total),
                           int(calibration), None, int(getattr(wl, "sink", 0)))
         set_mti(self.cfg, mti)
+        if selection not in (SEL_VIEW, SEL_DESTRUCTIVE):
+            raise ValueError(f"selection mode {selection}")
+        if selection == SEL_DESTRUCTIVE and calibration != 0:
+            raise ValueError("destructive selection takes a fixed temperature")
+        self.cfg.selection = int(selection)
         self.tau_unit = None
         if tau_unit is not None:
             self.tau_unit = np.ascontiguousarray(np.asarray(tau_unit, np.float32).ravel())

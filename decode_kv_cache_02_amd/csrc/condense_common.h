@@ -33,15 +33,15 @@ HK_DEV void condense_chain(const Args &a, int bh, int i, int64_t c, int64_t E, i
 #pragma unroll
   for (int k = 0; k < 8; ++k) ak[k] = av[k] = 0.0f;
   uint64_t wsum = 0;
-  int nblk = 0;
+  int nlive = 0;  // rows merged: those with a weight (all 64 of a block unless dropped)
   for (int64_t e = i; e < E; e += C) {
-    ++nblk;
     const size_t pb = (size_t)((c / BK + e) % P);
     const size_t row0 = pool_row0(a, bh, (int)pb);
     const char *kb = (const char *)a.pool_k + row0 * ROWB + sub * 8 * EB;
     const char *vb = (const char *)a.pool_v + row0 * ROWB + sub * 8 * EB;
     const uint32_t wl = a.weights[((size_t)bh * P + pb) * BK + lane];  // weight of row `lane`
     wsum += wl;
+    nlive += __popcll(ballot(wl != 0u));
     constexpr int UNB = LEAN ? 1 : 16 / NB;
 #pragma unroll UNB
     for (int bt = 0; bt < 16 / NB; ++bt) {
@@ -82,7 +82,7 @@ HK_DEV void condense_chain(const Args &a, int bh, int i, int64_t c, int64_t E, i
     wsum += ((uint64_t)hi << 32) | lo;
   }
   const double wa = (double)w_all;
-  const float inv = (float)(1.0 / wa);
+  const float inv = w_all ? (float)(1.0 / wa) : 0.0f;  // (no mass: every row dropped, nothing merged)
   if (lane < 16) {
     float4 *kn = reinterpret_cast<float4 *>(a.cond_kn + sg * HD + sub * 8);
     float4 *vn = reinterpret_cast<float4 *>(a.cond_vn + sg * HD + sub * 8);
@@ -101,8 +101,8 @@ HK_DEV void condense_chain(const Args &a, int bh, int i, int64_t c, int64_t E, i
     kn[0] = k0; kn[1] = k1; vn[0] = v0; vn[1] = v1;
   }
   if (lane == 0) {
-    a.cond_omega[sg] = (fresh ? 0.0f : a.cond_omega[sg]) + (float)((double)wsum / wa);
-    a.cond_n[sg] += BK * nblk;
+    a.cond_omega[sg] = (fresh ? 0.0f : a.cond_omega[sg]) + (w_all ? (float)((double)wsum / wa) : 0.0f);
+    a.cond_n[sg] += nlive;
   }
 }
 

@@ -117,6 +117,8 @@ int32_t plan(const hardkv_config *cfg, Plan &p) {
   if (cfg->calibration != HARDKV_CAL_FIXED && cfg->calibration != HARDKV_CAL_ENTROPY) return HARDKV_EINVAL;
   if (cfg->sink < 0 || cfg->sink % BK || cfg->sink > HARDKV_MAX_SINK) return HARDKV_EINVAL;
   if (cfg->pool_layout != HARDKV_POOL_RING && cfg->pool_layout != HARDKV_POOL_SHARED) return HARDKV_EINVAL;
+  if (cfg->selection != HARDKV_SEL_VIEW && cfg->selection != HARDKV_SEL_DESTRUCTIVE) return HARDKV_EINVAL;
+  if (cfg->selection == HARDKV_SEL_DESTRUCTIVE && cfg->calibration != HARDKV_CAL_FIXED) return HARDKV_EUNSUPPORTED;
   if (cfg->pool_layout == HARDKV_POOL_SHARED && (cfg->pool_total_blocks < 1 || cfg->pool_total_blocks >= (1 << 26)))
     return HARDKV_EINVAL;
 
@@ -136,6 +138,7 @@ int32_t plan(const hardkv_config *cfg, Plan &p) {
   a.calibration = cfg->calibration;
   a.view_rows = a.view_sum ? (int64_t)cfg->view_total
                            : (int64_t)cfg->batch * cfg->num_kv_heads * cfg->view_cap;
+  a.destructive = cfg->selection == HARDKV_SEL_DESTRUCTIVE ? 1 : 0;
   a.pool_shared = cfg->pool_layout == HARDKV_POOL_SHARED ? 1 : 0;
   a.NB = a.pool_shared ? cfg->pool_total_blocks : 0;
   a.reg_policy = cfg->regularize;
@@ -496,6 +499,9 @@ int32_t hardkv_step_noalloc(const hardkv_config *cfg, hardkv_state *st, const vo
   if (rc != HARDKV_OK) return rc;
   if (!st) return HARDKV_EINVAL;
   if (p.ws_bytes > (size_t)HARDKV_STATIC_SCRATCH_BYTES) return HARDKV_ESCRATCH;
+  // (a destructive selection reads the last selection's plan, which the shared scratch does
+  // not keep)
+  if (p.a.destructive) return HARDKV_EUNSUPPORTED;
   if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(out)) return HARDKV_EINVAL;
   // the state's own buffers, with the library's scratch in place of its workspace; the
   // pointer checks of bind() run on a stand-in address first, so that a bad state is
@@ -552,6 +558,7 @@ int32_t hardkv_select_fork(const hardkv_config *cfg, hardkv_state *st_next, cons
   if (rc != HARDKV_OK) return rc;
   rc = check_pipeline_pair(st_next, st_cur);
   if (rc != HARDKV_OK) return rc;
+  if (p.a.destructive) return HARDKV_EUNSUPPORTED;
   p.a.kx_src = pc.a.kx;
   return hip_status(launch_fork(p.a, (hipStream_t)stream));
 }
@@ -561,7 +568,7 @@ int32_t hardkv_select_ahead(const hardkv_config *cfg, hardkv_state *st_next, con
   Plan p;
   int32_t rc = setup(cfg, st_next, p);
   if (rc != HARDKV_OK) return rc;
-  if (p.a.view_sum) return HARDKV_EUNSUPPORTED;
+  if (p.a.view_sum || p.a.destructive) return HARDKV_EUNSUPPORTED;
   if (!aligned16(q)) return HARDKV_EINVAL;
   if (unit_begin < 0 || unit_count < 0 || (int64_t)unit_begin + unit_count > (int64_t)p.a.B * p.a.Hkv)
     return HARDKV_EINVAL;

@@ -107,6 +107,9 @@ struct Args {
   // 64 rows; btab maps ring block pb of unit bh to its physical block (-1: none); the free
   // blocks are free_list[0 .. *free_top)
   int pool_shared, NB;
+  // destructive selection: a pool row is in play iff it arrived after the last selection
+  // (at or past the pool end of its plan) or that selection kept it (its mask bit)
+  int destructive;
   int32_t *btab, *free_list, *free_top;
   int64_t *tsnap;     // [B] t of the step a selection made ahead is for (the pipeline)
   const uint32_t *kx_src;  // the current state's kx, copied by the pipeline's fork
@@ -365,6 +368,14 @@ HK_DEV size_t pool_row0(const Args &a, int bh, int pb) {
     return (size_t)(phys < 0 ? 0 : phys) * BK;
   }
   return ((size_t)bh * a.P + pb) * BK;
+}
+
+// Destructive selection: the pool end when the last selection ran (positions from here on
+// arrived since), read before this step's selection replaces the plan; and whether position
+// p of a block whose mask word is mw is in play.
+HK_DEV int64_t pend_last_selection(const Args &a, int bh) { return pool_end(a.head[bh].t_plan, a.W, a.S); }
+HK_DEV bool in_play(int64_t p, int64_t pend_last, uint64_t mw) {
+  return p >= pend_last || ((mw >> (p & (BK - 1))) & 1ull) != 0ull;
 }
 
 HK_DEV int64_t plan_E(int64_t N, int mode, int S_cap) {

@@ -302,14 +302,17 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_score(Args a) {
       g0 += 2 * STEP;
     }
     if (nb & 1) score(bufA, g0);
-    // the chunk's scores leave in one pass: wavefront w writes blocks w, w + 4, ...
+    // the chunk's scores leave in one pass: wavefront w writes blocks w, w + 4, ...; the
+    // chunk's maximum is over the rows in play (destructive selection: not the dropped ones)
     __syncthreads();
+    const int64_t pend_last = a.destructive ? pend_last_selection(a, bh) : 0;
     for (int rel = tid; rel < nrows; rel += NTHREADS) {
       int pb = pb0 + (rel >> 6);
       pb = pb >= P ? pb - P : pb;
       const float s = s_sc[rel];
       srow[pb * BK + (rel & (BK - 1))] = s;
-      wmax = s > wmax ? s : wmax;
+      const bool live = !a.destructive || in_play(row_lo + rel, pend_last, a.mask[(size_t)bh * P + pb]);
+      wmax = (live && s > wmax) ? s : wmax;
     }
   }
   wmax = wave_max(wmax);
@@ -480,6 +483,7 @@ HK_DEV uint32_t sum16(uint32_t v) {
 
 // The head's pool as the select stage sees it.
 struct SelGeo {
+  int bh;
   int64_t t, c, pend, E, u0;
   int nblk;   // pool blocks, at most P
   int nx;     // condensing blocks (they come first)
@@ -496,6 +500,7 @@ struct SelGeo {
 HK_DEV SelGeo sel_geo(const Args &a, int bh) {
   SelGeo g;
   const int b = bh / a.Hkv, h = bh - b * a.Hkv;
+  g.bh = bh;
   g.t = a.seq_len[b];
   g.c = a.pool_head[bh];
   g.pend = pool_end(g.t, a.W, a.S);
@@ -538,13 +543,18 @@ HK_DEV void sel_pass_a(const Args &a, const SelGeo &g, float m, int lo, int hi, 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int q4 = lane >> 4, r4 = (lane & 15) * 4;  // a load: block q4 of 4, rows r4 .. r4 + 3
   const int P = a.P;
+  // destructive selection: the rows in play are the last selection's kept rows (the mask
+  // words as it left them) and the positions since it; a dropped row weighs 0
+  const int64_t pend_last = a.destructive ? pend_last_selection(a, g.bh) : 0;
   for (int i0 = lo + wave * 4; i0 < hi; i0 += 4 * NW * UA) {
     float4 sv[UA];
+    uint64_t mw[UA];
 #pragma unroll
     for (int u = 0; u < UA; ++u) {
       const int i = i0 + u * 4 * NW + q4;
       sv[u] = i < hi ? *reinterpret_cast<const float4 *>(a.scores + g.rowbase + (size_t)g.ring(i, P) * BK + r4)
                      : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      mw[u] = (a.destructive && i < hi) ? a.mask[(size_t)g.bh * P + g.ring(i, P)] : 0ull;
     }
 #pragma unroll
     for (int u = 0; u < UA; ++u) {
@@ -557,9 +567,10 @@ HK_DEV void sel_pass_a(const Args &a, const SelGeo &g, float m, int lo, int hi, 
         for (int k = 0; k < 4; ++k) {
           const bool valid = p + k < g.pend;
           bad |= valid && !isfinite(s4[k]);
-          w4[k] = valid ? calib_weight(s4[k], m, g.kap, a.coeff) : 0u;
+          const bool live = !a.destructive || in_play(p + k, pend_last, mw[u]);
+          w4[k] = (valid && live) ? calib_weight(s4[k], m, g.kap, a.coeff) : 0u;
           my_all += w4[k];
-          if (valid && i >= g.nx) {
+          if (valid && live && i >= g.nx) {
             my_u += w4[k];
             atomicAdd(&sh.hist[wkey(w4[k]) >> 16], (unsigned long long)w4[k]);
           }
@@ -604,7 +615,8 @@ HK_DEV void sel_pass_b(const Args &a, int bh, const SelGeo &g, int b1, int jlo, 
       uint32_t n_above = 0;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const bool valid = j < jhi && p + k < g.pend;
+        // (a row dropped by a destructive selection weighs 0 and has no key)
+        const bool valid = j < jhi && p + k < g.pend && w4[k] != 0u;
         const uint32_t key = wkey(w4[k]);
         const int kb = (int)(key >> 16);
         n_above += (valid && kb > b1) ? 1u : 0u;
@@ -824,8 +836,10 @@ __global__ __launch_bounds__(SEL_THREADS) void hardkv_select(Args a) {
 
   for (int i = tid; i < NB1; i += SEL_THREADS) sh.hist[i] = 0ull;
   if (tid == 0) sh.ncand = 0;
-  // every mask word starts empty; the rewrite kernel writes the survivor blocks' words
-  for (int i = tid; i < P; i += SEL_THREADS) a.mask[(size_t)bh * P + i] = 0ull;
+  // every mask word starts empty; the rewrite kernel writes the survivor blocks' words (a
+  // destructive selection reads the last selection's words in pass A first)
+  if (!a.destructive)
+    for (int i = tid; i < P; i += SEL_THREADS) a.mask[(size_t)bh * P + i] = 0ull;
   const float m = sel_max(a, bh, sh);  // (its barrier also orders the clears above)
 
   uint64_t my_all = 0, my_u = 0;
@@ -834,6 +848,8 @@ __global__ __launch_bounds__(SEL_THREADS) void hardkv_select(Args a) {
   if (ballot(bad) && lane == 0) atomicOr(a.error_word, HARDKV_ERR_NONFINITE);
   const uint64_t W_all = block_sum_u64(my_all, sh, 0);
   const uint64_t W_U = block_sum_u64(my_u, sh, 1);
+  if (a.destructive)  // (after the barriers above: every thread's pass A has read its words)
+    for (int i = tid; i < P; i += SEL_THREADS) a.mask[(size_t)bh * P + i] = 0ull;
   const uint64_t Tm = ((uint64_t)a.pq * W_U + 65535ull) >> 16;
   uint64_t R1 = 0;
   int b1 = 0;
@@ -864,7 +880,8 @@ __global__ __launch_bounds__(SEL_THREADS) void hardkv_sel_weigh(Args a) {
 
   for (int i = tid; i < NB1; i += SEL_THREADS) sh.hist[i] = 0ull;
   const int zs = (P + a.nsp - 1) / a.nsp;
-  for (int i = slice * zs + tid; i < min(P, (slice + 1) * zs); i += SEL_THREADS) a.mask[(size_t)bh * P + i] = 0ull;
+  if (!a.destructive)  // (a destructive selection's words are read by every slice: the cut clears them)
+    for (int i = slice * zs + tid; i < min(P, (slice + 1) * zs); i += SEL_THREADS) a.mask[(size_t)bh * P + i] = 0ull;
   if (slice == 0 && tid == 0) a.selh[bh].ncand = 0u;
   const float m = sel_max(a, bh, sh);
 
@@ -911,6 +928,8 @@ __global__ __launch_bounds__(SEL_THREADS) void hardkv_sel_cut(Args a) {
   const int tid = threadIdx.x;
   extern __shared__ unsigned char smem_raw[];
   SelShared &sh = *reinterpret_cast<SelShared *>(smem_raw);
+  if (a.destructive)  // every slice has read the last selection's words
+    for (int i = tid; i < a.P; i += SEL_THREADS) a.mask[(size_t)bh * a.P + i] = 0ull;
   uint64_t W_all, W_U;
   sel_masses(a, bh, W_all, W_U);
   const uint64_t T = ((uint64_t)a.pq * W_U + 65535ull) >> 16;

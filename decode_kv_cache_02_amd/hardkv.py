@@ -28,6 +28,7 @@ MTI_DEFAULT = dict(mti_horizon=0, mti_c_view=97000, mti_c_write=68000, mti_c_sca
                    mti_c_score=44000, mti_c_gather=[124000] * 9, mti_fixed=0)
 HARDKV_VIEW_MAXLEN, HARDKV_VIEW_SUM = 0, 1
 HARDKV_POOL_RING, HARDKV_POOL_SHARED = 0, 1
+HARDKV_SEL_VIEW, HARDKV_SEL_DESTRUCTIVE = 0, 1
 HARDKV_CAL_FIXED, HARDKV_CAL_ENTROPY = 0, 1
 HARDKV_ERR_POOL_OVERFLOW, HARDKV_ERR_VIEW_OVERFLOW, HARDKV_ERR_NONFINITE = 1, 2, 4
 BLOCK, HEAD_DIM = 64, 128
@@ -59,7 +60,7 @@ class hardkv_config(C.Structure):
         ("mti_horizon", C.c_int32), ("mti_c_view", C.c_uint32), ("mti_c_write", C.c_uint32),
         ("mti_c_scan", C.c_uint32), ("mti_c_hold", C.c_uint32), ("mti_c_score", C.c_uint32),
         ("mti_c_gather", C.c_uint32 * 9), ("mti_fixed", C.c_int64),
-        ("pool_layout", C.c_int32), ("pool_total_blocks", C.c_int32),
+        ("pool_layout", C.c_int32), ("pool_total_blocks", C.c_int32), ("selection", C.c_int32),
     ]
 
 
@@ -155,7 +156,8 @@ class Config:
                  regularize: int = HARDKV_REG_REWRITE, mti_lower: int = 0, mti_upper: int = 0,
                  view_layout: int = HARDKV_VIEW_MAXLEN, view_total: int = 0,
                  calibration: int = HARDKV_CAL_FIXED, sink: int = 0, mti: Optional[dict] = None,
-                 pool_layout: int = HARDKV_POOL_RING, pool_total_blocks: int = 0):
+                 pool_layout: int = HARDKV_POOL_RING, pool_total_blocks: int = 0,
+                 selection: int = HARDKV_SEL_VIEW):
         self.tau_arr = (C.c_float * max(1, len(tau)))(*[float(x) for x in tau])
         self.c = hardkv_config(batch, num_q_heads, num_kv_heads, head_dim,
                                HARDKV_BF16 if dtype == "bf16" else HARDKV_F32, dense_window,
@@ -170,6 +172,7 @@ class Config:
             setattr(self.c, k, (C.c_uint32 * 9)(*[int(x) for x in v]) if k == "mti_c_gather" else int(v))
         self.c.pool_layout = int(pool_layout)
         self.c.pool_total_blocks = int(pool_total_blocks)
+        self.c.selection = int(selection)
         self.dtype = dtype
 
     @classmethod
@@ -178,7 +181,8 @@ class Config:
                       mti_lower: int = 0, mti_upper: int = 0, view_layout: int = HARDKV_VIEW_MAXLEN,
                       view_total: int = 0, calibration: int = HARDKV_CAL_FIXED,
                       sink: Optional[int] = None, mti: Optional[dict] = None,
-                      pool_layout: int = HARDKV_POOL_RING, pool_total_blocks: int = 0) -> "Config":
+                      pool_layout: int = HARDKV_POOL_RING, pool_total_blocks: int = 0,
+                      selection: int = HARDKV_SEL_VIEW) -> "Config":
         return cls(wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.dtype, wl.dense_window, wl.P_blk,
                    wl.sparse_cap, wl.V_cap, wl.condensed_slots,
                    wl.cond_mode if cond_mode is None else cond_mode,
@@ -188,7 +192,7 @@ class Config:
                    mti_lower=mti_lower, mti_upper=mti_upper, view_layout=view_layout,
                    view_total=view_total, calibration=calibration,
                    sink=int(getattr(wl, "sink", 0)) if sink is None else int(sink), mti=mti,
-                   pool_layout=pool_layout, pool_total_blocks=pool_total_blocks)
+                   pool_layout=pool_layout, pool_total_blocks=pool_total_blocks, selection=selection)
 
     def __getattr__(self, name):
         return getattr(self.__dict__["c"], name)

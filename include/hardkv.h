@@ -164,6 +164,22 @@ typedef enum { HARDKV_VIEW_MAXLEN = 0, HARDKV_VIEW_SUM = 1 } hardkv_view_layout;
  *           append takes depends on the order of the appends' atomics, every result does
  *           not.  hardkv_shared_pool_blocks sizes a pool that cannot overflow. */
 typedef enum { HARDKV_POOL_RING = 0, HARDKV_POOL_SHARED = 1 } hardkv_pool_layout;
+/* What a selection does to the survivors it does not keep (section 2.A: the sparse tier
+ * retains the tokens the calibrated top-p selects; the pages leave open whether the others
+ * are gone for good):
+ *   VIEW         nothing: every selection chooses among the whole pool (default);
+ *   DESTRUCTIVE  they are dropped for good: the next selection chooses among the rows the
+ *                last one kept and the positions that arrived since it (the whole pool
+ *                before the first selection after a prefill).  Dropped rows keep their pool
+ *                rows but take no part: the calibration maximum is over the rows in play, a
+ *                dropped row weighs 0 (weights[] holds 0; it is in no mass, never kept), and
+ *                a condensation merges only the rows in play (a block adds their count to
+ *                n; one with none adds nothing).  Selections run when the caller takes
+ *                hardkv_step (hardkv_step_reuse between them keeps the last one), so with a
+ *                selection every step the tier shrinks towards what top-p keeps of a few
+ *                arrivals.  With p = 1 it is VIEW.  Needs the FIXED calibration, and is not
+ *                taken by the pipeline calls or hardkv_step_noalloc (HARDKV_EUNSUPPORTED). */
+typedef enum { HARDKV_SEL_VIEW = 0, HARDKV_SEL_DESTRUCTIVE = 1 } hardkv_selection_mode;
 
 /* Logits Calibration temperature (section 2.B calibrates the scores by the temperature of
  * the attention scores without fixing how it is obtained):
@@ -223,6 +239,7 @@ typedef struct {
   int64_t mti_fixed;       /* F per rewritten head, in [0, HARDKV_MTI_MAX_FIXED] */
   int32_t pool_layout;     /* hardkv_pool_layout (0: RING) */
   int32_t pool_total_blocks; /* NB, physical blocks of the SHARED pool, in [1, 2^26) */
+  int32_t selection;       /* hardkv_selection_mode (0: VIEW) */
 } hardkv_config;
 
 /* Device buffers of one layer.  All fixed capacity; 16-byte aligned.
@@ -349,7 +366,9 @@ int32_t hardkv_step_reuse(const hardkv_config *cfg, hardkv_state *st, const void
  *     stepped by this call lacks that record in its own workspace afterwards: keep stepping
  *     it with this call (or prefill it again) rather than with the calls that read the
  *     workspace (hardkv_step, hardkv_step_reuse, hardkv_regularize, hardkv_condense,
- *     hardkv_attend, hardkv_attend_sparse). */
+ *     hardkv_attend, hardkv_attend_sparse).
+ *   - A DESTRUCTIVE selection reads the last selection's plan, which the array does not keep:
+ *     HARDKV_EUNSUPPORTED. */
 int32_t hardkv_step_noalloc(const hardkv_config *cfg, hardkv_state *st, const void *q, const void *k_new,
                             const void *v_new, float *out, void *stream);
 

@@ -47,14 +47,15 @@ class Pair:
 
     def __init__(self, wl, inputs=None, top_p=None, tau=None, cond_mode=None, merge_bias=True,
                  device="cuda", oracle_units=None, layer=0, regularize=0, mti_lower=0, mti_upper=0,
-                 view_layout=0, view_total=0, make_state=None, mti=None, pool_layout=0, pool_total_blocks=0):
+                 view_layout=0, view_total=0, make_state=None, mti=None, pool_layout=0, pool_total_blocks=0,
+                 selection=0):
         self.wl = wl if cond_mode is None else wl.with_(cond_mode=cond_mode)
         if top_p is not None:
             self.wl = self.wl.with_(top_p=top_p)
         self.inp = inputs if inputs is not None else make_inputs(self.wl, layer=layer, device=device)
         self.tau = [self.wl.tau] * self.wl.num_kv_heads if tau is None else list(tau)
         pol = dict(regularize=regularize, mti_lower=mti_lower, mti_upper=mti_upper,
-                   view_layout=view_layout, view_total=view_total)
+                   view_layout=view_layout, view_total=view_total, selection=selection)
         self.packed = view_layout == hk.HARDKV_VIEW_SUM
         assert not (self.packed and oracle_units is not None), "packed views need the whole layer"
         # the memory-time controller's inputs (policy MTI_AUTO), the same on both sides

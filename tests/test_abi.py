@@ -72,6 +72,8 @@ def _cfg(**over):
     (dict(pool_layout=2), hk.HARDKV_EINVAL),
     (dict(pool_layout=hk.HARDKV_POOL_SHARED, pool_total_blocks=0), hk.HARDKV_EINVAL),
     (dict(pool_layout=hk.HARDKV_POOL_SHARED, pool_total_blocks=1 << 26), hk.HARDKV_EINVAL),
+    (dict(selection=2), hk.HARDKV_EINVAL),
+    (dict(selection=hk.HARDKV_SEL_DESTRUCTIVE, calibration=hk.HARDKV_CAL_ENTROPY), hk.HARDKV_EUNSUPPORTED),
     (dict(view_layout=2), hk.HARDKV_EINVAL),
     (dict(view_layout=1, view_total=-1), hk.HARDKV_EINVAL),
     (dict(calibration=2), hk.HARDKV_EINVAL),
@@ -299,3 +301,21 @@ def test_shared_pool_blocks_by_hand():
                 ([1, 2, 3, 4, (1 << 40) + 1], 0)):
         with pytest.raises(hk.HardKVError):
             hk.hardkv_shared_pool_blocks(cfg, *bad)
+
+
+@_no_gpu
+def test_destructive_selection_is_not_taken_by_the_pipeline_or_the_noalloc_step():
+    """A destructive selection reads the last selection's plan and mask: the calls that make a
+    selection ahead of its use, and the step whose scratch keeps nothing between calls, refuse
+    it before anything is enqueued."""
+    cfg = _cfg(selection=hk.HARDKV_SEL_DESTRUCTIVE)
+    L = hk.lib()
+    ok = C.c_void_p(1 << 41)
+    a, b = _fake_state(cfg), _fake_state(cfg)
+    for n in ("view_k", "view_v", "view_pos", "scores", "weights", "mask", "budget", "n_condense", "w_all", "w_u",
+              "thresh", "regularized", "view_off", "tau_fit", "workspace"):
+        setattr(b, n, getattr(b, n) + (1 << 36))  # its own selection buffers, the shared cache
+    assert L.hardkv_select_fork(C.byref(cfg.c), C.byref(b), C.byref(a), None) == hk.HARDKV_EUNSUPPORTED
+    assert L.hardkv_select_ahead(C.byref(cfg.c), C.byref(b), ok, 0, 1, None) == hk.HARDKV_EUNSUPPORTED
+    st = _fake_state(cfg, null="workspace", ws_bytes=0)
+    assert L.hardkv_step_noalloc(C.byref(cfg.c), C.byref(st), ok, ok, ok, ok, None) == hk.HARDKV_EUNSUPPORTED

@@ -65,7 +65,8 @@ STAGE_NAMES = ["append", "score", "select", "condense", "rewrite_attend", "combi
 REPEATABLE = [1, 2, 4, 5]  # stages that only read what earlier stages wrote
 # the workloads measured beside the headline: the three target workloads (the mixed-length
 # one at each p of its sweep, and at p = 0.9 in the shared block pool) and the streaming one
-EXTRA_DEFAULT = "c1,c2,c3:0.8,c3:0.9,c3:0.99,c3:0.9:shared,c4"
+# (also with destructive selection); a spec is workload[:p[:pool layout[:selection]]]
+EXTRA_DEFAULT = "c1,c2,c3:0.8,c3:0.9,c3:0.99,c3:0.9:shared,c4,c4:::destructive"
 POLICY_DEFAULT = "c2,c4,c5"
 
 
@@ -113,6 +114,8 @@ def parse():
     ap.add_argument("--pool-layout", choices=["ring", "shared"], default="ring",
                     help="the pool: a ring per (sequence, KV head), or the shared block pool sized for the "
                          "prefilled lengths")
+    ap.add_argument("--selection", choices=["view", "destructive"], default="view",
+                    help="what a selection does to the survivors it does not keep: nothing, or drop them for good")
     ap.add_argument("--select-every", type=int, default=1,
                     help="also time steps that select once every R steps and reuse the selection in "
                          "between (hardkv_step_reuse), reported under select_every; the pool ring gets "
@@ -134,7 +137,10 @@ def parse():
                          "summary, then exits")
     ap.add_argument("--cmd", action="append", default=[], help="command recorded in a summary")
     ap.add_argument("--child", action="store_true", help=argparse.SUPPRESS)
-    return ap.parse_args()
+    args = ap.parse_args()
+    if args.selection == "destructive" and (args.calibration == "entropy" or args.pipeline):
+        ap.error("--selection destructive needs the fixed temperature and no --pipeline")
+    return args
 
 
 # ---- layers ------------------------------------------------------------------------------
@@ -147,14 +153,15 @@ POLICY = {"rewrite": hk.HARDKV_REG_REWRITE, "sparse": hk.HARDKV_REG_SPARSE, "mti
 
 class Layer:
     def __init__(self, wl, layer, steps, top_p=None, policy=("rewrite", 0, 0, 0), view=("maxlen", 0),
-                 calibration="fixed", pool_layout="ring"):
+                 calibration="fixed", pool_layout="ring", selection="view"):
         self.wl = wl
         self.inp = make_inputs(wl, layer=layer, device="cuda", steps=steps)
         total = view[1] or wl.batch * wl.num_kv_heads * wl.V_cap
         kw = dict(top_p=top_p, regularize=POLICY[policy[0]], mti_lower=policy[1], mti_upper=policy[2],
                   mti=dict(mti_horizon=policy[3]),
                   view_layout=hk.HARDKV_VIEW_SUM if view[0] == "sum" else hk.HARDKV_VIEW_MAXLEN, view_total=total,
-                  calibration=hk.HARDKV_CAL_ENTROPY if calibration == "entropy" else hk.HARDKV_CAL_FIXED)
+                  calibration=hk.HARDKV_CAL_ENTROPY if calibration == "entropy" else hk.HARDKV_CAL_FIXED,
+                  selection=hk.HARDKV_SEL_DESTRUCTIVE if selection == "destructive" else hk.HARDKV_SEL_VIEW)
         self.cfg = hk.Config.from_workload(wl, **kw)
         self.shared = pool_layout == "shared"
         if self.shared:
@@ -554,8 +561,25 @@ def unit_bytes(wl, N, kstar, E, t, c_occ, rw):
     }
 
 
+def rows_in_play(L, c, pend):
+    """Per unit, the pool rows [c, pend) that the last selection weighed: every survivor, or
+    under destructive selection the rows in play (they all weigh at least 1)."""
+    wl = L.wl
+    P, BH = wl.P_blk, wl.batch * wl.num_kv_heads
+    dev = L.st.weights.device
+    c = torch.as_tensor(c.reshape(BH), device=dev)
+    pend = torch.as_tensor(np.broadcast_to(pend, (wl.batch, wl.num_kv_heads)).reshape(BH), device=dev)
+    ring = torch.arange(P * 64, device=dev)
+    blk_off = (ring[None, :] // 64 - ((c // 64) % P)[:, None]) % P
+    pos = c[:, None] + blk_off * 64 + ring[None, :] % 64
+    w = L.st.weights.reshape(BH, P * 64)
+    n = ((w != 0) & (pos < pend[:, None])).sum(1)
+    return n.cpu().numpy().astype(np.int64).reshape(wl.batch, wl.num_kv_heads)
+
+
 def step_accounting(layers, s):
-    """Runs step s of every layer eagerly and returns (bytes per stage, pool tokens scanned)."""
+    """Runs step s of every layer eagerly and returns (bytes per stage, pool tokens scanned).
+    Under destructive selection the score pass reads only the rows in play."""
     tot = {k: 0.0 for k in STAGE_NAMES}
     scanned = 0
     for L in layers:
@@ -563,9 +587,12 @@ def step_accounting(layers, s):
         t = L.st.seq_len.cpu().numpy().astype(np.int64)
         c = L.st.pool_head.cpu().numpy().astype(np.int64)
         t1 = (t + 1)[:, None]
-        N = np.maximum(wl.sink, t1 - wl.dense_window) - c
+        pend = np.maximum(wl.sink, t1 - wl.dense_window)
+        N = pend - c
         L.step(s)
         torch.cuda.synchronize()
+        if L.cfg.c.selection == hk.HARDKV_SEL_DESTRUCTIVE:
+            N = rows_in_play(L, c, pend)
         kstar = L.st.budget.cpu().numpy().astype(np.int64)
         E = L.st.n_condense.cpu().numpy().astype(np.int64)
         c_occ = (L.st.cond_n.cpu().numpy() > 0).sum(-1)
@@ -693,7 +720,8 @@ def run_options(args, wl):
             "mti": [args.mti_lower, args.mti_upper] if args.regularize == "mti" else None,
             "calibration": args.calibration, "view_layout": args.view_layout,
             "view_total": args.view_total if args.view_layout == "sum" else None, "sink": wl.sink,
-            "pool_layout": args.pool_layout, "select_every": max(1, args.select_every)}
+            "pool_layout": args.pool_layout, "select_every": max(1, args.select_every),
+            "selection": args.selection}
 
 
 def summarize_traffic(fetch_csv, write_csv, cal_fetch_csv, cal_write_csv, calib_mib, wl, cmds, options):
@@ -830,13 +858,16 @@ def run_extras(args):
         return out
     for spec in args.extra_configs.split(","):
         key, _, rest = spec.partition(":")
-        p, _, layout = rest.partition(":")
+        p, _, rest = rest.partition(":")
+        layout, _, selection = rest.partition(":")
         cmd = [sys.executable, os.path.abspath(__file__), "--child", "--config", key, "--steps", str(args.steps),
                "--warmup", str(args.warmup), "--no-cpu-baseline", "--extra-configs", "none"]
         if p:
             cmd += ["--top-p", p]
         if layout:
             cmd += ["--pool-layout", layout]
+        if selection:
+            cmd += ["--selection", selection]
         t0 = time.perf_counter()
         r = subprocess.run(cmd, capture_output=True, text=True, timeout=300)
         wall = time.perf_counter() - t0
@@ -845,7 +876,8 @@ def run_extras(args):
         d = json.loads(r.stdout.strip().splitlines()[-1])
         rf = d["roofline"]
         out.append({"workload": d["config"]["workload"], "top_p": d["config"]["top_p"],
-                    "pool_layout": d["config"]["pool_layout"], "pool_bytes": d["pool_bytes"],
+                    "pool_layout": d["config"]["pool_layout"], "selection": d["config"]["selection"],
+                    "pool_bytes": d["pool_bytes"],
                     "ms_per_step": d["ms_per_step"], "steps_per_s": d["value"],
                     "kv_tokens_scanned_per_s": d["kv_tokens_scanned_per_s"],
                     "algorithmic_bytes_per_step": d["algorithmic_bytes_per_step"],
@@ -866,7 +898,8 @@ def shared_pool_summary(extras):
         if sh["pool_layout"] != "shared":
             continue
         for rg in extras:
-            if rg["pool_layout"] == "ring" and rg["workload"] == sh["workload"] and rg["top_p"] == sh["top_p"]:
+            if (rg["pool_layout"] == "ring" and rg["workload"] == sh["workload"] and rg["top_p"] == sh["top_p"]
+                    and rg.get("selection") == sh.get("selection")):
                 def pair(x, y):
                     return {"ring": x, "shared": y, "shared_over_ring": y / x if x else None}
                 return {"workload": sh["workload"], "top_p": sh["top_p"],
@@ -973,7 +1006,7 @@ def main():
         L = Layer(wl, layer, nsteps, top_p=top_p,
                   policy=(args.regularize, args.mti_lower, args.mti_upper, horizon),
                   view=(args.view_layout, args.view_total), calibration=args.calibration,
-                  pool_layout=args.pool_layout)
+                  pool_layout=args.pool_layout, selection=args.selection)
         if layer == 0 and not args.no_cpu_baseline:
             L.inp_cpu_source = {"k_ctx": L.inp.k_ctx, "v_ctx": L.inp.v_ctx, "ctx_len": L.inp.ctx_len}
         else:
@@ -1128,7 +1161,7 @@ def main():
                    f"mti [{args.mti_lower}, {args.mti_upper}]",
                    "mti_horizon": horizon if args.regularize == "mti-auto" else None,
                    "view_layout": args.view_layout, "calibration": args.calibration,
-                   "pool_layout": args.pool_layout,
+                   "pool_layout": args.pool_layout, "selection": args.selection,
                    "timing": ("one-step graph replay from the prefilled state" if restore_mode else
                               "graph of the K streaming steps") + (" (eager)" if args.eager else "")},
         "kv_tokens_scanned_per_s": scanned_step * steps_per_s,

@@ -17,7 +17,10 @@
 //   group queries.  Writes the scores and the chunk's maximum.  With 16-bit elements
 //   every product is exact unless an element is tiny or huge; while the head's pool
 //   holds no such key and the queries none either, a level-1 node is one fused
-//   multiply-add (the same value, a fifth fewer vector instructions per row).
+//   multiply-add (the same value, a fifth fewer vector instructions per row).  Under
+//   destructive selection the chunk first lists its rows in play in LDS (the last
+//   selection's kept rows and the arrivals since) and streams only those: the pass costs
+//   what the selection keeps, not what the pool holds.
 //
 // hardkv_select, grid (B*Hkv), 1024 threads: one workgroup per head.  Pass A turns the
 //   scores into integer weights and builds a mass histogram of the survivors on the top
@@ -135,8 +138,9 @@ HK_DEV void ent_add(float &m, float &z, float &w, float x) {
 
 // SHARED: the pool is the shared block pool (rows of a chunk's blocks anywhere in it, loaded
 // through flat addresses from the block table), else the unit's own ring (one buffer resource).
-template <typename T, int G, bool ENT, bool SHARED>
+template <typename T, int G, bool ENT, bool SHARED, bool LIVE>
 __global__ __launch_bounds__(NTHREADS) void hardkv_score(Args a) {
+  static_assert(!(ENT && LIVE), "destructive selection runs with the fixed temperature");
   constexpr int EB = Elem<T>::bytes;
   const int lin = xcd_swizzle(blockIdx.y * gridDim.x + blockIdx.x, gridDim.x * gridDim.y);
   const int bh = a.bh0 + lin / gridDim.x, chunk = lin % gridDim.x;
@@ -148,6 +152,11 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_score(Args a) {
   const int P = a.P;
 
   __shared__ float s_sc[8 * BK];  // the chunk's scores (at most 8 blocks), stored at the end
+  // LIVE (destructive selection): the chunk's rows in play, compacted -- the ring row and the
+  // physical row of the e-th of them, and the count per block
+  __shared__ uint32_t s_lrow[LIVE ? 8 * BK : 1];
+  __shared__ uint32_t s_prow[LIVE && SHARED ? 8 * BK : 1];
+  __shared__ int s_bcnt[LIVE ? 8 : 1];
   __shared__ float s_wmax[4];
   __shared__ float s_ent[ENT ? 4 : 1][G][3];
   // entropy calibration: lane `sub` < G keeps query sub's softmax piece over its rows
@@ -193,7 +202,6 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_score(Args a) {
     // subtraction wraps the ring index
     const int pb0 = (int)((row_lo / BK) % P);
     const int nrows = (int)(row_hi - row_lo);
-    const int ngroups = (nrows + 15) / 16;
     const int nblk_c = (nrows + BK - 1) / BK;  // blocks of the chunk (at most 8)
     // shared pool: lane i < nblk_c holds the physical block of the chunk's block i, read out
     // by the wavefront for each batch (the batch's block is the same in every lane)
@@ -206,6 +214,49 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_score(Args a) {
         phys_lane = ph < 0 ? 0 : ph;
       }
     }
+    // The rows scored: the chunk's rows, or (LIVE) only those in play -- the last selection's
+    // kept rows and the positions that arrived after it.  A dropped row is neither read nor
+    // scored; its score entry keeps what it held.  Wavefront w lists blocks w and w + 4.
+    int nwork = nrows;
+    if constexpr (LIVE) {
+      const int64_t pend_last = pend_last_selection(a, bh);
+      uint64_t lm[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int bi = wave + 4 * j;
+        bool live = false;
+        if (bi < nblk_c) {
+          int pb = pb0 + bi;
+          pb = pb >= P ? pb - P : pb;
+          const int rel = bi * BK + lane;
+          live = rel < nrows && in_play(row_lo + rel, pend_last, a.mask[(size_t)bh * P + pb]);
+        }
+        lm[j] = ballot(live);
+        if (lane == 0) s_bcnt[bi] = __popcll(lm[j]);
+      }
+      __syncthreads();
+      int pre[8];
+      nwork = 0;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        pre[k] = nwork;
+        nwork += s_bcnt[k];
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int bi = wave + 4 * j;
+        if ((lm[j] >> lane) & 1ull) {
+          int pb = pb0 + bi;
+          pb = pb >= P ? pb - P : pb;
+          const int e = pre[bi] + (int)popc_below(lm[j]);
+          s_lrow[e] = (uint32_t)(pb * BK + lane);
+          if constexpr (SHARED)
+            s_prow[e] = (uint32_t)__builtin_amdgcn_readlane(phys_lane, bi) * BK + lane;
+        }
+      }
+      __syncthreads();
+    }
+    const int ngroups = (nwork + 15) / 16;
     // Each wavefront takes row groups wave, wave + 4, ...; a batch is UNR of them
     // (UNR * 4 loads of 1 KB).  Two batches live in registers: the next batch's loads are
     // in flight while the current one is scored.
@@ -218,7 +269,19 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_score(Args a) {
 #pragma unroll
         for (int l = 0; l < 4; ++l) {
           const int rel = gi * 16 + l * 4 + grp;
-          if constexpr (SHARED) {
+          if constexpr (LIVE) {
+            // the e-th row in play (entries past them read zeros, or in the shared pool the
+            // first block's first row, and are not kept)
+            const bool ok = (gi < ngroups) & (rel < nwork);
+            if constexpr (SHARED) {
+              const uint32_t first = (uint32_t)__builtin_amdgcn_readlane(phys_lane, 0) * BK;
+              const uint32_t prow = ok ? s_prow[ok ? rel : 0] : first;
+              raw_load_nt((const char *)a.pool_k + (size_t)prow * (HD * EB) + lane_b, buf[u][l]);
+            } else {
+              const uint32_t off = ok ? s_lrow[ok ? rel : 0] * (uint32_t)(HD * EB) + lane_b : BUF_SKIP;
+              buf_load_nt(kb, off, buf[u][l]);
+            }
+          } else if constexpr (SHARED) {
             // a row of one of the chunk's blocks (rows past the chunk read a row of its last
             // block and are not kept)
             const int bi = min(gi >> 2, nblk_c - 1);
@@ -268,12 +331,12 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_score(Args a) {
           float dmine;
           float s = group_dots(kf, dmine, fused);
           const int rel = gi * 16 + l * 4 + grp;
-          if (ENT && sub < G && rel < nrows) ent_add(em, ez, ew, dmine * c2);
+          if (ENT && sub < G && rel < nwork) ent_add(em, ez, ew, dmine * c2);
           s = s + 0.0f;  // a zero score is +0
           // s is needed in every lane here, so that the last tree level stays one DPP add
           // rather than a move plus an add sunk into the store's branch
           asm volatile("" : "+v"(s));
-          if (sub == 0 && rel < nrows) s_sc[rel] = s;
+          if (sub == 0 && rel < nwork) s_sc[rel] = s;
         }
       }
     };
@@ -302,17 +365,20 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_score(Args a) {
       g0 += 2 * STEP;
     }
     if (nb & 1) score(bufA, g0);
-    // the chunk's scores leave in one pass: wavefront w writes blocks w, w + 4, ...; the
-    // chunk's maximum is over the rows in play (destructive selection: not the dropped ones)
+    // the chunk's scores leave in one pass, with the chunk's maximum over the rows scored
     __syncthreads();
-    const int64_t pend_last = a.destructive ? pend_last_selection(a, bh) : 0;
-    for (int rel = tid; rel < nrows; rel += NTHREADS) {
-      int pb = pb0 + (rel >> 6);
-      pb = pb >= P ? pb - P : pb;
+    for (int rel = tid; rel < nwork; rel += NTHREADS) {
+      uint32_t row;
+      if constexpr (LIVE) {
+        row = s_lrow[rel];
+      } else {
+        int pb = pb0 + (rel >> 6);
+        pb = pb >= P ? pb - P : pb;
+        row = (uint32_t)(pb * BK + (rel & (BK - 1)));
+      }
       const float s = s_sc[rel];
-      srow[pb * BK + (rel & (BK - 1))] = s;
-      const bool live = !a.destructive || in_play(row_lo + rel, pend_last, a.mask[(size_t)bh * P + pb]);
-      wmax = (live && s > wmax) ? s : wmax;
+      srow[row] = s;
+      wmax = s > wmax ? s : wmax;
     }
   }
   wmax = wave_max(wmax);
@@ -1413,14 +1479,14 @@ __global__ __launch_bounds__(FIT_THREADS) void hardkv_fit_final(Args a) {
   fit_store(a, bh, N, lo, hi);
 }
 
-template <typename T, bool ENT, bool SHARED>
+template <typename T, bool ENT, bool SHARED, bool LIVE = false>
 hipError_t launch_score_ge(const Args &a, hipStream_t s) {
   dim3 grid(a.nch_score, a.nbh);
   switch (a.G) {
-    case 1: hipLaunchKernelGGL((hardkv_score<T, 1, ENT, SHARED>), grid, dim3(NTHREADS), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((hardkv_score<T, 2, ENT, SHARED>), grid, dim3(NTHREADS), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((hardkv_score<T, 4, ENT, SHARED>), grid, dim3(NTHREADS), 0, s, a); break;
-    case 8: hipLaunchKernelGGL((hardkv_score<T, 8, ENT, SHARED>), grid, dim3(NTHREADS), 0, s, a); break;
+    case 1: hipLaunchKernelGGL((hardkv_score<T, 1, ENT, SHARED, LIVE>), grid, dim3(NTHREADS), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((hardkv_score<T, 2, ENT, SHARED, LIVE>), grid, dim3(NTHREADS), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((hardkv_score<T, 4, ENT, SHARED, LIVE>), grid, dim3(NTHREADS), 0, s, a); break;
+    case 8: hipLaunchKernelGGL((hardkv_score<T, 8, ENT, SHARED, LIVE>), grid, dim3(NTHREADS), 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -1428,6 +1494,8 @@ hipError_t launch_score_ge(const Args &a, hipStream_t s) {
 
 template <typename T>
 hipError_t launch_score_g(const Args &a, hipStream_t s) {
+  if (a.destructive)  // (the fixed temperature: no entropy pieces)
+    return a.pool_shared ? launch_score_ge<T, false, true, true>(a, s) : launch_score_ge<T, false, false, true>(a, s);
   if (a.pool_shared)
     return a.calibration ? launch_score_ge<T, true, true>(a, s) : launch_score_ge<T, false, true>(a, s);
   return a.calibration ? launch_score_ge<T, true, false>(a, s) : launch_score_ge<T, false, false>(a, s);

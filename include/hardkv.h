@@ -258,7 +258,8 @@ typedef struct {
   int32_t *cond_cursor;      /* [B][Hkv]: next slot of the ring                                   */
   int64_t *seq_len;          /* [B]: t                                                            */
   int64_t *pool_head;        /* [B][Hkv]: c, a multiple of 64                                     */
-  float *scores;             /* fp32 [B][Hkv][P*64]: s by pool ring row (rows outside the pool unspecified) */
+  float *scores;             /* fp32 [B][Hkv][P*64]: s by pool ring row (rows outside the pool, and rows a
+                                destructive selection dropped, unspecified) */
   uint32_t *weights;         /* [B][Hkv][P*64]: w by pool ring row                                */
   uint64_t *mask;            /* [B][Hkv][P]: word (p/64) mod P, bit p%64 set iff p is kept        */
   int32_t *budget;           /* [B][Hkv]: k*                                                      */

@@ -57,6 +57,7 @@ class Pair:
         pol = dict(regularize=regularize, mti_lower=mti_lower, mti_upper=mti_upper,
                    view_layout=view_layout, view_total=view_total, selection=selection)
         self.packed = view_layout == hk.HARDKV_VIEW_SUM
+        self.destructive = selection == hk.HARDKV_SEL_DESTRUCTIVE
         assert not (self.packed and oracle_units is not None), "packed views need the whole layer"
         # the memory-time controller's inputs (policy MTI_AUTO), the same on both sides
         self.mti = dict(hk.MTI_DEFAULT, **(mti or {}))
@@ -201,11 +202,17 @@ class Pair:
                 c0 = int(pre[key][ob, oh])
                 pos = np.arange(c0, pend)
                 rows = (pos // 64) % P * 64 + pos % 64
-                gs = g["scores"].numpy()[rows].view(np.uint32)
-                os_ = o.scores[ob, oh][rows].view(np.uint32)
+                spos, srows = pos, rows
+                if self.destructive:
+                    # a destructive selection scores only the rows in play, which all weigh at
+                    # least 1: a dropped row's score entry is unspecified
+                    play = o.weights[ob, oh][rows] != 0
+                    spos, srows = pos[play], rows[play]
+                gs = g["scores"].numpy()[srows].view(np.uint32)
+                os_ = o.scores[ob, oh][srows].view(np.uint32)
                 if not np.array_equal(gs, os_):
                     bad = np.nonzero(gs != os_)[0][:5]
-                    raise AssertionError(f"{tag} scores differ at positions {pos[bad]}: "
+                    raise AssertionError(f"{tag} scores differ at positions {spos[bad]}: "
                                          f"{gs[bad].view(np.float32)} vs {os_[bad].view(np.float32)}")
                 assert np.array_equal(g["weights"].numpy().view(np.uint32)[rows], o.weights[ob, oh][rows]), f"{tag} weights"
                 assert np.array_equal(g["mask"].numpy().view(np.uint64), o.mask[ob, oh]), f"{tag} mask"

@@ -149,6 +149,28 @@ def test_c4_streaming_256_steps():
     assert int(pr.st.seq_len[0]) == 131072 + 256
 
 
+def test_c4_streaming_destructive():
+    """The streaming workload under destructive selection: every selection chooses among
+    the last one's kept rows and the arrivals since, so the kept set shrinks to a few rows
+    per head; selection state on the sampled units at every step, attention and views at
+    the sampled steps, the layer's properties on every unit."""
+    from decode_kv_cache_02_amd import hardkv as hk
+    from parity import Pair, check_layer_properties
+    wl = get_workload("c4")
+    print("workload", wl.name, "destructive", flush=True)
+    pr = Pair(wl, oracle_units=[(0, 1), (1, 6), (2, 2), (3, 4)], selection=hk.HARDKV_SEL_DESTRUCTIVE)
+    pr.drop_context()
+    sampled = {0, 1, 2, 64, 65, 130, 255}
+    for s in range(wl.steps):
+        full = s in sampled
+        pr.step(attend=full, check_attend=full, check_views=full)
+        if full:
+            check_layer_properties(pr)
+            print("step", s, "ok, budgets", pr.st.budget.flatten()[:8].tolist(), flush=True)
+    assert int(pr.st.seq_len[0]) == 131072 + 256
+    assert int(pr.st.error_word[0].item()) == 0
+
+
 @pytest.mark.parametrize("layer", [0, 17, 31])
 def test_c5_layers(layer):
     """Layers of the 32-layer batch-32, 16k-context step (each layer is independent)."""

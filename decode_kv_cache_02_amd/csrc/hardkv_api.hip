@@ -168,7 +168,9 @@ int32_t plan(const hardkv_config *cfg, Plan &p) {
 
   const int64_t BH = (int64_t)a.B * a.Hkv;
   const int64_t work = (int64_t)a.P * BH;
-  const int cb = (int)std::max<int64_t>(1, std::min<int64_t>(8, work / 1024));
+  // (destructive selection scores only the rows in play, so its chunks span more blocks)
+  const int cb_max = a.destructive ? SCORE_LIVE_BLOCKS : 8;
+  const int cb = (int)std::max<int64_t>(1, std::min<int64_t>(cb_max, work / 1024));
   a.cb_score = cb;
   a.nch_score = (a.P + cb - 1) / cb;
   // rewrite chunks of 4 blocks (one per wavefront) over the survivor blocks only: at most

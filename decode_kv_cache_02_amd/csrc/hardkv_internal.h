@@ -20,6 +20,7 @@ constexpr int CAND_CAP = 8192;        // cut-bucket candidates resolved in LDS
 constexpr int SEL_SLICE_BLOCKS = 256; // pool blocks per workgroup when a head's select is split
 constexpr int SEL_SPLIT_MIN = 4;      // slices per head from which the select is split
 constexpr int FUSE_COND_BLOCKS = 4;   // blocks per step up to which the step's select condenses
+constexpr int SCORE_LIVE_BLOCKS = 32; // most blocks per score workgroup under destructive selection
 
 // Per-head values that the split select passes between its kernels.
 struct alignas(128) SelHead {

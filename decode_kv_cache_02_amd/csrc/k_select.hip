@@ -142,6 +142,7 @@ template <typename T, int G, bool ENT, bool SHARED, bool LIVE>
 __global__ __launch_bounds__(NTHREADS) void hardkv_score(Args a) {
   static_assert(!(ENT && LIVE), "destructive selection runs with the fixed temperature");
   constexpr int EB = Elem<T>::bytes;
+  constexpr int CBL = LIVE ? SCORE_LIVE_BLOCKS : 8;  // most blocks of a chunk
   const int lin = xcd_swizzle(blockIdx.y * gridDim.x + blockIdx.x, gridDim.x * gridDim.y);
   const int bh = a.bh0 + lin / gridDim.x, chunk = lin % gridDim.x;
   const int b = bh / a.Hkv, h = bh - b * a.Hkv;
@@ -151,12 +152,12 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_score(Args a) {
   const int sub = lane & 15, grp = lane >> 4;
   const int P = a.P;
 
-  __shared__ float s_sc[8 * BK];  // the chunk's scores (at most 8 blocks), stored at the end
+  __shared__ float s_sc[CBL * BK];  // the chunk's scores, stored at the end
   // LIVE (destructive selection): the chunk's rows in play, compacted -- the ring row and the
   // physical row of the e-th of them, and the count per block
-  __shared__ uint32_t s_lrow[LIVE ? 8 * BK : 1];
-  __shared__ uint32_t s_prow[LIVE && SHARED ? 8 * BK : 1];
-  __shared__ int s_bcnt[LIVE ? 8 : 1];
+  __shared__ uint32_t s_lrow[LIVE ? CBL * BK : 1];
+  __shared__ uint32_t s_prow[LIVE && SHARED ? CBL * BK : 1];
+  __shared__ int s_bcnt[LIVE ? CBL : 1];
   __shared__ float s_wmax[4];
   __shared__ float s_ent[ENT ? 4 : 1][G][3];
   // entropy calibration: lane `sub` < G keeps query sub's softmax piece over its rows
@@ -202,7 +203,7 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_score(Args a) {
     // subtraction wraps the ring index
     const int pb0 = (int)((row_lo / BK) % P);
     const int nrows = (int)(row_hi - row_lo);
-    const int nblk_c = (nrows + BK - 1) / BK;  // blocks of the chunk (at most 8)
+    const int nblk_c = (nrows + BK - 1) / BK;  // blocks of the chunk (at most CBL)
     // shared pool: lane i < nblk_c holds the physical block of the chunk's block i, read out
     // by the wavefront for each batch (the batch's block is the same in every lane)
     int32_t phys_lane = 0;
@@ -216,13 +217,15 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_score(Args a) {
     }
     // The rows scored: the chunk's rows, or (LIVE) only those in play -- the last selection's
     // kept rows and the positions that arrived after it.  A dropped row is neither read nor
-    // scored; its score entry keeps what it held.  Wavefront w lists blocks w and w + 4.
+    // scored; its score entry keeps what it held.  Wavefront w lists blocks w, w + 4, ...
+    // (a chunk of LIVE spans more blocks, so that a pool with few rows in play costs few
+    // workgroups).
     int nwork = nrows;
     if constexpr (LIVE) {
       const int64_t pend_last = pend_last_selection(a, bh);
-      uint64_t lm[2];
+      uint64_t lm[CBL / 4];
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
+      for (int j = 0; j < CBL / 4; ++j) {
         const int bi = wave + 4 * j;
         bool live = false;
         if (bi < nblk_c) {
@@ -235,20 +238,24 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_score(Args a) {
         if (lane == 0) s_bcnt[bi] = __popcll(lm[j]);
       }
       __syncthreads();
-      int pre[8];
-      nwork = 0;
+      // the blocks' first entries: an exclusive scan of the counts over lanes 0 .. CBL - 1
+      const int cnt = lane < CBL ? s_bcnt[lane] : 0;
+      int incl = cnt;
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        pre[k] = nwork;
-        nwork += s_bcnt[k];
+      for (int off = 1; off < CBL; off <<= 1) {
+        const int y = __shfl_up(incl, off);
+        incl += lane >= off ? y : 0;
       }
+      nwork = __builtin_amdgcn_readlane(incl, CBL - 1);
+      const int excl = incl - cnt;
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
+      for (int j = 0; j < CBL / 4; ++j) {
         const int bi = wave + 4 * j;
+        const int first = __builtin_amdgcn_readlane(excl, bi);
         if ((lm[j] >> lane) & 1ull) {
           int pb = pb0 + bi;
           pb = pb >= P ? pb - P : pb;
-          const int e = pre[bi] + (int)popc_below(lm[j]);
+          const int e = first + (int)popc_below(lm[j]);
           s_lrow[e] = (uint32_t)(pb * BK + lane);
           if constexpr (SHARED)
             s_prow[e] = (uint32_t)__builtin_amdgcn_readlane(phys_lane, bi) * BK + lane;

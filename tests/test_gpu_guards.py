@@ -2,7 +2,7 @@
 workspace) sits between guard zones filled with a byte pattern, and after prefills, steps
 with and without selection and the separate calls, the guards are unchanged, for layouts
 that fill each capacity (pool ring wrap, condensed ring wrap, packed views that overflow
-their rows, sinks, split select, split entropy fit)."""
+their rows, sinks, split select, split entropy fit, the shared pool, destructive selection)."""
 
 import pytest
 import torch
@@ -57,7 +57,7 @@ CASES = {
 
 
 @pytest.mark.parametrize("name", list(CASES))
-@pytest.mark.parametrize("layout", ["maxlen", "packed_short", "shared", "shared_short"])
+@pytest.mark.parametrize("layout", ["maxlen", "packed_short", "shared", "shared_short", "destructive"])
 def test_guards_untouched(name, layout):
     kw = dict(CASES[name])
     steps = kw.pop("steps")
@@ -71,7 +71,10 @@ def test_guards_untouched(name, layout):
         need = (hk.hardkv_shared_pool_blocks(ring, inp.ctx_len.cpu(), steps + 2) if layout == "shared"
                 else hk.hardkv_shared_pool_blocks(ring, inp.ctx_len.cpu(), 0) - 1)
         extra = dict(pool_layout=hk.HARDKV_POOL_SHARED, pool_total_blocks=need)
-    for cal in (hk.HARDKV_CAL_FIXED, hk.HARDKV_CAL_ENTROPY):
+    elif layout == "destructive":  # (with the fixed temperature only)
+        extra = dict(selection=hk.HARDKV_SEL_DESTRUCTIVE)
+    cals = (hk.HARDKV_CAL_FIXED,) if layout == "destructive" else (hk.HARDKV_CAL_FIXED, hk.HARDKV_CAL_ENTROPY)
+    for cal in cals:
         cfg = hk.Config.from_workload(wl, calibration=cal, **extra)
         st = GuardedState(cfg)
         out = torch.zeros((wl.batch, wl.num_q_heads, wl.head_dim), dtype=torch.float32, device="cuda")

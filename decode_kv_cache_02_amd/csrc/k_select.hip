@@ -9,7 +9,7 @@
 // flags: on MI355X each agent-scope release/acquire writes back or invalidates a whole
 // XCD's L2).
 //
-// hardkv_score, grid (chunks, B*Hkv), 256 threads (XCD-swizzled): streams a chunk of the head's pool
+// hardkv_score, grid (chunks, B*Hkv), 256 threads (units interleaved over the XCDs): streams a chunk of the head's pool
 //   keys with 16-byte loads; 16 lanes hold one 256-byte bf16 row (8 elements each), a
 //   wavefront covers 4 rows per load.  Each lane forms the pairwise sum of its 8
 //   products in registers (tree levels 1-3); levels 4-7 are DPP exchanges inside the
@@ -138,13 +138,31 @@ HK_DEV void ent_add(float &m, float &z, float &w, float x) {
 
 // SHARED: the pool is the shared block pool (rows of a chunk's blocks anywhere in it, loaded
 // through flat addresses from the block table), else the unit's own ring (one buffer resource).
+// The score workgroup's (unit, chunk).  Workgroup i goes to XCD i mod 8; when the units
+// come in groups of 8 (the KV heads of a sequence share its length), XCD x takes units
+// x, x + 8, ..., each unit's chunks in order, so that every XCD gets the same share of
+// long and short sequences.  Otherwise, contiguous ranges of the work (xcd_swizzle).
+HK_DEV void score_work(int lin, int nch, int nbh, int &bh_rel, int &chunk) {
+  if ((nbh & 7) == 0) {
+    const int x = lin & 7, k = lin >> 3;
+    const int j = k / nch;
+    chunk = k - j * nch;
+    bh_rel = x + 8 * j;
+  } else {
+    const int w = xcd_swizzle(lin, nch * nbh);
+    bh_rel = w / nch;
+    chunk = w - bh_rel * nch;
+  }
+}
+
 template <typename T, int G, bool ENT, bool SHARED, bool LIVE>
 __global__ __launch_bounds__(NTHREADS) void hardkv_score(Args a) {
   static_assert(!(ENT && LIVE), "destructive selection runs with the fixed temperature");
   constexpr int EB = Elem<T>::bytes;
   constexpr int CBL = LIVE ? SCORE_LIVE_BLOCKS : 8;  // most blocks of a chunk
-  const int lin = xcd_swizzle(blockIdx.y * gridDim.x + blockIdx.x, gridDim.x * gridDim.y);
-  const int bh = a.bh0 + lin / gridDim.x, chunk = lin % gridDim.x;
+  int bh_rel, chunk;
+  score_work(blockIdx.y * gridDim.x + blockIdx.x, gridDim.x, gridDim.y, bh_rel, chunk);
+  const int bh = a.bh0 + bh_rel;
   const int b = bh / a.Hkv, h = bh - b * a.Hkv;
   // the wavefront index is uniform (readfirstlane tells the compiler so: its batch loop
   // then runs on scalar branches)

@@ -481,7 +481,8 @@ constexpr int UA = 4;                  // 16-byte loads in flight per lane in th
 // A candidate of the cut bucket b1 packs its survivor block j and the low 16 bits of its
 // key: (j << 16) | (key & 0xffff); its key is (b1 << 16) | (cand & 0xffff).
 struct SelShared {
-  unsigned long long hist[NB1];  // mass histogram (level 1, then levels 2 and 3)
+  unsigned long long hist[NB1];  // mass histogram of level 1
+  unsigned long long h2[256], h3[256];  // levels 2 and 3 (cleared when the workgroup starts)
   uint32_t cand[CAND_CAP];       // the cut bucket's tokens
   unsigned long long red[2][NW];
   float fred[NW];
@@ -495,6 +496,10 @@ struct SelShared {
 };
 // Dynamic LDS: SelShared, then uint32_t blk[P], per survivor block gt | eq << 16.
 constexpr size_t sel_lds_bytes(int P) { return sizeof(SelShared) + sizeof(uint32_t) * (size_t)P; }
+
+HK_DEV void clear_levels(SelShared &sh) {
+  for (int i = threadIdx.x; i < 256; i += SEL_THREADS) sh.h2[i] = sh.h3[i] = 0ull;
+}
 
 HK_DEV uint64_t block_sum_u64(uint64_t v, SelShared &sh, int which) {
   const int tid = threadIdx.x;
@@ -563,6 +568,41 @@ HK_DEV int find_cut(SelShared &sh, int nb, uint64_t target, uint64_t *above) {
   const int r = sh.res_bucket;
   __syncthreads();
   return r;
+}
+
+// find_cut over 256 buckets, by every wavefront on its own (no barrier): lane l sums
+// buckets 4l .. 4l + 3, a suffix scan over the lanes finds the lane that holds the cut,
+// and that lane walks its four buckets down.  The histogram must be complete and must
+// not change until every wavefront has returned.
+HK_DEV int find_cut256(const unsigned long long *h, uint64_t target, uint64_t *above) {
+  const int lane = threadIdx.x & 63;
+  uint64_t v[4], mine = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    v[k] = h[4 * lane + k];
+    mine += v[k];
+  }
+  uint64_t incl = mine;  // sum(h[4 lane ..])
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint64_t x = shfl_u64(incl, lane + off < 64 ? lane + off : 63);
+    if (lane + off < 64) incl += x;
+  }
+  const uint64_t excl = incl - mine;  // sum(h[4 lane + 4 ..])
+  const uint64_t hit = ballot(excl < target && incl >= target);
+  const int src = hit ? __ffsll((long long)hit) - 1 : 0;
+  int b = 4 * lane;
+  uint64_t acc = excl;
+#pragma unroll
+  for (int k = 3; k >= 0; --k) {
+    if (acc + v[k] >= target) {
+      b = 4 * lane + k;
+      break;
+    }
+    acc += v[k];
+  }
+  *above = shfl_u64(acc, src);
+  return __shfl(b, src);
 }
 
 // the sum of 16-lane groups (lanes 16q .. 16q + 15), in every lane of the group
@@ -776,24 +816,20 @@ HK_DEV void sel_finish(const Args &a, int bh, const SelGeo &g, SelShared &sh, ui
       w_th = sh.w_th;
       r = sh.r;
     } else if (ncand <= (uint32_t)CAND_CAP) {
-      // levels 2 and 3 over the candidates in LDS
-      for (int i = tid; i < 256; i += SEL_THREADS) sh.hist[i] = 0ull;
-      __syncthreads();
+      // levels 2 and 3 over the candidates in LDS (their histograms start cleared)
       for (uint32_t i = tid; i < ncand; i += SEL_THREADS) {
         const uint32_t k = kb1 | (sh.cand[i] & 0xffffu);
-        atomicAdd(&sh.hist[(k >> 8) & 255u], (unsigned long long)key_to_w(k));
+        atomicAdd(&sh.h2[(k >> 8) & 255u], (unsigned long long)key_to_w(k));
       }
       __syncthreads();
-      const int b2 = find_cut(sh, 256, R1, &above2);
+      const int b2 = find_cut256(sh.h2, R1, &above2);
       const uint32_t pre = ((uint32_t)b1 << 8) | (uint32_t)b2;
-      for (int i = tid; i < 256; i += SEL_THREADS) sh.hist[i] = 0ull;
-      __syncthreads();
       for (uint32_t i = tid; i < ncand; i += SEL_THREADS) {
         const uint32_t k = kb1 | (sh.cand[i] & 0xffffu);
-        if ((k >> 8) == pre) atomicAdd(&sh.hist[k & 255u], (unsigned long long)key_to_w(k));
+        if ((k >> 8) == pre) atomicAdd(&sh.h3[k & 255u], (unsigned long long)key_to_w(k));
       }
       __syncthreads();
-      const int b3 = find_cut(sh, 256, R1 - above2, &above3);
+      const int b3 = find_cut256(sh.h3, R1 - above2, &above3);
       w_th = key_to_w((pre << 8) | (uint32_t)b3);
       r = (uint32_t)((R1 - above2 - above3 + w_th - 1) / w_th);
     }
@@ -809,31 +845,27 @@ HK_DEV void sel_finish(const Args &a, int bh, const SelGeo &g, SelShared &sh, ui
     } else {
       // a bucket too full for LDS (for example many equal weights): levels 2 and 3 and
       // the per-block counts over the survivors' weights in memory
-      for (int i = tid; i < 256; i += SEL_THREADS) sh.hist[i] = 0ull;
-      __syncthreads();
       for (int j = wave; j < nub; j += NW) {
         const int64_t p = u0 + (int64_t)j * BK + lane;
         if (p < pend) {
           const uint32_t w = a.weights[rowbase + (size_t)ring(nx + j) * BK + lane];
           const uint32_t k = wkey(w);
-          if ((int)(k >> 16) == b1) atomicAdd(&sh.hist[(k >> 8) & 255u], (unsigned long long)w);
+          if ((int)(k >> 16) == b1) atomicAdd(&sh.h2[(k >> 8) & 255u], (unsigned long long)w);
         }
       }
       __syncthreads();
-      const int b2 = find_cut(sh, 256, R1, &above2);
+      const int b2 = find_cut256(sh.h2, R1, &above2);
       const uint32_t pre = ((uint32_t)b1 << 8) | (uint32_t)b2;
-      for (int i = tid; i < 256; i += SEL_THREADS) sh.hist[i] = 0ull;
-      __syncthreads();
       for (int j = wave; j < nub; j += NW) {
         const int64_t p = u0 + (int64_t)j * BK + lane;
         if (p < pend) {
           const uint32_t w = a.weights[rowbase + (size_t)ring(nx + j) * BK + lane];
           const uint32_t k = wkey(w);
-          if ((k >> 8) == pre) atomicAdd(&sh.hist[k & 255u], (unsigned long long)w);
+          if ((k >> 8) == pre) atomicAdd(&sh.h3[k & 255u], (unsigned long long)w);
         }
       }
       __syncthreads();
-      const int b3 = find_cut(sh, 256, R1 - above2, &above3);
+      const int b3 = find_cut256(sh.h3, R1 - above2, &above3);
       w_th = key_to_w((pre << 8) | (uint32_t)b3);
       r = (uint32_t)((R1 - above2 - above3 + w_th - 1) / w_th);
       for (int j = wave; j < nub; j += NW) {
@@ -926,6 +958,7 @@ __global__ __launch_bounds__(SEL_THREADS) void hardkv_select(Args a) {
   const int32_t nu = FUSE ? a.cond_cursor[bh] : 0;
 
   for (int i = tid; i < NB1; i += SEL_THREADS) sh.hist[i] = 0ull;
+  clear_levels(sh);
   if (tid == 0) sh.ncand = 0;
   // every mask word starts empty; the rewrite kernel writes the survivor blocks' words (a
   // destructive selection reads the last selection's words in pass A first)
@@ -1110,6 +1143,7 @@ __global__ __launch_bounds__(SEL_THREADS) void hardkv_sel_finish(Args a) {
   const uint64_t W_all = sx->w_all, W_U = sx->w_u, Tm = sx->T;
   uint64_t R1 = 0;
   int b1 = 0;
+  clear_levels(sh);  // (ordered before sel_finish by the barrier below, or unused)
   if (W_U > 0) {
     R1 = sx->R1;
     b1 = sx->b1;

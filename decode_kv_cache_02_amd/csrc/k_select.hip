@@ -485,10 +485,9 @@ struct SelShared {
   unsigned long long h2[256], h3[256];  // levels 2 and 3 (cleared when the workgroup starts)
   uint32_t cand[CAND_CAP];       // the cut bucket's tokens
   unsigned long long red[2][NW];
+  unsigned long long wt[NW];     // level-1 cut: each wavefront's segment of 256 buckets
   float fred[NW];
   uint32_t ncand;
-  int res_bucket;
-  unsigned long long res_above;
   unsigned long long carry;
   unsigned long long total;
   uint32_t w_th, r;
@@ -501,15 +500,24 @@ HK_DEV void clear_levels(SelShared &sh) {
   for (int i = threadIdx.x; i < 256; i += SEL_THREADS) sh.h2[i] = sh.h3[i] = 0ull;
 }
 
-HK_DEV uint64_t block_sum_u64(uint64_t v, SelShared &sh, int which) {
+// the workgroup's sums of two values, with one barrier
+HK_DEV void block_sum2_u64(uint64_t &x, uint64_t &y, SelShared &sh) {
   const int tid = threadIdx.x;
-  v = wave_sum_u64(v);
-  if ((tid & 63) == 0) sh.red[which][tid >> 6] = v;
+  x = wave_sum_u64(x);
+  y = wave_sum_u64(y);
+  if ((tid & 63) == 0) {
+    sh.red[0][tid >> 6] = x;
+    sh.red[1][tid >> 6] = y;
+  }
   __syncthreads();
-  uint64_t s = 0;
+  uint64_t sx = 0, sy = 0;
 #pragma unroll
-  for (int w = 0; w < NW; ++w) s += sh.red[which][w];
-  return s;
+  for (int w = 0; w < NW; ++w) {
+    sx += sh.red[0][w];
+    sy += sh.red[1][w];
+  }
+  x = sx;
+  y = sy;
 }
 
 HK_DEV uint64_t shfl_u64(uint64_t v, int src) {
@@ -539,47 +547,18 @@ HK_DEV uint64_t block_scan_u64(uint64_t mine, SelShared &sh, bool suffix) {
   return before + v;
 }
 
-// largest bucket b of hist[0..nb) with sum(hist[b..]) >= target (1 <= target <= total);
-// *above = sum(hist[b+1..]).
-HK_DEV int find_cut(SelShared &sh, int nb, uint64_t target, uint64_t *above) {
-  const int tid = threadIdx.x;
-  const int per = (nb + SEL_THREADS - 1) / SEL_THREADS;
-  const int lo = tid * per, hi = min(lo + per, nb);
-  uint64_t mine = 0;
-  for (int i = lo; i < hi; ++i) mine += sh.hist[i];
-  if (tid == 0) {
-    sh.res_bucket = 0;
-    sh.res_above = 0;
-  }
-  const uint64_t incl = block_scan_u64(mine, sh, true), excl = incl - mine;
-  if (excl < target && incl >= target) {
-    uint64_t acc = excl;
-    for (int i = hi - 1; i >= lo; --i) {
-      if (acc + sh.hist[i] >= target) {
-        sh.res_bucket = i;
-        sh.res_above = acc;
-        break;
-      }
-      acc += sh.hist[i];
-    }
-  }
-  __syncthreads();
-  *above = sh.res_above;
-  const int r = sh.res_bucket;
-  __syncthreads();
-  return r;
-}
-
-// find_cut over 256 buckets, by every wavefront on its own (no barrier): lane l sums
+// The cut of a mass histogram: the largest bucket b with sum(h[b..]) >= target (1 <= target
+// <= total), and *above = sum(h[b + 1 ..]).
+// Over 256 buckets, by every wavefront on its own (no barrier): lane l sums
 // buckets 4l .. 4l + 3, a suffix scan over the lanes finds the lane that holds the cut,
 // and that lane walks its four buckets down.  The histogram must be complete and must
 // not change until every wavefront has returned.
-HK_DEV int find_cut256(const unsigned long long *h, uint64_t target, uint64_t *above) {
+HK_DEV int find_cut256(const unsigned long long *h, uint64_t target, uint64_t *above, int nb = 256) {
   const int lane = threadIdx.x & 63;
   uint64_t v[4], mine = 0;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    v[k] = h[4 * lane + k];
+    v[k] = 4 * lane + k < nb ? h[4 * lane + k] : 0ull;
     mine += v[k];
   }
   uint64_t incl = mine;  // sum(h[4 lane ..])
@@ -603,6 +582,40 @@ HK_DEV int find_cut256(const unsigned long long *h, uint64_t target, uint64_t *a
   }
   *above = shfl_u64(acc, src);
   return __shfl(b, src);
+}
+
+// The cut over the NB1 level-1 buckets, with one barrier: wavefront w totals buckets
+// [256 w, 256 w + 256); then every wavefront finds the segment that holds the cut from the
+// totals and the bucket inside it with find_cut256.  The histogram must be complete, and
+// must not change (nor sh.wt) until every wavefront has returned.
+HK_DEV int find_cut_l1(SelShared &sh, uint64_t target, uint64_t *above) {
+  static_assert(NW * 256 >= NB1, "the wavefronts' segments cover the level-1 buckets");
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  uint64_t mine = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int i = 256 * wave + 4 * lane + k;
+    mine += i < NB1 ? sh.hist[i] : 0ull;
+  }
+  mine = wave_sum_u64(mine);
+  if (lane == 0) sh.wt[wave] = mine;
+  __syncthreads();
+  // suffix sums of the segment totals over lanes 0 .. NW - 1
+  const uint64_t t = lane < NW ? sh.wt[lane] : 0ull;
+  uint64_t incl = t;
+#pragma unroll
+  for (int off = 1; off < NW; off <<= 1) {
+    const uint64_t x = shfl_u64(incl, lane + off < 64 ? lane + off : 63);
+    if (lane + off < NW) incl += x;
+  }
+  const uint64_t excl = incl - t;
+  const uint64_t hit = ballot(lane < NW && excl < target && incl >= target);
+  const int seg = hit ? __ffsll((long long)hit) - 1 : 0;
+  const uint64_t above_seg = shfl_u64(excl, seg);
+  uint64_t above_in = 0;
+  const int b = find_cut256(sh.hist + 256 * seg, target - above_seg, &above_in, NB1 - 256 * seg);
+  *above = above_seg + above_in;
+  return 256 * seg + b;
 }
 
 // the sum of 16-lane groups (lanes 16q .. 16q + 15), in every lane of the group
@@ -881,6 +894,20 @@ HK_DEV void sel_finish(const Args &a, int bh, const SelGeo &g, SelShared &sh, ui
 
     // scan over survivor blocks in position order: first view row GT_before +
     // min(EQ_before, r), and EQ_before for the tie ranks of the mask bits
+    if (nub <= SEL_THREADS) {
+      // one round: no carry between rounds
+      const uint32_t v = (tid < nub) ? blk[tid] : 0u;
+      const uint64_t mine = (uint64_t)(v & 0xffffu) | ((uint64_t)(v >> 16) << 32);
+      const uint64_t incl = block_scan_u64(mine, sh, false);
+      const uint64_t before = incl - mine;
+      if (tid < nub) {
+        const uint32_t gt_b = (uint32_t)before, eq_b = (uint32_t)(before >> 32);
+        a.blkinfo[(size_t)bh * P + ring(nx + tid)] = make_uint2(gt_b + min(eq_b, r), eq_b);
+      }
+      if (tid == SEL_THREADS - 1) sh.total = incl;
+      __syncthreads();
+      n_gt = sh.total & 0xffffffffull;
+    } else {
     if (tid == 0) sh.carry = 0ull;
     __syncthreads();
     for (int base = 0; base < nub; base += SEL_THREADS) {
@@ -900,6 +927,7 @@ HK_DEV void sel_finish(const Args &a, int bh, const SelGeo &g, SelShared &sh, ui
       __syncthreads();
     }
     n_gt = sh.carry & 0xffffffffull;
+    }
   }
 
   if (tid == 0) {
@@ -970,8 +998,8 @@ __global__ __launch_bounds__(SEL_THREADS) void hardkv_select(Args a) {
   bool bad = false;
   sel_pass_a(a, g, m, 0, g.nblk, sh, my_all, my_u, bad);
   if (ballot(bad) && lane == 0) atomicOr(a.error_word, HARDKV_ERR_NONFINITE);
-  const uint64_t W_all = block_sum_u64(my_all, sh, 0);
-  const uint64_t W_U = block_sum_u64(my_u, sh, 1);
+  uint64_t W_all = my_all, W_U = my_u;
+  block_sum2_u64(W_all, W_U, sh);
   if (a.destructive)  // (after the barriers above: every thread's pass A has read its words)
     for (int i = tid; i < P; i += SEL_THREADS) a.mask[(size_t)bh * P + i] = 0ull;
   const uint64_t Tm = ((uint64_t)a.pq * W_U + 65535ull) >> 16;
@@ -979,7 +1007,7 @@ __global__ __launch_bounds__(SEL_THREADS) void hardkv_select(Args a) {
   int b1 = 0;
   if (W_U > 0) {
     uint64_t above1;
-    b1 = find_cut(sh, NB1, Tm, &above1);
+    b1 = find_cut_l1(sh, Tm, &above1);
     R1 = Tm - above1;  // mass still needed from the cut bucket
     sel_pass_b<false>(a, bh, g, b1, 0, g.nub, blk, sh.cand, &sh.ncand);
     __syncthreads();
@@ -1014,8 +1042,8 @@ __global__ __launch_bounds__(SEL_THREADS) void hardkv_sel_weigh(Args a) {
   const int lo = slice * SEL_SLICE_BLOCKS, hi = min(g.nblk, lo + SEL_SLICE_BLOCKS);
   sel_pass_a(a, g, m, lo, hi, sh, my_all, my_u, bad);
   if (ballot(bad) && lane == 0) atomicOr(a.error_word, HARDKV_ERR_NONFINITE);
-  const uint64_t s_all = block_sum_u64(my_all, sh, 0);
-  const uint64_t s_u = block_sum_u64(my_u, sh, 1);  // (its barrier also orders the histogram)
+  uint64_t s_all = my_all, s_u = my_u;
+  block_sum2_u64(s_all, s_u, sh);  // (its barrier also orders the histogram)
   unsigned long long *ph = a.phist + ((size_t)bh * a.nsp + slice) * NB1;
   for (int i = tid; i < NB1; i += SEL_THREADS) ph[i] = sh.hist[i];
   if (tid == 0) {
@@ -1085,7 +1113,7 @@ __global__ __launch_bounds__(SEL_THREADS) void hardkv_sel_cut(Args a) {
     for (int q = 0; q < PER; ++q)
       if (tid + q * SEL_THREADS < NB1) sh.hist[tid + q * SEL_THREADS] = acc[q];
     __syncthreads();
-    b1 = find_cut(sh, NB1, T, &above1);
+    b1 = find_cut_l1(sh, T, &above1);
   }
   if (tid == 0) {
     SelHead *sx = a.selh + bh;

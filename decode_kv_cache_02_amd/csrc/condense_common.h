@@ -1,5 +1,6 @@
-// condense_common.h -- the condensation of one ring slot, shared by the condense kernel and
-// by the select kernels that condense in the same launch when few blocks can condense.
+// condense_common.h -- the condensation of one ring slot (the condense kernel) and the
+// advance of the pool head past the condensed blocks (also taken by the select kernels that
+// condense in the same launch when few blocks can condense).
 //
 // HARD-KV explainer, technical summary 2.A (tier 3): the oldest blocks are evicted or
 // merged by weight into storage of constant size.  Condensed block e (of the E oldest,
@@ -14,10 +15,8 @@ namespace hardkv {
 // that lands there (blocks i, i + C, ...).  Inside a block, 16 lanes hold one row (8 head
 // dims each) and a load covers 4 rows; NB loads of keys and NB of values per lane are in
 // flight per batch.  Each lane accumulates w k and w v for its dims over its rows, the
-// four row groups are summed by lane exchanges, and 16 lanes update the slot.  LEAN: the
-// batches one after another (no later batch's loads hoisted into an earlier one), for a
-// caller with fewer registers to spare.
-template <typename T, int NB, bool LEAN = false>
+// four row groups are summed by lane exchanges, and 16 lanes update the slot.
+template <typename T, int NB>
 HK_DEV void condense_chain(const Args &a, int bh, int i, int64_t c, int64_t E, int32_t nu, uint64_t w_all) {
   constexpr int EB = Elem<T>::bytes;
   constexpr size_t ROWB = (size_t)HD * EB;
@@ -42,8 +41,7 @@ HK_DEV void condense_chain(const Args &a, int bh, int i, int64_t c, int64_t E, i
     const uint32_t wl = a.weights[((size_t)bh * P + pb) * BK + lane];  // weight of row `lane`
     wsum += wl;
     nlive += __popcll(ballot(wl != 0u));
-    constexpr int UNB = LEAN ? 1 : 16 / NB;
-#pragma unroll UNB
+#pragma unroll
     for (int bt = 0; bt < 16 / NB; ++bt) {
       Raw8<T> kr[NB], vr[NB];
 #pragma unroll

@@ -483,7 +483,10 @@ constexpr int UA = 4;                  // 16-byte loads in flight per lane in th
 struct SelShared {
   unsigned long long hist[NB1];  // mass histogram of level 1
   unsigned long long h2[256], h3[256];  // levels 2 and 3 (cleared when the workgroup starts)
-  uint32_t cand[CAND_CAP];       // the cut bucket's tokens
+  union {
+    uint32_t cand[CAND_CAP];     // the cut bucket's tokens
+    float fold[NW][2][HD];       // after the selection: the wavefronts' sums of a condensing block
+  };
   unsigned long long red[2][NW];
   unsigned long long wt[NW];     // level-1 cut: each wavefront's segment of 256 buckets
   float fred[NW];
@@ -960,15 +963,87 @@ HK_DEV void sel_finish(const Args &a, int bh, const SelGeo &g, SelShared &sh, ui
 }
 
 // The condensation of the head's E oldest blocks by the select workgroup itself (FUSE:
-// the fused step, when at most FUSE_COND_BLOCKS blocks can condense per step): one
-// wavefront per ring slot, after the plan is written (its cursor read comes first).
+// the fused step, when at most FUSE_COND_BLOCKS blocks can condense per step), after the
+// plan is written (its cursor read comes first).  MERGE folds the blocks one after
+// another with the whole workgroup: each wavefront takes
+// 4 of the block's 64 rows (16 lanes a row, 8 head dims a lane) and sums w k and w v over
+// them; the wavefronts' sums meet in LDS (in the candidate buffer, free once the plan is
+// written) and 256 threads add them to the slot in wavefront order.  Blocks that land on
+// the same slot (more than C of them) are added in age order.
 template <typename T>
-HK_DEV void select_condense(const Args &a, int bh, const SelGeo &g, int32_t nu, uint64_t W_all) {
-  const int tid = threadIdx.x, wave = tid >> 6;
+HK_DEV void select_condense(const Args &a, int bh, const SelGeo &g, int32_t nu, uint64_t W_all, SelShared &sh) {
+  constexpr int EB = Elem<T>::bytes;
+  constexpr size_t ROWB = (size_t)HD * EB;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int sub = lane & 15, grp = lane >> 4;
+  const int P = a.P, C = a.C;
   __syncthreads();
-  if (a.mode == HARDKV_COND_MERGE)
-    for (int i = wave; i < g.E && i < a.C; i += NW)
-      condense_chain<T, Elem<T>::bytes == 2 ? 4 : 2, true>(a, bh, i, g.c, g.E, nu, W_all);
+  if (a.mode == HARDKV_COND_MERGE) {
+    const float inv = W_all ? (float)(1.0 / (double)W_all) : 0.0f;
+    for (int64_t e = 0; e < g.E; ++e) {
+      const size_t pb = (size_t)((g.c / BK + e) % P);
+      const size_t sg = (size_t)bh * C + (size_t)((nu + e) % C);
+      const bool fresh = a.cond_n[sg] == 0;  // (read before this block's count is added)
+      const int row = wave * 4 + grp;
+      const uint32_t wl = a.weights[((size_t)bh * P + pb) * BK + row];
+      const char *base = (const char *)a.pool_k + pool_row0(a, bh, (int)pb) * ROWB;
+      const size_t roff = (size_t)row * ROWB + sub * 8 * EB;
+      Raw8<T> kr, vr;
+      raw_load_nt(base + roff, kr);
+      raw_load_nt((const char *)a.pool_v + pool_row0(a, bh, (int)pb) * ROWB + roff, vr);
+      float kf[8], vf[8], ak[8], av[8];
+      raw_to_f(kr, kf);
+      raw_to_f(vr, vf);
+      const float wf = (float)wl;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        ak[k] = wf * kf[k];
+        av[k] = wf * vf[k];
+      }
+#pragma unroll
+      for (int off = 16; off <= 32; off <<= 1) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          ak[k] += __shfl_xor(ak[k], off);
+          av[k] += __shfl_xor(av[k], off);
+        }
+      }
+      const uint64_t wsum = wave_sum_u64(sub == 0 ? (uint64_t)wl : 0ull);
+      const int nlive = __popcll(ballot(sub == 0 && wl != 0u));
+      if (lane < 16) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          sh.fold[wave][0][sub * 8 + k] = ak[k];
+          sh.fold[wave][1][sub * 8 + k] = av[k];
+        }
+      }
+      if (lane == 0) {
+        sh.red[0][wave] = wsum;
+        sh.red[1][wave] = (unsigned long long)nlive;
+      }
+      __syncthreads();
+      if (tid < 2 * HD) {
+        const int half = tid / HD, d = tid - half * HD;
+        float acc = 0.0f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) acc += sh.fold[w][half][d];
+        float *num = (half ? a.cond_vn : a.cond_kn) + sg * HD + d;
+        *num = (fresh ? 0.0f : *num) + acc * inv;
+      }
+      if (tid == 0) {
+        uint64_t ws = 0;
+        int n = 0;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+          ws += sh.red[0][w];
+          n += (int)sh.red[1][w];
+        }
+        a.cond_omega[sg] = (fresh ? 0.0f : a.cond_omega[sg]) + (W_all ? (float)((double)ws / (double)W_all) : 0.0f);
+        a.cond_n[sg] += n;
+      }
+      __syncthreads();  // (the sums are read before the next block writes them)
+    }
+  }
   if (wave == 0) condense_advance(a, bh, g.c, g.E, nu);
 }
 
@@ -1013,7 +1088,7 @@ __global__ __launch_bounds__(SEL_THREADS) void hardkv_select(Args a) {
     __syncthreads();
   }
   sel_finish(a, bh, g, sh, blk, W_all, W_U, Tm, R1, b1);
-  if (FUSE) select_condense<T>(a, bh, g, nu, W_all);
+  if (FUSE) select_condense<T>(a, bh, g, nu, W_all, sh);
 }
 
 // Split select, for long pools: the head's blocks in slices of SEL_SLICE_BLOCKS, one
@@ -1184,7 +1259,7 @@ __global__ __launch_bounds__(SEL_THREADS) void hardkv_sel_finish(Args a) {
     __syncthreads();
   }
   sel_finish(a, bh, g, sh, blk, W_all, W_U, Tm, R1, b1);
-  if (FUSE) select_condense<T>(a, bh, g, nu, W_all);
+  if (FUSE) select_condense<T>(a, bh, g, nu, W_all, sh);
 }
 
 // Flatten Index to the sum: one workgroup scans n_u = k* (rewritten heads) or 0 over

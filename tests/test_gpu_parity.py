@@ -83,6 +83,11 @@ SPLIT_CASES = {
     "split_evict_f32": dict(dtype="f32", pool_blocks=1030, sparse_cap=16384, ctx_len=30000, ctx_min=20000),
     # nothing in the pool yet: no survivor mass, nothing to cut
     "split_empty_pool": dict(pool_blocks=1100, sparse_cap=4096, ctx_len=20, ctx_min=0, dense_window=32),
+    # the largest ring the select indexes (HARDKV_MAX_POOL_BLOCKS = 6144 blocks, 24 slices):
+    # the prefill fills all but its last block, the first append starts the last one, and
+    # four blocks condense
+    "split_max_ring": dict(batch=1, pool_blocks=6144, sparse_cap=6140 * 64, ctx_len=6143 * 64 + 32,
+                           ctx_min=6143 * 64 + 32, cond_mode=COND_MERGE, dense_window=32),
 }
 
 

@@ -307,12 +307,19 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_score(Args a) {
               buf_load_nt(kb, off, buf[u][l]);
             }
           } else if constexpr (SHARED) {
-            // a row of one of the chunk's blocks (rows past the chunk read a row of its last
-            // block and are not kept)
+            // a row of the batch's block (the same in every lane) through the buffer
+            // resource of the 1 GB pool segment that holds the block, so that every offset
+            // stays inside a resource's range; rows past the chunk read zeros (offset
+            // BUF_SKIP), with no branch
+            constexpr uint32_t SEGB = (1u << 30) / (uint32_t)(BK * HD * EB);  // blocks per segment
             const int bi = min(gi >> 2, nblk_c - 1);
             const uint32_t phys = (uint32_t)__builtin_amdgcn_readlane(phys_lane, bi);
-            const size_t row = (size_t)phys * BK + (size_t)(rel & (BK - 1));
-            raw_load_nt((const char *)a.pool_k + row * (HD * EB) + lane_b, buf[u][l]);
+            const uint32_t seg = phys / SEGB, local = phys % SEGB;
+            const uint64_t seg_bytes = (uint64_t)min((uint32_t)a.NB - seg * SEGB, SEGB) * BK * HD * EB;
+            const BufRes sr = make_buf((const char *)a.pool_k + (size_t)seg * SEGB * BK * HD * EB, seg_bytes);
+            const uint32_t row_b = (local * BK + (uint32_t)(rel & (BK - 1))) * (uint32_t)(HD * EB) + lane_b;
+            const uint32_t off = ((gi < ngroups) & (rel < nrows)) ? row_b : BUF_SKIP;
+            buf_load_nt(sr, off, buf[u][l]);
           } else {
             // rows past the chunk read zeros (offset BUF_SKIP), with no branch
             const uint32_t row_b = (uint32_t)(pb * BK + (rel & (BK - 1))) * (uint32_t)(HD * EB) + lane_b;

@@ -11,10 +11,42 @@
 
 namespace hardkv {
 
+// The buffer resources over a ring block's rows (K and V) and the block's first row inside
+// them: the unit's own ring, or in the shared pool the 1 GB segment that holds the block's
+// physical block (one resource reaches 2 GB; the pool can be larger).  Wave-uniform.
+template <typename T>
+struct BlockRows {
+  BufRes k, v;
+  uint32_t row0;
+};
+template <typename T>
+HK_DEV BlockRows<T> block_rows(const Args &a, int bh, int pb) {
+  constexpr uint32_t ROWB = (uint32_t)(HD * Elem<T>::bytes);
+  constexpr uint64_t BLKB = (uint64_t)BK * ROWB;
+  BlockRows<T> r;
+  if (a.pool_shared) {
+    constexpr uint32_t SEGB = (uint32_t)((1ull << 30) / BLKB);  // blocks per segment
+    const int32_t ph = a.btab[(size_t)bh * a.P + pb];
+    const uint32_t phys = ph < 0 ? 0u : (uint32_t)ph;
+    const uint32_t seg = phys / SEGB;
+    const size_t base = (size_t)seg * SEGB * BLKB;
+    const uint64_t bytes = (uint64_t)min((uint32_t)a.NB - seg * SEGB, SEGB) * BLKB;
+    r.k = make_buf((const char *)a.pool_k + base, bytes);
+    r.v = make_buf((const char *)a.pool_v + base, bytes);
+    r.row0 = (phys % SEGB) * BK;
+  } else {
+    const size_t base = (size_t)bh * a.P * BLKB;
+    r.k = make_buf((const char *)a.pool_k + base, (uint64_t)a.P * BLKB);
+    r.v = make_buf((const char *)a.pool_v + base, (uint64_t)a.P * BLKB);
+    r.row0 = (uint32_t)pb * BK;
+  }
+  return r;
+}
+
 // One wavefront folds into ring slot (nu + i) mod C, in age order, every condensing block
 // that lands there (blocks i, i + C, ...).  Inside a block, 16 lanes hold one row (8 head
-// dims each) and a load covers 4 rows; NB loads of keys and NB of values per lane are in
-// flight per batch.  Each lane accumulates w k and w v for its dims over its rows, the
+// dims each) and a load covers 4 rows, through the block's buffer resources; NB loads of
+// keys and NB of values per lane are in flight per batch.  Each lane accumulates w k and w v for its dims over its rows, the
 // four row groups are summed by lane exchanges, and 16 lanes update the slot.
 template <typename T, int NB>
 HK_DEV void condense_chain(const Args &a, int bh, int i, int64_t c, int64_t E, int32_t nu, uint64_t w_all) {
@@ -35,9 +67,8 @@ HK_DEV void condense_chain(const Args &a, int bh, int i, int64_t c, int64_t E, i
   int nlive = 0;  // rows merged: those with a weight (all 64 of a block unless dropped)
   for (int64_t e = i; e < E; e += C) {
     const size_t pb = (size_t)((c / BK + e) % P);
-    const size_t row0 = pool_row0(a, bh, (int)pb);
-    const char *kb = (const char *)a.pool_k + row0 * ROWB + sub * 8 * EB;
-    const char *vb = (const char *)a.pool_v + row0 * ROWB + sub * 8 * EB;
+    const BlockRows<T> br = block_rows<T>(a, bh, (int)pb);
+    const uint32_t lane_off = br.row0 * (uint32_t)ROWB + (uint32_t)(sub * 8 * EB);
     const uint32_t wl = a.weights[((size_t)bh * P + pb) * BK + lane];  // weight of row `lane`
     wsum += wl;
     nlive += __popcll(ballot(wl != 0u));
@@ -47,8 +78,8 @@ HK_DEV void condense_chain(const Args &a, int bh, int i, int64_t c, int64_t E, i
 #pragma unroll
       for (int it = 0; it < NB; ++it) {
         const int row = (bt * NB + it) * 4 + grp;
-        raw_load_nt(kb + (size_t)row * ROWB, kr[it]);
-        raw_load_nt(vb + (size_t)row * ROWB, vr[it]);
+        buf_load_nt(br.k, lane_off + (uint32_t)(row * ROWB), kr[it]);
+        buf_load_nt(br.v, lane_off + (uint32_t)(row * ROWB), vr[it]);
       }
 #pragma unroll
       for (int it = 0; it < NB; ++it) {

@@ -31,7 +31,7 @@ __global__ __launch_bounds__(NTHREADS) void hardkv_condense(Args a) {
   const int64_t E = hd->E;
   const int32_t nu = hd->nu_plan;
   if (a.mode == HARDKV_COND_MERGE && i < E && i < a.C)  // chain heads: blocks 0 .. min(E, C) - 1
-    condense_chain<T, 8>(a, bh, i, c, E, nu, hd->w_all);
+    condense_chain<T, Elem<T>::bytes == 2 ? 8 : 4>(a, bh, i, c, E, nu, hd->w_all);
   if (i == 0) condense_advance(a, bh, c, E, nu);  // (the whole wavefront of slot 0)
 }
 
